@@ -1,0 +1,139 @@
+"""Float64 CPU oracle for the chunked SSD scan (test infrastructure).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package. The product path
+(``chunked_ssd_scan_amd``) never imports, links or calls it, and the two share
+no code.
+
+The oracle itself is ``ssd_oracle.c``: the plain token-by-token recurrence in
+double precision (see that file's header for the definition and the page
+passages it follows). This module builds it with gcc and wraps it with ctypes.
+Pins that tie it to the pages and to mathematics live in
+``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_oracle.c")
+_LIB = os.path.join(_HERE, "libssd_oracle.so")
+_libs = {}
+
+GCC_FLAGS = ["-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
+    """Compile ssd_oracle.c with gcc (-O2, no fast-math, OpenMP)."""
+    if force or not os.path.exists(out):
+        tmp = out + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", *GCC_FLAGS, "-o", tmp, src, "-lm"], check=True)
+        os.replace(tmp, out)
+    return out
+
+
+def _load(path: Optional[str] = None):
+    """Load the oracle library (``path`` selects another build of the same source)."""
+    key = path or _LIB
+    if key not in _libs:
+        if path is None and (not os.path.exists(_LIB)
+                             or os.path.getmtime(_LIB) < os.path.getmtime(_SRC)):
+            build()
+        lib = ctypes.CDLL(key)
+        i64, vp = ctypes.c_int64, ctypes.c_void_p
+        lib.ssd_oracle_f64.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 7 + [vp, i64, vp, vp, ctypes.c_int]
+        lib.ssd_oracle_f64.restype = ctypes.c_int
+        lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        _libs[key] = lib
+    return _libs[key]
+
+
+def max_threads() -> int:
+    return int(_load().ssd_oracle_max_threads())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    assert t.device.type == "cpu" and t.is_contiguous()
+    return t.data_ptr()
+
+
+def ssd_oracle(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+               D: Optional[torch.Tensor] = None, init_state: Optional[torch.Tensor] = None,
+               theta: Optional[torch.Tensor] = None,
+               bh: Optional[Sequence[int]] = None, want_y: bool = True,
+               nthreads: int = 0, lib_path: Optional[str] = None):
+    """Float64 oracle on CPU tensors.
+
+    Shapes: x [b,T,R,H,P], da [b,T,H], B/C [b,T,R,G,N] (fp32 or bf16; the
+    tests may pass float64 for all three),
+    D [H], init_state [b,H,P,N], theta [b,T,H,N/2] (fp32).
+
+    With ``bh=None`` returns (y [b,T,R,H,P], final [b,H,P,N]) as float64
+    numpy arrays. With a list of slice indices bh = b*H + h it returns
+    (y_sel [n,T,R,P], final_sel [n,P,N]) for just those slices.
+    ``want_y=False`` skips storing y (y is returned as None).
+    ``lib_path`` runs another build of the oracle source (the tests use it to
+    check that planted mistakes are caught by the pins).
+    """
+    lib = _load(lib_path)
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    assert da.shape == (b, T, H)
+    assert B.shape == C.shape == (b, T, R, G, N)
+    if x.dtype == torch.bfloat16:
+        dt = 1
+    elif x.dtype == torch.float32:
+        dt = 0
+    elif x.dtype == torch.float64:
+        dt = 2
+    else:
+        raise TypeError(f"unsupported input dtype {x.dtype}")
+    assert B.dtype == x.dtype and C.dtype == x.dtype
+    for t in (da, D, init_state, theta):
+        assert t is None or t.dtype == torch.float32
+    cont = lambda t: None if t is None else t.detach().cpu().contiguous()
+    x, da, B, C, D, init_state, theta = map(cont, (x, da, B, C, D, init_state, theta))
+
+    if bh is None:
+        n = b * H
+        bh_arr = None
+    else:
+        bh_arr = np.ascontiguousarray(np.asarray(bh, dtype=np.int64))
+        n = int(bh_arr.size)
+    y_sel = np.empty((n, T, R, P), dtype=np.float64) if want_y else None
+    fin = np.empty((n, P, N), dtype=np.float64)
+    rc = lib.ssd_oracle_f64(
+        b, T, H, P, N, G, R, dt,
+        _ptr(x), _ptr(da), _ptr(B), _ptr(C), _ptr(D), _ptr(init_state), _ptr(theta),
+        None if bh_arr is None else bh_arr.ctypes.data, n,
+        None if y_sel is None else y_sel.ctypes.data, fin.ctypes.data, int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_oracle_f64 failed with code {rc}")
+    if bh is not None:
+        return y_sel, fin
+    y = None
+    if want_y:
+        y = y_sel.reshape(b, H, T, R, P).transpose(0, 2, 3, 1, 4).copy()
+    return y, fin.reshape(b, H, P, N)
+
+
+def ssd_oracle_inputs(inp, bh=None, want_y=True, nthreads=0):
+    """Convenience wrapper taking an ``ssd_inputs.Inputs`` bundle."""
+    return ssd_oracle(inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state, inp.theta,
+                      bh=bh, want_y=want_y, nthreads=nthreads)
+
+
+def time_oracle(inp, bh: Sequence[int], nthreads: int = 0):
+    """Wall time of the oracle on the given slices (steady clock)."""
+    t0 = time.perf_counter()
+    ssd_oracle_inputs(inp, bh=bh, want_y=True, nthreads=nthreads)
+    return time.perf_counter() - t0

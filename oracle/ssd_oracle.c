@@ -1,0 +1,181 @@
+/*
+ * Float64 token-by-token oracle for the chunked SSD scan.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the bench's CPU
+ * baseline leg do. It shares no code with the HIP path.
+ *
+ * What it computes (for every batch b and head h, group g = h / (H/G)):
+ *
+ *   S = init_state[b,h]  (P x N, or zero)
+ *   for t = 0 .. T-1:
+ *     if theta: every N-axis pair (2k, 2k+1) of S is turned by the plane
+ *               rotation R(theta[b,t,h,k]) = [[cos, -sin], [sin, cos]]
+ *     S = exp(da[b,t,h]) * S + sum_r x[b,t,r,h,:] (outer) B[b,t,r,g,:]
+ *     y[b,t,r,h,p] = sum_n C[b,t,r,g,n] * S[p,n] + D[h] * x[b,t,r,h,p]
+ *   final_state[b,h] = S
+ *
+ * Sources (cited by page title and section):
+ *  - "SSM Selective Scan" (LeetGPU challenge write-up), problem statement:
+ *    the selective-scan recurrence h_t = Abar_t h_{t-1} + Bbar_t u_t,
+ *    y_t = C_t . h_t + skip * u_t, with a zero starting state. Here the decay
+ *    is one scalar per head (Mamba-2), Abar = exp(da), and x already carries
+ *    the input scaling (dt enters only through da).
+ *  - burn-mamba "mamba3/ssd/serial.rs", ssd_serial and k1..k5: the multi-rank
+ *    (MIMO) form. The R writes of one step are summed into the state under a
+ *    single decay, and every rank's read at step t sees all R writes of step t
+ *    (the K5 mask keeps the full R x R diagonal block).
+ *  - "mamba3/scan.py", module docstring ("THE TRICK"): the rotated recurrence
+ *    h_t = alpha_t R(theta_t) h_{t-1} + S_t (trapezoid weights beta=0,
+ *    gamma=1); rotate_by gives the pair convention (even = c*a - s*b,
+ *    odd = s*a + c*b). final_state is the physical state h_{T-1}.
+ *
+ * Inputs x, B, C are read at their stored precision (fp32, or bf16 decoded
+ * exactly; the tests may also hand in float64); da, D, theta, init_state are
+ * fp32. All arithmetic is double.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_IN_F32 0
+#define ORACLE_IN_BF16 1
+#define ORACLE_IN_F64 2
+
+typedef struct {
+    int64_t batch, T, H, P, N, G, R;
+    int in_dtype;
+    const void *x, *B, *C;
+    const float *da, *D, *init_state, *theta;
+} oracle_problem;
+
+/* Exact widening of one stored input element to double. */
+static double load_elem(const void *base, int64_t i, int dtype) {
+    if (dtype == ORACLE_IN_F32) return (double)((const float *)base)[i];
+    if (dtype == ORACLE_IN_F64) return ((const double *)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* One (b, h) slice: y_out is [T][R][P], fin_out is [P][N], S is P*N scratch. */
+static void run_slice(const oracle_problem *pr, int64_t b, int64_t h,
+                      double *y_out, double *fin_out, double *S) {
+    const int64_t T = pr->T, H = pr->H, P = pr->P, N = pr->N, G = pr->G, R = pr->R;
+    const int64_t g = h / (H / G);
+
+    if (pr->init_state) {
+        const float *h0 = pr->init_state + (b * H + h) * P * N;
+        for (int64_t i = 0; i < P * N; ++i) S[i] = (double)h0[i];
+    } else {
+        memset(S, 0, sizeof(double) * (size_t)(P * N));
+    }
+
+    for (int64_t t = 0; t < T; ++t) {
+        /* rotation of the carried state, pair (2k, 2k+1) by theta[b,t,h,k] */
+        if (pr->theta) {
+            const float *th = pr->theta + ((b * T + t) * H + h) * (N / 2);
+            for (int64_t k = 0; k < N / 2; ++k) {
+                double c = cos((double)th[k]), s = sin((double)th[k]);
+                for (int64_t p = 0; p < P; ++p) {
+                    double a0 = S[p * N + 2 * k], a1 = S[p * N + 2 * k + 1];
+                    S[p * N + 2 * k] = c * a0 - s * a1;
+                    S[p * N + 2 * k + 1] = s * a0 + c * a1;
+                }
+            }
+        }
+        /* decay, then the R rank-one writes of step t */
+        double a = exp((double)pr->da[(b * T + t) * H + h]);
+        for (int64_t i = 0; i < P * N; ++i) S[i] *= a;
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t xrow = (((b * T + t) * R + r) * H + h) * P;
+            int64_t brow = (((b * T + t) * R + r) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double xv = load_elem(pr->x, xrow + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    S[p * N + n] += xv * load_elem(pr->B, brow + n, pr->in_dtype);
+            }
+        }
+        /* every rank reads the state after all writes of step t */
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t xrow = (((b * T + t) * R + r) * H + h) * P;
+            int64_t crow = (((b * T + t) * R + r) * G + g) * N;
+            double dh = pr->D ? (double)pr->D[h] : 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += load_elem(pr->C, crow + n, pr->in_dtype) * S[p * N + n];
+                acc += dh * load_elem(pr->x, xrow + p, pr->in_dtype);
+                y_out[(t * R + r) * P + p] = acc;
+            }
+        }
+    }
+    memcpy(fin_out, S, sizeof(double) * (size_t)(P * N));
+}
+
+/*
+ * Runs the recurrence on the selected (b, h) slices.
+ *   bh_list: n_bh indices bh = b*H + h (NULL: every slice, in bh order).
+ *   y_sel:   [n_bh][T][R][P] doubles (may be NULL to skip y).
+ *   fin_sel: [n_bh][P][N] doubles.
+ *   nthreads <= 0 uses the OpenMP default.
+ * Returns 0, or a negative code for a bad argument.
+ */
+int ssd_oracle_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
+                   int64_t G, int64_t R, int in_dtype,
+                   const void *x, const float *da, const void *B, const void *C,
+                   const float *D, const float *init_state, const float *theta,
+                   const int64_t *bh_list, int64_t n_bh,
+                   double *y_sel, double *fin_sel, int nthreads) {
+    if (batch < 1 || T < 1 || H < 1 || P < 1 || N < 1 || G < 1 || R < 1) return -1;
+    if (H % G != 0) return -2;
+    if (theta && (N % 2)) return -3;
+    if (in_dtype != ORACLE_IN_F32 && in_dtype != ORACLE_IN_BF16 && in_dtype != ORACLE_IN_F64)
+        return -4;
+    if (!x || !da || !B || !C || !fin_sel) return -5;
+    if (!bh_list) n_bh = batch * H;
+    for (int64_t i = 0; bh_list && i < n_bh; ++i)
+        if (bh_list[i] < 0 || bh_list[i] >= batch * H) return -6;
+
+    oracle_problem pr = {batch, T, H, P, N, G, R, in_dtype, x, B, C, da, D, init_state, theta};
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *S = (double *)malloc(sizeof(double) * (size_t)(P * N));
+        double *ytmp = y_sel ? NULL : (double *)malloc(sizeof(double) * (size_t)(T * R * P));
+        int ok = S && (y_sel || ytmp);
+        if (!ok) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_bh; ++i) {
+            if (!ok) continue;
+            int64_t bh = bh_list ? bh_list[i] : i;
+            double *yo = y_sel ? y_sel + i * T * R * P : ytmp;
+            run_slice(&pr, bh / H, bh % H, yo, fin_sel + i * P * N, S);
+        }
+        free(S);
+        free(ytmp);
+    }
+    return err;
+}
+
+/* Number of threads an OpenMP parallel region would use (for reporting). */
+int ssd_oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,329 @@
+"""Pins that tie the float64 oracle to the pages and to mathematics (CPU only).
+
+Each test computes the expected value another way than the oracle's token
+recurrence: closed forms, the one-chunk quadratic (segsum) form, the K1..K5
+chunk algorithm, explicit decay products, the Mamba-1 selective-scan statement,
+exact invariants (linearity, causality, split calls), and the decay factors
+printed in the LeetGPU worked example. The last test plants mistakes in copies
+of the oracle source and checks that the pins catch every one of them.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import torch
+
+import forms
+import oracle
+import ssd_inputs as si
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+TOL = 1e-10   # float64 formulations that differ only in summation order
+
+
+def relerr(a, ref):
+    a, ref = np.asarray(a), np.asarray(ref)
+    return float(np.abs(a - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def ora(inp, **kw):
+    return oracle.ssd_oracle_inputs(inp, **kw)
+
+
+def args(inp):
+    return (inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state, inp.theta)
+
+
+CASES = {
+    "siso": dict(),
+    "siso_init": dict(init_state=True),
+    "mimo3": dict(mimo_rank=3),
+    "rot": dict(rotation=True),
+    "rot_init_mimo2": dict(rotation=True, init_state=True, mimo_rank=2),
+    "groups2": dict(nheads=4, ngroups=2, init_state=True),
+    "bf16": dict(dtype="bf16", mimo_rank=2, rotation=True),
+    "noskip": dict(skip="none", seqlen=20),
+    "t1": dict(seqlen=1, init_state=True, rotation=True, mimo_rank=2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_quadratic_form(name):
+    inp = si.make_inputs(si.small_shape(**CASES[name]), seed=1)
+    y, f = ora(inp)
+    yq, fq = forms.quadratic_form(*args(inp))
+    assert relerr(y, yq) < TOL and relerr(f, fq) < TOL
+
+
+@pytest.mark.parametrize("chunk_len", [1, 3, 8, 16, 37, 64])
+def test_chunk_length_independence(chunk_len):
+    # "mamba3/scan.py" verify(): chunk sizes 8/16/64 and a ragged length 37
+    inp = si.make_inputs(si.small_shape(seqlen=37, mimo_rank=2, rotation=True,
+                                        init_state=True), seed=2)
+    y, f = ora(inp)
+    yc, fc = forms.chunked_form(*args(inp), chunk_len=chunk_len)
+    assert relerr(y, yc) < TOL and relerr(f, fc) < TOL
+
+
+def test_product_form_tiny():
+    inp = si.make_inputs(si.small_shape(batch=1, seqlen=9, nheads=2, headdim=4, dstate=6,
+                                        mimo_rank=2, rotation=True, init_state=True), seed=3)
+    y, f = ora(inp)
+    yp, fp = forms.product_form(*args(inp))
+    assert relerr(y, yp) < TOL and relerr(f, fp) < TOL
+
+
+def test_da_zero_is_pure_cumsum():
+    inp = si.make_inputs(si.small_shape(mimo_rank=2, init_state=True), seed=4)
+    inp.da.zero_()
+    y, f = ora(inp)
+    x, B, C, D, h0 = map(forms.f64, (inp.x, inp.B, inp.C, inp.D, inp.init_state))
+    # S_t = h0 + sum_{s<=t} sum_r x_{s,r} (outer) B_{s,r}
+    W = np.einsum("btrhp,btrhn->bthpn", x, np.repeat(B, x.shape[3] // B.shape[3], axis=3))
+    S = np.cumsum(W, axis=1) + h0[:, None]
+    Cx = np.repeat(C, x.shape[3] // C.shape[3], axis=3)
+    yc = np.einsum("btrhn,bthpn->btrhp", Cx, S) + D[None, None, None, :, None] * x
+    assert relerr(y, yc) < TOL and relerr(f, S[:, -1]) < TOL
+
+
+@pytest.mark.parametrize("a", [-0.3, -1.7])
+def test_constant_decay_geometric_series(a):
+    T = 50
+    x = torch.ones(1, T, 1, 1, 1)
+    B = torch.ones(1, T, 1, 1, 1)
+    y, f = oracle.ssd_oracle(x, torch.full((1, T, 1), a), B, B.clone())
+    a = float(np.float32(a))                                 # da is stored in fp32
+    t = np.arange(T)
+    expect = (1 - np.exp(a * (t + 1))) / (1 - np.exp(a))   # the write at t is read at t
+    assert relerr(y[0, :, 0, 0, 0], expect) < 1e-13
+    assert abs(f[0, 0, 0, 0] - expect[-1]) < 1e-13
+
+
+def test_constant_theta_closed_form():
+    # one write at t=0 of (1, 0), no decay: the state turns by theta each later step
+    T, th = 40, 0.37
+    x = torch.zeros(1, T, 1, 1, 1)
+    x[0, 0] = 1.0
+    B = torch.zeros(1, T, 1, 1, 2)
+    B[0, 0, 0, 0, 0] = 1.0
+    C = torch.zeros(1, T, 2, 1, 2)   # rank 0 reads cos, rank 1 reads sin
+    C[..., 0, 0, 0] = 1.0
+    C[..., 1, 0, 1] = 1.0
+    x2 = torch.cat([x, x * 0], dim=2)
+    B2 = torch.cat([B, B * 0], dim=2)
+    theta = torch.full((1, T, 1, 1), th)
+    y, f = oracle.ssd_oracle(x2, torch.zeros(1, T, 1), B2, C, theta=theta)
+    th = float(np.float32(th))                               # theta is stored in fp32
+    t = np.arange(T)
+    assert relerr(y[0, :, 0, 0, 0], np.cos(t * th)) < 1e-12
+    assert relerr(y[0, :, 1, 0, 0], np.sin(t * th)) < 1e-12
+    # an initial state is turned by the inclusive cumulative angle (t+1)*theta
+    h0 = torch.zeros(1, 1, 1, 2)
+    h0[0, 0, 0, 0] = 1.0
+    y, f = oracle.ssd_oracle(x2 * 0, torch.zeros(1, T, 1), B2, C, init_state=h0, theta=theta)
+    assert relerr(y[0, :, 0, 0, 0], np.cos((t + 1) * th)) < 1e-12
+    assert relerr(y[0, :, 1, 0, 0], np.sin((t + 1) * th)) < 1e-12
+    assert relerr(f[0, 0, 0], [math.cos(T * th), math.sin(T * th)]) < 1e-12
+
+
+def test_theta_zero_is_no_rotation():
+    inp = si.make_inputs(si.small_shape(rotation=True, init_state=True), seed=5)
+    inp.theta.zero_()
+    y, f = ora(inp)
+    y0, f0 = oracle.ssd_oracle(inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state)
+    assert np.array_equal(y, y0) and np.array_equal(f, f0)
+
+
+def test_rotation_identity_folded_frame():
+    # h_t = R(Phi_t) g_t: the physical recurrence equals the un-rotated recurrence
+    # on B~ = R(-Phi) B, C~ = R(-Phi) C, and the final states differ by R(Phi_{T-1})
+    inp = si.make_inputs(si.small_shape(rotation=True, init_state=True, mimo_rank=2,
+                                        nheads=2), seed=6)
+    y, f = ora(inp)
+    b, T, R, G, N = inp.B.shape
+    H = inp.x.shape[3]
+    assert G == 1
+    Phi = np.cumsum(forms.f64(inp.theta), axis=1)          # [b,T,H,N/2]
+    for h in range(H):
+        Bt = forms.rotate_pairs(forms.f64(inp.B)[:, :, :, 0, :], -Phi[:, :, None, h, :])
+        Ct = forms.rotate_pairs(forms.f64(inp.C)[:, :, :, 0, :], -Phi[:, :, None, h, :])
+        tt = lambda a: torch.from_numpy(np.ascontiguousarray(a[:, :, :, None, :]))
+        yg, fg = oracle.ssd_oracle(inp.x[:, :, :, h:h + 1].double().contiguous(), inp.da[:, :, h:h + 1].contiguous(),
+                                   tt(Bt), tt(Ct), inp.D[h:h + 1].contiguous(),
+                                   inp.init_state[:, h:h + 1].contiguous())
+        assert relerr(y[:, :, :, h], yg[:, :, :, 0]) < TOL
+        fphys = forms.rotate_pairs(fg[:, 0], Phi[:, -1, h][:, None, :])
+        assert relerr(f[:, h], fphys) < TOL
+
+
+def _slice_t(inp, t0, t1, init):
+    sl = lambda a: None if a is None else a[:, t0:t1].contiguous()
+    return oracle.ssd_oracle(sl(inp.x), sl(inp.da), sl(inp.B), sl(inp.C), inp.D,
+                             init, sl(inp.theta))
+
+
+@pytest.mark.parametrize("split", [1, 13, 36])
+def test_split_call_composition(split):
+    inp = si.make_inputs(si.small_shape(seqlen=37, rotation=True, init_state=True,
+                                        mimo_rank=2), seed=7)
+    y, f = ora(inp)
+    y1, f1 = _slice_t(inp, 0, split, inp.init_state)
+    y2, f2 = _slice_t(inp, split, 37, torch.from_numpy(f1).float())
+    # the hand-over rounds the carried state to fp32 (init_state is fp32)
+    assert relerr(np.concatenate([y1, y2], axis=1), y) < 1e-6
+    assert relerr(f2, f) < 1e-6
+
+
+def test_mimo_extra_ranks_zero_is_siso():
+    inp = si.make_inputs(si.small_shape(mimo_rank=3, skip="none", init_state=True), seed=8)
+    inp.x[:, :, 1:] = 0
+    y, f = ora(inp)
+    for r in range(3):
+        yr, fr = oracle.ssd_oracle(inp.x[:, :, :1].contiguous(), inp.da,
+                                   inp.B[:, :, :1].contiguous(), inp.C[:, :, r:r + 1].contiguous(),
+                                   None, inp.init_state)
+        assert relerr(y[:, :, r], yr[:, :, 0]) < TOL
+        assert relerr(f, fr) < TOL
+
+
+def test_linearity_in_x_and_initial_state():
+    inp = si.make_inputs(si.small_shape(mimo_rank=2, rotation=True, init_state=True,
+                                        skip="none"), seed=9)
+    y, f = ora(inp)
+    yx, fx = oracle.ssd_oracle(inp.x, inp.da, inp.B, inp.C, None, None, inp.theta)
+    yh, fh = oracle.ssd_oracle(inp.x * 0, inp.da, inp.B, inp.C, None, inp.init_state, inp.theta)
+    assert relerr(yx + yh, y) < TOL and relerr(fx + fh, f) < TOL
+
+
+def test_skip_term():
+    inp = si.make_inputs(si.small_shape(mimo_rank=2), seed=10)
+    y, _ = ora(inp)
+    y0, _ = oracle.ssd_oracle(inp.x, inp.da, inp.B, inp.C, None)
+    Dx = forms.f64(inp.D)[None, None, None, :, None] * forms.f64(inp.x)
+    assert relerr(y - y0, Dx) < TOL
+
+
+def test_causality():
+    # "mamba3/scan.py" verify(): appending large future tokens leaves the past unchanged
+    inp = si.make_inputs(si.small_shape(seqlen=30, mimo_rank=2, rotation=True,
+                                        init_state=True), seed=11)
+    y, _ = ora(inp)
+    t0 = 17
+    for t in (inp.x, inp.B, inp.C, inp.theta):
+        t[:, t0:] *= 50
+    inp.da[:, t0:] = -5.0
+    y2, _ = ora(inp)
+    assert np.array_equal(y[:, :t0], y2[:, :t0])
+    assert not np.allclose(y[:, t0:], y2[:, t0:])
+
+
+def test_mamba1_selective_scan_special_case():
+    # The LeetGPU statement with a decay row constant over n (A[d, n] = a_d) is this
+    # scan with one head per channel, P = 1, G = 1, x = delta*u, da = delta*a_d.
+    # Its skip term multiplies u (not x = delta*u), so it is added outside.
+    g = torch.Generator().manual_seed(12)
+    b, T, Dm, N = 2, 23, 5, 7
+    u = torch.randn(b, T, Dm, generator=g)
+    delta = torch.nn.functional.softplus(torch.randn(b, T, Dm, generator=g))
+    a = -torch.rand(Dm, generator=g) * 2 - 0.1
+    A = a[:, None].expand(Dm, N).contiguous()
+    Bm = torch.randn(b, T, N, generator=g)
+    Cm = torch.randn(b, T, N, generator=g)
+    skip = torch.randn(Dm, generator=g)
+    ref = forms.mamba1_scan(u, delta, A, Bm, Cm, skip)
+    x = (delta * u)[:, :, None, :, None].contiguous()        # [b,T,1,H=D,P=1]
+    da = (delta * a).contiguous()                             # [b,T,H]
+    y, _ = oracle.ssd_oracle(x, da, Bm[:, :, None, None, :].contiguous(),
+                             Cm[:, :, None, None, :].contiguous())
+    got = y[:, :, 0, :, 0] + forms.f64(skip) * forms.f64(u)
+    assert relerr(got, ref) < 1e-6                            # x, da rounded to fp32
+
+
+def test_single_step():
+    inp = si.make_inputs(si.small_shape(seqlen=1, init_state=True, mimo_rank=2), seed=13)
+    y, f = ora(inp)
+    x, da, B, C, D, h0 = map(forms.f64, (inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state))
+    for bi in range(x.shape[0]):
+        for h in range(x.shape[3]):
+            S = math.exp(da[bi, 0, h]) * h0[bi, h] + x[bi, 0, :, h].T @ B[bi, 0, :, 0]
+            assert relerr(f[bi, h], S) < TOL
+            yy = C[bi, 0, :, 0] @ S.T + D[h] * x[bi, 0, :, h]
+            assert relerr(y[bi, 0, :, h], yy) < TOL
+
+
+def test_golden_selective_scan_decay_factors():
+    gold = json.load(open(os.path.join(HERE, "golden", "selective_scan_abar.json")))
+    T = 4
+    for a, printed in zip(gold["A_row"], gold["Abar_printed"]):
+        x = torch.zeros(1, T, 1, 1, 1)
+        x[0, 0] = 1.0
+        ones = torch.ones(1, T, 1, 1, 1)
+        da = torch.full((1, T, 1), gold["delta"] * a)
+        y, _ = oracle.ssd_oracle(x, da, ones, ones.clone())
+        ratio = y[0, 1:, 0, 0, 0] / y[0, :-1, 0, 0, 0]           # one step of decay
+        assert np.allclose(np.round(ratio, gold["decimals"]), printed)
+
+
+def test_bf16_inputs_are_decoded_exactly():
+    inp = si.make_inputs(si.small_shape(dtype="bf16", rotation=True, mimo_rank=2), seed=14)
+    y, f = ora(inp)
+    y32, f32 = oracle.ssd_oracle(inp.x.float(), inp.da, inp.B.float(), inp.C.float(),
+                                 inp.D, None, inp.theta)
+    assert np.array_equal(y, y32) and np.array_equal(f, f32)
+
+
+def test_slice_selection_matches_full_run():
+    inp = si.make_inputs(si.small_shape(mimo_rank=2, rotation=True), seed=15)
+    y, f = ora(inp)
+    H = inp.x.shape[3]
+    sel = [4, 0, 3]
+    ys, fs = ora(inp, bh=sel)
+    for i, bh in enumerate(sel):
+        assert np.array_equal(ys[i], y[bh // H, :, :, bh % H])
+        assert np.array_equal(fs[i], f[bh // H, bh % H])
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes: each mutant copy of the oracle must fail some pin.
+# ----------------------------------------------------------------------------
+MUTANTS = {
+    "rotation_sign": ("S[p * N + 2 * k] = c * a0 - s * a1;", "S[p * N + 2 * k] = c * a0 + s * a1;"),
+    "dropped_skip": ("acc += dh * load_elem", "acc += 0.0 * dh * load_elem"),
+    "decay_sign": ("double a = exp((double)pr->da", "double a = exp(-(double)pr->da"),
+    "decay_one_step_late": ("pr->da[(b * T + t) * H + h]", "pr->da[(b * T + (t > 0 ? t - 1 : 0)) * H + h]"),
+    "rank_zero_only_written": ("int64_t xrow = (((b * T + t) * R + r) * H + h) * P;\n            int64_t brow",
+                               "int64_t xrow = (((b * T + t) * R + 0) * H + h) * P;\n            int64_t brow"),
+    "group_index": ("const int64_t g = h / (H / G);", "const int64_t g = h % G;"),
+    "write_uses_C": ("load_elem(pr->B, brow + n", "load_elem(pr->C, brow + n"),
+    "init_ignored": ("S[i] = (double)h0[i];", "S[i] = 0.0 * h0[i];"),
+    "theta_wrong_head": ("((b * T + t) * H + h) * (N / 2)", "((b * T + t) * H + (H - 1 - h)) * (N / 2)"),
+}
+
+
+def _pin_battery(lib_path):
+    """Quadratic-form and closed-form checks against a given oracle build."""
+    worst = 0.0
+    for kw in (dict(mimo_rank=2, rotation=True, init_state=True, nheads=4, ngroups=2),
+               dict(seqlen=12, skip="randn")):
+        inp = si.make_inputs(si.small_shape(**kw), seed=16)
+        y, f = oracle.ssd_oracle(*args(inp), lib_path=lib_path)
+        yq, fq = forms.quadratic_form(*args(inp))
+        worst = max(worst, relerr(y, yq), relerr(f, fq))
+    return worst
+
+
+def test_pins_catch_planted_mistakes(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
+    assert _pin_battery(None) < TOL
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) == 1, name
+        path = tmp_path / f"{name}.c"
+        path.write_text(src.replace(old, new))
+        so = str(tmp_path / f"{name}.so")
+        subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
+        assert _pin_battery(so) > 1e-6, f"planted mistake {name!r} was not caught"
