@@ -1,0 +1,202 @@
+#!/usr/bin/env python3
+"""Throughput of the chunked SSD scan forward on one MI355X.
+
+Workload: the Mamba-2 2.7B layer shape, b=8, T=8192, H=80, P=64, N=128, G=1,
+chunk_len=256, x/B/C in bf16, da/D fp32, y and final_state fp32, seeded
+synthetic inputs (ssd_inputs.CONFIGS[2]) resident in HBM before timing.
+A step is one full forward scan (every stage) over the batch.
+
+Prints one JSON line with tokens/s, the HBM roofline of the dominant kernel
+(algorithmic bytes / kernel time measured with HIP events on the launch
+stream) and the float64 CPU oracle timed on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_bytes(s) -> int:
+    """Compulsory I/O: every input read once at its dtype, outputs written once."""
+    esz = 2 if s.dtype == "bf16" else 4
+    b, T, H, P, N, G, R = s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.mimo_rank
+    n = b * T * R * H * P * esz            # x
+    n += b * T * H * 4                      # da
+    n += 2 * b * T * R * G * N * esz        # B, C
+    n += H * 4 if s.skip != "none" else 0   # D
+    n += b * H * P * N * 4 if s.init_state else 0
+    n += b * T * H * (N // 2) * 4 if s.rotation else 0
+    n += b * T * R * H * P * 4              # y
+    n += b * H * P * N * 4                  # final_state
+    return n
+
+
+def algorithmic_flops(s) -> int:
+    """Causal (block-)lower-triangular K2 + K3 + K5 flops at the given chunk length."""
+    b, T, H, P, N, G, R, l = (s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
+                              s.mimo_rank, s.chunk_len)
+    nc = -(-T // l)
+    L = l * R
+    tri = L * (L + 1) // 2
+    k3 = 2 * b * H * T * R * P * N
+    k5_off = 2 * b * H * T * R * P * N
+    k5_diag = 2 * b * H * nc * tri * P
+    k2 = 2 * b * nc * tri * N * (H if s.rotation else G)
+    return k3 + k5_off + k5_diag + k2
+
+
+def source_digest() -> str:
+    src = os.path.join(ROOT, "chunked_ssd_scan_amd", "csrc", "ssd_scan.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def profiled_traffic(workload_tag: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
+
+    The summary carries a fenced json block with the calibrated bytes and the
+    digest of the kernel source it was measured on; a stale digest gives None.
+    """
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_tag}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\s*(\{.*?\})\s*```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_sha256_16") != source_digest():
+        return None
+    return int(d["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(inp, shape, nslices: int):
+    import oracle
+    nbh = shape.batch * shape.nheads
+    nslices = max(1, min(nslices, nbh))
+    step = nbh / nslices
+    sel = [int(i * step) for i in range(nslices)]
+    threads = len(os.sched_getaffinity(0))
+    secs = oracle.time_oracle(inp, sel, nthreads=threads)
+    tokens = shape.batch * shape.seqlen * (nslices / nbh)
+    return {
+        "value": tokens / secs,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{nslices} of the {nbh} (batch, head) slices over the full T={shape.seqlen}; "
+                   f"{secs:.2f} s wall; tokens/s scaled by the slice fraction"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=2,
+                    help="workload id in ssd_inputs.CONFIGS (the reported line uses 2)")
+    ap.add_argument("--cpu-slices", type=int, default=64)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--segments", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the scan shards over (batch, head) without communication; see DESIGN.md)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    ssd.load_library()
+    shape = si.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    inp = si.make_inputs(shape, seed=0)
+    g = inp.to(dev)
+    b, T, R, H, P = g.x.shape
+    y = torch.empty(g.x.shape, device=dev, dtype=torch.float32)
+    fin = torch.empty((b, H, P, shape.dstate), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        ssd.forward(g.x, g.da, g.B, g.C, g.D, g.init_state, shape.chunk_len, g.theta,
+                    y=y, final_state=fin, segments=args.segments, stream=stream.cuda_stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
+        print("non-finite output", file=sys.stderr)
+        return 1
+
+    tokens = shape.batch * shape.seqlen
+    ms_per_step = wall * 1e3 / args.steps
+    nbytes = algorithmic_bytes(shape)
+    flops = algorithmic_flops(shape)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    tag = f"cfg{args.config}"
+    traffic = profiled_traffic(tag)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    out = {
+        "metric": "SSD scan fwd tokens/s + % of HBM/MFMA roofline (b8,T8192,H80,P64,N128)",
+        "value": tokens * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded, layer-shaped; see ssd_inputs.py)",
+        "config": {"workload": shape.name, "batch": shape.batch, "seqlen": shape.seqlen,
+                   "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
+                   "ngroups": shape.ngroups, "mimo_rank": shape.mimo_rank,
+                   "chunk_len": shape.chunk_len, "rotation": shape.rotation,
+                   "segments": args.segments or "auto"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": nbytes, "kernel_ms": launch_ms},
+        "mfma": {"algorithmic_tflop": flops / 1e12,
+                 "achieved_tflops": flops / (launch_ms * 1e-3) / 1e12,
+                 "peak_tflops": mfma_peak,
+                 "frac": flops / (launch_ms * 1e-3) / 1e12 / mfma_peak},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_slices)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,166 @@
+"""Python binding of the chunked SSD scan C ABI (``include/ssd_scan.h``).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+``libssd_scan.so``. PyTorch is used for device memory and the current stream.
+Importing works without a GPU; calling the scan needs the built library and
+a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
+
+C entry points, mirrored here under the same names:
+  ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_status_str
+plus ``forward(...)``, a tensor-level convenience over ssd_forward_ex.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd_scan.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+SSD_OK = 0
+SSD_ERR_NULL_ARG = 1
+SSD_ERR_BAD_SHAPE = 2
+SSD_ERR_UNSUPPORTED = 3
+SSD_ERR_ALIAS = 4
+SSD_ERR_HIP = 5
+
+EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_status_str")
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("in_dtype", ctypes.c_int32)]
+
+
+class SsdLaunchOpts(ctypes.Structure):
+    _fields_ = [("segments", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ssd_status_str(status)} ({status})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libssd_scan.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"HIP library not built: {path} is missing "
+                "(run `python -c 'import __graft_entry__ as g; g.build()'`)")
+        lib = ctypes.CDLL(path)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        common = [ctypes.POINTER(SsdDims), vp, vp, vp, vp, vp, vp, i64, i64, vp, vp, vp]
+        lib.ssd_forward.argtypes = common + [vp]
+        lib.ssd_forward.restype = ctypes.c_int
+        lib.ssd_forward_ex.argtypes = common + [ctypes.POINTER(SsdLaunchOpts), vp]
+        lib.ssd_forward_ex.restype = ctypes.c_int
+        lib.ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims), i64, i64]
+        lib.ssd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_status_str.argtypes = [ctypes.c_int32]
+        lib.ssd_status_str.restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, in_dtype) -> SsdDims:
+    return SsdDims(int(batch), int(seqlen), int(nheads), int(headdim), int(dstate),
+                   int(ngroups), int(in_dtype))
+
+
+# ---- raw C-ABI mirrors (pointers are ints or None) -------------------------
+
+def ssd_forward(dims: Optional[SsdDims], x, da, B, C, D, init_state, chunk_len, R,
+                theta, y, final_state, stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_forward(None if dims is None else ctypes.byref(dims), x, da, B, C, D,
+                               init_state, int(chunk_len), int(R), theta, y, final_state, stream))
+
+
+def ssd_forward_ex(dims: Optional[SsdDims], x, da, B, C, D, init_state, chunk_len, R,
+                   theta, y, final_state, opts: Optional[SsdLaunchOpts], stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_forward_ex(None if dims is None else ctypes.byref(dims), x, da, B, C, D,
+                                  init_state, int(chunk_len), int(R), theta, y, final_state,
+                                  None if opts is None else ctypes.byref(opts), stream))
+
+
+def ssd_workspace_bytes(dims: SsdDims, chunk_len: int, R: int) -> int:
+    return int(load_library().ssd_workspace_bytes(ctypes.byref(dims), int(chunk_len), int(R)))
+
+
+def ssd_status_str(status: int) -> str:
+    return load_library().ssd_status_str(int(status)).decode()
+
+
+# ---- tensor-level convenience ---------------------------------------------
+
+def _dptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=None,
+            y=None, final_state=None, segments: int = 0, stream=None
+            ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Run the scan on device tensors; returns (y, final_state).
+
+    x [b,T,R,H,P] (or [b,T,H,P] for R = 1), da [b,T,H], B/C [b,T,R,G,N]
+    (or [b,T,G,N]); D [H], init_state [b,H,P,N], theta [b,T,H,N/2] fp32.
+    y / final_state may be given (fp32, contiguous) to write in place;
+    final_state may be init_state itself.
+    """
+    import torch
+
+    if x.dim() == 4:
+        x5, B5, C5 = x.unsqueeze(2), B.unsqueeze(2), C.unsqueeze(2)
+    else:
+        x5, B5, C5 = x, B, C
+    b, T, R, H, P = x5.shape
+    G, N = B5.shape[3], B5.shape[4]
+    if x.device.type != "cuda":
+        raise ValueError("chunked_ssd_scan_amd.forward needs device tensors")
+    dev = x.device
+    for name, t in (("x", x), ("da", da), ("B", B), ("C", C), ("D", D),
+                    ("init_state", init_state), ("theta", theta)):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dtype == torch.bfloat16:
+        in_dtype = SSD_BF16
+    elif x.dtype == torch.float32:
+        in_dtype = SSD_F32
+    else:
+        raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
+    if B.dtype != x.dtype or C.dtype != x.dtype:
+        raise TypeError("x, B and C must share one dtype")
+    for name, t in (("da", da), ("D", D), ("init_state", init_state), ("theta", theta)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if y is None:
+        y = torch.empty(x.shape, device=dev, dtype=torch.float32)
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), device=dev, dtype=torch.float32)
+    dims = make_dims(b, T, H, P, N, G, in_dtype)
+    opts = SsdLaunchOpts()
+    opts.segments = int(segments)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = ssd_forward_ex(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), C.data_ptr(),
+                            _dptr(D), _dptr(init_state), chunk_len, R, _dptr(theta),
+                            y.data_ptr(), final_state.data_ptr(), opts, stream)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_forward_ex")
+    return y, final_state

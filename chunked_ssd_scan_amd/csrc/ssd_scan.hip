@@ -1,0 +1,920 @@
+// Chunked SSD scan forward for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// One workgroup owns one (batch, head, sequence segment) and walks the
+// segment's tiles in order. A tile is 32 rank-fused rows (32/R time steps).
+// Per tile it runs the chunk algorithm of burn-mamba "mamba3/ssd/serial.rs"
+// (k1..k5) on that tile:
+//   K1  inclusive prefix sum of da over the tile (wave shuffles)
+//   K2  C B^T on the tile's fused rows (MFMA), turned into the decay matrix
+//       L o CB with L[i,j] = exp(cum_i - cum_j) when step(i) >= step(j)
+//       (masked before exp, burn-mamba "modules/misc/segsum.rs")
+//   K5  y = exp(cum_i) C h_in + (L o CB) x   (+ D x, folded into L's diagonal)
+//   K3+K4  h <- exp(cum_last) h + sum_j exp(cum_last - cum_j) x_j (outer) B_j
+// The running state h (P x N fp32) never leaves the accumulator registers:
+// wave w holds the state columns p in [16w, 16w+16) for every n, so the K4
+// state passing between tiles is a register update, not a memory round trip.
+//
+// With a rotation ("mamba3/scan.py", cumulative_angles / rotate_by), B and C
+// are turned by R(-Phi_t) while they are staged into LDS, Phi being the
+// inclusive cumulative angle from the segment start; the final state is
+// turned back by R(Phi) to the physical frame.
+//
+// Long sequences with few (batch, head) pairs are split into S segments:
+// pass A computes each segment's end state from zero (state-only walk),
+// pass B carries states across segments (h_{s+1} = e^{Lambda_s} R(Phi_s) h_s
+// + local_s), pass C walks every segment from its carried state and writes y.
+//
+// MFMA usage: v_mfma_f32_16x16x32_bf16 for bf16 inputs and
+// v_mfma_f32_16x16x4_f32 for fp32 inputs. Lane layouts (16x16 output tile):
+//   A operand: lane l holds row l%16, reduction slots 8*(l/16) .. +7
+//   B operand: lane l holds col l%16, the same reduction slots
+//   D output : lane l holds col l%16, rows 4*(l/16) .. +3
+// Any bijection between (lane group, slot) and the reduction index is valid
+// as long as A and B use the same one; the kernels pick the bijection that
+// lets accumulator registers be reused directly as operands.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "ssd_scan.h"
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) float f32x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+constexpr int kRows = 32;  // fused rows per tile
+
+// ---------------------------------------------------------------------------
+// element type helpers: TI = uint16_t (bf16 bits) or float
+// ---------------------------------------------------------------------------
+template <typename TI> struct Ops;
+
+template <> struct Ops<uint16_t> {
+    typedef bf16x8 frag;
+    static constexpr int kPad = 8;  // 16 bytes of row padding in LDS
+    __device__ static inline float to_f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+    __device__ static inline uint16_t from_f(float f) {
+        __bf16 b = (__bf16)f;
+        return __builtin_bit_cast(uint16_t, b);
+    }
+    // 8 contiguous elements
+    __device__ static inline frag ld8(const uint16_t* p) {
+        return __builtin_bit_cast(frag, *reinterpret_cast<const uint4*>(p));
+    }
+    // elements p[0..3] and p[16..19]
+    __device__ static inline frag ld4x2(const uint16_t* p) {
+        uint2 a = *reinterpret_cast<const uint2*>(p);
+        uint2 b = *reinterpret_cast<const uint2*>(p + 16);
+        uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+        return __builtin_bit_cast(frag, v);
+    }
+    __device__ static inline void unpack(frag f, float* o) {
+        uint4 v = __builtin_bit_cast(uint4, f);
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = __uint_as_float(w[i] << 16);
+            o[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+    __device__ static inline frag pack(const float* v) {
+        frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (__bf16)v[i];
+        return f;
+    }
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Ops<float> {
+    typedef f32x8 frag;
+    static constexpr int kPad = 4;
+    __device__ static inline float to_f(float v) { return v; }
+    __device__ static inline float from_f(float f) { return f; }
+    __device__ static inline frag ld8(const float* p) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 4);
+        frag f = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return f;
+    }
+    __device__ static inline frag ld4x2(const float* p) {
+        float4 a = *reinterpret_cast<const float4*>(p);
+        float4 b = *reinterpret_cast<const float4*>(p + 16);
+        frag f = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        return f;
+    }
+    __device__ static inline void unpack(frag f, float* o) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = f[i];
+    }
+    __device__ static inline frag pack(const float* v) {
+        frag f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = v[i];
+        return f;
+    }
+    __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], c, 0, 0, 0);
+        return c;
+    }
+};
+
+// State row permutation. State tile t (16 rows) holds, in accumulator row
+// rho = 4*q + v, the state index n = phi(t, rho). With this order the two
+// tiles 2s and 2s+1 of one lane form, slot for slot, the standard reduction
+// layout of n in [32s, 32s+32): slot e of lane group q is n = 32s + 8q + e.
+__device__ __forceinline__ int phi_row(int t, int rho) {
+    return 32 * (t >> 1) + 8 * (rho >> 2) + 4 * (t & 1) + (rho & 3);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs. Give each XCD a
+// contiguous range of work items so that heads sharing B/C tiles (same batch,
+// segment and group) share one L2.
+__device__ __forceinline__ int xcd_item(int wg, int nwg) {
+    const int q = nwg >> 3, r = nwg & 7;
+    const int xcd = wg & 7, j = wg >> 3;
+    return (xcd < r) ? xcd * (q + 1) + j : r * (q + 1) + (xcd - r) * q + j;
+}
+
+struct WalkArgs {
+    const void* x;
+    const float* da;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* init;     // segment-0 initial state [b,H,P,N] or null
+    const float* theta;    // [b,T,H,N/2] or null
+    float* y;
+    float* final_state;
+    float* ws_state;       // [b*H][S][P][N] segment states / carries
+    float* ws_misc;        // [b*H][S][1 + N/2]: Lambda, Phi per pair
+    int64_t T, H, G, N, R;
+    int S;                 // segments
+    int seg_items;         // segments this launch covers (S or S-1)
+    int nsub;              // tiles per sequence
+    int log2R;
+    int Qt;                // time steps per tile (32 / R)
+};
+
+// ---------------------------------------------------------------------------
+// The tile walk. MODE 0: output pass (y, final state). MODE 1: state-only
+// pass (segment end states for the carry).
+// ---------------------------------------------------------------------------
+template <typename TI, int P, int NP, bool ROT, int MODE>
+__global__ __launch_bounds__(4 * P) void ssd_walk_kernel(WalkArgs a) {
+    using O = Ops<TI>;
+    typedef typename O::frag frag;
+    constexpr int W = P / 16;          // waves
+    constexpr int NT = 64 * W;         // threads
+    constexpr int F = kRows;
+    constexpr int PAD = O::kPad;
+    constexpr int LDR = NP + PAD;      // row-major tile row stride (elements)
+    constexpr int LDT = F + PAD;       // transposed tile row stride
+    constexpr int NTILE = NP / 16;     // state tiles per wave
+    constexpr int KS = NP / 32;        // reduction steps over n
+    constexpr bool OUT = (MODE == 0);
+
+    __shared__ __attribute__((aligned(16))) TI sC[OUT ? F * LDR : 1];
+    __shared__ __attribute__((aligned(16))) TI sB[OUT ? F * LDR : 1];
+    __shared__ __attribute__((aligned(16))) TI sBt[NP * LDT];
+    __shared__ __attribute__((aligned(16))) TI sXt[P * LDT];
+    __shared__ float sCum[F], sEin[F], sW[F], sCarry[1];
+    __shared__ float sPhi[ROT ? NP / 2 : 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int q = lane >> 4, l16 = lane & 15;
+    const int p0 = wv * 16;
+
+    const int64_t T = a.T, H = a.H, N = a.N, R = a.R;
+    const int S = a.S;
+    const int nwg = gridDim.x;
+    const int item = xcd_item(blockIdx.x, nwg);
+    const int h = (int)(item % H);
+    const int bs = (int)(item / H);
+    const int seg = bs % a.seg_items;
+    const int b = bs / a.seg_items;
+    const int64_t grp = h / (H / a.G);
+    const int64_t bh = (int64_t)b * H + h;
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S);
+    const int k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    const int64_t TR = T * R;
+    const int log2R = a.log2R;
+    const int Qt = a.Qt;
+
+    const TI* xg = static_cast<const TI*>(a.x);
+    const TI* Bg = static_cast<const TI*>(a.B);
+    const TI* Cg = static_cast<const TI*>(a.C);
+
+    // ---- initial state (physical; the segment's rotation frame starts at 0)
+    f32x4 hs[NTILE];
+    {
+        // S == 1: the caller's initial state. S > 1: the carry pass has stored
+        // the state entering every segment (segment 0 included) in ws slot seg,
+        // so init_state is never read here and may alias final_state.
+        const float* src = nullptr;
+        if (OUT) {
+            if (S == 1)
+                src = a.init ? a.init + bh * P * N : nullptr;
+            else
+                src = a.ws_state + (bh * S + seg) * P * N;
+        }
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = phi_row(t, 4 * q + v);
+                hs[t][v] = (src && n < N) ? src[(int64_t)(p0 + l16) * N + n] : 0.f;
+            }
+        }
+    }
+
+    const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
+    float lam = 0.f;  // sum of da over the segment (wave 0, lane 0)
+
+    // ---- staging registers (non-rotated B/C and x are prefetched one tile ahead)
+    constexpr int XU = (sizeof(TI) == 2) ? 16 * (P / 4) : F * (P / 4);         // x units
+    constexpr int XPT = (XU + NT - 1) / NT;
+    constexpr int BU = (sizeof(TI) == 2) ? 16 * (NP / 4) : F * (NP / 4);       // B units
+    constexpr int BPT = (BU + NT - 1) / NT;
+    constexpr int CU = F * NP * (int)sizeof(TI) / 16;                           // C 16B units
+    constexpr int CPT = (CU + NT - 1) / NT;
+    uint4 rx[XPT];
+    uint4 rb[ROT ? 1 : BPT];
+    uint4 rc[(ROT || !OUT) ? 1 : CPT];
+    float rda = 0.f;
+
+    // rotation bookkeeping: slot = (pair block of 16, time group of Qt/4)
+    constexpr int RSLOTS = (NP / 2) * 4;
+    constexpr int RPT = ROT ? (RSLOTS + NT - 1) / NT : 1;
+    float phib[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) phib[m] = 0.f;
+
+    auto row_x = [&](int64_t fr) -> const TI* { return xg + ((b * TR + fr) * H + h) * P; };
+    auto row_bc = [&](const TI* base, int64_t fr) -> const TI* { return base + ((b * TR + fr) * a.G + grp) * N; };
+
+    auto stage_load = [&](int k) {
+        const int64_t fbase = (int64_t)k * F;
+#pragma unroll
+        for (int m = 0; m < XPT; ++m) {
+            const int u = tid + m * NT;
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (u < XU) {
+                if (sizeof(TI) == 2) {
+                    const int ra = u / (P / 4), c = u % (P / 4);
+                    const int64_t f0 = fbase + 2 * ra;
+                    if (f0 < TR) {
+                        uint2 lo = *reinterpret_cast<const uint2*>(row_x(f0) + 4 * c);
+                        v.x = lo.x; v.y = lo.y;
+                    }
+                    if (f0 + 1 < TR) {
+                        uint2 hi = *reinterpret_cast<const uint2*>(row_x(f0 + 1) + 4 * c);
+                        v.z = hi.x; v.w = hi.y;
+                    }
+                } else {
+                    const int f = u / (P / 4), c = u % (P / 4);
+                    if (fbase + f < TR) v = *reinterpret_cast<const uint4*>(row_x(fbase + f) + 4 * c);
+                }
+            }
+            rx[m] = v;
+        }
+        if (!ROT) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m) {
+                const int u = tid + m * NT;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (u < BU) {
+                    if (sizeof(TI) == 2) {
+                        const int ra = u / (NP / 4), c = u % (NP / 4);
+                        const int64_t f0 = fbase + 2 * ra;
+                        if (4 * c < N) {
+                            if (f0 < TR) {
+                                uint2 lo = *reinterpret_cast<const uint2*>(row_bc(Bg, f0) + 4 * c);
+                                v.x = lo.x; v.y = lo.y;
+                            }
+                            if (f0 + 1 < TR) {
+                                uint2 hi = *reinterpret_cast<const uint2*>(row_bc(Bg, f0 + 1) + 4 * c);
+                                v.z = hi.x; v.w = hi.y;
+                            }
+                        }
+                    } else {
+                        const int f = u / (NP / 4), c = u % (NP / 4);
+                        if (4 * c < N && fbase + f < TR)
+                            v = *reinterpret_cast<const uint4*>(row_bc(Bg, fbase + f) + 4 * c);
+                    }
+                }
+                rb[m] = v;
+            }
+            if (OUT) {
+                constexpr int EPU = 16 / (int)sizeof(TI);   // elements per 16B unit
+#pragma unroll
+                for (int m = 0; m < CPT; ++m) {
+                    const int u = tid + m * NT;
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (u < CU) {
+                        const int f = u / (NP / EPU), c = u % (NP / EPU);
+                        if (EPU * c < N && fbase + f < TR)
+                            v = *reinterpret_cast<const uint4*>(row_bc(Cg, fbase + f) + EPU * c);
+                    }
+                    rc[m] = v;
+                }
+            }
+        }
+        if (wv == 0) {
+            const int64_t t = (int64_t)k * Qt + lane;
+            rda = (lane < Qt && t < T) ? a.da[(b * T + t) * H + h] : 0.f;
+        }
+    };
+
+    auto stage_store = [&](int k) {
+        // x -> sXt (transposed: p rows, fused-row columns)
+#pragma unroll
+        for (int m = 0; m < XPT; ++m) {
+            const int u = tid + m * NT;
+            if (u < XU) {
+                const uint4 v = rx[m];
+                if (sizeof(TI) == 2) {
+                    const int ra = u / (P / 4), c = u % (P / 4);
+                    uint32_t* d0 = reinterpret_cast<uint32_t*>(sXt + (4 * c) * LDT + 2 * ra);
+                    const uint32_t lo[2] = {v.x, v.y}, hi[2] = {v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t wl = lo[e >> 1], wh = hi[e >> 1];
+                        const uint32_t pr = (e & 1) ? ((wl >> 16) | (wh & 0xffff0000u))
+                                                    : ((wl & 0xffffu) | (wh << 16));
+                        *reinterpret_cast<uint32_t*>(reinterpret_cast<TI*>(d0) + e * LDT) = pr;
+                    }
+                } else {
+                    const int f = u / (P / 4), c = u % (P / 4);
+                    const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        *reinterpret_cast<uint32_t*>(sXt + (4 * c + e) * LDT + f) = w4[e];
+                }
+            }
+        }
+        if (!ROT) {
+#pragma unroll
+            for (int m = 0; m < BPT; ++m) {
+                const int u = tid + m * NT;
+                if (u < BU) {
+                    const uint4 v = rb[m];
+                    if (sizeof(TI) == 2) {
+                        const int ra = u / (NP / 4), c = u % (NP / 4);
+                        if (OUT) {
+                            *reinterpret_cast<uint2*>(sB + (2 * ra) * LDR + 4 * c) = make_uint2(v.x, v.y);
+                            *reinterpret_cast<uint2*>(sB + (2 * ra + 1) * LDR + 4 * c) = make_uint2(v.z, v.w);
+                        }
+                        const uint32_t lo[2] = {v.x, v.y}, hi[2] = {v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t wl = lo[e >> 1], wh = hi[e >> 1];
+                            const uint32_t pr = (e & 1) ? ((wl >> 16) | (wh & 0xffff0000u))
+                                                        : ((wl & 0xffffu) | (wh << 16));
+                            *reinterpret_cast<uint32_t*>(sBt + (4 * c + e) * LDT + 2 * ra) = pr;
+                        }
+                    } else {
+                        const int f = u / (NP / 4), c = u % (NP / 4);
+                        if (OUT) *reinterpret_cast<uint4*>(sB + f * LDR + 4 * c) = v;
+                        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            *reinterpret_cast<uint32_t*>(sBt + (4 * c + e) * LDT + f) = w4[e];
+                    }
+                }
+            }
+            if (OUT) {
+                constexpr int EPU = 16 / (int)sizeof(TI);
+#pragma unroll
+                for (int m = 0; m < CPT; ++m) {
+                    const int u = tid + m * NT;
+                    if (u < CU) {
+                        const int f = u / (NP / EPU), c = u % (NP / EPU);
+                        *reinterpret_cast<uint4*>(sC + f * LDR + EPU * c) = rc[m];
+                    }
+                }
+            }
+        } else {
+            // Rotated B (and C): per (pair k, time group) slot, a prefix sum of
+            // theta over the group's steps, a cross-group scan by shuffles, then
+            // B~ = R(-Phi) B, C~ = R(-Phi) C for every rank of those steps.
+            const int64_t fbase = (int64_t)k * F;
+            const int TPG = (Qt + 3) / 4;
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) {
+                const int slot = tid + m * NT;
+                const int kk = (slot >> 6) * 16 + (slot & 15);
+                const int tg = (slot & 63) >> 4;
+                const bool kvalid = (slot < RSLOTS) && (2 * kk < N);
+                float part[8];
+                float run = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int tl = tg * TPG + j;
+                    const int64_t t = (int64_t)k * Qt + tl;
+                    float th = 0.f;
+                    if (j < TPG && tl < Qt && t < T && kvalid)
+                        th = a.theta[((b * T + t) * H + h) * (N / 2) + kk];
+                    run += th;
+                    part[j] = run;
+                }
+                // inclusive scan of group totals across the 4 groups of this block
+                float tot = run;
+                float u1 = __shfl_up(tot, 16);
+                if (tg >= 1) tot += u1;
+                float u2 = __shfl_up(tot, 32);
+                if (tg >= 2) tot += u2;
+                const float excl = tot - run;
+                const float all = __shfl(tot, (lane & 15) + 48);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int tl = tg * TPG + j;
+                    if (j < TPG && tl < Qt && slot < RSLOTS && kk < NP / 2) {
+                        float sn = 0.f, cs = 1.f;
+                        if (kvalid) sincosf(phib[m] + excl + part[j], &sn, &cs);
+                        for (int r = 0; r < (int)R; ++r) {
+                            const int f = tl * (int)R + r;
+                            const int64_t fr = fbase + f;
+                            float b0 = 0.f, b1 = 0.f, c0 = 0.f, c1 = 0.f;
+                            if (kvalid && fr < TR) {
+                                const TI* pb = row_bc(Bg, fr) + 2 * kk;
+                                b0 = O::to_f(pb[0]); b1 = O::to_f(pb[1]);
+                                if (OUT) {
+                                    const TI* pc = row_bc(Cg, fr) + 2 * kk;
+                                    c0 = O::to_f(pc[0]); c1 = O::to_f(pc[1]);
+                                }
+                            }
+                            // R(-phi): (a, b) -> (cos a + sin b, -sin a + cos b)
+                            const TI rb0 = O::from_f(cs * b0 + sn * b1);
+                            const TI rb1 = O::from_f(cs * b1 - sn * b0);
+                            sBt[(2 * kk) * LDT + f] = rb0;
+                            sBt[(2 * kk + 1) * LDT + f] = rb1;
+                            if (OUT) {
+                                sB[f * LDR + 2 * kk] = rb0;
+                                sB[f * LDR + 2 * kk + 1] = rb1;
+                                sC[f * LDR + 2 * kk] = O::from_f(cs * c0 + sn * c1);
+                                sC[f * LDR + 2 * kk + 1] = O::from_f(cs * c1 - sn * c0);
+                            }
+                        }
+                    }
+                }
+                phib[m] += all;
+            }
+        }
+        // K1: inclusive prefix of da over the tile's time steps (wave 0)
+        if (wv == 0) {
+            float v = rda;
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) {
+                const float u = __shfl_up(v, o);
+                if (lane >= o) v += u;
+            }
+            const float last = __shfl(v, Qt - 1);
+            const float cf = __shfl(v, (lane & 31) >> log2R);
+            if (lane < F) {
+                sCum[lane] = cf;
+                sEin[lane] = __expf(cf);
+                sW[lane] = __expf(last - cf);
+            }
+            if (lane == 0) {
+                sCarry[0] = __expf(last);
+                lam += last;
+            }
+        }
+    };
+
+    // ---- the walk
+    stage_load(k0);
+    stage_store(k0);
+    __syncthreads();
+    for (int k = k0; k < k1; ++k) {
+        if (k + 1 < k1) stage_load(k + 1);
+
+        if (OUT) {
+            // K5 off-diagonal term and K2 tiles, one reduction step over n at a time
+            f32x4 yacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            f32x4 cb00 = {0.f, 0.f, 0.f, 0.f}, cb01 = cb00, cb11 = cb00;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                float hv[8];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    hv[v] = hs[2 * s][v];
+                    hv[4 + v] = hs[2 * s + 1][v];
+                }
+                const frag hA = O::pack(hv);
+                const frag c0 = O::ld8(sC + (l16) * LDR + 32 * s + 8 * q);
+                const frag c1 = O::ld8(sC + (16 + l16) * LDR + 32 * s + 8 * q);
+                const frag b0 = O::ld8(sB + (l16) * LDR + 32 * s + 8 * q);
+                const frag b1 = O::ld8(sB + (16 + l16) * LDR + 32 * s + 8 * q);
+                yacc[0] = O::mma(hA, c0, yacc[0]);
+                yacc[1] = O::mma(hA, c1, yacc[1]);
+                cb00 = O::mma(b0, c0, cb00);
+                cb01 = O::mma(b0, c1, cb01);
+                cb11 = O::mma(b1, c1, cb11);
+            }
+            // exp(cum_i) on the off-diagonal term (column i of y^T)
+            {
+                const float e0 = sEin[l16], e1 = sEin[16 + l16];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    yacc[0][v] *= e0;
+                    yacc[1][v] *= e1;
+                }
+            }
+            // decay matrix L o CB^T: element (j = 16J + 4q + v, i = 16I + l16)
+            float m00[4], m01[4], m11[4];
+            {
+                const float ci0 = sCum[l16], ci1 = sCum[16 + l16];
+                const int ti0 = l16 >> log2R, ti1 = (16 + l16) >> log2R;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j0 = 4 * q + v, j1 = 16 + 4 * q + v;
+                    const float cj0 = sCum[j0], cj1 = sCum[j1];
+                    const int tj0 = j0 >> log2R, tj1 = j1 >> log2R;
+                    m00[v] = (ti0 >= tj0) ? cb00[v] * __expf(ci0 - cj0) : 0.f;
+                    m01[v] = (ti1 >= tj0) ? cb01[v] * __expf(ci1 - cj0) : 0.f;
+                    m11[v] = (ti1 >= tj1) ? cb11[v] * __expf(ci1 - cj1) : 0.f;
+                    if (j0 == l16) m00[v] += Dh;
+                    if (j1 == 16 + l16) m11[v] += Dh;
+                }
+            }
+            // K5 diagonal block: y^T[p, i] += sum_j x^T[p, j] (L o CB^T)[j, i]
+            {
+                const frag xa = O::ld4x2(sXt + (p0 + l16) * LDT + 4 * q);
+                float mv0[8], mv1[8];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    mv0[v] = m00[v];
+                    mv0[4 + v] = 0.f;        // rows j >= 16 never reach i < 16
+                    mv1[v] = m01[v];
+                    mv1[4 + v] = m11[v];
+                }
+                yacc[0] = O::mma(xa, O::pack(mv0), yacc[0]);
+                yacc[1] = O::mma(xa, O::pack(mv1), yacc[1]);
+            }
+            // store y: lane holds y[row i][p0 + 4q .. +3]
+            const int64_t fbase = (int64_t)k * F;
+#pragma unroll
+            for (int I = 0; I < 2; ++I) {
+                const int64_t fr = fbase + 16 * I + l16;
+                if (fr < TR) {
+                    float* dst = a.y + ((b * TR + fr) * H + h) * P + p0 + 4 * q;
+                    *reinterpret_cast<f32x4*>(dst) = yacc[I];
+                }
+            }
+        }
+
+        // K3 + K4: h <- exp(cum_last) h + sum_j w_j x_j (outer) B_j
+        {
+            const float carry = sCarry[0];
+            float xv[8], wv8[8];
+            O::unpack(O::ld8(sXt + (p0 + l16) * LDT + 8 * q), xv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wv8[e] = sW[8 * q + e];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[e] *= wv8[e];
+            const frag xw = O::pack(xv);
+#pragma unroll
+            for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) hs[t][v] *= carry;
+                const frag bt = O::ld8(sBt + phi_row(t, l16) * LDT + 8 * q);
+                hs[t] = O::mma(bt, xw, hs[t]);
+            }
+        }
+
+        __syncthreads();
+        if (k + 1 < k1) {
+            stage_store(k + 1);
+            __syncthreads();
+        }
+    }
+
+    // ---- epilogue: rotate the state back to the physical frame
+    if (ROT) {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int slot = tid + m * NT;
+            const int kk = (slot >> 6) * 16 + (slot & 15);
+            const int tg = (slot & 63) >> 4;
+            if (slot < RSLOTS && tg == 0 && kk < NP / 2) sPhi[kk] = phib[m];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+                const int n = phi_row(t, 4 * q + v);   // even: pair (n, n+1)
+                float sn, cs;
+                sincosf(sPhi[n >> 1], &sn, &cs);
+                const float g0 = hs[t][v], g1 = hs[t][v + 1];
+                hs[t][v] = cs * g0 - sn * g1;
+                hs[t][v + 1] = sn * g0 + cs * g1;
+            }
+        }
+    }
+    float* dstate = nullptr;
+    if (OUT) {
+        if (seg == S - 1) dstate = a.final_state + bh * P * N;
+    } else {
+        dstate = a.ws_state + (bh * S + seg + 1) * P * N;
+        float* misc = a.ws_misc + (bh * S + seg) * (1 + N / 2);
+        if (tid == 0) misc[0] = lam;
+        if (ROT) {
+            for (int kk = tid; kk < N / 2; kk += NT) misc[1 + kk] = sPhi[kk];
+        }
+    }
+    if (dstate) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = phi_row(t, 4 * q + v);
+                if (n < N) dstate[(int64_t)(p0 + l16) * N + n] = hs[t][v];
+            }
+        }
+    }
+}
+
+// Pass B: carry states across segments, one thread per state pair (p, k).
+//   c_0 = init (or 0);  c_{s+1} = exp(Lambda_s) R(Phi_s) c_s + local_s
+// On entry ws_state slot s+1 holds local_s (segment s from a zero state); on
+// exit slot s holds c_s, the state entering segment s (slot 0: a copy of init).
+__global__ __launch_bounds__(256) void ssd_carry_kernel(const float* __restrict__ init,
+                                                       float* __restrict__ ws_state,
+                                                       const float* __restrict__ ws_misc,
+                                                       int64_t P, int64_t N, int S, int rot) {
+    const int64_t bh = blockIdx.y;
+    const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (pair >= P * (N / 2)) return;
+    const int64_t p = pair / (N / 2), kk = pair % (N / 2);
+    const int64_t off = p * N + 2 * kk;
+    float c0 = 0.f, c1 = 0.f;
+    if (init) {
+        c0 = init[bh * P * N + off];
+        c1 = init[bh * P * N + off + 1];
+    }
+    float* st0 = ws_state + bh * S * P * N + off;
+    st0[0] = c0;
+    st0[1] = c1;
+    for (int s = 0; s + 1 < S; ++s) {
+        const float* misc = ws_misc + (bh * S + s) * (1 + N / 2);
+        float* st = ws_state + (bh * S + s + 1) * P * N + off;
+        const float dec = __expf(misc[0]);
+        if (rot) {
+            float sn, cs;
+            sincosf(misc[1 + kk], &sn, &cs);
+            const float r0 = cs * c0 - sn * c1, r1 = sn * c0 + cs * c1;
+            c0 = r0;
+            c1 = r1;
+        }
+        c0 = dec * c0 + st[0];
+        c1 = dec * c1 + st[1];
+        st[0] = c0;
+        st[1] = c1;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+typedef void (*walk_fn)(WalkArgs);
+
+template <typename TI, int P, int NP, bool ROT, int MODE>
+void* walk_ptr() {
+    return reinterpret_cast<void*>(&ssd_walk_kernel<TI, P, NP, ROT, MODE>);
+}
+
+template <typename TI, int P, bool ROT, int MODE>
+void* walk_ptr_np(int NP) {
+    switch (NP) {
+        case 32: return walk_ptr<TI, P, 32, ROT, MODE>();
+        case 64: return walk_ptr<TI, P, 64, ROT, MODE>();
+        case 128: return walk_ptr<TI, P, 128, ROT, MODE>();
+        case 256: return walk_ptr<TI, P, 256, ROT, MODE>();
+    }
+    return nullptr;
+}
+
+template <typename TI, bool ROT, int MODE>
+void* walk_ptr_p(int P, int NP) {
+    switch (P) {
+        case 16: return walk_ptr_np<TI, 16, ROT, MODE>(NP);
+        case 32: return walk_ptr_np<TI, 32, ROT, MODE>(NP);
+        case 64: return walk_ptr_np<TI, 64, ROT, MODE>(NP);
+        case 128: return walk_ptr_np<TI, 128, ROT, MODE>(NP);
+    }
+    return nullptr;
+}
+
+void* select_walk(int dtype, bool rot, int mode, int P, int NP) {
+    if (dtype == SSD_BF16) {
+        if (rot) return mode ? walk_ptr_p<uint16_t, true, 1>(P, NP) : walk_ptr_p<uint16_t, true, 0>(P, NP);
+        return mode ? walk_ptr_p<uint16_t, false, 1>(P, NP) : walk_ptr_p<uint16_t, false, 0>(P, NP);
+    }
+    if (rot) return mode ? walk_ptr_p<float, true, 1>(P, NP) : walk_ptr_p<float, true, 0>(P, NP);
+    return mode ? walk_ptr_p<float, false, 1>(P, NP) : walk_ptr_p<float, false, 0>(P, NP);
+}
+
+struct Plan {
+    int64_t b, T, H, P, N, G, R, NP;
+    int dtype, S, nsub, Qt, log2R;
+};
+
+bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
+    if (v < lo || v > hi) return false;
+    return (v & (v - 1)) == 0;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+Span span_of(const void* p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + (uintptr_t)bytes};
+}
+
+ssd_status check_shape(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has_theta) {
+    if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+        d->ngroups < 1)
+        return SSD_ERR_BAD_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (chunk_len < 1 || R < 1) return SSD_ERR_BAD_SHAPE;
+    if (has_theta && (d->dstate % 2)) return SSD_ERR_BAD_SHAPE;
+    if (d->in_dtype != SSD_F32 && d->in_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (!is_pow2_in(d->headdim, 16, 128)) return SSD_ERR_UNSUPPORTED;
+    if (!is_pow2_in(d->dstate, 16, 256)) return SSD_ERR_UNSUPPORTED;
+    if (!is_pow2_in(R, 1, 16)) return SSD_ERR_UNSUPPORTED;
+    // sizes must stay addressable with 64-bit offsets and 32-bit tile counts
+    const int64_t TR = d->seqlen * R;
+    if (TR > ((int64_t)1 << 40) || d->batch * d->nheads > ((int64_t)1 << 30)) return SSD_ERR_UNSUPPORTED;
+    if ((TR + kRows - 1) / kRows > ((int64_t)1 << 30)) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+int auto_segments(int64_t bh, int nsub) {
+    // fill the chip: aim at >= 512 workgroups, but keep >= 4 tiles per segment
+    int64_t want = (512 + bh - 1) / bh;
+    int64_t cap = nsub / 4;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want > 256) want = 256;
+    return (int)(want < 1 ? 1 : want);
+}
+
+size_t workspace_for(const Plan& pl) {
+    if (pl.S <= 1) return 0;
+    const size_t bh = (size_t)(pl.b * pl.H);
+    const size_t st = bh * pl.S * pl.P * pl.N * sizeof(float);
+    const size_t misc = bh * pl.S * (1 + pl.N / 2) * sizeof(float);
+    return ((st + 255) & ~(size_t)255) + misc;
+}
+
+Plan make_plan(const ssd_dims* d, int64_t R, int segments) {
+    Plan pl;
+    pl.b = d->batch; pl.T = d->seqlen; pl.H = d->nheads; pl.P = d->headdim;
+    pl.N = d->dstate; pl.G = d->ngroups; pl.R = R;
+    pl.NP = pl.N < 32 ? 32 : pl.N;
+    pl.dtype = d->in_dtype;
+    pl.Qt = (int)(kRows / R);
+    pl.log2R = 0;
+    while ((1 << pl.log2R) < R) ++pl.log2R;
+    pl.nsub = (int)((pl.T * R + kRows - 1) / kRows);
+    pl.S = segments > 0 ? segments : auto_segments(pl.b * pl.H, pl.nsub);
+    if (pl.S > pl.nsub) pl.S = pl.nsub;
+    if (pl.S < 1) pl.S = 1;
+    return pl;
+}
+
+ssd_status launch_walk(const Plan& pl, int mode, bool rot, const WalkArgs& args, hipStream_t st) {
+    void* fn = select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
+    if (!fn) return SSD_ERR_UNSUPPORTED;
+    const int64_t nwg = pl.b * pl.H * args.seg_items;
+    if (nwg < 1 || nwg > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    dim3 grid((unsigned)nwg), block((unsigned)(4 * pl.P));
+    WalkArgs a = args;
+    void* kargs[] = {&a};
+    if (hipLaunchKernel(fn, grid, block, kargs, 0, st) != hipSuccess) return SSD_ERR_HIP;
+    return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_status_str(int32_t status) {
+    switch (status) {
+        case SSD_OK: return "SSD_OK";
+        case SSD_ERR_NULL_ARG: return "SSD_ERR_NULL_ARG";
+        case SSD_ERR_BAD_SHAPE: return "SSD_ERR_BAD_SHAPE";
+        case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+        case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS";
+        case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    }
+    return "unknown status";
+}
+
+size_t ssd_workspace_bytes(const ssd_dims* d, int64_t chunk_len, int64_t R) {
+    if (!d || check_shape(d, chunk_len, R, false) != SSD_OK) return 0;
+    return workspace_for(make_plan(d, R, 0));
+}
+
+ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, const void* B,
+                          const void* C, const float* D, const float* init_state,
+                          int64_t chunk_len, int64_t R, const float* theta, float* y,
+                          float* final_state, const ssd_launch_opts* opts, void* stream) {
+    if (!d || !x || !da || !B || !C || !y || !final_state) return SSD_ERR_NULL_ARG;
+    ssd_status st = check_shape(d, chunk_len, R, theta != nullptr);
+    if (st != SSD_OK) return st;
+    if (opts) {
+        if (opts->segments < 0) return SSD_ERR_BAD_SHAPE;
+        for (int i = 0; i < 7; ++i)
+            if (opts->reserved[i] != 0) return SSD_ERR_BAD_SHAPE;
+    }
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(final_state, 16) || (init_state && !aligned(init_state, 16)) || !aligned(da, 4) ||
+        (D && !aligned(D, 4)) || (theta && !aligned(theta, 4)))
+        return SSD_ERR_UNSUPPORTED;
+
+    const int64_t b = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate,
+                  G = d->ngroups;
+    const int64_t esz = d->in_dtype == SSD_BF16 ? 2 : 4;
+    const Span sy = span_of(y, b * T * R * H * P * 4);
+    const Span sf = span_of(final_state, b * H * P * N * 4);
+    const Span ins[] = {span_of(x, b * T * R * H * P * esz), span_of(da, b * T * H * 4),
+                        span_of(B, b * T * R * G * N * esz), span_of(C, b * T * R * G * N * esz),
+                        D ? span_of(D, H * 4) : Span{0, 0},
+                        init_state ? span_of(init_state, b * H * P * N * 4) : Span{0, 0},
+                        theta ? span_of(theta, b * T * H * (N / 2) * 4) : Span{0, 0}};
+    if (overlap(sy, sf)) return SSD_ERR_ALIAS;
+    for (int i = 0; i < 7; ++i) {
+        if (ins[i].hi == 0) continue;
+        if (overlap(sy, ins[i])) return SSD_ERR_ALIAS;
+        const bool same_state = (i == 5) && (const void*)final_state == (const void*)init_state;
+        if (!same_state && overlap(sf, ins[i])) return SSD_ERR_ALIAS;
+    }
+
+    const Plan pl = make_plan(d, R, opts ? opts->segments : 0);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    const bool rot = theta != nullptr;
+
+    WalkArgs args;
+    memset(&args, 0, sizeof(args));
+    args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
+    args.init = init_state; args.theta = theta; args.y = y; args.final_state = final_state;
+    args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
+    args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
+
+    void* ws = nullptr;
+    const size_t wsb = workspace_for(pl);
+    if (wsb) {
+        if (hipMallocAsync(&ws, wsb, hs) != hipSuccess) return SSD_ERR_HIP;
+        const size_t st_bytes = (size_t)(b * H) * pl.S * P * N * sizeof(float);
+        args.ws_state = static_cast<float*>(ws);
+        args.ws_misc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((st_bytes + 255) & ~(size_t)255));
+    }
+
+    ssd_status rs = SSD_OK;
+    if (pl.S > 1) {
+        // pass A: segment end states (segments 0 .. S-2)
+        args.seg_items = pl.S - 1;
+        rs = launch_walk(pl, 1, rot, args, hs);
+        // pass B: carries across segments
+        if (rs == SSD_OK) {
+            dim3 grid((unsigned)((P * (N / 2) + 255) / 256), (unsigned)(b * H));
+            hipLaunchKernelGGL(ssd_carry_kernel, grid, dim3(256), 0, hs, init_state, args.ws_state,
+                               args.ws_misc, P, N, pl.S, rot ? 1 : 0);
+            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+        }
+    }
+    if (rs == SSD_OK) {
+        args.seg_items = pl.S;
+        rs = launch_walk(pl, 0, rot, args, hs);
+    }
+    if (ws) {
+        if (hipFreeAsync(ws, hs) != hipSuccess && rs == SSD_OK) rs = SSD_ERR_HIP;
+    }
+    return rs;
+}
+
+ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* da, const void* B,
+                       const void* C, const float* D, const float* init_state, int64_t chunk_len,
+                       int64_t R, const float* theta, float* y, float* final_state, void* stream) {
+    return ssd_forward_ex(d, x, da, B, C, D, init_state, chunk_len, R, theta, y, final_state,
+                          nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+/*
+ * ssd_scan.h - C ABI of the chunked state-space-duality (SSD) scan forward
+ * pass on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h; g = h / (H/G) is the B/C group):
+ *
+ *   h_{-1}  = init_state[b,h]            (P x N, or zero when init_state is NULL)
+ *   h_t     = exp(da[b,t,h]) * R(theta[b,t,h]) h_{t-1}
+ *             + sum_{r<R} x[b,t,r,h,:] (outer) B[b,t,r,g,:]
+ *   y[b,t,r,h,p] = sum_n C[b,t,r,g,n] * h_t[p,n] + D[h] * x[b,t,r,h,p]
+ *   final_state[b,h] = h_{T-1}
+ *
+ * R(theta) turns every state pair (2k, 2k+1) by the plane rotation
+ * [[cos, -sin], [sin, cos]] of angle theta[b,t,h,k] (identity when theta is
+ * NULL). Sources, by page and section:
+ *  - burn-mamba "mamba3/ssd/serial.rs", ssd_serial with stages k1 (chunk
+ *    cumsum of da), k2 (C B^T on the rank-fused rows), k3 (chunk states),
+ *    k4 (serial state passing) and k5 (chunk scan Y_diag + Y_off): the
+ *    multi-rank (MIMO) chunked form, inputs pre-scaled (dt enters only via da),
+ *    the K5 mask keeping the whole R x R diagonal block, no skip inside.
+ *  - LeetGPU "SSM Selective Scan" write-up, problem statement: the skip term
+ *    D * x and the starting state of zero.
+ *  - "mamba3/scan.py", module docstring and cumulative_angles / rotate_by:
+ *    the data-dependent rotation, folded into B and C by inclusive cumulative
+ *    angles Phi_t (B~ = R(-Phi_t) B, C~ = R(-Phi_t) C); the returned
+ *    final_state is the physical state h_{T-1} = R(Phi_{T-1}) g_{T-1}.
+ *  - burn-mamba "modules/misc/segsum.rs": decays are exponentials of
+ *    differences of prefix sums, masked before exp.
+ *
+ * Layouts: dense, row-major, device memory.
+ *   x           [b, T, R, H, P]   in_dtype (fp32 or bf16)
+ *   da          [b, T, H]         fp32, finite and <= 0 (log of the decay)
+ *   B, C        [b, T, R, G, N]   in_dtype
+ *   D           [H]               fp32, may be NULL (no skip term)
+ *   init_state  [b, H, P, N]      fp32, may be NULL (zero initial state)
+ *   theta       [b, T, H, N/2]    fp32, may be NULL (no rotation)
+ *   y           [b, T, R, H, P]   fp32, written in full
+ *   final_state [b, H, P, N]      fp32, written in full
+ * x, B, C, init_state, y and final_state must be 16-byte aligned; da, D and
+ * theta 4-byte aligned.
+ *
+ * Ownership: the caller owns every buffer and keeps inputs alive until the
+ * work enqueued on `stream` has completed. Nothing is retained after return.
+ * Scratch (only when the sequence is split into segments, see
+ * ssd_workspace_bytes) is allocated and released stream-ordered on `stream`.
+ * final_state may be the same pointer as init_state (in-place state update);
+ * any other overlap between an output and another buffer is SSD_ERR_ALIAS.
+ *
+ * Errors: every argument is checked on the host before anything is enqueued;
+ * on any error status nothing is enqueued and no output is touched.
+ * The call is asynchronous: it returns after enqueueing on `stream` (a
+ * hipStream_t; NULL means the null stream) without synchronising.
+ * Different streams may call concurrently; calls share no mutable state.
+ *
+ * Supported envelope (SSD_ERR_UNSUPPORTED outside it):
+ *   P in {16, 32, 64, 128}; N in {16, 32, 64, 128, 256};
+ *   R in {1, 2, 4, 8, 16}; in_dtype fp32 or bf16.
+ */
+#ifndef SSD_SCAN_H
+#define SSD_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch;    /* b >= 1 */
+    int64_t seqlen;   /* T >= 1 time steps */
+    int64_t nheads;   /* H >= 1 */
+    int64_t headdim;  /* P */
+    int64_t dstate;   /* N */
+    int64_t ngroups;  /* G >= 1, H % G == 0 */
+    int32_t in_dtype; /* ssd_dtype of x, B and C */
+} ssd_dims;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_ARG = 1,    /* a required pointer (x, da, B, C, y, final_state, dims) is NULL */
+    SSD_ERR_BAD_SHAPE = 2,   /* T < 1, b/H/P/N/G < 1, H % G != 0, chunk_len < 1, R < 1, odd N with theta */
+    SSD_ERR_UNSUPPORTED = 3, /* valid but outside the kernels' envelope, or a misaligned pointer */
+    SSD_ERR_ALIAS = 4,       /* an output overlaps another buffer (final_state == init_state is allowed) */
+    SSD_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+} ssd_status;
+
+/* Launch choices that do not change the result beyond rounding. */
+typedef struct {
+    int32_t segments;    /* 0: automatic. k >= 1: split every sequence into k
+                            segments that run in parallel, joined by a state
+                            carry pass (clamped to the number of 32-row tiles) */
+    int32_t reserved[7]; /* must be zero */
+} ssd_launch_opts;
+
+/*
+ * Forward chunked SSD scan (see the header comment for the definition).
+ *   d          problem sizes and the dtype of x, B, C
+ *   chunk_len  chunk length in time steps (>= 1). The result is the same for
+ *              every chunk length up to rounding, because the chunked form is
+ *              exact; the kernels walk 32-row tiles (32/R time steps) and
+ *              accept any chunk_len >= 1.
+ *   R          MIMO rank (writes per time step)
+ *   stream     hipStream_t cast to void*, or NULL
+ */
+ssd_status ssd_forward(const ssd_dims *d, const void *x, const float *da,
+                       const void *B, const void *C, const float *D,
+                       const float *init_state, int64_t chunk_len, int64_t R,
+                       const float *theta, float *y, float *final_state,
+                       void *stream);
+
+/* ssd_forward with explicit launch options (NULL opts = automatic). */
+ssd_status ssd_forward_ex(const ssd_dims *d, const void *x, const float *da,
+                          const void *B, const void *C, const float *D,
+                          const float *init_state, int64_t chunk_len, int64_t R,
+                          const float *theta, float *y, float *final_state,
+                          const ssd_launch_opts *opts, void *stream);
+
+/* Bytes of stream-ordered scratch ssd_forward allocates for this problem with
+ * automatic launch options (0 when the sequence is not split). Returns 0 for
+ * invalid arguments. */
+size_t ssd_workspace_bytes(const ssd_dims *d, int64_t chunk_len, int64_t R);
+
+/* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
+const char *ssd_status_str(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_SCAN_H */

@@ -1,0 +1,125 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+rejects bad arguments on the host (no GPU needed: validation precedes any HIP
+call, and these calls never reach one)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_ssd_scan_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd_scan.h")
+
+# fake, 256-byte aligned device addresses: never dereferenced by these calls
+X, DA, BB, CC, DD, H0, TH, Y, FS = (0x10000000 * (i + 1) for i in range(9))
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.skip("libssd_scan.so not built")
+    return ssd.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(ssd.EXPORTED), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    names = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE",
+             3: "SSD_ERR_UNSUPPORTED", 4: "SSD_ERR_ALIAS", 5: "SSD_ERR_HIP"}
+    for k, v in names.items():
+        assert ssd.ssd_status_str(k) == v
+    assert ssd.ssd_status_str(99) == "unknown status"
+    assert ssd.ssd_status_str(-1) == "unknown status"
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=100, nheads=4, headdim=64, dstate=128, ngroups=1,
+                in_dtype=ssd.SSD_BF16)
+    base.update(kw)
+    return ssd.make_dims(**base)
+
+
+def call(d=None, x=X, da=DA, B=BB, C=CC, D=DD, init=H0, chunk=64, R=1, theta=None,
+         y=Y, fin=FS, opts=None, use_default=False):
+    if d is None and not use_default:
+        d = dims()
+    if opts is None:
+        return ssd.ssd_forward(d, x, da, B, C, D, init, chunk, R, theta, y, fin, None)
+    return ssd.ssd_forward_ex(d, x, da, B, C, D, init, chunk, R, theta, y, fin, opts, None)
+
+
+@pytest.mark.parametrize("field", ["x", "da", "B", "C", "y", "fin"])
+def test_null_required_pointer(lib, field):
+    assert call(**{field: None}) == ssd.SSD_ERR_NULL_ARG
+
+
+def test_null_dims(lib):
+    assert call(d=None, use_default=True) == ssd.SSD_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(seqlen=0), dict(batch=0), dict(nheads=0), dict(headdim=0),
+                                dict(dstate=0), dict(ngroups=0), dict(nheads=4, ngroups=3),
+                                dict(seqlen=-5)])
+def test_bad_shape(lib, kw):
+    assert call(d=dims(**kw)) == ssd.SSD_ERR_BAD_SHAPE
+
+
+def test_bad_chunk_and_rank(lib):
+    assert call(chunk=0) == ssd.SSD_ERR_BAD_SHAPE
+    assert call(R=0) == ssd.SSD_ERR_BAD_SHAPE
+    # an odd state size cannot be rotated pairwise
+    assert call(d=dims(dstate=17), theta=TH) == ssd.SSD_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("kw,R", [(dict(headdim=48), 1), (dict(headdim=256), 1), (dict(headdim=8), 1),
+                                  (dict(dstate=512), 1), (dict(dstate=96), 1), (dict(dstate=8), 1),
+                                  (dict(in_dtype=7), 1), (dict(), 3), (dict(), 32)])
+def test_unsupported(lib, kw, R):
+    assert call(d=dims(**kw), R=R) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_misaligned(lib):
+    assert call(x=X + 2) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(y=Y + 4) == ssd.SSD_ERR_UNSUPPORTED
+    assert call(da=DA + 1) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_alias(lib):
+    assert call(y=X) == ssd.SSD_ERR_ALIAS
+    assert call(fin=DA) == ssd.SSD_ERR_ALIAS
+    assert call(y=FS) == ssd.SSD_ERR_ALIAS
+    assert call(fin=Y + 4096) == ssd.SSD_ERR_ALIAS          # inside y
+    assert call(fin=H0 + 256) == ssd.SSD_ERR_ALIAS          # overlaps init but is not it
+
+
+def test_bad_launch_options(lib):
+    opts = ssd.SsdLaunchOpts()
+    opts.segments = -1
+    assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.reserved[3] = 1
+    assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+
+
+def test_workspace_bytes(lib):
+    # enough (batch, head) pairs to fill the chip: one segment, no scratch
+    assert ssd.ssd_workspace_bytes(dims(batch=8, seqlen=8192, nheads=80), 256, 1) == 0
+    # few pairs on a long sequence: segments, and scratch for their states
+    n = ssd.ssd_workspace_bytes(dims(batch=1, seqlen=131072, nheads=64), 256, 1)
+    assert n >= 64 * 2 * 64 * 128 * 4
+    assert ssd.ssd_workspace_bytes(dims(seqlen=0), 256, 1) == 0
