@@ -15,6 +15,9 @@ HIPCC_FLAGS = [
     "-O3", "--offload-arch=gfx950", "-std=c++17", "-fPIC", "-shared",
     # no packed-fp32 VALU instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the running state is also scaled by
+    # VALU every tile, and AGPR copies would cost more than they save
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

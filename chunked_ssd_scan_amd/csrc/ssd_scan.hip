@@ -44,6 +44,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kRows = 32;  // fused rows per tile
 
@@ -644,6 +645,497 @@ __global__ __launch_bounds__(4 * P) void ssd_walk_kernel(WalkArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Shared-B/C path (no rotation): B and C do not depend on the head, so the
+// K2 product C B^T of every tile is computed once per (batch, group, tile) by
+// ssd_cb_pack_kernel and reused by all heads of the group. The tile walk then
+// only stages row-major x, B, C tiles; operands that run along time (x^T, B^T)
+// come from the LDS transpose read (ds_read_b64_tr_b16).
+// ---------------------------------------------------------------------------
+
+// One wave per (batch, group, tile): CB^T for the three 16x16 blocks
+// (J, I) = (0,0), (0,1), (1,1) of the 32x32 tile, K = N, stored in
+// accumulator lane order: pack[tile][blk][lane][4] (fp32).
+template <typename TI, int NP>
+__global__ __launch_bounds__(64) void ssd_cb_pack_kernel(const void* __restrict__ Bv,
+                                                         const void* __restrict__ Cv,
+                                                         float* __restrict__ pack, int64_t TR,
+                                                         int64_t G, int64_t N, int nsub) {
+    using O = Ops<TI>;
+    typedef typename O::frag frag;
+    constexpr int KS = NP / 32;
+    const TI* Bg = static_cast<const TI*>(Bv);
+    const TI* Cg = static_cast<const TI*>(Cv);
+    const int lane = threadIdx.x, q = lane >> 4, l16 = lane & 15;
+    const int64_t tile = blockIdx.x;                  // (b*G + g)*nsub + k
+    const int64_t bg = tile / nsub;
+    const int k = (int)(tile % nsub);
+    const int64_t b = bg / G, g = bg % G;
+    const int64_t f0 = (int64_t)k * kRows;
+    auto row = [&](const TI* base, int r) -> const TI* { return base + ((b * TR + f0 + r) * G + g) * N; };
+    const bool ok0 = f0 + l16 < TR, ok1 = f0 + 16 + l16 < TR;
+    f32x4 c00 = {0.f, 0.f, 0.f, 0.f}, c01 = c00, c11 = c00;
+    const frag zero = O::pack((const float[8]){0, 0, 0, 0, 0, 0, 0, 0});
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+        const int n = 32 * s + 8 * q;
+        const bool nok = n < N;
+        const frag b0 = (ok0 && nok) ? O::ld8(row(Bg, l16) + n) : zero;
+        const frag b1 = (ok1 && nok) ? O::ld8(row(Bg, 16 + l16) + n) : zero;
+        const frag c0 = (ok0 && nok) ? O::ld8(row(Cg, l16) + n) : zero;
+        const frag c1 = (ok1 && nok) ? O::ld8(row(Cg, 16 + l16) + n) : zero;
+        c00 = O::mma(b0, c0, c00);
+        c01 = O::mma(b0, c1, c01);
+        c11 = O::mma(b1, c1, c11);
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(pack + tile * 768) + lane;
+    dst[0] = c00;
+    dst[64] = c01;
+    dst[128] = c11;
+}
+
+struct TileArgs {
+    const void* x;
+    const float* da;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* init;
+    float* y;
+    float* final_state;
+    float* ws_state;
+    float* ws_misc;
+    const float* cbpack;   // from ssd_cb_pack_kernel (output pass only)
+    int64_t T, H, G, N, R;
+    int S, seg_items, nsub, log2R, Qt;
+};
+
+// Operand whose reduction index runs down the rows of a row-major LDS tile:
+// lane (q, i) receives rows r0+q4 .. r0+q4+3 and r1+q4 .. r1+q4+3 (q4 = 4q)
+// of column col(i) = cb(i >> 2) + (i & 3). bf16: two ds_read_b64_tr_b16, where
+// within each 16-lane group lane s reads 4 elements at row r + (s >> 2),
+// column cb(s & 3). fp32: eight single-element reads.
+template <typename TI> struct RowRuns;
+
+template <> struct RowRuns<uint16_t> {
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    __device__ static inline bf16x8 load(const uint16_t* tile, int ld, int r0, int r1, int cb_src,
+                                         int /*col_own*/, int lane) {
+        const int s = lane & 15;
+        const uint16_t* p0 = tile + (r0 + (s >> 2)) * ld + cb_src;
+        const uint16_t* p1 = tile + (r1 + (s >> 2)) * ld + cb_src;
+        s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+        s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+        typedef __attribute__((ext_vector_type(8))) short s16x8;
+        s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, v);
+    }
+};
+
+template <> struct RowRuns<float> {
+    __device__ static inline f32x8 load(const float* tile, int ld, int r0, int r1, int /*cb_src*/,
+                                        int col_own, int /*lane*/) {
+        f32x8 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f[e] = tile[(r0 + e) * ld + col_own];
+            f[4 + e] = tile[(r1 + e) * ld + col_own];
+        }
+        return f;
+    }
+};
+
+// Row stride (elements) of a row-major LDS tile whose transposed operands are
+// read by row runs: a 16-lane group reads 4 consecutive rows, each at column
+// offsets {0, 8, 16, 24} + {0..3} elements of one 32-column block. Pick the
+// smallest padding (a multiple of 16 bytes) for which those 4 row slices fall
+// in distinct 4-byte banks of the 64-bank LDS.
+template <typename TI>
+constexpr int tr_row_stride(int ncols) {
+    constexpr int esz = (int)sizeof(TI);
+    const int row_dw = ncols * esz / 4;
+    for (int pad16 = 0; pad16 < 16; ++pad16) {
+        const int sdw = row_dw + 4 * pad16;
+        bool used[64] = {};
+        bool ok = true;
+        for (int r = 0; r < 4 && ok; ++r)
+            for (int c = 0; c < 4 && ok; ++c)
+                for (int w = 0; w < 2 * (esz == 2 ? 1 : 2) && ok; ++w) {
+                    const int bank = (r * sdw + (8 * c * esz) / 4 + w) & 63;
+                    if (used[bank]) ok = false;
+                    used[bank] = true;
+                }
+        if (ok) return ncols + pad16 * 16 / esz;
+    }
+    return ncols + 16 / esz;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
+// row-15 broadcast); lanes 0..31 are the only ones used.
+__device__ __forceinline__ float wave_prefix32(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    return v;
+}
+
+template <typename TI> struct MBlock;
+template <> struct MBlock<uint16_t> { typedef uint2 type; };
+template <> struct MBlock<float> { typedef float4 type; };
+
+template <typename TI>
+__device__ __forceinline__ typename MBlock<TI>::type pack_m(float a, float b, float c, float d) {
+    if constexpr (sizeof(TI) == 2) {
+        const uint32_t lo = (uint32_t)Ops<uint16_t>::from_f(a) | ((uint32_t)Ops<uint16_t>::from_f(b) << 16);
+        const uint32_t hi = (uint32_t)Ops<uint16_t>::from_f(c) | ((uint32_t)Ops<uint16_t>::from_f(d) << 16);
+        return make_uint2(lo, hi);
+    } else {
+        return make_float4(a, b, c, d);
+    }
+}
+
+template <typename TI>
+__device__ __forceinline__ typename Ops<TI>::frag join_m(typename MBlock<TI>::type lo,
+                                                       typename MBlock<TI>::type hi) {
+    if constexpr (sizeof(TI) == 2) {
+        return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    } else {
+        f32x8 f = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        return f;
+    }
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0).
+// Loads past `bytes` return zero and stores past it are dropped, which the
+// tile walk uses for ragged tails and for tiles beyond a segment's range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // lane offset that always falls outside a tile's range
+
+// The tile walk for the shared-B/C path. MODE 0: output pass; MODE 1:
+// state-only pass of the segmented schedule.
+template <typename TI, int P, int NP, int MODE>
+__global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
+    using O = Ops<TI>;
+    typedef typename O::frag frag;
+    typedef typename MBlock<TI>::type mblk;
+    constexpr int W = P / 16;
+    constexpr int NT = 64 * W;
+    constexpr int F = kRows;
+    constexpr int ESZ = (int)sizeof(TI);
+    constexpr int PAD = O::kPad;
+    constexpr int LDX = P + PAD;
+    constexpr int LDB = tr_row_stride<TI>(NP);     // B: read as B^T by row runs
+    constexpr int LDC = NP + PAD;                  // C: read along rows
+    constexpr int NTILE = NP / 16;
+    constexpr int KS = NP / 32;
+    constexpr bool OUT = (MODE == 0);
+    constexpr int EPU = 16 / ESZ;                  // elements per 16-byte unit
+    constexpr int XUR = P / EPU, BUR = NP / EPU;   // units per row
+    constexpr int XU = F * XUR, BU = F * BUR;
+    constexpr int XPT = (XU + NT - 1) / NT, BPT = (BU + NT - 1) / NT;
+    constexpr int NS = 2;                          // x prefetch depth (tiles, registers)
+
+    // one spare 16-byte unit at the end of each staged tile absorbs the
+    // writes of threads that have no unit (when a tile has fewer units than threads)
+    __shared__ __attribute__((aligned(16))) TI sX[2][F * LDX + EPU];
+    __shared__ __attribute__((aligned(16))) TI sB[2][F * LDB + EPU];
+    __shared__ __attribute__((aligned(16))) TI sC[OUT ? 2 : 1][OUT ? F * LDC + EPU : 1];
+    __shared__ __attribute__((aligned(16))) mblk sM[OUT ? 2 : 1][OUT ? 3 * 64 : 1];
+    __shared__ __attribute__((aligned(16))) float sEin[2][F], sW[2][F];
+    __shared__ float sCarry[2];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int q = lane >> 4, l16 = lane & 15;
+    const int p0 = wv * 16;
+
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R;
+    const int64_t TR = T * R;
+    const int S = a.S;
+    const int item = xcd_item(blockIdx.x, gridDim.x);
+    const int h = (int)(item % H);
+    const int bs = (int)(item / H);
+    const int seg = bs % a.seg_items;
+    const int b = bs / a.seg_items;
+    const int64_t grp = h / (H / G);
+    const int64_t bh = (int64_t)b * H + h;
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S);
+    const int k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    const int log2R = a.log2R;
+    const int Qt = a.Qt;
+
+    // ---- global addressing: uniform per-tile bases + fixed 32-bit lane offsets
+    const TI* xg = static_cast<const TI*>(a.x) + ((int64_t)b * TR * H + h) * P;
+    const TI* Bg = static_cast<const TI*>(a.B) + ((int64_t)b * TR * G + grp) * N;
+    const TI* Cg = static_cast<const TI*>(a.C) + ((int64_t)b * TR * G + grp) * N;
+    const float* dag = a.da + (int64_t)b * T * H + h;
+    float* yg = a.y + ((int64_t)b * TR * H + h) * P;
+    const int64_t xrow_el = H * P, brow_el = G * N;    // elements between fused rows
+    uint32_t xgoff[XPT], bgoff[BPT];
+    int xloff[XPT], bloff[BPT], cloff[BPT];
+#pragma unroll
+    for (int m = 0; m < XPT; ++m) {
+        const int u = tid + m * NT;
+        const int r = u / XUR, col = (u % XUR) * EPU;
+        xgoff[m] = (u < XU) ? (uint32_t)((r * xrow_el + col) * ESZ) : kOOB;
+        xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
+    }
+#pragma unroll
+    for (int m = 0; m < BPT; ++m) {
+        const int u = tid + m * NT;
+        const int r = u / BUR, col = (u % BUR) * EPU;
+        bgoff[m] = (u < BU && col < N) ? (uint32_t)((r * brow_el + col) * ESZ) : kOOB;
+        bloff[m] = (u < BU) ? r * LDB + col : F * LDB;
+        cloff[m] = (u < BU) ? r * LDC + col : F * LDC;
+    }
+    // decay-matrix blocks: wave w < 3 prefetches block w (W >= 3)
+    const float* cbg = OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub) * 768 : nullptr;
+    const uint32_t cboff = (uint32_t)((wv * 256 + lane * 4) * 4);
+    // da: lane f < 32 of a scanning wave reads da at step f >> log2R for the
+    // first rank of each step, so the scan over fused rows yields cum per row
+    const bool da_lane = (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
+    const uint32_t daoff = da_lane ? (uint32_t)((lane >> log2R) * H * 4) : kOOB;
+    uint32_t yoff[2];
+#pragma unroll
+    for (int I = 0; I < 2; ++I) yoff[I] = (uint32_t)(((16 * I + l16) * xrow_el + p0 + 4 * q) * 4);
+
+    // rows of tile k inside this segment (0 past its end)
+    auto valid_rows = [&](int k) -> int {
+        if (k >= k1) return 0;
+        const int64_t v = TR - (int64_t)k * F;
+        return v >= F ? F : (int)v;
+    };
+    auto span = [&](int vr, int64_t row_el, int64_t tail_el, int esz) -> uint32_t {
+        return vr > 0 ? (uint32_t)(((vr - 1) * row_el + tail_el) * esz) : 0u;
+    };
+
+    // ---- state (physical frame; S > 1 reads the carried state of the segment)
+    f32x4 hs[NTILE];
+    {
+        const float* src = nullptr;
+        if (OUT) {
+            if (S == 1)
+                src = a.init ? a.init + bh * P * N : nullptr;
+            else
+                src = a.ws_state + (bh * S + seg) * P * N;
+        }
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = phi_row(t, 4 * q + v);
+                hs[t][v] = (src && n < N) ? src[(int64_t)(p0 + l16) * N + n] : 0.f;
+            }
+        }
+    }
+    const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
+    float lam = 0.f;
+
+    // ---- register prefetch: x (streamed from HBM) NS tiles ahead in a ring,
+    // B / C / CB / da (shared by the heads, mostly L2 hits) one tile ahead
+    uint4 rx[NS][XPT], rb[BPT], rc[BPT];
+    float4 rcb;
+    float rda;
+
+    auto load_x = [&](int slot, int k) {
+        const int vr = valid_rows(k);
+        const auto rs = make_rsrc(xg + (int64_t)k * F * xrow_el, span(vr, xrow_el, P, ESZ));
+#pragma unroll
+        for (int m = 0; m < XPT; ++m)
+            rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, xgoff[m], 0, 2));
+    };
+    auto load_shared = [&](int k) {
+        const int vr = valid_rows(k);
+        const uint32_t nb = span(vr, brow_el, N, ESZ);
+        const auto rsb = make_rsrc(Bg + (int64_t)k * F * brow_el, nb);
+#pragma unroll
+        for (int m = 0; m < BPT; ++m)
+            rb[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bgoff[m], 0, 0));
+        if (OUT) {
+            const auto rsc = make_rsrc(Cg + (int64_t)k * F * brow_el, nb);
+#pragma unroll
+            for (int m = 0; m < BPT; ++m)
+                rc[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsc, bgoff[m], 0, 0));
+            if (W >= 3) {
+                const auto rscb = make_rsrc(cbg + (int64_t)k * 768, k < k1 ? 768 * 4 : 0);
+                rcb = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                     rscb, wv < 3 ? cboff : kOOB, 0, 0));
+            }
+        }
+        int vt = 0;
+        if (k < k1) {
+            const int64_t v = T - (int64_t)k * Qt;
+            vt = v >= Qt ? Qt : (int)v;
+        }
+        const auto rsd = make_rsrc(dag + (int64_t)k * Qt * H, vt > 0 ? (uint32_t)(((vt - 1) * H + 1) * 4) : 0u);
+        rda = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsd, daoff, 0, 0));
+    };
+
+    // Write a prefetched tile into LDS buffer `buf`, and build its per-row
+    // vectors and decay matrix.
+    auto store = [&](int slot, int buf, int k) {
+#pragma unroll
+        for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
+#pragma unroll
+        for (int m = 0; m < BPT; ++m) {
+            *reinterpret_cast<uint4*>(&sB[buf][bloff[m]]) = rb[m];
+            if (OUT) *reinterpret_cast<uint4*>(&sC[buf][cloff[m]]) = rc[m];
+        }
+        // K1: inclusive prefix of da over the tile's fused rows
+        const bool scan_wave = (wv == 0) || (OUT && wv < 3);
+        if (scan_wave) {
+            const float cum = wave_prefix32(rda);
+            const float last = __shfl(cum, F - 1);
+            if (wv == 0) {
+                if (lane < F) {
+                    sEin[buf][lane] = __expf(cum);
+                    sW[buf][lane] = __expf(last - cum);
+                }
+                if (lane == 0) {
+                    sCarry[buf] = __expf(last);
+                    lam += last;
+                }
+            }
+            if (OUT) {
+                // decay matrix blocks M = CB^T o L (+ D on the diagonal)
+                for (int blk = wv; blk < 3; blk += W) {
+                    float4 cbv;
+                    if (W >= 3) {
+                        cbv = rcb;
+                    } else {
+                        const auto rscb = make_rsrc(cbg + (int64_t)k * 768, k < k1 ? 768 * 4 : 0);
+                        cbv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                             rscb, (uint32_t)((blk * 256 + lane * 4) * 4), 0, 0));
+                    }
+                    const int J = blk == 2 ? 1 : 0, I = blk == 0 ? 0 : 1;
+                    const int i = 16 * I + l16;
+                    const float ci = __shfl(cum, i);
+                    const int ti = i >> log2R;
+                    float mv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int j = 16 * J + 4 * q + v;
+                        const float cj = __shfl(cum, j);
+                        mv[v] = (ti >= (j >> log2R)) ? cbv[v] * __expf(ci - cj) : 0.f;
+                        if (i == j) mv[v] += Dh;
+                    }
+                    sM[buf][blk * 64 + lane] = pack_m<TI>(mv[0], mv[1], mv[2], mv[3]);
+                }
+            }
+        }
+    };
+
+    auto compute = [&](int buf, int k) {
+        const TI* tX = sX[buf];
+        const TI* tB = sB[buf];
+        // x^T operand: rows j in {4q..4q+3} and {16+4q..16+4q+3}, column p0 + i
+        const frag xa = RowRuns<TI>::load(tX, LDX, 4 * q, 16 + 4 * q, p0 + 4 * (lane & 3),
+                                          p0 + l16, lane);
+        if (OUT) {
+            const TI* tC = sC[buf];
+            f32x4 yacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                float hv[8];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    hv[v] = hs[2 * s][v];
+                    hv[4 + v] = hs[2 * s + 1][v];
+                }
+                const frag hA = O::pack(hv);
+                yacc[0] = O::mma(hA, O::ld8(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
+                yacc[1] = O::mma(hA, O::ld8(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
+            }
+            const float e0 = sEin[buf][l16], e1 = sEin[buf][16 + l16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                yacc[0][v] *= e0;
+                yacc[1][v] *= e1;
+            }
+            const mblk m00 = sM[buf][lane], m01 = sM[buf][64 + lane], m11 = sM[buf][128 + lane];
+            const mblk zz = pack_m<TI>(0.f, 0.f, 0.f, 0.f);
+            yacc[0] = O::mma(xa, join_m<TI>(m00, zz), yacc[0]);
+            yacc[1] = O::mma(xa, join_m<TI>(m01, m11), yacc[1]);
+            const auto rsy = make_rsrc(yg + (int64_t)k * F * xrow_el, span(valid_rows(k), xrow_el, P, 4));
+#pragma unroll
+            for (int I = 0; I < 2; ++I)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yacc[I]), rsy, yoff[I], 0, 0);
+        }
+        // K3 + K4 with the same time order as the x^T operand
+        float xv[8];
+        O::unpack(xa, xv);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sW[buf][4 * q]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sW[buf][16 + 4 * q]);
+        xv[0] *= w0.x; xv[1] *= w0.y; xv[2] *= w0.z; xv[3] *= w0.w;
+        xv[4] *= w1.x; xv[5] *= w1.y; xv[6] *= w1.z; xv[7] *= w1.w;
+        const frag xw = O::pack(xv);
+        const float carry = sCarry[buf];
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+            // B^T operand rows n = phi(t, i): column base for 4-lane group a
+            const int cbs = 32 * (t >> 1) + 8 * (lane & 3) + 4 * (t & 1);
+            const int cown = 32 * (t >> 1) + 8 * (l16 >> 2) + 4 * (t & 1) + (l16 & 3);
+            const frag bt = RowRuns<TI>::load(tB, LDB, 4 * q, 16 + 4 * q, cbs, cown, lane);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hs[t][v] *= carry;
+            hs[t] = O::mma(bt, xw, hs[t]);
+        }
+    };
+
+    // ---- pipeline. Tile k is computed from LDS buffer (k - k0) & 1 while tile
+    // k+1 is staged into the other one; one barrier per tile. Memory counters
+    // retire in issue order, so each step issues the loads it waits on next
+    // (shared B/C, one tile ahead) before the far x prefetch and the y stores.
+    // Tiles are walked in pairs; a tile past the segment end loads zeros
+    // (da = 0, x = 0), which leaves the state unchanged, and stores nothing.
+    load_x(0, k0);
+    load_x(1, k0 + 1);
+    load_shared(k0);
+    store(0, 0, k0);
+    load_shared(k0 + 1);
+    load_x(0, k0 + NS);
+    __syncthreads();
+    for (int k = k0; k < k1; k += 2) {
+        // tile k (buffer 0), staging tile k+1 into buffer 1
+        store(1, 1, k + 1);
+        load_shared(k + 2);
+        load_x(1, k + 1 + NS);
+        compute(0, k);
+        __syncthreads();
+        // tile k+1 (buffer 1), staging tile k+2 into buffer 0
+        store(0, 0, k + 2);
+        load_shared(k + 3);
+        load_x(0, k + 2 + NS);
+        compute(1, k + 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue
+    float* dstate = nullptr;
+    if (OUT) {
+        if (seg == S - 1) dstate = a.final_state + bh * P * N;
+    } else {
+        dstate = a.ws_state + (bh * S + seg + 1) * P * N;
+        if (tid == 0) a.ws_misc[(bh * S + seg) * (1 + N / 2)] = lam;
+    }
+    if (dstate) {
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = phi_row(t, 4 * q + v);
+                if (n < N) dstate[(int64_t)(p0 + l16) * N + n] = hs[t][v];
+            }
+        }
+    }
+}
+
 // Pass B: carry states across segments, one thread per state pair (p, k).
 //   c_0 = init (or 0);  c_{s+1} = exp(Lambda_s) R(Phi_s) c_s + local_s
 // On entry ws_state slot s+1 holds local_s (segment s from a zero state); on
@@ -715,6 +1207,64 @@ void* walk_ptr_p(int P, int NP) {
     return nullptr;
 }
 
+// Static LDS bytes of ssd_tiles_kernel<TI, P, NP, MODE> (mirrors its arrays).
+template <typename TI, int P, int NP, int MODE>
+constexpr int tiles_lds_bytes() {
+    constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows;
+    constexpr int ldx = P + Ops<TI>::kPad, ldb = tr_row_stride<TI>(NP), ldc = NP + Ops<TI>::kPad;
+    constexpr int out = MODE == 0;
+    return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
+           (out ? 2 * (F * ldc + epu) * esz + 2 * 3 * 64 * 2 * esz * 4 / 2 : 0) + 2 * 2 * F * 4 + 2 * 4;
+}
+
+constexpr int kLdsLimit = 160 * 1024;
+
+template <typename TI, int P, int NP, int MODE>
+void* tiles_ptr() {
+    if constexpr (tiles_lds_bytes<TI, P, NP, MODE>() <= kLdsLimit)
+        return reinterpret_cast<void*>(&ssd_tiles_kernel<TI, P, NP, MODE>);
+    else
+        return nullptr;  // does not fit one CU's LDS: the caller uses the general tile walk
+}
+
+template <typename TI, int P, int MODE>
+void* tiles_ptr_np(int NP) {
+    switch (NP) {
+        case 32: return tiles_ptr<TI, P, 32, MODE>();
+        case 64: return tiles_ptr<TI, P, 64, MODE>();
+        case 128: return tiles_ptr<TI, P, 128, MODE>();
+        case 256: return tiles_ptr<TI, P, 256, MODE>();
+    }
+    return nullptr;
+}
+
+template <typename TI, int MODE>
+void* tiles_ptr_p(int P, int NP) {
+    switch (P) {
+        case 16: return tiles_ptr_np<TI, 16, MODE>(NP);
+        case 32: return tiles_ptr_np<TI, 32, MODE>(NP);
+        case 64: return tiles_ptr_np<TI, 64, MODE>(NP);
+        case 128: return tiles_ptr_np<TI, 128, MODE>(NP);
+    }
+    return nullptr;
+}
+
+void* select_tiles(int dtype, int mode, int P, int NP) {
+    if (dtype == SSD_BF16) return mode ? tiles_ptr_p<uint16_t, 1>(P, NP) : tiles_ptr_p<uint16_t, 0>(P, NP);
+    return mode ? tiles_ptr_p<float, 1>(P, NP) : tiles_ptr_p<float, 0>(P, NP);
+}
+
+template <typename TI>
+void* cb_pack_ptr(int NP) {
+    switch (NP) {
+        case 32: return reinterpret_cast<void*>(&ssd_cb_pack_kernel<TI, 32>);
+        case 64: return reinterpret_cast<void*>(&ssd_cb_pack_kernel<TI, 64>);
+        case 128: return reinterpret_cast<void*>(&ssd_cb_pack_kernel<TI, 128>);
+        case 256: return reinterpret_cast<void*>(&ssd_cb_pack_kernel<TI, 256>);
+    }
+    return nullptr;
+}
+
 void* select_walk(int dtype, bool rot, int mode, int P, int NP) {
     if (dtype == SSD_BF16) {
         if (rot) return mode ? walk_ptr_p<uint16_t, true, 1>(P, NP) : walk_ptr_p<uint16_t, true, 0>(P, NP);
@@ -775,12 +1325,23 @@ int auto_segments(int64_t bh, int nsub) {
     return (int)(want < 1 ? 1 : want);
 }
 
-size_t workspace_for(const Plan& pl) {
-    if (pl.S <= 1) return 0;
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Scratch layout: [segment states | segment Lambda/Phi | C B^T tile pack]
+struct WsLayout {
+    size_t state, misc, pack, total;
+};
+
+WsLayout workspace_layout(const Plan& pl, bool no_pack) {
+    WsLayout w{0, 0, 0, 0};
     const size_t bh = (size_t)(pl.b * pl.H);
-    const size_t st = bh * pl.S * pl.P * pl.N * sizeof(float);
-    const size_t misc = bh * pl.S * (1 + pl.N / 2) * sizeof(float);
-    return ((st + 255) & ~(size_t)255) + misc;
+    if (pl.S > 1) {
+        w.state = align256(bh * pl.S * pl.P * pl.N * sizeof(float));
+        w.misc = align256(bh * pl.S * (1 + pl.N / 2) * sizeof(float));
+    }
+    if (!no_pack) w.pack = align256((size_t)(pl.b * pl.G) * pl.nsub * 768 * sizeof(float));
+    w.total = w.state + w.misc + w.pack;
+    return w;
 }
 
 Plan make_plan(const ssd_dims* d, int64_t R, int segments) {
@@ -799,16 +1360,42 @@ Plan make_plan(const ssd_dims* d, int64_t R, int segments) {
     return pl;
 }
 
-ssd_status launch_walk(const Plan& pl, int mode, bool rot, const WalkArgs& args, hipStream_t st) {
-    void* fn = select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
+// Tile walks: `shared` selects the shared-B/C kernel (ssd_tiles_kernel), else
+// the general walk (ssd_walk_kernel, which also handles rotation).
+template <typename Args>
+ssd_status launch_walk(const Plan& pl, int mode, bool shared, bool rot, const Args& args, hipStream_t st) {
+    void* fn = shared ? select_tiles(pl.dtype, mode, (int)pl.P, (int)pl.NP)
+                      : select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
     if (!fn) return SSD_ERR_UNSUPPORTED;
     const int64_t nwg = pl.b * pl.H * args.seg_items;
     if (nwg < 1 || nwg > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     dim3 grid((unsigned)nwg), block((unsigned)(4 * pl.P));
-    WalkArgs a = args;
+    Args a = args;
     void* kargs[] = {&a};
     if (hipLaunchKernel(fn, grid, block, kargs, 0, st) != hipSuccess) return SSD_ERR_HIP;
     return SSD_OK;
+}
+
+// Pass A (segment end states), pass B (carry), pass C (outputs).
+template <typename Args>
+ssd_status run_passes(const Plan& pl, bool shared, bool rot, Args args, const float* init_state,
+                      hipStream_t hs) {
+    ssd_status rs = SSD_OK;
+    if (pl.S > 1) {
+        args.seg_items = pl.S - 1;
+        rs = launch_walk(pl, 1, shared, rot, args, hs);
+        if (rs == SSD_OK) {
+            dim3 grid((unsigned)((pl.P * (pl.N / 2) + 255) / 256), (unsigned)(pl.b * pl.H));
+            hipLaunchKernelGGL(ssd_carry_kernel, grid, dim3(256), 0, hs, init_state, args.ws_state,
+                               args.ws_misc, pl.P, pl.N, pl.S, rot ? 1 : 0);
+            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+        }
+    }
+    if (rs == SSD_OK) {
+        args.seg_items = pl.S;
+        rs = launch_walk(pl, 0, shared, rot, args, hs);
+    }
+    return rs;
 }
 
 }  // namespace
@@ -829,7 +1416,7 @@ const char* ssd_status_str(int32_t status) {
 
 size_t ssd_workspace_bytes(const ssd_dims* d, int64_t chunk_len, int64_t R) {
     if (!d || check_shape(d, chunk_len, R, false) != SSD_OK) return 0;
-    return workspace_for(make_plan(d, R, 0));
+    return workspace_layout(make_plan(d, R, 0), false).total;
 }
 
 ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, const void* B,
@@ -871,38 +1458,53 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const bool rot = theta != nullptr;
 
-    WalkArgs args;
-    memset(&args, 0, sizeof(args));
-    args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
-    args.init = init_state; args.theta = theta; args.y = y; args.final_state = final_state;
-    args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
-    args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
-
+    // shared-B/C kernels when there is no rotation and the tile fits in LDS
+    const bool shared = !rot && select_tiles(pl.dtype, 0, (int)pl.P, (int)pl.NP) != nullptr &&
+                        select_tiles(pl.dtype, 1, (int)pl.P, (int)pl.NP) != nullptr;
+    const WsLayout wl = workspace_layout(pl, !shared);
     void* ws = nullptr;
-    const size_t wsb = workspace_for(pl);
-    if (wsb) {
-        if (hipMallocAsync(&ws, wsb, hs) != hipSuccess) return SSD_ERR_HIP;
-        const size_t st_bytes = (size_t)(b * H) * pl.S * P * N * sizeof(float);
-        args.ws_state = static_cast<float*>(ws);
-        args.ws_misc = reinterpret_cast<float*>(static_cast<char*>(ws) + ((st_bytes + 255) & ~(size_t)255));
+    if (wl.total) {
+        if (hipMallocAsync(&ws, wl.total, hs) != hipSuccess) return SSD_ERR_HIP;
     }
+    char* wsc = static_cast<char*>(ws);
+    float* ws_state = pl.S > 1 ? reinterpret_cast<float*>(wsc) : nullptr;
+    float* ws_misc = pl.S > 1 ? reinterpret_cast<float*>(wsc + wl.state) : nullptr;
+    float* ws_pack = shared ? reinterpret_cast<float*>(wsc + wl.state + wl.misc) : nullptr;
 
     ssd_status rs = SSD_OK;
-    if (pl.S > 1) {
-        // pass A: segment end states (segments 0 .. S-2)
-        args.seg_items = pl.S - 1;
-        rs = launch_walk(pl, 1, rot, args, hs);
-        // pass B: carries across segments
-        if (rs == SSD_OK) {
-            dim3 grid((unsigned)((P * (N / 2) + 255) / 256), (unsigned)(b * H));
-            hipLaunchKernelGGL(ssd_carry_kernel, grid, dim3(256), 0, hs, init_state, args.ws_state,
-                               args.ws_misc, P, N, pl.S, rot ? 1 : 0);
-            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+    if (!shared) {
+        WalkArgs args;
+        memset(&args, 0, sizeof(args));
+        args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
+        args.init = init_state; args.theta = theta; args.y = y; args.final_state = final_state;
+        args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
+        args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
+        args.ws_state = ws_state; args.ws_misc = ws_misc;
+        rs = run_passes(pl, false, rot, args, init_state, hs);
+    } else {
+        // K2 once per (batch, group, tile), shared by every head of the group
+        void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
+        const int64_t ntiles = pl.b * pl.G * pl.nsub;
+        if (!pk || ntiles > 0x7fffffff) {
+            rs = SSD_ERR_UNSUPPORTED;
+        } else {
+            const void* Bp = B;
+            const void* Cp = C;
+            int64_t TRv = T * R, Gv = G, Nv = N;
+            int nsub = pl.nsub;
+            void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub};
+            if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
         }
-    }
-    if (rs == SSD_OK) {
-        args.seg_items = pl.S;
-        rs = launch_walk(pl, 0, rot, args, hs);
+        if (rs == SSD_OK) {
+            TileArgs args;
+            memset(&args, 0, sizeof(args));
+            args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
+            args.init = init_state; args.y = y; args.final_state = final_state;
+            args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
+            args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
+            args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
+            rs = run_passes(pl, true, false, args, init_state, hs);
+        }
     }
     if (ws) {
         if (hipFreeAsync(ws, hs) != hipSuccess && rs == SSD_OK) rs = SSD_ERR_HIP;

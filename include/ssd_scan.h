@@ -41,8 +41,9 @@
  *
  * Ownership: the caller owns every buffer and keeps inputs alive until the
  * work enqueued on `stream` has completed. Nothing is retained after return.
- * Scratch (only when the sequence is split into segments, see
- * ssd_workspace_bytes) is allocated and released stream-ordered on `stream`.
+ * Scratch (the head-shared C B^T tile pack, and segment states when the
+ * sequence is split; see ssd_workspace_bytes) is allocated and released
+ * stream-ordered on `stream` (hipMallocAsync / hipFreeAsync).
  * final_state may be the same pointer as init_state (in-place state update);
  * any other overlap between an output and another buffer is SSD_ERR_ALIAS.
  *
@@ -119,8 +120,9 @@ ssd_status ssd_forward_ex(const ssd_dims *d, const void *x, const float *da,
                           const ssd_launch_opts *opts, void *stream);
 
 /* Bytes of stream-ordered scratch ssd_forward allocates for this problem with
- * automatic launch options (0 when the sequence is not split). Returns 0 for
- * invalid arguments. */
+ * automatic launch options and no rotation (an upper bound with rotation):
+ * the shared C B^T tile pack, plus segment states when the sequence is split.
+ * Returns 0 for invalid arguments. */
 size_t ssd_workspace_bytes(const ssd_dims *d, int64_t chunk_len, int64_t R);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
