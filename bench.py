@@ -107,9 +107,12 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=2,
                     help="workload id in ssd_inputs.CONFIGS (the reported line uses 2)")
-    ap.add_argument("--cpu-slices", type=int, default=64)
+    ap.add_argument("--cpu-slices", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
+    ap.add_argument("--block-slices", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (5 launches) for counter calibration")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -125,6 +128,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, device="cuda:0", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+        return 0
     ssd.load_library()
     shape = si.CONFIGS[args.config]
     dev = torch.device("cuda:0")
@@ -137,7 +149,8 @@ def main() -> int:
 
     def step():
         ssd.forward(g.x, g.da, g.B, g.C, g.D, g.init_state, shape.chunk_len, g.theta,
-                    y=y, final_state=fin, segments=args.segments, stream=stream.cuda_stream)
+                    y=y, final_state=fin, segments=args.segments,
+                    block_slices=args.block_slices, stream=stream.cuda_stream)
 
     for _ in range(args.warmup):
         step()
@@ -183,7 +196,8 @@ def main() -> int:
                    "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
                    "ngroups": shape.ngroups, "mimo_rank": shape.mimo_rank,
                    "chunk_len": shape.chunk_len, "rotation": shape.rotation,
-                   "segments": args.segments or "auto"},
+                   "segments": args.segments or "auto",
+                   "block_slices": args.block_slices or "auto"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": nbytes, "kernel_ms": launch_ms},

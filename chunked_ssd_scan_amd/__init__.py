@@ -37,7 +37,8 @@ class SsdDims(ctypes.Structure):
 
 
 class SsdLaunchOpts(ctypes.Structure):
-    _fields_ = [("segments", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("segments", ctypes.c_int32), ("block_slices", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 class SsdError(RuntimeError):
@@ -109,14 +110,15 @@ def _dptr(t):
 
 
 def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=None,
-            y=None, final_state=None, segments: int = 0, stream=None
-            ) -> Tuple["torch.Tensor", "torch.Tensor"]:
+            y=None, final_state=None, segments: int = 0, block_slices: int = 0,
+            stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Run the scan on device tensors; returns (y, final_state).
 
     x [b,T,R,H,P] (or [b,T,H,P] for R = 1), da [b,T,H], B/C [b,T,R,G,N]
     (or [b,T,G,N]); D [H], init_state [b,H,P,N], theta [b,T,H,N/2] fp32.
     y / final_state may be given (fp32, contiguous) to write in place;
-    final_state may be init_state itself.
+    final_state may be init_state itself. ``segments`` and ``block_slices``
+    are the launch options of ssd_forward_ex (0 = automatic).
     """
     import torch
 
@@ -155,6 +157,7 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     dims = make_dims(b, T, H, P, N, G, in_dtype)
     opts = SsdLaunchOpts()
     opts.segments = int(segments)
+    opts.block_slices = int(block_slices)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     with torch.cuda.device(dev):

@@ -1,9 +1,8 @@
 // Chunked SSD scan forward for AMD Instinct MI355X (gfx950, CDNA4).
 //
-// One workgroup owns one (batch, head, sequence segment) and walks the
-// segment's tiles in order. A tile is 32 rank-fused rows (32/R time steps).
-// Per tile it runs the chunk algorithm of burn-mamba "mamba3/ssd/serial.rs"
-// (k1..k5) on that tile:
+// A workgroup walks the tiles of one sequence segment in order. A tile is 32
+// rank-fused rows (32/R time steps). Per tile it runs the chunk algorithm of
+// burn-mamba "mamba3/ssd/serial.rs" (k1..k5) on that tile:
 //   K1  inclusive prefix sum of da over the tile (wave shuffles)
 //   K2  C B^T on the tile's fused rows (MFMA), turned into the decay matrix
 //       L o CB with L[i,j] = exp(cum_i - cum_j) when step(i) >= step(j)
@@ -11,8 +10,14 @@
 //   K5  y = exp(cum_i) C h_in + (L o CB) x   (+ D x, folded into L's diagonal)
 //   K3+K4  h <- exp(cum_last) h + sum_j exp(cum_last - cum_j) x_j (outer) B_j
 // The running state h (P x N fp32) never leaves the accumulator registers:
-// wave w holds the state columns p in [16w, 16w+16) for every n, so the K4
-// state passing between tiles is a register update, not a memory round trip.
+// each wave holds 16 state columns p for every n, so the K4 state passing
+// between tiles is a register update, not a memory round trip.
+//
+// Two walks: the column-block walk (no rotation) gives a workgroup W
+// consecutive 16-column slices of the time rows flattened over (head, p)
+// within one B/C group, so its x and y rows are contiguous and the B, C and
+// C B^T tiles it stages serve every head it touches; the general walk (any
+// rotation, or shapes the former does not fit) gives a workgroup one head.
 //
 // With a rotation ("mamba3/scan.py", cumulative_angles / rotate_by), B and C
 // are turned by R(-Phi_t) while they are staged into LDS, Phi being the
@@ -47,6 +52,7 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kRows = 32;  // fused rows per tile
+constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // element type helpers: TI = uint16_t (bf16 bits) or float
@@ -706,8 +712,9 @@ struct TileArgs {
     float* ws_state;
     float* ws_misc;
     const float* cbpack;   // from ssd_cb_pack_kernel (output pass only)
-    int64_t T, H, G, N, R;
+    int64_t T, H, G, N, R, P;
     int S, seg_items, nsub, log2R, Qt;
+    int NB;                // column blocks per B/C group
 };
 
 // Operand whose reduction index runs down the rows of a row-major LDS tile:
@@ -771,6 +778,31 @@ constexpr int tr_row_stride(int ncols) {
     return ncols + 16 / esz;
 }
 
+// Row stride (elements) of the per-head x tile of the grouped walk, read as
+// the x^T operand by row runs starting at 16-column slices: bf16 lanes of one
+// 16-lane group read 4 consecutive rows, 8 dwords each; fp32 lane groups read
+// rows 4 apart, 16 dwords each. Smallest padding (a multiple of 16 bytes) that
+// puts those row slices in distinct banks.
+template <typename TI>
+constexpr int x_row_stride(int ncols) {
+    constexpr int esz = (int)sizeof(TI);
+    const int row_dw = ncols * esz / 4;
+    const int rstep = esz == 2 ? 1 : 4, width = esz == 2 ? 8 : 16;
+    for (int pad16 = 0; pad16 < 16; ++pad16) {
+        const int sdw = row_dw + 4 * pad16;
+        bool used[64] = {};
+        bool ok = true;
+        for (int r = 0; r < 4 && ok; ++r)
+            for (int w = 0; w < width && ok; ++w) {
+                const int bank = (r * rstep * sdw + w) & 63;
+                if (used[bank]) ok = false;
+                used[bank] = true;
+            }
+        if (ok) return ncols + pad16 * 16 / esz;
+    }
+    return ncols + 16 / esz;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (DPP row shifts, then the
 // row-15 broadcast); lanes 0..31 are the only ones used.
 __device__ __forceinline__ float wave_prefix32(float v) {
@@ -817,68 +849,148 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 constexpr uint32_t kOOB = 0x80000000u;  // lane offset that always falls outside a tile's range
 
-// The tile walk for the shared-B/C path. MODE 0: output pass; MODE 1:
-// state-only pass of the segmented schedule.
-template <typename TI, int P, int NP, int MODE>
-__global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
+// ---------------------------------------------------------------------------
+// Column-block tile walk (shared B/C, no rotation). Flatten each time row of
+// x and y over (head, p) and cut the columns of one B/C group into slices of
+// 16; a workgroup owns W consecutive slices (one wave each), possibly
+// spanning several heads. Its x and y rows are then contiguous runs of 16 W
+// columns, and the B, C and C B^T tiles it stages serve every head it touches.
+// Wave w keeps the state columns p in [p0, p0 + 16) of its head h and scans
+// that head's decays itself. y goes through LDS and leaves as whole rows of
+// the block, one tile after it is computed.
+// ---------------------------------------------------------------------------
+
+// Row stride (floats) of the staged y block: eight consecutive rows written at
+// one 16-byte column by the MFMA output layout fall in distinct banks.
+constexpr int y_row_stride(int ncols) {
+    for (int pad = 0; pad < 64; pad += 4) {
+        const int s = ncols + pad;
+        bool used[64] = {};
+        bool ok = true;
+        for (int r = 0; r < 8 && ok; ++r)
+            for (int w = 0; w < 4 && ok; ++w) {
+                const int bank = (r * s + w) & 63;
+                if (used[bank]) ok = false;
+                used[bank] = true;
+            }
+        if (ok) return s;
+    }
+    return ncols + 4;
+}
+
+// Most heads a block of W slices may touch: W / 2 + 1 when every head has at
+// least two slices (headdim >= 32). The host checks the actual count.
+constexpr int cols_max_heads(int W) { return W / 2 + 1; }
+
+template <typename TI, int NP, int W>
+constexpr int cols_lds_bytes(int mode) {
+    constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows, CW = 16 * W, MH = cols_max_heads(W);
+    constexpr int ldx = x_row_stride<TI>(CW), ldb = tr_row_stride<TI>(NP), ldc = NP + Ops<TI>::kPad;
+    constexpr int mbytes = (int)sizeof(typename MBlock<TI>::type);
+    const int out = mode == 0;
+    return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
+           (out ? 2 * (F * ldc + epu) * esz + 2 * (768 + 4) * 4 + 2 * (F * y_row_stride(CW) + 4) * 4 +
+                      2 * MH * 3 * 64 * mbytes
+                : 0) +
+           4 * MH * (3 * F + 1) * 4;
+}
+
+template <typename TI, int NP, int W, int MODE>
+__global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     using O = Ops<TI>;
     typedef typename O::frag frag;
     typedef typename MBlock<TI>::type mblk;
-    constexpr int W = P / 16;
     constexpr int NT = 64 * W;
     constexpr int F = kRows;
     constexpr int ESZ = (int)sizeof(TI);
     constexpr int PAD = O::kPad;
-    constexpr int LDX = P + PAD;
-    constexpr int LDB = tr_row_stride<TI>(NP);     // B: read as B^T by row runs
-    constexpr int LDC = NP + PAD;                  // C: read along rows
+    constexpr int CW = 16 * W;                     // columns per workgroup
+    constexpr int MH = cols_max_heads(W);
+    constexpr int LDX = x_row_stride<TI>(CW);
+    constexpr int LDB = tr_row_stride<TI>(NP);
+    constexpr int LDC = NP + PAD;
+    constexpr int LDY = y_row_stride(CW);
     constexpr int NTILE = NP / 16;
     constexpr int KS = NP / 32;
     constexpr bool OUT = (MODE == 0);
-    constexpr int EPU = 16 / ESZ;                  // elements per 16-byte unit
-    constexpr int XUR = P / EPU, BUR = NP / EPU;   // units per row
-    constexpr int XU = F * XUR, BU = F * BUR;
-    constexpr int XPT = (XU + NT - 1) / NT, BPT = (BU + NT - 1) / NT;
-    constexpr int NS = 2;                          // x prefetch depth (tiles, registers)
+    constexpr int EPU = 16 / ESZ;
+    constexpr int XUR = CW / EPU, BUR = NP / EPU, YUR = CW / 4;   // 16-byte units per row
+    constexpr int XU = F * XUR, BU = F * BUR, CBU = 768 * 4 / 16, YU = F * YUR;
+    constexpr int XPT = (XU + NT - 1) / NT, BPT = (BU + NT - 1) / NT, CBPT = (CBU + NT - 1) / NT;
+    constexpr int YPT = (YU + NT - 1) / NT;
 
-    // one spare 16-byte unit at the end of each staged tile absorbs the
-    // writes of threads that have no unit (when a tile has fewer units than threads)
     __shared__ __attribute__((aligned(16))) TI sX[2][F * LDX + EPU];
     __shared__ __attribute__((aligned(16))) TI sB[2][F * LDB + EPU];
     __shared__ __attribute__((aligned(16))) TI sC[OUT ? 2 : 1][OUT ? F * LDC + EPU : 1];
-    __shared__ __attribute__((aligned(16))) mblk sM[OUT ? 2 : 1][OUT ? 3 * 64 : 1];
-    __shared__ __attribute__((aligned(16))) float sEin[2][F], sW[2][F];
-    __shared__ float sCarry[2];
+    __shared__ __attribute__((aligned(16))) float sCB[OUT ? 2 : 1][OUT ? 768 + 4 : 1];
+    __shared__ __attribute__((aligned(16))) float sY[OUT ? 2 : 1][OUT ? F * LDY + 4 : 1];
+    __shared__ __attribute__((aligned(16))) mblk sM[OUT ? 2 : 1][OUT ? MH * 3 * 64 : 1];
+    // per-head tile vectors, ring of 4 tiles: cumulative log2-decay, exp2 of
+    // it, the weight that carries row j to the tile end, and the tile decay
+    __shared__ __attribute__((aligned(16))) float sCum[4][MH][F], sEin[4][MH][F], sW[4][MH][F];
+    __shared__ float sCarry[4][MH];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    // wave index made visibly uniform, so per-head pointers stay scalar
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, l16 = lane & 15;
-    const int p0 = wv * 16;
 
-    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R;
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P;
     const int64_t TR = T * R;
     const int S = a.S;
-    const int item = xcd_item(blockIdx.x, gridDim.x);
-    const int h = (int)(item % H);
-    const int bs = (int)(item / H);
-    const int seg = bs % a.seg_items;
-    const int b = bs / a.seg_items;
-    const int64_t grp = h / (H / G);
+    const int SPH = (int)(P >> 4);                 // slices per head
+    const int NB = a.NB;                           // column blocks per B/C group
+    int item = xcd_item(blockIdx.x, gridDim.x);
+    const int jb = item % NB;
+    item /= NB;
+    const int64_t grp = item % G;
+    item /= (int)G;
+    const int seg = item % a.seg_items;
+    const int b = item / a.seg_items;
+    const int64_t col0 = grp * (H / G) * P + (int64_t)jb * CW;   // first flattened (h, p) column
+    const int s0 = jb * W;                                       // first slice of the block
+    const int hb0 = s0 / SPH;                                    // its head, within the group
+    const int nhb = (s0 + W - 1) / SPH - hb0 + 1;                // heads the block touches
+    const int64_t hfirst = grp * (H / G) + hb0;
+    const int slice = s0 + wv;                                   // this wave's slice
+    const int hl = slice / SPH - hb0;                            // its head within the block
+    const int64_t h = hfirst + hl;
+    const int p0 = (slice % SPH) * 16;
     const int64_t bh = (int64_t)b * H + h;
     const int k0 = (int)(((int64_t)seg * a.nsub) / S);
     const int k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     const int log2R = a.log2R;
     const int Qt = a.Qt;
+    // wave w < nhb scans the decays of head hfirst + w
+    const bool scanner = wv < nhb;
 
-    // ---- global addressing: uniform per-tile bases + fixed 32-bit lane offsets
-    const TI* xg = static_cast<const TI*>(a.x) + ((int64_t)b * TR * H + h) * P;
-    const TI* Bg = static_cast<const TI*>(a.B) + ((int64_t)b * TR * G + grp) * N;
-    const TI* Cg = static_cast<const TI*>(a.C) + ((int64_t)b * TR * G + grp) * N;
-    const float* dag = a.da + (int64_t)b * T * H + h;
-    float* yg = a.y + ((int64_t)b * TR * H + h) * P;
-    const int64_t xrow_el = H * P, brow_el = G * N;    // elements between fused rows
-    uint32_t xgoff[XPT], bgoff[BPT];
-    int xloff[XPT], bloff[BPT], cloff[BPT];
+    // ---- global addressing: one buffer resource per stream spanning the
+    // segment's valid rows, and per lane a fixed 32-bit offset advanced by a
+    // per-tile step. Rows past the segment (ragged tail, tiles prefetched
+    // beyond k1) fall outside the resource: loads return 0, stores are
+    // dropped. The host keeps every segment's span below 2^30 bytes.
+    const int64_t xrow_el = H * P, brow_el = G * N;
+    const int64_t row0 = (int64_t)k0 * F;
+    const int64_t row_end = ((int64_t)k1 * F < TR) ? (int64_t)k1 * F : TR;
+    const int64_t vrows = row_end - row0;                    // >= 1
+    const int64_t step0 = (int64_t)k0 * Qt;
+    const int64_t vsteps = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - step0;
+    const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
+                                (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
+    const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
+    const auto rs_b = make_rsrc(static_cast<const TI*>(a.B) + (b * TR + row0) * brow_el + grp * N, bspan);
+    const auto rs_c = make_rsrc(static_cast<const TI*>(a.C) + (b * TR + row0) * brow_el + grp * N, bspan);
+    const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
+                                 OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
+    const auto rs_da = make_rsrc(a.da + (b * T + step0) * H + hfirst + (scanner ? wv : 0),
+                                 (uint32_t)(((vsteps - 1) * H + 1) * 4));
+    const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0,
+                                (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
+    const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ), bstep = (uint32_t)(F * brow_el * ESZ);
+    const uint32_t ystep = (uint32_t)(F * xrow_el * 4), dastep = (uint32_t)(Qt * H * 4);
+
+    uint32_t xgoff[XPT], bgoff[BPT], cbgoff[CBPT], ygoff[YPT];
+    int xloff[XPT], bloff[BPT], cloff[BPT], cbloff[CBPT], yloff[YPT];
 #pragma unroll
     for (int m = 0; m < XPT; ++m) {
         const int u = tid + m * NT;
@@ -894,28 +1006,28 @@ __global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
         bloff[m] = (u < BU) ? r * LDB + col : F * LDB;
         cloff[m] = (u < BU) ? r * LDC + col : F * LDC;
     }
-    // decay-matrix blocks: wave w < 3 prefetches block w (W >= 3)
-    const float* cbg = OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub) * 768 : nullptr;
-    const uint32_t cboff = (uint32_t)((wv * 256 + lane * 4) * 4);
-    // da: lane f < 32 of a scanning wave reads da at step f >> log2R for the
-    // first rank of each step, so the scan over fused rows yields cum per row
-    const bool da_lane = (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
-    const uint32_t daoff = da_lane ? (uint32_t)((lane >> log2R) * H * 4) : kOOB;
-    uint32_t yoff[2];
 #pragma unroll
-    for (int I = 0; I < 2; ++I) yoff[I] = (uint32_t)(((16 * I + l16) * xrow_el + p0 + 4 * q) * 4);
+    for (int m = 0; m < CBPT; ++m) {
+        const int u = tid + m * NT;
+        cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
+        cbloff[m] = (u < CBU) ? u * 4 : 768;
+    }
+#pragma unroll
+    for (int m = 0; m < YPT; ++m) {
+        const int u = tid + m * NT;
+        const int r = u / YUR, col = (u % YUR) * 4;
+        ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
+        yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
+    }
+    // da: lane f < 32 of a scanning wave reads step f >> log2R for the first
+    // rank of each step, so the scan over fused rows yields cum per row
+    const bool da_lane = scanner && (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
+    const uint32_t daoff = da_lane ? (uint32_t)((lane >> log2R) * H * 4) : kOOB;
+    // this wave's y fragment in the staged block: rows 16 I + l16, columns
+    // 16 wv + 4 q .. + 3
+    const int ysoff = l16 * LDY + 16 * wv + 4 * q;
 
-    // rows of tile k inside this segment (0 past its end)
-    auto valid_rows = [&](int k) -> int {
-        if (k >= k1) return 0;
-        const int64_t v = TR - (int64_t)k * F;
-        return v >= F ? F : (int)v;
-    };
-    auto span = [&](int vr, int64_t row_el, int64_t tail_el, int esz) -> uint32_t {
-        return vr > 0 ? (uint32_t)(((vr - 1) * row_el + tail_el) * esz) : 0u;
-    };
-
-    // ---- state (physical frame; S > 1 reads the carried state of the segment)
+    // ---- state (physical frame)
     f32x4 hs[NTILE];
     {
         const float* src = nullptr;
@@ -934,109 +1046,111 @@ __global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
             }
         }
     }
-    const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
     float lam = 0.f;
 
-    // ---- register prefetch: x (streamed from HBM) NS tiles ahead in a ring,
-    // B / C / CB / da (shared by the heads, mostly L2 hits) one tile ahead
-    uint4 rx[NS][XPT], rb[BPT], rc[BPT];
-    float4 rcb;
-    float rda;
+    // register staging (two slots): x, B, C of tile t in slot t & 1, and the
+    // C B^T block and da of tile t in slot t & 1, issued one tile earlier
+    uint4 rx[2][XPT], rb[2][BPT], rc[2][BPT];
+    float4 rcb[2][CBPT];
+    float rda[2];
 
-    auto load_x = [&](int slot, int k) {
-        const int vr = valid_rows(k);
-        const auto rs = make_rsrc(xg + (int64_t)k * F * xrow_el, span(vr, xrow_el, P, ESZ));
+    // k is a tile index relative to the segment start
+    auto load_xbc = [&](int slot, int k) {
+        const uint32_t ox = (uint32_t)k * xstep, ob = (uint32_t)k * bstep;
 #pragma unroll
         for (int m = 0; m < XPT; ++m)
-            rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, xgoff[m], 0, 2));
-    };
-    auto load_shared = [&](int k) {
-        const int vr = valid_rows(k);
-        const uint32_t nb = span(vr, brow_el, N, ESZ);
-        const auto rsb = make_rsrc(Bg + (int64_t)k * F * brow_el, nb);
+            rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + ox, 0, 2));
 #pragma unroll
         for (int m = 0; m < BPT; ++m)
-            rb[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsb, bgoff[m], 0, 0));
+            rb[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bgoff[m] + ob, 0, 0));
         if (OUT) {
-            const auto rsc = make_rsrc(Cg + (int64_t)k * F * brow_el, nb);
 #pragma unroll
             for (int m = 0; m < BPT; ++m)
-                rc[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsc, bgoff[m], 0, 0));
-            if (W >= 3) {
-                const auto rscb = make_rsrc(cbg + (int64_t)k * 768, k < k1 ? 768 * 4 : 0);
-                rcb = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                     rscb, wv < 3 ? cboff : kOOB, 0, 0));
-            }
+                rc[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, bgoff[m] + ob, 0, 0));
         }
-        int vt = 0;
-        if (k < k1) {
-            const int64_t v = T - (int64_t)k * Qt;
-            vt = v >= Qt ? Qt : (int)v;
-        }
-        const auto rsd = make_rsrc(dag + (int64_t)k * Qt * H, vt > 0 ? (uint32_t)(((vt - 1) * H + 1) * 4) : 0u);
-        rda = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rsd, daoff, 0, 0));
     };
-
-    // Write a prefetched tile into LDS buffer `buf`, and build its per-row
-    // vectors and decay matrix.
-    auto store = [&](int slot, int buf, int k) {
+    auto load_cbda = [&](int slot, int k) {
+        if (OUT) {
+            const uint32_t ocb = (uint32_t)k * (768 * 4);
+#pragma unroll
+            for (int m = 0; m < CBPT; ++m)
+                rcb[slot][m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs_cb, cbgoff[m] + ocb, 0, 0));
+        }
+        rda[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_da, daoff + (uint32_t)k * dastep, 0, 0));
+    };
+    auto store_xbc = [&](int slot, int buf) {
 #pragma unroll
         for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
 #pragma unroll
         for (int m = 0; m < BPT; ++m) {
-            *reinterpret_cast<uint4*>(&sB[buf][bloff[m]]) = rb[m];
-            if (OUT) *reinterpret_cast<uint4*>(&sC[buf][cloff[m]]) = rc[m];
+            *reinterpret_cast<uint4*>(&sB[buf][bloff[m]]) = rb[slot][m];
+            if (OUT) *reinterpret_cast<uint4*>(&sC[buf][cloff[m]]) = rc[slot][m];
         }
-        // K1: inclusive prefix of da over the tile's fused rows
-        const bool scan_wave = (wv == 0) || (OUT && wv < 3);
-        if (scan_wave) {
-            const float cum = wave_prefix32(rda);
-            const float last = __shfl(cum, F - 1);
-            if (wv == 0) {
-                if (lane < F) {
-                    sEin[buf][lane] = __expf(cum);
-                    sW[buf][lane] = __expf(last - cum);
-                }
-                if (lane == 0) {
-                    sCarry[buf] = __expf(last);
-                    lam += last;
-                }
-            }
-            if (OUT) {
-                // decay matrix blocks M = CB^T o L (+ D on the diagonal)
-                for (int blk = wv; blk < 3; blk += W) {
-                    float4 cbv;
-                    if (W >= 3) {
-                        cbv = rcb;
-                    } else {
-                        const auto rscb = make_rsrc(cbg + (int64_t)k * 768, k < k1 ? 768 * 4 : 0);
-                        cbv = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                             rscb, (uint32_t)((blk * 256 + lane * 4) * 4), 0, 0));
-                    }
-                    const int J = blk == 2 ? 1 : 0, I = blk == 0 ? 0 : 1;
-                    const int i = 16 * I + l16;
-                    const float ci = __shfl(cum, i);
-                    const int ti = i >> log2R;
-                    float mv[4];
+    };
+    // C B^T block of tile k into LDS; K1 (prefix of da over the tile's fused
+    // rows, in base 2) by the scanning waves
+    auto store_cbda = [&](int slot, int k) {
+        if (OUT) {
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int j = 16 * J + 4 * q + v;
-                        const float cj = __shfl(cum, j);
-                        mv[v] = (ti >= (j >> log2R)) ? cbv[v] * __expf(ci - cj) : 0.f;
-                        if (i == j) mv[v] += Dh;
-                    }
-                    sM[buf][blk * 64 + lane] = pack_m<TI>(mv[0], mv[1], mv[2], mv[3]);
+            for (int m = 0; m < CBPT; ++m) *reinterpret_cast<float4*>(&sCB[k & 1][cbloff[m]]) = rcb[slot][m];
+        }
+        if (scanner) {
+            const float cum = wave_prefix32(rda[slot]);
+            const float last = __shfl(cum, F - 1);
+            const float c2 = cum * kLog2e, l2 = last * kLog2e;
+            if (lane < F) {
+                sCum[k & 3][wv][lane] = c2;
+                sEin[k & 3][wv][lane] = __builtin_amdgcn_exp2f(c2);
+                sW[k & 3][wv][lane] = __builtin_amdgcn_exp2f(l2 - c2);
+            }
+            if (lane == 0) sCarry[k & 3][wv] = __builtin_amdgcn_exp2f(l2);
+            lam += last;
+        }
+    };
+    // Decay matrices M = C B^T o L (+ D on the diagonal) of tile k for every
+    // head of the block, one (head, 16x16 block) unit per wave: element
+    // (j = 16 J + 4 q + v, i = 16 I + l16) of blocks (0,0), (0,1), (1,1).
+    auto build_m = [&](int k) {
+        if (OUT) {
+            for (int u = wv; u < 3 * nhb; u += W) {
+                const int uh = u / 3, blk = u - 3 * uh;
+                const int J = blk == 2 ? 1 : 0, I = blk == 0 ? 0 : 1;
+                const float* cum = sCum[k & 3][uh];
+                const float4 cb = *reinterpret_cast<const float4*>(&sCB[k & 1][blk * 256 + lane * 4]);
+                const float4 cj = *reinterpret_cast<const float4*>(&cum[16 * J + 4 * q]);
+                const int i = 16 * I + l16;
+                const float ci = cum[i];
+                const float Du = a.D ? a.D[hfirst + uh] : 0.f;
+                const float cbv[4] = {cb.x, cb.y, cb.z, cb.w}, cjv[4] = {cj.x, cj.y, cj.z, cj.w};
+                float mv[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int j = 16 * J + 4 * q + v;
+                    mv[v] = ((i >> log2R) >= (j >> log2R)) ? cbv[v] * __builtin_amdgcn_exp2f(ci - cjv[v]) : 0.f;
+                    if (i == j) mv[v] += Du;
                 }
+                sM[k & 1][u * 64 + lane] = pack_m<TI>(mv[0], mv[1], mv[2], mv[3]);
+            }
+        }
+    };
+    // Global stores of the y block staged in sY[buf] by tile k.
+    auto flush_y = [&](int buf, int k) {
+        if (OUT) {
+            const uint32_t o = (uint32_t)k * ystep;
+#pragma unroll
+            for (int m = 0; m < YPT; ++m) {
+                const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 0);
             }
         }
     };
 
     auto compute = [&](int buf, int k) {
-        const TI* tX = sX[buf];
         const TI* tB = sB[buf];
-        // x^T operand: rows j in {4q..4q+3} and {16+4q..16+4q+3}, column p0 + i
-        const frag xa = RowRuns<TI>::load(tX, LDX, 4 * q, 16 + 4 * q, p0 + 4 * (lane & 3),
-                                          p0 + l16, lane);
+        const int vb = k & 3;
+        // x^T operand: rows j in {4q..4q+3} and {16+4q..16+4q+3}, column 16 wv + i
+        const frag xa = RowRuns<TI>::load(sX[buf], LDX, 4 * q, 16 + 4 * q, 16 * wv + 4 * (lane & 3),
+                                          16 * wv + l16, lane);
         if (OUT) {
             const TI* tC = sC[buf];
             f32x4 yacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -1052,30 +1166,30 @@ __global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
                 yacc[0] = O::mma(hA, O::ld8(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
                 yacc[1] = O::mma(hA, O::ld8(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
             }
-            const float e0 = sEin[buf][l16], e1 = sEin[buf][16 + l16];
+            const float e0 = sEin[vb][hl][l16], e1 = sEin[vb][hl][16 + l16];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 yacc[0][v] *= e0;
                 yacc[1][v] *= e1;
             }
-            const mblk m00 = sM[buf][lane], m01 = sM[buf][64 + lane], m11 = sM[buf][128 + lane];
+            const mblk* mb = &sM[k & 1][hl * 3 * 64 + lane];
+            const mblk m00 = mb[0], m01 = mb[64], m11 = mb[128];
             const mblk zz = pack_m<TI>(0.f, 0.f, 0.f, 0.f);
             yacc[0] = O::mma(xa, join_m<TI>(m00, zz), yacc[0]);
             yacc[1] = O::mma(xa, join_m<TI>(m01, m11), yacc[1]);
-            const auto rsy = make_rsrc(yg + (int64_t)k * F * xrow_el, span(valid_rows(k), xrow_el, P, 4));
 #pragma unroll
             for (int I = 0; I < 2; ++I)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, yacc[I]), rsy, yoff[I], 0, 0);
+                *reinterpret_cast<f32x4*>(&sY[buf][ysoff + 16 * I * LDY]) = yacc[I];
         }
-        // K3 + K4 with the same time order as the x^T operand
+        // K3 + K4: decay the state over the tile and add the tile's writes
         float xv[8];
         O::unpack(xa, xv);
-        const float4 w0 = *reinterpret_cast<const float4*>(&sW[buf][4 * q]);
-        const float4 w1 = *reinterpret_cast<const float4*>(&sW[buf][16 + 4 * q]);
+        const float4 w0 = *reinterpret_cast<const float4*>(&sW[vb][hl][4 * q]);
+        const float4 w1 = *reinterpret_cast<const float4*>(&sW[vb][hl][16 + 4 * q]);
         xv[0] *= w0.x; xv[1] *= w0.y; xv[2] *= w0.z; xv[3] *= w0.w;
         xv[4] *= w1.x; xv[5] *= w1.y; xv[6] *= w1.z; xv[7] *= w1.w;
         const frag xw = O::pack(xv);
-        const float carry = sCarry[buf];
+        const float carry = sCarry[vb][hl];
 #pragma unroll
         for (int t = 0; t < NTILE; ++t) {
             // B^T operand rows n = phi(t, i): column base for 4-lane group a
@@ -1088,33 +1202,50 @@ __global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
         }
     };
 
-    // ---- pipeline. Tile k is computed from LDS buffer (k - k0) & 1 while tile
-    // k+1 is staged into the other one; one barrier per tile. Memory counters
-    // retire in issue order, so each step issues the loads it waits on next
-    // (shared B/C, one tile ahead) before the far x prefetch and the y stores.
-    // Tiles are walked in pairs; a tile past the segment end loads zeros
-    // (da = 0, x = 0), which leaves the state unchanged, and stores nothing.
-    load_x(0, k0);
-    load_x(1, k0 + 1);
-    load_shared(k0);
-    store(0, 0, k0);
-    load_shared(k0 + 1);
-    load_x(0, k0 + NS);
+    // ---- pipeline, tile indices relative to k0. x, B and C are staged in
+    // registers two tiles ahead and in LDS one tile ahead (buffer = tile
+    // parity); da and C B^T run one tile further ahead, so that the decay
+    // matrices of tile k+1 are built, once per head, while tile k is computed.
+    // y of tile k leaves from LDS during tile k + 1. One barrier per tile.
+    // Memory counters retire in issue order, and each step waits only for
+    // the oldest group in flight. Tiles are walked in pairs; a tile past the
+    // segment end loads zeros (da = 0, x = 0: the state is unchanged) and
+    // stores nothing. The first flush (tile -1) wraps to an offset beyond
+    // every resource and is dropped.
+    const int nk = k1 - k0;
+    load_xbc(0, 0);
+    load_cbda(0, 0);
+    load_cbda(1, 1);
+    load_xbc(1, 1);
+    store_xbc(0, 0);
+    store_cbda(0, 0);
+    load_cbda(0, 2);
+    store_cbda(1, 1);
+    load_xbc(0, 2);
+    load_cbda(1, 3);
     __syncthreads();
-    for (int k = k0; k < k1; k += 2) {
-        // tile k (buffer 0), staging tile k+1 into buffer 1
-        store(1, 1, k + 1);
-        load_shared(k + 2);
-        load_x(1, k + 1 + NS);
+    build_m(0);
+    __syncthreads();
+    int k = 0;
+    for (; k < nk; k += 2) {
+        store_xbc(1, 1);             // x, B, C of tile k+1
+        store_cbda(0, k + 2);
+        build_m(k + 1);
+        flush_y(1, k - 1);
+        load_xbc(1, k + 3);
+        load_cbda(0, k + 4);
         compute(0, k);
         __syncthreads();
-        // tile k+1 (buffer 1), staging tile k+2 into buffer 0
-        store(0, 0, k + 2);
-        load_shared(k + 3);
-        load_x(0, k + 2 + NS);
+        store_xbc(0, 0);             // x, B, C of tile k+2
+        store_cbda(1, k + 3);
+        build_m(k + 2);
+        flush_y(0, k);
+        load_xbc(0, k + 4);
+        load_cbda(1, k + 5);
         compute(1, k + 1);
         __syncthreads();
     }
+    flush_y(1, k - 1);
 
     // ---- epilogue
     float* dstate = nullptr;
@@ -1122,7 +1253,8 @@ __global__ __launch_bounds__(4 * P) void ssd_tiles_kernel(TileArgs a) {
         if (seg == S - 1) dstate = a.final_state + bh * P * N;
     } else {
         dstate = a.ws_state + (bh * S + seg + 1) * P * N;
-        if (tid == 0) a.ws_misc[(bh * S + seg) * (1 + N / 2)] = lam;
+        // Lambda of the segment, by the wave that scanned the head
+        if (scanner && lane == 0) a.ws_misc[(((int64_t)b * H + hfirst + wv) * S + seg) * (1 + N / 2)] = lam;
     }
     if (dstate) {
 #pragma unroll
@@ -1207,51 +1339,47 @@ void* walk_ptr_p(int P, int NP) {
     return nullptr;
 }
 
-// Static LDS bytes of ssd_tiles_kernel<TI, P, NP, MODE> (mirrors its arrays).
-template <typename TI, int P, int NP, int MODE>
-constexpr int tiles_lds_bytes() {
-    constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows;
-    constexpr int ldx = P + Ops<TI>::kPad, ldb = tr_row_stride<TI>(NP), ldc = NP + Ops<TI>::kPad;
-    constexpr int out = MODE == 0;
-    return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
-           (out ? 2 * (F * ldc + epu) * esz + 2 * 3 * 64 * 2 * esz * 4 / 2 : 0) + 2 * 2 * F * 4 + 2 * 4;
-}
-
 constexpr int kLdsLimit = 160 * 1024;
 
-template <typename TI, int P, int NP, int MODE>
-void* tiles_ptr() {
-    if constexpr (tiles_lds_bytes<TI, P, NP, MODE>() <= kLdsLimit)
-        return reinterpret_cast<void*>(&ssd_tiles_kernel<TI, P, NP, MODE>);
+// Column-block widths (16-column slices per workgroup), preferred first.
+constexpr int kColsWidths[] = {12, 10, 8, 6, 4, 2, 1};
+
+template <typename TI, int NP, int W, int MODE>
+void* cols_ptr() {
+    if constexpr (cols_lds_bytes<TI, NP, W>(MODE) <= kLdsLimit)
+        return reinterpret_cast<void*>(&ssd_cols_kernel<TI, NP, W, MODE>);
     else
-        return nullptr;  // does not fit one CU's LDS: the caller uses the general tile walk
+        return nullptr;  // does not fit one CU's LDS
 }
 
-template <typename TI, int P, int MODE>
-void* tiles_ptr_np(int NP) {
+template <typename TI, int W, int MODE>
+void* cols_ptr_np(int NP) {
     switch (NP) {
-        case 32: return tiles_ptr<TI, P, 32, MODE>();
-        case 64: return tiles_ptr<TI, P, 64, MODE>();
-        case 128: return tiles_ptr<TI, P, 128, MODE>();
-        case 256: return tiles_ptr<TI, P, 256, MODE>();
+        case 32: return cols_ptr<TI, 32, W, MODE>();
+        case 64: return cols_ptr<TI, 64, W, MODE>();
+        case 128: return cols_ptr<TI, 128, W, MODE>();
+        case 256: return cols_ptr<TI, 256, W, MODE>();
     }
     return nullptr;
 }
 
 template <typename TI, int MODE>
-void* tiles_ptr_p(int P, int NP) {
-    switch (P) {
-        case 16: return tiles_ptr_np<TI, 16, MODE>(NP);
-        case 32: return tiles_ptr_np<TI, 32, MODE>(NP);
-        case 64: return tiles_ptr_np<TI, 64, MODE>(NP);
-        case 128: return tiles_ptr_np<TI, 128, MODE>(NP);
+void* cols_ptr_w(int w, int NP) {
+    switch (w) {
+        case 1: return cols_ptr_np<TI, 1, MODE>(NP);
+        case 2: return cols_ptr_np<TI, 2, MODE>(NP);
+        case 4: return cols_ptr_np<TI, 4, MODE>(NP);
+        case 6: return cols_ptr_np<TI, 6, MODE>(NP);
+        case 8: return cols_ptr_np<TI, 8, MODE>(NP);
+        case 10: return cols_ptr_np<TI, 10, MODE>(NP);
+        case 12: return cols_ptr_np<TI, 12, MODE>(NP);
     }
     return nullptr;
 }
 
-void* select_tiles(int dtype, int mode, int P, int NP) {
-    if (dtype == SSD_BF16) return mode ? tiles_ptr_p<uint16_t, 1>(P, NP) : tiles_ptr_p<uint16_t, 0>(P, NP);
-    return mode ? tiles_ptr_p<float, 1>(P, NP) : tiles_ptr_p<float, 0>(P, NP);
+void* select_cols(int dtype, int mode, int w, int NP) {
+    if (dtype == SSD_BF16) return mode ? cols_ptr_w<uint16_t, 1>(w, NP) : cols_ptr_w<uint16_t, 0>(w, NP);
+    return mode ? cols_ptr_w<float, 1>(w, NP) : cols_ptr_w<float, 0>(w, NP);
 }
 
 template <typename TI>
@@ -1274,9 +1402,13 @@ void* select_walk(int dtype, bool rot, int mode, int P, int NP) {
     return mode ? walk_ptr_p<float, false, 1>(P, NP) : walk_ptr_p<float, false, 0>(P, NP);
 }
 
+enum PathKind { kWalkPath = 0, kColsPath = 1 };
+
 struct Plan {
     int64_t b, T, H, P, N, G, R, NP;
     int dtype, S, nsub, Qt, log2R;
+    int kind;  // PathKind
+    int W;     // column-block width in 16-column slices (column-block walk)
 };
 
 bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
@@ -1315,9 +1447,11 @@ ssd_status check_shape(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has
     return SSD_OK;
 }
 
-int auto_segments(int64_t bh, int nsub) {
-    // fill the chip: aim at >= 512 workgroups, but keep >= 4 tiles per segment
-    int64_t want = (512 + bh - 1) / bh;
+// Segments per sequence: aim at >= `target` workgroups of `units` per
+// segment, but keep >= 4 tiles per segment (each segment boundary costs a
+// state-only pass over the preceding tiles).
+int auto_segments(int64_t units, int nsub, int64_t target) {
+    int64_t want = (target + units - 1) / units;
     int64_t cap = nsub / 4;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;
@@ -1344,7 +1478,33 @@ WsLayout workspace_layout(const Plan& pl, bool no_pack) {
     return w;
 }
 
-Plan make_plan(const ssd_dims* d, int64_t R, int segments) {
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    return n;
+}
+
+// Most heads one block of w slices touches within a group.
+int64_t block_heads(const Plan& pl, int w) {
+    const int64_t sph = pl.P / 16, nb = (pl.H / pl.G) * sph / w;
+    int64_t most = 0;
+    for (int64_t j = 0; j < nb && j < sph; ++j) {   // the pattern repeats every sph blocks
+        const int64_t n = (j * w + w - 1) / sph - (j * w) / sph + 1;
+        if (n > most) most = n;
+    }
+    return most;
+}
+
+bool cols_ok(const Plan& pl, int w) {
+    const int64_t slices = (pl.H / pl.G) * (pl.P / 16);
+    return w >= 1 && slices % w == 0 && block_heads(pl, w) <= cols_max_heads(w) &&
+           select_cols(pl.dtype, 0, w, (int)pl.NP) && select_cols(pl.dtype, 1, w, (int)pl.NP);
+}
+
+// Kernel path, column-block width and segments. `w_req` and `segments` are
+// the caller's launch options (0 = automatic).
+ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w_req, Plan* out) {
     Plan pl;
     pl.b = d->batch; pl.T = d->seqlen; pl.H = d->nheads; pl.P = d->headdim;
     pl.N = d->dstate; pl.G = d->ngroups; pl.R = R;
@@ -1354,22 +1514,64 @@ Plan make_plan(const ssd_dims* d, int64_t R, int segments) {
     pl.log2R = 0;
     while ((1 << pl.log2R) < R) ++pl.log2R;
     pl.nsub = (int)((pl.T * R + kRows - 1) / kRows);
-    pl.S = segments > 0 ? segments : auto_segments(pl.b * pl.H, pl.nsub);
+    pl.kind = kWalkPath;
+    pl.W = 0;
+
+    // the column-block walk addresses a segment with 32-bit offsets: keep
+    // each segment, with the tiles prefetched past its end, under 2^30 bytes
+    const int64_t esz = pl.dtype == SSD_BF16 ? 2 : 4;
+    const int64_t row_bytes = pl.H * pl.P * 4 > pl.G * pl.N * esz ? pl.H * pl.P * 4 : pl.G * pl.N * esz;
+    const int64_t max_tiles = ((int64_t)1 << 30) / (kRows * row_bytes) - 4;
+    const int cus = device_cus();
+    if (!rot && max_tiles >= 1) {
+        const int64_t slices = pl.b * pl.G * (pl.H / pl.G) * (pl.P / 16);
+        if (w_req > 0) {
+            if (!cols_ok(pl, w_req)) return SSD_ERR_UNSUPPORTED;
+            pl.W = w_req;
+        } else {
+            // the widest block that still gives every CU a workgroup, else
+            // the narrowest (segments then add workgroups)
+            for (int w : kColsWidths) {
+                if (!cols_ok(pl, w)) continue;
+                if (pl.W == 0 || slices / w >= cus) pl.W = w;
+                if (slices / w >= cus) break;
+            }
+        }
+        if (pl.W > 0) pl.kind = kColsPath;
+    } else if (w_req > 0 && !rot) {
+        return SSD_ERR_UNSUPPORTED;
+    }
+    int64_t min_segments = 1, units = pl.b * pl.H, target = 2 * cus;
+    if (pl.kind == kColsPath) {
+        min_segments = (pl.nsub + max_tiles - 1) / max_tiles;
+        units = pl.b * pl.H * (pl.P / 16) / pl.W;
+        target = cus;
+    }
+    pl.S = segments > 0 ? segments : auto_segments(units, pl.nsub, target);
     if (pl.S > pl.nsub) pl.S = pl.nsub;
+    if (pl.S < min_segments) pl.S = (int)min_segments;
     if (pl.S < 1) pl.S = 1;
-    return pl;
+    *out = pl;
+    return SSD_OK;
 }
 
-// Tile walks: `shared` selects the shared-B/C kernel (ssd_tiles_kernel), else
-// the general walk (ssd_walk_kernel, which also handles rotation).
+// Tile walks: the column-block walk (ssd_cols_kernel, shared B/C) or the
+// general walk (ssd_walk_kernel, which also handles rotation).
 template <typename Args>
-ssd_status launch_walk(const Plan& pl, int mode, bool shared, bool rot, const Args& args, hipStream_t st) {
-    void* fn = shared ? select_tiles(pl.dtype, mode, (int)pl.P, (int)pl.NP)
-                      : select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
+ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hipStream_t st) {
+    void* fn = nullptr;
+    int64_t nwg = pl.b * pl.H * args.seg_items;
+    unsigned threads = (unsigned)(4 * pl.P);
+    if (pl.kind == kColsPath) {
+        fn = select_cols(pl.dtype, mode, pl.W, (int)pl.NP);
+        nwg = pl.b * args.seg_items * pl.H * (pl.P / 16) / pl.W;
+        threads = (unsigned)(64 * pl.W);
+    } else {
+        fn = select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
+    }
     if (!fn) return SSD_ERR_UNSUPPORTED;
-    const int64_t nwg = pl.b * pl.H * args.seg_items;
     if (nwg < 1 || nwg > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
-    dim3 grid((unsigned)nwg), block((unsigned)(4 * pl.P));
+    dim3 grid((unsigned)nwg), block(threads);
     Args a = args;
     void* kargs[] = {&a};
     if (hipLaunchKernel(fn, grid, block, kargs, 0, st) != hipSuccess) return SSD_ERR_HIP;
@@ -1378,12 +1580,11 @@ ssd_status launch_walk(const Plan& pl, int mode, bool shared, bool rot, const Ar
 
 // Pass A (segment end states), pass B (carry), pass C (outputs).
 template <typename Args>
-ssd_status run_passes(const Plan& pl, bool shared, bool rot, Args args, const float* init_state,
-                      hipStream_t hs) {
+ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs) {
     ssd_status rs = SSD_OK;
     if (pl.S > 1) {
         args.seg_items = pl.S - 1;
-        rs = launch_walk(pl, 1, shared, rot, args, hs);
+        rs = launch_walk(pl, 1, rot, args, hs);
         if (rs == SSD_OK) {
             dim3 grid((unsigned)((pl.P * (pl.N / 2) + 255) / 256), (unsigned)(pl.b * pl.H));
             hipLaunchKernelGGL(ssd_carry_kernel, grid, dim3(256), 0, hs, init_state, args.ws_state,
@@ -1393,7 +1594,7 @@ ssd_status run_passes(const Plan& pl, bool shared, bool rot, Args args, const fl
     }
     if (rs == SSD_OK) {
         args.seg_items = pl.S;
-        rs = launch_walk(pl, 0, shared, rot, args, hs);
+        rs = launch_walk(pl, 0, rot, args, hs);
     }
     return rs;
 }
@@ -1416,7 +1617,9 @@ const char* ssd_status_str(int32_t status) {
 
 size_t ssd_workspace_bytes(const ssd_dims* d, int64_t chunk_len, int64_t R) {
     if (!d || check_shape(d, chunk_len, R, false) != SSD_OK) return 0;
-    return workspace_layout(make_plan(d, R, 0), false).total;
+    Plan pl;
+    if (make_plan(d, R, false, 0, 0, &pl) != SSD_OK) return 0;
+    return workspace_layout(pl, pl.kind == kWalkPath).total;
 }
 
 ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, const void* B,
@@ -1427,8 +1630,8 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     ssd_status st = check_shape(d, chunk_len, R, theta != nullptr);
     if (st != SSD_OK) return st;
     if (opts) {
-        if (opts->segments < 0) return SSD_ERR_BAD_SHAPE;
-        for (int i = 0; i < 7; ++i)
+        if (opts->segments < 0 || opts->block_slices < 0) return SSD_ERR_BAD_SHAPE;
+        for (int i = 0; i < 6; ++i)
             if (opts->reserved[i] != 0) return SSD_ERR_BAD_SHAPE;
     }
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
@@ -1454,13 +1657,14 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
         if (!same_state && overlap(sf, ins[i])) return SSD_ERR_ALIAS;
     }
 
-    const Plan pl = make_plan(d, R, opts ? opts->segments : 0);
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     const bool rot = theta != nullptr;
+    Plan pl;
+    st = make_plan(d, R, rot, opts ? opts->segments : 0, opts ? opts->block_slices : 0, &pl);
+    if (st != SSD_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
-    // shared-B/C kernels when there is no rotation and the tile fits in LDS
-    const bool shared = !rot && select_tiles(pl.dtype, 0, (int)pl.P, (int)pl.NP) != nullptr &&
-                        select_tiles(pl.dtype, 1, (int)pl.P, (int)pl.NP) != nullptr;
+    // shared-B/C column-block walk unless rotation (or the shape) needs the general walk
+    const bool shared = pl.kind == kColsPath;
     const WsLayout wl = workspace_layout(pl, !shared);
     void* ws = nullptr;
     if (wl.total) {
@@ -1480,7 +1684,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
         args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
         args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
         args.ws_state = ws_state; args.ws_misc = ws_misc;
-        rs = run_passes(pl, false, rot, args, init_state, hs);
+        rs = run_passes(pl, rot, args, init_state, hs);
     } else {
         // K2 once per (batch, group, tile), shared by every head of the group
         void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
@@ -1500,10 +1704,11 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             memset(&args, 0, sizeof(args));
             args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
             args.init = init_state; args.y = y; args.final_state = final_state;
-            args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
+            args.T = T; args.H = H; args.G = G; args.N = N; args.R = R; args.P = P;
             args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
             args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
-            rs = run_passes(pl, true, false, args, init_state, hs);
+            args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
+            rs = run_passes(pl, false, args, init_state, hs);
         }
     }
     if (ws) {

@@ -90,10 +90,19 @@ typedef enum {
 
 /* Launch choices that do not change the result beyond rounding. */
 typedef struct {
-    int32_t segments;    /* 0: automatic. k >= 1: split every sequence into k
-                            segments that run in parallel, joined by a state
-                            carry pass (clamped to the number of 32-row tiles) */
-    int32_t reserved[7]; /* must be zero */
+    int32_t segments;        /* 0: automatic. k >= 1: split every sequence into k
+                                segments that run in parallel, joined by a state
+                                carry pass (clamped to the number of 32-row tiles) */
+    int32_t block_slices;    /* 0: automatic. k >= 1: each workgroup of the
+                                shared-B/C walk owns k consecutive 16-column
+                                slices of one time row flattened over
+                                (head, headdim) within a B/C group; k must be
+                                1, 2, 4, 6, 8, 10 or 12, divide
+                                (nheads / ngroups) * headdim / 16 and have a
+                                kernel for (dstate, dtype), else
+                                SSD_ERR_UNSUPPORTED. Ignored when theta is given
+                                (rotation uses the per-head walk). */
+    int32_t reserved[6];     /* must be zero */
 } ssd_launch_opts;
 
 /*

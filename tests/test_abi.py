@@ -112,8 +112,14 @@ def test_bad_launch_options(lib):
     opts.segments = -1
     assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
     opts = ssd.SsdLaunchOpts()
+    opts.block_slices = -2
+    assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
     opts.reserved[3] = 1
     assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.block_slices = 7             # not a column-block width
+    assert call(opts=opts) == ssd.SSD_ERR_UNSUPPORTED
 
 
 def test_workspace_bytes(lib):

@@ -36,13 +36,15 @@ def normwise(got, ref):
     return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
 
 
-def run_gpu(inp, chunk_len=None, segments=0, y=None, final_state=None, init_override=None):
+def run_gpu(inp, chunk_len=None, segments=0, y=None, final_state=None, init_override=None,
+            block_slices=0):
     ssd = _ssd()
     g = inp.to(_dev())
     init = g.init_state if init_override is None else init_override
     y, fin = ssd.forward(g.x, g.da, g.B, g.C, g.D, init,
                          inp.shape.chunk_len if chunk_len is None else chunk_len,
-                         g.theta, y=y, final_state=final_state, segments=segments)
+                         g.theta, y=y, final_state=final_state, segments=segments,
+                         block_slices=block_slices)
     torch.cuda.synchronize()
     return y, fin
 
@@ -143,6 +145,33 @@ def test_groups():
     inp = si.make_inputs(shape, seed=21)
     y, fin = run_gpu(inp)
     check_full(inp, y, fin, TOL["f32"], "groups G=3")
+
+
+# Column-block widths of the shared-B/C walk: blocks of W 16-column slices of
+# the (head, headdim)-flattened row, aligned with heads or spanning parts of
+# several heads, within one B/C group or several.
+BLOCKS = [
+    # (P, N, H, G, W, R, dtype, init, segments)
+    (64, 128, 5, 1, 10, 1, "bf16", True, 1),    # blocks of 2.5 heads
+    (64, 128, 5, 1, 4, 2, "bf16", True, 2),     # one head per block
+    (64, 128, 5, 1, 2, 1, "f32", False, 3),     # half a head per block
+    (32, 64, 6, 2, 6, 4, "f32", True, 1),       # 3 heads per block, 2 groups
+    (32, 256, 6, 3, 2, 1, "bf16", True, 2),
+    (16, 32, 8, 2, 2, 1, "f32", True, 1),       # one-slice heads
+    (16, 16, 3, 1, 1, 8, "bf16", False, 2),
+    (128, 64, 3, 1, 12, 1, "bf16", True, 1),    # 1.5 heads per block
+    (128, 128, 2, 1, 4, 2, "f32", True, 2),     # half a head per block
+    (64, 32, 12, 4, 6, 16, "bf16", True, 1),    # 1.5 heads per block, 4 groups
+]
+
+
+@pytest.mark.parametrize("P,N,H,G,W,R,dtype,init,segments", BLOCKS)
+def test_block_widths(P, N, H, G, W, R, dtype, init, segments):
+    shape = si.small_shape(batch=2, seqlen=173, nheads=H, ngroups=G, headdim=P, dstate=N,
+                           mimo_rank=R, dtype=dtype, init_state=init, dt_shift=4.0)
+    inp = si.make_inputs(shape, seed=P + N + H + W)
+    y, fin = run_gpu(inp, segments=segments, block_slices=W)
+    check_full(inp, y, fin, TOL[dtype], f"P{P} N{N} H{H} G{G} W{W} R{R} {dtype} S{segments}")
 
 
 @pytest.mark.parametrize("segments", [1, 2, 3, 7, 64])
