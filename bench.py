@@ -104,7 +104,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=2,
                     help="workload id in ssd_inputs.CONFIGS (the reported line uses 2)")
     ap.add_argument("--cpu-slices", type=int, default=320)

@@ -666,7 +666,7 @@ template <typename TI, int NP>
 __global__ __launch_bounds__(64) void ssd_cb_pack_kernel(const void* __restrict__ Bv,
                                                          const void* __restrict__ Cv,
                                                          float* __restrict__ pack, int64_t TR,
-                                                         int64_t G, int64_t N, int nsub) {
+                                                         int64_t G, int64_t N, int nsub, int log2R) {
     using O = Ops<TI>;
     typedef typename O::frag frag;
     constexpr int KS = NP / 32;
@@ -693,6 +693,13 @@ __global__ __launch_bounds__(64) void ssd_cb_pack_kernel(const void* __restrict_
         c00 = O::mma(b0, c0, c00);
         c01 = O::mma(b0, c1, c01);
         c11 = O::mma(b1, c1, c11);
+    }
+    // causal block mask (step(i) >= step(j)), applied here so that the walk
+    // multiplies by exp2(min(cum_i - cum_j, 0)) without a compare
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        if ((l16 >> log2R) < ((4 * q + v) >> log2R)) c00[v] = 0.f;
+        if (((16 + l16) >> log2R) < ((16 + 4 * q + v) >> log2R)) c11[v] = 0.f;
     }
     f32x4* dst = reinterpret_cast<f32x4*>(pack + tile * 768) + lane;
     dst[0] = c00;
@@ -821,9 +828,11 @@ template <> struct MBlock<float> { typedef float4 type; };
 template <typename TI>
 __device__ __forceinline__ typename MBlock<TI>::type pack_m(float a, float b, float c, float d) {
     if constexpr (sizeof(TI) == 2) {
-        const uint32_t lo = (uint32_t)Ops<uint16_t>::from_f(a) | ((uint32_t)Ops<uint16_t>::from_f(b) << 16);
-        const uint32_t hi = (uint32_t)Ops<uint16_t>::from_f(c) | ((uint32_t)Ops<uint16_t>::from_f(d) << 16);
-        return make_uint2(lo, hi);
+        typedef __attribute__((ext_vector_type(2))) float f32x2;
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 lo = __builtin_convertvector((f32x2){a, b}, bf16x2);
+        const bf16x2 hi = __builtin_convertvector((f32x2){c, d}, bf16x2);
+        return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
     } else {
         return make_float4(a, b, c, d);
     }
@@ -880,12 +889,34 @@ constexpr int y_row_stride(int ncols) {
 
 // Most heads a block of W slices may touch: W / 2 + 1 when every head has at
 // least two slices (headdim >= 32). The host checks the actual count.
+// Row stride (elements) of the staged C tile, read along rows as 16-byte
+// fragments (rows l16 of a 16-lane group). Measured on gfx950: rows whose
+// byte stride is 8 modulo 16 serve these reads without bank conflicts, 16-byte
+// multiples do not (they run at about 60%). Rows are then only 8-byte aligned.
+template <typename TI>
+constexpr int c_row_stride(int ncols) { return ncols + 8 / (int)sizeof(TI); }
+
+// 8 consecutive elements from an 8-byte aligned LDS address, as an MFMA operand.
+template <typename TI>
+__device__ __forceinline__ typename Ops<TI>::frag ld8_a8(const TI* p) {
+    const uint2* q = reinterpret_cast<const uint2*>(p);
+    if constexpr (sizeof(TI) == 2) {
+        const uint2 a = q[0], b = q[1];
+        return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+    } else {
+        const uint2 a = q[0], b = q[1], c = q[2], d = q[3];
+        f32x8 f = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(b.x), __uint_as_float(b.y),
+                   __uint_as_float(c.x), __uint_as_float(c.y), __uint_as_float(d.x), __uint_as_float(d.y)};
+        return f;
+    }
+}
+
 constexpr int cols_max_heads(int W) { return W / 2 + 1; }
 
 template <typename TI, int NP, int W>
 constexpr int cols_lds_bytes(int mode) {
     constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows, CW = 16 * W, MH = cols_max_heads(W);
-    constexpr int ldx = x_row_stride<TI>(CW), ldb = tr_row_stride<TI>(NP), ldc = NP + Ops<TI>::kPad;
+    constexpr int ldx = x_row_stride<TI>(CW), ldb = tr_row_stride<TI>(NP), ldc = c_row_stride<TI>(NP);
     constexpr int mbytes = (int)sizeof(typename MBlock<TI>::type);
     const int out = mode == 0;
     return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
@@ -895,20 +926,26 @@ constexpr int cols_lds_bytes(int mode) {
            4 * MH * (3 * F + 1) * 4;
 }
 
+// Memory waves per workgroup of the column-block walk: they carry the two
+// large HBM streams (x in, y out), so the W compute waves only wait on memory
+// counters for the small, L2-resident B, C, C B^T and da tiles they stage.
+constexpr int cols_mem_waves(int W) { return W >= 4 ? 2 : 1; }
+
 template <typename TI, int NP, int W, int MODE>
-__global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
+__global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(TileArgs a) {
     using O = Ops<TI>;
     typedef typename O::frag frag;
     typedef typename MBlock<TI>::type mblk;
-    constexpr int NT = 64 * W;
+    constexpr int MW = cols_mem_waves(W);
+    constexpr int NTM = 64 * MW;                   // memory threads
+    constexpr int NTC = 64 * W;                    // compute threads
     constexpr int F = kRows;
     constexpr int ESZ = (int)sizeof(TI);
-    constexpr int PAD = O::kPad;
     constexpr int CW = 16 * W;                     // columns per workgroup
     constexpr int MH = cols_max_heads(W);
     constexpr int LDX = x_row_stride<TI>(CW);
     constexpr int LDB = tr_row_stride<TI>(NP);
-    constexpr int LDC = NP + PAD;
+    constexpr int LDC = c_row_stride<TI>(NP);      // rows 8 bytes off 16-byte alignment
     constexpr int LDY = y_row_stride(CW);
     constexpr int NTILE = NP / 16;
     constexpr int KS = NP / 32;
@@ -916,8 +953,8 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     constexpr int EPU = 16 / ESZ;
     constexpr int XUR = CW / EPU, BUR = NP / EPU, YUR = CW / 4;   // 16-byte units per row
     constexpr int XU = F * XUR, BU = F * BUR, CBU = 768 * 4 / 16, YU = F * YUR;
-    constexpr int XPT = (XU + NT - 1) / NT, BPT = (BU + NT - 1) / NT, CBPT = (CBU + NT - 1) / NT;
-    constexpr int YPT = (YU + NT - 1) / NT;
+    constexpr int XPT = (XU + NTM - 1) / NTM, YPT = (YU + NTM - 1) / NTM;          // per memory thread
+    constexpr int BPT = (BU + NTC - 1) / NTC, CBPT = (CBU + NTC - 1) / NTC;        // per compute thread
 
     __shared__ __attribute__((aligned(16))) TI sX[2][F * LDX + EPU];
     __shared__ __attribute__((aligned(16))) TI sB[2][F * LDB + EPU];
@@ -934,6 +971,10 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     // wave index made visibly uniform, so per-head pointers stay scalar
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, l16 = lane & 15;
+    const bool memw = wv >= W;                     // memory wave
+    const int mt = tid - 64 * W;                   // memory thread index (memory waves)
+    const int mw = wv - W;                         // memory wave index
+    const int cwv = memw ? 0 : wv;                 // compute wave index (0 for memory waves)
 
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P;
     const int64_t TR = T * R;
@@ -952,7 +993,7 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     const int hb0 = s0 / SPH;                                    // its head, within the group
     const int nhb = (s0 + W - 1) / SPH - hb0 + 1;                // heads the block touches
     const int64_t hfirst = grp * (H / G) + hb0;
-    const int slice = s0 + wv;                                   // this wave's slice
+    const int slice = s0 + cwv;                                  // this compute wave's slice
     const int hl = slice / SPH - hb0;                            // its head within the block
     const int64_t h = hfirst + hl;
     const int p0 = (slice % SPH) * 16;
@@ -961,46 +1002,105 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     const int k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     const int log2R = a.log2R;
     const int Qt = a.Qt;
-    // wave w < nhb scans the decays of head hfirst + w
-    const bool scanner = wv < nhb;
+    const int nk = k1 - k0;
 
-    // ---- global addressing: one buffer resource per stream spanning the
-    // segment's valid rows, and per lane a fixed 32-bit offset advanced by a
-    // per-tile step. Rows past the segment (ragged tail, tiles prefetched
-    // beyond k1) fall outside the resource: loads return 0, stores are
-    // dropped. The host keeps every segment's span below 2^30 bytes.
+    // Buffer resources span the segment's valid rows; per lane a fixed 32-bit
+    // offset advances by a per-tile step. Rows past the segment (ragged tail,
+    // tiles prefetched beyond k1) fall outside the resource: loads return 0,
+    // stores are dropped. The host keeps every segment's span below 2^30 bytes.
     const int64_t xrow_el = H * P, brow_el = G * N;
     const int64_t row0 = (int64_t)k0 * F;
     const int64_t row_end = ((int64_t)k1 * F < TR) ? (int64_t)k1 * F : TR;
     const int64_t vrows = row_end - row0;                    // >= 1
+
+    if (memw) {
+        // ================= memory waves: x in, y out =================
+        const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
+                                    (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
+        const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0,
+                                    (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
+        const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ), ystep = (uint32_t)(F * xrow_el * 4);
+        uint32_t xgoff[XPT], ygoff[YPT];
+        int xloff[XPT], yloff[YPT];
+#pragma unroll
+        for (int m = 0; m < XPT; ++m) {
+            const int u = mt + m * NTM;
+            const int r = u / XUR, col = (u % XUR) * EPU;
+            xgoff[m] = (u < XU) ? (uint32_t)((r * xrow_el + col) * ESZ) : kOOB;
+            xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
+        }
+#pragma unroll
+        for (int m = 0; m < YPT; ++m) {
+            const int u = mt + m * NTM;
+            const int r = u / YUR, col = (u % YUR) * 4;
+            ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
+            yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
+        }
+        uint4 rx[2][XPT];            // x of tile t in slot t & 1
+        auto load_x = [&](int slot, int k) {
+            const uint32_t o = (uint32_t)k * xstep;
+#pragma unroll
+            for (int m = 0; m < XPT; ++m)
+                rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, 2));
+        };
+        auto store_x = [&](int slot, int buf) {
+#pragma unroll
+            for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
+        };
+        // global stores of the y block staged in sY[buf] by tile k
+        auto flush_y = [&](int buf, int k) {
+            if (OUT) {
+                const uint32_t o = (uint32_t)k * ystep;
+#pragma unroll
+                for (int m = 0; m < YPT; ++m) {
+                    const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 0);
+                }
+            }
+        };
+        // x is staged in registers two tiles ahead and in LDS one tile ahead
+        // (buffer = tile parity). y of tile k leaves from LDS during tile k+1;
+        // the first flush (tile -1) wraps to an offset beyond the resource and
+        // is dropped. Barriers match the compute waves' one for one.
+        load_x(0, 0);
+        load_x(1, 1);
+        store_x(0, 0);
+        load_x(0, 2);
+        __syncthreads();
+        __syncthreads();
+        int k = 0;
+        for (; k < nk; k += 2) {
+            store_x(1, 1);           // tile k+1
+            flush_y(1, k - 1);
+            load_x(1, k + 3);
+            __syncthreads();
+            store_x(0, 0);           // tile k+2
+            flush_y(0, k);
+            load_x(0, k + 4);
+            __syncthreads();
+        }
+        flush_y(1, k - 1);
+        return;
+    }
+
+    // ================= compute waves =================
     const int64_t step0 = (int64_t)k0 * Qt;
     const int64_t vsteps = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - step0;
-    const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
-                                (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
     const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
     const auto rs_b = make_rsrc(static_cast<const TI*>(a.B) + (b * TR + row0) * brow_el + grp * N, bspan);
     const auto rs_c = make_rsrc(static_cast<const TI*>(a.C) + (b * TR + row0) * brow_el + grp * N, bspan);
     const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
                                  OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
+    // wave w < nhb scans the decays of head hfirst + w
+    const bool scanner = wv < nhb;
     const auto rs_da = make_rsrc(a.da + (b * T + step0) * H + hfirst + (scanner ? wv : 0),
                                  (uint32_t)(((vsteps - 1) * H + 1) * 4));
-    const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0,
-                                (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
-    const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ), bstep = (uint32_t)(F * brow_el * ESZ);
-    const uint32_t ystep = (uint32_t)(F * xrow_el * 4), dastep = (uint32_t)(Qt * H * 4);
-
-    uint32_t xgoff[XPT], bgoff[BPT], cbgoff[CBPT], ygoff[YPT];
-    int xloff[XPT], bloff[BPT], cloff[BPT], cbloff[CBPT], yloff[YPT];
-#pragma unroll
-    for (int m = 0; m < XPT; ++m) {
-        const int u = tid + m * NT;
-        const int r = u / XUR, col = (u % XUR) * EPU;
-        xgoff[m] = (u < XU) ? (uint32_t)((r * xrow_el + col) * ESZ) : kOOB;
-        xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
-    }
+    const uint32_t bstep = (uint32_t)(F * brow_el * ESZ), dastep = (uint32_t)(Qt * H * 4);
+    uint32_t bgoff[BPT], cbgoff[CBPT];
+    int bloff[BPT], cloff[BPT], cbloff[CBPT];
 #pragma unroll
     for (int m = 0; m < BPT; ++m) {
-        const int u = tid + m * NT;
+        const int u = tid + m * NTC;
         const int r = u / BUR, col = (u % BUR) * EPU;
         bgoff[m] = (u < BU && col < N) ? (uint32_t)((r * brow_el + col) * ESZ) : kOOB;
         bloff[m] = (u < BU) ? r * LDB + col : F * LDB;
@@ -1008,16 +1108,9 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     }
 #pragma unroll
     for (int m = 0; m < CBPT; ++m) {
-        const int u = tid + m * NT;
+        const int u = tid + m * NTC;
         cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
         cbloff[m] = (u < CBU) ? u * 4 : 768;
-    }
-#pragma unroll
-    for (int m = 0; m < YPT; ++m) {
-        const int u = tid + m * NT;
-        const int r = u / YUR, col = (u % YUR) * 4;
-        ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
-        yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
     }
     // da: lane f < 32 of a scanning wave reads step f >> log2R for the first
     // rank of each step, so the scan over fused rows yields cum per row
@@ -1026,40 +1119,15 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
     // this wave's y fragment in the staged block: rows 16 I + l16, columns
     // 16 wv + 4 q .. + 3
     const int ysoff = l16 * LDY + 16 * wv + 4 * q;
-
-    // ---- state (physical frame)
-    f32x4 hs[NTILE];
-    {
-        const float* src = nullptr;
-        if (OUT) {
-            if (S == 1)
-                src = a.init ? a.init + bh * P * N : nullptr;
-            else
-                src = a.ws_state + (bh * S + seg) * P * N;
-        }
-#pragma unroll
-        for (int t = 0; t < NTILE; ++t) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int n = phi_row(t, 4 * q + v);
-                hs[t][v] = (src && n < N) ? src[(int64_t)(p0 + l16) * N + n] : 0.f;
-            }
-        }
-    }
     float lam = 0.f;
 
-    // register staging (two slots): x, B, C of tile t in slot t & 1, and the
+    // register staging (two slots): B and C of tile t in slot t & 1, and the
     // C B^T block and da of tile t in slot t & 1, issued one tile earlier
-    uint4 rx[2][XPT], rb[2][BPT], rc[2][BPT];
+    uint4 rb[2][BPT], rc[2][BPT];
     float4 rcb[2][CBPT];
     float rda[2];
-
-    // k is a tile index relative to the segment start
-    auto load_xbc = [&](int slot, int k) {
-        const uint32_t ox = (uint32_t)k * xstep, ob = (uint32_t)k * bstep;
-#pragma unroll
-        for (int m = 0; m < XPT; ++m)
-            rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + ox, 0, 2));
+    auto load_bc = [&](int slot, int k) {
+        const uint32_t ob = (uint32_t)k * bstep;
 #pragma unroll
         for (int m = 0; m < BPT; ++m)
             rb[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bgoff[m] + ob, 0, 0));
@@ -1078,13 +1146,16 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
         }
         rda[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_da, daoff + (uint32_t)k * dastep, 0, 0));
     };
-    auto store_xbc = [&](int slot, int buf) {
-#pragma unroll
-        for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
+    auto store_bc = [&](int slot, int buf) {
 #pragma unroll
         for (int m = 0; m < BPT; ++m) {
             *reinterpret_cast<uint4*>(&sB[buf][bloff[m]]) = rb[slot][m];
-            if (OUT) *reinterpret_cast<uint4*>(&sC[buf][cloff[m]]) = rc[slot][m];
+            if (OUT) {
+                // two 8-byte halves: C rows are only 8-byte aligned
+                uint2* d = reinterpret_cast<uint2*>(&sC[buf][cloff[m]]);
+                d[0] = make_uint2(rc[slot][m].x, rc[slot][m].y);
+                d[1] = make_uint2(rc[slot][m].z, rc[slot][m].w);
+            }
         }
     };
     // C B^T block of tile k into LDS; K1 (prefix of da over the tile's fused
@@ -1107,40 +1178,66 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
             lam += last;
         }
     };
-    // Decay matrices M = C B^T o L (+ D on the diagonal) of tile k for every
-    // head of the block, one (head, 16x16 block) unit per wave: element
-    // (j = 16 J + 4 q + v, i = 16 I + l16) of blocks (0,0), (0,1), (1,1).
-    auto build_m = [&](int k) {
+
+    // ---- state (physical frame)
+    f32x4 hs[NTILE];
+    {
+        const float* src = nullptr;
         if (OUT) {
-            for (int u = wv; u < 3 * nhb; u += W) {
-                const int uh = u / 3, blk = u - 3 * uh;
-                const int J = blk == 2 ? 1 : 0, I = blk == 0 ? 0 : 1;
-                const float* cum = sCum[k & 3][uh];
-                const float4 cb = *reinterpret_cast<const float4*>(&sCB[k & 1][blk * 256 + lane * 4]);
-                const float4 cj = *reinterpret_cast<const float4*>(&cum[16 * J + 4 * q]);
-                const int i = 16 * I + l16;
-                const float ci = cum[i];
-                const float Du = a.D ? a.D[hfirst + uh] : 0.f;
-                const float cbv[4] = {cb.x, cb.y, cb.z, cb.w}, cjv[4] = {cj.x, cj.y, cj.z, cj.w};
-                float mv[4];
+            if (S == 1)
+                src = a.init ? a.init + bh * P * N : nullptr;
+            else
+                src = a.ws_state + (bh * S + seg) * P * N;
+        }
+        // unconditional loads (clamped index), then one select: lets the
+        // loads issue back to back
+        const float* row = (src ? src : a.da) + (src ? (int64_t)(p0 + l16) * N : 0);
+        const int nmax = src ? (int)N - 1 : 0;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int j = 16 * J + 4 * q + v;
-                    mv[v] = ((i >> log2R) >= (j >> log2R)) ? cbv[v] * __builtin_amdgcn_exp2f(ci - cjv[v]) : 0.f;
-                    if (i == j) mv[v] += Du;
-                }
-                sM[k & 1][u * 64 + lane] = pack_m<TI>(mv[0], mv[1], mv[2], mv[3]);
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int n = phi_row(t, 4 * q + v);
+                const float val = row[n < nmax ? n : nmax];
+                hs[t][v] = (src && n < N) ? val : 0.f;
             }
         }
-    };
-    // Global stores of the y block staged in sY[buf] by tile k.
-    auto flush_y = [&](int buf, int k) {
-        if (OUT) {
-            const uint32_t o = (uint32_t)k * ystep;
+    }
+
+    // Decay matrices M = (C B^T o L) (+ D on the diagonal) of tile k for
+    // every head of the block, one (head, 16x16 block) unit per compute wave:
+    // element (j = 16 J + 4 q + v, i = 16 I + l16) of blocks (0,0), (0,1),
+    // (1,1). The pack already zeroes C B^T where step(i) < step(j), and cum is
+    // non-increasing, so exp2(min(cum_i - cum_j, 0)) is exact where it counts.
+    constexpr int UPW = (3 * MH + W - 1) / W;      // units per compute wave
+    float Du[UPW];
 #pragma unroll
-            for (int m = 0; m < YPT; ++m) {
-                const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 0);
+    for (int r = 0; r < UPW; ++r) {
+        const int u = wv + W * r;
+        Du[r] = (OUT && a.D && u < 3 * nhb && (u % 3) != 1) ? a.D[hfirst + u / 3] : 0.f;
+    }
+    float dsel[4];                                 // one-hot: this lane's diagonal slot
+#pragma unroll
+    for (int v = 0; v < 4; ++v) dsel[v] = (l16 == 4 * q + v) ? 1.f : 0.f;
+    auto build_m = [&](int k) {
+        if (OUT) {
+#pragma unroll
+            for (int r = 0; r < UPW; ++r) {
+                const int u = wv + W * r;
+                if (u < 3 * nhb) {
+                    const int uh = u / 3, blk = u - 3 * uh;
+                    const int J = blk == 2 ? 1 : 0, I = blk == 0 ? 0 : 1;
+                    const float* cum = sCum[k & 3][uh];
+                    const float4 cb = *reinterpret_cast<const float4*>(&sCB[k & 1][blk * 256 + lane * 4]);
+                    const float4 cj = *reinterpret_cast<const float4*>(&cum[16 * J + 4 * q]);
+                    const float ci = cum[16 * I + l16];
+                    const float cbv[4] = {cb.x, cb.y, cb.z, cb.w}, cjv[4] = {cj.x, cj.y, cj.z, cj.w};
+                    float mv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v)
+                        mv[v] = fmaf(dsel[v], Du[r], cbv[v] * __builtin_amdgcn_exp2f(fminf(ci - cjv[v], 0.f)));
+                    sM[k & 1][u * 64 + lane] = pack_m<TI>(mv[0], mv[1], mv[2], mv[3]);
+                }
             }
         }
     };
@@ -1163,8 +1260,8 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
                     hv[4 + v] = hs[2 * s + 1][v];
                 }
                 const frag hA = O::pack(hv);
-                yacc[0] = O::mma(hA, O::ld8(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
-                yacc[1] = O::mma(hA, O::ld8(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
+                yacc[0] = O::mma(hA, ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
+                yacc[1] = O::mma(hA, ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
             }
             const float e0 = sEin[vb][hl][l16], e1 = sEin[vb][hl][16 + l16];
 #pragma unroll
@@ -1202,50 +1299,41 @@ __global__ __launch_bounds__(64 * W) void ssd_cols_kernel(TileArgs a) {
         }
     };
 
-    // ---- pipeline, tile indices relative to k0. x, B and C are staged in
-    // registers two tiles ahead and in LDS one tile ahead (buffer = tile
-    // parity); da and C B^T run one tile further ahead, so that the decay
-    // matrices of tile k+1 are built, once per head, while tile k is computed.
-    // y of tile k leaves from LDS during tile k + 1. One barrier per tile.
-    // Memory counters retire in issue order, and each step waits only for
-    // the oldest group in flight. Tiles are walked in pairs; a tile past the
-    // segment end loads zeros (da = 0, x = 0: the state is unchanged) and
-    // stores nothing. The first flush (tile -1) wraps to an offset beyond
-    // every resource and is dropped.
-    const int nk = k1 - k0;
-    load_xbc(0, 0);
+    // ---- pipeline (barriers match the memory waves' one for one). B and C
+    // are staged in registers two tiles ahead and in LDS one tile ahead
+    // (buffer = tile parity); da and C B^T run one tile further ahead, so that
+    // the decay matrices of tile k+1 are built, once per head, while tile k is
+    // computed. Memory counters retire in issue order, and each step waits
+    // only for the oldest group in flight.
+    load_bc(0, 0);
     load_cbda(0, 0);
     load_cbda(1, 1);
-    load_xbc(1, 1);
-    store_xbc(0, 0);
+    load_bc(1, 1);
+    store_bc(0, 0);
     store_cbda(0, 0);
     load_cbda(0, 2);
     store_cbda(1, 1);
-    load_xbc(0, 2);
+    load_bc(0, 2);
     load_cbda(1, 3);
     __syncthreads();
     build_m(0);
     __syncthreads();
-    int k = 0;
-    for (; k < nk; k += 2) {
-        store_xbc(1, 1);             // x, B, C of tile k+1
+    for (int k = 0; k < nk; k += 2) {
+        store_bc(1, 1);              // B, C of tile k+1
         store_cbda(0, k + 2);
         build_m(k + 1);
-        flush_y(1, k - 1);
-        load_xbc(1, k + 3);
+        load_bc(1, k + 3);
         load_cbda(0, k + 4);
         compute(0, k);
         __syncthreads();
-        store_xbc(0, 0);             // x, B, C of tile k+2
+        store_bc(0, 0);              // B, C of tile k+2
         store_cbda(1, k + 3);
         build_m(k + 2);
-        flush_y(0, k);
-        load_xbc(0, k + 4);
+        load_bc(0, k + 4);
         load_cbda(1, k + 5);
         compute(1, k + 1);
         __syncthreads();
     }
-    flush_y(1, k - 1);
 
     // ---- epilogue
     float* dstate = nullptr;
@@ -1342,7 +1430,7 @@ void* walk_ptr_p(int P, int NP) {
 constexpr int kLdsLimit = 160 * 1024;
 
 // Column-block widths (16-column slices per workgroup), preferred first.
-constexpr int kColsWidths[] = {12, 10, 8, 6, 4, 2, 1};
+constexpr int kColsWidths[] = {10, 8, 6, 4, 2, 1};
 
 template <typename TI, int NP, int W, int MODE>
 void* cols_ptr() {
@@ -1372,7 +1460,6 @@ void* cols_ptr_w(int w, int NP) {
         case 6: return cols_ptr_np<TI, 6, MODE>(NP);
         case 8: return cols_ptr_np<TI, 8, MODE>(NP);
         case 10: return cols_ptr_np<TI, 10, MODE>(NP);
-        case 12: return cols_ptr_np<TI, 12, MODE>(NP);
     }
     return nullptr;
 }
@@ -1565,7 +1652,7 @@ ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hip
     if (pl.kind == kColsPath) {
         fn = select_cols(pl.dtype, mode, pl.W, (int)pl.NP);
         nwg = pl.b * args.seg_items * pl.H * (pl.P / 16) / pl.W;
-        threads = (unsigned)(64 * pl.W);
+        threads = (unsigned)(64 * (pl.W + cols_mem_waves(pl.W)));
     } else {
         fn = select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
     }
@@ -1695,8 +1782,8 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             const void* Bp = B;
             const void* Cp = C;
             int64_t TRv = T * R, Gv = G, Nv = N;
-            int nsub = pl.nsub;
-            void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub};
+            int nsub = pl.nsub, l2r = pl.log2R;
+            void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub, (void*)&l2r};
             if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
         }
         if (rs == SSD_OK) {

@@ -97,7 +97,7 @@ typedef struct {
                                 shared-B/C walk owns k consecutive 16-column
                                 slices of one time row flattened over
                                 (head, headdim) within a B/C group; k must be
-                                1, 2, 4, 6, 8, 10 or 12, divide
+                                1, 2, 4, 6, 8 or 10, divide
                                 (nheads / ngroups) * headdim / 16 and have a
                                 kernel for (dstate, dtype), else
                                 SSD_ERR_UNSUPPORTED. Ignored when theta is given

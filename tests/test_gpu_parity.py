@@ -159,7 +159,7 @@ BLOCKS = [
     (32, 256, 6, 3, 2, 1, "bf16", True, 2),
     (16, 32, 8, 2, 2, 1, "f32", True, 1),       # one-slice heads
     (16, 16, 3, 1, 1, 8, "bf16", False, 2),
-    (128, 64, 3, 1, 12, 1, "bf16", True, 1),    # 1.5 heads per block
+    (128, 64, 3, 1, 6, 1, "bf16", True, 1),     # 3/4 of a head per block
     (128, 128, 2, 1, 4, 2, "f32", True, 2),     # half a head per block
     (64, 32, 12, 4, 6, 16, "bf16", True, 1),    # 1.5 heads per block, 4 groups
 ]
