@@ -42,6 +42,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssd_scan.h"
 
 namespace {
@@ -1548,6 +1550,71 @@ int auto_segments(int64_t units, int nsub, int64_t target) {
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Scratch is cached per (device, stream) and grows on demand. Stream-ordered
+// allocation (hipMallocAsync / hipFreeAsync) would block the host while the
+// stream has work in flight, serialising the caller with the device. Calls
+// on one stream are ordered by the stream; each call also waits (on the
+// device) for the last call that used the buffer, which keeps a stream handle
+// that is destroyed and reissued from racing with the old stream's work.
+// Buffers live until the process ends.
+struct ScratchEntry {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+    hipEvent_t last;    // recorded after the last call that used ptr
+};
+
+std::mutex g_scratch_mu;
+ScratchEntry g_scratch[256];
+int g_scratch_n = 0;
+
+// Scratch of at least `bytes` for `stream` on the current device, ordered
+// after its previous use; nullptr on failure. *entry identifies it for
+// scratch_release.
+void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    int i = 0;
+    while (i < g_scratch_n && !(g_scratch[i].dev == dev && g_scratch[i].stream == stream)) ++i;
+    if (i == g_scratch_n) {
+        if (g_scratch_n == 256) return nullptr;
+        ScratchEntry& e = g_scratch[g_scratch_n];
+        e.dev = dev;
+        e.stream = stream;
+        e.ptr = nullptr;
+        e.bytes = 0;
+        if (hipEventCreateWithFlags(&e.last, hipEventDisableTiming) != hipSuccess) return nullptr;
+        ++g_scratch_n;
+    }
+    ScratchEntry& e = g_scratch[i];
+    if (e.bytes < bytes) {
+        // grow: wait for the old buffer's last use, then replace it
+        if (e.ptr) {
+            if (hipEventSynchronize(e.last) != hipSuccess || hipFree(e.ptr) != hipSuccess) return nullptr;
+            e.ptr = nullptr;
+            e.bytes = 0;
+        }
+        if (hipMalloc(&e.ptr, bytes) != hipSuccess) {
+            e.ptr = nullptr;
+            return nullptr;
+        }
+        e.bytes = bytes;
+    } else if (hipStreamWaitEvent(stream, e.last, 0) != hipSuccess) {
+        return nullptr;
+    }
+    *entry = i;
+    return e.ptr;
+}
+
+// Marks the end of this call's use of the scratch on its stream.
+bool scratch_release(int entry) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchEntry& e = g_scratch[entry];
+    return hipEventRecord(e.last, e.stream) == hipSuccess;
+}
+
 // Scratch layout: [segment states | segment Lambda/Phi | C B^T tile pack]
 struct WsLayout {
     size_t state, misc, pack, total;
@@ -1754,8 +1821,10 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     const bool shared = pl.kind == kColsPath;
     const WsLayout wl = workspace_layout(pl, !shared);
     void* ws = nullptr;
+    int ws_entry = -1;
     if (wl.total) {
-        if (hipMallocAsync(&ws, wl.total, hs) != hipSuccess) return SSD_ERR_HIP;
+        ws = scratch_acquire(hs, wl.total, &ws_entry);
+        if (!ws) return SSD_ERR_HIP;
     }
     char* wsc = static_cast<char*>(ws);
     float* ws_state = pl.S > 1 ? reinterpret_cast<float*>(wsc) : nullptr;
@@ -1798,9 +1867,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             rs = run_passes(pl, false, args, init_state, hs);
         }
     }
-    if (ws) {
-        if (hipFreeAsync(ws, hs) != hipSuccess && rs == SSD_OK) rs = SSD_ERR_HIP;
-    }
+    if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
 }
 

@@ -42,8 +42,13 @@
  * Ownership: the caller owns every buffer and keeps inputs alive until the
  * work enqueued on `stream` has completed. Nothing is retained after return.
  * Scratch (the head-shared C B^T tile pack, and segment states when the
- * sequence is split; see ssd_workspace_bytes) is allocated and released
- * stream-ordered on `stream` (hipMallocAsync / hipFreeAsync).
+ * sequence is split; see ssd_workspace_bytes) is the library's: one device
+ * buffer per (device, stream), allocated on first use, grown when a call
+ * needs more (hipMalloc, after the old buffer's last use has finished) and
+ * kept until the process ends. Each call orders its kernels after the
+ * previous call that used the buffer (an event), so calls are asynchronous.
+ * Calls on different streams use different buffers; calls on one stream are
+ * ordered by it.
  * final_state may be the same pointer as init_state (in-place state update);
  * any other overlap between an output and another buffer is SSD_ERR_ALIAS.
  *
@@ -51,7 +56,8 @@
  * on any error status nothing is enqueued and no output is touched.
  * The call is asynchronous: it returns after enqueueing on `stream` (a
  * hipStream_t; NULL means the null stream) without synchronising.
- * Different streams may call concurrently; calls share no mutable state.
+ * Different streams may call concurrently (host threads included); they
+ * share only the scratch cache's bookkeeping, which is locked.
  *
  * Supported envelope (SSD_ERR_UNSUPPORTED outside it):
  *   P in {16, 32, 64, 128}; N in {16, 32, 64, 128, 256};
