@@ -1042,7 +1042,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
         auto load_x = [&](int slot, int k) {
             const uint32_t o = (uint32_t)k * xstep;
 #pragma unroll
-            for (int m = 0; m < XPT; ++m)
+            for (int m = 0; m < XPT; ++m)   // non-temporal: x is read once
                 rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, 2));
         };
         auto store_x = [&](int slot, int buf) {
@@ -1056,7 +1056,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
 #pragma unroll
                 for (int m = 0; m < YPT; ++m) {
                     const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 0);
+                    // non-temporal: y is written once and never read back here
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 2);
                 }
             }
         };
@@ -1321,18 +1322,20 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     build_m(0);
     __syncthreads();
     for (int k = 0; k < nk; k += 2) {
+        // each register slot is refilled right after it is drained, before
+        // the memory waves' y stores of this tile queue up behind the barrier
         store_bc(1, 1);              // B, C of tile k+1
-        store_cbda(0, k + 2);
-        build_m(k + 1);
         load_bc(1, k + 3);
+        store_cbda(0, k + 2);
         load_cbda(0, k + 4);
+        build_m(k + 1);
         compute(0, k);
         __syncthreads();
         store_bc(0, 0);              // B, C of tile k+2
-        store_cbda(1, k + 3);
-        build_m(k + 2);
         load_bc(0, k + 4);
+        store_cbda(1, k + 3);
         load_cbda(1, k + 5);
+        build_m(k + 2);
         compute(1, k + 1);
         __syncthreads();
     }
