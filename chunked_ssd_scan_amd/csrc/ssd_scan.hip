@@ -925,12 +925,12 @@ constexpr int cols_lds_bytes(int mode) {
            (out ? 2 * (F * ldc + epu) * esz + 2 * (768 + 4) * 4 + 2 * (F * y_row_stride(CW) + 4) * 4 +
                       2 * MH * 3 * 64 * mbytes
                 : 0) +
-           4 * MH * (3 * F + 1) * 4;
+           4 * MH * (3 * F + 1) * 4 + 4 * F * 8 * 4;
 }
 
-// Memory waves per workgroup of the column-block walk: they carry the two
-// large HBM streams (x in, y out), so the W compute waves only wait on memory
-// counters for the small, L2-resident B, C, C B^T and da tiles they stage.
+// Memory waves per workgroup of the column-block walk: they issue every global
+// access of the walk (x in, y out, and the B, C, C B^T and da tiles), so the
+// W compute waves work from LDS and registers only.
 constexpr int cols_mem_waves(int W) { return W >= 4 ? 2 : 1; }
 
 template <typename TI, int NP, int W, int MODE>
@@ -956,7 +956,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     constexpr int XUR = CW / EPU, BUR = NP / EPU, YUR = CW / 4;   // 16-byte units per row
     constexpr int XU = F * XUR, BU = F * BUR, CBU = 768 * 4 / 16, YU = F * YUR;
     constexpr int XPT = (XU + NTM - 1) / NTM, YPT = (YU + NTM - 1) / NTM;          // per memory thread
-    constexpr int BPT = (BU + NTC - 1) / NTC, CBPT = (CBU + NTC - 1) / NTC;        // per compute thread
+    constexpr int CBPM = (CBU + NTM - 1) / NTM, DPM = (F * 8 + NTM - 1) / NTM;    // per memory thread
+    constexpr int BPM = (BU + NTM - 1) / NTM;
 
     __shared__ __attribute__((aligned(16))) TI sX[2][F * LDX + EPU];
     __shared__ __attribute__((aligned(16))) TI sB[2][F * LDB + EPU];
@@ -968,6 +969,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     // it, the weight that carries row j to the tile end, and the tile decay
     __shared__ __attribute__((aligned(16))) float sCum[4][MH][F], sEin[4][MH][F], sW[4][MH][F];
     __shared__ float sCarry[4][MH];
+    // da of the block's heads, staged by the memory waves: [tile ring][step][head]
+    __shared__ __attribute__((aligned(16))) float sDa[4][kRows][8];
 
     const int tid = threadIdx.x;
     // wave index made visibly uniform, so per-head pointers stay scalar
@@ -1016,7 +1019,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     const int64_t vrows = row_end - row0;                    // >= 1
 
     if (memw) {
-        // ================= memory waves: x in, y out =================
+        // ============ memory waves: x in, y out, B / C / C B^T / da staged ============
         const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
                                     (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
         const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0,
@@ -1039,6 +1042,92 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
             yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
         }
         uint4 rx[2][XPT];            // x of tile t in slot t & 1
+        // C B^T blocks of tile t in slot t & 1 (768 floats = CBU 16-byte units)
+        const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
+                                     OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
+        uint32_t cbgoff[CBPM];
+        int cbloff[CBPM];
+#pragma unroll
+        for (int m = 0; m < CBPM; ++m) {
+            const int u = mt + m * NTM;
+            cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
+            cbloff[m] = (u < CBU) ? u * 4 : 768;
+        }
+        float4 rcb[2][CBPM];
+        auto load_cb = [&](int slot, int k) {
+            if (OUT) {
+                const uint32_t o = (uint32_t)k * (768 * 4);
+#pragma unroll
+                for (int m = 0; m < CBPM; ++m)
+                    rcb[slot][m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs_cb, cbgoff[m] + o, 0, 0));
+            }
+        };
+        auto store_cb = [&](int slot, int k) {
+            if (OUT) {
+#pragma unroll
+                for (int m = 0; m < CBPM; ++m) *reinterpret_cast<float4*>(&sCB[k & 1][cbloff[m]]) = rcb[slot][m];
+            }
+        };
+        // da of tile t in slot t & 1: element (step, head) of the block's heads,
+        // lane-contiguous along the heads of a step (one short run per step)
+        const int64_t step0 = (int64_t)k0 * Qt;
+        const int64_t vsteps = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - step0;
+        const auto rs_da = make_rsrc(a.da + (b * T + step0) * H + hfirst, (uint32_t)(((vsteps - 1) * H + nhb) * 4));
+        const uint32_t dastep = (uint32_t)(Qt * H * 4);
+        uint32_t daoff[DPM];
+#pragma unroll
+        for (int m = 0; m < DPM; ++m) {
+            const int u = mt + m * NTM, st = u >> 3, hd = u & 7;
+            daoff[m] = (st < Qt && hd < nhb) ? (uint32_t)((st * H + hd) * 4) : kOOB;
+        }
+        float rda[2][DPM];
+        auto load_da = [&](int slot, int k) {
+            const uint32_t o = (uint32_t)k * dastep;
+#pragma unroll
+            for (int m = 0; m < DPM; ++m)
+                rda[slot][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_da, daoff[m] + o, 0, 0));
+        };
+        auto store_da = [&](int slot, int k) {
+#pragma unroll
+            for (int m = 0; m < DPM; ++m) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
+        };
+        // B and C of tile t: one register slot, refilled a tile ahead
+        const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
+        const auto rs_b = make_rsrc(static_cast<const TI*>(a.B) + (b * TR + row0) * brow_el + grp * N, bspan);
+        const auto rs_c = make_rsrc(static_cast<const TI*>(a.C) + (b * TR + row0) * brow_el + grp * N, bspan);
+        const uint32_t bstep = (uint32_t)(F * brow_el * ESZ);
+        // thread mt takes column unit mt % BUR of rows mt / BUR + m (NTM / BUR):
+        // the offsets advance by a fixed stride per unit
+        static_assert(NTM % BUR == 0, "memory threads cover whole B rows");
+        constexpr int RPM = NTM / BUR;               // rows per memory pass
+        const int br0 = mt / BUR, bcol = (mt % BUR) * EPU;
+        const bool bcol_ok = bcol < N;
+        const uint32_t bgo0 = (uint32_t)((br0 * brow_el + bcol) * ESZ);
+        const uint32_t bgstride = (uint32_t)(RPM * brow_el * ESZ);
+        const int blo0 = br0 * LDB + bcol, clo0 = br0 * LDC + bcol;
+        uint4 rb[BPM], rc[BPM];
+        auto load_bc = [&](int k) {
+            const uint32_t ob = (uint32_t)k * bstep;
+#pragma unroll
+            for (int m = 0; m < BPM; ++m) {
+                const uint32_t go = (bcol_ok && br0 + m * RPM < F) ? bgo0 + m * bgstride + ob : kOOB;
+                rb[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, go, 0, 0));
+                if (OUT) rc[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, go, 0, 0));
+            }
+        };
+        auto store_bc = [&](int buf) {
+#pragma unroll
+            for (int m = 0; m < BPM; ++m) {
+                if (br0 + m * RPM >= F) continue;
+                *reinterpret_cast<uint4*>(&sB[buf][blo0 + m * RPM * LDB]) = rb[m];
+                if (OUT) {
+                    // two 8-byte halves: C rows are only 8-byte aligned
+                    uint2* d = reinterpret_cast<uint2*>(&sC[buf][clo0 + m * RPM * LDC]);
+                    d[0] = make_uint2(rc[m].x, rc[m].y);
+                    d[1] = make_uint2(rc[m].z, rc[m].w);
+                }
+            }
+        };
         auto load_x = [&](int slot, int k) {
             const uint32_t o = (uint32_t)k * xstep;
 #pragma unroll
@@ -1062,24 +1151,57 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
             }
         };
         // x is staged in registers two tiles ahead and in LDS one tile ahead
-        // (buffer = tile parity). y of tile k leaves from LDS during tile k+1;
-        // the first flush (tile -1) wraps to an offset beyond the resource and
-        // is dropped. Barriers match the compute waves' one for one.
+        // (buffer = tile parity). The C B^T blocks and da run one tile further
+        // ahead, for the compute waves' decay matrices and scans. Each register
+        // slot is refilled right after it is drained, before this tile's y
+        // stores. y of tile k leaves from LDS during tile k+1; the first flush
+        // (tile -1) wraps to an offset beyond the resource and is dropped.
+        // Barriers match the compute waves' one for one.
+        load_bc(0);
         load_x(0, 0);
         load_x(1, 1);
+        load_cb(0, 0);
+        load_cb(1, 1);
+        load_da(0, 0);
+        load_da(1, 1);
+        store_bc(0);
+        load_bc(1);
         store_x(0, 0);
         load_x(0, 2);
+        store_cb(0, 0);
+        load_cb(0, 2);
+        store_cb(1, 1);
+        load_cb(1, 3);
+        store_da(0, 0);
+        load_da(0, 2);
+        store_da(1, 1);
+        load_da(1, 3);
+        __syncthreads();             // da of tiles 0, 1 for the compute waves' scans
+        store_da(0, 2);
+        load_da(0, 4);
         __syncthreads();
         __syncthreads();
         int k = 0;
         for (; k < nk; k += 2) {
-            store_x(1, 1);           // tile k+1
-            flush_y(1, k - 1);
+            store_bc(1);             // B, C of tile k+1
+            load_bc(k + 2);
+            store_x(1, 1);           // x of tile k+1
             load_x(1, k + 3);
+            store_cb(0, k + 2);
+            load_cb(0, k + 4);
+            store_da(1, k + 3);
+            load_da(1, k + 5);
+            flush_y(1, k - 1);
             __syncthreads();
-            store_x(0, 0);           // tile k+2
-            flush_y(0, k);
+            store_bc(0);             // B, C of tile k+2
+            load_bc(k + 3);
+            store_x(0, 0);           // x of tile k+2
             load_x(0, k + 4);
+            store_cb(1, k + 3);
+            load_cb(1, k + 5);
+            store_da(0, k + 4);
+            load_da(0, k + 6);
+            flush_y(0, k);
             __syncthreads();
         }
         flush_y(1, k - 1);
@@ -1087,89 +1209,23 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     }
 
     // ================= compute waves =================
-    const int64_t step0 = (int64_t)k0 * Qt;
-    const int64_t vsteps = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - step0;
-    const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
-    const auto rs_b = make_rsrc(static_cast<const TI*>(a.B) + (b * TR + row0) * brow_el + grp * N, bspan);
-    const auto rs_c = make_rsrc(static_cast<const TI*>(a.C) + (b * TR + row0) * brow_el + grp * N, bspan);
-    const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
-                                 OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
     // wave w < nhb scans the decays of head hfirst + w
     const bool scanner = wv < nhb;
-    const auto rs_da = make_rsrc(a.da + (b * T + step0) * H + hfirst + (scanner ? wv : 0),
-                                 (uint32_t)(((vsteps - 1) * H + 1) * 4));
-    const uint32_t bstep = (uint32_t)(F * brow_el * ESZ), dastep = (uint32_t)(Qt * H * 4);
-    uint32_t bgoff[BPT], cbgoff[CBPT];
-    int bloff[BPT], cloff[BPT], cbloff[CBPT];
-#pragma unroll
-    for (int m = 0; m < BPT; ++m) {
-        const int u = tid + m * NTC;
-        const int r = u / BUR, col = (u % BUR) * EPU;
-        bgoff[m] = (u < BU && col < N) ? (uint32_t)((r * brow_el + col) * ESZ) : kOOB;
-        bloff[m] = (u < BU) ? r * LDB + col : F * LDB;
-        cloff[m] = (u < BU) ? r * LDC + col : F * LDC;
-    }
-#pragma unroll
-    for (int m = 0; m < CBPT; ++m) {
-        const int u = tid + m * NTC;
-        cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
-        cbloff[m] = (u < CBU) ? u * 4 : 768;
-    }
-    // da: lane f < 32 of a scanning wave reads step f >> log2R for the first
-    // rank of each step, so the scan over fused rows yields cum per row
-    const bool da_lane = scanner && (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
-    const uint32_t daoff = da_lane ? (uint32_t)((lane >> log2R) * H * 4) : kOOB;
+    // da: lane f < 32 of a scanning wave takes step f >> log2R for the first
+    // rank of each step (0 for the others), so the scan over fused rows
+    // yields cum per row
+    const bool da_lane = (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
     // this wave's y fragment in the staged block: rows 16 I + l16, columns
     // 16 wv + 4 q .. + 3
     const int ysoff = l16 * LDY + 16 * wv + 4 * q;
     float lam = 0.f;
 
-    // register staging (two slots): B and C of tile t in slot t & 1, and the
-    // C B^T block and da of tile t in slot t & 1, issued one tile earlier
-    uint4 rb[2][BPT], rc[2][BPT];
-    float4 rcb[2][CBPT];
-    float rda[2];
-    auto load_bc = [&](int slot, int k) {
-        const uint32_t ob = (uint32_t)k * bstep;
-#pragma unroll
-        for (int m = 0; m < BPT; ++m)
-            rb[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, bgoff[m] + ob, 0, 0));
-        if (OUT) {
-#pragma unroll
-            for (int m = 0; m < BPT; ++m)
-                rc[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, bgoff[m] + ob, 0, 0));
-        }
-    };
-    auto load_cbda = [&](int slot, int k) {
-        if (OUT) {
-            const uint32_t ocb = (uint32_t)k * (768 * 4);
-#pragma unroll
-            for (int m = 0; m < CBPT; ++m)
-                rcb[slot][m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs_cb, cbgoff[m] + ocb, 0, 0));
-        }
-        rda[slot] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_da, daoff + (uint32_t)k * dastep, 0, 0));
-    };
-    auto store_bc = [&](int slot, int buf) {
-#pragma unroll
-        for (int m = 0; m < BPT; ++m) {
-            *reinterpret_cast<uint4*>(&sB[buf][bloff[m]]) = rb[slot][m];
-            if (OUT) {
-                // two 8-byte halves: C rows are only 8-byte aligned
-                uint2* d = reinterpret_cast<uint2*>(&sC[buf][cloff[m]]);
-                d[0] = make_uint2(rc[slot][m].x, rc[slot][m].y);
-                d[1] = make_uint2(rc[slot][m].z, rc[slot][m].w);
-            }
-        }
-    };
-    // C B^T block of tile k into LDS; K1 (prefix of da over the tile's fused
-    // rows, in base 2) by the scanning waves
-    auto store_cbda = [&](int slot, int k) {
-        if (OUT) {
-#pragma unroll
-            for (int m = 0; m < CBPT; ++m) *reinterpret_cast<float4*>(&sCB[k & 1][cbloff[m]]) = rcb[slot][m];
-        }
+    // K1 of tile k (prefix of da over the tile's fused rows, in base 2) by
+    // the scanning waves, from the da the memory waves staged
+    auto scan = [&](int k) {
         if (scanner) {
-            const float cum = wave_prefix32(rda[slot]);
+            const float dv = da_lane ? sDa[k & 3][lane >> log2R][wv] : 0.f;
+            const float cum = wave_prefix32(dv);
             const float last = __shfl(cum, F - 1);
             const float c2 = cum * kLog2e, l2 = last * kLog2e;
             if (lane < F) {
@@ -1304,37 +1360,23 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
 
     // ---- pipeline (barriers match the memory waves' one for one). B and C
     // are staged in registers two tiles ahead and in LDS one tile ahead
-    // (buffer = tile parity); da and C B^T run one tile further ahead, so that
-    // the decay matrices of tile k+1 are built, once per head, while tile k is
-    // computed. Memory counters retire in issue order, and each step waits
-    // only for the oldest group in flight.
-    load_bc(0, 0);
-    load_cbda(0, 0);
-    load_cbda(1, 1);
-    load_bc(1, 1);
-    store_bc(0, 0);
-    store_cbda(0, 0);
-    load_cbda(0, 2);
-    store_cbda(1, 1);
-    load_bc(0, 2);
-    load_cbda(1, 3);
+    // (buffer = tile parity); the da scans and the memory waves' C B^T blocks
+    // run one tile further ahead, so that the decay matrices of tile k+1 are
+    // built, once per head, while tile k is computed. Each register slot is
+    // refilled right after it is drained. Memory counters retire in issue
+    // order, and each step waits only for the oldest group in flight.
+    __syncthreads();                 // da of tiles 0, 1 staged
+    scan(0);
+    scan(1);
     __syncthreads();
     build_m(0);
     __syncthreads();
     for (int k = 0; k < nk; k += 2) {
-        // each register slot is refilled right after it is drained, before
-        // the memory waves' y stores of this tile queue up behind the barrier
-        store_bc(1, 1);              // B, C of tile k+1
-        load_bc(1, k + 3);
-        store_cbda(0, k + 2);
-        load_cbda(0, k + 4);
+        scan(k + 2);
         build_m(k + 1);
         compute(0, k);
         __syncthreads();
-        store_bc(0, 0);              // B, C of tile k+2
-        load_bc(0, k + 4);
-        store_cbda(1, k + 3);
-        load_cbda(1, k + 5);
+        scan(k + 3);
         build_m(k + 2);
         compute(1, k + 1);
         __syncthreads();
