@@ -38,7 +38,7 @@ class SsdDims(ctypes.Structure):
 
 class SsdLaunchOpts(ctypes.Structure):
     _fields_ = [("segments", ctypes.c_int32), ("block_slices", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("reserved", ctypes.c_int32 * 2), ("walk_events", ctypes.c_void_p * 2)]
 
 
 class SsdError(RuntimeError):
@@ -111,14 +111,16 @@ def _dptr(t):
 
 def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=None,
             y=None, final_state=None, segments: int = 0, block_slices: int = 0,
-            stream=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+            stream=None, walk_events=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
     """Run the scan on device tensors; returns (y, final_state).
 
     x [b,T,R,H,P] (or [b,T,H,P] for R = 1), da [b,T,H], B/C [b,T,R,G,N]
     (or [b,T,G,N]); D [H], init_state [b,H,P,N], theta [b,T,H,N/2] fp32.
     y / final_state may be given (fp32, contiguous) to write in place;
-    final_state may be init_state itself. ``segments`` and ``block_slices``
-    are the launch options of ssd_forward_ex (0 = automatic).
+    final_state may be init_state itself. ``segments``, ``block_slices`` and
+    ``walk_events`` (a pair of torch.cuda.Event, or of hipEvent_t handles as
+    ints, recorded around the output walk kernel) are the launch options of
+    ssd_forward_ex.
     """
     import torch
 
@@ -160,6 +162,17 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     opts.block_slices = int(block_slices)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    if walk_events is not None:
+        handles = []
+        for ev in walk_events:
+            if isinstance(ev, int):
+                handles.append(ev)              # a hipEvent_t handle
+                continue
+            if ev.cuda_event == 0:
+                # torch creates an event's HIP handle at its first record
+                ev.record(torch.cuda.ExternalStream(stream, device=dev))
+            handles.append(ev.cuda_event)
+        opts.walk_events[0], opts.walk_events[1] = handles
     with torch.cuda.device(dev):
         st = ssd_forward_ex(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), C.data_ptr(),
                             _dptr(D), _dptr(init_state), chunk_len, R, _dptr(theta),

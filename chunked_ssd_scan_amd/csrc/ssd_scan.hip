@@ -1779,7 +1779,8 @@ ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hip
 
 // Pass A (segment end states), pass B (carry), pass C (outputs).
 template <typename Args>
-ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs) {
+ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs,
+                      void* const* walk_events) {
     ssd_status rs = SSD_OK;
     if (pl.S > 1) {
         args.seg_items = pl.S - 1;
@@ -1793,7 +1794,12 @@ ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_sta
     }
     if (rs == SSD_OK) {
         args.seg_items = pl.S;
+        const bool timed = walk_events && walk_events[0];
+        if (timed && hipEventRecord(reinterpret_cast<hipEvent_t>(walk_events[0]), hs) != hipSuccess)
+            return SSD_ERR_HIP;
         rs = launch_walk(pl, 0, rot, args, hs);
+        if (rs == SSD_OK && timed && hipEventRecord(reinterpret_cast<hipEvent_t>(walk_events[1]), hs) != hipSuccess)
+            rs = SSD_ERR_HIP;
     }
     return rs;
 }
@@ -1830,8 +1836,9 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     if (st != SSD_OK) return st;
     if (opts) {
         if (opts->segments < 0 || opts->block_slices < 0) return SSD_ERR_BAD_SHAPE;
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 2; ++i)
             if (opts->reserved[i] != 0) return SSD_ERR_BAD_SHAPE;
+        if ((opts->walk_events[0] == nullptr) != (opts->walk_events[1] == nullptr)) return SSD_ERR_BAD_SHAPE;
     }
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(final_state, 16) || (init_state && !aligned(init_state, 16)) || !aligned(da, 4) ||
@@ -1885,7 +1892,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
         args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
         args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
         args.ws_state = ws_state; args.ws_misc = ws_misc;
-        rs = run_passes(pl, rot, args, init_state, hs);
+        rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
     } else {
         // K2 once per (batch, group, tile), shared by every head of the group
         void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
@@ -1909,7 +1916,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
             args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
             args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
-            rs = run_passes(pl, false, args, init_state, hs);
+            rs = run_passes(pl, false, args, init_state, hs, opts ? opts->walk_events : nullptr);
         }
     }
     if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;

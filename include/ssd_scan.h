@@ -108,7 +108,17 @@ typedef struct {
                                 kernel for (dstate, dtype), else
                                 SSD_ERR_UNSUPPORTED. Ignored when theta is given
                                 (rotation uses the per-head walk). */
-    int32_t reserved[6];     /* must be zero */
+    int32_t reserved[2];     /* must be zero */
+    void *walk_events[2];    /* NULL, NULL: none. Two hipEvent_t (cast to void*)
+                                created by the caller: the library records
+                                walk_events[0] on the stream just before the
+                                launch of the output walk (the kernel that
+                                writes y and final_state, which dominates the
+                                call's time) and walk_events[1] just after
+                                it, so the caller can time that kernel alone.
+                                Both or neither must be given, else
+                                SSD_ERR_BAD_SHAPE; a failed record is
+                                SSD_ERR_HIP. */
 } ssd_launch_opts;
 
 /*

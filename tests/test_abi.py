@@ -115,7 +115,10 @@ def test_bad_launch_options(lib):
     opts.block_slices = -2
     assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
     opts = ssd.SsdLaunchOpts()
-    opts.reserved[3] = 1
+    opts.reserved[1] = 1
+    assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.walk_events[0] = 1           # one event without the other
     assert call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
     opts = ssd.SsdLaunchOpts()
     opts.block_slices = 7             # not a column-block width

@@ -216,6 +216,28 @@ def test_chunk_len_does_not_change_result():
         assert torch.equal(y, outs[0][0]) and torch.equal(f, outs[0][1])
 
 
+@pytest.mark.parametrize("segments", [1, 3])
+def test_walk_events_time_the_output_walk(segments):
+    # the optional event pair brackets the output walk only: the result is
+    # unchanged and the bracketed time fits inside the whole call
+    shape = si.small_shape(batch=2, seqlen=700, nheads=4, headdim=64, dstate=128, dtype="bf16")
+    inp = si.make_inputs(shape, seed=27)
+    ssd = _ssd()
+    g = inp.to(_dev())
+    y0, f0 = run_gpu(inp, segments=segments)
+    walk = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    call[0].record()
+    y1, f1 = ssd.forward(g.x, g.da, g.B, g.C, g.D, g.init_state, shape.chunk_len, g.theta,
+                         segments=segments, walk_events=walk)
+    call[1].record()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+    t_walk, t_call = walk[0].elapsed_time(walk[1]), call[0].elapsed_time(call[1])
+    print(f"segments {segments}: walk {t_walk:.4f} ms of call {t_call:.4f} ms", flush=True)
+    assert 0.0 < t_walk <= t_call
+
+
 def test_deterministic():
     shape = si.small_shape(batch=2, seqlen=500, nheads=4, headdim=64, dstate=128, mimo_rank=4,
                            dtype="bf16", rotation=True, init_state=True)
