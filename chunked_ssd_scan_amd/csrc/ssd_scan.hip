@@ -929,8 +929,8 @@ constexpr int cols_lds_bytes(int mode) {
 }
 
 // Memory waves per workgroup of the column-block walk: they issue every global
-// access of the walk (x in, y out, and the B, C, C B^T and da tiles), so the
-// W compute waves work from LDS and registers only.
+// load of the walk (x, and the B, C, C B^T and da tiles), so the W compute
+// waves work from LDS and registers and only store y.
 constexpr int cols_mem_waves(int W) { return W >= 4 ? 2 : 1; }
 
 template <typename TI, int NP, int W, int MODE>
@@ -955,7 +955,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     constexpr int EPU = 16 / ESZ;
     constexpr int XUR = CW / EPU, BUR = NP / EPU, YUR = CW / 4;   // 16-byte units per row
     constexpr int XU = F * XUR, BU = F * BUR, CBU = 768 * 4 / 16, YU = F * YUR;
-    constexpr int XPT = (XU + NTM - 1) / NTM, YPT = (YU + NTM - 1) / NTM;          // per memory thread
+    constexpr int XPT = (XU + NTM - 1) / NTM;                                       // per memory thread
     constexpr int CBPM = (CBU + NTM - 1) / NTM, DPM = (F * 8 + NTM - 1) / NTM;    // per memory thread
     constexpr int BPM = (BU + NTM - 1) / NTM;
 
@@ -1019,27 +1019,18 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     const int64_t vrows = row_end - row0;                    // >= 1
 
     if (memw) {
-        // ============ memory waves: x in, y out, B / C / C B^T / da staged ============
+        // ============ memory waves: x, B, C, C B^T and da staged into LDS ============
         const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
                                     (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
-        const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0,
-                                    (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
-        const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ), ystep = (uint32_t)(F * xrow_el * 4);
-        uint32_t xgoff[XPT], ygoff[YPT];
-        int xloff[XPT], yloff[YPT];
+        const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ);
+        uint32_t xgoff[XPT];
+        int xloff[XPT];
 #pragma unroll
         for (int m = 0; m < XPT; ++m) {
             const int u = mt + m * NTM;
             const int r = u / XUR, col = (u % XUR) * EPU;
             xgoff[m] = (u < XU) ? (uint32_t)((r * xrow_el + col) * ESZ) : kOOB;
             xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
-        }
-#pragma unroll
-        for (int m = 0; m < YPT; ++m) {
-            const int u = mt + m * NTM;
-            const int r = u / YUR, col = (u % YUR) * 4;
-            ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
-            yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
         }
         uint4 rx[2][XPT];            // x of tile t in slot t & 1
         // C B^T blocks of tile t in slot t & 1 (768 floats = CBU 16-byte units)
@@ -1138,25 +1129,11 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
 #pragma unroll
             for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
         };
-        // global stores of the y block staged in sY[buf] by tile k
-        auto flush_y = [&](int buf, int k) {
-            if (OUT) {
-                const uint32_t o = (uint32_t)k * ystep;
-#pragma unroll
-                for (int m = 0; m < YPT; ++m) {
-                    const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
-                    // non-temporal: y is written once and never read back here
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 2);
-                }
-            }
-        };
         // x is staged in registers two tiles ahead and in LDS one tile ahead
         // (buffer = tile parity). The C B^T blocks and da run one tile further
         // ahead, for the compute waves' decay matrices and scans. Each register
-        // slot is refilled right after it is drained, before this tile's y
-        // stores. y of tile k leaves from LDS during tile k+1; the first flush
-        // (tile -1) wraps to an offset beyond the resource and is dropped.
-        // Barriers match the compute waves' one for one.
+        // slot is refilled right after it is drained. Barriers match the
+        // compute waves' one for one.
         load_bc(0);
         load_x(0, 0);
         load_x(1, 1);
@@ -1191,7 +1168,6 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
             load_cb(0, k + 4);
             store_da(1, k + 3);
             load_da(1, k + 5);
-            flush_y(1, k - 1);
             __syncthreads();
             store_bc(0);             // B, C of tile k+2
             load_bc(k + 3);
@@ -1201,10 +1177,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
             load_cb(1, k + 5);
             store_da(0, k + 4);
             load_da(0, k + 6);
-            flush_y(0, k);
             __syncthreads();
         }
-        flush_y(1, k - 1);
         return;
     }
 
@@ -1218,6 +1192,34 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     // this wave's y fragment in the staged block: rows 16 I + l16, columns
     // 16 wv + 4 q .. + 3
     const int ysoff = l16 * LDY + 16 * wv + 4 * q;
+    // y of tile k leaves from the staged block during tile k+1, in whole
+    // 16-byte units of the block's rows, spread over the compute threads
+    // (their barrier wait has room for it; the memory waves have less)
+    constexpr int YPC = (YU + NTC - 1) / NTC;
+    const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0, (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
+    const uint32_t ystep = (uint32_t)(F * xrow_el * 4);
+    uint32_t ygoff[YPC];
+    int yloff[YPC];
+#pragma unroll
+    for (int m = 0; m < YPC; ++m) {
+        const int u = tid + m * NTC;
+        const int r = u / YUR, col = (u % YUR) * 4;
+        ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
+        yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
+    }
+    // global stores of the y block staged in sY[buf] by tile k; the first
+    // flush (tile -1) wraps to an offset beyond the resource and is dropped
+    auto flush_y = [&](int buf, int k) {
+        if (OUT) {
+            const uint32_t o = (uint32_t)k * ystep;
+#pragma unroll
+            for (int m = 0; m < YPC; ++m) {
+                const float4 v = *reinterpret_cast<const float4*>(&sY[buf][yloff[m]]);
+                // non-temporal: y is written once and never read back here
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs_y, ygoff[m] + o, 0, 2);
+            }
+        }
+    };
     float lam = 0.f;
 
     // K1 of tile k (prefix of da over the tile's fused rows, in base 2) by
@@ -1372,15 +1374,18 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     build_m(0);
     __syncthreads();
     for (int k = 0; k < nk; k += 2) {
+        flush_y(1, k - 1);
         scan(k + 2);
         build_m(k + 1);
         compute(0, k);
         __syncthreads();
+        flush_y(0, k);
         scan(k + 3);
         build_m(k + 2);
         compute(1, k + 1);
         __syncthreads();
     }
+    flush_y(1, ((nk + 1) & ~1) - 1);   // the last tile walked (past nk when nk is odd: dropped)
 
     // ---- epilogue
     float* dstate = nullptr;
