@@ -1733,12 +1733,27 @@ ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w
             if (!cols_ok(pl, w_req)) return SSD_ERR_UNSUPPORTED;
             pl.W = w_req;
         } else {
-            // the widest block that still gives every CU a workgroup, else
-            // the narrowest (segments then add workgroups)
+            // The widest block whose workgroups, multiplied by the segments
+            // that auto_segments adds when the blocks alone are too few, fill
+            // whole rounds of the device (at least 3/4 of the last round);
+            // else the width that fills best. A narrow block leaves a CU too
+            // little work to hide latency, which costs more than the extra
+            // state pass of the segments.
+            double best_fill = -1.0;
             for (int w : kColsWidths) {
                 if (!cols_ok(pl, w)) continue;
-                if (pl.W == 0 || slices / w >= cus) pl.W = w;
-                if (slices / w >= cus) break;
+                const int64_t blocks = slices / w;
+                const int64_t wgs = blocks * auto_segments(blocks, pl.nsub, cus);
+                const int64_t rounds = (wgs + cus - 1) / cus;
+                const double fill = (double)wgs / (double)(rounds * cus);
+                if (fill > best_fill) {
+                    best_fill = fill;
+                    pl.W = w;
+                }
+                if (fill >= 0.75) {
+                    pl.W = w;
+                    break;
+                }
             }
         }
         if (pl.W > 0) pl.kind = kColsPath;
