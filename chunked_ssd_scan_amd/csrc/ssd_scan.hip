@@ -720,7 +720,8 @@ struct TileArgs {
     float* final_state;
     float* ws_state;
     float* ws_misc;
-    const float* cbpack;   // from ssd_cb_pack_kernel (output pass only)
+    const float* cbpack;   // from ssd_cb_pack_kernel (output pass without rotation)
+    const float* theta;    // [b,T,H,N/2] or null (rotation walk only)
     int64_t T, H, G, N, R, P;
     int S, seg_items, nsub, log2R, Qt;
     int NB;                // column blocks per B/C group
@@ -851,6 +852,36 @@ __device__ __forceinline__ typename Ops<TI>::frag join_m(typename MBlock<TI>::ty
     }
 }
 
+// One bf16 pair (a, b) (low half a) turned by R(-phi), given (cos, sin) and
+// (-sin, cos) as bf16 pairs: (cos a + sin b, -sin a + cos b), each a two-term
+// dot product accumulated in fp32, rounded back to a bf16 pair (nearest even).
+__device__ __forceinline__ uint32_t rot_pair(uint32_t w, uint32_t cs, uint32_t ms) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    const bf16x2 v = __builtin_bit_cast(bf16x2, w);
+    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2, cs), 0.f, false);
+    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2, ms), 0.f, false);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+constexpr float kInv2Pi = 0.15915494309189535f;
+
+// phi - 2 pi k with k = round(phi / 2 pi): the running angle kept in
+// [-pi, pi] so that its fp32 sums keep their absolute precision. 2 pi is split
+// into a head with few significant bits (k * head is exact) and a tail
+// (Cody and Waite's argument reduction).
+__device__ __forceinline__ float wrap_angle(float phi) {
+    const float k = rintf(phi * kInv2Pi);
+    phi = fmaf(-k, 6.28125f, phi);
+    return fmaf(-k, 1.9353071795864769e-3f, phi);
+}
+
 // Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0).
 // Loads past `bytes` return zero and stores past it are dropped, which the
 // tile walk uses for ragged tails and for tiles beyond a segment's range.
@@ -915,36 +946,44 @@ __device__ __forceinline__ typename Ops<TI>::frag ld8_a8(const TI* p) {
 
 constexpr int cols_max_heads(int W) { return W / 2 + 1; }
 
-template <typename TI, int NP, int W>
+// Rotation tables of the rotating column walk hold (time step, pair) entries
+// of one tile: at most this many, i.e. (32 / R) * dstate / 2 <= kRotEntries.
+constexpr int kRotEntries = 512;
+constexpr int rot_row_stride(int NP) { return NP / 2; }
+
+template <typename TI, int NP, int W, bool ROT>
 constexpr int cols_lds_bytes(int mode) {
-    constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows, CW = 16 * W, MH = cols_max_heads(W);
+    constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows, CW = 16 * W;
+    constexpr int MH = ROT ? 1 : cols_max_heads(W);
     constexpr int ldx = x_row_stride<TI>(CW), ldb = tr_row_stride<TI>(NP), ldc = c_row_stride<TI>(NP);
     constexpr int mbytes = (int)sizeof(typename MBlock<TI>::type);
     const int out = mode == 0;
     return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
-           (out ? 2 * (F * ldc + epu) * esz + 2 * (768 + 4) * 4 + 2 * (F * y_row_stride(CW) + 4) * 4 +
-                      2 * MH * 3 * 64 * mbytes
+           (out ? 2 * (F * ldc + epu) * esz + 2 * (F * y_row_stride(CW) + 4) * 4 +
+                      (ROT ? 0 : 2 * (768 + 4) * 4 + 2 * MH * 3 * 64 * mbytes)
                 : 0) +
-           4 * MH * (3 * F + 1) * 4 + 4 * F * 8 * 4;
+           4 * MH * (3 * F + 1) * 4 + 4 * F * (ROT ? 1 : 8) * 4 +
+           (ROT ? 4 * (kRotEntries / (NP / 2) / 2) * rot_row_stride(NP) * 8 + (NP / 2) * 4 : 0);
 }
 
 // Memory waves per workgroup of the column-block walk: they issue every global
 // load of the walk (x, and the B, C, C B^T and da tiles), so the W compute
-// waves work from LDS and registers and only store y.
-constexpr int cols_mem_waves(int W) { return W >= 4 ? 2 : 1; }
+// waves work from LDS and registers and only store y. The rotating walk runs
+// four, one per SIMD, each turning one 16-row block of B or C.
+constexpr int cols_mem_waves(int W, bool rot) { return rot ? 4 : (W >= 4 ? 2 : 1); }
 
-template <typename TI, int NP, int W, int MODE>
-__global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(TileArgs a) {
+template <typename TI, int NP, int W, int MODE, bool ROT>
+__global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_kernel(TileArgs a) {
     using O = Ops<TI>;
     typedef typename O::frag frag;
     typedef typename MBlock<TI>::type mblk;
-    constexpr int MW = cols_mem_waves(W);
+    constexpr int MW = cols_mem_waves(W, ROT);
     constexpr int NTM = 64 * MW;                   // memory threads
     constexpr int NTC = 64 * W;                    // compute threads
     constexpr int F = kRows;
     constexpr int ESZ = (int)sizeof(TI);
     constexpr int CW = 16 * W;                     // columns per workgroup
-    constexpr int MH = cols_max_heads(W);
+    constexpr int MH = ROT ? 1 : cols_max_heads(W);  // a rotating block is one head
     constexpr int LDX = x_row_stride<TI>(CW);
     constexpr int LDB = tr_row_stride<TI>(NP);
     constexpr int LDC = c_row_stride<TI>(NP);      // rows 8 bytes off 16-byte alignment
@@ -956,21 +995,29 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     constexpr int XUR = CW / EPU, BUR = NP / EPU, YUR = CW / 4;   // 16-byte units per row
     constexpr int XU = F * XUR, BU = F * BUR, CBU = 768 * 4 / 16, YU = F * YUR;
     constexpr int XPT = (XU + NTM - 1) / NTM;                                       // per memory thread
-    constexpr int CBPM = (CBU + NTM - 1) / NTM, DPM = (F * 8 + NTM - 1) / NTM;    // per memory thread
+    constexpr int DAH = ROT ? 1 : 8;               // heads per staged da step
+    constexpr int CBPM = (CBU + NTM - 1) / NTM, DPM = (F * DAH + NTM - 1) / NTM;  // per memory thread
     constexpr int BPM = (BU + NTM - 1) / NTM;
 
     __shared__ __attribute__((aligned(16))) TI sX[2][F * LDX + EPU];
     __shared__ __attribute__((aligned(16))) TI sB[2][F * LDB + EPU];
     __shared__ __attribute__((aligned(16))) TI sC[OUT ? 2 : 1][OUT ? F * LDC + EPU : 1];
-    __shared__ __attribute__((aligned(16))) float sCB[OUT ? 2 : 1][OUT ? 768 + 4 : 1];
+    __shared__ __attribute__((aligned(16))) float sCB[(OUT && !ROT) ? 2 : 1][(OUT && !ROT) ? 768 + 4 : 1];
     __shared__ __attribute__((aligned(16))) float sY[OUT ? 2 : 1][OUT ? F * LDY + 4 : 1];
-    __shared__ __attribute__((aligned(16))) mblk sM[OUT ? 2 : 1][OUT ? MH * 3 * 64 : 1];
+    __shared__ __attribute__((aligned(16))) mblk sM[(OUT && !ROT) ? 2 : 1][(OUT && !ROT) ? MH * 3 * 64 : 1];
     // per-head tile vectors, ring of 4 tiles: cumulative log2-decay, exp2 of
     // it, the weight that carries row j to the tile end, and the tile decay
     __shared__ __attribute__((aligned(16))) float sCum[4][MH][F], sEin[4][MH][F], sW[4][MH][F];
     __shared__ float sCarry[4][MH];
     // da of the block's heads, staged by the memory waves: [tile ring][step][head]
-    __shared__ __attribute__((aligned(16))) float sDa[4][kRows][8];
+    __shared__ __attribute__((aligned(16))) float sDa[4][kRows][DAH];
+    // rotation: each memory wave's table for the time steps of its 16-row
+    // block, entry (step, pair) = {bf16 (cos, sin), bf16 (-sin, cos)} of the
+    // angle Phi from the segment start; Phi at the segment end
+    constexpr int RSTR = rot_row_stride(NP);
+    constexpr int QTM = ROT ? kRotEntries / (NP / 2) : 1;        // most steps per tile
+    __shared__ __attribute__((aligned(16))) uint2 sRot[ROT ? 4 : 1][ROT ? (QTM / 2) * RSTR : 1];
+    __shared__ float sPhi[ROT ? NP / 2 : 1];
 
     const int tid = threadIdx.x;
     // wave index made visibly uniform, so per-head pointers stay scalar
@@ -1033,31 +1080,15 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
             xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
         }
         uint4 rx[2][XPT];            // x of tile t in slot t & 1
-        // C B^T blocks of tile t in slot t & 1 (768 floats = CBU 16-byte units)
-        const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
-                                     OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
-        uint32_t cbgoff[CBPM];
-        int cbloff[CBPM];
+        auto load_x = [&](int slot, int k) {
+            const uint32_t o = (uint32_t)k * xstep;
 #pragma unroll
-        for (int m = 0; m < CBPM; ++m) {
-            const int u = mt + m * NTM;
-            cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
-            cbloff[m] = (u < CBU) ? u * 4 : 768;
-        }
-        float4 rcb[2][CBPM];
-        auto load_cb = [&](int slot, int k) {
-            if (OUT) {
-                const uint32_t o = (uint32_t)k * (768 * 4);
-#pragma unroll
-                for (int m = 0; m < CBPM; ++m)
-                    rcb[slot][m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs_cb, cbgoff[m] + o, 0, 0));
-            }
+            for (int m = 0; m < XPT; ++m)   // non-temporal: x is read once
+                rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, 2));
         };
-        auto store_cb = [&](int slot, int k) {
-            if (OUT) {
+        auto store_x = [&](int slot, int buf) {
 #pragma unroll
-                for (int m = 0; m < CBPM; ++m) *reinterpret_cast<float4*>(&sCB[k & 1][cbloff[m]]) = rcb[slot][m];
-            }
+            for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
         };
         // da of tile t in slot t & 1: element (step, head) of the block's heads,
         // lane-contiguous along the heads of a step (one short run per step)
@@ -1068,7 +1099,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
         uint32_t daoff[DPM];
 #pragma unroll
         for (int m = 0; m < DPM; ++m) {
-            const int u = mt + m * NTM, st = u >> 3, hd = u & 7;
+            const int u = mt + m * NTM, st = u / DAH, hd = u % DAH;
             daoff[m] = (st < Qt && hd < nhb) ? (uint32_t)((st * H + hd) * 4) : kOOB;
         }
         float rda[2][DPM];
@@ -1080,103 +1111,243 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
         };
         auto store_da = [&](int slot, int k) {
 #pragma unroll
-            for (int m = 0; m < DPM; ++m) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
+            for (int m = 0; m < DPM; ++m)
+                if (mt + m * NTM < F * DAH) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
         };
         // B and C of tile t: one register slot, refilled a tile ahead
         const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
         const auto rs_b = make_rsrc(static_cast<const TI*>(a.B) + (b * TR + row0) * brow_el + grp * N, bspan);
         const auto rs_c = make_rsrc(static_cast<const TI*>(a.C) + (b * TR + row0) * brow_el + grp * N, bspan);
         const uint32_t bstep = (uint32_t)(F * brow_el * ESZ);
-        // thread mt takes column unit mt % BUR of rows mt / BUR + m (NTM / BUR):
-        // the offsets advance by a fixed stride per unit
-        static_assert(NTM % BUR == 0, "memory threads cover whole B rows");
-        constexpr int RPM = NTM / BUR;               // rows per memory pass
-        const int br0 = mt / BUR, bcol = (mt % BUR) * EPU;
-        const bool bcol_ok = bcol < N;
-        const uint32_t bgo0 = (uint32_t)((br0 * brow_el + bcol) * ESZ);
-        const uint32_t bgstride = (uint32_t)(RPM * brow_el * ESZ);
-        const int blo0 = br0 * LDB + bcol, clo0 = br0 * LDC + bcol;
-        uint4 rb[BPM], rc[BPM];
-        auto load_bc = [&](int k) {
-            const uint32_t ob = (uint32_t)k * bstep;
-#pragma unroll
-            for (int m = 0; m < BPM; ++m) {
-                const uint32_t go = (bcol_ok && br0 + m * RPM < F) ? bgo0 + m * bgstride + ob : kOOB;
-                rb[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, go, 0, 0));
-                if (OUT) rc[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, go, 0, 0));
+        if constexpr (!ROT) {
+            // C B^T blocks of tile t in slot t & 1 (768 floats = CBU 16-byte units)
+            const auto rs_cb = make_rsrc(OUT ? a.cbpack + ((int64_t)(b * G + grp) * a.nsub + k0) * 768 : a.da,
+                                         OUT ? (uint32_t)((k1 - k0) * 768 * 4) : 0u);
+            uint32_t cbgoff[CBPM];
+            int cbloff[CBPM];
+    #pragma unroll
+            for (int m = 0; m < CBPM; ++m) {
+                const int u = mt + m * NTM;
+                cbgoff[m] = (u < CBU) ? (uint32_t)(u * 16) : kOOB;
+                cbloff[m] = (u < CBU) ? u * 4 : 768;
             }
-        };
-        auto store_bc = [&](int buf) {
-#pragma unroll
-            for (int m = 0; m < BPM; ++m) {
-                if (br0 + m * RPM >= F) continue;
-                *reinterpret_cast<uint4*>(&sB[buf][blo0 + m * RPM * LDB]) = rb[m];
+            float4 rcb[2][CBPM];
+            auto load_cb = [&](int slot, int k) {
                 if (OUT) {
-                    // two 8-byte halves: C rows are only 8-byte aligned
-                    uint2* d = reinterpret_cast<uint2*>(&sC[buf][clo0 + m * RPM * LDC]);
-                    d[0] = make_uint2(rc[m].x, rc[m].y);
-                    d[1] = make_uint2(rc[m].z, rc[m].w);
+                    const uint32_t o = (uint32_t)k * (768 * 4);
+    #pragma unroll
+                    for (int m = 0; m < CBPM; ++m)
+                        rcb[slot][m] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(rs_cb, cbgoff[m] + o, 0, 0));
                 }
-            }
-        };
-        auto load_x = [&](int slot, int k) {
-            const uint32_t o = (uint32_t)k * xstep;
-#pragma unroll
-            for (int m = 0; m < XPT; ++m)   // non-temporal: x is read once
-                rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, 2));
-        };
-        auto store_x = [&](int slot, int buf) {
-#pragma unroll
-            for (int m = 0; m < XPT; ++m) *reinterpret_cast<uint4*>(&sX[buf][xloff[m]]) = rx[slot][m];
-        };
-        // x is staged in registers two tiles ahead and in LDS one tile ahead
-        // (buffer = tile parity). The C B^T blocks and da run one tile further
-        // ahead, for the compute waves' decay matrices and scans. Each register
-        // slot is refilled right after it is drained. Barriers match the
-        // compute waves' one for one.
-        load_bc(0);
-        load_x(0, 0);
-        load_x(1, 1);
-        load_cb(0, 0);
-        load_cb(1, 1);
-        load_da(0, 0);
-        load_da(1, 1);
-        store_bc(0);
-        load_bc(1);
-        store_x(0, 0);
-        load_x(0, 2);
-        store_cb(0, 0);
-        load_cb(0, 2);
-        store_cb(1, 1);
-        load_cb(1, 3);
-        store_da(0, 0);
-        load_da(0, 2);
-        store_da(1, 1);
-        load_da(1, 3);
-        __syncthreads();             // da of tiles 0, 1 for the compute waves' scans
-        store_da(0, 2);
-        load_da(0, 4);
-        __syncthreads();
-        __syncthreads();
-        int k = 0;
-        for (; k < nk; k += 2) {
-            store_bc(1);             // B, C of tile k+1
-            load_bc(k + 2);
-            store_x(1, 1);           // x of tile k+1
-            load_x(1, k + 3);
-            store_cb(0, k + 2);
-            load_cb(0, k + 4);
-            store_da(1, k + 3);
-            load_da(1, k + 5);
+            };
+            auto store_cb = [&](int slot, int k) {
+                if (OUT) {
+    #pragma unroll
+                    for (int m = 0; m < CBPM; ++m) *reinterpret_cast<float4*>(&sCB[k & 1][cbloff[m]]) = rcb[slot][m];
+                }
+            };
+            // thread mt takes column unit mt % BUR of rows mt / BUR + m (NTM / BUR):
+            // the offsets advance by a fixed stride per unit
+            static_assert(NTM % BUR == 0, "memory threads cover whole B rows");
+            constexpr int RPM = NTM / BUR;               // rows per memory pass
+            const int br0 = mt / BUR, bcol = (mt % BUR) * EPU;
+            const bool bcol_ok = bcol < N;
+            const uint32_t bgo0 = (uint32_t)((br0 * brow_el + bcol) * ESZ);
+            const uint32_t bgstride = (uint32_t)(RPM * brow_el * ESZ);
+            const int blo0 = br0 * LDB + bcol, clo0 = br0 * LDC + bcol;
+            uint4 rb[BPM], rc[BPM];
+            auto load_bc = [&](int k) {
+                const uint32_t ob = (uint32_t)k * bstep;
+    #pragma unroll
+                for (int m = 0; m < BPM; ++m) {
+                    const uint32_t go = (bcol_ok && br0 + m * RPM < F) ? bgo0 + m * bgstride + ob : kOOB;
+                    rb[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_b, go, 0, 0));
+                    if (OUT) rc[m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_c, go, 0, 0));
+                }
+            };
+            auto store_bc = [&](int buf) {
+    #pragma unroll
+                for (int m = 0; m < BPM; ++m) {
+                    if (br0 + m * RPM >= F) continue;
+                    *reinterpret_cast<uint4*>(&sB[buf][blo0 + m * RPM * LDB]) = rb[m];
+                    if (OUT) {
+                        // two 8-byte halves: C rows are only 8-byte aligned
+                        uint2* d = reinterpret_cast<uint2*>(&sC[buf][clo0 + m * RPM * LDC]);
+                        d[0] = make_uint2(rc[m].x, rc[m].y);
+                        d[1] = make_uint2(rc[m].z, rc[m].w);
+                    }
+                }
+            };
+            // x is staged in registers two tiles ahead and in LDS one tile ahead
+            // (buffer = tile parity). The C B^T blocks and da run one tile further
+            // ahead, for the compute waves' decay matrices and scans. Each register
+            // slot is refilled right after it is drained. Barriers match the
+            // compute waves' one for one.
+            load_bc(0);
+            load_x(0, 0);
+            load_x(1, 1);
+            load_cb(0, 0);
+            load_cb(1, 1);
+            load_da(0, 0);
+            load_da(1, 1);
+            store_bc(0);
+            load_bc(1);
+            store_x(0, 0);
+            load_x(0, 2);
+            store_cb(0, 0);
+            load_cb(0, 2);
+            store_cb(1, 1);
+            load_cb(1, 3);
+            store_da(0, 0);
+            load_da(0, 2);
+            store_da(1, 1);
+            load_da(1, 3);
+            __syncthreads();             // da of tiles 0, 1 for the compute waves' scans
+            store_da(0, 2);
+            load_da(0, 4);
             __syncthreads();
-            store_bc(0);             // B, C of tile k+2
-            load_bc(k + 3);
-            store_x(0, 0);           // x of tile k+2
-            load_x(0, k + 4);
-            store_cb(1, k + 3);
-            load_cb(1, k + 5);
-            store_da(0, k + 4);
-            load_da(0, k + 6);
+            __syncthreads();
+            int k = 0;
+            for (; k < nk; k += 2) {
+                store_bc(1);             // B, C of tile k+1
+                load_bc(k + 2);
+                store_x(1, 1);           // x of tile k+1
+                load_x(1, k + 3);
+                store_cb(0, k + 2);
+                load_cb(0, k + 4);
+                store_da(1, k + 3);
+                load_da(1, k + 5);
+                __syncthreads();
+                store_bc(0);             // B, C of tile k+2
+                load_bc(k + 3);
+                store_x(0, 0);           // x of tile k+2
+                load_x(0, k + 4);
+                store_cb(1, k + 3);
+                load_cb(1, k + 5);
+                store_da(0, k + 4);
+                load_da(0, k + 6);
+                __syncthreads();
+            }
+        } else {
+            // ---- rotation: each memory wave turns one 16-row block of B or C
+            // by R(-Phi) on its way to LDS (the state pass needs B only); the
+            // compute waves form K2 (C B^T) from the turned tiles.
+            static_assert(MW == 4, "the rotating walk runs four memory waves");
+            constexpr int NPP = NP / 2;                  // state pairs
+            static_assert(NPP <= 64, "one lane per state pair");
+            const int gmat = mw >> 1, grb = mw & 1;      // matrix (0 = B, 1 = C) and row block
+            const bool gon = OUT || gmat == 0;
+            const int grow = 16 * grb + l16;             // this lane's row of the tile
+            const uint32_t goff = gon ? (uint32_t)((grow * brow_el + 8 * q) * ESZ) : kOOB;
+            const auto rs_g = gmat ? rs_c : rs_b;
+            uint4 rf[KS];
+            auto load_frags = [&](int k) {
+                const uint32_t o = (uint32_t)k * bstep;
+#pragma unroll
+                for (int s = 0; s < KS; ++s)
+                    rf[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, goff + s * 64 + o, 0, 0));
+            };
+            // angles: every memory wave keeps, per pair (lane), the running
+            // angle from the segment start (wrapped to [-pi, pi]) and tables
+            // (cos, sin) at the time steps of its own row block
+            const int spb = 16 >> log2R;                 // time steps per 16-row block
+            const int st0 = grb * spb;
+            const int64_t NH2 = N / 2;
+            const auto rs_th = make_rsrc(a.theta + ((b * T + step0) * H + hfirst) * NH2,
+                                         (uint32_t)((((vsteps - 1) * H) * NH2 + NH2) * 4));
+            const uint32_t throw_b = (uint32_t)(H * NH2 * 4), thstep = (uint32_t)(Qt * H * NH2 * 4);
+            const uint32_t thoff = (gon && lane < NH2) ? (uint32_t)(lane * 4) : kOOB;
+            float rth[QTM], carry = 0.f;
+            auto load_th = [&](int k) {
+                const uint32_t o = (uint32_t)k * thstep;
+#pragma unroll
+                for (int st = 0; st < QTM; ++st)
+                    rth[st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                            rs_th, st < Qt ? thoff + st * throw_b + o : kOOB, 0, 0));
+            };
+            uint2* tab = sRot[mw];
+            // table of the tile whose angles are in rth, then B~ / C~ of that
+            // tile into buffer buf (the table is this wave's own: no barrier)
+            auto rotate_tile = [&](int buf) {
+                if (!gon) return;
+                float run = 0.f;
+#pragma unroll
+                for (int st = 0; st < QTM; ++st) {
+                    if (st < Qt) {
+                        run += rth[st];
+                        if (st >= st0 && st < st0 + spb) {
+                            // the hardware sine and cosine take revolutions
+                            const float rev = (carry + run) * kInv2Pi;
+                            const float c = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+                            if (lane < NPP)
+                                tab[(st - st0) * RSTR + lane] = make_uint2(pack_bf16x2(c, sn), pack_bf16x2(-sn, c));
+                        }
+                    }
+                }
+                carry = wrap_angle(carry + run);
+#pragma unroll
+                for (int s = 0; s < KS; ++s) {
+                    // pairs 16 s + 4 q .. + 3 at the time step of this row
+                    const uint4* tp = reinterpret_cast<const uint4*>(tab + (l16 >> log2R) * RSTR + 16 * s + 4 * q);
+                    const uint4 t01 = tp[0], t23 = tp[1];
+                    const uint4 w = rf[s];
+                    const uint4 r = make_uint4(rot_pair(w.x, t01.x, t01.y), rot_pair(w.y, t01.z, t01.w),
+                                               rot_pair(w.z, t23.x, t23.y), rot_pair(w.w, t23.z, t23.w));
+                    if (gmat == 0) {
+                        *reinterpret_cast<uint4*>(&sB[buf][grow * LDB + 32 * s + 8 * q]) = r;
+                    } else {
+                        uint2* d = reinterpret_cast<uint2*>(&sC[buf][grow * LDC + 32 * s + 8 * q]);
+                        d[0] = make_uint2(r.x, r.y);
+                        d[1] = make_uint2(r.z, r.w);
+                    }
+                }
+            };
+            // Same schedule as the shared walk: tile t is turned and stored
+            // during tile t-1, its angles and B/C fragments loaded during t-2.
+            load_frags(0);
+            load_th(0);
+            load_x(0, 0);
+            load_x(1, 1);
+            load_da(0, 0);
+            load_da(1, 1);
+            store_x(0, 0);
+            load_x(0, 2);
+            store_da(0, 0);
+            load_da(0, 2);
+            store_da(1, 1);
+            load_da(1, 3);
+            rotate_tile(0);
+            load_frags(1);
+            load_th(1);
+            __syncthreads();             // da of tiles 0, 1; B~, C~, x of tile 0
+            store_da(0, 2);
+            load_da(0, 4);
+            __syncthreads();
+            __syncthreads();
+            int k = 0;
+            for (; k < nk; k += 2) {
+                rotate_tile(1);          // tile k+1
+                load_frags(k + 2);
+                load_th(k + 2);
+                store_x(1, 1);
+                load_x(1, k + 3);
+                store_da(1, k + 3);
+                load_da(1, k + 5);
+                __syncthreads();
+                rotate_tile(0);          // tile k+2
+                load_frags(k + 3);
+                load_th(k + 3);
+                store_x(0, 0);
+                load_x(0, k + 4);
+                store_da(0, k + 4);
+                load_da(0, k + 6);
+                __syncthreads();
+            }
+            // the angle at the segment end (tiles past it add zero)
+            if (mw == 0 && lane < NH2) {
+                sPhi[lane] = carry;
+                if (!OUT) a.ws_misc[(((int64_t)b * H + hfirst) * S + seg) * (1 + NH2) + 1 + lane] = carry;
+            }
             __syncthreads();
         }
         return;
@@ -1280,8 +1451,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
     float dsel[4];                                 // one-hot: this lane's diagonal slot
 #pragma unroll
     for (int v = 0; v < 4; ++v) dsel[v] = (l16 == 4 * q + v) ? 1.f : 0.f;
+    const float Dr = (ROT && OUT && a.D) ? a.D[h] : 0.f;   // D of the rotating block's head
     auto build_m = [&](int k) {
-        if (OUT) {
+        if constexpr (OUT && !ROT) {
 #pragma unroll
             for (int r = 0; r < UPW; ++r) {
                 const int u = wv + W * r;
@@ -1312,6 +1484,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
         if (OUT) {
             const TI* tC = sC[buf];
             f32x4 yacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            // rotating walk: K2 of the block's head from the turned tiles,
+            // blocks (J, I) = (0,0), (0,1), (1,1) of C B^T (rows j, columns i)
+            f32x4 cb00 = {0.f, 0.f, 0.f, 0.f}, cb01 = cb00, cb11 = cb00;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 float hv[8];
@@ -1321,8 +1496,17 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
                     hv[4 + v] = hs[2 * s + 1][v];
                 }
                 const frag hA = O::pack(hv);
-                yacc[0] = O::mma(hA, ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
-                yacc[1] = O::mma(hA, ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
+                const frag c0 = ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q);
+                const frag c1 = ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q);
+                yacc[0] = O::mma(hA, c0, yacc[0]);
+                yacc[1] = O::mma(hA, c1, yacc[1]);
+                if constexpr (ROT) {
+                    const frag b0 = O::ld8(tB + l16 * LDB + 32 * s + 8 * q);
+                    const frag b1 = O::ld8(tB + (16 + l16) * LDB + 32 * s + 8 * q);
+                    cb00 = O::mma(b0, c0, cb00);
+                    cb01 = O::mma(b0, c1, cb01);
+                    cb11 = O::mma(b1, c1, cb11);
+                }
             }
             const float e0 = sEin[vb][hl][l16], e1 = sEin[vb][hl][16 + l16];
 #pragma unroll
@@ -1330,8 +1514,34 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
                 yacc[0][v] *= e0;
                 yacc[1][v] *= e1;
             }
-            const mblk* mb = &sM[k & 1][hl * 3 * 64 + lane];
-            const mblk m00 = mb[0], m01 = mb[64], m11 = mb[128];
+            mblk m00, m01, m11;
+            if constexpr (!ROT) {
+                const mblk* mb = &sM[k & 1][hl * 3 * 64 + lane];
+                m00 = mb[0];
+                m01 = mb[64];
+                m11 = mb[128];
+            } else {
+                // the block's one head: its decay matrices from its C B^T
+                // blocks, zero where step(i) < step(j) (cum is non-increasing,
+                // so exp2(min(cum_i - cum_j, 0)) is exact where it counts)
+                const float* cum = sCum[vb][0];
+                const float4 cj0 = *reinterpret_cast<const float4*>(&cum[4 * q]);
+                const float4 cj1 = *reinterpret_cast<const float4*>(&cum[16 + 4 * q]);
+                const float ci0 = cum[l16], ci1 = cum[16 + l16];
+                const float cjv0[4] = {cj0.x, cj0.y, cj0.z, cj0.w}, cjv1[4] = {cj1.x, cj1.y, cj1.z, cj1.w};
+                float v0[4], v1[4], v2[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const bool k00 = (l16 >> log2R) >= ((4 * q + v) >> log2R);
+                    const bool k11 = ((16 + l16) >> log2R) >= ((16 + 4 * q + v) >> log2R);
+                    v0[v] = fmaf(dsel[v], Dr, k00 ? cb00[v] * __builtin_amdgcn_exp2f(fminf(ci0 - cjv0[v], 0.f)) : 0.f);
+                    v1[v] = cb01[v] * __builtin_amdgcn_exp2f(fminf(ci1 - cjv0[v], 0.f));
+                    v2[v] = fmaf(dsel[v], Dr, k11 ? cb11[v] * __builtin_amdgcn_exp2f(fminf(ci1 - cjv1[v], 0.f)) : 0.f);
+                }
+                m00 = pack_m<TI>(v0[0], v0[1], v0[2], v0[3]);
+                m01 = pack_m<TI>(v1[0], v1[1], v1[2], v1[3]);
+                m11 = pack_m<TI>(v2[0], v2[1], v2[2], v2[3]);
+            }
             const mblk zz = pack_m<TI>(0.f, 0.f, 0.f, 0.f);
             yacc[0] = O::mma(xa, join_m<TI>(m00, zz), yacc[0]);
             yacc[1] = O::mma(xa, join_m<TI>(m01, m11), yacc[1]);
@@ -1386,6 +1596,24 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W))) void ssd_cols_kernel(
         __syncthreads();
     }
     flush_y(1, ((nk + 1) & ~1) - 1);   // the last tile walked (past nk when nk is odd: dropped)
+
+    if constexpr (ROT) {
+        // back to the physical frame: h = R(Phi_end) g, Phi_end from the
+        // memory waves' angle walk
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < NTILE; ++t) {
+#pragma unroll
+            for (int v = 0; v < 4; v += 2) {
+                const int n = phi_row(t, 4 * q + v);   // even: pair (n, n + 1)
+                float sn, cs;
+                sincosf(sPhi[n >> 1], &sn, &cs);
+                const float g0 = hs[t][v], g1 = hs[t][v + 1];
+                hs[t][v] = cs * g0 - sn * g1;
+                hs[t][v + 1] = sn * g0 + cs * g1;
+            }
+        }
+    }
 
     // ---- epilogue
     float* dstate = nullptr;
@@ -1484,21 +1712,21 @@ constexpr int kLdsLimit = 160 * 1024;
 // Column-block widths (16-column slices per workgroup), preferred first.
 constexpr int kColsWidths[] = {10, 8, 6, 4, 2, 1};
 
-template <typename TI, int NP, int W, int MODE>
+template <typename TI, int NP, int W, int MODE, bool ROT>
 void* cols_ptr() {
-    if constexpr (cols_lds_bytes<TI, NP, W>(MODE) <= kLdsLimit)
-        return reinterpret_cast<void*>(&ssd_cols_kernel<TI, NP, W, MODE>);
+    if constexpr (cols_lds_bytes<TI, NP, W, ROT>(MODE) <= kLdsLimit)
+        return reinterpret_cast<void*>(&ssd_cols_kernel<TI, NP, W, MODE, ROT>);
     else
         return nullptr;  // does not fit one CU's LDS
 }
 
-template <typename TI, int W, int MODE>
+template <typename TI, int W, int MODE, bool ROT>
 void* cols_ptr_np(int NP) {
     switch (NP) {
-        case 32: return cols_ptr<TI, 32, W, MODE>();
-        case 64: return cols_ptr<TI, 64, W, MODE>();
-        case 128: return cols_ptr<TI, 128, W, MODE>();
-        case 256: return cols_ptr<TI, 256, W, MODE>();
+        case 32: return cols_ptr<TI, 32, W, MODE, ROT>();
+        case 64: return cols_ptr<TI, 64, W, MODE, ROT>();
+        case 128: return cols_ptr<TI, 128, W, MODE, ROT>();
+        case 256: return cols_ptr<TI, 256, W, MODE, ROT>();
     }
     return nullptr;
 }
@@ -1506,12 +1734,12 @@ void* cols_ptr_np(int NP) {
 template <typename TI, int MODE>
 void* cols_ptr_w(int w, int NP) {
     switch (w) {
-        case 1: return cols_ptr_np<TI, 1, MODE>(NP);
-        case 2: return cols_ptr_np<TI, 2, MODE>(NP);
-        case 4: return cols_ptr_np<TI, 4, MODE>(NP);
-        case 6: return cols_ptr_np<TI, 6, MODE>(NP);
-        case 8: return cols_ptr_np<TI, 8, MODE>(NP);
-        case 10: return cols_ptr_np<TI, 10, MODE>(NP);
+        case 1: return cols_ptr_np<TI, 1, MODE, false>(NP);
+        case 2: return cols_ptr_np<TI, 2, MODE, false>(NP);
+        case 4: return cols_ptr_np<TI, 4, MODE, false>(NP);
+        case 6: return cols_ptr_np<TI, 6, MODE, false>(NP);
+        case 8: return cols_ptr_np<TI, 8, MODE, false>(NP);
+        case 10: return cols_ptr_np<TI, 10, MODE, false>(NP);
     }
     return nullptr;
 }
@@ -1519,6 +1747,24 @@ void* cols_ptr_w(int w, int NP) {
 void* select_cols(int dtype, int mode, int w, int NP) {
     if (dtype == SSD_BF16) return mode ? cols_ptr_w<uint16_t, 1>(w, NP) : cols_ptr_w<uint16_t, 0>(w, NP);
     return mode ? cols_ptr_w<float, 1>(w, NP) : cols_ptr_w<float, 0>(w, NP);
+}
+
+// Rotating column walk: bf16 only, one head (headdim 64 or 128) per block,
+// dstate 64 or 128 (one table lane per state pair).
+void* select_cols_rot(int dtype, int mode, int w, int NP) {
+    if (dtype != SSD_BF16) return nullptr;
+    if (w == 4) {
+        switch (NP) {
+            case 64: return mode ? cols_ptr<uint16_t, 64, 4, 1, true>() : cols_ptr<uint16_t, 64, 4, 0, true>();
+            case 128: return mode ? cols_ptr<uint16_t, 128, 4, 1, true>() : cols_ptr<uint16_t, 128, 4, 0, true>();
+        }
+    } else if (w == 8) {
+        switch (NP) {
+            case 64: return mode ? cols_ptr<uint16_t, 64, 8, 1, true>() : cols_ptr<uint16_t, 64, 8, 0, true>();
+            case 128: return mode ? cols_ptr<uint16_t, 128, 8, 1, true>() : cols_ptr<uint16_t, 128, 8, 0, true>();
+        }
+    }
+    return nullptr;
 }
 
 template <typename TI>
@@ -1706,6 +1952,14 @@ bool cols_ok(const Plan& pl, int w) {
            select_cols(pl.dtype, 0, w, (int)pl.NP) && select_cols(pl.dtype, 1, w, (int)pl.NP);
 }
 
+// The rotating column walk takes one head per block and a rotation table of
+// (32 / R) steps x dstate / 2 pairs per tile.
+bool cols_rot_ok(const Plan& pl) {
+    const int w = (int)(pl.P / 16);
+    return pl.N >= 64 && (int64_t)pl.Qt * (pl.NP / 2) <= kRotEntries &&
+           select_cols_rot(pl.dtype, 0, w, (int)pl.NP) && select_cols_rot(pl.dtype, 1, w, (int)pl.NP);
+}
+
 // Kernel path, column-block width and segments. `w_req` and `segments` are
 // the caller's launch options (0 = automatic).
 ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w_req, Plan* out) {
@@ -1724,10 +1978,14 @@ ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w
     // the column-block walk addresses a segment with 32-bit offsets: keep
     // each segment, with the tiles prefetched past its end, under 2^30 bytes
     const int64_t esz = pl.dtype == SSD_BF16 ? 2 : 4;
-    const int64_t row_bytes = pl.H * pl.P * 4 > pl.G * pl.N * esz ? pl.H * pl.P * 4 : pl.G * pl.N * esz;
+    int64_t row_bytes = pl.H * pl.P * 4 > pl.G * pl.N * esz ? pl.H * pl.P * 4 : pl.G * pl.N * esz;
+    if (rot && pl.H * pl.N * 2 > row_bytes) row_bytes = pl.H * pl.N * 2;   // theta rows, per step
     const int64_t max_tiles = ((int64_t)1 << 30) / (kRows * row_bytes) - 4;
     const int cus = device_cus();
-    if (!rot && max_tiles >= 1) {
+    if (rot && max_tiles >= 1 && cols_rot_ok(pl)) {
+        pl.W = (int)(pl.P / 16);
+        pl.kind = kColsPath;
+    } else if (!rot && max_tiles >= 1) {
         const int64_t slices = pl.b * pl.G * (pl.H / pl.G) * (pl.P / 16);
         if (w_req > 0) {
             if (!cols_ok(pl, w_req)) return SSD_ERR_UNSUPPORTED;
@@ -1765,6 +2023,14 @@ ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w
         min_segments = (pl.nsub + max_tiles - 1) / max_tiles;
         units = pl.b * pl.H * (pl.P / 16) / pl.W;
         target = cus;
+        if (rot) {
+            // one-head blocks are small: fill every workgroup slot of the device
+            int per_cu = 0;
+            void* fn = select_cols_rot(pl.dtype, 0, pl.W, (int)pl.NP);
+            if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, 64 * (pl.W + cols_mem_waves(pl.W, true)), 0) ==
+                    hipSuccess && per_cu > 1)
+                target = (int64_t)cus * per_cu;
+        }
     }
     pl.S = segments > 0 ? segments : auto_segments(units, pl.nsub, target);
     if (pl.S > pl.nsub) pl.S = pl.nsub;
@@ -1782,9 +2048,9 @@ ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hip
     int64_t nwg = pl.b * pl.H * args.seg_items;
     unsigned threads = (unsigned)(4 * pl.P);
     if (pl.kind == kColsPath) {
-        fn = select_cols(pl.dtype, mode, pl.W, (int)pl.NP);
+        fn = rot ? select_cols_rot(pl.dtype, mode, pl.W, (int)pl.NP) : select_cols(pl.dtype, mode, pl.W, (int)pl.NP);
         nwg = pl.b * args.seg_items * pl.H * (pl.P / 16) / pl.W;
-        threads = (unsigned)(64 * (pl.W + cols_mem_waves(pl.W)));
+        threads = (unsigned)(64 * (pl.W + cols_mem_waves(pl.W, rot)));
     } else {
         fn = select_walk(pl.dtype, rot, mode, (int)pl.P, (int)pl.NP);
     }
@@ -1842,9 +2108,13 @@ const char* ssd_status_str(int32_t status) {
 
 size_t ssd_workspace_bytes(const ssd_dims* d, int64_t chunk_len, int64_t R) {
     if (!d || check_shape(d, chunk_len, R, false) != SSD_OK) return 0;
-    Plan pl;
+    // the larger of the plans without and with rotation
+    Plan pl, pr;
     if (make_plan(d, R, false, 0, 0, &pl) != SSD_OK) return 0;
-    return workspace_layout(pl, pl.kind == kWalkPath).total;
+    const size_t plain = workspace_layout(pl, pl.kind == kWalkPath).total;
+    if (d->dstate % 2 || make_plan(d, R, true, 0, 0, &pr) != SSD_OK) return plain;
+    const size_t rotated = workspace_layout(pr, true).total;
+    return plain > rotated ? plain : rotated;
 }
 
 ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, const void* B,
@@ -1889,8 +2159,10 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     if (st != SSD_OK) return st;
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
-    // shared-B/C column-block walk unless rotation (or the shape) needs the general walk
-    const bool shared = pl.kind == kColsPath;
+    // column-block walk (C B^T tile pack shared by the heads of a group unless
+    // rotated), or the general walk for shapes it does not cover
+    const bool cols = pl.kind == kColsPath;
+    const bool shared = cols && !rot;
     const WsLayout wl = workspace_layout(pl, !shared);
     void* ws = nullptr;
     int ws_entry = -1;
@@ -1904,7 +2176,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     float* ws_pack = shared ? reinterpret_cast<float*>(wsc + wl.state + wl.misc) : nullptr;
 
     ssd_status rs = SSD_OK;
-    if (!shared) {
+    if (!cols) {
         WalkArgs args;
         memset(&args, 0, sizeof(args));
         args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
@@ -1914,18 +2186,21 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
         args.ws_state = ws_state; args.ws_misc = ws_misc;
         rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
     } else {
-        // K2 once per (batch, group, tile), shared by every head of the group
-        void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
-        const int64_t ntiles = pl.b * pl.G * pl.nsub;
-        if (!pk || ntiles > 0x7fffffff) {
-            rs = SSD_ERR_UNSUPPORTED;
-        } else {
-            const void* Bp = B;
-            const void* Cp = C;
-            int64_t TRv = T * R, Gv = G, Nv = N;
-            int nsub = pl.nsub, l2r = pl.log2R;
-            void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub, (void*)&l2r};
-            if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        // without rotation K2 runs once per (batch, group, tile), shared by
+        // every head of the group; the rotating walk forms it per head
+        if (shared) {
+            void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
+            const int64_t ntiles = pl.b * pl.G * pl.nsub;
+            if (!pk || ntiles > 0x7fffffff) {
+                rs = SSD_ERR_UNSUPPORTED;
+            } else {
+                const void* Bp = B;
+                const void* Cp = C;
+                int64_t TRv = T * R, Gv = G, Nv = N;
+                int nsub = pl.nsub, l2r = pl.log2R;
+                void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub, (void*)&l2r};
+                if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+            }
         }
         if (rs == SSD_OK) {
             TileArgs args;
@@ -1935,8 +2210,9 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             args.T = T; args.H = H; args.G = G; args.N = N; args.R = R; args.P = P;
             args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
             args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
+            args.theta = theta;
             args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
-            rs = run_passes(pl, false, args, init_state, hs, opts ? opts->walk_events : nullptr);
+            rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
         }
     }
     if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;

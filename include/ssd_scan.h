@@ -107,7 +107,7 @@ typedef struct {
                                 (nheads / ngroups) * headdim / 16 and have a
                                 kernel for (dstate, dtype), else
                                 SSD_ERR_UNSUPPORTED. Ignored when theta is given
-                                (rotation uses the per-head walk). */
+                                (rotation walks one head per workgroup). */
     int32_t reserved[2];     /* must be zero */
     void *walk_events[2];    /* NULL, NULL: none. Two hipEvent_t (cast to void*)
                                 created by the caller: the library records

@@ -174,6 +174,32 @@ def test_block_widths(P, N, H, G, W, R, dtype, init, segments):
     check_full(inp, y, fin, TOL[dtype], f"P{P} N{N} H{H} G{G} W{W} R{R} {dtype} S{segments}")
 
 
+# The rotating column walk (bf16, headdim 64 or 128, dstate 64 or 128,
+# (32 / R) * dstate / 2 <= 512): one head per workgroup, B and C turned while
+# staged, K2 per head. Ragged lengths, several tiles, angles past 2 pi.
+ROT_COLS = [
+    # (P, N, R, T, H, G, init, segments)
+    (64, 128, 4, 173, 3, 1, True, 1),
+    (64, 128, 4, 300, 2, 1, True, 3),
+    (64, 64, 2, 97, 4, 2, False, 1),
+    (128, 128, 4, 65, 2, 1, True, 2),
+    (128, 64, 8, 40, 3, 1, False, 1),
+    (64, 128, 16, 50, 2, 1, True, 2),
+    (64, 128, 4, 1, 2, 1, True, 1),
+    (64, 128, 8, 1000, 1, 1, True, 4),
+]
+
+
+@pytest.mark.parametrize("P,N,R,T,H,G,init,segments", ROT_COLS)
+def test_rotating_column_walk(P, N, R, T, H, G, init, segments):
+    shape = si.small_shape(batch=2, seqlen=T, nheads=H, ngroups=G, headdim=P, dstate=N,
+                           mimo_rank=R, dtype="bf16", rotation=True, init_state=init,
+                           dt_shift=4.0)
+    inp = si.make_inputs(shape, seed=P + N + R + T)
+    y, fin = run_gpu(inp, segments=segments)
+    check_full(inp, y, fin, TOL["bf16"], f"rot P{P} N{N} R{R} T{T} H{H} G{G} S{segments}")
+
+
 @pytest.mark.parametrize("segments", [1, 2, 3, 7, 64])
 def test_segments(segments):
     # splitting the sequence into parallel segments joined by the carry pass
