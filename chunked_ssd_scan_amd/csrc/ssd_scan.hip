@@ -852,18 +852,6 @@ __device__ __forceinline__ typename Ops<TI>::frag join_m(typename MBlock<TI>::ty
     }
 }
 
-// One bf16 pair (a, b) (low half a) turned by R(-phi), given (cos, sin) and
-// (-sin, cos) as bf16 pairs: (cos a + sin b, -sin a + cos b), each a two-term
-// dot product accumulated in fp32, rounded back to a bf16 pair (nearest even).
-__device__ __forceinline__ uint32_t rot_pair(uint32_t w, uint32_t cs, uint32_t ms) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    typedef __attribute__((ext_vector_type(2))) float f32x2;
-    const bf16x2 v = __builtin_bit_cast(bf16x2, w);
-    const float r0 = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2, cs), 0.f, false);
-    const float r1 = __builtin_amdgcn_fdot2_f32_bf16(v, __builtin_bit_cast(bf16x2, ms), 0.f, false);
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){r0, r1}, bf16x2));
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
     typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -949,7 +937,9 @@ constexpr int cols_max_heads(int W) { return W / 2 + 1; }
 // Rotation tables of the rotating column walk hold (time step, pair) entries
 // of one tile: at most this many, i.e. (32 / R) * dstate / 2 <= kRotEntries.
 constexpr int kRotEntries = 512;
-constexpr int rot_row_stride(int NP) { return NP / 2; }
+// row (one time step) of a memory wave's rotation table: per pair group of two
+// state pairs, the four rows of its 4x4 turning matrix (8 bytes each)
+constexpr int rot_row_stride(int NP) { return (NP / 4) * 4; }
 
 template <typename TI, int NP, int W, bool ROT>
 constexpr int cols_lds_bytes(int mode) {
@@ -1012,8 +1002,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     // da of the block's heads, staged by the memory waves: [tile ring][step][head]
     __shared__ __attribute__((aligned(16))) float sDa[4][kRows][DAH];
     // rotation: each memory wave's table for the time steps of its 16-row
-    // block, entry (step, pair) = {bf16 (cos, sin), bf16 (-sin, cos)} of the
-    // angle Phi from the segment start; Phi at the segment end
+    // block: per step and pair group (2 state pairs), the four rows of the bf16
+    // matrix that turns them by R(-Phi), Phi the angle from the segment start;
+    // Phi at the segment end
     constexpr int RSTR = rot_row_stride(NP);
     constexpr int QTM = ROT ? kRotEntries / (NP / 2) : 1;        // most steps per tile
     __shared__ __attribute__((aligned(16))) uint2 sRot[ROT ? 4 : 1][ROT ? (QTM / 2) * RSTR : 1];
@@ -1064,6 +1055,26 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     const int64_t row0 = (int64_t)k0 * F;
     const int64_t row_end = ((int64_t)k1 * F < TR) ? (int64_t)k1 * F : TR;
     const int64_t vrows = row_end - row0;                    // >= 1
+
+    // K1 of tile k for head hd of the block (prefix of da over the tile's
+    // fused rows, in base 2), from the da the memory waves staged. Lane f < 32
+    // takes step f >> log2R for the first rank of each step (0 for the others),
+    // so the scan over fused rows yields cum per row.
+    const bool da_lane = (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
+    float lam = 0.f;   // sum of da over the segment (lane 0 of the scanning wave)
+    auto scan_head = [&](int k, int hd) {
+        const float dv = da_lane ? sDa[k & 3][lane >> log2R][hd] : 0.f;
+        const float cum = wave_prefix32(dv);
+        const float last = __shfl(cum, F - 1);
+        const float c2 = cum * kLog2e, l2 = last * kLog2e;
+        if (lane < F) {
+            sCum[k & 3][hd][lane] = c2;
+            sEin[k & 3][hd][lane] = __builtin_amdgcn_exp2f(c2);
+            sW[k & 3][hd][lane] = __builtin_amdgcn_exp2f(l2 - c2);
+        }
+        if (lane == 0) sCarry[k & 3][hd] = __builtin_amdgcn_exp2f(l2);
+        lam += last;
+    };
 
     if (memw) {
         // ============ memory waves: x, B, C, C B^T and da staged into LDS ============
@@ -1240,12 +1251,14 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             const int grow = 16 * grb + l16;             // this lane's row of the tile
             const uint32_t goff = gon ? (uint32_t)((grow * brow_el + 8 * q) * ESZ) : kOOB;
             const auto rs_g = gmat ? rs_c : rs_b;
-            uint4 rf[KS];
-            auto load_frags = [&](int k) {
+            // B / C fragments and angles of tile t in register slot t & 1,
+            // loaded a full tile before they are used
+            uint4 rf[2][KS];
+            auto load_frags = [&](int slot, int k) {
                 const uint32_t o = (uint32_t)k * bstep;
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
-                    rf[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, goff + s * 64 + o, 0, 0));
+                    rf[slot][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, goff + s * 64 + o, 0, 0));
             };
             // angles: every memory wave keeps, per pair (lane), the running
             // angle from the segment start (wrapped to [-pi, pi]) and tables
@@ -1257,42 +1270,60 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                                          (uint32_t)((((vsteps - 1) * H) * NH2 + NH2) * 4));
             const uint32_t throw_b = (uint32_t)(H * NH2 * 4), thstep = (uint32_t)(Qt * H * NH2 * 4);
             const uint32_t thoff = (gon && lane < NH2) ? (uint32_t)(lane * 4) : kOOB;
-            float rth[QTM], carry = 0.f;
-            auto load_th = [&](int k) {
+            float rth[2][QTM], carry = 0.f;
+            auto load_th = [&](int slot, int k) {
                 const uint32_t o = (uint32_t)k * thstep;
 #pragma unroll
                 for (int st = 0; st < QTM; ++st)
-                    rth[st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                            rs_th, st < Qt ? thoff + st * throw_b + o : kOOB, 0, 0));
+                    rth[slot][st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                                  rs_th, st < Qt ? thoff + st * throw_b + o : kOOB, 0, 0));
             };
             uint2* tab = sRot[mw];
             // table of the tile whose angles are in rth, then B~ / C~ of that
-            // tile into buffer buf (the table is this wave's own: no barrier)
-            auto rotate_tile = [&](int buf) {
+            // tile into buffer buf (the table is this wave's own: no barrier).
+            // The turn is a 4x4x4 MFMA per pair group: its 16 blocks are 4-lane
+            // groups, i.e. 4 consecutive rows of one time step (R >= 4) and the
+            // same 2 pairs. Block row e of the matrix (lane 4b + e) is
+            //   e = 0: (c0, s0, 0, 0)   e = 1: (-s0, c0, 0, 0)
+            //   e = 2: (0, 0, c1, s1)   e = 3: (0, 0, -s1, c1)
+            // and lane 4b + r contributes its own row r of B or C, so that
+            // lane 4b + r receives out[r][e] = sum_k M[e][k] in[r][k] in slot e.
+            auto rotate_tile = [&](int buf, int slot) {
                 if (!gon) return;
                 float run = 0.f;
 #pragma unroll
                 for (int st = 0; st < QTM; ++st) {
                     if (st < Qt) {
-                        run += rth[st];
+                        run += rth[slot][st];
                         if (st >= st0 && st < st0 + spb) {
                             // the hardware sine and cosine take revolutions
                             const float rev = (carry + run) * kInv2Pi;
                             const float c = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
-                            if (lane < NPP)
-                                tab[(st - st0) * RSTR + lane] = make_uint2(pack_bf16x2(c, sn), pack_bf16x2(-sn, c));
+                            if (lane < NPP) {
+                                const uint32_t cs = pack_bf16x2(c, sn), ms = pack_bf16x2(-sn, c);
+                                const int h = lane & 1;
+                                uint2* e0 = tab + (st - st0) * RSTR + (lane >> 1) * 4 + 2 * h;
+                                e0[0] = h ? make_uint2(0u, cs) : make_uint2(cs, 0u);
+                                e0[1] = h ? make_uint2(0u, ms) : make_uint2(ms, 0u);
+                            }
                         }
                     }
                 }
                 carry = wrap_angle(carry + run);
+                typedef __attribute__((ext_vector_type(4))) short s16x4;
+                const uint2* trow = tab + (l16 >> log2R) * RSTR + (lane & 3);
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
-                    // pairs 16 s + 4 q .. + 3 at the time step of this row
-                    const uint4* tp = reinterpret_cast<const uint4*>(tab + (l16 >> log2R) * RSTR + 16 * s + 4 * q);
-                    const uint4 t01 = tp[0], t23 = tp[1];
-                    const uint4 w = rf[s];
-                    const uint4 r = make_uint4(rot_pair(w.x, t01.x, t01.y), rot_pair(w.y, t01.z, t01.w),
-                                               rot_pair(w.z, t23.x, t23.y), rot_pair(w.w, t23.z, t23.w));
+                    // pair groups 8 s + 2 q and 8 s + 2 q + 1 of this row's step
+                    const uint2 m0 = trow[(8 * s + 2 * q) * 4], m1 = trow[(8 * s + 2 * q + 1) * 4];
+                    const uint4 w = rf[slot][s];
+                    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4 d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                        __builtin_bit_cast(s16x4, m0), __builtin_bit_cast(s16x4, make_uint2(w.x, w.y)), zero4, 0, 0, 0);
+                    const f32x4 d1 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
+                        __builtin_bit_cast(s16x4, m1), __builtin_bit_cast(s16x4, make_uint2(w.z, w.w)), zero4, 0, 0, 0);
+                    const uint4 r = make_uint4(pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]),
+                                               pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]));
                     if (gmat == 0) {
                         *reinterpret_cast<uint4*>(&sB[buf][grow * LDB + 32 * s + 8 * q]) = r;
                     } else {
@@ -1302,10 +1333,13 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                     }
                 }
             };
-            // Same schedule as the shared walk: tile t is turned and stored
-            // during tile t-1, its angles and B/C fragments loaded during t-2.
-            load_frags(0);
-            load_th(0);
+            // Tile t is turned and stored during tile t-1; its angles and B/C
+            // fragments are loaded during tile t-3, as soon as their register
+            // slot drains, so that more than a tile of work covers the latency.
+            load_frags(0, 0);
+            load_th(0, 0);
+            load_frags(1, 1);
+            load_th(1, 1);
             load_x(0, 0);
             load_x(1, 1);
             load_da(0, 0);
@@ -1316,9 +1350,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             load_da(0, 2);
             store_da(1, 1);
             load_da(1, 3);
-            rotate_tile(0);
-            load_frags(1);
-            load_th(1);
+            rotate_tile(0, 0);
+            load_frags(0, 2);
+            load_th(0, 2);
             __syncthreads();             // da of tiles 0, 1; B~, C~, x of tile 0
             store_da(0, 2);
             load_da(0, 4);
@@ -1326,17 +1360,17 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             __syncthreads();
             int k = 0;
             for (; k < nk; k += 2) {
-                rotate_tile(1);          // tile k+1
-                load_frags(k + 2);
-                load_th(k + 2);
+                rotate_tile(1, 1);       // tile k+1
+                load_frags(1, k + 3);
+                load_th(1, k + 3);
                 store_x(1, 1);
                 load_x(1, k + 3);
                 store_da(1, k + 3);
                 load_da(1, k + 5);
                 __syncthreads();
-                rotate_tile(0);          // tile k+2
-                load_frags(k + 3);
-                load_th(k + 3);
+                rotate_tile(0, 0);       // tile k+2
+                load_frags(0, k + 4);
+                load_th(0, k + 4);
                 store_x(0, 0);
                 load_x(0, k + 4);
                 store_da(0, k + 4);
@@ -1356,10 +1390,6 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     // ================= compute waves =================
     // wave w < nhb scans the decays of head hfirst + w
     const bool scanner = wv < nhb;
-    // da: lane f < 32 of a scanning wave takes step f >> log2R for the first
-    // rank of each step (0 for the others), so the scan over fused rows
-    // yields cum per row
-    const bool da_lane = (lane < F) && ((lane & ((1 << log2R) - 1)) == 0);
     // this wave's y fragment in the staged block: rows 16 I + l16, columns
     // 16 wv + 4 q .. + 3
     const int ysoff = l16 * LDY + 16 * wv + 4 * q;
@@ -1391,24 +1421,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             }
         }
     };
-    float lam = 0.f;
-
-    // K1 of tile k (prefix of da over the tile's fused rows, in base 2) by
-    // the scanning waves, from the da the memory waves staged
+    // the scanning waves: wave w < nhb scans head hfirst + w
     auto scan = [&](int k) {
-        if (scanner) {
-            const float dv = da_lane ? sDa[k & 3][lane >> log2R][wv] : 0.f;
-            const float cum = wave_prefix32(dv);
-            const float last = __shfl(cum, F - 1);
-            const float c2 = cum * kLog2e, l2 = last * kLog2e;
-            if (lane < F) {
-                sCum[k & 3][wv][lane] = c2;
-                sEin[k & 3][wv][lane] = __builtin_amdgcn_exp2f(c2);
-                sW[k & 3][wv][lane] = __builtin_amdgcn_exp2f(l2 - c2);
-            }
-            if (lane == 0) sCarry[k & 3][wv] = __builtin_amdgcn_exp2f(l2);
-            lam += last;
-        }
+        if (scanner) scan_head(k, wv);
     };
 
     // ---- state (physical frame)
@@ -1952,11 +1967,12 @@ bool cols_ok(const Plan& pl, int w) {
            select_cols(pl.dtype, 0, w, (int)pl.NP) && select_cols(pl.dtype, 1, w, (int)pl.NP);
 }
 
-// The rotating column walk takes one head per block and a rotation table of
-// (32 / R) steps x dstate / 2 pairs per tile.
+// The rotating column walk takes one head per block, R >= 4 (a 4-row group of
+// a tile is one time step) and a rotation table of (32 / R) steps x dstate / 2
+// pairs per tile.
 bool cols_rot_ok(const Plan& pl) {
     const int w = (int)(pl.P / 16);
-    return pl.N >= 64 && (int64_t)pl.Qt * (pl.NP / 2) <= kRotEntries &&
+    return pl.N >= 64 && pl.R >= 4 && (int64_t)pl.Qt * (pl.NP / 2) <= kRotEntries &&
            select_cols_rot(pl.dtype, 0, w, (int)pl.NP) && select_cols_rot(pl.dtype, 1, w, (int)pl.NP);
 }
 
