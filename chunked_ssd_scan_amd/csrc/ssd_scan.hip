@@ -968,6 +968,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     typedef typename O::frag frag;
     typedef typename MBlock<TI>::type mblk;
     constexpr int MW = cols_mem_waves(W, ROT);
+    static_assert(!ROT || (W & (W - 1)) == 0, "the rotating walk deals tiles to a power-of-two wave count");
     constexpr int NTM = 64 * MW;                   // memory threads
     constexpr int NTC = 64 * W;                    // compute threads
     constexpr int F = kRows;
@@ -1009,6 +1010,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     constexpr int QTM = ROT ? kRotEntries / (NP / 2) : 1;        // most steps per tile
     __shared__ __attribute__((aligned(16))) uint2 sRot[ROT ? 4 : 1][ROT ? (QTM / 2) * RSTR : 1];
     __shared__ float sPhi[ROT ? NP / 2 : 1];
+    __shared__ float sLam[ROT ? W : 1];   // partial sums of da per compute wave
 
     const int tid = threadIdx.x;
     // wave index made visibly uniform, so per-head pointers stay scalar
@@ -1244,6 +1246,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             // by R(-Phi) on its way to LDS (the state pass needs B only); the
             // compute waves form K2 (C B^T) from the turned tiles.
             static_assert(MW == 4, "the rotating walk runs four memory waves");
+            // their turn of the next tile is the longer chain of a tile: issue
+            // ahead of the compute wave sharing the SIMD
+            __builtin_amdgcn_s_setprio(1);
             constexpr int NPP = NP / 2;                  // state pairs
             static_assert(NPP <= 64, "one lane per state pair");
             const int gmat = mw >> 1, grb = mw & 1;      // matrix (0 = B, 1 = C) and row block
@@ -1421,9 +1426,14 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             }
         }
     };
-    // the scanning waves: wave w < nhb scans head hfirst + w
+    // the scanning waves: wave w < nhb scans head hfirst + w; in the rotating
+    // walk (one head) the compute waves take the tiles in turn
     auto scan = [&](int k) {
-        if (scanner) scan_head(k, wv);
+        if constexpr (ROT) {
+            if (wv == (k & (W - 1))) scan_head(k, 0);
+        } else {
+            if (scanner) scan_head(k, wv);
+        }
     };
 
     // ---- state (physical frame)
@@ -1614,8 +1624,16 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
 
     if constexpr (ROT) {
         // back to the physical frame: h = R(Phi_end) g, Phi_end from the
-        // memory waves' angle walk
+        // memory waves' angle walk. The segment's sum of da, from the
+        // compute waves' partial sums, goes to wave 0.
+        if (lane == 0) sLam[wv] = lam;
         __syncthreads();
+        if (wv == 0) {
+            float tot = 0.f;
+#pragma unroll
+            for (int w = 0; w < W; ++w) tot += sLam[w];
+            lam = tot;
+        }
 #pragma unroll
         for (int t = 0; t < NTILE; ++t) {
 #pragma unroll
