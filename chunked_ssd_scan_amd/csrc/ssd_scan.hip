@@ -1125,7 +1125,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
         auto store_da = [&](int slot, int k) {
 #pragma unroll
             for (int m = 0; m < DPM; ++m)
-                if (mt + m * NTM < F * DAH) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
+                // (the shared walk's units fill the ring slot exactly; an
+                // unneeded guard there costs registers)
+                if (!ROT || mt + m * NTM < F * DAH) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
         };
         // B and C of tile t: one register slot, refilled a tile ahead
         const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
@@ -1521,16 +1523,19 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                     hv[4 + v] = hs[2 * s + 1][v];
                 }
                 const frag hA = O::pack(hv);
-                const frag c0 = ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q);
-                const frag c1 = ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q);
-                yacc[0] = O::mma(hA, c0, yacc[0]);
-                yacc[1] = O::mma(hA, c1, yacc[1]);
                 if constexpr (ROT) {
+                    const frag c0 = ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q);
+                    const frag c1 = ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q);
+                    yacc[0] = O::mma(hA, c0, yacc[0]);
+                    yacc[1] = O::mma(hA, c1, yacc[1]);
                     const frag b0 = O::ld8(tB + l16 * LDB + 32 * s + 8 * q);
                     const frag b1 = O::ld8(tB + (16 + l16) * LDB + 32 * s + 8 * q);
                     cb00 = O::mma(b0, c0, cb00);
                     cb01 = O::mma(b0, c1, cb01);
                     cb11 = O::mma(b1, c1, cb11);
+                } else {
+                    yacc[0] = O::mma(hA, ld8_a8<TI>(tC + l16 * LDC + 32 * s + 8 * q), yacc[0]);
+                    yacc[1] = O::mma(hA, ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q), yacc[1]);
                 }
             }
             const float e0 = sEin[vb][hl][l16], e1 = sEin[vb][hl][16 + l16];
