@@ -164,8 +164,9 @@ struct WalkArgs {
     float* ws_state;       // [b*H][S][P][N] segment states / carries
     float* ws_misc;        // [b*H][S][1 + N/2]: Lambda, Phi per pair
     int64_t T, H, G, N, R;
-    int S;                 // segments
-    int seg_items;         // segments this launch covers (S or S-1)
+    int S;                 // segments of this launch's division of the sequence
+    int seg_items;         // segments this launch covers
+    int SF;                // output pass: state-pass segments per segment
     int nsub;              // tiles per sequence
     int log2R;
     int Qt;                // time steps per tile (32 / R)
@@ -232,7 +233,7 @@ __global__ __launch_bounds__(4 * P) void ssd_walk_kernel(WalkArgs a) {
             if (S == 1)
                 src = a.init ? a.init + bh * P * N : nullptr;
             else
-                src = a.ws_state + (bh * S + seg) * P * N;
+                src = a.ws_state + (bh * S + seg) * a.SF * P * N;
         }
 #pragma unroll
         for (int t = 0; t < NTILE; ++t) {
@@ -724,6 +725,7 @@ struct TileArgs {
     const float* theta;    // [b,T,H,N/2] or null (rotation walk only)
     int64_t T, H, G, N, R, P;
     int S, seg_items, nsub, log2R, Qt;
+    int SF;                // output pass: state-pass segments per segment
     int NB;                // column blocks per B/C group
 };
 
@@ -1446,7 +1448,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             if (S == 1)
                 src = a.init ? a.init + bh * P * N : nullptr;
             else
-                src = a.ws_state + (bh * S + seg) * P * N;
+                src = a.ws_state + (bh * S + seg) * a.SF * P * N;
         }
         // unconditional loads (clamped index), then one select: lets the
         // loads issue back to back
@@ -1676,12 +1678,13 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
 
 // Pass B: carry states across segments, one thread per state pair (p, k).
 //   c_0 = init (or 0);  c_{s+1} = exp(Lambda_s) R(Phi_s) c_s + local_s
-// On entry ws_state slot s+1 holds local_s (segment s from a zero state); on
-// exit slot s holds c_s, the state entering segment s (slot 0: a copy of init).
+// over the S segments of the state pass, for s < upto. On entry ws_state slot
+// s+1 holds local_s (segment s from a zero state); on exit slot s holds c_s,
+// the state entering segment s (slot 0: a copy of init).
 __global__ __launch_bounds__(256) void ssd_carry_kernel(const float* __restrict__ init,
                                                        float* __restrict__ ws_state,
                                                        const float* __restrict__ ws_misc,
-                                                       int64_t P, int64_t N, int S, int rot) {
+                                                       int64_t P, int64_t N, int S, int upto, int rot) {
     const int64_t bh = blockIdx.y;
     const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (pair >= P * (N / 2)) return;
@@ -1695,7 +1698,7 @@ __global__ __launch_bounds__(256) void ssd_carry_kernel(const float* __restrict_
     float* st0 = ws_state + bh * S * P * N + off;
     st0[0] = c0;
     st0[1] = c1;
-    for (int s = 0; s + 1 < S; ++s) {
+    for (int s = 0; s < upto; ++s) {
         const float* misc = ws_misc + (bh * S + s) * (1 + N / 2);
         float* st = ws_state + (bh * S + s + 1) * P * N + off;
         const float dec = __expf(misc[0]);
@@ -1830,6 +1833,7 @@ enum PathKind { kWalkPath = 0, kColsPath = 1 };
 struct Plan {
     int64_t b, T, H, P, N, G, R, NP;
     int dtype, S, nsub, Qt, log2R;
+    int SF;    // state-pass segments per output segment (the state pass divides finer)
     int kind;  // PathKind
     int W;     // column-block width in 16-column slices (column-block walk)
 };
@@ -1956,10 +1960,10 @@ struct WsLayout {
 
 WsLayout workspace_layout(const Plan& pl, bool no_pack) {
     WsLayout w{0, 0, 0, 0};
-    const size_t bh = (size_t)(pl.b * pl.H);
+    const size_t bh = (size_t)(pl.b * pl.H), sa = (size_t)pl.S * pl.SF;
     if (pl.S > 1) {
-        w.state = align256(bh * pl.S * pl.P * pl.N * sizeof(float));
-        w.misc = align256(bh * pl.S * (1 + pl.N / 2) * sizeof(float));
+        w.state = align256(bh * sa * pl.P * pl.N * sizeof(float));
+        w.misc = align256(bh * sa * (1 + pl.N / 2) * sizeof(float));
     }
     if (!no_pack) w.pack = align256((size_t)(pl.b * pl.G) * pl.nsub * 768 * sizeof(float));
     w.total = w.state + w.misc + w.pack;
@@ -2013,6 +2017,7 @@ ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w
     pl.nsub = (int)((pl.T * R + kRows - 1) / kRows);
     pl.kind = kWalkPath;
     pl.W = 0;
+    pl.SF = 1;
 
     // the column-block walk addresses a segment with 32-bit offsets: keep
     // each segment, with the tiles prefetched past its end, under 2^30 bytes
@@ -2075,6 +2080,15 @@ ssd_status make_plan(const ssd_dims* d, int64_t R, bool rot, int segments, int w
     if (pl.S > pl.nsub) pl.S = pl.nsub;
     if (pl.S < min_segments) pl.S = (int)min_segments;
     if (pl.S < 1) pl.S = 1;
+    // The state pass runs over all but the last segment; when halving its
+    // segments still leaves one workgroup per CU at most, it divides each
+    // segment in two (the carry pass then joins twice as many segments, and
+    // the output pass starts from every other carried state). Measured: the
+    // rotated Mamba-3 workload's state pass goes from 128 to 256 workgroups of
+    // half the length (0.56 -> 0.45 ms a call); where the halves would need a
+    // second round of workgroups it does not pay.
+    pl.SF = 1;
+    if (pl.S > 1 && pl.nsub / (2 * pl.S) >= 4 && units * (2 * pl.S - 2) <= (int64_t)cus) pl.SF = 2;
     *out = pl;
     return SSD_OK;
 }
@@ -2107,17 +2121,21 @@ template <typename Args>
 ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs,
                       void* const* walk_events) {
     ssd_status rs = SSD_OK;
+    const int SA = pl.S * pl.SF;   // segments of the state pass
+    args.SF = pl.SF;
     if (pl.S > 1) {
-        args.seg_items = pl.S - 1;
+        args.S = SA;
+        args.seg_items = SA - pl.SF;
         rs = launch_walk(pl, 1, rot, args, hs);
         if (rs == SSD_OK) {
             dim3 grid((unsigned)((pl.P * (pl.N / 2) + 255) / 256), (unsigned)(pl.b * pl.H));
             hipLaunchKernelGGL(ssd_carry_kernel, grid, dim3(256), 0, hs, init_state, args.ws_state,
-                               args.ws_misc, pl.P, pl.N, pl.S, rot ? 1 : 0);
+                               args.ws_misc, pl.P, pl.N, SA, SA - pl.SF, rot ? 1 : 0);
             if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
         }
     }
     if (rs == SSD_OK) {
+        args.S = pl.S;
         args.seg_items = pl.S;
         const bool timed = walk_events && walk_events[0];
         if (timed && hipEventRecord(reinterpret_cast<hipEvent_t>(walk_events[0]), hs) != hipSuccess)
