@@ -200,6 +200,19 @@ def test_rotating_column_walk(P, N, R, T, H, G, init, segments):
     check_full(inp, y, fin, TOL["bf16"], f"rot P{P} N{N} R{R} T{T} H{H} G{G} S{segments}")
 
 
+# The state pass divided finer than the output pass (each output segment in
+# two state segments, when the halves still fit one workgroup per CU): few
+# blocks, long enough sequences. Shared walk and rotating walk.
+@pytest.mark.parametrize("segments,rot", [(2, False), (3, False), (5, False), (2, True), (3, True)])
+def test_state_pass_split(segments, rot):
+    shape = si.small_shape(batch=1, seqlen=2000, nheads=4, headdim=64, dstate=128,
+                           mimo_rank=4 if rot else 1, dtype="bf16", rotation=rot,
+                           init_state=True, dt_shift=5.0)
+    inp = si.make_inputs(shape, seed=77 + segments)
+    y, fin = run_gpu(inp, segments=segments)
+    check_full(inp, y, fin, TOL["bf16"], f"split state pass S{segments} rot{int(rot)}")
+
+
 @pytest.mark.parametrize("segments", [1, 2, 3, 7, 64])
 def test_segments(segments):
     # splitting the sequence into parallel segments joined by the carry pass
