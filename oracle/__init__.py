@@ -5,9 +5,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 (``chunked_ssd_scan_amd``) never imports, links or calls it, and the two share
 no code.
 
-The oracle itself is ``ssd_oracle.c``: the plain token-by-token recurrence in
-double precision (see that file's header for the definition and the page
-passages it follows). This module builds it with gcc and wraps it with ctypes.
+The oracle itself is ``ssd_oracle.c``: the plain token-by-token recurrences in
+double precision, of the chunked SSD scan and of the Mamba-1 selective scan
+(see that file for the definitions and the page passages they follow). This module builds it with gcc and wraps it with ctypes.
 Pins that tie it to the pages and to mathematics live in
 ``tests/test_oracle_pins.py``.
 """
@@ -51,6 +51,8 @@ def _load(path: Optional[str] = None):
         lib.ssd_oracle_f64.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 7 + [vp, i64, vp, vp, ctypes.c_int]
         lib.ssd_oracle_f64.restype = ctypes.c_int
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
+        lib.selective_scan_f64.argtypes = [i64] * 4 + [vp] * 7 + [i64, vp, ctypes.c_int]
+        lib.selective_scan_f64.restype = ctypes.c_int
         _libs[key] = lib
     return _libs[key]
 
@@ -137,3 +139,36 @@ def time_oracle(inp, bh: Sequence[int], nthreads: int = 0):
     t0 = time.perf_counter()
     ssd_oracle_inputs(inp, bh=bh, want_y=True, nthreads=nthreads)
     return time.perf_counter() - t0
+
+
+def selective_scan(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   C: torch.Tensor, skip: torch.Tensor, bd: Optional[Sequence[int]] = None,
+                   nthreads: int = 0, lib_path: Optional[str] = None):
+    """Float64 Mamba-1 selective scan ("SSM Selective Scan", problem statement).
+
+    u, delta [b,T,D]; A [D,N]; B, C [b,T,N]; skip [D]; all fp32 CPU tensors.
+    Returns y [b,T,D] as float64, or with ``bd`` (channel indices b*D + d)
+    y_sel [n,T] for just those channels.
+    """
+    lib = _load(lib_path)
+    b, T, Dm = u.shape
+    N = A.shape[1]
+    assert delta.shape == (b, T, Dm) and A.shape == (Dm, N) and skip.shape == (Dm,)
+    assert B.shape == C.shape == (b, T, N)
+    for t in (u, delta, A, B, C, skip):
+        assert t.dtype == torch.float32
+    cont = lambda t: t.detach().cpu().contiguous()
+    u, delta, A, B, C, skip = map(cont, (u, delta, A, B, C, skip))
+    if bd is None:
+        bd_arr, n = None, b * Dm
+        y = np.empty((b, T, Dm), dtype=np.float64)
+    else:
+        bd_arr = np.ascontiguousarray(np.asarray(bd, dtype=np.int64))
+        n = int(bd_arr.size)
+        y = np.empty((n, T), dtype=np.float64)
+    rc = lib.selective_scan_f64(b, T, Dm, N, _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(skip),
+                                None if bd_arr is None else bd_arr.ctypes.data, n, y.ctypes.data,
+                                int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"selective_scan_f64 failed with code {rc}")
+    return y

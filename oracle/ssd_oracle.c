@@ -1,5 +1,6 @@
 /*
- * Float64 token-by-token oracle for the chunked SSD scan.
+ * Float64 token-by-token oracle for the chunked SSD scan (and, at the end of
+ * this file, for the Mamba-1 selective scan).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
  * call this file; only the tests, the smoke check and the bench's CPU
@@ -178,4 +179,70 @@ int ssd_oracle_max_threads(void) {
 #else
     return 1;
 #endif
+}
+
+/*
+ * Mamba-1 selective scan with a per-(channel, state) decay, as the "SSM
+ * Selective Scan" page states it (problem statement): for every batch b,
+ * channel d and state index n, from a zero state,
+ *
+ *   Abar = exp(delta[b,t,d] * A[d,n]),   Bbar = delta[b,t,d] * B[b,t,n]
+ *   h[n] = Abar * h[n] + Bbar * u[b,t,d]
+ *   y[b,t,d] = sum_n C[b,t,n] * h[n] + skip[d] * u[b,t,d]
+ *
+ * Channels share B and C and have their own rows of A. Inputs are fp32,
+ * widened to double; y is double.
+ *   y:       [batch][T][Dm] doubles, or the selected channels only:
+ *   bd_list: n_bd indices bd = b*Dm + d (NULL: every channel, y in [b][T][Dm]);
+ *            with a list, y is [n_bd][T].
+ * Returns 0, or a negative code for a bad argument.
+ */
+int selective_scan_f64(int64_t batch, int64_t T, int64_t Dm, int64_t N,
+                       const float *u, const float *delta, const float *A, const float *B,
+                       const float *C, const float *skip, const int64_t *bd_list, int64_t n_bd,
+                       double *y, int nthreads) {
+    if (batch < 1 || T < 1 || Dm < 1 || N < 1) return -1;
+    if (!u || !delta || !A || !B || !C || !skip || !y) return -5;
+    if (!bd_list) n_bd = batch * Dm;
+    for (int64_t i = 0; bd_list && i < n_bd; ++i)
+        if (bd_list[i] < 0 || bd_list[i] >= batch * Dm) return -6;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *h = (double *)malloc(sizeof(double) * (size_t)N);
+        if (!h) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_bd; ++i) {
+            if (!h) continue;
+            const int64_t bd = bd_list ? bd_list[i] : i;
+            const int64_t b = bd / Dm, d = bd % Dm;
+            for (int64_t n = 0; n < N; ++n) h[n] = 0.0;
+            for (int64_t t = 0; t < T; ++t) {
+                const int64_t row = b * T + t;
+                const double dl = (double)delta[row * Dm + d], ut = (double)u[row * Dm + d];
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) {
+                    const double abar = exp(dl * (double)A[d * N + n]);
+                    const double bbar = dl * (double)B[row * N + n];
+                    h[n] = abar * h[n] + bbar * ut;
+                    acc += (double)C[row * N + n] * h[n];
+                }
+                acc += (double)skip[d] * ut;
+                if (bd_list)
+                    y[i * T + t] = acc;
+                else
+                    y[row * Dm + d] = acc;
+            }
+        }
+        free(h);
+    }
+    return err;
 }

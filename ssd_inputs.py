@@ -133,3 +133,61 @@ def small_shape(**kw) -> Shape:
                 rotation=False, init_state=False, dt_shift=2.0, name="small")
     base.update(kw)
     return Shape(**base)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-1 selective scan (per-(channel, state) decay): seeded inputs.
+# Recipe, one CPU generator seeded with ``seed``, in this order:
+#   1. u ~ N(0,1) [b,T,D]
+#   2. z ~ N(0,1) [b,T,D],  delta = softplus(z - shift)   (> 0; shift 2)
+#   3. r ~ U(0, ln 16) [D,N], A = -exp(r)                  (< 0)
+#   4. B ~ N(0,1) [b,T,N]
+#   5. C ~ N(0,1) [b,T,N]
+#   6. skip ~ N(0,1) [D]
+# all float32. The workload is the LeetGPU performance-test shape.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class ScanShape:
+    batch: int
+    seqlen: int
+    d_model: int
+    d_state: int
+    dt_shift: float = 2.0
+    name: str = ""
+
+
+SCAN_CONFIGS = {
+    0: ScanShape(1, 64, 8, 4, 2.0, "tiny b1 T64 D8 N4"),
+    1: ScanShape(4, 4096, 512, 16, 2.0, "selective scan b4 T4096 D512 N16"),
+}
+
+
+@dataclass
+class ScanInputs:
+    shape: ScanShape
+    u: torch.Tensor        # [b,T,D]
+    delta: torch.Tensor    # [b,T,D]
+    A: torch.Tensor        # [D,N]
+    B: torch.Tensor        # [b,T,N]
+    C: torch.Tensor        # [b,T,N]
+    skip: torch.Tensor     # [D]
+
+    def to(self, device) -> "ScanInputs":
+        return ScanInputs(self.shape, *(t.to(device) for t in (self.u, self.delta, self.A, self.B,
+                                                                 self.C, self.skip)))
+
+
+def make_scan_inputs(shape: ScanShape, seed: int = 0) -> ScanInputs:
+    """Draw one seeded selective-scan input set on the CPU (fixed draw order)."""
+    b, T, Dm, N = shape.batch, shape.seqlen, shape.d_model, shape.d_state
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    u = torch.randn(b, T, Dm, generator=g, dtype=torch.float32)
+    z = torch.randn(b, T, Dm, generator=g, dtype=torch.float32)
+    delta = torch.nn.functional.softplus(z - shape.dt_shift).contiguous()
+    A = (-torch.exp(torch.rand(Dm, N, generator=g, dtype=torch.float32) * math.log(16.0))).contiguous()
+    Bm = torch.randn(b, T, N, generator=g, dtype=torch.float32)
+    Cm = torch.randn(b, T, N, generator=g, dtype=torch.float32)
+    skip = torch.randn(Dm, generator=g, dtype=torch.float32)
+    return ScanInputs(shape, u, delta, A, Bm, Cm, skip)

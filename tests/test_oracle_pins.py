@@ -327,3 +327,118 @@ def test_pins_catch_planted_mistakes(tmp_path):
         so = str(tmp_path / f"{name}.so")
         subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
         assert _pin_battery(so) > 1e-6, f"planted mistake {name!r} was not caught"
+
+
+# --------------------------------------------------------------------------
+# Mamba-1 selective scan oracle ("SSM Selective Scan", problem statement)
+# --------------------------------------------------------------------------
+
+def _scan_inputs(b=2, T=29, Dm=5, N=3, seed=31):
+    return si.make_scan_inputs(si.ScanShape(b, T, Dm, N), seed=seed)
+
+
+def test_selective_scan_matches_the_statement_form():
+    # forms.mamba1_scan writes the page's four equations per (b, d) with NumPy;
+    # D != N and b > 1 catch transposed A or swapped B/C indices.
+    s = _scan_inputs()
+    y = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip)
+    ref = forms.mamba1_scan(s.u, s.delta, s.A, s.B, s.C, s.skip)
+    assert relerr(y, ref) < TOL
+
+
+def test_selective_scan_scalar_decay_is_the_ssd_scan():
+    # A[d, n] = a_d for all n: one head per channel, P = 1, x = delta*u,
+    # da = delta*a_d, shared B and C; the skip term multiplies u.
+    s = _scan_inputs(b=2, T=23, Dm=4, N=6, seed=32)
+    a = s.A[:, :1]
+    A = a.expand(-1, s.A.shape[1]).contiguous()
+    y = oracle.selective_scan(s.u, s.delta, A, s.B, s.C, s.skip)
+    x = (s.delta.double() * s.u.double())[:, :, None, :, None].contiguous()
+    da = (s.delta.double() * a[:, 0].double()).float().contiguous()
+    ys, _ = oracle.ssd_oracle(x, da, s.B.double()[:, :, None, None, :].contiguous(),
+                              s.C.double()[:, :, None, None, :].contiguous())
+    got = ys[:, :, 0, :, 0] + forms.f64(s.skip) * forms.f64(s.u)
+    assert relerr(y, got) < 1e-6          # da rounded to fp32 for the SSD oracle
+
+
+def test_selective_scan_closed_form_constant_inputs():
+    # Constant u, delta, B, C: h_t[n] = delta B_n u (1 - Abar_n^(t+1)) / (1 - Abar_n).
+    T, Dm, N = 40, 3, 4
+    g = torch.Generator().manual_seed(33)
+    A = -torch.rand(Dm, N, generator=g) * 2 - 0.05
+    dl, uu = 0.3, 1.7
+    Bv = torch.randn(N, generator=g)
+    Cv = torch.randn(N, generator=g)
+    skip = torch.randn(Dm, generator=g)
+    u = torch.full((1, T, Dm), uu)
+    delta = torch.full((1, T, Dm), dl)
+    Bm = Bv.expand(1, T, N).contiguous()
+    Cm = Cv.expand(1, T, N).contiguous()
+    y = oracle.selective_scan(u, delta, A, Bm, Cm, skip)
+    dl, uu = float(delta[0, 0, 0]), float(u[0, 0, 0])                    # the stored fp32 values
+    abar = np.exp(dl * forms.f64(A))                                       # [D,N]
+    t = np.arange(T)[:, None, None]
+    h = dl * forms.f64(Bv) * uu * (1 - abar[None] ** (t + 1)) / (1 - abar[None])   # [T,D,N]
+    ref = (h * forms.f64(Cv)).sum(-1) + forms.f64(skip) * uu
+    assert relerr(y[0], ref) < 1e-12
+
+
+def test_selective_scan_golden_decay_factors():
+    # The worked example's printed Abar for delta = 1 and its A row: a unit
+    # impulse at t = 0 with B = C = 1 decays by Abar per step.
+    gold = json.load(open(os.path.join(HERE, "golden", "selective_scan_abar.json")))
+    T = 4
+    for a, printed in zip(gold["A_row"], gold["Abar_printed"]):
+        u = torch.zeros(1, T, 1)
+        u[0, 0] = 1.0
+        ones = torch.ones(1, T, 1)
+        y = oracle.selective_scan(u, ones * gold["delta"], torch.tensor([[a]]), ones, ones.clone(),
+                                  torch.zeros(1))
+        ratio = y[0, 1:, 0] / y[0, :-1, 0]
+        assert np.allclose(np.round(ratio, gold["decimals"]), printed)
+
+
+def test_selective_scan_causal_and_channels_independent():
+    s = _scan_inputs(b=1, T=30, Dm=6, N=5, seed=34)
+    y = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip)
+    u2 = s.u.clone()
+    u2[:, 17:, 2] += 3.0
+    y2 = oracle.selective_scan(u2, s.delta, s.A, s.B, s.C, s.skip)
+    assert np.array_equal(y[:, :17], y2[:, :17])
+    others = [d for d in range(6) if d != 2]
+    assert np.array_equal(y[:, :, others], y2[:, :, others])
+    assert not np.allclose(y[:, 17:, 2], y2[:, 17:, 2])
+
+
+def test_selective_scan_selected_channels():
+    s = _scan_inputs(b=2, T=9, Dm=4, N=3, seed=35)
+    y = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip)
+    sel = [0, 5, 7]
+    ys = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip, bd=sel)
+    for i, bd in enumerate(sel):
+        assert np.array_equal(ys[i], y[bd // 4, :, bd % 4])
+
+
+SCAN_MUTANTS = {
+    "scan_dropped_skip": ("acc += (double)skip[d] * ut;", "acc += 0.0 * skip[d] * ut;"),
+    "scan_A_transposed": ("(double)A[d * N + n]", "(double)A[n * Dm + d]"),
+    "scan_bbar_without_delta": ("const double bbar = dl * (double)B[row * N + n];",
+                                "const double bbar = (double)B[row * N + n];"),
+    "scan_read_before_write": ("h[n] = abar * h[n] + bbar * ut;\n                    acc += (double)C[row * N + n] * h[n];",
+                               "acc += (double)C[row * N + n] * h[n];\n                    h[n] = abar * h[n] + bbar * ut;"),
+    "scan_B_for_C": ("acc += (double)C[row * N + n] * h[n];", "acc += (double)B[row * N + n] * h[n];"),
+}
+
+
+def test_selective_scan_pins_catch_planted_mistakes(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
+    s = _scan_inputs(b=2, T=17, Dm=5, N=3, seed=36)
+    ref = forms.mamba1_scan(s.u, s.delta, s.A, s.B, s.C, s.skip)
+    for name, (old, new) in SCAN_MUTANTS.items():
+        assert src.count(old) == 1, name
+        path = tmp_path / f"{name}.c"
+        path.write_text(src.replace(old, new))
+        so = str(tmp_path / f"{name}.so")
+        subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
+        y = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip, lib_path=so)
+        assert relerr(y, ref) > 1e-6, f"planted mistake {name!r} was not caught"
