@@ -6,8 +6,10 @@ Importing works without a GPU; calling the scan needs the built library and
 a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
 
 C entry points, mirrored here under the same names:
-  ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_status_str
-plus ``forward(...)``, a tensor-level convenience over ssd_forward_ex.
+  ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_selective_scan,
+  ssd_status_str
+plus ``forward(...)`` and ``selective_scan(...)``, tensor-level conveniences
+over ssd_forward_ex and ssd_selective_scan.
 """
 from __future__ import annotations
 
@@ -26,7 +28,8 @@ SSD_ERR_UNSUPPORTED = 3
 SSD_ERR_ALIAS = 4
 SSD_ERR_HIP = 5
 
-EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_status_str")
+EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
+            "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -67,6 +70,8 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_forward_ex.restype = ctypes.c_int
         lib.ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims), i64, i64]
         lib.ssd_workspace_bytes.restype = ctypes.c_size_t
+        lib.ssd_selective_scan.argtypes = [vp] * 7 + [i64] * 4 + [vp]
+        lib.ssd_selective_scan.restype = ctypes.c_int
         lib.ssd_status_str.argtypes = [ctypes.c_int32]
         lib.ssd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -97,6 +102,13 @@ def ssd_forward_ex(dims: Optional[SsdDims], x, da, B, C, D, init_state, chunk_le
 
 def ssd_workspace_bytes(dims: SsdDims, chunk_len: int, R: int) -> int:
     return int(load_library().ssd_workspace_bytes(ctypes.byref(dims), int(chunk_len), int(R)))
+
+
+def ssd_selective_scan(u, delta, A, B, C, skip, y, batch, seq_len, d_model, d_state,
+                       stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_selective_scan(u, delta, A, B, C, skip, y, int(batch), int(seq_len),
+                                      int(d_model), int(d_state), stream))
 
 
 def ssd_status_str(status: int) -> str:
@@ -180,3 +192,41 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     if st != SSD_OK:
         raise SsdError(st, "ssd_forward_ex")
     return y, final_state
+
+
+def selective_scan(u, delta, A, B, C, skip, y=None, stream=None) -> "torch.Tensor":
+    """Run the diagonal selective scan on device tensors; returns y.
+
+    u, delta [b,T,D], A [D,N], B/C [b,T,N], skip [D]: fp32, contiguous, one
+    device. y (fp32 [b,T,D], contiguous) may be given to write in place.
+    """
+    import torch
+
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, seq_len, d_model]")
+    b, T, Dm = u.shape
+    N = A.shape[-1]
+    if u.device.type != "cuda":
+        raise ValueError("chunked_ssd_scan_amd.selective_scan needs device tensors")
+    dev = u.device
+    want = {"u": (b, T, Dm), "delta": (b, T, Dm), "A": (Dm, N), "B": (b, T, N),
+            "C": (b, T, N), "skip": (Dm,)}
+    for name, t in (("u", u), ("delta", delta), ("A", A), ("B", B), ("C", C), ("skip", skip)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if tuple(t.shape) != want[name]:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
+    if y is None:
+        y = torch.empty((b, T, Dm), device=dev, dtype=torch.float32)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = ssd_selective_scan(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(),
+                                C.data_ptr(), skip.data_ptr(), y.data_ptr(), b, T, Dm, N, stream)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_selective_scan")
+    return y

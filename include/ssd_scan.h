@@ -150,6 +150,34 @@ ssd_status ssd_forward_ex(const ssd_dims *d, const void *x, const float *da,
  * Returns 0 for invalid arguments. */
 size_t ssd_workspace_bytes(const ssd_dims *d, int64_t chunk_len, int64_t R);
 
+/*
+ * Diagonal selective scan (Mamba-1 form), LeetGPU "SSM Selective Scan"
+ * write-up, problem statement: per batch b, channel d and state n, from a
+ * zero state,
+ *   h[n]      = exp(delta[b,t,d] * A[d,n]) * h[n] + delta[b,t,d] * B[b,t,n] * u[b,t,d]
+ *   y[b,t,d]  = sum_n C[b,t,n] * h[n] + skip[d] * u[b,t,d]
+ * (the decay is diagonal per (d, n); B and C are shared by every channel).
+ *
+ * Layouts: dense, row-major, fp32, device memory, 4-byte aligned.
+ *   u, delta  [batch, seq_len, d_model]
+ *   A         [d_model, d_state]
+ *   B, C      [batch, seq_len, d_state]
+ *   skip      [d_model]
+ *   y         [batch, seq_len, d_model], written in full
+ * Sizes: batch in 1..65535, seq_len >= 1, d_model in 1..2^22, d_state in
+ * 1..64 (SSD_ERR_UNSUPPORTED above these bounds). Ownership, asynchrony and scratch are as
+ * for ssd_forward: the sequence is cut into chunks that run in parallel and
+ * are joined by a carry pass through the per-(device, stream) scratch buffer.
+ * Errors: SSD_ERR_NULL_ARG for a NULL pointer, SSD_ERR_BAD_SHAPE for a size
+ * below 1, SSD_ERR_ALIAS when y overlaps an input, SSD_ERR_UNSUPPORTED for
+ * a misaligned pointer or sizes outside the envelope; nothing is enqueued on
+ * any of these.
+ */
+ssd_status ssd_selective_scan(const float *u, const float *delta, const float *A,
+                              const float *B, const float *C, const float *skip,
+                              float *y, int64_t batch, int64_t seq_len,
+                              int64_t d_model, int64_t d_state, void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssd_status_str(int32_t status);
 

@@ -134,3 +134,36 @@ def test_workspace_bytes(lib):
     n = ssd.ssd_workspace_bytes(dims(batch=1, seqlen=131072, nheads=64), 256, 1)
     assert n >= 64 * 2 * 64 * 128 * 4 + (131072 // 32) * 768 * 4
     assert ssd.ssd_workspace_bytes(dims(seqlen=0), 256, 1) == 0
+
+
+# ---- ssd_selective_scan ----------------------------------------------------
+
+U, DL, AA, SB, SC, SK, SY = (0x10000000 * (i + 20) for i in range(7))
+
+
+def sel_call(u=U, delta=DL, A=AA, B=SB, C=SC, skip=SK, y=SY, b=2, T=100, D=512, N=16):
+    return ssd.ssd_selective_scan(u, delta, A, B, C, skip, y, b, T, D, N, None)
+
+
+@pytest.mark.parametrize("field", ["u", "delta", "A", "B", "C", "skip", "y"])
+def test_selective_null_pointer(lib, field):
+    assert sel_call(**{field: None}) == ssd.SSD_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("kw", [dict(b=0), dict(T=0), dict(D=0), dict(N=0), dict(T=-3)])
+def test_selective_bad_shape(lib, kw):
+    assert sel_call(**kw) == ssd.SSD_ERR_BAD_SHAPE
+
+
+def test_selective_unsupported(lib):
+    assert sel_call(N=65) == ssd.SSD_ERR_UNSUPPORTED
+    assert sel_call(b=65536) == ssd.SSD_ERR_UNSUPPORTED
+    assert sel_call(b=1, T=1, D=(1 << 22) + 1) == ssd.SSD_ERR_UNSUPPORTED
+    assert sel_call(u=U + 2) == ssd.SSD_ERR_UNSUPPORTED
+    assert sel_call(y=SY + 1) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_selective_alias(lib):
+    assert sel_call(y=U) == ssd.SSD_ERR_ALIAS
+    assert sel_call(y=DL + 4096) == ssd.SSD_ERR_ALIAS        # inside delta
+    assert sel_call(y=AA - 4) == ssd.SSD_ERR_ALIAS           # runs into A

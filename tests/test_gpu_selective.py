@@ -1,0 +1,109 @@
+"""Diagonal selective scan on the GPU vs the float64 oracle (needs a gfx950 GPU).
+
+Bar: normwise max relative error ||y - ref||_inf / ||ref||_inf within 1e-4
+(fp32 inputs, fp32 arithmetic). At the full b4 T4096 D512 N16 size the oracle
+runs on sampled channels over the whole sequence, each held to the bar
+against its own norm.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-4
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _ssd():
+    import chunked_ssd_scan_amd as ssd
+    ssd.load_library()
+    return ssd
+
+
+def normwise(got, ref):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def run(inp, y=None):
+    ssd = _ssd()
+    g = inp.to(_dev())
+    y = ssd.selective_scan(g.u, g.delta, g.A, g.B, g.C, g.skip, y=y)
+    torch.cuda.synchronize()
+    return y
+
+
+def check(inp, label):
+    y = run(inp)
+    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip)
+    err = normwise(y.cpu().double().numpy(), ref)
+    print(f"{label} y err {err:.3e} (tol {TOL:g})", flush=True)
+    assert err <= TOL, (label, err)
+
+
+def test_tiny_config():
+    check(si.make_scan_inputs(si.SCAN_CONFIGS[0], seed=0), "tiny")
+
+
+# (batch, T, D, N, dt_shift): ragged channel groups (D not a multiple of 64),
+# odd state sizes in each kernel width, sequences shorter than a chunk, and
+# long sequences on few channels (many chunks joined by the carry pass)
+SHAPES = [
+    (1, 1, 8, 4, 2.0), (1, 15, 64, 16, 2.0), (1, 16, 65, 16, 2.0), (1, 17, 1, 1, 2.0),
+    (2, 100, 63, 17, 2.0), (3, 333, 130, 32, 2.0), (1, 257, 64, 33, 2.0),
+    (2, 1000, 200, 64, 2.0), (1, 2000, 64, 16, 2.0), (1, 3001, 7, 5, 2.0),
+    (1, 4096, 64, 16, 6.0), (2, 1500, 96, 48, 0.0), (1, 20001, 3, 2, 2.0),
+]
+
+
+@pytest.mark.parametrize("b,T,D,N,shift", SHAPES)
+def test_shapes(b, T, D, N, shift):
+    shape = si.ScanShape(b, T, D, N, shift, f"b{b} T{T} D{D} N{N}")
+    check(si.make_scan_inputs(shape, seed=b * 7 + T), shape.name)
+
+
+def test_full_size_sampled():
+    inp = si.make_scan_inputs(si.SCAN_CONFIGS[1], seed=0)
+    b, T, Dm = inp.u.shape
+    y = run(inp).cpu()
+    rng = np.random.default_rng(1)
+    sel = sorted(set(rng.integers(0, b * Dm, 24).tolist()) | {0, Dm - 1, b * Dm - 1, 63, 64})
+    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip, bd=sel)
+    worst = 0.0
+    for i, bd in enumerate(sel):
+        bb, d = divmod(bd, Dm)
+        err = normwise(y[bb, :, d].double().numpy(), ref[i])
+        worst = max(worst, err)
+        assert err <= TOL, (bd, err)
+    print(f"full size: {len(sel)} channels, worst y err {worst:.3e}", flush=True)
+
+
+def test_deterministic_and_in_place():
+    inp = si.make_scan_inputs(si.ScanShape(2, 777, 100, 16, 2.0, ""), seed=3)
+    y1 = run(inp)
+    y2 = torch.full_like(y1, float("nan"))
+    y2 = run(inp, y=y2)
+    assert torch.equal(y1, y2)
+
+
+def test_nan_stays_in_its_channel():
+    # B and C are shared by every channel; a NaN in one channel's input must
+    # not reach another channel, nor the same channel before it appears
+    inp = si.make_scan_inputs(si.ScanShape(1, 600, 70, 16, 2.0, ""), seed=5)
+    inp.u[0, 400, 9] = float("nan")
+    y = run(inp).cpu()
+    assert torch.isnan(y[0, 400:, 9]).all()
+    assert torch.isfinite(y[0, :400, 9]).all()
+    others = torch.cat([y[0, :, :9], y[0, :, 10:]], dim=1)
+    assert torch.isfinite(others).all()
