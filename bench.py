@@ -27,6 +27,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3
+# VALU issue of unpacked fp32: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane
+# slots per second; a full-rate op takes one slot per lane, exp2 two (half rate)
+VALU_SLOTS_PER_S = 256 * 4 * 16 * 2.4e9
+SEL_SLOTS_PER_UPDATE = 6       # dl*A, exp2 (2 slots), (dl*u)*B, state fma, C.h fma
 
 
 def algorithmic_bytes(s) -> int:
@@ -58,16 +62,26 @@ def algorithmic_flops(s) -> int:
     return k3 + k5_off + k5_diag + k2
 
 
-def source_digest() -> str:
-    src = os.path.join(ROOT, "chunked_ssd_scan_amd", "csrc", "ssd_scan.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+# kernel sources behind each workload's counter summary
+KERNEL_SOURCES = {
+    "ssd": ("ssd_scan.hip", "ssd_common.h"),
+    "selective_scan": ("sel_scan.hip", "ssd_common.h"),
+}
 
 
-def profiled_traffic(workload_tag: str):
+def source_digest(workload: str = "ssd") -> str:
+    """First 16 hex digits of the SHA-256 over the workload's kernel sources."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[workload]:
+        h.update(open(os.path.join(ROOT, "chunked_ssd_scan_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload_tag: str, workload: str = "ssd"):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or None.
 
     The summary carries a fenced json block with the calibrated bytes and the
-    digest of the kernel source it was measured on; a stale digest gives None.
+    digest of the kernel sources it was measured on; a stale digest gives None.
     """
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_tag}.md")
     if not os.path.exists(path):
@@ -76,7 +90,7 @@ def profiled_traffic(workload_tag: str):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("source_sha256_16") != source_digest():
+    if d.get("source_sha256_16") != source_digest(workload):
         return None
     return int(d["hbm_bytes_per_launch"])
 
@@ -133,6 +147,80 @@ def cpu_baseline(inp, shape, nslices: int):
     }
 
 
+def selective_bench(args) -> dict:
+    """The diagonal selective scan (b4 T4096 D512 N16, fp32) as its own line."""
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    shape = si.SCAN_CONFIGS[1]
+    dev = torch.device("cuda:0")
+    inp = si.make_scan_inputs(shape, seed=0)
+    g = inp.to(dev)
+    y = torch.empty_like(g.u)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(walk_events=None):
+        ssd.selective_scan(g.u, g.delta, g.A, g.B, g.C, g.skip, y=y, stream=stream.cuda_stream,
+                           chunks=args.segments, walk_events=walk_events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = start.elapsed_time(end) / args.steps
+    out_ms = time_walk(step, args.steps)
+    if not torch.isfinite(y).all():
+        raise RuntimeError("non-finite output")
+    b, T, D, N = shape.batch, shape.seqlen, shape.d_model, shape.d_state
+    updates = b * T * D * N
+    slots = updates * SEL_SLOTS_PER_UPDATE
+    achieved = slots / (out_ms * 1e-3) / 1e12
+    peak = VALU_SLOTS_PER_S / 1e12
+    nbytes = (3 * b * T * D + 2 * b * T * N + D * N + D) * 4
+    out = {
+        "metric": "selective scan fwd tokens/s + % of VALU issue (b4,T4096,D512,N16)",
+        "value": b * T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; see ssd_inputs.make_scan_inputs)",
+        "config": {"workload": shape.name, "batch": b, "seqlen": T, "d_model": D, "d_state": N,
+                   "chunks": args.segments or "auto"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TOP/s",
+                     "frac": achieved / peak,
+                     "traffic": profiled_traffic("selective_scan", "selective_scan"),
+                     "algorithmic_slots": slots, "kernel_ms": out_ms, "forward_ms": call_ms,
+                     "forward_frac": slots / (call_ms * 1e-3) / 1e12 / peak,
+                     "hbm_frac_forward": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        reps = 3
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip, nthreads=threads)
+        secs = (time.perf_counter() - t1) / reps
+        out["cpu_baseline"] = {"value": b * T / secs, "unit": "tokens/s", "cores": threads,
+                               "kind": "oracle",
+                               "sample": f"the whole workload, {reps} runs, {secs:.3f} s each"}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -144,6 +232,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--block-slices", type=int, default=0)
+    ap.add_argument("--workload", choices=("ssd", "selective_scan"), default="ssd",
+                    help="ssd: the chunked SSD scan (the reported line); selective_scan: "
+                         "the diagonal selective scan, b4 T4096 D512 N16 (--segments = chunks)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) for counter calibration")
     args = ap.parse_args()
@@ -171,6 +262,9 @@ def main() -> int:
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
         return 0
     ssd.load_library()
+    if args.workload == "selective_scan":
+        print(json.dumps(selective_bench(args)), flush=True)
+        return 0
     shape = si.CONFIGS[args.config]
     dev = torch.device("cuda:0")
     inp = si.make_inputs(shape, seed=0)

@@ -7,9 +7,9 @@ a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
 
 C entry points, mirrored here under the same names:
   ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_selective_scan,
-  ssd_status_str
+  ssd_selective_scan_ex, ssd_status_str
 plus ``forward(...)`` and ``selective_scan(...)``, tensor-level conveniences
-over ssd_forward_ex and ssd_selective_scan.
+over ssd_forward_ex and ssd_selective_scan_ex.
 """
 from __future__ import annotations
 
@@ -29,7 +29,7 @@ SSD_ERR_ALIAS = 4
 SSD_ERR_HIP = 5
 
 EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
-            "ssd_status_str")
+            "ssd_selective_scan_ex", "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -72,6 +72,8 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_selective_scan.argtypes = [vp] * 7 + [i64] * 4 + [vp]
         lib.ssd_selective_scan.restype = ctypes.c_int
+        lib.ssd_selective_scan_ex.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.POINTER(SsdLaunchOpts), vp]
+        lib.ssd_selective_scan_ex.restype = ctypes.c_int
         lib.ssd_status_str.argtypes = [ctypes.c_int32]
         lib.ssd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -111,6 +113,14 @@ def ssd_selective_scan(u, delta, A, B, C, skip, y, batch, seq_len, d_model, d_st
                                       int(d_model), int(d_state), stream))
 
 
+def ssd_selective_scan_ex(u, delta, A, B, C, skip, y, batch, seq_len, d_model, d_state,
+                          opts: Optional[SsdLaunchOpts], stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_selective_scan_ex(u, delta, A, B, C, skip, y, int(batch), int(seq_len),
+                                         int(d_model), int(d_state),
+                                         None if opts is None else ctypes.byref(opts), stream))
+
+
 def ssd_status_str(status: int) -> str:
     return load_library().ssd_status_str(int(status)).decode()
 
@@ -119,6 +129,22 @@ def ssd_status_str(status: int) -> str:
 
 def _dptr(t):
     return None if t is None else t.data_ptr()
+
+
+def _event_handles(events, stream, dev):
+    """hipEvent_t handles of a pair of torch.cuda.Event (or of ints, taken as handles)."""
+    import torch
+
+    handles = []
+    for ev in events:
+        if isinstance(ev, int):
+            handles.append(ev)
+            continue
+        if ev.cuda_event == 0:
+            # torch creates an event's HIP handle at its first record
+            ev.record(torch.cuda.ExternalStream(stream, device=dev))
+        handles.append(ev.cuda_event)
+    return handles
 
 
 def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=None,
@@ -175,16 +201,7 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
     if walk_events is not None:
-        handles = []
-        for ev in walk_events:
-            if isinstance(ev, int):
-                handles.append(ev)              # a hipEvent_t handle
-                continue
-            if ev.cuda_event == 0:
-                # torch creates an event's HIP handle at its first record
-                ev.record(torch.cuda.ExternalStream(stream, device=dev))
-            handles.append(ev.cuda_event)
-        opts.walk_events[0], opts.walk_events[1] = handles
+        opts.walk_events[0], opts.walk_events[1] = _event_handles(walk_events, stream, dev)
     with torch.cuda.device(dev):
         st = ssd_forward_ex(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), C.data_ptr(),
                             _dptr(D), _dptr(init_state), chunk_len, R, _dptr(theta),
@@ -194,11 +211,14 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     return y, final_state
 
 
-def selective_scan(u, delta, A, B, C, skip, y=None, stream=None) -> "torch.Tensor":
+def selective_scan(u, delta, A, B, C, skip, y=None, stream=None, chunks: int = 0,
+                   walk_events=None) -> "torch.Tensor":
     """Run the diagonal selective scan on device tensors; returns y.
 
     u, delta [b,T,D], A [D,N], B/C [b,T,N], skip [D]: fp32, contiguous, one
     device. y (fp32 [b,T,D], contiguous) may be given to write in place.
+    ``chunks`` (0: automatic) and ``walk_events`` (recorded around the output
+    pass) are the launch options of ssd_selective_scan_ex.
     """
     import torch
 
@@ -224,9 +244,14 @@ def selective_scan(u, delta, A, B, C, skip, y=None, stream=None) -> "torch.Tenso
         y = torch.empty((b, T, Dm), device=dev, dtype=torch.float32)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
+    opts = SsdLaunchOpts()
+    opts.segments = int(chunks)
+    if walk_events is not None:
+        opts.walk_events[0], opts.walk_events[1] = _event_handles(walk_events, stream, dev)
     with torch.cuda.device(dev):
-        st = ssd_selective_scan(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(),
-                                C.data_ptr(), skip.data_ptr(), y.data_ptr(), b, T, Dm, N, stream)
+        st = ssd_selective_scan_ex(u.data_ptr(), delta.data_ptr(), A.data_ptr(), B.data_ptr(),
+                                   C.data_ptr(), skip.data_ptr(), y.data_ptr(), b, T, Dm, N,
+                                   opts, stream)
     if st != SSD_OK:
-        raise SsdError(st, "ssd_selective_scan")
+        raise SsdError(st, "ssd_selective_scan_ex")
     return y

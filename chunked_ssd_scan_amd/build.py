@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "ssd_scan.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssd_scan.hip", "sel_scan.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd_scan.so")
 
@@ -28,9 +28,9 @@ def hipcc() -> str:
 
 
 def build(out: str = LIB, extra=()) -> str:
-    """Compile ssd_scan.hip into ``out`` (atomic replace)."""
+    """Compile the HIP sources into ``out`` (atomic replace)."""
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, SRC]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", INCLUDE, "-o", tmp, *SRCS]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

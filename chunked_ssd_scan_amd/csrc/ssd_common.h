@@ -1,0 +1,53 @@
+// Helpers shared by the chunked SSD scan (ssd_scan.hip) and the diagonal
+// selective scan (sel_scan.hip), both linked into libssd_scan.so.
+#ifndef SSD_COMMON_H
+#define SSD_COMMON_H
+
+#include <hip/hip_runtime.h>
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ssd_scan.h"
+
+namespace ssd_detail {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0).
+// Loads past `bytes` return zero and stores past it are dropped, which the
+// kernels use for ragged tails and for rows beyond a segment's range.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kOOB = 0x80000000u;  // lane offset that always falls outside a range
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Span {
+    uintptr_t lo, hi;
+};
+
+inline bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
+
+inline Span span_of(const void* p, int64_t bytes) {
+    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Span{lo, lo + (uintptr_t)bytes};
+}
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Scratch of at least `bytes` for `stream` on the current device, cached per
+// (device, stream) and ordered after its previous use; nullptr on failure.
+// *entry identifies it for scratch_release, which marks the end of this
+// call's use on the stream (defined in ssd_scan.hip).
+void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry);
+bool scratch_release(int entry);
+
+// Compute units of the current device (256 if the query fails).
+int device_cus();
+
+}  // namespace ssd_detail
+
+#endif  // SSD_COMMON_H

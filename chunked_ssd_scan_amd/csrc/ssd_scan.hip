@@ -44,9 +44,87 @@
 
 #include <mutex>
 
-#include "ssd_scan.h"
+#include "ssd_common.h"
+
+namespace ssd_detail {
+
+// Scratch is cached per (device, stream) and grows on demand. Stream-ordered
+// allocation (hipMallocAsync / hipFreeAsync) would block the host while the
+// stream has work in flight, serialising the caller with the device. Calls
+// on one stream are ordered by the stream; each call also waits (on the
+// device) for the last call that used the buffer, which keeps a stream handle
+// that is destroyed and reissued from racing with the old stream's work.
+// Buffers live until the process ends.
+struct ScratchEntry {
+    int dev;
+    hipStream_t stream;
+    void* ptr;
+    size_t bytes;
+    hipEvent_t last;    // recorded after the last call that used ptr
+};
+
+std::mutex g_scratch_mu;
+ScratchEntry g_scratch[256];
+int g_scratch_n = 0;
+
+// Scratch of at least `bytes` for `stream` on the current device, ordered
+// after its previous use; nullptr on failure. *entry identifies it for
+// scratch_release.
+void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    int i = 0;
+    while (i < g_scratch_n && !(g_scratch[i].dev == dev && g_scratch[i].stream == stream)) ++i;
+    if (i == g_scratch_n) {
+        if (g_scratch_n == 256) return nullptr;
+        ScratchEntry& e = g_scratch[g_scratch_n];
+        e.dev = dev;
+        e.stream = stream;
+        e.ptr = nullptr;
+        e.bytes = 0;
+        if (hipEventCreateWithFlags(&e.last, hipEventDisableTiming) != hipSuccess) return nullptr;
+        ++g_scratch_n;
+    }
+    ScratchEntry& e = g_scratch[i];
+    if (e.bytes < bytes) {
+        // grow: wait for the old buffer's last use, then replace it
+        if (e.ptr) {
+            if (hipEventSynchronize(e.last) != hipSuccess || hipFree(e.ptr) != hipSuccess) return nullptr;
+            e.ptr = nullptr;
+            e.bytes = 0;
+        }
+        if (hipMalloc(&e.ptr, bytes) != hipSuccess) {
+            e.ptr = nullptr;
+            return nullptr;
+        }
+        e.bytes = bytes;
+    } else if (hipStreamWaitEvent(stream, e.last, 0) != hipSuccess) {
+        return nullptr;
+    }
+    *entry = i;
+    return e.ptr;
+}
+
+// Marks the end of this call's use of the scratch on its stream.
+bool scratch_release(int entry) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ScratchEntry& e = g_scratch[entry];
+    return hipEventRecord(e.last, e.stream) == hipSuccess;
+}
+
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
+    return n;
+}
+
+}  // namespace ssd_detail
 
 namespace {
+
+using namespace ssd_detail;
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) float f32x8;
@@ -54,7 +132,6 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 constexpr int kRows = 32;  // fused rows per tile
-constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
 // element type helpers: TI = uint16_t (bf16 bits) or float
@@ -872,14 +949,6 @@ __device__ __forceinline__ float wrap_angle(float phi) {
     return fmaf(-k, 1.9353071795864769e-3f, phi);
 }
 
-// Buffer resource over `bytes` bytes at `base` (raw addressing, stride 0).
-// Loads past `bytes` return zero and stores past it are dropped, which the
-// tile walk uses for ragged tails and for tiles beyond a segment's range.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
-constexpr uint32_t kOOB = 0x80000000u;  // lane offset that always falls outside a tile's range
 
 // ---------------------------------------------------------------------------
 // Column-block tile walk (shared B/C, no rotation). Flatten each time row of
@@ -1843,18 +1912,6 @@ bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
     return (v & (v - 1)) == 0;
 }
 
-bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
-
-struct Span {
-    uintptr_t lo, hi;
-};
-
-bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi; }
-
-Span span_of(const void* p, int64_t bytes) {
-    uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-    return Span{lo, lo + (uintptr_t)bytes};
-}
 
 ssd_status check_shape(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has_theta) {
     if (d->batch < 1 || d->seqlen < 1 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
@@ -1886,72 +1943,7 @@ int auto_segments(int64_t units, int nsub, int64_t target) {
     return (int)(want < 1 ? 1 : want);
 }
 
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Scratch is cached per (device, stream) and grows on demand. Stream-ordered
-// allocation (hipMallocAsync / hipFreeAsync) would block the host while the
-// stream has work in flight, serialising the caller with the device. Calls
-// on one stream are ordered by the stream; each call also waits (on the
-// device) for the last call that used the buffer, which keeps a stream handle
-// that is destroyed and reissued from racing with the old stream's work.
-// Buffers live until the process ends.
-struct ScratchEntry {
-    int dev;
-    hipStream_t stream;
-    void* ptr;
-    size_t bytes;
-    hipEvent_t last;    // recorded after the last call that used ptr
-};
-
-std::mutex g_scratch_mu;
-ScratchEntry g_scratch[256];
-int g_scratch_n = 0;
-
-// Scratch of at least `bytes` for `stream` on the current device, ordered
-// after its previous use; nullptr on failure. *entry identifies it for
-// scratch_release.
-void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    int i = 0;
-    while (i < g_scratch_n && !(g_scratch[i].dev == dev && g_scratch[i].stream == stream)) ++i;
-    if (i == g_scratch_n) {
-        if (g_scratch_n == 256) return nullptr;
-        ScratchEntry& e = g_scratch[g_scratch_n];
-        e.dev = dev;
-        e.stream = stream;
-        e.ptr = nullptr;
-        e.bytes = 0;
-        if (hipEventCreateWithFlags(&e.last, hipEventDisableTiming) != hipSuccess) return nullptr;
-        ++g_scratch_n;
-    }
-    ScratchEntry& e = g_scratch[i];
-    if (e.bytes < bytes) {
-        // grow: wait for the old buffer's last use, then replace it
-        if (e.ptr) {
-            if (hipEventSynchronize(e.last) != hipSuccess || hipFree(e.ptr) != hipSuccess) return nullptr;
-            e.ptr = nullptr;
-            e.bytes = 0;
-        }
-        if (hipMalloc(&e.ptr, bytes) != hipSuccess) {
-            e.ptr = nullptr;
-            return nullptr;
-        }
-        e.bytes = bytes;
-    } else if (hipStreamWaitEvent(stream, e.last, 0) != hipSuccess) {
-        return nullptr;
-    }
-    *entry = i;
-    return e.ptr;
-}
-
-// Marks the end of this call's use of the scratch on its stream.
-bool scratch_release(int entry) {
-    std::lock_guard<std::mutex> lock(g_scratch_mu);
-    ScratchEntry& e = g_scratch[entry];
-    return hipEventRecord(e.last, e.stream) == hipSuccess;
-}
 
 // Scratch layout: [segment states | segment Lambda/Phi | C B^T tile pack]
 struct WsLayout {
@@ -1970,12 +1962,6 @@ WsLayout workspace_layout(const Plan& pl, bool no_pack) {
     return w;
 }
 
-int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) return 256;
-    return n;
-}
 
 // Most heads one block of w slices touches within a group.
 int64_t block_heads(const Plan& pl, int w) {
@@ -2147,282 +2133,6 @@ ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_sta
     return rs;
 }
 
-// ---------------------------------------------------------------------------
-// Mamba-1 selective scan ("SSM Selective Scan", problem statement): per
-// channel d and state n, h_n <- exp(delta A[d,n]) h_n + delta B_n u, and
-// y = sum_n C_n h_n + skip u, from a zero state. One lane per (batch,
-// channel), the N states in registers; B and C of a time step are the same
-// for every lane (scalar loads), u, delta and y rows are contiguous over the
-// 64 channels of a wave. The sequence is cut into K chunks that run in
-// parallel: pass 1 walks each chunk from zero and keeps its end state and its
-// sum of delta, pass 2 carries the states across chunks (the decay over a
-// chunk is exp(A[d,n] sum delta)), pass 3 walks each chunk again from its
-// carried state and writes y.
-// ---------------------------------------------------------------------------
-struct SelArgs {
-    const float* u;
-    const float* delta;
-    const float* A;
-    const float* B;
-    const float* C;
-    const float* skip;
-    float* y;
-    float* ws_h;     // [b][K][N][D]: chunk end states (pass 1), then carried states (pass 2)
-    float* ws_s;     // [b][K][D]: sum of delta over the chunk
-    int64_t T, Dm, N;
-    int K;           // chunks
-    int Kw;          // chunks this launch walks (the state pass skips the last)
-    int DG;          // 64-channel groups
-};
-
-// Steps per block: a block's B and C rows (TB * NN floats each) take two
-// loads per lane; u and delta of the next block are in flight in registers
-// while the current one is computed.
-template <int NN>
-constexpr int sel_block_steps() { return 128 / NN; }
-
-template <int NN, int MODE>   // MODE 1: chunk states; MODE 0: outputs
-__global__ __launch_bounds__(64) void sel_scan_kernel(SelArgs a) {
-    constexpr int TB = sel_block_steps<NN>();
-    constexpr int PER = TB * NN / 64;                    // B (and C) values each lane stages
-    __shared__ float4 sBC4[2][2][TB * NN / 4];           // [buffer][B, C][step * NN + n]
-    const int lane = threadIdx.x;
-    int item = blockIdx.x;
-    const int dg = item % a.DG;
-    item /= a.DG;
-    const int k = item % a.Kw;
-    const int b = item / a.Kw;
-    const int64_t T = a.T, Dm = a.Dm, N = a.N;
-    const int64_t d = (int64_t)dg * 64 + lane;
-    const bool dok = d < Dm;
-    const int64_t dd = dok ? d : Dm - 1;                 // clamped for loads
-    const int64_t t0 = (int64_t)k * T / a.K, t1 = (int64_t)(k + 1) * T / a.K;
-    const int nblk = (int)((t1 - t0 + TB - 1) / TB);
-    // A rows of this wave's channels and, past the first chunk, the entering
-    // states: one load each, states past N and channels past Dm read as zero
-    const int64_t hrow = ((int64_t)b * a.K + k) * N;      // ws_h row of (b, k, n = 0)
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a.A + (int64_t)dg * 64 * N, (uint32_t)((Dm - (int64_t)dg * 64) * N * 4));
-    const __amdgpu_buffer_rsrc_t rH = make_rsrc(a.ws_h + hrow * Dm + (int64_t)dg * 64, (uint32_t)(N * Dm * 4 - (int64_t)dg * 256));
-    float A2[NN], h[NN];
-#pragma unroll
-    for (int n = 0; n < NN; ++n) {
-        const uint32_t ao = n < N ? (uint32_t)((lane * N + n) * 4) : kOOB;
-        A2[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rA, ao, 0, 0)) * kLog2e;
-        h[n] = 0.f;
-    }
-    if (MODE == 0 && k > 0) {
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const uint32_t ho = n < N ? (uint32_t)(n * Dm * 4) + (uint32_t)lane * 4 : kOOB;
-            h[n] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rH, ho, 0, 0));
-        }
-    }
-    const float sk = (MODE == 0) ? a.skip[dd] : 0.f;
-    // per-lane byte offsets: u/delta rows are Dm floats apart; B/C staging
-    // element e = lane + 64 j sits at (step e / NN, state e % NN)
-    const uint32_t DmB = (uint32_t)(Dm * 4);
-    const uint32_t uoff = dok ? (uint32_t)lane * 4 : kOOB;
-    uint32_t bcoff[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int e = lane + 64 * j, st = e / NN, n = e % NN;
-        bcoff[j] = n < N ? (uint32_t)((st * N + n) * 4) : kOOB;
-    }
-    float pu[TB], pd[TB], pb[PER], pc[PER];
-    // loads of one block; rows past the chunk read as zero (outside the range)
-    auto fetch = [&](int blk) {
-        const int64_t tb = t0 + (int64_t)blk * TB;
-        const int64_t rows = t1 - tb < TB ? t1 - tb : TB;
-        const int64_t ue = ((int64_t)b * T + tb) * Dm + (int64_t)dg * 64;
-        const uint32_t ubytes = (uint32_t)(rows * Dm * 4 - (int64_t)dg * 256);
-        const __amdgpu_buffer_rsrc_t ru = make_rsrc(a.u + ue, ubytes);
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.delta + ue, ubytes);
-#pragma unroll
-        for (int st = 0; st < TB; ++st) {
-            const uint32_t o = uoff + (uint32_t)st * DmB;
-            pu[st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ru, o, 0, 0));
-            pd[st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, o, 0, 0));
-        }
-        const int64_t be = ((int64_t)b * T + tb) * N;
-        const uint32_t bbytes = (uint32_t)(rows * N * 4);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.B + be, bbytes);
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(a.C + be, bbytes);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            pb[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, bcoff[j], 0, 0));
-            if (MODE == 0) pc[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rc, bcoff[j], 0, 0));
-            else pc[j] = 0.f;
-        }
-    };
-    fetch(0);
-    float dsum = 0.f;
-    for (int blk = 0; blk < nblk; ++blk) {
-        float cu[TB], cd[TB];
-#pragma unroll
-        for (int s = 0; s < TB; ++s) {
-            cu[s] = pu[s];
-            cd[s] = pd[s];
-        }
-        float* sB = reinterpret_cast<float*>(sBC4[blk & 1][0]);
-        float* sC = reinterpret_cast<float*>(sBC4[blk & 1][1]);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            sB[lane + 64 * j] = pb[j];
-            if (MODE == 0) sC[lane + 64 * j] = pc[j];
-        }
-        __syncthreads();
-        if (blk + 1 < nblk) fetch(blk + 1);
-        // rows past the chunk were loaded as zeros: delta = 0 turns the step
-        // into h = 1 * h + 0, so only the store of y needs the row bound
-        const int64_t tb = t0 + (int64_t)blk * TB;
-        const int rows = (int)(t1 - tb < TB ? t1 - tb : TB);
-#pragma unroll
-        for (int s = 0; s < TB; ++s) {
-            const float dl = cd[s], uu = cu[s], su = dl * uu;
-            const float4* B4 = sBC4[blk & 1][0] + s * (NN / 4);
-            const float4* C4 = sBC4[blk & 1][1] + s * (NN / 4);
-            float acc0 = sk * uu, acc1 = 0.f;
-#pragma unroll
-            for (int q = 0; q < NN / 4; ++q) {
-                const float4 bq = B4[q];
-                const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-                float cv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (MODE == 0) {
-                    const float4 cq = C4[q];
-                    cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int n = 4 * q + i;
-                    h[n] = fmaf(__builtin_amdgcn_exp2f(dl * A2[n]), h[n], su * bv[i]);
-                    if (MODE == 0) {
-                        if (i & 1) acc1 = fmaf(cv[i], h[n], acc1);
-                        else acc0 = fmaf(cv[i], h[n], acc0);
-                    }
-                }
-            }
-            dsum += dl;
-            if (MODE == 0 && dok && s < rows) a.y[((int64_t)b * T + tb + s) * Dm + d] = acc0 + acc1;
-        }
-    }
-    if (MODE == 1) {
-#pragma unroll
-        for (int n = 0; n < NN; ++n) {
-            const uint32_t ho = (n < N && dok) ? (uint32_t)(n * Dm * 4) + (uint32_t)lane * 4 : kOOB;
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, h[n]), rH, ho, 0, 0);
-        }
-        if (dok) a.ws_s[((int64_t)b * a.K + k) * Dm + d] = dsum;
-    }
-}
-
-// Pass 2: across chunks the state follows c_{k+1} = exp(A[d,n] s_k) c_k + l_k
-// (l_k: chunk k's end state from zero, s_k: its sum of delta), an affine scan.
-// A workgroup takes 64 channels of one (batch, state) and cuts the chunks into
-// blockDim.y runs: each run folds its chunks from zero (phase 1), one thread
-// per channel joins the runs in order (phase 2), and each run walks its chunks
-// again from its true entering state, storing it per chunk (phase 3). The
-// decay across a run is exp(A[d,n] times the run's sum of s_k), so the join
-// needs one exponential per run. Slot k of ws_h holds l_k on entry and the
-// state entering chunk k on exit (slot 0: zero, never read).
-constexpr int kCarryBatch = 8;
-constexpr int kCarryRuns = 16;
-
-__global__ __launch_bounds__(64 * kCarryRuns) void sel_carry_kernel(SelArgs a) {
-    __shared__ float sL[kCarryRuns][64], sS[kCarryRuns][64];
-    const int lane = threadIdx.x, g = threadIdx.y, runs = blockDim.y;
-    const int64_t Dm = a.Dm, N = a.N;
-    int item = blockIdx.x;
-    const int dg = item % a.DG;
-    item /= a.DG;
-    const int64_t n = item % N;
-    const int b = (int)(item / N);
-    const int64_t d = (int64_t)dg * 64 + lane;
-    const bool dok = d < Dm;
-    const int64_t dd = dok ? d : Dm - 1;
-    const float a2 = a.A[dd * N + n] * kLog2e;
-    const int nk = a.K - 1;                            // chunks whose end state is carried
-    const int per = (nk + runs - 1) / runs;
-    const int k0 = min(nk, g * per), k1 = min(nk, k0 + per);
-    const int64_t hstep = N * Dm;
-    float* hp = a.ws_h + ((int64_t)b * a.K * N + n) * Dm + dd;
-    const float* sp = a.ws_s + (int64_t)b * a.K * Dm + dd;
-
-    // folds chunks [k0, k1) into c; with `store`, writes the entering state
-    // of each chunk first. The next kCarryBatch chunks load while the current
-    // ones are folded.
-    auto walk = [&](float c, bool store, float& ssum) {
-        float nl[kCarryBatch], ns[kCarryBatch];
-        auto fetch = [&](int kb) {
-#pragma unroll
-            for (int j = 0; j < kCarryBatch; ++j) {
-                const int kk = kb + j < k1 ? kb + j : k1 - 1;
-                nl[j] = hp[kk * hstep];
-                ns[j] = sp[kk * Dm];
-            }
-        };
-        if (k1 > k0) fetch(k0);
-        for (int kb = k0; kb < k1; kb += kCarryBatch) {
-            float cl[kCarryBatch], cs[kCarryBatch];
-#pragma unroll
-            for (int j = 0; j < kCarryBatch; ++j) {
-                cl[j] = nl[j];
-                cs[j] = ns[j];
-            }
-            if (kb + kCarryBatch < k1) fetch(kb + kCarryBatch);
-#pragma unroll
-            for (int j = 0; j < kCarryBatch; ++j) {
-                if (kb + j < k1) {
-                    if (store && dok) hp[(kb + j) * hstep] = c;
-                    c = fmaf(__builtin_amdgcn_exp2f(a2 * cs[j]), c, cl[j]);
-                    ssum += cs[j];
-                }
-            }
-        }
-        return c;
-    };
-    float ssum = 0.f;
-    sL[g][lane] = walk(0.f, false, ssum);
-    sS[g][lane] = ssum;
-    __syncthreads();
-    if (g == 0) {
-        float run = 0.f;
-        for (int r = 0; r < runs; ++r) {
-            const float l = sL[r][lane];
-            sL[r][lane] = run;
-            run = fmaf(__builtin_amdgcn_exp2f(a2 * sS[r][lane]), run, l);
-        }
-    }
-    __syncthreads();
-    float unused = 0.f;
-    const float c = walk(sL[g][lane], true, unused);
-    if (k1 == nk && k1 > k0 && dok) hp[nk * hstep] = c;
-}
-
-// Runs per carry workgroup: about the square root of the carried chunks.
-int sel_carry_runs(int K) {
-    int r = 1;
-    while (r < kCarryRuns && r * r < K - 1) r *= 2;
-    return r;
-}
-
-template <int MODE>
-void* sel_ptr(int64_t N) {
-    if (N <= 16) return reinterpret_cast<void*>(&sel_scan_kernel<16, MODE>);
-    if (N <= 32) return reinterpret_cast<void*>(&sel_scan_kernel<32, MODE>);
-    if (N <= 64) return reinterpret_cast<void*>(&sel_scan_kernel<64, MODE>);
-    return nullptr;
-}
-
-// Chunks: enough waves for ~8 per CU, chunks of at least 16 steps.
-int sel_chunks(int64_t b, int64_t T, int64_t DG, int cus) {
-    const int64_t want = (8 * (int64_t)cus + b * DG - 1) / (b * DG);
-    int64_t cap = T / 16;
-    if (cap < 1) cap = 1;
-    int64_t K = want < cap ? want : cap;
-    if (K > 1024) K = 1024;
-    return (int)(K < 1 ? 1 : K);
-}
-
 }  // namespace
 
 extern "C" {
@@ -2559,63 +2269,5 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* da, const 
                           nullptr, stream);
 }
 
-
-ssd_status ssd_selective_scan(const float* u, const float* delta, const float* A, const float* B,
-                              const float* C, const float* skip, float* y, int64_t batch,
-                              int64_t seq_len, int64_t d_model, int64_t d_state, void* stream) {
-    if (!u || !delta || !A || !B || !C || !skip || !y) return SSD_ERR_NULL_ARG;
-    if (batch < 1 || seq_len < 1 || d_model < 1 || d_state < 1) return SSD_ERR_BAD_SHAPE;
-    // d_model bound: a chunk's states (d_state x d_model floats) and a block's
-    // u/delta rows must stay below 2^31 bytes of buffer offset
-    if (d_state > 64 || batch > 65535 || d_model > ((int64_t)1 << 22)) return SSD_ERR_UNSUPPORTED;
-    const float* ins[] = {u, delta, A, B, C, skip};
-    for (const float* p : ins)
-        if (!aligned(p, 4)) return SSD_ERR_UNSUPPORTED;
-    if (!aligned(y, 4)) return SSD_ERR_UNSUPPORTED;
-    const int64_t b = batch, T = seq_len, Dm = d_model, N = d_state;
-    const Span sy = span_of(y, b * T * Dm * 4);
-    const Span sins[] = {span_of(u, b * T * Dm * 4), span_of(delta, b * T * Dm * 4), span_of(A, Dm * N * 4),
-                         span_of(B, b * T * N * 4), span_of(C, b * T * N * 4), span_of(skip, Dm * 4)};
-    for (const Span& si : sins)
-        if (overlap(sy, si)) return SSD_ERR_ALIAS;
-    if (b * T * Dm > ((int64_t)1 << 40)) return SSD_ERR_UNSUPPORTED;
-
-    SelArgs a;
-    memset(&a, 0, sizeof(a));
-    a.u = u; a.delta = delta; a.A = A; a.B = B; a.C = C; a.skip = skip; a.y = y;
-    a.T = T; a.Dm = Dm; a.N = N;
-    a.DG = (int)((Dm + 63) / 64);
-    a.K = sel_chunks(b, T, a.DG, device_cus());
-    const int64_t nwg = b * a.K * a.DG;
-    if (nwg > 0x7fffffff || b * N * a.DG > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    void* ws = nullptr;
-    int ws_entry = -1;
-    if (a.K > 1) {
-        const size_t hbytes = align256((size_t)(b * a.K) * N * Dm * sizeof(float));
-        ws = scratch_acquire(hs, hbytes + (size_t)(b * a.K) * Dm * sizeof(float), &ws_entry);
-        if (!ws) return SSD_ERR_HIP;
-        a.ws_h = static_cast<float*>(ws);
-        a.ws_s = reinterpret_cast<float*>(static_cast<char*>(ws) + hbytes);
-    }
-    ssd_status rs = SSD_OK;
-    void* kargs[] = {&a};
-    if (a.K > 1) {
-        a.Kw = a.K - 1;     // the last chunk's end state is never needed
-        if (hipLaunchKernel(sel_ptr<1>(N), dim3((unsigned)(b * a.Kw * a.DG)), dim3(64), kargs, 0, hs) != hipSuccess)
-            rs = SSD_ERR_HIP;
-        if (rs == SSD_OK) {
-            const int runs = sel_carry_runs(a.K);
-            hipLaunchKernelGGL(sel_carry_kernel, dim3((unsigned)(b * N * a.DG)), dim3(64, runs), 0, hs, a);
-            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
-        }
-    }
-    a.Kw = a.K;
-    if (rs == SSD_OK &&
-        hipLaunchKernel(sel_ptr<0>(N), dim3((unsigned)nwg), dim3(64), kargs, 0, hs) != hipSuccess)
-        rs = SSD_ERR_HIP;
-    if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
-    return rs;
-}
 
 }  // extern "C"

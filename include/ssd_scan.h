@@ -178,6 +178,21 @@ ssd_status ssd_selective_scan(const float *u, const float *delta, const float *A
                               float *y, int64_t batch, int64_t seq_len,
                               int64_t d_model, int64_t d_state, void *stream);
 
+/* ssd_selective_scan with launch options (NULL opts = automatic):
+ *   segments      0: automatic; k >= 1: cut every sequence into chunks of
+ *                 ceil(seq_len / k') steps, k' = min(k, seq_len, 4096) (the
+ *                 last chunk may be shorter; there are at most k' chunks)
+ *   block_slices  must be 0 (SSD_ERR_UNSUPPORTED otherwise)
+ *   reserved      must be zero (SSD_ERR_BAD_SHAPE otherwise)
+ *   walk_events   recorded just before and just after the output pass (the
+ *                 kernel that writes y); both or neither (SSD_ERR_BAD_SHAPE)
+ * The result does not depend on the options beyond rounding. */
+ssd_status ssd_selective_scan_ex(const float *u, const float *delta, const float *A,
+                                 const float *B, const float *C, const float *skip,
+                                 float *y, int64_t batch, int64_t seq_len,
+                                 int64_t d_model, int64_t d_state,
+                                 const ssd_launch_opts *opts, void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssd_status_str(int32_t status);
 

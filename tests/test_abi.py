@@ -167,3 +167,22 @@ def test_selective_alias(lib):
     assert sel_call(y=U) == ssd.SSD_ERR_ALIAS
     assert sel_call(y=DL + 4096) == ssd.SSD_ERR_ALIAS        # inside delta
     assert sel_call(y=AA - 4) == ssd.SSD_ERR_ALIAS           # runs into A
+
+
+def test_selective_launch_options(lib):
+    def ex(opts):
+        return ssd.ssd_selective_scan_ex(U, DL, AA, SB, SC, SK, SY, 2, 100, 512, 16, opts, None)
+    opts = ssd.SsdLaunchOpts()
+    opts.segments = -1
+    assert ex(opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.reserved[0] = 3
+    assert ex(opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.walk_events[1] = 1
+    assert ex(opts) == ssd.SSD_ERR_BAD_SHAPE
+    opts = ssd.SsdLaunchOpts()
+    opts.block_slices = 2
+    assert ex(opts) == ssd.SSD_ERR_UNSUPPORTED
+    assert ssd.ssd_selective_scan_ex(None, DL, AA, SB, SC, SK, SY, 2, 100, 512, 16, None,
+                                     None) == ssd.SSD_ERR_NULL_ARG

@@ -107,3 +107,34 @@ def test_nan_stays_in_its_channel():
     assert torch.isfinite(y[0, :400, 9]).all()
     others = torch.cat([y[0, :, :9], y[0, :, 10:]], dim=1)
     assert torch.isfinite(others).all()
+
+
+@pytest.mark.parametrize("chunks", [1, 2, 7, 100, 999, 5000])
+def test_chunk_count_does_not_change_result(chunks):
+    # explicit chunk counts, including more chunks than blocks of steps and
+    # counts clamped to the sequence length (chunks of one step or empty)
+    inp = si.make_scan_inputs(si.ScanShape(2, 999, 70, 16, 2.0, ""), seed=11)
+    ssd = _ssd()
+    g = inp.to(_dev())
+    y = ssd.selective_scan(g.u, g.delta, g.A, g.B, g.C, g.skip, chunks=chunks)
+    torch.cuda.synchronize()
+    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip)
+    err = normwise(y.cpu().double().numpy(), ref)
+    print(f"chunks {chunks}: y err {err:.3e}", flush=True)
+    assert err <= TOL, (chunks, err)
+
+
+def test_walk_events_time_the_output_pass():
+    ssd = _ssd()
+    inp = si.make_scan_inputs(si.ScanShape(2, 2048, 256, 16, 2.0, ""), seed=2)
+    g = inp.to(_dev())
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    call[0].record()
+    y = ssd.selective_scan(g.u, g.delta, g.A, g.B, g.C, g.skip, walk_events=ev)
+    call[1].record()
+    torch.cuda.synchronize()
+    t_out, t_call = ev[0].elapsed_time(ev[1]), call[0].elapsed_time(call[1])
+    assert 0.0 < t_out <= t_call, (t_out, t_call)
+    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip)
+    assert normwise(y.cpu().double().numpy(), ref) <= TOL
