@@ -251,8 +251,30 @@ __global__ __launch_bounds__(64 * kCarryRuns) void sel_carry_kernel(SelArgs a) {
         }
         return c;
     };
+    // a run of at most kCarryBatch chunks is loaded once and kept in
+    // registers for phase 3
+    const bool one_batch = per <= kCarryBatch;
+    float kl[kCarryBatch], ks[kCarryBatch];
     float ssum = 0.f;
-    sL[g][lane] = walk(0.f, false, ssum);
+    if (one_batch) {
+        float c = 0.f;
+#pragma unroll
+        for (int j = 0; j < kCarryBatch; ++j) {
+            const bool in = k0 + j < k1;
+            const int kk = in ? k0 + j : k0;          // k0 <= K - 1: a valid slot
+            const float l = hp[kk * hstep], sv = sp[kk * Dm];
+            kl[j] = in ? l : 0.f;
+            ks[j] = in ? sv : 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kCarryBatch; ++j) {
+            c = fmaf(__builtin_amdgcn_exp2f(a2 * ks[j]), c, kl[j]);
+            ssum += ks[j];
+        }
+        sL[g][lane] = c;
+    } else {
+        sL[g][lane] = walk(0.f, false, ssum);
+    }
     sS[g][lane] = ssum;
     __syncthreads();
     if (g == 0) {
@@ -264,8 +286,19 @@ __global__ __launch_bounds__(64 * kCarryRuns) void sel_carry_kernel(SelArgs a) {
         }
     }
     __syncthreads();
-    float unused = 0.f;
-    const float c = walk(sL[g][lane], true, unused);
+    float c = sL[g][lane];
+    if (one_batch) {
+#pragma unroll
+        for (int j = 0; j < kCarryBatch; ++j) {
+            if (k0 + j < k1) {
+                if (dok) hp[(k0 + j) * hstep] = c;
+                c = fmaf(__builtin_amdgcn_exp2f(a2 * ks[j]), c, kl[j]);
+            }
+        }
+    } else {
+        float unused = 0.f;
+        c = walk(c, true, unused);
+    }
     if (k1 == nk && k1 > k0 && dok) hp[nk * hstep] = c;
 }
 
