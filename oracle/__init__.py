@@ -53,6 +53,8 @@ def _load(path: Optional[str] = None):
         lib.ssd_oracle_max_threads.restype = ctypes.c_int
         lib.selective_scan_f64.argtypes = [i64] * 4 + [vp] * 7 + [i64, vp, ctypes.c_int]
         lib.selective_scan_f64.restype = ctypes.c_int
+        lib.trapezoid_f64.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, i64, vp, vp, ctypes.c_int]
+        lib.trapezoid_f64.restype = ctypes.c_int
         _libs[key] = lib
     return _libs[key]
 
@@ -172,3 +174,51 @@ def selective_scan(u: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: tor
     if rc != 0:
         raise RuntimeError(f"selective_scan_f64 failed with code {rc}")
     return y
+
+
+def trapezoid(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+              beta: torch.Tensor, gamma: torch.Tensor, prev_x: Optional[torch.Tensor] = None,
+              prev_B: Optional[torch.Tensor] = None, init_state: Optional[torch.Tensor] = None,
+              theta: Optional[torch.Tensor] = None, bh: Optional[Sequence[int]] = None,
+              nthreads: int = 0, lib_path: Optional[str] = None):
+    """Float64 Mamba-3 trapezoid recurrence ("mamba3/scan.py", docstring and
+    scan_forward; "mamba3/moments.rs", build_moments_input).
+
+    Shapes as ssd_oracle (no D), plus beta, gamma [b,T,H] fp32, prev_x
+    [b,R,H,P] and prev_B [b,R,G,N] (x's dtype; both or neither). Returns
+    (y [b,T,R,H,P], final [b,H,P,N]) as float64, or with ``bh`` the selected
+    slices (y_sel [n,T,R,P], final_sel [n,P,N]).
+    """
+    lib = _load(lib_path)
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    assert da.shape == beta.shape == gamma.shape == (b, T, H)
+    assert B.shape == C.shape == (b, T, R, G, N)
+    assert (prev_x is None) == (prev_B is None)
+    if prev_x is not None:
+        assert prev_x.shape == (b, R, H, P) and prev_B.shape == (b, R, G, N)
+        assert prev_x.dtype == x.dtype and prev_B.dtype == x.dtype
+    dt = {torch.bfloat16: 1, torch.float32: 0, torch.float64: 2}[x.dtype]
+    assert B.dtype == x.dtype and C.dtype == x.dtype
+    for t in (da, beta, gamma, init_state, theta):
+        assert t is None or t.dtype == torch.float32
+    cont = lambda t: None if t is None else t.detach().cpu().contiguous()
+    x, da, B, C, beta, gamma, prev_x, prev_B, init_state, theta = map(
+        cont, (x, da, B, C, beta, gamma, prev_x, prev_B, init_state, theta))
+    if bh is None:
+        n, bh_arr = b * H, None
+    else:
+        bh_arr = np.ascontiguousarray(np.asarray(bh, dtype=np.int64))
+        n = int(bh_arr.size)
+    y_sel = np.empty((n, T, R, P), dtype=np.float64)
+    fin = np.empty((n, P, N), dtype=np.float64)
+    rc = lib.trapezoid_f64(
+        b, T, H, P, N, G, R, dt, _ptr(x), _ptr(da), _ptr(B), _ptr(C), _ptr(beta), _ptr(gamma),
+        _ptr(prev_x), _ptr(prev_B), _ptr(init_state), _ptr(theta),
+        None if bh_arr is None else bh_arr.ctypes.data, n, y_sel.ctypes.data, fin.ctypes.data,
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"trapezoid_f64 failed with code {rc}")
+    if bh is not None:
+        return y_sel, fin
+    return y_sel.reshape(b, H, T, R, P).transpose(0, 2, 3, 1, 4).copy(), fin.reshape(b, H, P, N)

@@ -1,6 +1,6 @@
 /*
  * Float64 token-by-token oracle for the chunked SSD scan (and, at the end of
- * this file, for the Mamba-1 selective scan).
+ * this file, for the Mamba-1 selective scan and the Mamba-3 trapezoid).
  *
  * TEST INFRASTRUCTURE ONLY. Nothing on the product path may link, load or
  * call this file; only the tests, the smoke check and the bench's CPU
@@ -243,6 +243,148 @@ int selective_scan_f64(int64_t batch, int64_t T, int64_t Dm, int64_t N,
             }
         }
         free(h);
+    }
+    return err;
+}
+
+/*
+ * Mamba-3 trapezoid (two-write) recurrence in the physical frame, for every
+ * batch b and head h (group g = h / (H/G)):
+ *
+ *   W_t  = sum_r x[b,t,r,h,:] (outer) B[b,t,r,g,:]            (P x N)
+ *   W_-1 = sum_r prev_x[b,r,h,:] (outer) prev_B[b,r,g,:]       (zero if absent)
+ *   h_t  = R(theta[b,t,h]) (exp(da[b,t,h]) h_{t-1} + beta[b,t,h] W_{t-1})
+ *          + gamma[b,t,h] W_t
+ *   y[b,t,r,h,p] = sum_n C[b,t,r,g,n] h_t[p,n]
+ *   h_-1 = init_state[b,h] (or zero); final_state[b,h] = h_{T-1}
+ *
+ * Sources (cited by page title and section):
+ *  - "mamba3/scan.py", module docstring: h_t = alpha_t R(theta_t) h_{t-1}
+ *    + beta_t S_{t-1} + gamma_t S_t; and scan_forward, whose comment (citing
+ *    the Mamba-3 paper's eq. 11) turns the beta write by the previous step's
+ *    cumulative angle. In the physical frame that makes the beta write part
+ *    of what step t rotates, as written above. The docstring's literal form
+ *    (beta write not rotated at step t) is the other reading; this file
+ *    follows the code and eq. 11.
+ *  - burn-mamba "mamba3/moments.rs", module documentation and
+ *    build_moments_input: the beta stream is the previous token's x and
+ *    rotated B scaled by the current beta; its first element comes from the
+ *    cache's previous-token entries (prev_x, prev_B here); the initial state
+ *    enters once.
+ * No skip term (the Mamba-3 scan has none). x, B, C, prev_x, prev_B at their
+ * stored precision; the rest fp32; double arithmetic.
+ */
+static void run_trap_slice(const oracle_problem *pr, const float *beta, const float *gamma,
+                           const void *prev_x, const void *prev_B, int64_t b, int64_t h,
+                           double *y_out, double *fin_out, double *S, double *Wp, double *Wc) {
+    const int64_t T = pr->T, H = pr->H, P = pr->P, N = pr->N, G = pr->G, R = pr->R;
+    const int64_t g = h / (H / G);
+
+    if (pr->init_state) {
+        const float *h0 = pr->init_state + (b * H + h) * P * N;
+        for (int64_t i = 0; i < P * N; ++i) S[i] = (double)h0[i];
+    } else {
+        memset(S, 0, sizeof(double) * (size_t)(P * N));
+    }
+    memset(Wp, 0, sizeof(double) * (size_t)(P * N));
+    if (prev_x && prev_B) {
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t xrow = ((b * R + r) * H + h) * P, brow = ((b * R + r) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double xv = load_elem(prev_x, xrow + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    Wp[p * N + n] += xv * load_elem(prev_B, brow + n, pr->in_dtype);
+            }
+        }
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t sh = (b * T + t) * H + h;
+        /* this step's write W_t */
+        memset(Wc, 0, sizeof(double) * (size_t)(P * N));
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t xrow = (((b * T + t) * R + r) * H + h) * P;
+            int64_t brow = (((b * T + t) * R + r) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double xv = load_elem(pr->x, xrow + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    Wc[p * N + n] += xv * load_elem(pr->B, brow + n, pr->in_dtype);
+            }
+        }
+        /* decayed state plus the previous step's write, then the rotation */
+        const double a = exp((double)pr->da[sh]), be = (double)beta[sh], ga = (double)gamma[sh];
+        for (int64_t i = 0; i < P * N; ++i) S[i] = a * S[i] + be * Wp[i];
+        if (pr->theta) {
+            const float *th = pr->theta + sh * (N / 2);
+            for (int64_t k = 0; k < N / 2; ++k) {
+                double c = cos((double)th[k]), s = sin((double)th[k]);
+                for (int64_t p = 0; p < P; ++p) {
+                    double a0 = S[p * N + 2 * k], a1 = S[p * N + 2 * k + 1];
+                    S[p * N + 2 * k] = c * a0 - s * a1;
+                    S[p * N + 2 * k + 1] = s * a0 + c * a1;
+                }
+            }
+        }
+        for (int64_t i = 0; i < P * N; ++i) S[i] += ga * Wc[i];
+        /* every rank reads the state after both writes of step t */
+        for (int64_t r = 0; r < R; ++r) {
+            int64_t crow = (((b * T + t) * R + r) * G + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n)
+                    acc += load_elem(pr->C, crow + n, pr->in_dtype) * S[p * N + n];
+                y_out[(t * R + r) * P + p] = acc;
+            }
+        }
+        memcpy(Wp, Wc, sizeof(double) * (size_t)(P * N));
+    }
+    memcpy(fin_out, S, sizeof(double) * (size_t)(P * N));
+}
+
+/*
+ * Runs the trapezoid recurrence on the selected (b, h) slices; arguments as
+ * ssd_oracle_f64 (no D), plus beta, gamma [b,T,H] fp32 and the optional
+ * previous-token entries prev_x [b,R,H,P], prev_B [b,R,G,N] (both or neither).
+ */
+int trapezoid_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
+                  int64_t G, int64_t R, int in_dtype,
+                  const void *x, const float *da, const void *B, const void *C,
+                  const float *beta, const float *gamma, const void *prev_x, const void *prev_B,
+                  const float *init_state, const float *theta,
+                  const int64_t *bh_list, int64_t n_bh,
+                  double *y_sel, double *fin_sel, int nthreads) {
+    if (batch < 1 || T < 1 || H < 1 || P < 1 || N < 1 || G < 1 || R < 1) return -1;
+    if (H % G != 0) return -2;
+    if (theta && (N % 2)) return -3;
+    if (in_dtype != ORACLE_IN_F32 && in_dtype != ORACLE_IN_BF16 && in_dtype != ORACLE_IN_F64)
+        return -4;
+    if (!x || !da || !B || !C || !beta || !gamma || !fin_sel || !y_sel) return -5;
+    if ((prev_x == NULL) != (prev_B == NULL)) return -5;
+    if (!bh_list) n_bh = batch * H;
+    for (int64_t i = 0; bh_list && i < n_bh; ++i)
+        if (bh_list[i] < 0 || bh_list[i] >= batch * H) return -6;
+
+    oracle_problem pr = {batch, T, H, P, N, G, R, in_dtype, x, B, C, da, NULL, init_state, theta};
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *buf = (double *)malloc(sizeof(double) * (size_t)(3 * P * N));
+        if (!buf) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_bh; ++i) {
+            if (!buf) continue;
+            int64_t bh = bh_list ? bh_list[i] : i;
+            run_trap_slice(&pr, beta, gamma, prev_x, prev_B, bh / H, bh % H,
+                           y_sel + i * T * R * P, fin_sel + i * P * N, buf, buf + P * N, buf + 2 * P * N);
+        }
+        free(buf);
     }
     return err;
 }

@@ -191,3 +191,47 @@ def make_scan_inputs(shape: ScanShape, seed: int = 0) -> ScanInputs:
     Cm = torch.randn(b, T, N, generator=g, dtype=torch.float32)
     skip = torch.randn(Dm, generator=g, dtype=torch.float32)
     return ScanInputs(shape, u, delta, A, Bm, Cm, skip)
+
+
+# ---------------------------------------------------------------------------
+# Mamba-3 trapezoid (two-write) inputs: an SSD input set plus the trapezoid
+# weights and the previous-token entries.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class TrapInputs:
+    base: Inputs             # x, da, B, C, theta, init_state (D is not used)
+    beta: torch.Tensor       # [b,T,H] fp32, weight of the previous step's write
+    gamma: torch.Tensor      # [b,T,H] fp32, weight of this step's write
+    prev_x: Optional[torch.Tensor]   # [b,R,H,P], x's dtype
+    prev_B: Optional[torch.Tensor]   # [b,R,G,N], x's dtype
+
+    def to(self, device) -> "TrapInputs":
+        mv = lambda t: None if t is None else t.to(device)
+        return TrapInputs(self.base.to(device), mv(self.beta), mv(self.gamma), mv(self.prev_x),
+                          mv(self.prev_B))
+
+
+def make_trapezoid_inputs(shape: Shape, seed: int = 0, prev: bool = True) -> TrapInputs:
+    """Seeded trapezoid inputs on the CPU.
+
+    The SSD inputs come from make_inputs(shape, seed). A second generator,
+    seeded with seed + 7919, then draws in this order: lam ~ U(0, 1) [b,T,H],
+    gamma = lam, beta = (1 - lam) * exp(da) (the trapezoid rule's weights with
+    the step size already in x); prev_x ~ N(0, 1) [b,R,H,P] and
+    prev_B ~ N(0, 1) [b,R,G,N], cast to x's dtype (when ``prev``).
+    """
+    base = make_inputs(shape, seed)
+    b, T, H, P, N, G, R = (shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate,
+                           shape.ngroups, shape.mimo_rank)
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 7919)
+    lam = torch.rand(b, T, H, generator=g, dtype=torch.float32)
+    gamma = lam.contiguous()
+    beta = ((1.0 - lam) * torch.exp(base.da)).contiguous()
+    prev_x = prev_B = None
+    if prev:
+        dt = base.x.dtype
+        prev_x = torch.randn(b, R, H, P, generator=g, dtype=torch.float32).to(dt).contiguous()
+        prev_B = torch.randn(b, R, G, N, generator=g, dtype=torch.float32).to(dt).contiguous()
+    return TrapInputs(base, beta, gamma, prev_x, prev_B)

@@ -17,6 +17,10 @@ quantity another way, as the pages describe it:
   and explicit composed rotations R(Phi_t - Phi_s); for tiny T only.
 * ``mamba1_scan``: the LeetGPU "SSM Selective Scan" statement (Abar, Bbar, h, y
   with skip), per channel d and state index n, written from that page.
+* ``trapezoid_frame_form``: the Mamba-3 trapezoid as "mamba3/scan.py"'s
+  scan_forward computes it: both writes turned into the cumulative frame
+  separately (this step's by R(-Phi_t), the previous step's by R(-Phi_{t-1})),
+  a plain first-order scan g_t = alpha_t g_{t-1} + w_t, then h_t = R(Phi_t) g_t.
 """
 from __future__ import annotations
 
@@ -203,3 +207,38 @@ def mamba1_scan(u, delta, A, Bm, Cm, skip):
                 h = Abar * h + Bbar * u[bi, t, d]
                 y[bi, t, d] = Cm[bi, t] @ h + skip[d] * u[bi, t, d]
     return y
+
+
+def trapezoid_frame_form(x, da, B, C, beta, gamma, prev_x=None, prev_B=None, h0=None,
+                         theta=None):
+    """y [b,T,R,H,P], final [b,H,P,N] via the cumulative-angle frame.
+
+    The state is held as [N, P] per (b, h) as in scan.py (S = B x^T), so the
+    rotation acts on its first axis.
+    """
+    x, da, B, C, beta, gamma = map(f64, (x, da, B, C, beta, gamma))
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    gi = _groups(H, G)
+    Bh, Ch = B[:, :, :, gi, :], C[:, :, :, gi, :]                 # [b,T,R,H,N]
+    S = np.einsum("btrhn,btrhp->bthnp", Bh, x)                     # this step's write
+    if prev_x is not None:
+        Sm1 = np.einsum("brhn,brhp->bhnp", f64(prev_B)[:, :, gi, :], f64(prev_x))
+    else:
+        Sm1 = np.zeros((b, H, N, P))
+    Sprev = np.concatenate([Sm1[:, None], S[:, :-1]], axis=1)
+    if theta is not None:
+        Phi = np.cumsum(f64(theta), axis=1)                         # [b,T,H,N/2]
+    else:
+        Phi = np.zeros((b, T, H, N // 2))
+    Phi_prev = np.concatenate([np.zeros_like(Phi[:, :1]), Phi[:, :-1]], axis=1)
+    rot_n = lambda v, ang: np.swapaxes(rotate_pairs(np.swapaxes(v, -1, -2), ang[..., None, :]), -1, -2)
+    w = (gamma[..., None, None] * rot_n(S, -Phi) + beta[..., None, None] * rot_n(Sprev, -Phi_prev))
+    g = np.zeros((b, H, N, P)) if h0 is None else np.swapaxes(f64(h0), -1, -2).copy()
+    alpha = np.exp(da)
+    y = np.empty((b, T, R, H, P))
+    for t in range(T):
+        g = alpha[:, t, :, None, None] * g + w[:, t]
+        h = rot_n(g, Phi[:, t])
+        y[:, t] = np.einsum("brhn,bhnp->brhp", Ch[:, t], h)
+    return y, np.swapaxes(h, -1, -2)

@@ -442,3 +442,163 @@ def test_selective_scan_pins_catch_planted_mistakes(tmp_path):
         subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
         y = oracle.selective_scan(s.u, s.delta, s.A, s.B, s.C, s.skip, lib_path=so)
         assert relerr(y, ref) > 1e-6, f"planted mistake {name!r} was not caught"
+
+
+# ---------------------------------------------------------------------------
+# Mamba-3 trapezoid (two-write) recurrence
+# ---------------------------------------------------------------------------
+
+def _trap(ti, lib_path=None, **kw):
+    bi = ti.base
+    args = dict(prev_x=ti.prev_x, prev_B=ti.prev_B, init_state=bi.init_state, theta=bi.theta)
+    args.update(kw)
+    return oracle.trapezoid(bi.x, bi.da, bi.B, bi.C, ti.beta, ti.gamma, lib_path=lib_path, **args)
+
+
+TRAP_SHAPES = [dict(seqlen=23, rotation=True, init_state=True, mimo_rank=2),
+               dict(seqlen=17, rotation=False, init_state=False, mimo_rank=1, ngroups=3, nheads=3),
+               dict(seqlen=11, rotation=True, init_state=True, mimo_rank=1, dtype="bf16")]
+
+
+def test_trapezoid_beta0_gamma1_is_the_ssd_scan():
+    # beta = 0, gamma = 1 leaves the single-write recurrence ("mamba3/scan.py",
+    # docstring, with the trapezoid weights at their one-write values)
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=19, rotation=True, init_state=True,
+                                                 mimo_rank=2), seed=40)
+    bi = ti.base
+    y, f = oracle.trapezoid(bi.x, bi.da, bi.B, bi.C, torch.zeros_like(ti.beta),
+                            torch.ones_like(ti.gamma), ti.prev_x, ti.prev_B, bi.init_state,
+                            bi.theta)
+    ys, fs = oracle.ssd_oracle(ti.base.x, ti.base.da, ti.base.B, ti.base.C, None,
+                               ti.base.init_state, ti.base.theta)
+    assert relerr(y, ys) < 1e-12 and relerr(f, fs) < 1e-12
+
+
+@pytest.mark.parametrize("kw", TRAP_SHAPES)
+def test_trapezoid_matches_the_frame_form(kw):
+    ti = si.make_trapezoid_inputs(si.small_shape(**kw), seed=41)
+    y, f = _trap(ti)
+    bi = ti.base
+    yr, fr = forms.trapezoid_frame_form(bi.x, bi.da, bi.B, bi.C, ti.beta, ti.gamma, ti.prev_x,
+                                        ti.prev_B, bi.init_state, bi.theta)
+    assert relerr(y, yr) < TOL and relerr(f, fr) < TOL
+
+
+def test_trapezoid_matches_the_two_channel_expansion():
+    # "mamba3/moments.rs", module documentation: the trapezoid as one
+    # scalar-decay system with 2R channels, x^ = [gamma x, beta x_prev],
+    # b^ = [B~, B~_prev] (rotated B, the previous token's shifted in), run by
+    # the single-write oracle without rotation in the rotated frame
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=21, rotation=True, init_state=True,
+                                                 mimo_rank=2, nheads=2), seed=42)
+    bi = ti.base
+    y, f = _trap(ti)
+    x, B, C = forms.f64(bi.x), forms.f64(bi.B), forms.f64(bi.C)
+    b, T, R, H, P = x.shape
+    N = B.shape[-1]
+    Phi = np.cumsum(forms.f64(bi.theta), axis=1)                       # [b,T,H,N/2]
+    Phi_prev = np.concatenate([np.zeros_like(Phi[:, :1]), Phi[:, :-1]], axis=1)
+    Bh = np.repeat(B, H, axis=3) if B.shape[3] == 1 else B              # per head
+    Ch = np.repeat(C, H, axis=3) if C.shape[3] == 1 else C
+    Bt = forms.rotate_pairs(Bh, -Phi[:, :, None])                       # B~_t
+    Ct = forms.rotate_pairs(Ch, -Phi[:, :, None])
+    Bp = np.concatenate([np.repeat(forms.f64(ti.prev_B), H, axis=2)[:, None], Bh[:, :-1]], axis=1)
+    Btp = forms.rotate_pairs(Bp, -Phi_prev[:, :, None])                 # B~_{t-1}
+    xp = np.concatenate([forms.f64(ti.prev_x)[:, None], x[:, :-1]], axis=1)
+    ga, be = forms.f64(ti.gamma), forms.f64(ti.beta)
+    xh = np.concatenate([ga[:, :, None, :, None] * x, be[:, :, None, :, None] * xp], axis=2)
+    bh = np.concatenate([Bt, Btp], axis=2)
+    ch = np.concatenate([Ct, Ct], axis=2)
+    tt = lambda a: torch.from_numpy(np.ascontiguousarray(a))
+    ye, fe = oracle.ssd_oracle(tt(xh), bi.da, tt(bh), tt(ch), None, bi.init_state)
+    assert relerr(y, ye[:, :, :R]) < TOL
+    fphys = forms.rotate_pairs(fe, Phi[:, -1][:, :, None, :])
+    assert relerr(f, fphys) < TOL
+
+
+def test_trapezoid_closed_form_constant_inputs():
+    # no rotation, one rank, constant decay, weights and write S = x B^T, no
+    # previous token: h_0 = gamma S, h_t = a h_{t-1} + (beta + gamma) S, so
+    # h_t = a^t gamma S + (beta + gamma) S (1 - a^t) / (1 - a)
+    b, T, H, P, N = 1, 12, 1, 3, 4
+    rng = np.random.default_rng(5)
+    xv = rng.standard_normal(P).astype(np.float32)
+    bv = rng.standard_normal(N).astype(np.float32)
+    cv = rng.standard_normal(N).astype(np.float32)
+    x = torch.from_numpy(np.tile(xv, (b, T, 1, H, 1)))
+    B = torch.from_numpy(np.tile(bv, (b, T, 1, 1, 1)))
+    C = torch.from_numpy(np.tile(cv, (b, T, 1, 1, 1)))
+    da = torch.full((b, T, H), -0.3)
+    beta, gamma = torch.full((b, T, H), 0.45), torch.full((b, T, H), 0.7)
+    y, f = oracle.trapezoid(x, da, B, C, beta, gamma)
+    a, be, ga = math.exp(float(da[0, 0, 0])), float(beta[0, 0, 0]), float(gamma[0, 0, 0])
+    S = np.outer(xv.astype(np.float64), bv.astype(np.float64))
+    for t in range(T):
+        ht = a ** t * ga * S + (be + ga) * S * (1 - a ** t) / (1 - a)
+        assert np.allclose(y[0, t, 0, 0], ht @ cv.astype(np.float64), rtol=1e-12, atol=1e-12)
+    assert np.allclose(f[0, 0], ht, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("split", [1, 9, 22])
+def test_trapezoid_split_call_composition(split):
+    # the second call takes the first's final state and its last token as the
+    # previous-token entries ("mamba3/moments.rs": the beta stream's first
+    # element comes from the cache)
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=23, rotation=True, init_state=True,
+                                                 mimo_rank=2), seed=43)
+    bi = ti.base
+    y, f = _trap(ti)
+    sl = lambda a, t0, t1: a[:, t0:t1].contiguous()
+    y1, f1 = oracle.trapezoid(sl(bi.x, 0, split), sl(bi.da, 0, split), sl(bi.B, 0, split),
+                              sl(bi.C, 0, split), sl(ti.beta, 0, split), sl(ti.gamma, 0, split),
+                              ti.prev_x, ti.prev_B, bi.init_state, sl(bi.theta, 0, split))
+    y2, f2 = oracle.trapezoid(sl(bi.x, split, 23), sl(bi.da, split, 23), sl(bi.B, split, 23),
+                              sl(bi.C, split, 23), sl(ti.beta, split, 23), sl(ti.gamma, split, 23),
+                              bi.x[:, split - 1].contiguous(), bi.B[:, split - 1].contiguous(),
+                              torch.from_numpy(f1).float(), sl(bi.theta, split, 23))
+    assert relerr(np.concatenate([y1, y2], axis=1), y) < 1e-6
+    assert relerr(f2, f) < 1e-6
+
+
+def test_trapezoid_selected_slices():
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=13, rotation=True, nheads=3), seed=44)
+    y, f = _trap(ti)
+    ys, fs = _trap(ti, bh=[5, 0, 3])
+    H = ti.base.x.shape[3]
+    for i, bh in enumerate([5, 0, 3]):
+        bb, h = divmod(bh, H)
+        assert np.array_equal(ys[i], y[bb, :, :, h]) and np.array_equal(fs[i], f[bb, h])
+
+
+TRAP_MUTANTS = {
+    # the docstring's literal form: the previous write added after the rotation
+    "trap_beta_not_rotated": [
+        ("for (int64_t i = 0; i < P * N; ++i) S[i] = a * S[i] + be * Wp[i];",
+         "for (int64_t i = 0; i < P * N; ++i) S[i] = a * S[i];"),
+        ("for (int64_t i = 0; i < P * N; ++i) S[i] += ga * Wc[i];",
+         "for (int64_t i = 0; i < P * N; ++i) S[i] += ga * Wc[i] + be * Wp[i];")],
+    "trap_no_shift": [("S[i] = a * S[i] + be * Wp[i];", "S[i] = a * S[i] + be * Wc[i];")],
+    "trap_gamma_dropped": [("S[i] += ga * Wc[i];", "S[i] += Wc[i];")],
+    "trap_prev_ignored": [("if (prev_x && prev_B) {", "if (0) {")],
+    "trap_beta_undecayed": [("S[i] = a * S[i] + be * Wp[i];", "S[i] = a * (S[i] + be * Wp[i]);")],
+}
+
+
+def test_trapezoid_pins_catch_planted_mistakes(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=15, rotation=True, init_state=True,
+                                                 mimo_rank=2), seed=45)
+    bi = ti.base
+    yr, fr = forms.trapezoid_frame_form(bi.x, bi.da, bi.B, bi.C, ti.beta, ti.gamma, ti.prev_x,
+                                        ti.prev_B, bi.init_state, bi.theta)
+    for name, edits in TRAP_MUTANTS.items():
+        mutated = src
+        for old, new in edits:
+            assert mutated.count(old) == 1, (name, old)
+            mutated = mutated.replace(old, new)
+        path = tmp_path / f"{name}.c"
+        path.write_text(mutated)
+        so = str(tmp_path / f"{name}.so")
+        subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
+        y, f = _trap(ti, lib_path=so)
+        assert relerr(y, yr) > 1e-6 or relerr(f, fr) > 1e-6, name
