@@ -316,11 +316,12 @@ static void run_trap_slice(const oracle_problem *pr, const float *beta, const fl
         if (pr->theta) {
             const float *th = pr->theta + sh * (N / 2);
             for (int64_t k = 0; k < N / 2; ++k) {
-                double c = cos((double)th[k]), s = sin((double)th[k]);
+                const double cs = cos((double)th[k]), sn = sin((double)th[k]);
                 for (int64_t p = 0; p < P; ++p) {
-                    double a0 = S[p * N + 2 * k], a1 = S[p * N + 2 * k + 1];
-                    S[p * N + 2 * k] = c * a0 - s * a1;
-                    S[p * N + 2 * k + 1] = s * a0 + c * a1;
+                    double *pair = S + p * N + 2 * k;
+                    const double ev = pair[0], od = pair[1];
+                    pair[0] = cs * ev - sn * od;
+                    pair[1] = sn * ev + cs * od;
                 }
             }
         }
