@@ -320,10 +320,13 @@ def _pin_battery(lib_path):
 def test_pins_catch_planted_mistakes(tmp_path):
     src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
     assert _pin_battery(None) < TOL
+    # each mistake is planted in the SSD recurrence's slice function only
+    a, b = src.index("static void run_slice("), src.index("int ssd_oracle_f64(")
+    body = src[a:b]
     for name, (old, new) in MUTANTS.items():
-        assert src.count(old) == 1, name
+        assert body.count(old) == 1, name
         path = tmp_path / f"{name}.c"
-        path.write_text(src.replace(old, new))
+        path.write_text(src[:a] + body.replace(old, new) + src[b:])
         so = str(tmp_path / f"{name}.so")
         subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
         assert _pin_battery(so) > 1e-6, f"planted mistake {name!r} was not caught"
