@@ -7,9 +7,10 @@ a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
 
 C entry points, mirrored here under the same names:
   ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_selective_scan,
-  ssd_selective_scan_ex, ssd_status_str
-plus ``forward(...)`` and ``selective_scan(...)``, tensor-level conveniences
-over ssd_forward_ex and ssd_selective_scan_ex.
+  ssd_selective_scan_ex, ssd_trapezoid_forward, ssd_status_str
+plus ``forward(...)``, ``selective_scan(...)`` and ``trapezoid(...)``,
+tensor-level conveniences over ssd_forward_ex, ssd_selective_scan_ex and
+ssd_trapezoid_forward.
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ SSD_ERR_ALIAS = 4
 SSD_ERR_HIP = 5
 
 EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
-            "ssd_selective_scan_ex", "ssd_status_str")
+            "ssd_selective_scan_ex", "ssd_trapezoid_forward", "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -74,6 +75,9 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_selective_scan.restype = ctypes.c_int
         lib.ssd_selective_scan_ex.argtypes = [vp] * 7 + [i64] * 4 + [ctypes.POINTER(SsdLaunchOpts), vp]
         lib.ssd_selective_scan_ex.restype = ctypes.c_int
+        lib.ssd_trapezoid_forward.argtypes = ([ctypes.POINTER(SsdDims)] + [vp] * 9 + [i64, i64]
+                                              + [vp] * 3 + [ctypes.POINTER(SsdLaunchOpts), vp])
+        lib.ssd_trapezoid_forward.restype = ctypes.c_int
         lib.ssd_status_str.argtypes = [ctypes.c_int32]
         lib.ssd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -118,6 +122,16 @@ def ssd_selective_scan_ex(u, delta, A, B, C, skip, y, batch, seq_len, d_model, d
     lib = load_library()
     return int(lib.ssd_selective_scan_ex(u, delta, A, B, C, skip, y, int(batch), int(seq_len),
                                          int(d_model), int(d_state),
+                                         None if opts is None else ctypes.byref(opts), stream))
+
+
+def ssd_trapezoid_forward(dims: Optional[SsdDims], x, da, B, C, beta, gamma, prev_x, prev_B,
+                          init_state, chunk_len, R, theta, y, final_state,
+                          opts: Optional[SsdLaunchOpts], stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_trapezoid_forward(None if dims is None else ctypes.byref(dims), x, da, B, C,
+                                         beta, gamma, prev_x, prev_B, init_state, int(chunk_len),
+                                         int(R), theta, y, final_state,
                                          None if opts is None else ctypes.byref(opts), stream))
 
 
@@ -255,3 +269,68 @@ def selective_scan(u, delta, A, B, C, skip, y=None, stream=None, chunks: int = 0
     if st != SSD_OK:
         raise SsdError(st, "ssd_selective_scan_ex")
     return y
+
+
+def trapezoid(x, da, B, C, beta, gamma, prev_x=None, prev_B=None, init_state=None,
+              chunk_len: int = 256, theta=None, y=None, final_state=None, segments: int = 0,
+              stream=None, walk_events=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
+    """Run the Mamba-3 trapezoid forward on device tensors; returns (y, final_state).
+
+    Shapes as ``forward`` (no D), plus beta, gamma [b,T,H] fp32 and the
+    optional previous-token entries prev_x [b,R,H,P], prev_B [b,R,G,N] in
+    x's dtype (both or neither).
+    """
+    import torch
+
+    if x.dim() == 4:
+        x5, B5, C5 = x.unsqueeze(2), B.unsqueeze(2), C.unsqueeze(2)
+        if prev_x is not None:
+            prev_x, prev_B = prev_x.unsqueeze(1), prev_B.unsqueeze(1)
+    else:
+        x5, B5, C5 = x, B, C
+    b, T, R, H, P = x5.shape
+    G, N = B5.shape[3], B5.shape[4]
+    if x.device.type != "cuda":
+        raise ValueError("chunked_ssd_scan_amd.trapezoid needs device tensors")
+    dev = x.device
+    for name, t in (("x", x), ("da", da), ("B", B), ("C", C), ("beta", beta), ("gamma", gamma),
+                    ("prev_x", prev_x), ("prev_B", prev_B), ("init_state", init_state),
+                    ("theta", theta)):
+        if t is None:
+            continue
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if x.dtype == torch.bfloat16:
+        in_dtype = SSD_BF16
+    elif x.dtype == torch.float32:
+        in_dtype = SSD_F32
+    else:
+        raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
+    for name, t in (("B", B), ("C", C), ("prev_x", prev_x), ("prev_B", prev_B)):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype")
+    for name, t in (("da", da), ("beta", beta), ("gamma", gamma), ("init_state", init_state),
+                    ("theta", theta)):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError(f"{name} must be float32")
+    if y is None:
+        y = torch.empty(x.shape, device=dev, dtype=torch.float32)
+    if final_state is None:
+        final_state = torch.empty((b, H, P, N), device=dev, dtype=torch.float32)
+    dims = make_dims(b, T, H, P, N, G, in_dtype)
+    opts = SsdLaunchOpts()
+    opts.segments = int(segments)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    if walk_events is not None:
+        opts.walk_events[0], opts.walk_events[1] = _event_handles(walk_events, stream, dev)
+    with torch.cuda.device(dev):
+        st = ssd_trapezoid_forward(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), C.data_ptr(),
+                                   beta.data_ptr(), gamma.data_ptr(), _dptr(prev_x), _dptr(prev_B),
+                                   _dptr(init_state), chunk_len, R, _dptr(theta), y.data_ptr(),
+                                   final_state.data_ptr(), opts, stream)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_trapezoid_forward")
+    return y, final_state

@@ -7,7 +7,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssd_scan.hip", "sel_scan.hip")]
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("ssd_scan.hip", "sel_scan.hip", "trap_scan.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd_scan.so")
 

@@ -39,14 +39,20 @@ inline Span span_of(const void* p, int64_t bytes) {
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 // Scratch of at least `bytes` for `stream` on the current device, cached per
-// (device, stream) and ordered after its previous use; nullptr on failure.
-// *entry identifies it for scratch_release, which marks the end of this
-// call's use on the stream (defined in ssd_scan.hip).
-void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry);
+// (device, stream, slot) and ordered after its previous use; nullptr on
+// failure. *entry identifies it for scratch_release, which marks the end of
+// this call's use on the stream (defined in ssd_scan.hip). A call that runs
+// another entry point inside it keeps its own buffers in another slot.
+enum { kSlotWork = 0, kSlotExpand = 1 };
+void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry, int slot = kSlotWork);
 bool scratch_release(int entry);
 
 // Compute units of the current device (256 if the query fails).
 int device_cus();
+
+// The shape checks of ssd_forward (sizes, envelope, dtype; defined in
+// ssd_scan.hip).
+ssd_status forward_shape_status(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has_theta);
 
 }  // namespace ssd_detail
 

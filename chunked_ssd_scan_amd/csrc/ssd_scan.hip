@@ -58,6 +58,7 @@ namespace ssd_detail {
 struct ScratchEntry {
     int dev;
     hipStream_t stream;
+    int slot;
     void* ptr;
     size_t bytes;
     hipEvent_t last;    // recorded after the last call that used ptr
@@ -70,17 +71,20 @@ int g_scratch_n = 0;
 // Scratch of at least `bytes` for `stream` on the current device, ordered
 // after its previous use; nullptr on failure. *entry identifies it for
 // scratch_release.
-void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry) {
+void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry, int slot) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return nullptr;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     int i = 0;
-    while (i < g_scratch_n && !(g_scratch[i].dev == dev && g_scratch[i].stream == stream)) ++i;
+    while (i < g_scratch_n &&
+           !(g_scratch[i].dev == dev && g_scratch[i].stream == stream && g_scratch[i].slot == slot))
+        ++i;
     if (i == g_scratch_n) {
         if (g_scratch_n == 256) return nullptr;
         ScratchEntry& e = g_scratch[g_scratch_n];
         e.dev = dev;
         e.stream = stream;
+        e.slot = slot;
         e.ptr = nullptr;
         e.bytes = 0;
         if (hipEventCreateWithFlags(&e.last, hipEventDisableTiming) != hipSuccess) return nullptr;
@@ -2134,6 +2138,14 @@ ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_sta
 }
 
 }  // namespace
+
+namespace ssd_detail {
+
+ssd_status forward_shape_status(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has_theta) {
+    return check_shape(d, chunk_len, R, has_theta);
+}
+
+}  // namespace ssd_detail
 
 extern "C" {
 

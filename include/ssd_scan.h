@@ -193,6 +193,39 @@ ssd_status ssd_selective_scan_ex(const float *u, const float *delta, const float
                                  int64_t d_model, int64_t d_state,
                                  const ssd_launch_opts *opts, void *stream);
 
+/*
+ * Mamba-3 trapezoid (two-write) forward. "mamba3/scan.py", module docstring
+ * and scan_forward (whose comment cites the Mamba-3 paper's eq. 11), and
+ * burn-mamba "mamba3/moments.rs", build_moments_input (previous-token
+ * entries). Per batch b and head h (group g = h / (H/G)):
+ *
+ *   W_t  = sum_r x[b,t,r,h,:] (outer) B[b,t,r,g,:]
+ *   W_-1 = sum_r prev_x[b,r,h,:] (outer) prev_B[b,r,g,:]   (zero when NULL)
+ *   h_t  = R(theta[b,t,h]) (exp(da[b,t,h]) h_{t-1} + beta[b,t,h] W_{t-1})
+ *          + gamma[b,t,h] W_t
+ *   y[b,t,r,h,p] = sum_n C[b,t,r,g,n] h_t[p,n]        (no skip term)
+ *   h_-1 = init_state (or zero), final_state = h_{T-1}
+ *
+ * The previous step's write is turned by theta_t with the decayed state
+ * (it enters the cumulative frame at the previous step's angle).
+ * Arguments as ssd_forward_ex (without D), plus:
+ *   beta, gamma  [b, T, H] fp32, 4-byte aligned
+ *   prev_x       [b, R, H, P] in_dtype, element-aligned, may be NULL
+ *   prev_B       [b, R, G, N] in_dtype, element-aligned; NULL exactly when
+ *                prev_x is (SSD_ERR_NULL_ARG otherwise)
+ * Runs as the single-write scan over 2T sub-steps (decay then turn), so the
+ * envelope is ssd_forward's at seqlen 2T; opts apply to that scan (walk
+ * events bracket its output walk). Scratch: the sub-step inputs and outputs
+ * (about 2x x, B, C, da, theta and 2x y in bytes) in a second per-(device,
+ * stream) buffer of the library, besides ssd_forward's own.
+ */
+ssd_status ssd_trapezoid_forward(const ssd_dims *d, const void *x, const float *da,
+                                 const void *B, const void *C, const float *beta,
+                                 const float *gamma, const void *prev_x, const void *prev_B,
+                                 const float *init_state, int64_t chunk_len, int64_t R,
+                                 const float *theta, float *y, float *final_state,
+                                 const ssd_launch_opts *opts, void *stream);
+
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssd_status_str(int32_t status);
 

@@ -186,3 +186,50 @@ def test_selective_launch_options(lib):
     assert ex(opts) == ssd.SSD_ERR_UNSUPPORTED
     assert ssd.ssd_selective_scan_ex(None, DL, AA, SB, SC, SK, SY, 2, 100, 512, 16, None,
                                      None) == ssd.SSD_ERR_NULL_ARG
+
+
+# ---- ssd_trapezoid_forward -------------------------------------------------
+
+BE, GA, PX, PB = (0x10000000 * (i + 40) for i in range(4))
+
+
+def trap_call(d=None, x=X, da=DA, B=BB, C=CC, beta=BE, gamma=GA, px=PX, pb=PB, init=H0,
+              chunk=64, R=1, theta=None, y=Y, fin=FS, opts=None):
+    if d is None:
+        d = dims()
+    return ssd.ssd_trapezoid_forward(d, x, da, B, C, beta, gamma, px, pb, init, chunk, R, theta,
+                                     y, fin, opts, None)
+
+
+@pytest.mark.parametrize("field", ["x", "da", "B", "C", "beta", "gamma", "y", "fin"])
+def test_trapezoid_null_pointer(lib, field):
+    assert trap_call(**{field: None}) == ssd.SSD_ERR_NULL_ARG
+
+
+def test_trapezoid_prev_both_or_neither(lib):
+    assert trap_call(px=None) == ssd.SSD_ERR_NULL_ARG
+    assert trap_call(pb=None) == ssd.SSD_ERR_NULL_ARG
+    assert ssd.ssd_trapezoid_forward(None, X, DA, BB, CC, BE, GA, None, None, None, 64, 1, None, Y,
+                                     FS, None, None) == ssd.SSD_ERR_NULL_ARG
+
+
+def test_trapezoid_shape_and_envelope(lib):
+    assert trap_call(d=dims(seqlen=0)) == ssd.SSD_ERR_BAD_SHAPE
+    assert trap_call(d=dims(nheads=4, ngroups=3)) == ssd.SSD_ERR_BAD_SHAPE
+    assert trap_call(d=dims(dstate=17), theta=TH) == ssd.SSD_ERR_BAD_SHAPE
+    assert trap_call(d=dims(headdim=48)) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(R=3) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(x=X + 2) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(beta=BE + 2) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(px=PX + 1) == ssd.SSD_ERR_UNSUPPORTED
+
+
+def test_trapezoid_alias(lib):
+    assert trap_call(y=X) == ssd.SSD_ERR_ALIAS
+    assert trap_call(y=BE) == ssd.SSD_ERR_ALIAS
+    assert trap_call(fin=GA) == ssd.SSD_ERR_ALIAS
+    assert trap_call(fin=H0 + 256) == ssd.SSD_ERR_ALIAS
+    assert trap_call(y=FS) == ssd.SSD_ERR_ALIAS
+    opts = ssd.SsdLaunchOpts()
+    opts.reserved[0] = 1
+    assert trap_call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
