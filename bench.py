@@ -221,6 +221,93 @@ def selective_bench(args) -> dict:
     return out
 
 
+def trapezoid_bench(args) -> dict:
+    """The Mamba-3 trapezoid forward on the Mamba-3 MIMO layer shape as its own line."""
+    import dataclasses
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    shape = si.CONFIGS[3]
+    dev = torch.device("cuda:0")
+    ti = si.make_trapezoid_inputs(shape, seed=0)
+    g = ti.to(dev)
+    bi = g.base
+    b, T, R, H, P = bi.x.shape
+    N = shape.dstate
+    y = torch.empty((b, T, R, H, P), device=dev, dtype=torch.float32)
+    fin = torch.empty((b, H, P, N), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(walk_events=None):
+        ssd.trapezoid(bi.x, bi.da, bi.B, bi.C, g.beta, g.gamma, g.prev_x, g.prev_B, bi.init_state,
+                      shape.chunk_len, bi.theta, y=y, final_state=fin, segments=args.segments,
+                      stream=stream.cuda_stream, walk_events=walk_events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = start.elapsed_time(end) / args.steps
+    walk_ms = time_walk(step, args.steps)
+    if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
+        raise RuntimeError("non-finite output")
+    # the dominant kernel is the rotating walk over 2T sub-steps: its own
+    # compulsory bytes are those of that single-write problem (no D)
+    sub = dataclasses.replace(shape, seqlen=2 * T, skip="none")
+    walk_bytes = algorithmic_bytes(sub)
+    esz = 2 if shape.dtype == "bf16" else 4
+    trap_bytes = (algorithmic_bytes(dataclasses.replace(shape, skip="none"))
+                  + 2 * b * T * H * 4 + b * R * (H * P + shape.ngroups * N) * esz)
+    achieved = walk_bytes / (walk_ms * 1e-3) / 1e9
+    out = {
+        "metric": "trapezoid fwd tokens/s + % of HBM roofline (b4,T4096,H32,P64,N128,R4)",
+        "value": b * T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; see ssd_inputs.make_trapezoid_inputs)",
+        "config": {"workload": "mamba3 MIMO layer, trapezoid " + shape.name, "batch": b,
+                   "seqlen": T, "nheads": H, "headdim": P, "dstate": N, "mimo_rank": R,
+                   "rotation": True, "init_state": True, "prev_token": True,
+                   "segments": args.segments or "auto"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": walk_bytes, "kernel_ms": walk_ms, "forward_ms": call_ms,
+                     "forward_bytes": trap_bytes,
+                     "forward_frac": trap_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        nbh = b * H
+        nsl = max(1, min(args.cpu_slices // 8, nbh))
+        sel = [int(i * nbh / nsl) for i in range(nsl)]
+        t1 = time.perf_counter()
+        oracle.trapezoid(ti.base.x, ti.base.da, ti.base.B, ti.base.C, ti.beta, ti.gamma, ti.prev_x,
+                         ti.prev_B, ti.base.init_state, ti.base.theta, bh=sel, nthreads=threads)
+        secs = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": b * T * (nsl / nbh) / secs, "unit": "tokens/s",
+                               "cores": threads, "kind": "oracle",
+                               "sample": (f"{nsl} of the {nbh} (batch, head) slices over the full "
+                                          f"T={T}; {secs:.2f} s wall; tokens/s scaled by the "
+                                          f"slice fraction")}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,9 +319,10 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--block-slices", type=int, default=0)
-    ap.add_argument("--workload", choices=("ssd", "selective_scan"), default="ssd",
+    ap.add_argument("--workload", choices=("ssd", "selective_scan", "trapezoid"), default="ssd",
                     help="ssd: the chunked SSD scan (the reported line); selective_scan: "
-                         "the diagonal selective scan, b4 T4096 D512 N16 (--segments = chunks)")
+                         "the diagonal selective scan, b4 T4096 D512 N16 (--segments = chunks); "
+                         "trapezoid: the Mamba-3 two-write forward on the MIMO layer shape")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) for counter calibration")
     args = ap.parse_args()
@@ -264,6 +352,9 @@ def main() -> int:
     ssd.load_library()
     if args.workload == "selective_scan":
         print(json.dumps(selective_bench(args)), flush=True)
+        return 0
+    if args.workload == "trapezoid":
+        print(json.dumps(trapezoid_bench(args)), flush=True)
         return 0
     shape = si.CONFIGS[args.config]
     dev = torch.device("cuda:0")

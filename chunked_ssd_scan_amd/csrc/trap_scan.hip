@@ -25,16 +25,6 @@ namespace {
 
 using namespace ssd_detail;
 
-__device__ __forceinline__ float load_as_f(const float* p, int64_t i) { return p[i]; }
-__device__ __forceinline__ float load_as_f(const uint16_t* p, int64_t i) {
-    return __uint_as_float((uint32_t)p[i] << 16);
-}
-__device__ __forceinline__ void store_from_f(float* p, int64_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void store_from_f(uint16_t* p, int64_t i, float v) {
-    const __bf16 h = (__bf16)v;                       // round to nearest even
-    p[i] = __builtin_bit_cast(uint16_t, h);
-}
-
 struct ExpandArgs {
     const void* x;
     const float* da;
@@ -51,96 +41,87 @@ struct ExpandArgs {
     void* Ch;        // [b][2T][R][G][N]
     float* thh;      // [b][2T][H][N/2], or null
     int64_t b, T, R, H, P, G, N;
+    int esz;         // bytes per x/B/C element (2: bf16, 4: fp32)
 };
 
-// x^: sub-step 2t takes beta_t x_{t-1} (prev_x at t = 0), 2t+1 takes gamma_t x_t
-template <typename TI>
-__global__ __launch_bounds__(256) void trap_expand_x(ExpandArgs a) {
-    const int64_t row = a.R * a.H * a.P, hp = a.H * a.P;
-    const int64_t total = a.b * a.T * row;
-    const TI* x = static_cast<const TI*>(a.x);
-    const TI* px = static_cast<const TI*>(a.prev_x);
-    TI* xh = static_cast<TI*>(a.xh);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t bt = i / row, e = i - bt * row;
-        const int64_t bb = bt / a.T, t = bt - bb * a.T;
-        const int64_t h = (e % hp) / a.P;
-        const int64_t sh = bt * a.H + h;
-        float prev = 0.f;
-        if (t > 0) prev = load_as_f(x, i - row);
-        else if (px) prev = load_as_f(px, bb * row + e);
-        const int64_t o = (bb * 2 * a.T + 2 * t) * row + e;
-        store_from_f(xh, o, a.beta[sh] * prev);
-        store_from_f(xh, o + row, a.gamma[sh] * load_as_f(x, i));
+// 16 bytes of x scaled by w: 8 bf16 or 4 fp32 lanes, rounded back to the
+// stored type (bf16: round to nearest even)
+__device__ __forceinline__ uint4 scale16(uint4 v, float w, bool bf) {
+    uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    if (bf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(u[i] << 16) * w, hi = __uint_as_float(u[i] & 0xffff0000u) * w;
+            const __bf16 l = (__bf16)lo, h = (__bf16)hi;
+            u[i] = (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = __float_as_uint(__uint_as_float(u[i]) * w);
     }
+    return make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-// B^, C^ (raw element copies): B^_{2t} = B_{t-1} (prev_B at t = 0),
-// B^_{2t+1} = B_t, C^_{2t} = C^_{2t+1} = C_t (sub-step 2t's y is not kept)
-template <typename TI>
-__global__ __launch_bounds__(256) void trap_expand_bc(ExpandArgs a) {
-    const int64_t row = a.R * a.G * a.N;
-    const int64_t total = a.b * a.T * row;
-    const TI* B = static_cast<const TI*>(a.B);
-    const TI* C = static_cast<const TI*>(a.C);
-    const TI* pB = static_cast<const TI*>(a.prev_B);
-    TI* Bh = static_cast<TI*>(a.Bh);
-    TI* Ch = static_cast<TI*>(a.Ch);
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t bt = i / row, e = i - bt * row;
-        const int64_t bb = bt / a.T, t = bt - bb * a.T;
-        TI prev = (TI)0;
-        if (t > 0) prev = B[i - row];
-        else if (pB) prev = pB[bb * row + e];
-        const int64_t o = (bb * 2 * a.T + 2 * t) * row + e;
-        const TI c = C[i];
-        Bh[o] = prev;
-        Bh[o + row] = B[i];
-        Ch[o] = c;
-        Ch[o + row] = c;
+// One workgroup per (batch, step) row; builds sub-steps 2t and 2t+1:
+//   x^_{2t} = beta_t x_{t-1} (prev_x at t = 0),  x^_{2t+1} = gamma_t x_t
+//   B^_{2t} = B_{t-1} (prev_B at t = 0),         B^_{2t+1} = B_t
+//   C^_{2t} = C^_{2t+1} = C_t                    (sub-step 2t's y is not kept)
+//   da^_{2t} = da_t, da^_{2t+1} = 0;  theta^_{2t} = 0, theta^_{2t+1} = theta_t
+// x, B and C rows move in 16-byte vectors (rows are multiples of 32 bytes).
+__global__ __launch_bounds__(256) void trap_expand_rows(ExpandArgs a) {
+    const int64_t bt = blockIdx.x;
+    const int64_t bb = bt / a.T, t = bt - bb * a.T;
+    const int64_t o = bb * 2 * a.T + 2 * t;            // row of sub-step 2t
+    const bool bf = a.esz == 2;
+    const int per = 16 / a.esz;                        // elements per vector
+    // x
+    const int64_t xrow = a.R * a.H * a.P, xv = xrow * a.esz / 16, hp = a.H * a.P;
+    const uint4* x = static_cast<const uint4*>(a.x);
+    const uint4* xprev = t > 0 ? x + (bt - 1) * xv : (a.prev_x ? static_cast<const uint4*>(a.prev_x) + bb * xv : nullptr);
+    uint4* xh = static_cast<uint4*>(a.xh);
+    for (int64_t j = threadIdx.x; j < xv; j += blockDim.x) {
+        const int64_t h = ((j * per) % hp) / a.P;      // a vector never straddles two heads
+        const float be = a.beta[bt * a.H + h], ga = a.gamma[bt * a.H + h];
+        const uint4 cur = x[bt * xv + j];
+        const uint4 prv = xprev ? xprev[j] : make_uint4(0, 0, 0, 0);
+        xh[o * xv + j] = scale16(prv, be, bf);
+        xh[(o + 1) * xv + j] = scale16(cur, ga, bf);
     }
-}
-
-// da^ and theta^: sub-step 2t decays by da_t without turning, 2t+1 turns by
-// theta_t without decaying
-__global__ __launch_bounds__(256) void trap_expand_da_theta(ExpandArgs a) {
-    const int64_t K = a.N / 2;
-    const int64_t total = a.b * a.T * a.H;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t bt = i / a.H, h = i - bt * a.H;
-        const int64_t bb = bt / a.T, t = bt - bb * a.T;
-        const int64_t o = (bb * 2 * a.T + 2 * t) * a.H + h;
-        a.dah[o] = a.da[i];
-        a.dah[o + a.H] = 0.f;
-        if (a.thh) {
-            for (int64_t k = 0; k < K; ++k) {
-                a.thh[o * K + k] = 0.f;
-                a.thh[(o + a.H) * K + k] = a.theta[i * K + k];
-            }
+    // B, C
+    const int64_t bv = a.R * a.G * a.N * a.esz / 16;
+    const uint4* B = static_cast<const uint4*>(a.B);
+    const uint4* C = static_cast<const uint4*>(a.C);
+    const uint4* bprev = t > 0 ? B + (bt - 1) * bv : (a.prev_B ? static_cast<const uint4*>(a.prev_B) + bb * bv : nullptr);
+    uint4* Bh = static_cast<uint4*>(a.Bh);
+    uint4* Ch = static_cast<uint4*>(a.Ch);
+    for (int64_t j = threadIdx.x; j < bv; j += blockDim.x) {
+        const uint4 c = C[bt * bv + j];
+        Bh[o * bv + j] = bprev ? bprev[j] : make_uint4(0, 0, 0, 0);
+        Bh[(o + 1) * bv + j] = B[bt * bv + j];
+        Ch[o * bv + j] = c;
+        Ch[(o + 1) * bv + j] = c;
+    }
+    // da, theta
+    for (int64_t j = threadIdx.x; j < a.H; j += blockDim.x) {
+        a.dah[o * a.H + j] = a.da[bt * a.H + j];
+        a.dah[(o + 1) * a.H + j] = 0.f;
+    }
+    if (a.thh) {
+        const int64_t tr = a.H * (a.N / 2);
+        for (int64_t j = threadIdx.x; j < tr; j += blockDim.x) {
+            a.thh[o * tr + j] = 0.f;
+            a.thh[(o + 1) * tr + j] = a.theta[bt * tr + j];
         }
     }
 }
 
-// y_t = y^_{2t+1}; rows of R*H*P floats, a multiple of 4
-__global__ __launch_bounds__(256) void trap_gather_y(const float4* yh, float4* y, int64_t b, int64_t T,
-                                                     int64_t row4) {
-    const int64_t total = b * T * row4;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t bt = i / row4, e = i - bt * row4;
-        const int64_t bb = bt / T, t = bt - bb * T;
-        y[i] = yh[(bb * 2 * T + 2 * t + 1) * row4 + e];
-    }
-}
-
-unsigned grid_for(int64_t n) {
-    int64_t g = (n + 255) / 256;
-    const int64_t cap = 256 * 64;     // grid-stride beyond 64 blocks per CU
-    if (g > cap) g = cap;
-    return (unsigned)(g < 1 ? 1 : g);
+// y_t = y^_{2t+1}: one workgroup per (batch, step) row of R*H*P floats
+__global__ __launch_bounds__(256) void trap_gather_y(const float4* yh, float4* y, int64_t T, int64_t row4) {
+    const int64_t bt = blockIdx.x;
+    const int64_t bb = bt / T, t = bt - bb * T;
+    const float4* src = yh + (bb * 2 * T + 2 * t + 1) * row4;
+    float4* dst = y + bt * row4;
+    for (int64_t j = threadIdx.x; j < row4; j += blockDim.x) dst[j] = src[j];
 }
 
 }  // namespace
@@ -156,7 +137,7 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
     if ((prev_x == nullptr) != (prev_B == nullptr)) return SSD_ERR_NULL_ARG;
     ssd_status st = forward_shape_status(d, chunk_len, R, theta != nullptr);
     if (st != SSD_OK) return st;
-    if (d->seqlen > ((int64_t)1 << 39)) return SSD_ERR_UNSUPPORTED;
+    if (d->seqlen > ((int64_t)1 << 39) || d->batch * d->seqlen > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     ssd_dims d2 = *d;
     d2.seqlen = 2 * d->seqlen;
     st = forward_shape_status(&d2, chunk_len, R, theta != nullptr);
@@ -174,7 +155,7 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
         !aligned(final_state, 16) || (init_state && !aligned(init_state, 16)))
         return SSD_ERR_UNSUPPORTED;
     if (!aligned(da, 4) || !aligned(beta, 4) || !aligned(gamma, 4) || (theta && !aligned(theta, 4)) ||
-        (prev_x && !aligned(prev_x, (uintptr_t)esz)) || (prev_B && !aligned(prev_B, (uintptr_t)esz)))
+        (prev_x && !aligned(prev_x, 16)) || (prev_B && !aligned(prev_B, 16)))
         return SSD_ERR_UNSUPPORTED;
     const Span sy = span_of(y, b * T * R * H * P * 4);
     const Span sf = span_of(final_state, b * H * P * N * 4);
@@ -218,23 +199,16 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
     a.b = b; a.T = T; a.R = R; a.H = H; a.P = P; a.G = G; a.N = N;
 
     ssd_status rs = SSD_OK;
-    const bool bf = d->in_dtype == SSD_BF16;
-    if (bf) {
-        hipLaunchKernelGGL(trap_expand_x<uint16_t>, dim3(grid_for(b * T * R * H * P)), dim3(256), 0, hs, a);
-        hipLaunchKernelGGL(trap_expand_bc<uint16_t>, dim3(grid_for(b * T * R * G * N)), dim3(256), 0, hs, a);
-    } else {
-        hipLaunchKernelGGL(trap_expand_x<float>, dim3(grid_for(b * T * R * H * P)), dim3(256), 0, hs, a);
-        hipLaunchKernelGGL(trap_expand_bc<float>, dim3(grid_for(b * T * R * G * N)), dim3(256), 0, hs, a);
-    }
-    hipLaunchKernelGGL(trap_expand_da_theta, dim3(grid_for(b * T * H)), dim3(256), 0, hs, a);
+    a.esz = (int)esz;
+    hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(b * T)), dim3(256), 0, hs, a);
     if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
     if (rs == SSD_OK)
         rs = ssd_forward_ex(&d2, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, chunk_len, R, a.thh, yh,
                             final_state, opts, stream);
     if (rs == SSD_OK) {
         const int64_t row4 = R * H * P / 4;
-        hipLaunchKernelGGL(trap_gather_y, dim3(grid_for(b * T * row4)), dim3(256), 0, hs,
-                           reinterpret_cast<const float4*>(yh), reinterpret_cast<float4*>(y), b, T, row4);
+        hipLaunchKernelGGL(trap_gather_y, dim3((unsigned)(b * T)), dim3(256), 0, hs,
+                           reinterpret_cast<const float4*>(yh), reinterpret_cast<float4*>(y), T, row4);
         if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
     }
     if (!scratch_release(entry) && rs == SSD_OK) rs = SSD_ERR_HIP;

@@ -210,9 +210,10 @@ ssd_status ssd_selective_scan_ex(const float *u, const float *delta, const float
  * (it enters the cumulative frame at the previous step's angle).
  * Arguments as ssd_forward_ex (without D), plus:
  *   beta, gamma  [b, T, H] fp32, 4-byte aligned
- *   prev_x       [b, R, H, P] in_dtype, element-aligned, may be NULL
- *   prev_B       [b, R, G, N] in_dtype, element-aligned; NULL exactly when
+ *   prev_x       [b, R, H, P] in_dtype, 16-byte aligned, may be NULL
+ *   prev_B       [b, R, G, N] in_dtype, 16-byte aligned; NULL exactly when
  *                prev_x is (SSD_ERR_NULL_ARG otherwise)
+ *   batch * seqlen must stay below 2^31 (SSD_ERR_UNSUPPORTED)
  * Runs as the single-write scan over 2T sub-steps (decay then turn), so the
  * envelope is ssd_forward's at seqlen 2T; opts apply to that scan (walk
  * events bracket its output walk). Scratch: the sub-step inputs and outputs

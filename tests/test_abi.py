@@ -221,7 +221,8 @@ def test_trapezoid_shape_and_envelope(lib):
     assert trap_call(R=3) == ssd.SSD_ERR_UNSUPPORTED
     assert trap_call(x=X + 2) == ssd.SSD_ERR_UNSUPPORTED
     assert trap_call(beta=BE + 2) == ssd.SSD_ERR_UNSUPPORTED
-    assert trap_call(px=PX + 1) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(px=PX + 8) == ssd.SSD_ERR_UNSUPPORTED
+    assert trap_call(pb=PB + 2) == ssd.SSD_ERR_UNSUPPORTED
 
 
 def test_trapezoid_alias(lib):
