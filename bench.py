@@ -66,6 +66,7 @@ def algorithmic_flops(s) -> int:
 KERNEL_SOURCES = {
     "ssd": ("ssd_scan.hip", "ssd_common.h"),
     "selective_scan": ("sel_scan.hip", "ssd_common.h"),
+    "trapezoid": ("ssd_scan.hip", "ssd_common.h", "trap_scan.hip"),
 }
 
 
@@ -260,9 +261,10 @@ def trapezoid_bench(args) -> dict:
     if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite output")
     # the dominant kernel is the rotating walk over 2T sub-steps: its own
-    # compulsory bytes are those of that single-write problem (no D)
+    # compulsory bytes are those of that single-write problem (no D), less
+    # the y of the even sub-steps, which it does not write
     sub = dataclasses.replace(shape, seqlen=2 * T, skip="none")
-    walk_bytes = algorithmic_bytes(sub)
+    walk_bytes = algorithmic_bytes(sub) - b * T * R * H * P * 4
     esz = 2 if shape.dtype == "bf16" else 4
     trap_bytes = (algorithmic_bytes(dataclasses.replace(shape, skip="none"))
                   + 2 * b * T * H * 4 + b * R * (H * P + shape.ngroups * N) * esz)
@@ -285,7 +287,8 @@ def trapezoid_bench(args) -> dict:
                    "rotation": True, "init_state": True, "prev_token": True,
                    "segments": args.segments or "auto"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic("trapezoid", "trapezoid"),
                      "algorithmic_bytes": walk_bytes, "kernel_ms": walk_ms, "forward_ms": call_ms,
                      "forward_bytes": trap_bytes,
                      "forward_frac": trap_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},

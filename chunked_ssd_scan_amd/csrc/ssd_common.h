@@ -54,6 +54,14 @@ int device_cus();
 // ssd_scan.hip).
 ssd_status forward_shape_status(const ssd_dims* d, int64_t chunk_len, int64_t R, bool has_theta);
 
+// ssd_forward_ex; with ysub = 1 (seqlen even) y keeps only the odd time
+// steps, step 2s + 1 written as step s of a y with seqlen / 2 steps (defined
+// in ssd_scan.hip).
+ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const void* B,
+                        const void* C, const float* D, const float* init_state, int64_t chunk_len,
+                        int64_t R, const float* theta, float* y, float* final_state,
+                        const ssd_launch_opts* opts, void* stream, int ysub);
+
 }  // namespace ssd_detail
 
 #endif  // SSD_COMMON_H

@@ -251,6 +251,7 @@ struct WalkArgs {
     int nsub;              // tiles per sequence
     int log2R;
     int Qt;                // time steps per tile (32 / R)
+    int ysub;              // 1: y keeps only the odd time steps, as step (t - 1) / 2
 };
 
 // ---------------------------------------------------------------------------
@@ -656,8 +657,13 @@ __global__ __launch_bounds__(4 * P) void ssd_walk_kernel(WalkArgs a) {
 #pragma unroll
             for (int I = 0; I < 2; ++I) {
                 const int64_t fr = fbase + 16 * I + l16;
-                if (fr < TR) {
-                    float* dst = a.y + ((b * TR + fr) * H + h) * P + p0 + 4 * q;
+                // with ysub, only odd steps are kept: row fr = t R + r goes to
+                // ((t - 1) / 2) R + r of a y with T / 2 steps
+                const int64_t st = fr >> log2R;
+                if (fr < TR && (!a.ysub || (st & 1))) {
+                    const int64_t yr = a.ysub ? (((st >> 1) << log2R) | (fr & ((1 << log2R) - 1))) : fr;
+                    const int64_t ytr = a.ysub ? TR / 2 : TR;
+                    float* dst = a.y + ((b * ytr + yr) * H + h) * P + p0 + 4 * q;
                     *reinterpret_cast<f32x4*>(dst) = yacc[I];
                 }
             }
@@ -808,6 +814,7 @@ struct TileArgs {
     int S, seg_items, nsub, log2R, Qt;
     int SF;                // output pass: state-pass segments per segment
     int NB;                // column blocks per B/C group
+    int ysub;              // 1: y keeps only the odd time steps, as step (t - 1) / 2
 };
 
 // Operand whose reduction index runs down the rows of a row-major LDS tile:
@@ -1479,15 +1486,23 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     // 16-byte units of the block's rows, spread over the compute threads
     // (their barrier wait has room for it; the memory waves have less)
     constexpr int YPC = (YU + NTC - 1) / NTC;
-    const auto rs_y = make_rsrc(a.y + (b * TR + row0) * xrow_el + col0, (uint32_t)(((vrows - 1) * xrow_el + CW) * 4));
-    const uint32_t ystep = (uint32_t)(F * xrow_el * 4);
+    // with ysub, y holds only the odd steps (a tile starts at an even step,
+    // 32 / R being even): local row r = j R + k of an odd step j goes to
+    // compact row (j >> 1) R + k, half a tile of rows per tile
+    const int ys = a.ysub ? 1 : 0;
+    const auto rs_y = make_rsrc(a.y + (b * (TR >> ys) + (row0 >> ys)) * xrow_el + col0,
+                                (uint32_t)((((vrows >> ys) - 1) * xrow_el + CW) * 4));
+    const uint32_t ystep = (uint32_t)((F >> ys) * xrow_el * 4);
     uint32_t ygoff[YPC];
     int yloff[YPC];
 #pragma unroll
     for (int m = 0; m < YPC; ++m) {
         const int u = tid + m * NTC;
         const int r = u / YUR, col = (u % YUR) * 4;
-        ygoff[m] = (u < YU) ? (uint32_t)((r * xrow_el + col) * 4) : kOOB;
+        const int j = r >> log2R;
+        const bool keep = u < YU && (!ys || (j & 1));
+        const int yr = ys ? (((j >> 1) << log2R) | (r & ((1 << log2R) - 1))) : r;
+        ygoff[m] = keep ? (uint32_t)((yr * xrow_el + col) * 4) : kOOB;
         yloff[m] = (u < YU) ? r * LDY + col : F * LDY;
     }
     // global stores of the y block staged in sY[buf] by tile k; the first
@@ -2176,7 +2191,20 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
                           const void* C, const float* D, const float* init_state,
                           int64_t chunk_len, int64_t R, const float* theta, float* y,
                           float* final_state, const ssd_launch_opts* opts, void* stream) {
+    return ssd_detail::forward_impl(d, x, da, B, C, D, init_state, chunk_len, R, theta, y,
+                                    final_state, opts, stream, 0);
+}
+
+}  // extern "C"
+
+namespace ssd_detail {
+
+ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const void* B,
+                        const void* C, const float* D, const float* init_state, int64_t chunk_len,
+                        int64_t R, const float* theta, float* y, float* final_state,
+                        const ssd_launch_opts* opts, void* stream, int ysub) {
     if (!d || !x || !da || !B || !C || !y || !final_state) return SSD_ERR_NULL_ARG;
+    if (ysub && (d->seqlen % 2)) return SSD_ERR_BAD_SHAPE;
     ssd_status st = check_shape(d, chunk_len, R, theta != nullptr);
     if (st != SSD_OK) return st;
     if (opts) {
@@ -2193,7 +2221,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
     const int64_t b = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate,
                   G = d->ngroups;
     const int64_t esz = d->in_dtype == SSD_BF16 ? 2 : 4;
-    const Span sy = span_of(y, b * T * R * H * P * 4);
+    const Span sy = span_of(y, (ysub ? b * T / 2 : b * T) * R * H * P * 4);
     const Span sf = span_of(final_state, b * H * P * N * 4);
     const Span ins[] = {span_of(x, b * T * R * H * P * esz), span_of(da, b * T * H * 4),
                         span_of(B, b * T * R * G * N * esz), span_of(C, b * T * R * G * N * esz),
@@ -2239,6 +2267,7 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
         args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
         args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
         args.ws_state = ws_state; args.ws_misc = ws_misc;
+        args.ysub = ysub;
         rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
     } else {
         // without rotation K2 runs once per (batch, group, tile), shared by
@@ -2267,12 +2296,17 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
             args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
             args.theta = theta;
             args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
+            args.ysub = ysub;
             rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
         }
     }
     if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
 }
+
+}  // namespace ssd_detail
+
+extern "C" {
 
 ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* da, const void* B,
                        const void* C, const float* D, const float* init_state, int64_t chunk_len,

@@ -10,10 +10,10 @@
 //   2t    : decay exp(da_t), no rotation, write beta_t x_{t-1} (outer) B_{t-1}
 //   2t+1  : no decay, rotation theta_t, write gamma_t x_t (outer) B_t, read C_t
 // which gives h_{2t+1} = R(theta_t)(exp(da_t) h + beta_t W_{t-1}) + gamma_t W_t,
-// exactly the step above. So the trapezoid runs as ssd_forward_ex on a
+// exactly the step above. So the trapezoid runs as the single-write scan on a
 // sequence of 2T sub-steps: B and C stay per group, the rotation and the
 // chunked kernels are the SSD path's own. This file builds the sub-step
-// inputs, calls the scan, and keeps the odd sub-steps' y.
+// inputs and calls the scan, which stores only the odd sub-steps' y.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -115,15 +115,6 @@ __global__ __launch_bounds__(256) void trap_expand_rows(ExpandArgs a) {
     }
 }
 
-// y_t = y^_{2t+1}: one workgroup per (batch, step) row of R*H*P floats
-__global__ __launch_bounds__(256) void trap_gather_y(const float4* yh, float4* y, int64_t T, int64_t row4) {
-    const int64_t bt = blockIdx.x;
-    const int64_t bb = bt / T, t = bt - bb * T;
-    const float4* src = yh + (bb * 2 * T + 2 * t + 1) * row4;
-    float4* dst = y + bt * row4;
-    for (int64_t j = threadIdx.x; j < row4; j += blockDim.x) dst[j] = src[j];
-}
-
 }  // namespace
 
 extern "C" {
@@ -176,15 +167,14 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
         overlap(sf, span_of(init_state, b * H * P * N * 4)))
         return SSD_ERR_ALIAS;
 
-    // sub-step inputs and the sub-step y in the expansion slot
+    // sub-step inputs in the expansion slot
     const size_t nx = align256((size_t)(b * 2 * T * R * H * P) * esz);
     const size_t nbc = align256((size_t)(b * 2 * T * R * G * N) * esz);
     const size_t nda = align256((size_t)(b * 2 * T * H) * 4);
     const size_t nth = theta ? align256((size_t)(b * 2 * T * H * (N / 2)) * 4) : 0;
-    const size_t ny = align256((size_t)(b * 2 * T * R * H * P) * 4);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     int entry = -1;
-    char* ws = static_cast<char*>(scratch_acquire(hs, nx + 2 * nbc + nda + nth + ny, &entry, kSlotExpand));
+    char* ws = static_cast<char*>(scratch_acquire(hs, nx + 2 * nbc + nda + nth, &entry, kSlotExpand));
     if (!ws) return SSD_ERR_HIP;
     ExpandArgs a;
     memset(&a, 0, sizeof(a));
@@ -195,7 +185,6 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
     a.Ch = ws + nx + nbc;
     a.dah = reinterpret_cast<float*>(ws + nx + 2 * nbc);
     a.thh = theta ? reinterpret_cast<float*>(ws + nx + 2 * nbc + nda) : nullptr;
-    float* yh = reinterpret_cast<float*>(ws + nx + 2 * nbc + nda + nth);
     a.b = b; a.T = T; a.R = R; a.H = H; a.P = P; a.G = G; a.N = N;
 
     ssd_status rs = SSD_OK;
@@ -203,14 +192,8 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
     hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(b * T)), dim3(256), 0, hs, a);
     if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
     if (rs == SSD_OK)
-        rs = ssd_forward_ex(&d2, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, chunk_len, R, a.thh, yh,
-                            final_state, opts, stream);
-    if (rs == SSD_OK) {
-        const int64_t row4 = R * H * P / 4;
-        hipLaunchKernelGGL(trap_gather_y, dim3((unsigned)(b * T)), dim3(256), 0, hs,
-                           reinterpret_cast<const float4*>(yh), reinterpret_cast<float4*>(y), T, row4);
-        if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
-    }
+        rs = forward_impl(&d2, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, chunk_len, R, a.thh, y,
+                          final_state, opts, stream, 1);
     if (!scratch_release(entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
 }

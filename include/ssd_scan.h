@@ -214,11 +214,12 @@ ssd_status ssd_selective_scan_ex(const float *u, const float *delta, const float
  *   prev_B       [b, R, G, N] in_dtype, 16-byte aligned; NULL exactly when
  *                prev_x is (SSD_ERR_NULL_ARG otherwise)
  *   batch * seqlen must stay below 2^31 (SSD_ERR_UNSUPPORTED)
- * Runs as the single-write scan over 2T sub-steps (decay then turn), so the
- * envelope is ssd_forward's at seqlen 2T; opts apply to that scan (walk
- * events bracket its output walk). Scratch: the sub-step inputs and outputs
- * (about 2x x, B, C, da, theta and 2x y in bytes) in a second per-(device,
- * stream) buffer of the library, besides ssd_forward's own.
+ * Runs as the single-write scan over 2T sub-steps (decay then turn), which
+ * writes y for the odd sub-steps only, so the envelope is ssd_forward's at
+ * seqlen 2T; opts apply to that scan (walk events bracket its output walk).
+ * Scratch: the sub-step inputs (about 2x x, B, C, da and theta in bytes) in
+ * a second per-(device, stream) buffer of the library, besides
+ * ssd_forward's own.
  */
 ssd_status ssd_trapezoid_forward(const ssd_dims *d, const void *x, const float *da,
                                  const void *B, const void *C, const float *beta,
