@@ -1044,7 +1044,8 @@ constexpr int cols_lds_bytes(int mode) {
 // four, one per SIMD, each turning one 16-row block of B or C.
 constexpr int cols_mem_waves(int W, bool rot) { return rot ? 4 : (W >= 4 ? 2 : 1); }
 
-template <typename TI, int NP, int W, int MODE, bool ROT>
+// YS (output pass only): y keeps only the odd time steps (TileArgs::ysub).
+template <typename TI, int NP, int W, int MODE, bool ROT, bool YS = false>
 __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_kernel(TileArgs a) {
     using O = Ops<TI>;
     typedef typename O::frag frag;
@@ -1489,7 +1490,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     // with ysub, y holds only the odd steps (a tile starts at an even step,
     // 32 / R being even): local row r = j R + k of an odd step j goes to
     // compact row (j >> 1) R + k, half a tile of rows per tile
-    const int ys = a.ysub ? 1 : 0;
+    constexpr int ys = YS ? 1 : 0;
     const auto rs_y = make_rsrc(a.y + (b * (TR >> ys) + (row0 >> ys)) * xrow_el + col0,
                                 (uint32_t)((((vrows >> ys) - 1) * xrow_el + CW) * 4));
     const uint32_t ystep = (uint32_t)((F >> ys) * xrow_el * 4);
@@ -1841,56 +1842,65 @@ constexpr int kLdsLimit = 160 * 1024;
 // Column-block widths (16-column slices per workgroup), preferred first.
 constexpr int kColsWidths[] = {10, 8, 6, 4, 2, 1};
 
-template <typename TI, int NP, int W, int MODE, bool ROT>
+template <typename TI, int NP, int W, int MODE, bool ROT, bool YS = false>
 void* cols_ptr() {
     if constexpr (cols_lds_bytes<TI, NP, W, ROT>(MODE) <= kLdsLimit)
-        return reinterpret_cast<void*>(&ssd_cols_kernel<TI, NP, W, MODE, ROT>);
+        return reinterpret_cast<void*>(&ssd_cols_kernel<TI, NP, W, MODE, ROT, YS>);
     else
         return nullptr;  // does not fit one CU's LDS
 }
 
-template <typename TI, int W, int MODE, bool ROT>
+template <typename TI, int W, int MODE, bool ROT, bool YS = false>
 void* cols_ptr_np(int NP) {
     switch (NP) {
-        case 32: return cols_ptr<TI, 32, W, MODE, ROT>();
-        case 64: return cols_ptr<TI, 64, W, MODE, ROT>();
-        case 128: return cols_ptr<TI, 128, W, MODE, ROT>();
-        case 256: return cols_ptr<TI, 256, W, MODE, ROT>();
+        case 32: return cols_ptr<TI, 32, W, MODE, ROT, YS>();
+        case 64: return cols_ptr<TI, 64, W, MODE, ROT, YS>();
+        case 128: return cols_ptr<TI, 128, W, MODE, ROT, YS>();
+        case 256: return cols_ptr<TI, 256, W, MODE, ROT, YS>();
     }
     return nullptr;
 }
 
-template <typename TI, int MODE>
+template <typename TI, int MODE, bool YS = false>
 void* cols_ptr_w(int w, int NP) {
     switch (w) {
-        case 1: return cols_ptr_np<TI, 1, MODE, false>(NP);
-        case 2: return cols_ptr_np<TI, 2, MODE, false>(NP);
-        case 4: return cols_ptr_np<TI, 4, MODE, false>(NP);
-        case 6: return cols_ptr_np<TI, 6, MODE, false>(NP);
-        case 8: return cols_ptr_np<TI, 8, MODE, false>(NP);
-        case 10: return cols_ptr_np<TI, 10, MODE, false>(NP);
+        case 1: return cols_ptr_np<TI, 1, MODE, false, YS>(NP);
+        case 2: return cols_ptr_np<TI, 2, MODE, false, YS>(NP);
+        case 4: return cols_ptr_np<TI, 4, MODE, false, YS>(NP);
+        case 6: return cols_ptr_np<TI, 6, MODE, false, YS>(NP);
+        case 8: return cols_ptr_np<TI, 8, MODE, false, YS>(NP);
+        case 10: return cols_ptr_np<TI, 10, MODE, false, YS>(NP);
     }
     return nullptr;
 }
 
-void* select_cols(int dtype, int mode, int w, int NP) {
-    if (dtype == SSD_BF16) return mode ? cols_ptr_w<uint16_t, 1>(w, NP) : cols_ptr_w<uint16_t, 0>(w, NP);
-    return mode ? cols_ptr_w<float, 1>(w, NP) : cols_ptr_w<float, 0>(w, NP);
+// ysub selects the output-pass instantiations that keep only odd steps of y
+void* select_cols(int dtype, int mode, int w, int NP, bool ysub = false) {
+    if (dtype == SSD_BF16) {
+        if (mode) return cols_ptr_w<uint16_t, 1>(w, NP);
+        return ysub ? cols_ptr_w<uint16_t, 0, true>(w, NP) : cols_ptr_w<uint16_t, 0>(w, NP);
+    }
+    if (mode) return cols_ptr_w<float, 1>(w, NP);
+    return ysub ? cols_ptr_w<float, 0, true>(w, NP) : cols_ptr_w<float, 0>(w, NP);
 }
 
 // Rotating column walk: bf16 only, one head (headdim 64 or 128) per block,
 // dstate 64 or 128 (one table lane per state pair).
-void* select_cols_rot(int dtype, int mode, int w, int NP) {
+void* select_cols_rot(int dtype, int mode, int w, int NP, bool ysub = false) {
     if (dtype != SSD_BF16) return nullptr;
     if (w == 4) {
         switch (NP) {
-            case 64: return mode ? cols_ptr<uint16_t, 64, 4, 1, true>() : cols_ptr<uint16_t, 64, 4, 0, true>();
-            case 128: return mode ? cols_ptr<uint16_t, 128, 4, 1, true>() : cols_ptr<uint16_t, 128, 4, 0, true>();
+            case 64: return mode ? cols_ptr<uint16_t, 64, 4, 1, true>()
+                                 : ysub ? cols_ptr<uint16_t, 64, 4, 0, true, true>() : cols_ptr<uint16_t, 64, 4, 0, true>();
+            case 128: return mode ? cols_ptr<uint16_t, 128, 4, 1, true>()
+                                  : ysub ? cols_ptr<uint16_t, 128, 4, 0, true, true>() : cols_ptr<uint16_t, 128, 4, 0, true>();
         }
     } else if (w == 8) {
         switch (NP) {
-            case 64: return mode ? cols_ptr<uint16_t, 64, 8, 1, true>() : cols_ptr<uint16_t, 64, 8, 0, true>();
-            case 128: return mode ? cols_ptr<uint16_t, 128, 8, 1, true>() : cols_ptr<uint16_t, 128, 8, 0, true>();
+            case 64: return mode ? cols_ptr<uint16_t, 64, 8, 1, true>()
+                                 : ysub ? cols_ptr<uint16_t, 64, 8, 0, true, true>() : cols_ptr<uint16_t, 64, 8, 0, true>();
+            case 128: return mode ? cols_ptr<uint16_t, 128, 8, 1, true>()
+                                  : ysub ? cols_ptr<uint16_t, 128, 8, 0, true, true>() : cols_ptr<uint16_t, 128, 8, 0, true>();
         }
     }
     return nullptr;
@@ -2106,7 +2116,9 @@ ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hip
     int64_t nwg = pl.b * pl.H * args.seg_items;
     unsigned threads = (unsigned)(4 * pl.P);
     if (pl.kind == kColsPath) {
-        fn = rot ? select_cols_rot(pl.dtype, mode, pl.W, (int)pl.NP) : select_cols(pl.dtype, mode, pl.W, (int)pl.NP);
+        const bool ysub = args.ysub != 0;
+        fn = rot ? select_cols_rot(pl.dtype, mode, pl.W, (int)pl.NP, ysub)
+                 : select_cols(pl.dtype, mode, pl.W, (int)pl.NP, ysub);
         nwg = pl.b * args.seg_items * pl.H * (pl.P / 16) / pl.W;
         threads = (unsigned)(64 * (pl.W + cols_mem_waves(pl.W, rot)));
     } else {
