@@ -147,21 +147,46 @@ __global__ __launch_bounds__(64) void sel_scan_kernel(SelArgs a) {
         // into h = 1 * h + 0, so only the store of y needs the row bound
         const int64_t tb = t0 + (int64_t)blk * TB;
         const int rows = (int)(t1 - tb < TB ? t1 - tb : TB);
+        // up to 32 states the B (and C) row of step s + 1 is read from LDS
+        // while step s is computed; at 64 the extra registers cost more
+        // occupancy than the overlap gains
+        constexpr bool kAhead = NN <= 32;
+        const float4* B4 = sBC4[blk & 1][0];
+        const float4* C4 = sBC4[blk & 1][1];
+        float4 nb[NN / 4], nc[NN / 4];
+        if constexpr (kAhead) {
+#pragma unroll
+            for (int q = 0; q < NN / 4; ++q) {
+                nb[q] = B4[q];
+                nc[q] = MODE == 0 ? C4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < TB; ++s) {
             const float dl = cd[s], uu = cu[s], su = dl * uu;
-            const float4* B4 = sBC4[blk & 1][0] + s * (NN / 4);
-            const float4* C4 = sBC4[blk & 1][1] + s * (NN / 4);
+            float4 cb[NN / 4], cc[NN / 4];
+            if constexpr (kAhead) {
+#pragma unroll
+                for (int q = 0; q < NN / 4; ++q) {
+                    cb[q] = nb[q];
+                    cc[q] = nc[q];
+                }
+                if (s + 1 < TB) {
+#pragma unroll
+                    for (int q = 0; q < NN / 4; ++q) {
+                        nb[q] = B4[(s + 1) * (NN / 4) + q];
+                        if (MODE == 0) nc[q] = C4[(s + 1) * (NN / 4) + q];
+                    }
+                }
+            }
             float acc0 = sk * uu, acc1 = 0.f;
 #pragma unroll
             for (int q = 0; q < NN / 4; ++q) {
-                const float4 bq = B4[q];
+                // without the read-ahead each 16-byte read sits next to its use
+                const float4 bq = kAhead ? cb[q] : B4[s * (NN / 4) + q];
+                const float4 cq = kAhead ? cc[q] : (MODE == 0 ? C4[s * (NN / 4) + q] : make_float4(0.f, 0.f, 0.f, 0.f));
                 const float bv[4] = {bq.x, bq.y, bq.z, bq.w};
-                float cv[4] = {0.f, 0.f, 0.f, 0.f};
-                if (MODE == 0) {
-                    const float4 cq = C4[q];
-                    cv[0] = cq.x; cv[1] = cq.y; cv[2] = cq.z; cv[3] = cq.w;
-                }
+                const float cv[4] = {cq.x, cq.y, cq.z, cq.w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int n = 4 * q + i;
