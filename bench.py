@@ -331,8 +331,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the scan shards over (batch, head) without communication; see DESIGN.md)",
+        print("bench.py measures one GPU: there is no multi-GPU path "
+              "(the scan shards over (batch, head) without communication)",
               file=sys.stderr)
         return 2
 
