@@ -138,3 +138,24 @@ def test_trapezoid_final_state_in_place():
     torch.cuda.synchronize()
     assert f2.data_ptr() == h.data_ptr()
     assert torch.equal(y2, y) and torch.equal(f2, f)
+
+
+@pytest.mark.parametrize("segments", [1, 3])
+def test_trapezoid_launch_options(segments):
+    # explicit segment counts for the scan over the 2T sub-steps, and walk
+    # events around its output walk, leave the result within the bar
+    shape = si.small_shape(seqlen=400, headdim=64, dstate=128, mimo_rank=4, nheads=2,
+                           dtype="bf16", rotation=True, init_state=True, skip="none")
+    ti = si.make_trapezoid_inputs(shape, seed=12)
+    ev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    call = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    _dev()
+    call[0].record()
+    y, f = run(ti, segments=segments, walk_events=ev)
+    call[1].record()
+    torch.cuda.synchronize()
+    assert 0.0 < ev[0].elapsed_time(ev[1]) <= call[0].elapsed_time(call[1])
+    yr, fr = ref(ti)
+    ey, ef = normwise(y.cpu().numpy(), yr), normwise(f.cpu().numpy(), fr)
+    print(f"segments {segments}: y err {ey:.3e} final err {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (segments, ey, ef)
