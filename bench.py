@@ -48,17 +48,26 @@ def algorithmic_bytes(s) -> int:
     return n
 
 
-def algorithmic_flops(s) -> int:
-    """Causal (block-)lower-triangular K2 + K3 + K5 flops at the given chunk length."""
-    b, T, H, P, N, G, R, l = (s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
-                              s.mimo_rank, s.chunk_len)
-    nc = -(-T // l)
-    L = l * R
-    tri = L * (L + 1) // 2
+KERNEL_TILE_ROWS = 32            # fused rows (t, r) per tile the walks run, for any chunk_len
+
+
+def algorithmic_flops(s, tile_rows: int = KERNEL_TILE_ROWS) -> int:
+    """Causal (block-)lower-triangular K2 + K3 + K5 flops at the tile the kernels walk.
+
+    The walks run 32-row tiles of fused (step, rank) rows whatever chunk_len is
+    (the chunked form is exact for any chunk length), so the intra-tile terms,
+    K2 and the K5 diagonal block, are counted at that tile: per tile the
+    (row, column) pairs with step(row) >= step(column).
+    """
+    b, T, H, P, N, G, R = (s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
+                           s.mimo_rank)
+    ntiles = -(-(T * R) // tile_rows)
+    q = tile_rows // R                       # steps per tile
+    pairs = R * R * q * (q + 1) // 2         # causal (row, column) pairs per tile
     k3 = 2 * b * H * T * R * P * N
     k5_off = 2 * b * H * T * R * P * N
-    k5_diag = 2 * b * H * nc * tri * P
-    k2 = 2 * b * nc * tri * N * (H if s.rotation else G)
+    k5_diag = 2 * b * H * ntiles * pairs * P
+    k2 = 2 * b * ntiles * pairs * N * (H if s.rotation else G)
     return k3 + k5_off + k5_diag + k2
 
 
@@ -96,37 +105,90 @@ def profiled_traffic(workload_tag: str, workload: str = "ssd"):
     return int(d["hbm_bytes_per_launch"])
 
 
-def time_walk(step, steps: int) -> float:
-    """Mean duration (ms) of the output walk kernel over `steps` calls.
-
-    Each call gets its own pair of HIP events, created without the system-scope
-    fence (a timing-only event: no cache writeback between the two kernels of
-    a call), which the library records just before and after the walk launch.
-    """
+def _hip():
     import ctypes
-    hip = ctypes.CDLL("libamdhip64.so")
-    no_fence = 0x20000000                      # hipEventDisableSystemFence
+    return ctypes.CDLL("libamdhip64.so")
 
-    def event():
-        e = ctypes.c_void_p()
-        if hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(no_fence)) != 0:
-            raise RuntimeError("hipEventCreateWithFlags failed")
-        return e.value
 
-    pairs = [(event(), event()) for _ in range(steps)]
-    for pr in pairs:
-        step(walk_events=pr)
+def _timing_event(hip):
+    """A HIP event created without the system-scope fence (timing only: no
+    cache writeback between the kernels of a call)."""
+    import ctypes
+    e = ctypes.c_void_p()
+    if hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(0x20000000)) != 0:
+        raise RuntimeError("hipEventCreateWithFlags failed")
+    return e.value
+
+
+def _elapsed_ms(hip, a, b) -> float:
+    import ctypes
+    ms = ctypes.c_float()
+    if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+        raise RuntimeError("hipEventElapsedTime failed")
+    return float(ms.value)
+
+
+def prewarm(step, seconds: float) -> int:
+    """Run whole calls back to back for at least ``seconds`` of wall time, so
+    that the shader clock has left its idle state before anything is timed.
+    Returns the number of calls."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def time_calls(step, calls: int, flush_bytes: int) -> dict:
+    """Per-call HIP event timing of the whole call and of its output walk.
+
+    Before each call a plain fill overwrites ``flush_bytes`` of device memory
+    (outside both event pairs), so that no call finds its inputs in the L2 or
+    the MALL left there by the previous one. The call is bracketed by one pair
+    of events on the launch stream, and the library records a second pair just
+    before and after the output walk. Returns the median and min of each.
+    """
+    import statistics
+    import torch
+    hip = _hip()
+    flush = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = [(_timing_event(hip), _timing_event(hip), _timing_event(hip), _timing_event(hip))
+          for _ in range(calls)]
+    vp = __import__("ctypes").c_void_p
+    for i, (c0, c1, w0, w1) in enumerate(ev):
+        flush.fill_(float(i))
+        if hip.hipEventRecord(vp(c0), vp(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+        step(walk_events=(w0, w1))
+        if hip.hipEventRecord(vp(c1), vp(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
     if hip.hipDeviceSynchronize() != 0:
         raise RuntimeError("hipDeviceSynchronize failed")
-    total = 0.0
-    for a, b in pairs:
-        ms = ctypes.c_float()
-        if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
-            raise RuntimeError("hipEventElapsedTime failed")
-        total += ms.value
-        hip.hipEventDestroy(ctypes.c_void_p(a))
-        hip.hipEventDestroy(ctypes.c_void_p(b))
-    return total / steps
+    call = [_elapsed_ms(hip, c0, c1) for c0, c1, _, _ in ev]
+    walk = [_elapsed_ms(hip, w0, w1) for _, _, w0, w1 in ev]
+    for e in ev:
+        for h in e:
+            hip.hipEventDestroy(vp(h))
+    del flush
+    return {"call_ms_median": statistics.median(call), "call_ms_min": min(call),
+            "walk_ms_median": statistics.median(walk), "walk_ms_min": min(walk),
+            "calls": calls, "flush_bytes": flush_bytes}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, shape, nslices: int):
@@ -143,6 +205,7 @@ def cpu_baseline(inp, shape, nslices: int):
         "unit": "tokens/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": (f"{nslices} of the {nbh} (batch, head) slices over the full T={shape.seqlen}; "
                    f"{secs:.2f} s wall; tokens/s scaled by the slice fraction"),
     }
@@ -165,19 +228,10 @@ def selective_bench(args) -> dict:
         ssd.selective_scan(g.u, g.delta, g.A, g.B, g.C, g.skip, y=y, stream=stream.cuda_stream,
                            chunks=args.segments, walk_events=walk_events)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    call_ms = start.elapsed_time(end) / args.steps
-    out_ms = time_walk(step, args.steps)
+    nwarm = prewarm(step, args.prewarm)
+    wall = timed_region(step, args)
+    tc = time_calls(step, args.calls, FLUSH_BYTES)
+    call_ms, out_ms = tc["call_ms_median"], tc["walk_ms_median"]
     if not torch.isfinite(y).all():
         raise RuntimeError("non-finite output")
     b, T, D, N = shape.batch, shape.seqlen, shape.d_model, shape.d_state
@@ -217,7 +271,7 @@ def selective_bench(args) -> dict:
             oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip, nthreads=threads)
         secs = (time.perf_counter() - t1) / reps
         out["cpu_baseline"] = {"value": b * T / secs, "unit": "tokens/s", "cores": threads,
-                               "kind": "oracle",
+                               "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"the whole workload, {reps} runs, {secs:.3f} s each"}
     return out
 
@@ -245,19 +299,10 @@ def trapezoid_bench(args) -> dict:
                       shape.chunk_len, bi.theta, y=y, final_state=fin, segments=args.segments,
                       stream=stream.cuda_stream, walk_events=walk_events)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    call_ms = start.elapsed_time(end) / args.steps
-    walk_ms = time_walk(step, args.steps)
+    nwarm = prewarm(step, args.prewarm)
+    wall = timed_region(step, args)
+    tc = time_calls(step, args.calls, FLUSH_BYTES)
+    call_ms, walk_ms = tc["call_ms_median"], tc["walk_ms_median"]
     if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite output")
     # the dominant kernel is the rotating walk over 2T sub-steps: its own
@@ -304,11 +349,76 @@ def trapezoid_bench(args) -> dict:
                          ti.prev_B, ti.base.init_state, ti.base.theta, bh=sel, nthreads=threads)
         secs = time.perf_counter() - t1
         out["cpu_baseline"] = {"value": b * T * (nsl / nbh) / secs, "unit": "tokens/s",
-                               "cores": threads, "kind": "oracle",
+                               "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": (f"{nsl} of the {nbh} (batch, head) slices over the full "
                                           f"T={T}; {secs:.2f} s wall; tokens/s scaled by the "
                                           f"slice fraction")}
     return out
+
+
+FLUSH_BYTES = 1 << 30           # overwritten before each per-call timing: beyond L2 and MALL
+
+
+def timed_region(step, args) -> float:
+    """The contract's timed loop: W warm-up steps, then exactly K steps
+    bracketed by device synchronisation. Returns the wall time of the K steps."""
+    import torch
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def ssd_step_fn(ssd, g, shape, y, fin, stream, segments=0, block_slices=0):
+    def step(walk_events=None):
+        ssd.forward(g.x, g.da, g.B, g.C, g.D, g.init_state, shape.chunk_len, g.theta,
+                    y=y, final_state=fin, segments=segments, block_slices=block_slices,
+                    stream=stream, walk_events=walk_events)
+    return step
+
+
+def ssd_workload(cfg: int, args, with_timed_region: bool):
+    """Inputs of workload ``cfg`` resident in HBM, pre-warm, then the flushed
+    per-call timing (and the contract's timed loop when asked)."""
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    shape = si.CONFIGS[cfg]
+    dev = torch.device("cuda:0")
+    inp = si.make_inputs(shape, seed=0)
+    g = inp.to(dev)
+    b, T, R, H, P = g.x.shape
+    y = torch.empty(g.x.shape, device=dev, dtype=torch.float32)
+    fin = torch.empty((b, H, P, shape.dstate), device=dev, dtype=torch.float32)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    step = ssd_step_fn(ssd, g, shape, y, fin, stream, args.segments, args.block_slices)
+    nwarm = prewarm(step, args.prewarm)
+    wall = timed_region(step, args) if with_timed_region else None
+    tc = time_calls(step, args.calls, FLUSH_BYTES)
+    if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
+        raise RuntimeError(f"workload {cfg}: non-finite output")
+    nbytes = algorithmic_bytes(shape)
+    flops = algorithmic_flops(shape)
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    gbs = lambda ms: nbytes / (ms * 1e-3) / 1e9
+    summary = {
+        "workload": shape.name, "tokens": shape.tokens,
+        "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+        "walk_ms_median": tc["walk_ms_median"], "walk_ms_min": tc["walk_ms_min"],
+        "forward_ms_median": tc["call_ms_median"], "forward_ms_min": tc["call_ms_min"],
+        "walk_hbm_frac": gbs(tc["walk_ms_median"]) / HBM_PEAK_GBS,
+        "forward_hbm_frac": gbs(tc["call_ms_median"]) / HBM_PEAK_GBS,
+        "forward_tokens_per_s": shape.tokens / (tc["call_ms_median"] * 1e-3),
+        "mfma_frac_walk": flops / (tc["walk_ms_median"] * 1e-3) / 1e12 / mfma_peak,
+        "traffic": profiled_traffic(f"cfg{cfg}"),
+        "prewarm_calls": nwarm,
+    }
+    return shape, inp, wall, tc, summary
 
 
 def main() -> int:
@@ -316,8 +426,16 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--prewarm", type=float, default=2.0, metavar="SECONDS",
+                    help="whole calls run back to back for this long before anything is timed, "
+                         "whatever --warmup is (the shader clock ramps up from idle)")
+    ap.add_argument("--calls", type=int, default=40,
+                    help="per-call event timings (each after a 1 GiB flush) for median and min")
     ap.add_argument("--config", type=int, default=2,
                     help="workload id in ssd_inputs.CONFIGS (the reported line uses 2)")
+    ap.add_argument("--other-workloads", default="1,3,4",
+                    help="further workload ids timed the same way and reported under "
+                         "'workloads' (empty: none)")
     ap.add_argument("--cpu-slices", type=int, default=320)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
@@ -338,7 +456,6 @@ def main() -> int:
 
     import torch
     import chunked_ssd_scan_amd as ssd
-    import ssd_inputs as si
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -359,51 +476,27 @@ def main() -> int:
     if args.workload == "trapezoid":
         print(json.dumps(trapezoid_bench(args)), flush=True)
         return 0
-    shape = si.CONFIGS[args.config]
-    dev = torch.device("cuda:0")
-    inp = si.make_inputs(shape, seed=0)
-    g = inp.to(dev)
-    b, T, R, H, P = g.x.shape
-    y = torch.empty(g.x.shape, device=dev, dtype=torch.float32)
-    fin = torch.empty((b, H, P, shape.dstate), device=dev, dtype=torch.float32)
-    stream = torch.cuda.current_stream(dev)
 
-    def step(walk_events=None):
-        ssd.forward(g.x, g.da, g.B, g.C, g.D, g.init_state, shape.chunk_len, g.theta,
-                    y=y, final_state=fin, segments=args.segments,
-                    block_slices=args.block_slices, stream=stream.cuda_stream,
-                    walk_events=walk_events)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # one event pair on the launch stream around the whole timed region: the
-    # average forward (both kernels, back to back) without per-step markers
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    launch_ms = start.elapsed_time(end) / args.steps
-    # the dominant kernel alone: the library records a HIP event pair just
-    # before and after the output walk of each call (same number of calls)
-    walk_ms = time_walk(step, args.steps)
-    if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
-        print("non-finite output", file=sys.stderr)
-        return 1
+    shape, inp, wall, tc, main_summary = ssd_workload(args.config, args, with_timed_region=True)
+    print(f"# workload {args.config}: walk median {tc['walk_ms_median']:.4f} ms, call median "
+          f"{tc['call_ms_median']:.4f} ms", file=sys.stderr, flush=True)
+    others = {}
+    for w in [int(v) for v in args.other_workloads.split(",") if v.strip()]:
+        if w == args.config:
+            continue
+        _, _, _, otc, osum = ssd_workload(w, args, with_timed_region=False)
+        print(f"# workload {w}: walk median {otc['walk_ms_median']:.4f} ms, call median "
+              f"{otc['call_ms_median']:.4f} ms", file=sys.stderr, flush=True)
+        others[str(w)] = osum
+        torch.cuda.empty_cache()
 
     tokens = shape.batch * shape.seqlen
     ms_per_step = wall * 1e3 / args.steps
     nbytes = algorithmic_bytes(shape)
     flops = algorithmic_flops(shape)
+    walk_ms = tc["walk_ms_median"]
+    call_ms = tc["call_ms_median"]
     achieved = nbytes / (walk_ms * 1e-3) / 1e9
-    tag = f"cfg{args.config}"
-    traffic = profiled_traffic(tag)
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     out = {
         "metric": "SSD scan fwd tokens/s + % of HBM/MFMA roofline (b8,T8192,H80,P64,N128)",
@@ -421,18 +514,27 @@ def main() -> int:
         "config": {"workload": shape.name, "batch": shape.batch, "seqlen": shape.seqlen,
                    "nheads": shape.nheads, "headdim": shape.headdim, "dstate": shape.dstate,
                    "ngroups": shape.ngroups, "mimo_rank": shape.mimo_rank,
-                   "chunk_len": shape.chunk_len, "rotation": shape.rotation,
+                   "chunk_len": shape.chunk_len, "kernel_tile_rows": KERNEL_TILE_ROWS,
+                   "rotation": shape.rotation,
                    "segments": args.segments or "auto",
                    "block_slices": args.block_slices or "auto"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": main_summary["traffic"],
                      "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
-                     "forward_ms": launch_ms,
-                     "forward_frac": nbytes / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "kernel_ms_min": tc["walk_ms_min"],
+                     "forward_ms": call_ms, "forward_ms_min": tc["call_ms_min"],
+                     "forward_frac": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "mfma": {"algorithmic_tflop": flops / 1e12,
+                 "tile_rows": KERNEL_TILE_ROWS,
                  "achieved_tflops": flops / (walk_ms * 1e-3) / 1e12,
                  "peak_tflops": mfma_peak,
                  "frac": flops / (walk_ms * 1e-3) / 1e12 / mfma_peak},
+        "timing": {"prewarm_s": args.prewarm, "prewarm_calls": main_summary["prewarm_calls"],
+                   "per_call": f"{args.calls} calls, each after a {FLUSH_BYTES >> 20} MiB fill "
+                               "that evicts L2 and MALL; medians reported, min beside them",
+                   "timed_region": "the K steps back to back, wall clock between two device "
+                                   "synchronisations"},
+        "workloads": others,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, shape, args.cpu_slices)

@@ -161,6 +161,67 @@ def _event_handles(events, stream, dev):
     return handles
 
 
+def _check(name, t, shape, dtype, dev, optional=False):
+    """Raise unless ``t`` is a contiguous tensor of ``shape`` and ``dtype`` on ``dev``.
+
+    Shape and dtype are checked before the device, so that the checks can be
+    exercised on any device; nothing is launched.
+    """
+    import torch
+
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _in_dtype(x):
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        return SSD_BF16
+    if x.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
+
+
+def _need_device(x, what):
+    if x.device.type != "cuda":
+        raise ValueError(f"chunked_ssd_scan_amd.{what} needs device tensors (x is on {x.device})")
+
+
+def _ssd_sizes(x, B, prev_x=None, prev_B=None):
+    """(x5, B5, (b, T, R, H, P, G, N), prev_x, prev_B): rank-4 Mamba-2 layouts
+    get a rank axis of 1."""
+    if x.dim() not in (4, 5):
+        raise ValueError(f"x must be [b,T,H,P] or [b,T,R,H,P], got {tuple(x.shape)}")
+    if B.dim() != x.dim():
+        raise ValueError(f"B must have x's rank ({x.dim()}), got {tuple(B.shape)}")
+    if x.dim() == 4:
+        x5, B5 = x.unsqueeze(2), B.unsqueeze(2)
+        if prev_x is not None:
+            prev_x = prev_x.unsqueeze(1)
+        if prev_B is not None:
+            prev_B = prev_B.unsqueeze(1)
+    else:
+        x5, B5 = x, B
+    b, T, R, H, P = x5.shape
+    G, N = B5.shape[3], B5.shape[4]
+    if tuple(B5.shape[:3]) != (b, T, R):
+        raise ValueError(f"B has shape {tuple(B.shape)}, which does not match x {tuple(x.shape)}")
+    return (b, T, R, H, P, G, N), prev_x, prev_B
+
+
 def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=None,
             y=None, final_state=None, segments: int = 0, block_slices: int = 0,
             stream=None, walk_events=None) -> Tuple["torch.Tensor", "torch.Tensor"]:
@@ -176,34 +237,25 @@ def forward(x, da, B, C, D=None, init_state=None, chunk_len: int = 256, theta=No
     """
     import torch
 
-    if x.dim() == 4:
-        x5, B5, C5 = x.unsqueeze(2), B.unsqueeze(2), C.unsqueeze(2)
-    else:
-        x5, B5, C5 = x, B, C
-    b, T, R, H, P = x5.shape
-    G, N = B5.shape[3], B5.shape[4]
-    if x.device.type != "cuda":
-        raise ValueError("chunked_ssd_scan_amd.forward needs device tensors")
+    (b, T, R, H, P, G, N), _, _ = _ssd_sizes(x, B)
+    in_dtype = _in_dtype(x)
+    f32 = torch.float32
+    dev = None if x.device.type == "cpu" else x.device
+    _check("x", x, x.shape, x.dtype, dev)
+    _check("B", B, B.shape, x.dtype, dev)
+    _check("C", C, B.shape, x.dtype, dev)
+    _check("da", da, (b, T, H), f32, dev)
+    _check("D", D, (H,), f32, dev, optional=True)
+    _check("init_state", init_state, (b, H, P, N), f32, dev, optional=True)
+    _check("theta", theta, (b, T, H, N // 2), f32, dev, optional=True)
+    _check("y", y, x.shape, f32, dev, optional=True)
+    _check("final_state", final_state, (b, H, P, N), f32, dev, optional=True)
+    _need_device(x, "forward")
     dev = x.device
-    for name, t in (("x", x), ("da", da), ("B", B), ("C", C), ("D", D),
-                    ("init_state", init_state), ("theta", theta)):
-        if t is None:
-            continue
-        if t.device != dev:
+    for name, t in (("B", B), ("C", C), ("da", da), ("D", D), ("init_state", init_state),
+                    ("theta", theta), ("y", y), ("final_state", final_state)):
+        if t is not None and t.device != dev:
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if x.dtype == torch.bfloat16:
-        in_dtype = SSD_BF16
-    elif x.dtype == torch.float32:
-        in_dtype = SSD_F32
-    else:
-        raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
-    if B.dtype != x.dtype or C.dtype != x.dtype:
-        raise TypeError("x, B and C must share one dtype")
-    for name, t in (("da", da), ("D", D), ("init_state", init_state), ("theta", theta)):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
     if y is None:
         y = torch.empty(x.shape, device=dev, dtype=torch.float32)
     if final_state is None:
@@ -236,24 +288,25 @@ def selective_scan(u, delta, A, B, C, skip, y=None, stream=None, chunks: int = 0
     """
     import torch
 
-    if u.dim() != 3:
-        raise ValueError("u must be [batch, seq_len, d_model]")
+    if not isinstance(u, torch.Tensor) or u.dim() != 3:
+        raise ValueError("u must be a [batch, seq_len, d_model] tensor")
+    if not isinstance(A, torch.Tensor) or A.dim() != 2:
+        raise ValueError("A must be a [d_model, d_state] tensor")
     b, T, Dm = u.shape
     N = A.shape[-1]
-    if u.device.type != "cuda":
-        raise ValueError("chunked_ssd_scan_amd.selective_scan needs device tensors")
-    dev = u.device
+    f32 = torch.float32
+    dev = None if u.device.type == "cpu" else u.device
     want = {"u": (b, T, Dm), "delta": (b, T, Dm), "A": (Dm, N), "B": (b, T, N),
             "C": (b, T, N), "skip": (Dm,)}
     for name, t in (("u", u), ("delta", delta), ("A", A), ("B", B), ("C", C), ("skip", skip)):
-        if t.device != dev:
+        _check(name, t, want[name], f32, dev)
+    _check("y", y, (b, T, Dm), f32, dev, optional=True)
+    if u.device.type != "cuda":
+        raise ValueError("chunked_ssd_scan_amd.selective_scan needs device tensors")
+    dev = u.device
+    for name, t in (("delta", delta), ("A", A), ("B", B), ("C", C), ("skip", skip), ("y", y)):
+        if t is not None and t.device != dev:
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
-        if t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-        if tuple(t.shape) != want[name]:
-            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want[name]}")
     if y is None:
         y = torch.empty((b, T, Dm), device=dev, dtype=torch.float32)
     if stream is None:
@@ -282,39 +335,34 @@ def trapezoid(x, da, B, C, beta, gamma, prev_x=None, prev_B=None, init_state=Non
     """
     import torch
 
-    if x.dim() == 4:
-        x5, B5, C5 = x.unsqueeze(2), B.unsqueeze(2), C.unsqueeze(2)
-        if prev_x is not None:
-            prev_x, prev_B = prev_x.unsqueeze(1), prev_B.unsqueeze(1)
-    else:
-        x5, B5, C5 = x, B, C
-    b, T, R, H, P = x5.shape
-    G, N = B5.shape[3], B5.shape[4]
-    if x.device.type != "cuda":
-        raise ValueError("chunked_ssd_scan_amd.trapezoid needs device tensors")
+    if (prev_x is None) != (prev_B is None):
+        raise ValueError("prev_x and prev_B go together (both or neither)")
+    (b, T, R, H, P, G, N), px5, pB5 = _ssd_sizes(x, B, prev_x, prev_B)
+    in_dtype = _in_dtype(x)
+    f32 = torch.float32
+    dev = None if x.device.type == "cpu" else x.device
+    _check("x", x, x.shape, x.dtype, dev)
+    _check("B", B, B.shape, x.dtype, dev)
+    _check("C", C, B.shape, x.dtype, dev)
+    _check("da", da, (b, T, H), f32, dev)
+    _check("beta", beta, (b, T, H), f32, dev)
+    _check("gamma", gamma, (b, T, H), f32, dev)
+    if px5 is not None:
+        _check("prev_x", px5, (b, R, H, P), x.dtype, None)
+        _check("prev_B", pB5, (b, R, G, N), x.dtype, None)
+        _check("prev_x", prev_x, prev_x.shape, x.dtype, dev)
+        _check("prev_B", prev_B, prev_B.shape, x.dtype, dev)
+    _check("init_state", init_state, (b, H, P, N), f32, dev, optional=True)
+    _check("theta", theta, (b, T, H, N // 2), f32, dev, optional=True)
+    _check("y", y, x.shape, f32, dev, optional=True)
+    _check("final_state", final_state, (b, H, P, N), f32, dev, optional=True)
+    _need_device(x, "trapezoid")
     dev = x.device
-    for name, t in (("x", x), ("da", da), ("B", B), ("C", C), ("beta", beta), ("gamma", gamma),
+    for name, t in (("B", B), ("C", C), ("da", da), ("beta", beta), ("gamma", gamma),
                     ("prev_x", prev_x), ("prev_B", prev_B), ("init_state", init_state),
-                    ("theta", theta)):
-        if t is None:
-            continue
-        if t.device != dev:
+                    ("theta", theta), ("y", y), ("final_state", final_state)):
+        if t is not None and t.device != dev:
             raise ValueError(f"{name} is on {t.device}, expected {dev}")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if x.dtype == torch.bfloat16:
-        in_dtype = SSD_BF16
-    elif x.dtype == torch.float32:
-        in_dtype = SSD_F32
-    else:
-        raise TypeError(f"x must be bf16 or fp32, got {x.dtype}")
-    for name, t in (("B", B), ("C", C), ("prev_x", prev_x), ("prev_B", prev_B)):
-        if t is not None and t.dtype != x.dtype:
-            raise TypeError(f"{name} must have x's dtype")
-    for name, t in (("da", da), ("beta", beta), ("gamma", gamma), ("init_state", init_state),
-                    ("theta", theta)):
-        if t is not None and t.dtype != torch.float32:
-            raise TypeError(f"{name} must be float32")
     if y is None:
         y = torch.empty(x.shape, device=dev, dtype=torch.float32)
     if final_state is None:

@@ -62,6 +62,33 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const
                         int64_t R, const float* theta, float* y, float* final_state,
                         const ssd_launch_opts* opts, void* stream, int ysub);
 
+// ssd_forward_ex in two phases. forward_plan checks every argument and picks
+// the launch plan (host only: no HIP call but device queries); ws_bytes is the
+// workspace the launch needs. forward_launch enqueues the kernels with a
+// workspace of at least ws_bytes (may be null when ws_bytes is 0); it fails
+// only on a HIP error, possibly after part of the work was enqueued.
+struct Plan {
+    int64_t b, T, H, P, N, G, R, NP;
+    int dtype, S, nsub, Qt, log2R;
+    int SF;    // state-pass segments per output segment (the state pass divides finer)
+    int kind;  // kernel path: general walk or column-block walk
+    int W;     // column-block width in 16-column slices (column-block walk)
+};
+struct FwdPlan {
+    Plan pl;
+    bool rot, cols, shared;
+    size_t ws_bytes;
+    int ysub;
+};
+ssd_status forward_plan(const ssd_dims* d, const void* x, const float* da, const void* B,
+                        const void* C, const float* D, const float* init_state, int64_t chunk_len,
+                        int64_t R, const float* theta, float* y, float* final_state,
+                        const ssd_launch_opts* opts, int ysub, FwdPlan* out);
+ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, const void* B,
+                          const void* C, const float* D, const float* init_state, const float* theta,
+                          float* y, float* final_state, void* ws, void* const* walk_events,
+                          hipStream_t hs);
+
 }  // namespace ssd_detail
 
 #endif  // SSD_COMMON_H

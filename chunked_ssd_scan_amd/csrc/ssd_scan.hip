@@ -1928,14 +1928,6 @@ void* select_walk(int dtype, bool rot, int mode, int P, int NP) {
 
 enum PathKind { kWalkPath = 0, kColsPath = 1 };
 
-struct Plan {
-    int64_t b, T, H, P, N, G, R, NP;
-    int dtype, S, nsub, Qt, log2R;
-    int SF;    // state-pass segments per output segment (the state pass divides finer)
-    int kind;  // PathKind
-    int W;     // column-block width in 16-column slices (column-block walk)
-};
-
 bool is_pow2_in(int64_t v, int64_t lo, int64_t hi) {
     if (v < lo || v > hi) return false;
     return (v & (v - 1)) == 0;
@@ -2211,10 +2203,10 @@ ssd_status ssd_forward_ex(const ssd_dims* d, const void* x, const float* da, con
 
 namespace ssd_detail {
 
-ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const void* B,
+ssd_status forward_plan(const ssd_dims* d, const void* x, const float* da, const void* B,
                         const void* C, const float* D, const float* init_state, int64_t chunk_len,
                         int64_t R, const float* theta, float* y, float* final_state,
-                        const ssd_launch_opts* opts, void* stream, int ysub) {
+                        const ssd_launch_opts* opts, int ysub, FwdPlan* out) {
     if (!d || !x || !da || !B || !C || !y || !final_state) return SSD_ERR_NULL_ARG;
     if (ysub && (d->seqlen % 2)) return SSD_ERR_BAD_SHAPE;
     ssd_status st = check_shape(d, chunk_len, R, theta != nullptr);
@@ -2248,30 +2240,39 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const
         if (!same_state && overlap(sf, ins[i])) return SSD_ERR_ALIAS;
     }
 
-    const bool rot = theta != nullptr;
-    Plan pl;
-    st = make_plan(d, R, rot, opts ? opts->segments : 0, opts ? opts->block_slices : 0, &pl);
+    FwdPlan fp;
+    fp.rot = theta != nullptr;
+    st = make_plan(d, R, fp.rot, opts ? opts->segments : 0, opts ? opts->block_slices : 0, &fp.pl);
     if (st != SSD_OK) return st;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-
     // column-block walk (C B^T tile pack shared by the heads of a group unless
     // rotated), or the general walk for shapes it does not cover
-    const bool cols = pl.kind == kColsPath;
-    const bool shared = cols && !rot;
-    const WsLayout wl = workspace_layout(pl, !shared);
-    void* ws = nullptr;
-    int ws_entry = -1;
-    if (wl.total) {
-        ws = scratch_acquire(hs, wl.total, &ws_entry);
-        if (!ws) return SSD_ERR_HIP;
+    fp.cols = fp.pl.kind == kColsPath;
+    fp.shared = fp.cols && !fp.rot;
+    if (fp.shared) {
+        const void* pk = fp.pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)fp.pl.NP)
+                                                 : cb_pack_ptr<float>((int)fp.pl.NP);
+        if (!pk || fp.pl.b * fp.pl.G * fp.pl.nsub > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     }
+    fp.ws_bytes = workspace_layout(fp.pl, !fp.shared).total;
+    fp.ysub = ysub;
+    *out = fp;
+    return SSD_OK;
+}
+
+ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, const void* B,
+                          const void* C, const float* D, const float* init_state, const float* theta,
+                          float* y, float* final_state, void* ws, void* const* walk_events,
+                          hipStream_t hs) {
+    const Plan& pl = fp.pl;
+    const WsLayout wl = workspace_layout(pl, !fp.shared);
     char* wsc = static_cast<char*>(ws);
     float* ws_state = pl.S > 1 ? reinterpret_cast<float*>(wsc) : nullptr;
     float* ws_misc = pl.S > 1 ? reinterpret_cast<float*>(wsc + wl.state) : nullptr;
-    float* ws_pack = shared ? reinterpret_cast<float*>(wsc + wl.state + wl.misc) : nullptr;
+    float* ws_pack = fp.shared ? reinterpret_cast<float*>(wsc + wl.state + wl.misc) : nullptr;
+    const int64_t T = pl.T, H = pl.H, G = pl.G, N = pl.N, R = pl.R, P = pl.P;
 
     ssd_status rs = SSD_OK;
-    if (!cols) {
+    if (!fp.cols) {
         WalkArgs args;
         memset(&args, 0, sizeof(args));
         args.x = x; args.da = da; args.B = B; args.C = C; args.D = D;
@@ -2279,24 +2280,20 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const
         args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
         args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
         args.ws_state = ws_state; args.ws_misc = ws_misc;
-        args.ysub = ysub;
-        rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
+        args.ysub = fp.ysub;
+        rs = run_passes(pl, fp.rot, args, init_state, hs, walk_events);
     } else {
         // without rotation K2 runs once per (batch, group, tile), shared by
         // every head of the group; the rotating walk forms it per head
-        if (shared) {
+        if (fp.shared) {
             void* pk = pl.dtype == SSD_BF16 ? cb_pack_ptr<uint16_t>((int)pl.NP) : cb_pack_ptr<float>((int)pl.NP);
             const int64_t ntiles = pl.b * pl.G * pl.nsub;
-            if (!pk || ntiles > 0x7fffffff) {
-                rs = SSD_ERR_UNSUPPORTED;
-            } else {
-                const void* Bp = B;
-                const void* Cp = C;
-                int64_t TRv = T * R, Gv = G, Nv = N;
-                int nsub = pl.nsub, l2r = pl.log2R;
-                void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub, (void*)&l2r};
-                if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
-            }
+            const void* Bp = B;
+            const void* Cp = C;
+            int64_t TRv = T * R, Gv = G, Nv = N;
+            int nsub = pl.nsub, l2r = pl.log2R;
+            void* kargs[] = {(void*)&Bp, (void*)&Cp, (void*)&ws_pack, (void*)&TRv, (void*)&Gv, (void*)&Nv, (void*)&nsub, (void*)&l2r};
+            if (hipLaunchKernel(pk, dim3((unsigned)ntiles), dim3(64), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
         }
         if (rs == SSD_OK) {
             TileArgs args;
@@ -2308,10 +2305,30 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const
             args.ws_state = ws_state; args.ws_misc = ws_misc; args.cbpack = ws_pack;
             args.theta = theta;
             args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
-            args.ysub = ysub;
-            rs = run_passes(pl, rot, args, init_state, hs, opts ? opts->walk_events : nullptr);
+            args.ysub = fp.ysub;
+            rs = run_passes(pl, fp.rot, args, init_state, hs, walk_events);
         }
     }
+    return rs;
+}
+
+ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const void* B,
+                        const void* C, const float* D, const float* init_state, int64_t chunk_len,
+                        int64_t R, const float* theta, float* y, float* final_state,
+                        const ssd_launch_opts* opts, void* stream, int ysub) {
+    FwdPlan fp;
+    ssd_status st = forward_plan(d, x, da, B, C, D, init_state, chunk_len, R, theta, y, final_state,
+                                 opts, ysub, &fp);
+    if (st != SSD_OK) return st;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    void* ws = nullptr;
+    int ws_entry = -1;
+    if (fp.ws_bytes) {
+        ws = scratch_acquire(hs, fp.ws_bytes, &ws_entry);
+        if (!ws) return SSD_ERR_HIP;
+    }
+    ssd_status rs = forward_launch(fp, x, da, B, C, D, init_state, theta, y, final_state, ws,
+                                   opts ? opts->walk_events : nullptr, hs);
     if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
 }

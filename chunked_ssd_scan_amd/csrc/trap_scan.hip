@@ -186,14 +186,27 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
     a.dah = reinterpret_cast<float*>(ws + nx + 2 * nbc);
     a.thh = theta ? reinterpret_cast<float*>(ws + nx + 2 * nbc + nda) : nullptr;
     a.b = b; a.T = T; a.R = R; a.H = H; a.P = P; a.G = G; a.N = N;
-
-    ssd_status rs = SSD_OK;
     a.esz = (int)esz;
-    hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(b * T)), dim3(256), 0, hs, a);
-    if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+
+    // plan the scan over the 2T sub-steps (and take its scratch) before the
+    // expansion is enqueued, so that a rejected plan launches nothing
+    FwdPlan fp;
+    ssd_status rs = forward_plan(&d2, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, chunk_len, R,
+                                 a.thh, y, final_state, opts, 1, &fp);
+    void* fws = nullptr;
+    int fentry = -1;
+    if (rs == SSD_OK && fp.ws_bytes) {
+        fws = scratch_acquire(hs, fp.ws_bytes, &fentry);
+        if (!fws) rs = SSD_ERR_HIP;
+    }
+    if (rs == SSD_OK) {
+        hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(b * T)), dim3(256), 0, hs, a);
+        if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+    }
     if (rs == SSD_OK)
-        rs = forward_impl(&d2, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, chunk_len, R, a.thh, y,
-                          final_state, opts, stream, 1);
+        rs = forward_launch(fp, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, a.thh, y, final_state,
+                            fws, opts ? opts->walk_events : nullptr, hs);
+    if (fws && !scratch_release(fentry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     if (!scratch_release(entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
 }

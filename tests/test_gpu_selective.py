@@ -1,9 +1,9 @@
 """Diagonal selective scan on the GPU vs the float64 oracle (needs a gfx950 GPU).
 
 Bar: normwise max relative error ||y - ref||_inf / ||ref||_inf within 1e-4
-(fp32 inputs, fp32 arithmetic). At the full b4 T4096 D512 N16 size the oracle
-runs on sampled channels over the whole sequence, each held to the bar
-against its own norm.
+(fp32 inputs, fp32 arithmetic). At the full b4 T4096 D512 N16 size every
+(batch, channel) sequence is compared; each is also held to the bar against
+its own norm.
 """
 from __future__ import annotations
 
@@ -73,20 +73,18 @@ def test_shapes(b, T, D, N, shift):
     check(si.make_scan_inputs(shape, seed=b * 7 + T), shape.name)
 
 
-def test_full_size_sampled():
+def test_full_size_every_channel():
+    # b4 T4096 D512 N16: every one of the 2048 (batch, channel) sequences
     inp = si.make_scan_inputs(si.SCAN_CONFIGS[1], seed=0)
     b, T, Dm = inp.u.shape
-    y = run(inp).cpu()
-    rng = np.random.default_rng(1)
-    sel = sorted(set(rng.integers(0, b * Dm, 24).tolist()) | {0, Dm - 1, b * Dm - 1, 63, 64})
-    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip, bd=sel)
-    worst = 0.0
-    for i, bd in enumerate(sel):
-        bb, d = divmod(bd, Dm)
-        err = normwise(y[bb, :, d].double().numpy(), ref[i])
-        worst = max(worst, err)
-        assert err <= TOL, (bd, err)
-    print(f"full size: {len(sel)} channels, worst y err {worst:.3e}", flush=True)
+    y = run(inp).cpu().double().numpy()
+    ref = oracle.selective_scan(inp.u, inp.delta, inp.A, inp.B, inp.C, inp.skip)
+    err = normwise(y, ref)
+    per = np.abs(y - ref).max(axis=1) / np.maximum(np.abs(ref).max(axis=1), 1e-300)
+    print(f"full size: all {b * Dm} channels, tensor y err {err:.3e}, worst channel "
+          f"{float(per.max()):.3e}", flush=True)
+    assert err <= TOL
+    assert float(per.max()) <= TOL
 
 
 def test_deterministic_and_in_place():
