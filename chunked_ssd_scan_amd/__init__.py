@@ -7,7 +7,8 @@ a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
 
 C entry points, mirrored here under the same names:
   ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_selective_scan,
-  ssd_selective_scan_ex, ssd_trapezoid_forward, ssd_status_str
+  ssd_selective_scan_ex, ssd_trapezoid_forward, ssd_forward_noalloc,
+  ssd_status_str
 plus ``forward(...)``, ``selective_scan(...)`` and ``trapezoid(...)``,
 tensor-level conveniences over ssd_forward_ex, ssd_selective_scan_ex and
 ssd_trapezoid_forward.
@@ -28,9 +29,12 @@ SSD_ERR_BAD_SHAPE = 2
 SSD_ERR_UNSUPPORTED = 3
 SSD_ERR_ALIAS = 4
 SSD_ERR_HIP = 5
+SSD_ERR_WORKSPACE = 6
+SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
-            "ssd_selective_scan_ex", "ssd_trapezoid_forward", "ssd_status_str")
+            "ssd_selective_scan_ex", "ssd_trapezoid_forward", "ssd_forward_noalloc",
+            "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -69,6 +73,8 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_forward.restype = ctypes.c_int
         lib.ssd_forward_ex.argtypes = common + [ctypes.POINTER(SsdLaunchOpts), vp]
         lib.ssd_forward_ex.restype = ctypes.c_int
+        lib.ssd_forward_noalloc.argtypes = common + [ctypes.POINTER(SsdLaunchOpts), vp]
+        lib.ssd_forward_noalloc.restype = ctypes.c_int
         lib.ssd_workspace_bytes.argtypes = [ctypes.POINTER(SsdDims), i64, i64]
         lib.ssd_workspace_bytes.restype = ctypes.c_size_t
         lib.ssd_selective_scan.argtypes = [vp] * 7 + [i64] * 4 + [vp]
@@ -104,6 +110,15 @@ def ssd_forward_ex(dims: Optional[SsdDims], x, da, B, C, D, init_state, chunk_le
     return int(lib.ssd_forward_ex(None if dims is None else ctypes.byref(dims), x, da, B, C, D,
                                   init_state, int(chunk_len), int(R), theta, y, final_state,
                                   None if opts is None else ctypes.byref(opts), stream))
+
+
+def ssd_forward_noalloc(dims: Optional[SsdDims], x, da, B, C, D, init_state, chunk_len, R,
+                        theta, y, final_state, opts: Optional[SsdLaunchOpts], stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_forward_noalloc(None if dims is None else ctypes.byref(dims), x, da, B, C,
+                                       D, init_state, int(chunk_len), int(R), theta, y,
+                                       final_state, None if opts is None else ctypes.byref(opts),
+                                       stream))
 
 
 def ssd_workspace_bytes(dims: SsdDims, chunk_len: int, R: int) -> int:

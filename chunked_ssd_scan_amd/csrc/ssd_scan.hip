@@ -2176,6 +2176,7 @@ const char* ssd_status_str(int32_t status) {
         case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
         case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS";
         case SSD_ERR_HIP: return "SSD_ERR_HIP";
+        case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
     }
     return "unknown status";
 }
@@ -2346,3 +2347,52 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* da, const 
 
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// No-allocation entry point: the scratch is this fixed device array. Each GPU
+// that runs the library holds its own copy at its own address; host code uses
+// that address (looked up once per device), never the array's name.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_noalloc_mu;
+constexpr int kMaxDevices = 64;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch` (looked up on the first
+// call on each device); nullptr when the lookup fails.
+void* noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_noalloc_ptr[dev] = ptr;
+    }
+    return g_noalloc_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" ssd_status ssd_forward_noalloc(const ssd_dims* d, const void* x, const float* da,
+                                          const void* B, const void* C, const float* D,
+                                          const float* init_state, int64_t chunk_len, int64_t R,
+                                          const float* theta, float* y, float* final_state,
+                                          const ssd_launch_opts* opts, void* stream) {
+    ssd_detail::FwdPlan fp;
+    ssd_status st = ssd_detail::forward_plan(d, x, da, B, C, D, init_state, chunk_len, R, theta, y,
+                                             final_state, opts, 0, &fp);
+    if (st != SSD_OK) return st;
+    if (fp.ws_bytes > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (fp.ws_bytes) {
+        ws = noalloc_scratch();
+        if (!ws) return SSD_ERR_HIP;
+    }
+    return ssd_detail::forward_launch(fp, x, da, B, C, D, init_state, theta, y, final_state, ws,
+                                      opts ? opts->walk_events : nullptr,
+                                      reinterpret_cast<hipStream_t>(stream));
+}

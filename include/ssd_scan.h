@@ -91,7 +91,9 @@ typedef enum {
     SSD_ERR_BAD_SHAPE = 2,   /* T < 1, b/H/P/N/G < 1, H % G != 0, chunk_len < 1, R < 1, odd N with theta */
     SSD_ERR_UNSUPPORTED = 3, /* valid but outside the kernels' envelope, or a misaligned pointer */
     SSD_ERR_ALIAS = 4,       /* an output overlaps another buffer (final_state == init_state is allowed) */
-    SSD_ERR_HIP = 5          /* a HIP call or kernel launch failed */
+    SSD_ERR_HIP = 5,         /* a HIP call or kernel launch failed */
+    SSD_ERR_WORKSPACE = 6    /* ssd_forward_noalloc: the problem needs more scratch than
+                                SSD_NOALLOC_SCRATCH_BYTES */
 } ssd_status;
 
 /* Launch choices that do not change the result beyond rounding. */
@@ -227,6 +229,31 @@ ssd_status ssd_trapezoid_forward(const ssd_dims *d, const void *x, const float *
                                  const float *init_state, int64_t chunk_len, int64_t R,
                                  const float *theta, float *y, float *final_state,
                                  const ssd_launch_opts *opts, void *stream);
+
+/*
+ * ssd_forward_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
+ * Same arguments, result and launch plan as ssd_forward_ex (bitwise the same
+ * output), but the scratch (C B^T tile pack, segment states; the bytes
+ * ssd_workspace_bytes reports for the plan) lives in a fixed device array of
+ * SSD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends. The call makes no hipMalloc, hipFree or other
+ * allocating call; the first call on a device looks up that device's copy of
+ * the array once (hipGetSymbolAddress).
+ * Every call on one GPU shares that GPU's array and leaves the last call's
+ * contents in it: calls that may overlap on one GPU (different streams or
+ * host threads without ordering between them) race and must not be made.
+ * Calls ordered on one stream are safe.
+ * Errors: as ssd_forward_ex, plus SSD_ERR_WORKSPACE when the plan needs more
+ * than SSD_NOALLOC_SCRATCH_BYTES (nothing is launched); SSD_ERR_HIP when the
+ * array's address cannot be found.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+ssd_status ssd_forward_noalloc(const ssd_dims *d, const void *x, const float *da,
+                               const void *B, const void *C, const float *D,
+                               const float *init_state, int64_t chunk_len, int64_t R,
+                               const float *theta, float *y, float *final_state,
+                               const ssd_launch_opts *opts, void *stream);
 
 /* Static, NUL-terminated name of a status code ("unknown status" otherwise). */
 const char *ssd_status_str(int32_t status);

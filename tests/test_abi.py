@@ -40,7 +40,8 @@ def test_exports_every_declared_symbol(lib):
 
 def test_status_strings(lib):
     names = {0: "SSD_OK", 1: "SSD_ERR_NULL_ARG", 2: "SSD_ERR_BAD_SHAPE",
-             3: "SSD_ERR_UNSUPPORTED", 4: "SSD_ERR_ALIAS", 5: "SSD_ERR_HIP"}
+             3: "SSD_ERR_UNSUPPORTED", 4: "SSD_ERR_ALIAS", 5: "SSD_ERR_HIP",
+             6: "SSD_ERR_WORKSPACE"}
     for k, v in names.items():
         assert ssd.ssd_status_str(k) == v
     assert ssd.ssd_status_str(99) == "unknown status"
@@ -234,3 +235,20 @@ def test_trapezoid_alias(lib):
     opts = ssd.SsdLaunchOpts()
     opts.reserved[0] = 1
     assert trap_call(opts=opts) == ssd.SSD_ERR_BAD_SHAPE
+
+
+def test_noalloc_checks_before_anything(lib):
+    # the no-allocation entry point validates as ssd_forward_ex does and
+    # rejects a plan larger than its fixed scratch, all on the host
+    d = dims()
+    assert ssd.ssd_forward_noalloc(None, X, DA, BB, CC, DD, H0, 64, 1, None, Y, FS, None,
+                                   None) == ssd.SSD_ERR_NULL_ARG
+    assert ssd.ssd_forward_noalloc(d, X, DA, BB, CC, DD, H0, 0, 1, None, Y, FS, None,
+                                   None) == ssd.SSD_ERR_BAD_SHAPE
+    assert ssd.ssd_forward_noalloc(d, X, DA, BB, CC, DD, H0, 64, 1, None, X, FS, None,
+                                   None) == ssd.SSD_ERR_ALIAS
+    big = dims(batch=64, seqlen=65536)
+    assert ssd.ssd_workspace_bytes(big, 256, 1) > ssd.SSD_NOALLOC_SCRATCH_BYTES
+    far = [(i + 1) << 36 for i in range(6)]    # spans of this size do not overlap
+    assert ssd.ssd_forward_noalloc(big, far[0], far[1], far[2], far[3], None, None, 256, 1, None,
+                                   far[4], far[5], None, None) == ssd.SSD_ERR_WORKSPACE
