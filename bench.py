@@ -72,10 +72,12 @@ def algorithmic_flops(s, tile_rows: int = KERNEL_TILE_ROWS) -> int:
 
 
 # kernel sources behind each workload's counter summary
+SSD_SOURCES = ("ssd_scan.hip", "ssd_kernels.h", "ssd_select.h", "ssd_common.h",
+               "ssd_cols_bf16.hip", "ssd_cols_f32.hip", "ssd_walk_bf16.hip", "ssd_walk_f32.hip")
 KERNEL_SOURCES = {
-    "ssd": ("ssd_scan.hip", "ssd_common.h"),
+    "ssd": SSD_SOURCES,
     "selective_scan": ("sel_scan.hip", "ssd_common.h"),
-    "trapezoid": ("ssd_scan.hip", "ssd_common.h", "trap_scan.hip"),
+    "trapezoid": SSD_SOURCES + ("trap_scan.hip",),
 }
 
 

@@ -89,6 +89,18 @@ ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, con
                           float* y, float* final_state, void* ws, void* const* walk_events,
                           hipStream_t hs);
 
+// Kernel addresses for a launch plan, nullptr when no instantiation fits
+// (defined in the instantiation units ssd_walk_{bf16,f32}.hip and
+// ssd_cols_{bf16,f32}.hip). mode 1: state-only pass, 0: output pass; ysub:
+// the output pass that keeps only odd steps of y.
+void* select_walk_bf16(bool rot, int mode, int P, int NP);
+void* select_walk_f32(bool rot, int mode, int P, int NP);
+void* select_cols_bf16(int mode, int w, int NP, bool ysub);
+void* select_cols_f32(int mode, int w, int NP, bool ysub);
+void* select_cols_rot_bf16(int mode, int w, int NP, bool ysub);
+void* cb_pack_bf16(int NP);
+void* cb_pack_f32(int NP);
+
 }  // namespace ssd_detail
 
 #endif  // SSD_COMMON_H
