@@ -52,8 +52,11 @@
  * final_state may be the same pointer as init_state (in-place state update);
  * any other overlap between an output and another buffer is SSD_ERR_ALIAS.
  *
- * Errors: every argument is checked on the host before anything is enqueued;
- * on any error status nothing is enqueued and no output is touched.
+ * Errors: every argument, the launch plan and the scratch buffer are checked
+ * or obtained on the host before the first kernel is enqueued. On every error
+ * status except SSD_ERR_HIP no kernel is launched and no output is touched.
+ * SSD_ERR_HIP (a failed HIP call) can come after part of the call's kernels
+ * were enqueued; y and final_state are then unspecified.
  * The call is asynchronous: it returns after enqueueing on `stream` (a
  * hipStream_t; NULL means the null stream) without synchronising.
  * Different streams may call concurrently (host threads included); they
@@ -146,10 +149,11 @@ ssd_status ssd_forward_ex(const ssd_dims *d, const void *x, const float *da,
                           const float *theta, float *y, float *final_state,
                           const ssd_launch_opts *opts, void *stream);
 
-/* Bytes of stream-ordered scratch ssd_forward allocates for this problem with
- * automatic launch options and no rotation (an upper bound with rotation):
- * the shared C B^T tile pack, plus segment states when the sequence is split.
- * Returns 0 for invalid arguments. */
+/* Bytes of scratch ssd_forward needs for this problem with automatic launch
+ * options: the larger of the plans without and with rotation (the shared
+ * C B^T tile pack, plus segment states when the sequence is split). The
+ * library takes it from its per-(device, stream) cache (ssd_forward_ex) or
+ * from its fixed array (ssd_forward_noalloc). Returns 0 for invalid arguments. */
 size_t ssd_workspace_bytes(const ssd_dims *d, int64_t chunk_len, int64_t R);
 
 /*
