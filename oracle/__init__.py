@@ -6,8 +6,9 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 no code.
 
 The oracle itself is ``ssd_oracle.c``: the plain token-by-token recurrences in
-double precision, of the chunked SSD scan and of the Mamba-1 selective scan
-(see that file for the definitions and the page passages they follow). This module builds it with gcc and wraps it with ctypes.
+double precision, of the chunked SSD scan, the Mamba-1 selective scan and the
+Mamba-3 trapezoid, and the physical-frame state moments (see that file for the
+definitions and the page passages they follow). This module builds it with gcc and wraps it with ctypes.
 Pins that tie it to the pages and to mathematics live in
 ``tests/test_oracle_pins.py``.
 """
@@ -55,6 +56,9 @@ def _load(path: Optional[str] = None):
         lib.selective_scan_f64.restype = ctypes.c_int
         lib.trapezoid_f64.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 10 + [vp, i64, vp, vp, ctypes.c_int]
         lib.trapezoid_f64.restype = ctypes.c_int
+        lib.state_moments_f64.argtypes = ([i64] * 7 + [ctypes.c_int] + [vp] * 9 + [i64]
+                                          + [vp, i64, vp, vp, ctypes.c_int])
+        lib.state_moments_f64.restype = ctypes.c_int
         _libs[key] = lib
     return _libs[key]
 
@@ -222,3 +226,52 @@ def trapezoid(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor, C: torch.Tenso
     if bh is not None:
         return y_sel, fin
     return y_sel.reshape(b, H, T, R, P).transpose(0, 2, 3, 1, 4).copy(), fin.reshape(b, H, P, N)
+
+
+def state_moments(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor,
+                  beta: Optional[torch.Tensor] = None, gamma: Optional[torch.Tensor] = None,
+                  prev_x: Optional[torch.Tensor] = None, prev_B: Optional[torch.Tensor] = None,
+                  init_state: Optional[torch.Tensor] = None, theta: Optional[torch.Tensor] = None,
+                  valid_len: Optional[int] = None, bh: Optional[Sequence[int]] = None,
+                  nthreads: int = 0, lib_path: Optional[str] = None):
+    """Float64 physical-frame state moments (burn-mamba "mamba3/moments.rs",
+    module documentation and state_moments_phys).
+
+    Shapes as ``trapezoid`` (without C); beta and gamma both None for the
+    single-write recurrence. valid_len defaults to T. Returns (m2 [b,H,N,N],
+    m1 [b,H,N]) as float64, or with ``bh`` the selected slices (m2 [n,N,N],
+    m1 [n,N]).
+    """
+    lib = _load(lib_path)
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    assert da.shape == (b, T, H) and B.shape[:3] == (b, T, R)
+    assert (beta is None) == (gamma is None)
+    if beta is None:
+        prev_x = prev_B = None
+    else:
+        assert beta.shape == gamma.shape == (b, T, H)
+    assert (prev_x is None) == (prev_B is None)
+    dt = {torch.bfloat16: 1, torch.float32: 0, torch.float64: 2}[x.dtype]
+    assert B.dtype == x.dtype
+    vl = T if valid_len is None else int(valid_len)
+    cont = lambda t: None if t is None else t.detach().cpu().contiguous()
+    x, da, B, beta, gamma, prev_x, prev_B, init_state, theta = map(
+        cont, (x, da, B, beta, gamma, prev_x, prev_B, init_state, theta))
+    if bh is None:
+        n, bh_arr = b * H, None
+    else:
+        bh_arr = np.ascontiguousarray(np.asarray(bh, dtype=np.int64))
+        n = int(bh_arr.size)
+    m2 = np.empty((n, N, N), dtype=np.float64)
+    m1 = np.empty((n, N), dtype=np.float64)
+    rc = lib.state_moments_f64(
+        b, T, H, P, N, G, R, dt, _ptr(x), _ptr(da), _ptr(B), _ptr(beta), _ptr(gamma),
+        _ptr(prev_x), _ptr(prev_B), _ptr(init_state), _ptr(theta), vl,
+        None if bh_arr is None else bh_arr.ctypes.data, n, m2.ctypes.data, m1.ctypes.data,
+        int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"state_moments_f64 failed with code {rc}")
+    if bh is not None:
+        return m2, m1
+    return m2.reshape(b, H, N, N), m1.reshape(b, H, N)

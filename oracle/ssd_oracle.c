@@ -389,3 +389,131 @@ int trapezoid_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
     }
     return err;
 }
+
+/*
+ * Physical-frame state moments, burn-mamba "mamba3/moments.rs": module
+ * documentation (the per-token physical state c_t, steps 1-4: states,
+ * de-rotation to the physical frame, plain real m2/m1 sums masked to
+ * valid_len) and state_moments_phys (raw sums, count = valid_len * P).
+ * For every (b, h), with h_t the physical state after step t of the
+ * trapezoid recurrence of trapezoid_f64 (or, when beta and gamma are NULL,
+ * of the single-write recurrence: beta = 0, gamma = 1, no previous token):
+ *
+ *   m2[b,h][n][n'] = sum_{t < valid_len} sum_p h_t[p][n] h_t[p][n']
+ *   m1[b,h][n]     = sum_{t < valid_len} sum_p h_t[p][n]
+ *
+ * The moments see the states only; y and C play no part. Tokens at
+ * t >= valid_len still step the state but are not counted.
+ *   m2_sel: [n_bh][N][N], m1_sel: [n_bh][N] doubles.
+ */
+static void run_moments_slice(const oracle_problem *pr, const float *beta, const float *gamma,
+                              const void *prev_x, const void *prev_B, int64_t valid_len,
+                              int64_t b, int64_t h, double *m2, double *m1,
+                              double *st, double *wlast, double *wnow) {
+    const int64_t T = pr->T, H = pr->H, P = pr->P, N = pr->N, G = pr->G, R = pr->R;
+    const int64_t g = h / (H / G);
+    const int64_t PN = P * N;
+
+    for (int64_t i = 0; i < PN; ++i)
+        st[i] = pr->init_state ? (double)pr->init_state[(b * H + h) * PN + i] : 0.0;
+    for (int64_t i = 0; i < PN; ++i) wlast[i] = 0.0;
+    if (beta && prev_x && prev_B) {
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t p = 0; p < P; ++p) {
+                const double xe = load_elem(prev_x, ((b * R + r) * H + h) * P + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    wlast[p * N + n] += xe * load_elem(prev_B, ((b * R + r) * G + g) * N + n, pr->in_dtype);
+            }
+    }
+    for (int64_t i = 0; i < N * N; ++i) m2[i] = 0.0;
+    for (int64_t n = 0; n < N; ++n) m1[n] = 0.0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        const int64_t row = (b * T + t) * H + h;
+        /* this step's rank-R write */
+        for (int64_t i = 0; i < PN; ++i) wnow[i] = 0.0;
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t p = 0; p < P; ++p) {
+                const double xe = load_elem(pr->x, (((b * T + t) * R + r) * H + h) * P + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    wnow[p * N + n] += xe * load_elem(pr->B, (((b * T + t) * R + r) * G + g) * N + n, pr->in_dtype);
+            }
+        const double dec = exp((double)pr->da[row]);
+        const double wb = beta ? (double)beta[row] : 0.0, wg = gamma ? (double)gamma[row] : 1.0;
+        /* decay and the previous step's write, the turn of step t, this step's write */
+        for (int64_t i = 0; i < PN; ++i) st[i] = dec * st[i] + wb * wlast[i];
+        if (pr->theta) {
+            for (int64_t k = 0; k < N / 2; ++k) {
+                const double ang = (double)pr->theta[row * (N / 2) + k];
+                const double co = cos(ang), si = sin(ang);
+                for (int64_t p = 0; p < P; ++p) {
+                    const double e0 = st[p * N + 2 * k], e1 = st[p * N + 2 * k + 1];
+                    st[p * N + 2 * k] = co * e0 - si * e1;
+                    st[p * N + 2 * k + 1] = si * e0 + co * e1;
+                }
+            }
+        }
+        for (int64_t i = 0; i < PN; ++i) st[i] += wg * wnow[i];
+        for (int64_t i = 0; i < PN; ++i) wlast[i] = wnow[i];
+        /* the sums, over the tokens inside valid_len */
+        if (t < valid_len) {
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n) {
+                    const double hv = st[p * N + n];
+                    m1[n] += hv;
+                    for (int64_t n2 = 0; n2 < N; ++n2) m2[n * N + n2] += hv * st[p * N + n2];
+                }
+        }
+    }
+}
+
+/*
+ * Runs the moments on the selected (b, h) slices; arguments as
+ * trapezoid_f64 without C and y (beta and gamma both NULL for the
+ * single-write recurrence, when prev_x and prev_B are ignored), plus
+ * valid_len in 1..T.
+ */
+int state_moments_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
+                      int64_t G, int64_t R, int in_dtype,
+                      const void *x, const float *da, const void *B,
+                      const float *beta, const float *gamma, const void *prev_x, const void *prev_B,
+                      const float *init_state, const float *theta, int64_t valid_len,
+                      const int64_t *bh_list, int64_t n_bh,
+                      double *m2_sel, double *m1_sel, int nthreads) {
+    if (batch < 1 || T < 1 || H < 1 || P < 1 || N < 1 || G < 1 || R < 1) return -1;
+    if (H % G != 0) return -2;
+    if (theta && (N % 2)) return -3;
+    if (in_dtype != ORACLE_IN_F32 && in_dtype != ORACLE_IN_BF16 && in_dtype != ORACLE_IN_F64)
+        return -4;
+    if (!x || !da || !B || !m2_sel || !m1_sel) return -5;
+    if ((beta == NULL) != (gamma == NULL) || (prev_x == NULL) != (prev_B == NULL)) return -5;
+    if (valid_len < 1 || valid_len > T) return -8;
+    if (!bh_list) n_bh = batch * H;
+    for (int64_t i = 0; bh_list && i < n_bh; ++i)
+        if (bh_list[i] < 0 || bh_list[i] >= batch * H) return -6;
+
+    oracle_problem pr = {batch, T, H, P, N, G, R, in_dtype, x, B, NULL, da, NULL, init_state, theta};
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(3 * P * N));
+        if (!work) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t i = 0; i < n_bh; ++i) {
+            if (!work) continue;
+            const int64_t bh = bh_list ? bh_list[i] : i;
+            run_moments_slice(&pr, beta, gamma, prev_x, prev_B, valid_len, bh / H, bh % H,
+                              m2_sel + i * N * N, m1_sel + i * N, work, work + P * N, work + 2 * P * N);
+        }
+        free(work);
+    }
+    return err;
+}

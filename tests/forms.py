@@ -242,3 +242,40 @@ def trapezoid_frame_form(x, da, B, C, beta, gamma, prev_x=None, prev_B=None, h0=
         h = rot_n(g, Phi[:, t])
         y[:, t] = np.einsum("brhn,bhnp->brhp", Ch[:, t], h)
     return y, np.swapaxes(h, -1, -2)
+
+
+def trapezoid_frame_states(x, da, B, beta=None, gamma=None, prev_x=None, prev_B=None, h0=None,
+                           theta=None):
+    """Every physical state h_t [b,T,H,P,N] of the trapezoid (or, with beta
+    and gamma None, the single-write) recurrence, via the cumulative-angle
+    frame as ``trapezoid_frame_form`` builds it: the writes turned into the
+    frame, a first-order scan g_t, then h_t = R(Phi_t) g_t ("mamba3/scan.py",
+    scan_forward; "mamba3/moments.rs", module documentation: the cache-frame
+    states de-rotated to the physical frame, step 3)."""
+    x, da, B = map(f64, (x, da, B))
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    gi = _groups(H, G)
+    Bh = B[:, :, :, gi, :]
+    S = np.einsum("btrhn,btrhp->bthnp", Bh, x)
+    if beta is None:
+        beta, gamma = np.zeros((b, T, H)), np.ones((b, T, H))
+        prev_x = prev_B = None
+    else:
+        beta, gamma = f64(beta), f64(gamma)
+    if prev_x is not None:
+        Sm1 = np.einsum("brhn,brhp->bhnp", f64(prev_B)[:, :, gi, :], f64(prev_x))
+    else:
+        Sm1 = np.zeros((b, H, N, P))
+    Sprev = np.concatenate([Sm1[:, None], S[:, :-1]], axis=1)
+    Phi = np.cumsum(f64(theta), axis=1) if theta is not None else np.zeros((b, T, H, N // 2))
+    Phi_prev = np.concatenate([np.zeros_like(Phi[:, :1]), Phi[:, :-1]], axis=1)
+    rot_n = lambda v, ang: np.swapaxes(rotate_pairs(np.swapaxes(v, -1, -2), ang[..., None, :]), -1, -2)
+    w = gamma[..., None, None] * rot_n(S, -Phi) + beta[..., None, None] * rot_n(Sprev, -Phi_prev)
+    g = np.zeros((b, H, N, P)) if h0 is None else np.swapaxes(f64(h0), -1, -2).copy()
+    alpha = np.exp(da)
+    out = np.empty((b, T, H, P, N))
+    for t in range(T):
+        g = alpha[:, t, :, None, None] * g + w[:, t]
+        out[:, t] = np.swapaxes(rot_n(g, Phi[:, t]), -1, -2)
+    return out

@@ -605,3 +605,152 @@ def test_trapezoid_pins_catch_planted_mistakes(tmp_path):
         subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
         y, f = _trap(ti, lib_path=so)
         assert relerr(y, yr) > 1e-6 or relerr(f, fr) > 1e-6, name
+
+
+# ---------------------------------------------------------------------------
+# Physical-frame state moments ("mamba3/moments.rs", module documentation
+# steps 1-4 and state_moments_phys)
+# ---------------------------------------------------------------------------
+
+def _moments(ti, trap=True, lib_path=None, **kw):
+    bi = ti.base
+    if trap:
+        args = dict(beta=ti.beta, gamma=ti.gamma, prev_x=ti.prev_x, prev_B=ti.prev_B)
+    else:
+        args = {}
+    args.update(init_state=bi.init_state, theta=bi.theta)
+    args.update(kw)
+    return oracle.state_moments(bi.x, bi.da, bi.B, lib_path=lib_path, **args)
+
+
+def _sums(states, valid_len):
+    """m2, m1 of states [b,T,H,P,N] over t < valid_len, written out."""
+    h = states[:, :valid_len]
+    m2 = np.einsum("bthpn,bthpk->bhnk", h, h)
+    m1 = h.sum(axis=(1, 3))
+    return m2, m1
+
+
+MOMENT_CASES = [
+    (True, dict(seqlen=19, rotation=True, init_state=True, mimo_rank=2), 19),
+    (True, dict(seqlen=23, rotation=True, init_state=False, mimo_rank=1, nheads=3, ngroups=3), 15),
+    (False, dict(seqlen=21, rotation=True, init_state=True, mimo_rank=4), 21),
+    (False, dict(seqlen=17, rotation=False, init_state=True, mimo_rank=1, dtype="bf16"), 9),
+    (True, dict(seqlen=13, rotation=True, init_state=True, mimo_rank=2, dtype="bf16"), 1),
+]
+
+
+@pytest.mark.parametrize("trap,kw,vl", MOMENT_CASES)
+def test_moments_from_prefix_final_states(trap, kw, vl):
+    # h_t is the final state of the prefix [0, t]: the moments from the
+    # final states the pinned recurrences give for every prefix
+    ti = si.make_trapezoid_inputs(si.small_shape(**kw), seed=50 + vl)
+    bi = ti.base
+    m2, m1 = _moments(ti, trap, valid_len=vl)
+    b, T, R, H, P = bi.x.shape
+    N = bi.B.shape[-1]
+    states = np.empty((b, vl, H, P, N))
+    sl = lambda a, t: None if a is None else a[:, :t + 1].contiguous()
+    for t in range(vl):
+        if trap:
+            _, f = oracle.trapezoid(sl(bi.x, t), sl(bi.da, t), sl(bi.B, t), sl(bi.C, t),
+                                    sl(ti.beta, t), sl(ti.gamma, t), ti.prev_x, ti.prev_B,
+                                    bi.init_state, sl(bi.theta, t))
+        else:
+            _, f = oracle.ssd_oracle(sl(bi.x, t), sl(bi.da, t), sl(bi.B, t), sl(bi.C, t), None,
+                                     bi.init_state, sl(bi.theta, t))
+        states[:, t] = f
+    r2, r1 = _sums(states, vl)
+    assert relerr(m2, r2) < 1e-12 and relerr(m1, r1) < 1e-12
+
+
+@pytest.mark.parametrize("trap,kw,vl", MOMENT_CASES)
+def test_moments_match_the_frame_form_states(trap, kw, vl):
+    ti = si.make_trapezoid_inputs(si.small_shape(**kw), seed=60 + vl)
+    bi = ti.base
+    m2, m1 = _moments(ti, trap, valid_len=vl)
+    if trap:
+        st = forms.trapezoid_frame_states(bi.x, bi.da, bi.B, ti.beta, ti.gamma, ti.prev_x,
+                                          ti.prev_B, bi.init_state, bi.theta)
+    else:
+        st = forms.trapezoid_frame_states(bi.x, bi.da, bi.B, h0=bi.init_state, theta=bi.theta)
+    r2, r1 = _sums(st, vl)
+    assert relerr(m2, r2) < TOL and relerr(m1, r1) < TOL
+
+
+def test_moments_ignore_padded_tokens():
+    # tokens at t >= valid_len step the state but do not count, whatever
+    # their values ("mamba3/moments.rs": the valid_len mask alone excludes
+    # pad garbage)
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=30, rotation=True, init_state=True,
+                                                 mimo_rank=2), seed=70)
+    bi = ti.base
+    m2, m1 = _moments(ti, valid_len=30)
+    pad = si.make_trapezoid_inputs(si.small_shape(seqlen=41, rotation=True, init_state=True,
+                                                  mimo_rank=2), seed=71)
+    cat = lambda a, p: torch.cat([a, p[:, 30:]], dim=1)
+    pb = pad.base
+    q2, q1 = oracle.state_moments(cat(bi.x, pb.x), cat(bi.da, pb.da), cat(bi.B, pb.B),
+                                  cat(ti.beta, pad.beta), cat(ti.gamma, pad.gamma), ti.prev_x,
+                                  ti.prev_B, bi.init_state, cat(bi.theta, pb.theta), valid_len=30)
+    assert np.array_equal(m2, q2) and np.array_equal(m1, q1)
+
+
+def test_moments_pure_cumsum_closed_form():
+    # da = 0, no rotation, no initial state, single write: h_t is the
+    # cumulative sum of the writes x_s (outer) B_s
+    shape = si.small_shape(seqlen=16, rotation=False, init_state=False, mimo_rank=2)
+    inp = si.make_inputs(shape, seed=72)
+    da = torch.zeros_like(inp.da)
+    m2, m1 = oracle.state_moments(inp.x, da, inp.B)
+    x, B = forms.f64(inp.x), forms.f64(inp.B)
+    W = np.einsum("btrhp,btrhn->bthpn", x, B[:, :, :, forms._groups(x.shape[3], B.shape[3])])
+    r2, r1 = _sums(np.cumsum(W, axis=1), 16)
+    assert relerr(m2, r2) < 1e-12 and relerr(m1, r1) < 1e-12
+
+
+def test_moments_selected_slices():
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=12, rotation=True, nheads=3), seed=73)
+    m2, m1 = _moments(ti)
+    s2, s1 = _moments(ti, bh=[4, 1])
+    H = ti.base.x.shape[3]
+    for i, bh in enumerate([4, 1]):
+        bb, h = divmod(bh, H)
+        assert np.array_equal(s2[i], m2[bb, h]) and np.array_equal(s1[i], m1[bb, h])
+
+
+MOMENT_MUTANTS = {
+    "mom_mask_off_by_one": [("if (t < valid_len) {", "if (t <= valid_len && t < T) {")],
+    "mom_gram_diagonal": [("m2[n * N + n2] += hv * st[p * N + n2];",
+                           "m2[n * N + n2] += hv * st[p * N + n];")],
+    "mom_m1_squared": [("m1[n] += hv;", "m1[n] += hv * hv;")],
+    "mom_turn_sign": [("st[p * N + 2 * k] = co * e0 - si * e1;", "st[p * N + 2 * k] = co * e0 + si * e1;")],
+    "mom_counted_before_write": [
+        ("for (int64_t i = 0; i < PN; ++i) st[i] += wg * wnow[i];\n        for (int64_t i = 0; i < PN; ++i) wlast[i] = wnow[i];",
+         "for (int64_t i = 0; i < PN; ++i) wlast[i] = wnow[i];"),
+        ("                    for (int64_t n2 = 0; n2 < N; ++n2) m2[n * N + n2] += hv * st[p * N + n2];\n                }\n        }",
+         "                    for (int64_t n2 = 0; n2 < N; ++n2) m2[n * N + n2] += hv * st[p * N + n2];\n                }\n        }\n        for (int64_t i = 0; i < PN; ++i) st[i] += wg * wnow[i];")],
+    "mom_init_dropped": [("st[i] = pr->init_state ? (double)pr->init_state[(b * H + h) * PN + i] : 0.0;",
+                          "st[i] = 0.0;")],
+}
+
+
+def test_moments_pins_catch_planted_mistakes(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
+    ti = si.make_trapezoid_inputs(si.small_shape(seqlen=15, rotation=True, init_state=True,
+                                                 mimo_rank=2), seed=74)
+    bi = ti.base
+    st = forms.trapezoid_frame_states(bi.x, bi.da, bi.B, ti.beta, ti.gamma, ti.prev_x, ti.prev_B,
+                                      bi.init_state, bi.theta)
+    r2, r1 = _sums(st, 11)
+    for name, edits in MOMENT_MUTANTS.items():
+        mutated = src
+        for old, new in edits:
+            assert mutated.count(old) == 1, (name, old)
+            mutated = mutated.replace(old, new)
+        path = tmp_path / f"{name}.c"
+        path.write_text(mutated)
+        so = str(tmp_path / f"{name}.so")
+        subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
+        m2, m1 = _moments(ti, lib_path=so, valid_len=11)
+        assert relerr(m2, r2) > 1e-6 or relerr(m1, r1) > 1e-6, name
