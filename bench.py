@@ -423,6 +423,103 @@ def ssd_workload(cfg: int, args, with_timed_region: bool):
     return shape, inp, wall, tc, summary
 
 
+def moments_flops(shape, trap: bool, valid_len: int) -> int:
+    """Algorithmic flops of the state moments: per counted step and (batch,
+    head) the unique entries of the Gram sum_p h[p,n] h[p,n'] (P N (N + 1) / 2
+    multiply-adds) and the m1 sum (P N adds), plus the state writes of every
+    step (2 P N R, twice for the two-write trapezoid)."""
+    b, T, H, P, N, R = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, \
+        shape.mimo_rank
+    gram = P * N * (N + 1) + P * N
+    writes = 2 * P * N * R * (2 if trap else 1)
+    return b * H * (valid_len * gram + T * writes)
+
+
+def moments_bench(args) -> dict:
+    """Physical-frame state moments of the Mamba-3 trapezoid on the MIMO layer shape."""
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    shape = si.CONFIGS[3]
+    dev = torch.device("cuda:0")
+    ti = si.make_trapezoid_inputs(shape, seed=0)
+    g = ti.to(dev)
+    bi = g.base
+    b, T, R, H, P = bi.x.shape
+    N = shape.dstate
+    vl = T
+    m2 = torch.empty((b, H, N, N), device=dev)
+    m1 = torch.empty((b, H, N), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(walk_events=None):
+        ssd.state_moments(bi.x, bi.da, bi.B, g.beta, g.gamma, g.prev_x, g.prev_B, bi.init_state,
+                          bi.theta, valid_len=vl, m2=m2, m1=m1, stream=stream.cuda_stream)
+
+    nwarm = prewarm(step, args.prewarm)
+    wall = timed_region(step, args)
+    # per-call event timing after the same flush as the other lines (the
+    # moments entry point has no walk events: the call is the unit)
+    import statistics
+    flush = torch.empty(FLUSH_BYTES // 4, device=dev)
+    ts = []
+    for i in range(args.calls):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del flush
+    call_ms = statistics.median(ts)
+    if not (torch.isfinite(m2).all() and torch.isfinite(m1).all()):
+        raise RuntimeError("non-finite output")
+    flops = moments_flops(shape, True, vl)
+    achieved = flops / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": "state moments tokens/s + % of MFMA roofline (b4,T4096,H32,P64,N128,R4 trapezoid)",
+        "value": b * T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; see ssd_inputs.make_trapezoid_inputs)",
+        "config": {"workload": "mamba3 MIMO layer, trapezoid state moments " + shape.name,
+                   "batch": b, "seqlen": T, "nheads": H, "headdim": P, "dstate": N,
+                   "mimo_rank": R, "valid_len": vl, "rotation": True, "init_state": True,
+                   "prev_token": True},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": None, "algorithmic_flops": flops, "kernel_ms": call_ms,
+                     "kernel_ms_min": min(ts), "forward_ms": call_ms},
+        "timing": {"prewarm_s": args.prewarm, "prewarm_calls": nwarm},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        nbh = b * H
+        nsl = max(1, min(args.cpu_slices // 40, nbh))
+        sel = [int(i * nbh / nsl) for i in range(nsl)]
+        t1 = time.perf_counter()
+        oracle.state_moments(ti.base.x, ti.base.da, ti.base.B, ti.beta, ti.gamma, ti.prev_x,
+                             ti.prev_B, ti.base.init_state, ti.base.theta, valid_len=vl, bh=sel,
+                             nthreads=threads)
+        secs = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": b * T * (nsl / nbh) / secs, "unit": "tokens/s",
+                               "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": (f"{nsl} of the {nbh} (batch, head) slices over the full "
+                                          f"T={T}; {secs:.2f} s wall; tokens/s scaled by the "
+                                          f"slice fraction")}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -442,10 +539,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--block-slices", type=int, default=0)
-    ap.add_argument("--workload", choices=("ssd", "selective_scan", "trapezoid"), default="ssd",
+    ap.add_argument("--workload", choices=("ssd", "selective_scan", "trapezoid", "moments"),
+                    default="ssd",
                     help="ssd: the chunked SSD scan (the reported line); selective_scan: "
                          "the diagonal selective scan, b4 T4096 D512 N16 (--segments = chunks); "
-                         "trapezoid: the Mamba-3 two-write forward on the MIMO layer shape")
+                         "trapezoid: the Mamba-3 two-write forward on the MIMO layer shape; "
+                         "moments: its physical-frame state moments")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) for counter calibration")
     args = ap.parse_args()
@@ -477,6 +576,9 @@ def main() -> int:
         return 0
     if args.workload == "trapezoid":
         print(json.dumps(trapezoid_bench(args)), flush=True)
+        return 0
+    if args.workload == "moments":
+        print(json.dumps(moments_bench(args)), flush=True)
         return 0
 
     shape, inp, wall, tc, main_summary = ssd_workload(args.config, args, with_timed_region=True)

@@ -8,7 +8,7 @@ a gfx950 device, and fails loudly otherwise (there is no CPU fallback).
 C entry points, mirrored here under the same names:
   ssd_forward, ssd_forward_ex, ssd_workspace_bytes, ssd_selective_scan,
   ssd_selective_scan_ex, ssd_trapezoid_forward, ssd_forward_noalloc,
-  ssd_status_str
+  ssd_state_moments, ssd_status_str
 plus ``forward(...)``, ``selective_scan(...)`` and ``trapezoid(...)``,
 tensor-level conveniences over ssd_forward_ex, ssd_selective_scan_ex and
 ssd_trapezoid_forward.
@@ -34,7 +34,7 @@ SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
             "ssd_selective_scan_ex", "ssd_trapezoid_forward", "ssd_forward_noalloc",
-            "ssd_status_str")
+            "ssd_state_moments", "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -84,6 +84,9 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_trapezoid_forward.argtypes = ([ctypes.POINTER(SsdDims)] + [vp] * 9 + [i64, i64]
                                               + [vp] * 3 + [ctypes.POINTER(SsdLaunchOpts), vp])
         lib.ssd_trapezoid_forward.restype = ctypes.c_int
+        lib.ssd_state_moments.argtypes = ([ctypes.POINTER(SsdDims)] + [vp] * 8 + [i64, vp, i64]
+                                          + [vp] * 3)
+        lib.ssd_state_moments.restype = ctypes.c_int
         lib.ssd_status_str.argtypes = [ctypes.c_int32]
         lib.ssd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -148,6 +151,14 @@ def ssd_trapezoid_forward(dims: Optional[SsdDims], x, da, B, C, beta, gamma, pre
                                          beta, gamma, prev_x, prev_B, init_state, int(chunk_len),
                                          int(R), theta, y, final_state,
                                          None if opts is None else ctypes.byref(opts), stream))
+
+
+def ssd_state_moments(dims: Optional[SsdDims], x, da, B, beta, gamma, prev_x, prev_B,
+                      init_state, R, theta, valid_len, m2, m1, stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_state_moments(None if dims is None else ctypes.byref(dims), x, da, B, beta,
+                                     gamma, prev_x, prev_B, init_state, int(R), theta,
+                                     int(valid_len), m2, m1, stream))
 
 
 def ssd_status_str(status: int) -> str:
@@ -397,3 +408,63 @@ def trapezoid(x, da, B, C, beta, gamma, prev_x=None, prev_B=None, init_state=Non
     if st != SSD_OK:
         raise SsdError(st, "ssd_trapezoid_forward")
     return y, final_state
+
+
+def state_moments(x, da, B, beta=None, gamma=None, prev_x=None, prev_B=None, init_state=None,
+                  theta=None, valid_len=None, m2=None, m1=None, stream=None):
+    """Physical-frame state moments on device tensors; returns (m2, m1).
+
+    Shapes as ``trapezoid`` without C (beta and gamma both None for the
+    single-write recurrence of ``forward``); valid_len defaults to T.
+    m2 [b,H,N,N] and m1 [b,H,N] fp32 may be given to write in place.
+    """
+    import torch
+
+    if (beta is None) != (gamma is None):
+        raise ValueError("beta and gamma go together (both or neither)")
+    if (prev_x is None) != (prev_B is None):
+        raise ValueError("prev_x and prev_B go together (both or neither)")
+    if prev_x is not None and beta is None:
+        raise ValueError("prev_x and prev_B belong to the trapezoid (beta, gamma)")
+    (b, T, R, H, P, G, N), px5, pB5 = _ssd_sizes(x, B, prev_x, prev_B)
+    in_dtype = _in_dtype(x)
+    f32 = torch.float32
+    dev = None if x.device.type == "cpu" else x.device
+    _check("x", x, x.shape, x.dtype, dev)
+    _check("B", B, B.shape, x.dtype, dev)
+    _check("da", da, (b, T, H), f32, dev)
+    _check("beta", beta, (b, T, H), f32, dev, optional=True)
+    _check("gamma", gamma, (b, T, H), f32, dev, optional=True)
+    if px5 is not None:
+        _check("prev_x", px5, (b, R, H, P), x.dtype, None)
+        _check("prev_B", pB5, (b, R, G, N), x.dtype, None)
+        _check("prev_x", prev_x, prev_x.shape, x.dtype, dev)
+        _check("prev_B", prev_B, prev_B.shape, x.dtype, dev)
+    _check("init_state", init_state, (b, H, P, N), f32, dev, optional=True)
+    _check("theta", theta, (b, T, H, N // 2), f32, dev, optional=True)
+    _check("m2", m2, (b, H, N, N), f32, dev, optional=True)
+    _check("m1", m1, (b, H, N), f32, dev, optional=True)
+    vl = T if valid_len is None else int(valid_len)
+    if not 1 <= vl <= T:
+        raise ValueError(f"valid_len {vl} outside 1..{T}")
+    _need_device(x, "state_moments")
+    dev = x.device
+    for name, t in (("B", B), ("da", da), ("beta", beta), ("gamma", gamma), ("prev_x", prev_x),
+                    ("prev_B", prev_B), ("init_state", init_state), ("theta", theta), ("m2", m2),
+                    ("m1", m1)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if m2 is None:
+        m2 = torch.empty((b, H, N, N), device=dev, dtype=f32)
+    if m1 is None:
+        m1 = torch.empty((b, H, N), device=dev, dtype=f32)
+    dims = make_dims(b, T, H, P, N, G, in_dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = ssd_state_moments(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), _dptr(beta),
+                               _dptr(gamma), _dptr(prev_x), _dptr(prev_B), _dptr(init_state), R,
+                               _dptr(theta), vl, m2.data_ptr(), m1.data_ptr(), stream)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_state_moments")
+    return m2, m1

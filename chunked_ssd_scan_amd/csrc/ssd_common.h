@@ -43,7 +43,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // failure. *entry identifies it for scratch_release, which marks the end of
 // this call's use on the stream (defined in ssd_scan.hip). A call that runs
 // another entry point inside it keeps its own buffers in another slot.
-enum { kSlotWork = 0, kSlotExpand = 1 };
+enum { kSlotWork = 0, kSlotExpand = 1, kSlotMoments = 2 };
 void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry, int slot = kSlotWork);
 bool scratch_release(int entry);
 
@@ -88,6 +88,45 @@ ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, con
                           const void* C, const float* D, const float* init_state, const float* theta,
                           float* y, float* final_state, void* ws, void* const* walk_events,
                           hipStream_t hs);
+
+// The trapezoid's sub-step inputs (trap_scan.hip): every step t of the
+// two-write recurrence becomes sub-steps 2t (decay, the previous write scaled
+// by beta) and 2t + 1 (turn by theta, this write scaled by gamma). The
+// expanded arrays live in a workspace: trap_expand_bytes sizes it (C may be
+// left out), trap_expand_setup points the output arrays into it, and
+// trap_expand_launch enqueues the expansion kernel.
+struct TrapExpand {
+    const void* x;
+    const float* da;
+    const void* B;
+    const void* C;           // may be null: no C^ is built
+    const float* beta;
+    const float* gamma;
+    const void* prev_x;
+    const void* prev_B;
+    const float* theta;
+    void* xh;                // [b][2T][R][H][P]
+    float* dah;              // [b][2T][H]
+    void* Bh;                // [b][2T][R][G][N]
+    void* Ch;                // [b][2T][R][G][N], or null
+    float* thh;              // [b][2T][H][N/2], or null
+    int64_t b, T, R, H, P, G, N;
+    int esz;                 // bytes per x/B/C element (2: bf16, 4: fp32)
+};
+size_t trap_expand_bytes(const TrapExpand& a);
+void trap_expand_setup(TrapExpand* a, void* ws);
+ssd_status trap_expand_launch(const TrapExpand& a, hipStream_t hs);
+
+// The forward's state passes alone (pass A and the carry), for callers that
+// need the state entering every segment: states_plan makes the forward's
+// launch plan for (d, R, rot) and the workspace those passes need;
+// states_launch enqueues them (nothing when the plan has one segment) and
+// returns in *ws_state the [b*H][S*SF][P][N] entering states (nullptr with
+// one segment: the caller starts from init_state).
+ssd_status states_plan(const ssd_dims* d, int64_t R, bool rot, Plan* pl, size_t* ws_bytes);
+ssd_status states_launch(const Plan& pl, bool rot, const void* x, const float* da, const void* B,
+                         const float* init_state, const float* theta, void* ws, hipStream_t hs,
+                         float** ws_state);
 
 // Kernel addresses for a launch plan, nullptr when no instantiation fits
 // (defined in the instantiation units ssd_walk_{bf16,f32}.hip and

@@ -394,10 +394,11 @@ ssd_status launch_walk(const Plan& pl, int mode, bool rot, const Args& args, hip
     return SSD_OK;
 }
 
-// Pass A (segment end states), pass B (carry), pass C (outputs).
+// Pass A (segment end states) and pass B (carry): with S > 1 segments,
+// ws_state slot s of every (batch, head) then holds the physical state
+// entering state-pass segment s (S SF of them; slot 0 a copy of init_state).
 template <typename Args>
-ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs,
-                      void* const* walk_events) {
+ssd_status run_state_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs) {
     ssd_status rs = SSD_OK;
     const int SA = pl.S * pl.SF;   // segments of the state pass
     args.SF = pl.SF;
@@ -412,6 +413,15 @@ ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_sta
             if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
         }
     }
+    return rs;
+}
+
+// Pass A (segment end states), pass B (carry), pass C (outputs).
+template <typename Args>
+ssd_status run_passes(const Plan& pl, bool rot, Args args, const float* init_state, hipStream_t hs,
+                      void* const* walk_events) {
+    args.SF = pl.SF;
+    ssd_status rs = run_state_passes(pl, rot, args, init_state, hs);
     if (rs == SSD_OK) {
         args.S = pl.S;
         args.seg_items = pl.S;
@@ -600,6 +610,45 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* da, const
                                    opts ? opts->walk_events : nullptr, hs);
     if (ws && !scratch_release(ws_entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
     return rs;
+}
+
+ssd_status states_plan(const ssd_dims* d, int64_t R, bool rot, Plan* pl, size_t* ws_bytes) {
+    ssd_status st = make_plan(d, R, rot, 0, 0, pl);
+    if (st != SSD_OK) return st;
+    *ws_bytes = workspace_layout(*pl, true).total;
+    return SSD_OK;
+}
+
+ssd_status states_launch(const Plan& pl, bool rot, const void* x, const float* da, const void* B,
+                         const float* init_state, const float* theta, void* ws, hipStream_t hs,
+                         float** ws_state) {
+    const WsLayout wl = workspace_layout(pl, true);
+    char* wsc = static_cast<char*>(ws);
+    float* wstate = pl.S > 1 ? reinterpret_cast<float*>(wsc) : nullptr;
+    float* wmisc = pl.S > 1 ? reinterpret_cast<float*>(wsc + wl.state) : nullptr;
+    *ws_state = wstate;
+    if (pl.S == 1) return SSD_OK;
+    const int64_t T = pl.T, H = pl.H, G = pl.G, N = pl.N, R = pl.R, P = pl.P;
+    if (pl.kind != kColsPath) {
+        WalkArgs args;
+        memset(&args, 0, sizeof(args));
+        args.x = x; args.da = da; args.B = B; args.C = B;
+        args.init = init_state; args.theta = theta;
+        args.T = T; args.H = H; args.G = G; args.N = N; args.R = R;
+        args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
+        args.ws_state = wstate; args.ws_misc = wmisc;
+        return run_state_passes(pl, rot, args, init_state, hs);
+    }
+    TileArgs args;
+    memset(&args, 0, sizeof(args));
+    args.x = x; args.da = da; args.B = B; args.C = B;
+    args.init = init_state;
+    args.T = T; args.H = H; args.G = G; args.N = N; args.R = R; args.P = P;
+    args.S = pl.S; args.nsub = pl.nsub; args.log2R = pl.log2R; args.Qt = pl.Qt;
+    args.ws_state = wstate; args.ws_misc = wmisc;
+    args.theta = theta;
+    args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
+    return run_state_passes(pl, rot, args, init_state, hs);
 }
 
 }  // namespace ssd_detail

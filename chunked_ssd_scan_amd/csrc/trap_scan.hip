@@ -25,25 +25,6 @@ namespace {
 
 using namespace ssd_detail;
 
-struct ExpandArgs {
-    const void* x;
-    const float* da;
-    const void* B;
-    const void* C;
-    const float* beta;
-    const float* gamma;
-    const void* prev_x;
-    const void* prev_B;
-    const float* theta;
-    void* xh;        // [b][2T][R][H][P]
-    float* dah;      // [b][2T][H]
-    void* Bh;        // [b][2T][R][G][N]
-    void* Ch;        // [b][2T][R][G][N]
-    float* thh;      // [b][2T][H][N/2], or null
-    int64_t b, T, R, H, P, G, N;
-    int esz;         // bytes per x/B/C element (2: bf16, 4: fp32)
-};
-
 // 16 bytes of x scaled by w: 8 bf16 or 4 fp32 lanes, rounded back to the
 // stored type (bf16: round to nearest even)
 __device__ __forceinline__ uint4 scale16(uint4 v, float w, bool bf) {
@@ -68,7 +49,7 @@ __device__ __forceinline__ uint4 scale16(uint4 v, float w, bool bf) {
 //   C^_{2t} = C^_{2t+1} = C_t                    (sub-step 2t's y is not kept)
 //   da^_{2t} = da_t, da^_{2t+1} = 0;  theta^_{2t} = 0, theta^_{2t+1} = theta_t
 // x, B and C rows move in 16-byte vectors (rows are multiples of 32 bytes).
-__global__ __launch_bounds__(256) void trap_expand_rows(ExpandArgs a) {
+__global__ __launch_bounds__(256) void trap_expand_rows(TrapExpand a) {
     const int64_t bt = blockIdx.x;
     const int64_t bb = bt / a.T, t = bt - bb * a.T;
     const int64_t o = bb * 2 * a.T + 2 * t;            // row of sub-step 2t
@@ -95,11 +76,13 @@ __global__ __launch_bounds__(256) void trap_expand_rows(ExpandArgs a) {
     uint4* Bh = static_cast<uint4*>(a.Bh);
     uint4* Ch = static_cast<uint4*>(a.Ch);
     for (int64_t j = threadIdx.x; j < bv; j += blockDim.x) {
-        const uint4 c = C[bt * bv + j];
         Bh[o * bv + j] = bprev ? bprev[j] : make_uint4(0, 0, 0, 0);
         Bh[(o + 1) * bv + j] = B[bt * bv + j];
-        Ch[o * bv + j] = c;
-        Ch[(o + 1) * bv + j] = c;
+        if (Ch) {
+            const uint4 c = C[bt * bv + j];
+            Ch[o * bv + j] = c;
+            Ch[(o + 1) * bv + j] = c;
+        }
     }
     // da, theta
     for (int64_t j = threadIdx.x; j < a.H; j += blockDim.x) {
@@ -116,6 +99,36 @@ __global__ __launch_bounds__(256) void trap_expand_rows(ExpandArgs a) {
 }
 
 }  // namespace
+
+namespace ssd_detail {
+
+size_t trap_expand_bytes(const TrapExpand& a) {
+    const size_t nx = align256((size_t)(a.b * 2 * a.T * a.R * a.H * a.P) * a.esz);
+    const size_t nbc = align256((size_t)(a.b * 2 * a.T * a.R * a.G * a.N) * a.esz);
+    const size_t nda = align256((size_t)(a.b * 2 * a.T * a.H) * 4);
+    const size_t nth = a.theta ? align256((size_t)(a.b * 2 * a.T * a.H * (a.N / 2)) * 4) : 0;
+    return nx + (a.C ? 2 : 1) * nbc + nda + nth;
+}
+
+void trap_expand_setup(TrapExpand* a, void* ws) {
+    char* w = static_cast<char*>(ws);
+    const size_t nx = align256((size_t)(a->b * 2 * a->T * a->R * a->H * a->P) * a->esz);
+    const size_t nbc = align256((size_t)(a->b * 2 * a->T * a->R * a->G * a->N) * a->esz);
+    const size_t nda = align256((size_t)(a->b * 2 * a->T * a->H) * 4);
+    a->xh = w;
+    a->Bh = w + nx;
+    a->Ch = a->C ? w + nx + nbc : nullptr;
+    char* rest = w + nx + (a->C ? 2 : 1) * nbc;
+    a->dah = reinterpret_cast<float*>(rest);
+    a->thh = a->theta ? reinterpret_cast<float*>(rest + nda) : nullptr;
+}
+
+ssd_status trap_expand_launch(const TrapExpand& a, hipStream_t hs) {
+    hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(a.b * a.T)), dim3(256), 0, hs, a);
+    return hipGetLastError() == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace ssd_detail
 
 extern "C" {
 
@@ -168,25 +181,17 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
         return SSD_ERR_ALIAS;
 
     // sub-step inputs in the expansion slot
-    const size_t nx = align256((size_t)(b * 2 * T * R * H * P) * esz);
-    const size_t nbc = align256((size_t)(b * 2 * T * R * G * N) * esz);
-    const size_t nda = align256((size_t)(b * 2 * T * H) * 4);
-    const size_t nth = theta ? align256((size_t)(b * 2 * T * H * (N / 2)) * 4) : 0;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-    int entry = -1;
-    char* ws = static_cast<char*>(scratch_acquire(hs, nx + 2 * nbc + nda + nth, &entry, kSlotExpand));
-    if (!ws) return SSD_ERR_HIP;
-    ExpandArgs a;
+    TrapExpand a;
     memset(&a, 0, sizeof(a));
     a.x = x; a.da = da; a.B = B; a.C = C; a.beta = beta; a.gamma = gamma;
     a.prev_x = prev_x; a.prev_B = prev_B; a.theta = theta;
-    a.xh = ws;
-    a.Bh = ws + nx;
-    a.Ch = ws + nx + nbc;
-    a.dah = reinterpret_cast<float*>(ws + nx + 2 * nbc);
-    a.thh = theta ? reinterpret_cast<float*>(ws + nx + 2 * nbc + nda) : nullptr;
     a.b = b; a.T = T; a.R = R; a.H = H; a.P = P; a.G = G; a.N = N;
     a.esz = (int)esz;
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    int entry = -1;
+    void* ws = scratch_acquire(hs, trap_expand_bytes(a), &entry, kSlotExpand);
+    if (!ws) return SSD_ERR_HIP;
+    trap_expand_setup(&a, ws);
 
     // plan the scan over the 2T sub-steps (and take its scratch) before the
     // expansion is enqueued, so that a rejected plan launches nothing
@@ -199,10 +204,7 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
         fws = scratch_acquire(hs, fp.ws_bytes, &fentry);
         if (!fws) rs = SSD_ERR_HIP;
     }
-    if (rs == SSD_OK) {
-        hipLaunchKernelGGL(trap_expand_rows, dim3((unsigned)(b * T)), dim3(256), 0, hs, a);
-        if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
-    }
+    if (rs == SSD_OK) rs = trap_expand_launch(a, hs);
     if (rs == SSD_OK)
         rs = forward_launch(fp, a.xh, a.dah, a.Bh, a.Ch, nullptr, init_state, a.thh, y, final_state,
                             fws, opts ? opts->walk_events : nullptr, hs);

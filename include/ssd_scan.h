@@ -235,6 +235,40 @@ ssd_status ssd_trapezoid_forward(const ssd_dims *d, const void *x, const float *
                                  const ssd_launch_opts *opts, void *stream);
 
 /*
+ * Physical-frame state moments, burn-mamba "mamba3/moments.rs", module
+ * documentation (per-token states, de-rotated to the physical frame, plain
+ * real sums masked to valid_len) and state_moments_phys. For every batch b
+ * and head h, with h_t the physical state (P x N) after step t:
+ *
+ *   m2[b,h][n][n'] = sum_{t < valid_len} sum_p h_t[p][n] h_t[p][n']
+ *   m1[b,h][n]     = sum_{t < valid_len} sum_p h_t[p][n]
+ *
+ * (count = valid_len * P samples per (b, h)). h_t follows
+ *   - with beta and gamma NULL: the recurrence of ssd_forward,
+ *     h_t = exp(da_t) R(theta_t) h_{t-1} + sum_r x_{t,r} (outer) B_{t,r};
+ *   - with beta and gamma: the Mamba-3 trapezoid of ssd_trapezoid_forward,
+ *     with the optional previous-token entries prev_x, prev_B.
+ * Steps t >= valid_len still advance the state but are not counted (their
+ * inputs cannot change the result). C, y and D play no part.
+ * Arguments: as ssd_forward / ssd_trapezoid_forward (same layouts and
+ * dtypes), plus
+ *   valid_len   1 <= valid_len <= seqlen, else SSD_ERR_BAD_SHAPE
+ *   m2          [b, H, N, N] fp32, written in full (symmetric), 16-byte aligned
+ *   m1          [b, H, N]    fp32, written in full
+ * Envelope: as ssd_forward with dstate <= 128; theta 16-byte aligned.
+ * Errors: SSD_ERR_NULL_ARG for a NULL required pointer or a lone beta/gamma or
+ * prev_x/prev_B; SSD_ERR_BAD_SHAPE also for prev_x without beta; SSD_ERR_ALIAS
+ * when m2 or m1 overlaps an input or each other. Ownership, scratch and
+ * asynchrony as ssd_trapezoid_forward (the state passes of the forward give
+ * each segment its entering state).
+ */
+ssd_status ssd_state_moments(const ssd_dims *d, const void *x, const float *da, const void *B,
+                             const float *beta, const float *gamma, const void *prev_x,
+                             const void *prev_B, const float *init_state, int64_t R,
+                             const float *theta, int64_t valid_len, float *m2, float *m1,
+                             void *stream);
+
+/*
  * ssd_forward_ex for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
  * Same arguments, result and launch plan as ssd_forward_ex (bitwise the same

@@ -252,3 +252,25 @@ def test_noalloc_checks_before_anything(lib):
     far = [(i + 1) << 36 for i in range(6)]    # spans of this size do not overlap
     assert ssd.ssd_forward_noalloc(big, far[0], far[1], far[2], far[3], None, None, 256, 1, None,
                                    far[4], far[5], None, None) == ssd.SSD_ERR_WORKSPACE
+
+
+def test_state_moments_checks(lib):
+    # host-side checks of ssd_state_moments (fake pointers, never dereferenced)
+    d = dims()
+    M2, M1 = (0x10000000 * (i + 20) for i in range(2))
+    bt, gm = 0x10000000 * 30, 0x10000000 * 31
+    call_m = lambda **kw: ssd.ssd_state_moments(
+        kw.get("d", d), X, DA, BB, kw.get("beta"), kw.get("gamma"), kw.get("px"), kw.get("pB"),
+        H0, kw.get("R", 1), kw.get("theta"), kw.get("vl", 100), kw.get("m2", M2), kw.get("m1", M1),
+        None)
+    assert call_m(d=None) == ssd.SSD_ERR_NULL_ARG
+    assert call_m(m2=None) == ssd.SSD_ERR_NULL_ARG
+    assert call_m(beta=bt) == ssd.SSD_ERR_NULL_ARG                 # beta without gamma
+    assert call_m(px=X) == ssd.SSD_ERR_NULL_ARG                    # prev_x without prev_B
+    assert call_m(px=X, pB=BB) == ssd.SSD_ERR_BAD_SHAPE            # previous token without beta
+    assert call_m(vl=0) == ssd.SSD_ERR_BAD_SHAPE
+    assert call_m(vl=101) == ssd.SSD_ERR_BAD_SHAPE
+    assert call_m(d=dims(dstate=256)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_m(m2=X) == ssd.SSD_ERR_ALIAS
+    assert call_m(m1=M2) == ssd.SSD_ERR_ALIAS
+    assert call_m(theta=TH + 4) == ssd.SSD_ERR_UNSUPPORTED         # theta not 16-byte aligned
