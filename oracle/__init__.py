@@ -59,6 +59,8 @@ def _load(path: Optional[str] = None):
         lib.state_moments_f64.argtypes = ([i64] * 7 + [ctypes.c_int] + [vp] * 9 + [i64]
                                           + [vp, i64, vp, vp, ctypes.c_int])
         lib.state_moments_f64.restype = ctypes.c_int
+        lib.ssd_backward_f64.argtypes = [i64] * 7 + [ctypes.c_int] + [vp] * 16 + [ctypes.c_int]
+        lib.ssd_backward_f64.restype = ctypes.c_int
         _libs[key] = lib
     return _libs[key]
 
@@ -275,3 +277,40 @@ def state_moments(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor,
     if bh is not None:
         return m2, m1
     return m2.reshape(b, H, N, N), m1.reshape(b, H, N)
+
+
+def ssd_backward(x: torch.Tensor, da: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                 dy: torch.Tensor, D: Optional[torch.Tensor] = None,
+                 init_state: Optional[torch.Tensor] = None, theta: Optional[torch.Tensor] = None,
+                 dfinal: Optional[torch.Tensor] = None, nthreads: int = 0,
+                 lib_path: Optional[str] = None) -> dict:
+    """Float64 gradients of the scan (reverse mode over the token recurrence).
+
+    Inputs as ``ssd_oracle`` plus dy [b,T,R,H,P] and dfinal [b,H,P,N] (fp32;
+    dfinal None means zero). Returns a dict of float64 arrays: dx, dda, dB,
+    dC, dinit, and dtheta / dD when theta / D are given.
+    """
+    lib = _load(lib_path)
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    assert da.shape == (b, T, H) and B.shape == C.shape == (b, T, R, G, N)
+    assert dy.shape == (b, T, R, H, P) and dy.dtype == torch.float32
+    assert dfinal is None or (dfinal.shape == (b, H, P, N) and dfinal.dtype == torch.float32)
+    dt = {torch.bfloat16: 1, torch.float32: 0, torch.float64: 2}[x.dtype]
+    assert B.dtype == x.dtype and C.dtype == x.dtype
+    cont = lambda t: None if t is None else t.detach().cpu().contiguous()
+    x, da, B, C, D, init_state, theta, dy, dfinal = map(
+        cont, (x, da, B, C, D, init_state, theta, dy, dfinal))
+    out = {"dx": np.empty((b, T, R, H, P)), "dda": np.empty((b, T, H)),
+           "dB": np.empty((b, T, R, G, N)), "dC": np.empty((b, T, R, G, N)),
+           "dinit": np.empty((b, H, P, N))}
+    out["dtheta"] = np.empty((b, T, H, N // 2)) if theta is not None else None
+    out["dD"] = np.empty((H,)) if D is not None else None
+    pa = lambda a: None if a is None else a.ctypes.data
+    rc = lib.ssd_backward_f64(b, T, H, P, N, G, R, dt, _ptr(x), _ptr(da), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(init_state), _ptr(theta), _ptr(dy), _ptr(dfinal),
+                              pa(out["dx"]), pa(out["dda"]), pa(out["dB"]), pa(out["dC"]),
+                              pa(out["dtheta"]), pa(out["dinit"]), pa(out["dD"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"ssd_backward_f64 failed with code {rc}")
+    return {k: v for k, v in out.items() if v is not None}

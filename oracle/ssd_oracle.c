@@ -517,3 +517,185 @@ int state_moments_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
     }
     return err;
 }
+
+/*
+ * Gradients of the scan of ssd_oracle_f64 (reverse mode, written out for the
+ * token recurrence). "mamba3/scan.py", verify(): the backward is checked
+ * against the recurrence at float64; burn-mamba "mamba3/moments.rs", module
+ * documentation: the recompute discipline, here the plain form that keeps
+ * every state of a slice. With S_t the state after step t (S_-1 = init or 0),
+ * U_t = R(theta_t) S_{t-1} and a_t = exp(da_t), so S_t = a_t U_t + W_t,
+ * and G the gradient of the loss with respect to S_t, going backwards from
+ * G = dfinal:
+ *
+ *   G      += sum_r dy[t,r] (outer) C[t,r]          (y_t reads S_t)
+ *   dC[t,r][n] += sum_p dy[t,r][p] S_t[p][n]        (summed over the heads of a group)
+ *   dx[t,r][p]  = sum_n G[p][n] B[t,r][n] + D dy[t,r][p]
+ *   dB[t,r][n] += sum_p G[p][n] x[t,r][p]           (summed over the heads of a group)
+ *   dD         += sum_{r,p} dy[t,r][p] x[t,r][p]
+ *   dda[t]      = a_t sum_{p,n} G[p][n] U_t[p][n]
+ *   dtheta[t,k] = a_t sum_p (G[p][2k+1] U_t[p][2k] - G[p][2k] U_t[p][2k+1])
+ *   G           = a_t R(theta_t)^T G               (gradient with respect to S_{t-1})
+ *
+ * and dinit = G at the end. dy is fp32 [b,T,R,H,P]; dfinal fp32 [b,H,P,N] or
+ * NULL (zero). Outputs are double: dx [b,T,R,H,P], dda [b,T,H],
+ * dB and dC [b,T,R,G,N], dtheta [b,T,H,N/2] (when theta), dinit [b,H,P,N],
+ * dD [H] (when D). Parallel over (batch, group) pairs; each keeps the T + 1
+ * states of one head at a time.
+ */
+static void backward_head(const oracle_problem *pr, const float *dy, const float *dfinal,
+                          int64_t b, int64_t h, double *st_all, double *G, double *U,
+                          double *dx, double *dda, double *dB, double *dC, double *dth,
+                          double *dinit, double *dD_h) {
+    const int64_t T = pr->T, H = pr->H, P = pr->P, N = pr->N, G_ = pr->G, R = pr->R;
+    const int64_t g = h / (H / G_);
+    const int64_t PN = P * N;
+    /* forward, keeping S_-1 .. S_{T-1} */
+    double *s0 = st_all;
+    for (int64_t i = 0; i < PN; ++i)
+        s0[i] = pr->init_state ? (double)pr->init_state[(b * H + h) * PN + i] : 0.0;
+    for (int64_t t = 0; t < T; ++t) {
+        const double *sp = st_all + t * PN;
+        double *sn = st_all + (t + 1) * PN;
+        const int64_t row = (b * T + t) * H + h;
+        for (int64_t i = 0; i < PN; ++i) sn[i] = sp[i];
+        if (pr->theta) {
+            for (int64_t k = 0; k < N / 2; ++k) {
+                const double ang = (double)pr->theta[row * (N / 2) + k], co = cos(ang), si = sin(ang);
+                for (int64_t p = 0; p < P; ++p) {
+                    const double u0 = sp[p * N + 2 * k], u1 = sp[p * N + 2 * k + 1];
+                    sn[p * N + 2 * k] = co * u0 - si * u1;
+                    sn[p * N + 2 * k + 1] = si * u0 + co * u1;
+                }
+            }
+        }
+        const double at = exp((double)pr->da[row]);
+        for (int64_t i = 0; i < PN; ++i) sn[i] *= at;
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t p = 0; p < P; ++p) {
+                const double xe = load_elem(pr->x, (((b * T + t) * R + r) * H + h) * P + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n)
+                    sn[p * N + n] += xe * load_elem(pr->B, (((b * T + t) * R + r) * G_ + g) * N + n, pr->in_dtype);
+            }
+    }
+    /* backward */
+    for (int64_t i = 0; i < PN; ++i) G[i] = dfinal ? (double)dfinal[(b * H + h) * PN + i] : 0.0;
+    const double dh = pr->D ? (double)pr->D[h] : 0.0;
+    for (int64_t t = T - 1; t >= 0; --t) {
+        const double *sc = st_all + (t + 1) * PN, *sp = st_all + t * PN;
+        const int64_t row = (b * T + t) * H + h;
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t yrow = (((b * T + t) * R + r) * H + h) * P;
+            const int64_t crow = (((b * T + t) * R + r) * G_ + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                const double dyv = (double)dy[yrow + p];
+                for (int64_t n = 0; n < N; ++n) {
+                    G[p * N + n] += dyv * load_elem(pr->C, crow + n, pr->in_dtype);
+                    dC[crow + n] += dyv * sc[p * N + n];
+                }
+            }
+        }
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t xrow = (((b * T + t) * R + r) * H + h) * P;
+            const int64_t brow = (((b * T + t) * R + r) * G_ + g) * N;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                const double xe = load_elem(pr->x, xrow + p, pr->in_dtype);
+                for (int64_t n = 0; n < N; ++n) {
+                    acc += G[p * N + n] * load_elem(pr->B, brow + n, pr->in_dtype);
+                    dB[brow + n] += G[p * N + n] * xe;
+                }
+                const double dyv = (double)dy[xrow + p];
+                dx[xrow + p] = acc + dh * dyv;
+                *dD_h += dyv * xe;
+            }
+        }
+        /* U_t = R(theta_t) S_{t-1} */
+        for (int64_t i = 0; i < PN; ++i) U[i] = sp[i];
+        if (pr->theta) {
+            for (int64_t k = 0; k < N / 2; ++k) {
+                const double ang = (double)pr->theta[row * (N / 2) + k], co = cos(ang), si = sin(ang);
+                for (int64_t p = 0; p < P; ++p) {
+                    const double u0 = sp[p * N + 2 * k], u1 = sp[p * N + 2 * k + 1];
+                    U[p * N + 2 * k] = co * u0 - si * u1;
+                    U[p * N + 2 * k + 1] = si * u0 + co * u1;
+                }
+            }
+        }
+        const double at = exp((double)pr->da[row]);
+        double acc = 0.0;
+        for (int64_t i = 0; i < PN; ++i) acc += G[i] * U[i];
+        dda[row] = at * acc;
+        if (pr->theta) {
+            for (int64_t k = 0; k < N / 2; ++k) {
+                double tk = 0.0;
+                for (int64_t p = 0; p < P; ++p)
+                    tk += G[p * N + 2 * k + 1] * U[p * N + 2 * k] - G[p * N + 2 * k] * U[p * N + 2 * k + 1];
+                dth[row * (N / 2) + k] = at * tk;
+            }
+        }
+        /* G <- a_t R(theta_t)^T G */
+        if (pr->theta) {
+            for (int64_t k = 0; k < N / 2; ++k) {
+                const double ang = (double)pr->theta[row * (N / 2) + k], co = cos(ang), si = sin(ang);
+                for (int64_t p = 0; p < P; ++p) {
+                    const double g0 = G[p * N + 2 * k], g1 = G[p * N + 2 * k + 1];
+                    G[p * N + 2 * k] = co * g0 + si * g1;
+                    G[p * N + 2 * k + 1] = -si * g0 + co * g1;
+                }
+            }
+        }
+        for (int64_t i = 0; i < PN; ++i) G[i] *= at;
+    }
+    for (int64_t i = 0; i < PN; ++i) dinit[(b * H + h) * PN + i] = G[i];
+}
+
+int ssd_backward_f64(int64_t batch, int64_t T, int64_t H, int64_t P, int64_t N,
+                     int64_t G, int64_t R, int in_dtype,
+                     const void *x, const float *da, const void *B, const void *C,
+                     const float *D, const float *init_state, const float *theta,
+                     const float *dy, const float *dfinal,
+                     double *dx, double *dda, double *dB, double *dC, double *dtheta,
+                     double *dinit, double *dD, int nthreads) {
+    if (batch < 1 || T < 1 || H < 1 || P < 1 || N < 1 || G < 1 || R < 1) return -1;
+    if (H % G != 0) return -2;
+    if (theta && (N % 2)) return -3;
+    if (in_dtype != ORACLE_IN_F32 && in_dtype != ORACLE_IN_BF16 && in_dtype != ORACLE_IN_F64)
+        return -4;
+    if (!x || !da || !B || !C || !dy || !dx || !dda || !dB || !dC || !dinit) return -5;
+    if ((theta && !dtheta) || (D && !dD)) return -5;
+    oracle_problem pr = {batch, T, H, P, N, G, R, in_dtype, x, B, C, da, D, init_state, theta};
+    for (int64_t i = 0; i < batch * T * R * G * N; ++i) dB[i] = dC[i] = 0.0;
+    if (dD)
+        for (int64_t h = 0; h < H; ++h) dD[h] = 0.0;
+    int err = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+    double *dDpart = (double *)calloc((size_t)(batch * H), sizeof(double));
+    if (!dDpart) return -7;
+#pragma omp parallel
+    {
+        double *work = (double *)malloc(sizeof(double) * (size_t)((T + 3) * P * N));
+        if (!work) {
+#pragma omp atomic write
+            err = -7;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bg = 0; bg < batch * G; ++bg) {
+            if (!work) continue;
+            const int64_t b = bg / G, g = bg % G;
+            for (int64_t h = g * (H / G); h < (g + 1) * (H / G); ++h)
+                backward_head(&pr, dy, dfinal, b, h, work + 2 * P * N, work, work + P * N, dx, dda, dB,
+                              dC, dtheta, dinit, dDpart + b * H + h);
+        }
+        free(work);
+    }
+    if (dD)
+        for (int64_t b = 0; b < batch; ++b)
+            for (int64_t h = 0; h < H; ++h) dD[h] += dDpart[b * H + h];
+    free(dDpart);
+    return err;
+}

@@ -279,3 +279,48 @@ def trapezoid_frame_states(x, da, B, beta=None, gamma=None, prev_x=None, prev_B=
         g = alpha[:, t, :, None, None] * g + w[:, t]
         out[:, t] = np.swapaxes(rot_n(g, Phi[:, t]), -1, -2)
     return out
+
+
+def autograd_gradients(x, da, B, C, dy, D=None, h0=None, theta=None, dfinal=None):
+    """Float64 torch autograd of the token recurrence, written here as plain
+    tensor ops ("mamba3/scan.py", verify(): the backward checked against the
+    recurrence at float64). Loss = <dy, y> + <dfinal, final>, so the
+    gradients are the vector-Jacobian products the oracle's backward gives.
+    Returns a dict of float64 numpy arrays (dx, dda, dB, dC, dinit, dtheta,
+    dD as present)."""
+    import torch
+
+    t64 = lambda a: None if a is None else torch.tensor(f64(a), dtype=torch.float64,
+                                                       requires_grad=True)
+    x, da, B, C = map(t64, (x, da, B, C))
+    D, h0, theta = t64(D), t64(h0), t64(theta)
+    b, T, R, H, P = x.shape
+    G, N = B.shape[3], B.shape[4]
+    gi = torch.as_tensor(_groups(H, G))
+    S = (h0 if h0 is not None else torch.zeros(b, H, P, N, dtype=torch.float64))
+    ys = []
+    for t in range(T):
+        if theta is not None:
+            c, s = torch.cos(theta[:, t]), torch.sin(theta[:, t])      # [b,H,N/2]
+            e, o = S[..., 0::2], S[..., 1::2]
+            S = torch.stack((c[:, :, None] * e - s[:, :, None] * o,
+                             s[:, :, None] * e + c[:, :, None] * o), dim=-1).flatten(-2)
+        S = torch.exp(da[:, t])[:, :, None, None] * S
+        Bh, Ch = B[:, t][:, :, gi], C[:, t][:, :, gi]                  # [b,R,H,N]
+        S = S + torch.einsum("brhp,brhn->bhpn", x[:, t], Bh)
+        yt = torch.einsum("brhn,bhpn->brhp", Ch, S)
+        if D is not None:
+            yt = yt + D[None, None, :, None] * x[:, t]
+        ys.append(yt)
+    y = torch.stack(ys, dim=1)
+    loss = (y * torch.tensor(f64(dy))).sum()
+    if dfinal is not None:
+        loss = loss + (S * torch.tensor(f64(dfinal))).sum()
+    loss.backward()
+    out = {"dx": x.grad.numpy(), "dda": da.grad.numpy(), "dB": B.grad.numpy(), "dC": C.grad.numpy(),
+           "dinit": h0.grad.numpy() if h0 is not None else None}
+    if theta is not None:
+        out["dtheta"] = theta.grad.numpy()
+    if D is not None:
+        out["dD"] = D.grad.numpy()
+    return {k: v for k, v in out.items() if v is not None}

@@ -754,3 +754,142 @@ def test_moments_pins_catch_planted_mistakes(tmp_path):
         subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
         m2, m1 = _moments(ti, lib_path=so, valid_len=11)
         assert relerr(m2, r2) > 1e-6 or relerr(m1, r1) > 1e-6, name
+
+
+# ---------------------------------------------------------------------------
+# Backward ("mamba3/scan.py", verify(): forward and backward checked
+# separately against the recurrence at float64)
+# ---------------------------------------------------------------------------
+
+def _bwd_inputs(seed, T=13, H=3, G=1, P=4, N=6, R=2, rot=True, init=True, skip=True,
+                dtype="f32", dfinal=True):
+    shape = si.small_shape(seqlen=T, nheads=H, ngroups=G, headdim=P, dstate=N, mimo_rank=R,
+                           dtype=dtype, rotation=rot, init_state=init,
+                           skip="randn" if skip else "none", dt_shift=1.0)
+    inp = si.make_inputs(shape, seed=seed)
+    g = torch.Generator().manual_seed(seed + 1000)
+    b = shape.batch
+    dy = torch.randn((b, T, R, H, P), generator=g)
+    df = torch.randn((b, H, P, N), generator=g) if dfinal else None
+    return inp, dy, df
+
+
+def _bwd(inp, dy, df, lib_path=None):
+    return oracle.ssd_backward(inp.x, inp.da, inp.B, inp.C, dy, inp.D, inp.init_state, inp.theta,
+                               df, lib_path=lib_path)
+
+
+BWD_CASES = [dict(), dict(rot=False), dict(init=False, skip=False, dfinal=False),
+             dict(R=1, G=3, H=3), dict(dtype="bf16", R=4, N=8), dict(T=1)]
+
+
+@pytest.mark.parametrize("kw", BWD_CASES)
+def test_backward_matches_float64_autograd(kw):
+    inp, dy, df = _bwd_inputs(80 + len(kw), **kw)
+    got = _bwd(inp, dy, df)
+    ref = forms.autograd_gradients(inp.x, inp.da, inp.B, inp.C, dy, inp.D, inp.init_state,
+                                   inp.theta, df)
+    if inp.init_state is None:
+        ref["dinit"] = None
+    for k, v in ref.items():
+        if v is None:
+            continue
+        assert relerr(got[k], v) < 1e-12, (k, relerr(got[k], v))
+
+
+def test_backward_finite_differences():
+    # central differences of L = <dy, y> + <dfinal, final> through the forward
+    # oracle, for a few elements of x (float64 inputs) and of da
+    inp, dy, df = _bwd_inputs(90, T=7, H=2, P=3, N=4, R=2)
+    inp.x, inp.B, inp.C = inp.x.double(), inp.B.double(), inp.C.double()
+    got = _bwd(inp, dy, df)
+    d64 = lambda a: a.double().numpy()
+
+    def loss(x=None, da=None):
+        y, f = oracle.ssd_oracle(inp.x if x is None else x, inp.da if da is None else da, inp.B,
+                                 inp.C, inp.D, inp.init_state, inp.theta)
+        return float((y * d64(dy)).sum() + (f * d64(df)).sum())
+
+    eps = 1e-6
+    for idx in [(0, 0, 0, 0, 0), (1, 3, 1, 1, 2), (0, 6, 1, 0, 1)]:
+        xp, xm = inp.x.clone(), inp.x.clone()
+        xp[idx] += eps
+        xm[idx] -= eps
+        fd = (loss(x=xp) - loss(x=xm)) / (2 * eps)
+        assert abs(fd - got["dx"][idx]) < 1e-6 * max(1.0, abs(fd)), (idx, fd, got["dx"][idx])
+    for idx in [(0, 0, 0), (1, 4, 1), (0, 6, 1)]:
+        # da is float32: the difference quotient uses the perturbation as stored
+        h = 2.0 ** -12
+        dp, dm = inp.da.clone(), inp.da.clone()
+        dp[idx] += h
+        dm[idx] -= h
+        step = float(dp[idx].double() - dm[idx].double())
+        fd = (loss(da=dp) - loss(da=dm)) / step
+        assert abs(fd - got["dda"][idx]) < 1e-5 * max(1.0, abs(fd)), (idx, fd, got["dda"][idx])
+
+
+def _reverse_cumsum(a, axis=1):
+    return np.flip(np.cumsum(np.flip(a, axis), axis), axis)
+
+
+def test_backward_dda_is_a_reverse_cumsum():
+    # dda_t = sum_{s >= t} (dy_s . (y_s - D x_s) - x_s . (dx_s - D dy_s)) per
+    # head, plus <dfinal, final> at the last step: the gradient of one decay
+    # counts every (write before t, read at or after t) pair once
+    inp, dy, df = _bwd_inputs(91, T=15, H=3, R=2)
+    got = _bwd(inp, dy, df)
+    y, f = oracle.ssd_oracle(inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state, inp.theta)
+    x, dyv, D = forms.f64(inp.x), forms.f64(dy), forms.f64(inp.D)
+    Dx = D[None, None, None, :, None]
+    A = np.einsum("btrhp,btrhp->bth", dyv, y - Dx * x)
+    Bc = np.einsum("btrhp,btrhp->bth", x, got["dx"] - Dx * dyv)
+    A[:, -1] += np.einsum("bhpn,bhpn->bh", forms.f64(df), f)
+    assert relerr(got["dda"], _reverse_cumsum(A - Bc)) < 1e-11
+
+
+def test_backward_dtheta_is_a_reverse_cumsum():
+    # dtheta_t,k = sum_{s >= t} of the pair cross products (dC_2k C_2k+1 -
+    # dC_2k+1 C_2k) + (dB_2k B_2k+1 - dB_2k+1 B_2k) over ranks, plus the
+    # final state's (dfinal_2k+1 h_2k - dfinal_2k h_2k+1) at the last step;
+    # one head per group, so dB and dC are per head
+    inp, dy, df = _bwd_inputs(92, T=11, H=2, G=2, R=2, N=6)
+    got = _bwd(inp, dy, df)
+    _, f = oracle.ssd_oracle(inp.x, inp.da, inp.B, inp.C, inp.D, inp.init_state, inp.theta)
+    Bv, Cv = forms.f64(inp.B), forms.f64(inp.C)
+    dB, dC = got["dB"], got["dC"]
+    cross = lambda d, v: d[..., 0::2] * v[..., 1::2] - d[..., 1::2] * v[..., 0::2]
+    Th = (cross(dC, Cv) + cross(dB, Bv)).sum(axis=2)                   # [b,T,G=H,N/2]
+    dfv = forms.f64(df)
+    Th[:, -1] += (dfv[..., 1::2] * f[..., 0::2] - dfv[..., 0::2] * f[..., 1::2]).sum(axis=2)
+    assert relerr(got["dtheta"], _reverse_cumsum(Th)) < 1e-11
+
+
+BWD_MUTANTS = {
+    "bwd_turn_not_transposed": [("G[p * N + 2 * k] = co * g0 + si * g1;", "G[p * N + 2 * k] = co * g0 - si * g1;"),
+                                ("G[p * N + 2 * k + 1] = -si * g0 + co * g1;", "G[p * N + 2 * k + 1] = si * g0 + co * g1;")],
+    "bwd_dda_no_decay": [("dda[row] = at * acc;", "dda[row] = acc;")],
+    "bwd_dC_previous_state": [("dC[crow + n] += dyv * sc[p * N + n];", "dC[crow + n] += dyv * sp[p * N + n];")],
+    "bwd_dtheta_sign": [("dth[row * (N / 2) + k] = at * tk;", "dth[row * (N / 2) + k] = -at * tk;")],
+    "bwd_dx_no_skip": [("dx[xrow + p] = acc + dh * dyv;", "dx[xrow + p] = acc;")],
+    "bwd_read_before_write": [("G[p * N + n] += dyv * load_elem(pr->C, crow + n, pr->in_dtype);",
+                               "G[p * N + n] += 0.0 * dyv;")],
+}
+
+
+def test_backward_pins_catch_planted_mistakes(tmp_path):
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")).read()
+    inp, dy, df = _bwd_inputs(93, T=9)
+    ref = forms.autograd_gradients(inp.x, inp.da, inp.B, inp.C, dy, inp.D, inp.init_state,
+                                   inp.theta, df)
+    for name, edits in BWD_MUTANTS.items():
+        mutated = src
+        for old, new in edits:
+            assert mutated.count(old) == 1, (name, old)
+            mutated = mutated.replace(old, new)
+        path = tmp_path / f"{name}.c"
+        path.write_text(mutated)
+        so = str(tmp_path / f"{name}.so")
+        subprocess.run(["gcc", *oracle.GCC_FLAGS, "-o", so, str(path), "-lm"], check=True)
+        got = _bwd(inp, dy, df, lib_path=so)
+        worst = max(relerr(got[k], v) for k, v in ref.items())
+        assert worst > 1e-6, name
