@@ -34,7 +34,7 @@ SSD_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 EXPORTED = ("ssd_forward", "ssd_forward_ex", "ssd_workspace_bytes", "ssd_selective_scan",
             "ssd_selective_scan_ex", "ssd_trapezoid_forward", "ssd_forward_noalloc",
-            "ssd_state_moments", "ssd_status_str")
+            "ssd_state_moments", "ssd_backward", "ssd_status_str")
 
 
 class SsdDims(ctypes.Structure):
@@ -87,6 +87,8 @@ def load_library(path: str = LIB_PATH):
         lib.ssd_state_moments.argtypes = ([ctypes.POINTER(SsdDims)] + [vp] * 8 + [i64, vp, i64]
                                           + [vp] * 3)
         lib.ssd_state_moments.restype = ctypes.c_int
+        lib.ssd_backward.argtypes = [ctypes.POINTER(SsdDims)] + [vp] * 6 + [i64] + [vp] * 11
+        lib.ssd_backward.restype = ctypes.c_int
         lib.ssd_status_str.argtypes = [ctypes.c_int32]
         lib.ssd_status_str.restype = ctypes.c_char_p
         _lib = lib
@@ -159,6 +161,14 @@ def ssd_state_moments(dims: Optional[SsdDims], x, da, B, beta, gamma, prev_x, pr
     return int(lib.ssd_state_moments(None if dims is None else ctypes.byref(dims), x, da, B, beta,
                                      gamma, prev_x, prev_B, init_state, int(R), theta,
                                      int(valid_len), m2, m1, stream))
+
+
+def ssd_backward(dims: Optional[SsdDims], x, da, B, C, D, init_state, R, theta, dy, dfinal,
+                 dx, dda, dB, dC, dtheta, dinit, dD, stream) -> int:
+    lib = load_library()
+    return int(lib.ssd_backward(None if dims is None else ctypes.byref(dims), x, da, B, C, D,
+                                init_state, int(R), theta, dy, dfinal, dx, dda, dB, dC, dtheta,
+                                dinit, dD, stream))
 
 
 def ssd_status_str(status: int) -> str:
@@ -468,3 +478,63 @@ def state_moments(x, da, B, beta=None, gamma=None, prev_x=None, prev_B=None, ini
     if st != SSD_OK:
         raise SsdError(st, "ssd_state_moments")
     return m2, m1
+
+
+def backward(x, da, B, C, dy, D=None, init_state=None, theta=None, dfinal=None,
+             want_dinit: bool = True, out=None, stream=None) -> dict:
+    """Gradients of ``forward`` on device tensors; returns a dict of fp32 tensors.
+
+    Inputs as ``forward`` plus dy (fp32, shaped like x) and dfinal [b,H,P,N]
+    fp32 (None: zero). Keys: dx (shaped like x), dda, dB and dC (shaped like
+    B), dinit (when want_dinit), dtheta (when theta is given), dD (when D is
+    given). ``out`` may hold tensors under those keys to write in place.
+    """
+    import torch
+
+    (b, T, R, H, P, G, N), _, _ = _ssd_sizes(x, B)
+    in_dtype = _in_dtype(x)
+    f32 = torch.float32
+    dev = None if x.device.type == "cpu" else x.device
+    _check("x", x, x.shape, x.dtype, dev)
+    _check("B", B, B.shape, x.dtype, dev)
+    _check("C", C, B.shape, x.dtype, dev)
+    _check("da", da, (b, T, H), f32, dev)
+    _check("D", D, (H,), f32, dev, optional=True)
+    _check("init_state", init_state, (b, H, P, N), f32, dev, optional=True)
+    _check("theta", theta, (b, T, H, N // 2), f32, dev, optional=True)
+    _check("dy", dy, x.shape, f32, dev)
+    _check("dfinal", dfinal, (b, H, P, N), f32, dev, optional=True)
+    out = dict(out or {})
+    shapes = {"dx": x.shape, "dda": (b, T, H), "dB": B.shape, "dC": B.shape}
+    if want_dinit:
+        shapes["dinit"] = (b, H, P, N)
+    if theta is not None:
+        shapes["dtheta"] = (b, T, H, N // 2)
+    if D is not None:
+        shapes["dD"] = (H,)
+    for k in out:
+        if k not in shapes:
+            raise ValueError(f"out[{k!r}] is not an output of this call")
+    for k, shp in shapes.items():
+        _check(k, out.get(k), shp, f32, dev, optional=True)
+    _need_device(x, "backward")
+    dev = x.device
+    for name, t in [("B", B), ("C", C), ("da", da), ("D", D), ("init_state", init_state),
+                    ("theta", theta), ("dy", dy), ("dfinal", dfinal)] + list(out.items()):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    for k, shp in shapes.items():
+        if out.get(k) is None:
+            out[k] = torch.empty(shp, device=dev, dtype=f32)
+    dims = make_dims(b, T, H, P, N, G, in_dtype)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.device(dev):
+        st = ssd_backward(dims, x.data_ptr(), da.data_ptr(), B.data_ptr(), C.data_ptr(), _dptr(D),
+                          _dptr(init_state), R, _dptr(theta), dy.data_ptr(), _dptr(dfinal),
+                          out["dx"].data_ptr(), out["dda"].data_ptr(), out["dB"].data_ptr(),
+                          out["dC"].data_ptr(), _dptr(out.get("dtheta")), _dptr(out.get("dinit")),
+                          _dptr(out.get("dD")), stream)
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_backward")
+    return out

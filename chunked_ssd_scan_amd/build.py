@@ -13,7 +13,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC_NAMES = ("ssd_scan.hip", "ssd_walk_bf16.hip", "ssd_walk_f32.hip", "ssd_cols_bf16.hip",
-             "ssd_cols_f32.hip", "sel_scan.hip", "trap_scan.hip", "moments.hip")
+             "ssd_cols_f32.hip", "sel_scan.hip", "trap_scan.hip", "moments.hip",
+             "ssd_backward.hip")
 SRCS = [os.path.join(HERE, "csrc", f) for f in SRC_NAMES]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libssd_scan.so")

@@ -1,0 +1,1022 @@
+// Backward of the chunked SSD scan for AMD Instinct MI355X (gfx950).
+//
+// Gradients of a loss with respect to x, da, B, C, theta, init_state and D,
+// given dy and the final-state gradient dfinal ("mamba3/scan.py", verify():
+// the backward is checked against the recurrence, separately from the
+// forward; burn-mamba "mamba3/moments.rs", module documentation: the
+// recompute discipline, states re-materialised instead of kept). Per
+// (batch, head), with h_t the physical state after step t and
+// H_t = dL/dh_t (h_t = a_t R(theta_t) h_{t-1} + sum_r x_{t,r} (outer) B_{t,r},
+// a_t = exp(da_t)):
+//
+//   H_t       = a_{t+1} R(theta_{t+1})^T H_{t+1} + sum_r dy_{t,r} (outer) C_{t,r}
+//               (H_{T-1} starts from dfinal)
+//   dx_{t,r}  = H_t B_{t,r} + D dy_{t,r}          dinit = a_0 R(theta_0)^T H_0
+//   dB_{t,r}  = sum_p H_t[p,:] x_{t,r}[p]          (summed over a group's heads)
+//   dC_{t,r}  = sum_p dy_{t,r}[p] h_t[p,:]         (summed over a group's heads)
+//   dD        = sum dy . x
+//   dda_t     = sum_{s >= t} (sum_r C_s . dC_s - sum_r B_s . dB_s)   (per head)
+//               + <dfinal, h_{T-1}>
+//   dtheta_t,k = sum_{s >= t} sum_r [(dC_2k C_2k+1 - dC_2k+1 C_2k) + (dB_2k B_2k+1 - dB_2k+1 B_2k)]
+//               + sum_p (dfinal_2k+1 h_2k - dfinal_2k h_2k+1)          (per head)
+//
+// The last two follow from the chain rule: the decay of step t multiplies
+// every pair (write before t, read at or after t) once, so its gradient is a
+// reverse cumulative sum of per-step inner products; the turn of a state pair
+// likewise, with the 2-D cross product (J = d R / d theta at zero). So no
+// kernel pairs a state with its gradient: dC needs only the states (a walk
+// forwards in time), dx and dB only the state gradients (a walk backwards),
+// each with its own segment states from a state pass and a carry.
+//
+// Both walks step one time step at a time with the state in registers as
+// 16 x 16 MFMA accumulators, a workgroup per (batch, head, group of at most
+// 64 state rows p, segment), two memory waves staging each 32-row tile.
+// Contractions over p (dC, dB) need the layout D[p][n] (lanes across n); the
+// contraction over n (dx) needs D[n][p] (lanes across p), so the backward walk
+// keeps its state gradient in both layouts and updates both.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "ssd_common.h"
+#include "ssd_step.h"
+
+namespace {
+
+using namespace ssd_detail;
+using namespace ssd_step;
+
+constexpr int kTileRows = 32;        // fused rows (step, rank) staged per tile
+constexpr int kPadRows = 4;          // zero rows after a tile (reads past its last step)
+constexpr int kRowGroup = 64;        // most state rows p per workgroup
+constexpr int kMemWaves = 2;
+constexpr int kMaxWaves = kRowGroup / 16 + kMemWaves;
+
+struct BwdArgs {
+    const void* x;
+    const float* da;
+    const void* B;
+    const void* C;
+    const float* theta;     // [b,T,H,N/2] or null
+    const float* dy;        // [b,T,R,H,P] fp32
+    const float* D;         // [H] or null
+    const float* init;      // [b,H,P,N] or null
+    const float* dfinal;    // [b,H,P,N] or null
+    const float* seg_in;    // entering (adjoint) states [b*H][S*SF][P][N] (forward walk) or
+                            // [b*H][S][P][N] (backward walk), null with one segment
+    float* seg_out;         // backward state pass: local adjoints [b*H][S][P][N]
+    float* part;            // per-head partials [b*H][npg][T*R][N] (dC or dB)
+    float* dx;              // [b,T,R,H,P]
+    float* dinit;           // [b,H,P,N] or null
+    float* final_state;     // forward walk: h_{T-1} [b,H,P,N]
+    float* dDp;             // [b*H][npg][S] partial sums of dy . x
+    int64_t T, H, G, N, R, P;
+    int PG, S, SF, nsub, Qt;
+};
+
+// Staging of one 32-row tile by the memory waves: x, dy (as TI), B, C rows,
+// and per step the decay a = exp(da) and (cos, sin) of every state pair's turn.
+template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C>
+struct Stage {
+    static constexpr int ESZ = (int)sizeof(TI);
+    static constexpr int EPU = 16 / ESZ;
+    static constexpr int LDX = kRowGroup + 16 / ESZ;   // x and dy rows (a row group)
+    static constexpr int LDB = NP + 16 / ESZ;          // B and C rows
+    static constexpr int PAD = ESZ == 2 ? kPadRows : 0;  // the fp32 path reads no row past a step
+    static constexpr int ROWS = kTileRows + PAD;
+    static constexpr int NH = NP / 2;
+    static constexpr int NTM = 64 * kMemWaves;
+    static constexpr int XR = kTileRows * kRowGroup / EPU / NTM;   // 16-byte units per memory thread
+    static constexpr int DYR = kTileRows * kRowGroup / 4 / NTM;    // dy: 4 floats per unit
+    static constexpr int BRG = kTileRows * NP / EPU / NTM;
+    static constexpr int THR = (kTileRows * NH / 4 + NTM - 1) / NTM;
+};
+
+// The staging buffers, each two tiles ([2][ROWS][ld]) flattened.
+template <typename TI>
+struct StageMem {
+    TI* sX;
+    TI* sDy;
+    TI* sB;
+    TI* sC;
+    float2* sCs;
+    float* sA;
+};
+
+template <typename TI>
+__device__ __forceinline__ float to_f32(TI v) {
+    if constexpr (sizeof(TI) == 2) return __uint_as_float((uint32_t)v << 16);
+    else return v;
+}
+
+// One memory thread's staging of tile k into registers (load) and LDS (store).
+template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C>
+struct Stager {
+    using St = Stage<TI, NP, WANT_X, WANT_B, WANT_C>;
+    uint4 rx[WANT_X ? St::XR : 1];
+    float4 rdy[St::DYR];
+    uint4 rb[WANT_B ? St::BRG : 1];
+    uint4 rc[WANT_C ? St::BRG : 1];
+    float4 rth[St::THR];
+    float rda;
+
+    __device__ void load(const BwdArgs& a, int k, int mt, int64_t b, int64_t h, int64_t g, int pbase) {
+        const int64_t T = a.T, H = a.H, G = a.G, N = a.N, P = a.P, TR = a.T * a.R;
+        const int64_t f0 = (int64_t)k * kTileRows;
+        const int PG = a.PG;
+        const int xur = PG / St::EPU, dur = PG / 4, nbu = (int)(N / St::EPU), thu = (int)(N / 8);
+        if constexpr (WANT_X) {
+            const TI* xg = static_cast<const TI*>(a.x);
+#pragma unroll
+            for (int m = 0; m < St::XR; ++m) {
+                const int u = mt + m * St::NTM, r = u / xur, c = (u % xur) * St::EPU;
+                rx[m] = (u < kTileRows * xur && f0 + r < TR)
+                            ? *reinterpret_cast<const uint4*>(xg + ((b * TR + f0 + r) * H + h) * P + pbase + c)
+                            : make_uint4(0, 0, 0, 0);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < St::DYR; ++m) {
+            const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
+            rdy[m] = (u < kTileRows * dur && f0 + r < TR)
+                         ? *reinterpret_cast<const float4*>(a.dy + ((b * TR + f0 + r) * H + h) * P + pbase + c)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        if constexpr (WANT_B) {
+            const TI* Bg = static_cast<const TI*>(a.B);
+#pragma unroll
+            for (int m = 0; m < St::BRG; ++m) {
+                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                rb[m] = (u < kTileRows * nbu && f0 + r < TR)
+                            ? *reinterpret_cast<const uint4*>(Bg + ((b * TR + f0 + r) * G + g) * N + c)
+                            : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if constexpr (WANT_C) {
+            const TI* Cg = static_cast<const TI*>(a.C);
+#pragma unroll
+            for (int m = 0; m < St::BRG; ++m) {
+                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                rc[m] = (u < kTileRows * nbu && f0 + r < TR)
+                            ? *reinterpret_cast<const uint4*>(Cg + ((b * TR + f0 + r) * G + g) * N + c)
+                            : make_uint4(0, 0, 0, 0);
+            }
+        }
+        const int64_t t0 = (int64_t)k * a.Qt;
+#pragma unroll
+        for (int m = 0; m < St::THR; ++m) {
+            const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (a.theta && st < a.Qt && t0 + st < T)
+                v = *reinterpret_cast<const float4*>(a.theta + ((b * T + t0 + st) * H + h) * (N / 2) + c);
+            rth[m] = v;
+        }
+        rda = (mt < a.Qt && t0 + mt < T) ? a.da[(b * T + t0 + mt) * H + h] : 0.f;
+    }
+
+    __device__ void store(const StageMem<TI>& s, const BwdArgs& a, int buf, int mt) {
+        constexpr int XS = St::ROWS * St::LDX, BS = St::ROWS * St::LDB;
+        const int PG = a.PG, N = (int)a.N;
+        const int xur = PG / St::EPU, dur = PG / 4, nbu = N / St::EPU, thu = N / 8;
+        if constexpr (WANT_X) {
+#pragma unroll
+            for (int m = 0; m < St::XR; ++m) {
+                const int u = mt + m * St::NTM, r = u / xur, c = (u % xur) * St::EPU;
+                if (u < kTileRows * xur) *reinterpret_cast<uint4*>(&s.sX[buf * XS + r * St::LDX + c]) = rx[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < St::DYR; ++m) {
+            const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
+            if (u < kTileRows * dur) {
+                TI* d = &s.sDy[buf * XS + r * St::LDX + c];
+                if constexpr (sizeof(TI) == 2) {
+                    d[0] = __builtin_bit_cast(uint16_t, (__bf16)rdy[m].x);
+                    d[1] = __builtin_bit_cast(uint16_t, (__bf16)rdy[m].y);
+                    d[2] = __builtin_bit_cast(uint16_t, (__bf16)rdy[m].z);
+                    d[3] = __builtin_bit_cast(uint16_t, (__bf16)rdy[m].w);
+                } else {
+                    *reinterpret_cast<float4*>(d) = rdy[m];
+                }
+            }
+        }
+        if constexpr (WANT_B) {
+#pragma unroll
+            for (int m = 0; m < St::BRG; ++m) {
+                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                if (u < kTileRows * nbu) *reinterpret_cast<uint4*>(&s.sB[buf * BS + r * St::LDB + c]) = rb[m];
+            }
+        }
+        if constexpr (WANT_C) {
+#pragma unroll
+            for (int m = 0; m < St::BRG; ++m) {
+                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                if (u < kTileRows * nbu) *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = rc[m];
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < St::THR; ++m) {
+            const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
+            if (st < a.Qt) {
+                const float v4[4] = {rth[m].x, rth[m].y, rth[m].z, rth[m].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float rev = v4[e] * kInv2Pi;
+                    s.sCs[buf * kTileRows * St::NH + st * St::NH + c + e] =
+                        make_float2(__builtin_amdgcn_cosf(rev), __builtin_amdgcn_sinf(rev));
+                }
+            }
+        }
+        if (mt < a.Qt) s.sA[buf * kTileRows + mt] = __expf(rda);
+    }
+};
+
+// The contraction operand of one step: rows m of a 16-row block of the tile
+// that belong to step s (fused rows s R .. s R + R - 1), zero elsewhere;
+// k = 4 (lane / 16) .. + 3 of the 16 columns at `col`.
+template <typename TI>
+__device__ __forceinline__ s16x4 step_rows(const TI* tile, int ld, int blk, int r_lo, int r_hi, int col, int lane) {
+    const int m = 16 * blk + (lane & 15);
+    const s16x4 z = {0, 0, 0, 0};
+    if (m < r_lo || m >= r_hi) return z;
+    return row4(reinterpret_cast<const uint16_t*>(tile) + m * ld + col + 4 * (lane >> 4));
+}
+
+// A compute wave's share of per-head rows [32][NP] (two row blocks of NT
+// accumulator tiles) into the reduction buffer: wave 0 stores, the others add
+// in wave order, one barrier between waves (the caller's).
+template <int NT>
+__device__ __forceinline__ void put_share(float* sZ, const f32x4 (&z)[2][NT], bool first, int lane) {
+    constexpr int NP = 16 * NT;
+    const int q = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                float* zp = &sZ[(16 * i + 4 * q + v) * NP + 16 * c + l16];
+                *zp = first ? z[i][c][v] : *zp + z[i][c][v];
+            }
+}
+
+// The reduced rows of a tile (those before TR) to the head's partial.
+template <int NP>
+__device__ __forceinline__ void copy_rows(const float* sZ, float* dst, int64_t f0, int64_t TR, int N, int tid,
+                                          int nthr) {
+    const int nu = N / 4;
+    for (int i = tid; i < kTileRows * nu; i += nthr) {
+        const int r = i / nu, c = (i % nu) * 4;
+        if (f0 + r < TR)
+            *reinterpret_cast<float4*>(dst + (f0 + r) * N + c) = *reinterpret_cast<const float4*>(&sZ[r * NP + c]);
+    }
+}
+
+// ------------------------------------------------------------------------
+// Forward walk: the states h_t, and per head dC_{t,r} = sum_p dy h_t[p,:]
+// over the workgroup's rows p; the final state.
+//
+// Per tile: the memory waves stage tile k + 1 into the free buffer while the
+// compute waves walk tile k, then nw barriers (the shares added in wave order)
+// and one after the copy to the partial.
+// ------------------------------------------------------------------------
+template <typename TI, int NP>
+__global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_forward_kernel(BwdArgs a) {
+    using St = Stage<TI, NP, true, true, false>;
+    constexpr bool BF = sizeof(TI) == 2;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, NH = St::NH, ROWS = St::ROWS, PAD = St::PAD;
+    __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
+    __shared__ __attribute__((aligned(16))) float2 sCs[2][kTileRows * NH];
+    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) float sZ[kTileRows * NP];
+    const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], nullptr, &sCs[0][0], &sA[0][0]};
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, l16 = lane & 15;
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
+    const int PG = a.PG, nw = PG >> 4, S = a.S, npg = (int)(P / PG), Qt = a.Qt, Ri = (int)R;
+    const bool memw = wv >= nw;
+    const int mt = tid - 64 * nw;
+    int item = blockIdx.x;
+    const int seg = item % S;
+    item /= S;
+    const int pg = item % npg;
+    const int64_t bh = item / npg;
+    const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    const int pbase = pg * PG;
+    float* dst = a.part + (bh * npg + pg) * TR * N;
+
+    if constexpr (PAD > 0)
+        for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
+            sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+            sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+        }
+    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    __syncthreads();
+
+    if (memw) {
+        Stager<TI, NP, true, true, false> st;
+        st.load(a, k0, mt, b, h, g, pbase);
+        st.store(sm, a, 0, mt);
+        __syncthreads();
+        for (int k = k0; k < k1; ++k) {
+            const int buf = (k - k0) & 1;
+            if (k + 1 < k1) {
+                st.load(a, k + 1, mt, b, h, g, pbase);
+                st.store(sm, a, buf ^ 1, mt);
+            }
+            for (int w = 0; w < nw; ++w) __syncthreads();
+            copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ---- compute waves: state tiles D[p][n] of rows p0 .. p0 + 15
+    const int p0 = pbase + 16 * wv, xcol = 16 * wv;
+    f32x4 hs[NT];
+    {
+        const float* src = (S == 1) ? a.init : a.seg_in;
+        const int64_t off = (S == 1) ? bh * P * N : (bh * S + seg) * (int64_t)a.SF * P * N;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                hs[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
+        }
+    }
+    const int kr0 = (4 * q < Ri) ? 4 * q : 0;
+    __syncthreads();
+    for (int k = k0; k < k1; ++k) {
+        const int buf = (k - k0) & 1;
+        f32x4 z[2][NT];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int c = 0; c < NT; ++c) z[i][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < Qt; ++s) {
+            const int64_t t = (int64_t)k * Qt + s;
+            if (t >= T) break;
+            // decay and turn: h <- a R(theta) h
+            const float at = sA[buf][s];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                const int n = 16 * c + l16;
+                const float2 cs = (n < N) ? sCs[buf][s * NH + (n >> 1)] : make_float2(1.f, 0.f);
+                const float self = at * cs.x, part = (n & 1) ? at * cs.y : -at * cs.y;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float pv = swap_pair(hs[c][v]);
+                    hs[c][v] = fmaf(self, hs[c][v], part * pv);
+                }
+            }
+            const int row = s * Ri;
+            const int blk = row >> 4;
+            if constexpr (BF) {
+                // the rank-R write x (outer) B
+                s16x4 xa = tr_rows4(reinterpret_cast<const uint16_t*>(sX[buf]), LDX, row + kr0, xcol, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q + e >= Ri) xa[e] = 0;
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const s16x4 bb = tr_rows4(reinterpret_cast<const uint16_t*>(sB[buf]), LDB, row + kr0, 16 * c, lane);
+                    hs[c] = mma16(xa, bb, hs[c]);
+                }
+                // dC share: rows of this step, dy (k = p) times the state tiles
+                const s16x4 dya = step_rows<TI>(sDy[buf], LDX, blk, row, row + Ri, xcol, lane);
+                if (blk == 0) {
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) z[0][c] = mma16(dya, pack4_bf16(hs[c]), z[0][c]);
+                } else {
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) z[1][c] = mma16(dya, pack4_bf16(hs[c]), z[1][c]);
+                }
+            } else {
+                for (int j = 0; 4 * j < Ri; ++j) {
+                    const int r = 4 * j + q, rr = r < Ri ? r : 0;
+                    const float xv = r < Ri ? (float)sX[buf][(row + rr) * LDX + xcol + l16] : 0.f;
+#pragma unroll
+                    for (int c = 0; c < NT; ++c)
+                        hs[c] = mma4f(xv, (float)sB[buf][(row + rr) * LDB + 16 * c + l16], hs[c]);
+                }
+                const int m = 16 * blk + l16;
+                const bool mine = m >= row && m < row + Ri;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float dv = mine ? (float)sDy[buf][m * LDX + xcol + 4 * q + v] : 0.f;
+                    if (blk == 0) {
+#pragma unroll
+                        for (int c = 0; c < NT; ++c) z[0][c] = mma4f(dv, hs[c][v], z[0][c]);
+                    } else {
+#pragma unroll
+                        for (int c = 0; c < NT; ++c) z[1][c] = mma4f(dv, hs[c][v], z[1][c]);
+                    }
+                }
+            }
+        }
+        for (int w = 0; w < nw; ++w) {
+            if (wv == w) put_share<NT>(sZ, z, w == 0, lane);
+            __syncthreads();
+        }
+        copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+        __syncthreads();
+    }
+    if (seg == S - 1 && a.final_state) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n < N) a.final_state[bh * P * N + (int64_t)(p0 + 4 * q + v) * N + n] = hs[c][v];
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Backward walk (tiles and steps in reverse): the state gradient in both
+// layouts, Hp = D[p][n] (for dB) and Hn = D[n][p] (for dx). MODE 1: the
+// segment's own contribution at its left end (from a zero gradient), for the
+// carry; MODE 0: dx, the head's dB partial, the dy . x partial, dinit.
+// ------------------------------------------------------------------------
+template <typename TI, int NP, int MODE>
+__global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArgs a) {
+    constexpr bool OUT = MODE == 0;
+    using St = Stage<TI, NP, OUT, OUT, true>;
+    constexpr bool BF = sizeof(TI) == 2;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, NH = St::NH, ROWS = St::ROWS, PAD = St::PAD;
+    __shared__ __attribute__((aligned(16))) TI sX[2][OUT ? ROWS * LDX : 8];
+    __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sB[2][OUT ? ROWS * LDB : 8];
+    __shared__ __attribute__((aligned(16))) TI sC[2][ROWS * LDB];
+    __shared__ __attribute__((aligned(16))) float2 sCs[2][kTileRows * NH];
+    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) float sZ[OUT ? kTileRows * NP : 4];
+    __shared__ float sDd[kRowGroup / 16];
+    const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], &sC[0][0], &sCs[0][0], &sA[0][0]};
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, l16 = lane & 15;
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
+    const int PG = a.PG, nw = PG >> 4, S = a.S, npg = (int)(P / PG), Qt = a.Qt, Ri = (int)R;
+    const bool memw = wv >= nw;
+    const int mt = tid - 64 * nw;
+    int item = blockIdx.x;
+    const int seg = item % S;
+    item /= S;
+    const int pg = item % npg;
+    const int64_t bh = item / npg;
+    const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    const int pbase = pg * PG;
+    float* dst = OUT ? a.part + (bh * npg + pg) * TR * N : nullptr;
+
+    if constexpr (PAD > 0)
+        for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
+            if (OUT) sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+            sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+        }
+    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) {
+        if (OUT) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+        sC[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    }
+    __syncthreads();
+
+    if (memw) {
+        Stager<TI, NP, OUT, OUT, true> st;
+        if (k1 > k0) {
+            st.load(a, k1 - 1, mt, b, h, g, pbase);
+            st.store(sm, a, 0, mt);
+        }
+        __syncthreads();
+        for (int k = k1 - 1; k >= k0; --k) {
+            const int buf = (k1 - 1 - k) & 1;
+            if (k > k0) {
+                st.load(a, k - 1, mt, b, h, g, pbase);
+                st.store(sm, a, buf ^ 1, mt);
+            }
+            if constexpr (OUT) {
+                for (int w = 0; w < nw; ++w) __syncthreads();
+                copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+            }
+            __syncthreads();
+        }
+        __syncthreads();                           // the dy . x shares
+        return;
+    }
+
+    // ---- compute waves
+    const int p0 = pbase + 16 * wv, xcol = 16 * wv;
+    f32x4 hp[NT], hn[NT];                          // D[p][n] and D[n][p] tiles
+    {
+        const float* src = nullptr;
+        int64_t off = 0;
+        if (OUT) {
+            if (seg == S - 1) {
+                src = a.dfinal;
+                off = bh * P * N;
+            } else {
+                src = a.seg_in;
+                off = (bh * S + seg) * P * N;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                hp[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
+                const int nn = 16 * c + 4 * q + v;
+                hn[c][v] = (src && nn < N) ? src[off + (int64_t)(p0 + l16) * N + nn] : 0.f;
+            }
+        }
+    }
+    const int kr0 = (4 * q < Ri) ? 4 * q : 0;
+    const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
+    float dd = 0.f;                                // this lane's share of sum dy . x
+    __syncthreads();
+    for (int k = k1 - 1; k >= k0; --k) {
+        const int buf = (k1 - 1 - k) & 1;
+        f32x4 zb[2][OUT ? NT : 1], zx[2];
+        if constexpr (OUT) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                zx[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NT; ++c) zb[i][c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        for (int s = Qt - 1; s >= 0; --s) {
+            const int64_t t = (int64_t)k * Qt + s;
+            if (t >= T) continue;
+            const int row = s * Ri;
+            const int blk = row >> 4;
+            // the reads of step t: H += sum_r dy_{t,r} (outer) C_{t,r}
+            if constexpr (BF) {
+                s16x4 dyM = tr_rows4(reinterpret_cast<const uint16_t*>(sDy[buf]), LDX, row + kr0, xcol, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (4 * q + e >= Ri) dyM[e] = 0;
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    s16x4 cc = tr_rows4(reinterpret_cast<const uint16_t*>(sC[buf]), LDB, row + kr0, 16 * c, lane);
+                    hp[c] = mma16(dyM, cc, hp[c]);     // D[p][n]: A = dy^T (rows p), B = C
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (4 * q + e >= Ri) cc[e] = 0;
+                    hn[c] = mma16(cc, dyM, hn[c]);     // D[n][p]: A = C^T (rows n), B = dy
+                }
+            } else {
+                for (int j = 0; 4 * j < Ri; ++j) {
+                    const int r = 4 * j + q, rr = r < Ri ? r : 0;
+                    const float dv = r < Ri ? (float)sDy[buf][(row + rr) * LDX + xcol + l16] : 0.f;
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) {
+                        const float cv = r < Ri ? (float)sC[buf][(row + rr) * LDB + 16 * c + l16] : 0.f;
+                        hp[c] = mma4f(dv, cv, hp[c]);
+                        hn[c] = mma4f(cv, dv, hn[c]);
+                    }
+                }
+            }
+            if constexpr (OUT) {
+                // dx rows of step t: B (k = n) times Hn; dB share: x (k = p) times Hp
+                if constexpr (BF) {
+                    const s16x4 xs = step_rows<TI>(sX[buf], LDX, blk, row, row + Ri, xcol, lane);
+#pragma unroll
+                    for (int c = 0; c < NT; ++c) {
+                        const s16x4 bs = step_rows<TI>(sB[buf], LDB, blk, row, row + Ri, 16 * c, lane);
+                        if (blk == 0) {
+                            zx[0] = mma16(bs, pack4_bf16(hn[c]), zx[0]);
+                            zb[0][c] = mma16(xs, pack4_bf16(hp[c]), zb[0][c]);
+                        } else {
+                            zx[1] = mma16(bs, pack4_bf16(hn[c]), zx[1]);
+                            zb[1][c] = mma16(xs, pack4_bf16(hp[c]), zb[1][c]);
+                        }
+                    }
+                } else {
+                    const int m = 16 * blk + l16;
+                    const bool mine = m >= row && m < row + Ri;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float xv = mine ? (float)sX[buf][m * LDX + xcol + 4 * q + v] : 0.f;
+#pragma unroll
+                        for (int c = 0; c < NT; ++c) {
+                            const float bv = mine ? (float)sB[buf][m * LDB + 16 * c + 4 * q + v] : 0.f;
+                            if (blk == 0) {
+                                zx[0] = mma4f(bv, hn[c][v], zx[0]);
+                                zb[0][c] = mma4f(xv, hp[c][v], zb[0][c]);
+                            } else {
+                                zx[1] = mma4f(bv, hn[c][v], zx[1]);
+                                zb[1][c] = mma4f(xv, hp[c][v], zb[1][c]);
+                            }
+                        }
+                    }
+                }
+            }
+            // into step t - 1: H <- a_t R(theta_t)^T H
+            const float at = sA[buf][s];
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                const int n = 16 * c + l16;
+                const float2 cs = (n < N) ? sCs[buf][s * NH + (n >> 1)] : make_float2(1.f, 0.f);
+                const float self = at * cs.x, part = (n & 1) ? -at * cs.y : at * cs.y;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const float pv = swap_pair(hp[c][v]);
+                    hp[c][v] = fmaf(self, hp[c][v], part * pv);
+                }
+#pragma unroll
+                for (int v = 0; v < 4; v += 2) {
+                    const int nn = 16 * c + 4 * q + v;   // even: pair (nn, nn + 1) in this lane
+                    const float2 cp = (nn < N) ? sCs[buf][s * NH + (nn >> 1)] : make_float2(1.f, 0.f);
+                    const float e0 = hn[c][v], e1 = hn[c][v + 1];
+                    hn[c][v] = at * fmaf(cp.x, e0, cp.y * e1);
+                    hn[c][v + 1] = at * fmaf(cp.x, e1, -cp.y * e0);
+                }
+            }
+        }
+        if constexpr (OUT) {
+            // dx = zx + D dy for the tile's rows, this wave's 16 columns (dy and
+            // the dy . x sum from the fp32 dy)
+            const int64_t f0 = (int64_t)k * kTileRows;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * q + v;
+                    if (f0 + r < TR) {
+                        const int64_t o = ((b * TR + f0 + r) * H + h) * P + p0 + l16;
+                        const float dyv = a.dy[o];
+                        a.dx[o] = fmaf(Dh, dyv, zx[i][v]);
+                        dd = fmaf(dyv, to_f32(sX[buf][r * LDX + xcol + l16]), dd);
+                    }
+                }
+            for (int w = 0; w < nw; ++w) {
+                if (wv == w) put_share<NT>(sZ, zb, w == 0, lane);
+                __syncthreads();
+            }
+            copy_rows<NP>(sZ, dst, f0, TR, (int)N, tid, nthr);
+        }
+        __syncthreads();
+    }
+    // the state gradient at the segment's left end (after its first step's
+    // decay and turn): the carry's local term (MODE 1), or dinit (segment 0)
+    float* out = nullptr;
+    if (!OUT && seg > 0) out = a.seg_out + (bh * S + seg) * P * N;
+    if (OUT && seg == 0 && a.dinit) out = a.dinit + bh * P * N;
+    if (out) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n < N) out[(int64_t)(p0 + 4 * q + v) * N + n] = hp[c][v];
+        }
+    }
+    if constexpr (OUT) {
+        for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
+        if (lane == 0) sDd[wv] = dd;
+    }
+    __syncthreads();
+    if (OUT && tid == 0) {
+        float acc = 0.f;
+        for (int w = 0; w < nw; ++w) acc += sDd[w];
+        a.dDp[(bh * npg + pg) * S + seg] = acc;
+    }
+}
+
+// Per (batch, head, segment): Lambda = sum of da and Phi[k] = sum of theta over
+// the segment's steps (thread k < N/2: Phi[k]; thread N/2: Lambda).
+__global__ __launch_bounds__(128) void ssd_bwd_segsums(const float* __restrict__ da, const float* __restrict__ theta,
+                                                      float* __restrict__ sums, int64_t T, int64_t H, int64_t N,
+                                                      int S, int nsub, int Qt) {
+    const int64_t bh = blockIdx.x / S;
+    const int seg = blockIdx.x % S;
+    const int64_t b = bh / H, h = bh % H;
+    const int64_t t0 = ((int64_t)seg * nsub / S) * Qt, t1raw = ((int64_t)(seg + 1) * nsub / S) * Qt;
+    const int64_t t1 = t1raw < T ? t1raw : T;
+    const int k = threadIdx.x;
+    float acc = 0.f;
+    if (k < N / 2) {
+        if (theta)
+            for (int64_t t = t0; t < t1; ++t) acc += theta[((b * T + t) * H + h) * (N / 2) + k];
+    } else if (k == N / 2) {
+        for (int64_t t = t0; t < t1; ++t) acc += da[(b * T + t) * H + h];
+    }
+    if (k <= N / 2) sums[(bh * S + seg) * (N / 2 + 1) + k] = acc;
+}
+
+// Reverse carry, one thread per (p, state pair): c_{S-1} = dfinal (or 0);
+// c_s = e^{Lambda_{s+1}} R(Phi_{s+1})^T c_{s+1} + local_{s+1}, the gradient
+// entering segment s from the right, into slot s of seg_in.
+__global__ __launch_bounds__(256) void ssd_bwd_carry(const float* __restrict__ dfinal, const float* __restrict__ local,
+                                                    const float* __restrict__ sums, float* __restrict__ seg_in,
+                                                    int64_t P, int64_t N, int S) {
+    const int64_t bh = blockIdx.y;
+    const int64_t pair = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (pair >= P * (N / 2)) return;
+    const int64_t p = pair / (N / 2), kk = pair % (N / 2), off = p * N + 2 * kk;
+    float c0 = dfinal ? dfinal[bh * P * N + off] : 0.f, c1 = dfinal ? dfinal[bh * P * N + off + 1] : 0.f;
+    for (int s = S - 1; s >= 0; --s) {
+        if (s < S - 1) {
+            const float* sm = sums + (bh * S + s + 1) * (N / 2 + 1);
+            const float dec = __expf(sm[N / 2]);
+            float sn, cs;
+            sincosf(sm[kk], &sn, &cs);
+            const float* lo = local + (bh * S + s + 1) * P * N + off;
+            const float r0 = cs * c0 + sn * c1, r1 = -sn * c0 + cs * c1;
+            c0 = dec * r0 + lo[0];
+            c1 = dec * r1 + lo[1];
+        }
+        float* d = seg_in + (bh * S + s) * P * N + off;
+        d[0] = c0;
+        d[1] = c1;
+    }
+}
+
+// dB and dC of every group (the heads' and row groups' partials added in
+// order) and, per head and step, the inner products and pair cross products
+// of the decay and turn gradients. One workgroup per (batch, step); thread n.
+template <typename TI>
+__global__ __launch_bounds__(128) void ssd_bwd_reduce(const float* __restrict__ pC, const float* __restrict__ pB,
+                                                     const void* __restrict__ Bv, const void* __restrict__ Cv,
+                                                     float* __restrict__ dB, float* __restrict__ dC,
+                                                     float* __restrict__ hv, float* __restrict__ th,
+                                                     int64_t T, int64_t H, int64_t G, int64_t N, int64_t R, int npg,
+                                                     int rot) {
+    const int64_t bt = blockIdx.x, b = bt / T, t = bt % T;
+    const int n = threadIdx.x, lane = n & 63, wvi = n >> 6;
+    const int64_t TR = T * R, HG = H / G;
+    const TI* Bg = static_cast<const TI*>(Bv);
+    const TI* Cg = static_cast<const TI*>(Cv);
+    auto ld = [](const TI* p, int64_t i) -> float {
+        if constexpr (sizeof(TI) == 2) return __uint_as_float((uint32_t)p[i] << 16);
+        else return p[i];
+    };
+    __shared__ float sred[2][2];
+    for (int64_t g = 0; g < G; ++g) {
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t row = (b * TR + t * R + r);
+            const float bn = n < N ? ld(Bg, (row * G + g) * N + n) : 0.f;
+            const float cn = n < N ? ld(Cg, (row * G + g) * N + n) : 0.f;
+            float sb = 0.f, sc = 0.f;
+            for (int64_t hh = 0; hh < HG; ++hh) {
+                const int64_t h = g * HG + hh, bh = b * H + h;
+                float db = 0.f, dc = 0.f;
+                for (int pg = 0; pg < npg; ++pg) {
+                    const int64_t base = ((bh * npg + pg) * TR + t * R + r) * N + n;
+                    if (n < N) {
+                        db += pB[base];
+                        dc += pC[base];
+                    }
+                }
+                sb += db;
+                sc += dc;
+                // per head: C . dC - B . dB over n (and ranks), and the pair cross products
+                float v = cn * dc - bn * db;
+                for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+                if (lane == 0) sred[wvi][0] = v;
+                if (rot) {
+                    // lanes n (even) and n + 1: (dC_n C_n+1 - dC_n+1 C_n) + (dB_n B_n+1 - dB_n+1 B_n)
+                    const float dcn = __shfl_xor(dc, 1), cnn = __shfl_xor(cn, 1);
+                    const float dbn = __shfl_xor(db, 1), bnn = __shfl_xor(bn, 1);
+                    if ((n & 1) == 0 && n < N) {
+                        const float cr = (dc * cnn - dcn * cn) + (db * bnn - dbn * bn);
+                        float* tp = th + (((b * T + t) * H + h) * (N / 2) + n / 2);
+                        *tp = (r == 0 ? 0.f : *tp) + cr;
+                    }
+                }
+                __syncthreads();
+                if (n == 0) {
+                    float* hp = hv + (b * T + t) * H + h;
+                    *hp = (r == 0 ? 0.f : *hp) + sred[0][0] + sred[1][0];
+                }
+                __syncthreads();
+            }
+            if (n < N) {
+                dB[(row * G + g) * N + n] = sb;
+                dC[(row * G + g) * N + n] = sc;
+            }
+        }
+    }
+}
+
+// dda and dtheta: reverse cumulative sums over the steps of the per-step
+// terms, with the final state's terms at the last step; dD over the partials.
+// One workgroup per (batch, head): thread k < N/2 for dtheta[.., k], thread
+// N/2 for dda; the final-state inner product reduced by the whole group.
+__global__ __launch_bounds__(128) void ssd_bwd_cumsum(const float* __restrict__ hv, const float* __restrict__ th,
+                                                     const float* __restrict__ dfinal, const float* __restrict__ fin,
+                                                     const float* __restrict__ dDp, float* __restrict__ dda,
+                                                     float* __restrict__ dtheta, float* __restrict__ dD,
+                                                     int64_t B_, int64_t T, int64_t H, int64_t P, int64_t N, int nparts) {
+    const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
+    const int k = threadIdx.x;
+    __shared__ float sfin[2];
+    // <dfinal, final>
+    float v = 0.f;
+    if (dfinal)
+        for (int64_t i = k; i < P * N; i += blockDim.x) v += dfinal[bh * P * N + i] * fin[bh * P * N + i];
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    if ((k & 63) == 0) sfin[k >> 6] = v;
+    __syncthreads();
+    if (k < N / 2 && dtheta) {
+        float acc = 0.f;
+        if (dfinal)
+            for (int64_t p = 0; p < P; ++p) {
+                const int64_t o = bh * P * N + p * N + 2 * k;
+                acc += dfinal[o + 1] * fin[o] - dfinal[o] * fin[o + 1];
+            }
+        for (int64_t t = T - 1; t >= 0; --t) {
+            acc += th[((b * T + t) * H + h) * (N / 2) + k];
+            dtheta[((b * T + t) * H + h) * (N / 2) + k] = acc;
+        }
+    } else if (k == N / 2) {
+        float acc = sfin[0] + sfin[1];
+        for (int64_t t = T - 1; t >= 0; --t) {
+            acc += hv[(b * T + t) * H + h];
+            dda[(b * T + t) * H + h] = acc;
+        }
+    } else if (k == N / 2 + 1 && dD && b == 0) {
+        float acc = 0.f;
+        for (int64_t bb = 0; bb < B_; ++bb)
+            for (int i = 0; i < nparts; ++i) acc += dDp[(bb * H + h) * nparts + i];
+        dD[h] = acc;
+    }
+}
+
+template <typename TI>
+void* bwd_forward_np(int NP) {
+    switch (NP) {
+        case 32: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 32>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 64>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 128>);
+    }
+    return nullptr;
+}
+
+template <typename TI, int MODE>
+void* bwd_backward_np(int NP) {
+    switch (NP) {
+        case 32: return reinterpret_cast<void*>(&ssd_bwd_backward_kernel<TI, 32, MODE>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwd_backward_kernel<TI, 64, MODE>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwd_backward_kernel<TI, 128, MODE>);
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float* da, const void* B,
+                                   const void* C, const float* D, const float* init_state, int64_t R,
+                                   const float* theta, const float* dy, const float* dfinal, float* dx,
+                                   float* dda, float* dB, float* dC, float* dtheta, float* dinit, float* dD,
+                                   void* stream) {
+    if (!d || !x || !da || !B || !C || !dy || !dx || !dda || !dB || !dC) return SSD_ERR_NULL_ARG;
+    if ((theta == nullptr) != (dtheta == nullptr) || (D == nullptr) != (dD == nullptr)) return SSD_ERR_NULL_ARG;
+    ssd_status st = forward_shape_status(d, 1, R, theta != nullptr);
+    if (st != SSD_OK) return st;
+    if (d->dstate > 128) return SSD_ERR_UNSUPPORTED;
+    const int64_t b = d->batch, T = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+    const int64_t esz = d->in_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) || !aligned(dx, 16) ||
+        (init_state && !aligned(init_state, 16)) || (dfinal && !aligned(dfinal, 16)) ||
+        (dinit && !aligned(dinit, 16)) || (theta && !aligned(theta, 16)) || !aligned(da, 4) ||
+        !aligned(dda, 4) || !aligned(dB, 4) || !aligned(dC, 4) || (dtheta && !aligned(dtheta, 4)) ||
+        (D && !aligned(D, 4)) || (dD && !aligned(dD, 4)))
+        return SSD_ERR_UNSUPPORTED;
+    const Span outs[] = {span_of(dx, b * T * R * H * P * 4), span_of(dda, b * T * H * 4),
+                         span_of(dB, b * T * R * G * N * 4), span_of(dC, b * T * R * G * N * 4),
+                         dtheta ? span_of(dtheta, b * T * H * (N / 2) * 4) : Span{0, 0},
+                         dinit ? span_of(dinit, b * H * P * N * 4) : Span{0, 0},
+                         dD ? span_of(dD, H * 4) : Span{0, 0}};
+    const Span ins[] = {span_of(x, b * T * R * H * P * esz), span_of(da, b * T * H * 4),
+                        span_of(B, b * T * R * G * N * esz), span_of(C, b * T * R * G * N * esz),
+                        D ? span_of(D, H * 4) : Span{0, 0},
+                        init_state ? span_of(init_state, b * H * P * N * 4) : Span{0, 0},
+                        theta ? span_of(theta, b * T * H * (N / 2) * 4) : Span{0, 0},
+                        span_of(dy, b * T * R * H * P * 4),
+                        dfinal ? span_of(dfinal, b * H * P * N * 4) : Span{0, 0}};
+    for (int i = 0; i < 7; ++i) {
+        if (outs[i].hi == 0) continue;
+        for (int j = i + 1; j < 7; ++j)
+            if (outs[j].hi && overlap(outs[i], outs[j])) return SSD_ERR_ALIAS;
+        for (const Span& si : ins)
+            if (si.hi && overlap(outs[i], si)) return SSD_ERR_ALIAS;
+    }
+
+    // the forward's plan gives the segments (and, with more than one, the
+    // states entering them from its state passes)
+    const bool rot = theta != nullptr;
+    Plan pl;
+    size_t st_bytes = 0;
+    st = states_plan(d, R, rot, &pl, &st_bytes);
+    if (st != SSD_OK) return st;
+    const int NP = (int)pl.NP;
+    const bool bf = d->in_dtype == SSD_BF16;
+    void* kf = bf ? bwd_forward_np<uint16_t>(NP) : bwd_forward_np<float>(NP);
+    void* kb0 = bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
+    void* kb1 = bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
+    void* kr = bf ? reinterpret_cast<void*>(&ssd_bwd_reduce<uint16_t>) : reinterpret_cast<void*>(&ssd_bwd_reduce<float>);
+    if (!kf || !kb0 || !kb1) return SSD_ERR_UNSUPPORTED;
+    const int PG = (int)(P < kRowGroup ? P : kRowGroup), npg = (int)(P / PG);
+    const int S = pl.S;
+    const int64_t nwg = b * H * npg * S;
+    if (nwg > 0x7fffffff || b * T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+
+    // workspace: forward state passes | partial dC | partial dB | final state |
+    // per-step terms (hv, th) | dD partials | backward segment states, locals, sums
+    const size_t n_part = (size_t)(b * H * npg) * (size_t)(T * R * N);
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
+    const size_t o_states = take(st_bytes);
+    const size_t o_pC = take(n_part * 4), o_pB = take(n_part * 4);
+    const size_t o_fin = take((size_t)(b * H * P * N) * 4);
+    const size_t o_hv = take((size_t)(b * T * H) * 4);
+    const size_t o_th = take(rot ? (size_t)(b * T * H * (N / 2)) * 4 : 4);
+    const size_t o_dd = take((size_t)(b * H * npg * S) * 4);
+    const size_t o_segin = take(S > 1 ? (size_t)(b * H * S * P * N) * 4 : 4);
+    const size_t o_local = take(S > 1 ? (size_t)(b * H * S * P * N) * 4 : 4);
+    const size_t o_sums = take(S > 1 ? (size_t)(b * H * S * (N / 2 + 1)) * 4 : 4);
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    int entry = -1;
+    char* ws = static_cast<char*>(scratch_acquire(hs, off, &entry, kSlotBackward));
+    if (!ws) return SSD_ERR_HIP;
+    float* fin = reinterpret_cast<float*>(ws + o_fin);
+
+    BwdArgs ba;
+    memset(&ba, 0, sizeof(ba));
+    ba.x = x; ba.da = da; ba.B = B; ba.C = C; ba.theta = theta; ba.dy = dy; ba.D = D;
+    ba.init = init_state; ba.dfinal = dfinal; ba.dx = dx; ba.dinit = dinit;
+    ba.T = T; ba.H = H; ba.G = G; ba.N = N; ba.R = R; ba.P = P;
+    ba.PG = PG; ba.S = S; ba.SF = pl.SF; ba.nsub = pl.nsub; ba.Qt = pl.Qt;
+    const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + kMemWaves)));
+
+    // 1. forward walk: states from the forward's state passes, dC partials, final state
+    float* fws_state = nullptr;
+    ssd_status rs = states_launch(pl, rot, x, da, B, init_state, theta, ws + o_states, hs, &fws_state);
+    if (rs == SSD_OK) {
+        BwdArgs fa = ba;
+        fa.seg_in = fws_state;
+        fa.part = reinterpret_cast<float*>(ws + o_pC);
+        fa.final_state = fin;
+        void* kargs[] = {&fa};
+        if (hipLaunchKernel(kf, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+    }
+    // 2. backward state pass and reverse carry (more than one segment)
+    float* seg_in = reinterpret_cast<float*>(ws + o_segin);
+    if (rs == SSD_OK && S > 1) {
+        hipLaunchKernelGGL(ssd_bwd_segsums, dim3((unsigned)(b * H * S)), dim3(128), 0, hs, da, theta,
+                           reinterpret_cast<float*>(ws + o_sums), T, H, N, S, pl.nsub, pl.Qt);
+        if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+        if (rs == SSD_OK) {
+            BwdArgs la = ba;
+            la.seg_out = reinterpret_cast<float*>(ws + o_local);
+            void* kargs[] = {&la};
+            if (hipLaunchKernel(kb1, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        }
+        if (rs == SSD_OK) {
+            dim3 cg((unsigned)((P * (N / 2) + 255) / 256), (unsigned)(b * H));
+            hipLaunchKernelGGL(ssd_bwd_carry, cg, dim3(256), 0, hs, dfinal,
+                               reinterpret_cast<const float*>(ws + o_local),
+                               reinterpret_cast<const float*>(ws + o_sums), seg_in, P, N, S);
+            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+        }
+    }
+    // 3. backward walk: dx, dB partials, dD partials, dinit
+    if (rs == SSD_OK) {
+        BwdArgs oa = ba;
+        oa.seg_in = S > 1 ? seg_in : nullptr;
+        oa.part = reinterpret_cast<float*>(ws + o_pB);
+        oa.dDp = reinterpret_cast<float*>(ws + o_dd);
+        void* kargs[] = {&oa};
+        if (hipLaunchKernel(kb0, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+    }
+    // 4. group sums and per-step terms; 5. reverse cumulative sums
+    if (rs == SSD_OK) {
+        const float* pC = reinterpret_cast<const float*>(ws + o_pC);
+        const float* pB = reinterpret_cast<const float*>(ws + o_pB);
+        float* hv = reinterpret_cast<float*>(ws + o_hv);
+        float* th = reinterpret_cast<float*>(ws + o_th);
+        int64_t Tv = T, Hv = H, Gv = G, Nv = N, Rv = R;
+        int npgv = npg, rotv = rot ? 1 : 0;
+        void* kargs[] = {(void*)&pC, (void*)&pB, (void*)&B, (void*)&C, (void*)&dB, (void*)&dC, (void*)&hv,
+                         (void*)&th, (void*)&Tv, (void*)&Hv, (void*)&Gv, (void*)&Nv, (void*)&Rv, (void*)&npgv,
+                         (void*)&rotv};
+        if (hipLaunchKernel(kr, dim3((unsigned)(b * T)), dim3(128), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        if (rs == SSD_OK) {
+            hipLaunchKernelGGL(ssd_bwd_cumsum, dim3((unsigned)(b * H)), dim3(128), 0, hs, hv, th, dfinal, fin,
+                               reinterpret_cast<const float*>(ws + o_dd), dda, dtheta, dD, b, T, H, P, N, npg * S);
+            if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+        }
+    }
+    if (!scratch_release(entry) && rs == SSD_OK) rs = SSD_ERR_HIP;
+    return rs;
+}

@@ -43,7 +43,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // failure. *entry identifies it for scratch_release, which marks the end of
 // this call's use on the stream (defined in ssd_scan.hip). A call that runs
 // another entry point inside it keeps its own buffers in another slot.
-enum { kSlotWork = 0, kSlotExpand = 1, kSlotMoments = 2 };
+enum { kSlotWork = 0, kSlotExpand = 1, kSlotMoments = 2, kSlotBackward = 3 };
 void* scratch_acquire(hipStream_t stream, size_t bytes, int* entry, int slot = kSlotWork);
 bool scratch_release(int entry);
 

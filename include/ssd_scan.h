@@ -269,6 +269,51 @@ ssd_status ssd_state_moments(const ssd_dims *d, const void *x, const float *da, 
                              void *stream);
 
 /*
+ * Gradients of the scan ("mamba3/scan.py", verify(): the backward of the fast
+ * scan is checked against the token recurrence; burn-mamba
+ * "mamba3/moments.rs", module documentation: states recomputed in the
+ * backward rather than stored). For the recurrence of ssd_forward (no chunk
+ * length: the result does not depend on one), given dy = dL/dy and
+ * dfinal = dL/dfinal_state, with h_t the physical state after step t,
+ * a_t = exp(da_t) and H_t = dL/dh_t:
+ *
+ *   H_t   = a_{t+1} R(theta_{t+1})^T H_{t+1} + sum_r dy_{t,r} (outer) C_{t,r}
+ *           (H_{T-1} from dfinal)
+ *   dx[b,t,r,h,p] = sum_n H_t[p,n] B[b,t,r,g,n] + D[h] dy[b,t,r,h,p]
+ *   dB[b,t,r,g,n] = sum_{h in g} sum_p H_t[p,n] x[b,t,r,h,p]
+ *   dC[b,t,r,g,n] = sum_{h in g} sum_p dy[b,t,r,h,p] h_t[p,n]
+ *   dda[b,t,h]    = sum_{s >= t} sum_{p,n} H_s[p,n] (h_s - W_s)[p,n]
+ *                   (W_s the write of step s), as a reverse cumulative sum
+ *   dtheta[b,t,h,k] = the same sum for the turn of pair k (2-D cross products)
+ *   dinit[b,h]    = a_0 R(theta_0)^T H_0
+ *   dD[h]         = sum_{b,t,r,p} dy x
+ *
+ * Arguments: d, x, da, B, C, D, init_state, R, theta as ssd_forward_ex (same
+ * layouts, dtypes and alignment; no chunk length), plus
+ *   dy      [b, T, R, H, P] fp32, 16-byte aligned
+ *   dfinal  [b, H, P, N] fp32, 16-byte aligned, or NULL (zero)
+ *   dx      [b, T, R, H, P] fp32, 16-byte aligned
+ *   dda     [b, T, H] fp32
+ *   dB, dC  [b, T, R, G, N] fp32
+ *   dtheta  [b, T, H, N/2] fp32: required exactly when theta is given
+ *   dinit   [b, H, P, N] fp32, 16-byte aligned, or NULL (not wanted)
+ *   dD      [H] fp32: required exactly when D is given
+ * Every output is written in full (none accumulates into what it held).
+ * Envelope: as ssd_forward with dstate <= 128 (SSD_ERR_UNSUPPORTED beyond).
+ * Errors: SSD_ERR_NULL_ARG for a NULL required pointer or a dtheta/dD that
+ * does not match theta/D; SSD_ERR_ALIAS when an output overlaps an input or
+ * another output. Ownership and asynchrony as ssd_forward; scratch: the
+ * forward's segment states, per-head partial sums of dB and dC
+ * (2 b H T R N fp32) and the backward's segment states, in a separate
+ * per-(device, stream) buffer of the library.
+ */
+ssd_status ssd_backward(const ssd_dims *d, const void *x, const float *da, const void *B,
+                        const void *C, const float *D, const float *init_state, int64_t R,
+                        const float *theta, const float *dy, const float *dfinal, float *dx,
+                        float *dda, float *dB, float *dC, float *dtheta, float *dinit, float *dD,
+                        void *stream);
+
+/*
  * ssd_forward_ex for callers that cannot allocate device memory: code under
  * HIP graph capture, tight serving loops, and harnesses that forbid hipMalloc.
  * Same arguments, result and launch plan as ssd_forward_ex (bitwise the same

@@ -126,6 +126,20 @@ def make_inputs(shape: Shape, seed: int = 0) -> Inputs:
     return Inputs(shape, x.contiguous(), da, Bm.contiguous(), Cm.contiguous(), D, theta, init)
 
 
+def make_cotangents(shape: Shape, seed: int = 0, dfinal: bool = True):
+    """Seeded cotangents for the backward: (dy, dfinal or None), float32.
+
+    Their own CPU generator seeded with ``seed + 1000``, in this order:
+    dy ~ N(0,1) [b,T,R,H,P], then dfinal ~ N(0,1) [b,H,P,N].
+    """
+    b, T, H, P, N = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed + 1000)
+    dy = torch.randn((b, T, shape.mimo_rank, H, P), generator=g, dtype=torch.float32)
+    df = torch.randn((b, H, P, N), generator=g, dtype=torch.float32) if dfinal else None
+    return dy, df
+
+
 def small_shape(**kw) -> Shape:
     """A Shape with defaults suited to quick oracle/parity cases."""
     base = dict(batch=2, seqlen=37, nheads=3, headdim=16, dstate=32, ngroups=1,

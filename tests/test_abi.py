@@ -274,3 +274,32 @@ def test_state_moments_checks(lib):
     assert call_m(m2=X) == ssd.SSD_ERR_ALIAS
     assert call_m(m1=M2) == ssd.SSD_ERR_ALIAS
     assert call_m(theta=TH + 4) == ssd.SSD_ERR_UNSUPPORTED         # theta not 16-byte aligned
+
+
+def test_backward_checks(lib):
+    # host-side checks of ssd_backward (fake pointers, never dereferenced)
+    d = dims()
+    DY, DF, DX, DDA, DB, DC, DTH, DI, DDD = (0x10000000 * (i + 40) for i in range(9))
+
+    def call_b(**kw):
+        g = lambda k, v: kw[k] if k in kw else v
+        return ssd.ssd_backward(g("d", d), X, DA, BB, CC, g("D", None), H0, g("R", 1),
+                                g("theta", None), g("dy", DY), g("dfinal", DF), g("dx", DX),
+                                DDA, DB, DC, g("dtheta", None), g("dinit", DI), g("dD", None),
+                                None)
+    assert call_b(d=None) == ssd.SSD_ERR_NULL_ARG
+    assert call_b(dy=None) == ssd.SSD_ERR_NULL_ARG
+    assert call_b(dx=None) == ssd.SSD_ERR_NULL_ARG
+    assert call_b(theta=TH) == ssd.SSD_ERR_NULL_ARG                # theta without dtheta
+    assert call_b(dtheta=DTH) == ssd.SSD_ERR_NULL_ARG              # dtheta without theta
+    assert call_b(D=DD) == ssd.SSD_ERR_NULL_ARG                    # D without dD
+    assert call_b(dD=DDD) == ssd.SSD_ERR_NULL_ARG
+    assert call_b(d=dims(dstate=256)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_b(d=dims(headdim=48)) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_b(d=dims(nheads=3, ngroups=2)) == ssd.SSD_ERR_BAD_SHAPE
+    assert call_b(R=3) == ssd.SSD_ERR_UNSUPPORTED
+    assert call_b(dx=X) == ssd.SSD_ERR_ALIAS                       # dx over x
+    assert call_b(dx=DY) == ssd.SSD_ERR_ALIAS                      # dx over dy
+    assert call_b(dinit=DX) == ssd.SSD_ERR_ALIAS                   # two outputs overlap
+    assert call_b(dfinal=DF + 8) == ssd.SSD_ERR_UNSUPPORTED        # dfinal not 16-byte aligned
+    assert call_b(theta=TH + 4, dtheta=DTH) == ssd.SSD_ERR_UNSUPPORTED

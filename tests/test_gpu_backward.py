@@ -1,0 +1,131 @@
+"""Gradients of the scan on the GPU vs the float64 oracle (needs a gfx950 GPU).
+
+Bar: normwise max relative error ||out - ref||_inf / ||ref||_inf per output
+(dx, dda, dB, dC, dinit, dtheta, dD) within 1e-4 for fp32 inputs and 2e-2 for
+bf16 inputs (the contractions take dy and the state gradient in bf16 there).
+dda and dtheta are sums of per-step inner products that can cancel to zero
+(exactly so at T = 1 from a zero state), so their denominator is at least the
+size of those products, max over (b, t) of sum |C dC| + |B dB|.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _ssd():
+    import chunked_ssd_scan_amd as ssd
+    ssd.load_library()
+    return ssd
+
+
+def normwise(got, ref):
+    got, ref = np.asarray(got, dtype=np.float64), np.asarray(ref, dtype=np.float64)
+    return float(np.abs(got - ref).max() / max(np.abs(ref).max(), 1e-300))
+
+
+def run(inp, dy, df):
+    ssd = _ssd()
+    dev = _dev()
+    g = inp.to(dev)
+    out = ssd.backward(g.x, g.da, g.B, g.C, dy.to(dev), D=g.D, init_state=g.init_state,
+                       theta=g.theta, dfinal=None if df is None else df.to(dev))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def ref(inp, dy, df):
+    return oracle.ssd_backward(inp.x, inp.da, inp.B, inp.C, dy, inp.D, inp.init_state, inp.theta,
+                               df)
+
+
+def step_scale(inp, want):
+    C, B = inp.C.double().numpy(), inp.B.double().numpy()
+    per_step = (np.abs(C * want["dC"]) + np.abs(B * want["dB"])).sum(axis=(2, 3, 4))
+    return float(per_step.max())
+
+
+def compare(got, want, tol, label, inp):
+    assert set(got) == set(want), (sorted(got), sorted(want))
+    floor = step_scale(inp, want)
+    errs = {}
+    for k in want:
+        g, w = np.asarray(got[k], np.float64), np.asarray(want[k], np.float64)
+        den = max(np.abs(w).max(), floor if k in ("dda", "dtheta") else 0.0, 1e-300)
+        errs[k] = float(np.abs(g - w).max() / den)
+    print(f"{label}: " + " ".join(f"{k} {e:.2e}" for k, e in errs.items()) + f" (tol {tol:g})",
+          flush=True)
+    for k, e in errs.items():
+        assert e <= tol, (k, e)
+    return errs
+
+
+# (T, P, N, R, H, G, dtype, rotation, init, skip, dfinal)
+CASES = [
+    (1, 16, 16, 1, 2, 1, "f32", False, False, "none", False),
+    (1, 16, 16, 1, 2, 1, "f32", True, True, "randn", True),
+    (100, 16, 32, 2, 3, 1, "f32", True, True, "randn", True),
+    (97, 128, 64, 8, 2, 1, "f32", True, False, "randn", True),
+    (45, 64, 128, 1, 2, 2, "f32", True, True, "none", True),
+    (200, 32, 16, 16, 4, 2, "f32", False, True, "randn", False),
+    (333, 64, 128, 4, 2, 1, "bf16", True, True, "none", True),
+    (257, 32, 64, 1, 4, 2, "bf16", False, True, "randn", True),
+    (64, 64, 128, 16, 2, 1, "bf16", True, True, "randn", False),
+    (130, 128, 128, 2, 2, 1, "bf16", True, False, "none", True),
+]
+
+
+@pytest.mark.parametrize("T,P,N,R,H,G,dtype,rot,init,skip,dfin", CASES)
+def test_backward_cases(T, P, N, R, H, G, dtype, rot, init, skip, dfin):
+    shape = si.small_shape(seqlen=T, headdim=P, dstate=N, mimo_rank=R, nheads=H, ngroups=G,
+                           dtype=dtype, rotation=rot, init_state=init, skip=skip, dt_shift=3.0)
+    seed = T + 7 * R + N
+    inp = si.make_inputs(shape, seed=seed)
+    dy, df = si.make_cotangents(shape, seed=seed, dfinal=dfin)
+    compare(run(inp, dy, df), ref(inp, dy, df), TOL[dtype],
+            f"T{T} P{P} N{N} R{R} H{H} G{G} {dtype} rot={rot} init={init} D={skip} dfinal={dfin}",
+            inp)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_long_sequence_segments(dtype):
+    # few (batch, head) pairs and a long sequence: the plan splits it into
+    # segments, so both walks start from carried states (forward: the state
+    # passes; backward: the reverse state pass and its carry)
+    shape = si.small_shape(batch=1, seqlen=3000, nheads=2, headdim=64, dstate=128, mimo_rank=4,
+                           dtype=dtype, rotation=True, init_state=True, skip="randn", dt_shift=5.0)
+    inp = si.make_inputs(shape, seed=91)
+    dy, df = si.make_cotangents(shape, seed=91)
+    compare(run(inp, dy, df), ref(inp, dy, df), TOL[dtype], f"segments {dtype}", inp)
+
+
+def test_backward_in_place_and_deterministic():
+    ssd = _ssd()
+    dev = _dev()
+    shape = si.small_shape(seqlen=150, headdim=64, dstate=64, mimo_rank=2, nheads=2,
+                           rotation=True, init_state=True, skip="randn", dtype="bf16")
+    inp = si.make_inputs(shape, seed=92)
+    dy, df = si.make_cotangents(shape, seed=92)
+    first = run(inp, dy, df)
+    g = inp.to(dev)
+    out = {k: torch.full(v.shape, float("nan"), device=dev) for k, v in first.items()}
+    res = ssd.backward(g.x, g.da, g.B, g.C, dy.to(dev), D=g.D, init_state=g.init_state,
+                       theta=g.theta, dfinal=df.to(dev), out=out)
+    torch.cuda.synchronize()
+    for k, v in first.items():
+        assert res[k].data_ptr() == out[k].data_ptr()
+        assert np.array_equal(res[k].cpu().numpy(), v), k
