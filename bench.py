@@ -520,6 +520,128 @@ def moments_bench(args) -> dict:
     return out
 
 
+def backward_bytes(shape) -> int:
+    """Compulsory HBM bytes of the backward: x, B, C (input dtype), da, dy,
+    theta, D, init and dfinal read once; dx, dda, dB, dC, dtheta, dinit and
+    dD (fp32) written once."""
+    b, T, H, P, N, G, R = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, \
+        shape.ngroups, shape.mimo_rank
+    esz = 2 if shape.dtype == "bf16" else 4
+    xs, bs = b * T * R * H * P, b * T * R * G * N
+    rd = xs * esz + 2 * bs * esz + b * T * H * 4 + xs * 4 + b * H * P * N * 4
+    wr = xs * 4 + 2 * bs * 4 + b * T * H * 4 + b * H * P * N * 4
+    if shape.rotation:
+        rd += b * T * H * (N // 2) * 4
+        wr += b * T * H * (N // 2) * 4
+    if shape.init_state:
+        rd += b * H * P * N * 4
+    if shape.skip != "none":
+        rd += H * 4
+        wr += H * 4
+    return rd + wr
+
+
+def backward_flops(shape) -> int:
+    """Algorithmic flops of the backward: per (batch, step, head) five rank-R
+    contractions of a P x N state, 2 P N R each (the recomputed write
+    x B^T, dC = dy^T h, the state-gradient read dy C^T, dx = H B, dB = H^T x)."""
+    b, T, H, P, N, R = shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate, \
+        shape.mimo_rank
+    return 10 * b * T * H * P * N * R
+
+
+def backward_bench(args) -> dict:
+    """Gradients of the scan (dx, dda, dB, dC, dinit, dtheta, dD) on one layer shape."""
+    import statistics
+    import torch
+    import chunked_ssd_scan_amd as ssd
+    import ssd_inputs as si
+
+    shape = si.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    inp = si.make_inputs(shape, seed=0)
+    dy, df = si.make_cotangents(shape, seed=0)
+    g = inp.to(dev)
+    dyg, dfg = dy.to(dev), df.to(dev)
+    b, T, R, H, P = g.x.shape
+    N = shape.dstate
+    stream = torch.cuda.current_stream(dev)
+    out_t = {"dx": torch.empty(g.x.shape, device=dev), "dda": torch.empty((b, T, H), device=dev),
+             "dB": torch.empty(g.B.shape, device=dev), "dC": torch.empty(g.B.shape, device=dev),
+             "dinit": torch.empty((b, H, P, N), device=dev)}
+    if g.theta is not None:
+        out_t["dtheta"] = torch.empty((b, T, H, N // 2), device=dev)
+    if g.D is not None:
+        out_t["dD"] = torch.empty((H,), device=dev)
+
+    def step(walk_events=None):
+        ssd.backward(g.x, g.da, g.B, g.C, dyg, D=g.D, init_state=g.init_state, theta=g.theta,
+                     dfinal=dfg, out=out_t, stream=stream.cuda_stream)
+
+    nwarm = prewarm(step, args.prewarm)
+    wall = timed_region(step, args)
+    flush = torch.empty(FLUSH_BYTES // 4, device=dev)
+    ts = []
+    for i in range(args.calls):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del flush
+    call_ms = statistics.median(ts)
+    for k, v in out_t.items():
+        if not torch.isfinite(v).all():
+            raise RuntimeError(f"non-finite {k}")
+    nbytes, flops = backward_bytes(shape), backward_flops(shape)
+    achieved = nbytes / (call_ms * 1e-3) / 1e9
+    mfma_peak = MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    out = {
+        "metric": f"backward tokens/s + % of HBM roofline ({shape.name})",
+        "value": b * T * args.steps / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": shape.dtype,
+        "data": "synthetic (seeded; see ssd_inputs.make_inputs and make_cotangents)",
+        "config": {"workload": "backward " + shape.name, "batch": b, "seqlen": T, "nheads": H,
+                   "headdim": P, "dstate": N, "mimo_rank": R, "rotation": shape.rotation,
+                   "init_state": shape.init_state, "skip": shape.skip, "dfinal": True},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                     "mfma_frac": flops / (call_ms * 1e-3) / 1e12 / mfma_peak,
+                     "kernel_ms": call_ms, "kernel_ms_min": min(ts), "unit_timed": "whole call"},
+        "timing": {"prewarm_s": args.prewarm, "prewarm_calls": nwarm},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        bs = max(1, min(b, threads))
+        ts_tok = max(64, min(T, args.cpu_slices * 1024 // max(1, H * R)))
+        cut = lambda t: None if t is None else t[:bs, :ts_tok].contiguous()
+        x, da, Bm, Cm, th, dys = map(cut, (inp.x, inp.da, inp.B, inp.C, inp.theta, dy))
+        h0 = None if inp.init_state is None else inp.init_state[:bs].contiguous()
+        t1 = time.perf_counter()
+        oracle.ssd_backward(x, da, Bm, Cm, dys, inp.D, h0, th, df[:bs].contiguous(),
+                            nthreads=threads)
+        secs = time.perf_counter() - t1
+        used = min(threads, bs * shape.ngroups)
+        out["cpu_baseline"] = {"value": bs * ts_tok / secs, "unit": "tokens/s", "cores": used,
+                               "kind": "oracle", "cpu_model": cpu_model(),
+                               "sample": (f"batches 0..{bs - 1}, the first {ts_tok} of T={T} "
+                                          f"tokens, all {H} heads; {secs:.2f} s wall (the "
+                                          f"oracle runs one thread per (batch, group))")}
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -539,12 +661,14 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--segments", type=int, default=0)
     ap.add_argument("--block-slices", type=int, default=0)
-    ap.add_argument("--workload", choices=("ssd", "selective_scan", "trapezoid", "moments"),
+    ap.add_argument("--workload", choices=("ssd", "selective_scan", "trapezoid", "moments",
+                                           "backward"),
                     default="ssd",
                     help="ssd: the chunked SSD scan (the reported line); selective_scan: "
                          "the diagonal selective scan, b4 T4096 D512 N16 (--segments = chunks); "
                          "trapezoid: the Mamba-3 two-write forward on the MIMO layer shape; "
-                         "moments: its physical-frame state moments")
+                         "moments: its physical-frame state moments; backward: the gradients "
+                         "of the scan on workload --config")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (5 launches) for counter calibration")
     args = ap.parse_args()
@@ -579,6 +703,9 @@ def main() -> int:
         return 0
     if args.workload == "moments":
         print(json.dumps(moments_bench(args)), flush=True)
+        return 0
+    if args.workload == "backward":
+        print(json.dumps(backward_bench(args)), flush=True)
         return 0
 
     shape, inp, wall, tc, main_summary = ssd_workload(args.config, args, with_timed_region=True)

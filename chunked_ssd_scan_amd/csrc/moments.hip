@@ -34,14 +34,12 @@
 #include <string.h>
 
 #include "ssd_common.h"
+#include "ssd_step.h"
 
 namespace {
 
 using namespace ssd_detail;
-
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+using namespace ssd_step;
 
 constexpr int kTileRows = 32;        // fused rows staged per tile (32 / R steps)
 constexpr int kPadRows = 4;          // zero rows after a tile: reads past its last step
@@ -65,26 +63,6 @@ struct MomArgs {
 
 // upper-triangle block index of (a, b), a <= b < nt
 __host__ __device__ constexpr int ublk(int a, int b, int nt) { return a * nt - a * (a - 1) / 2 + (b - a); }
-
-// Four consecutive rows r0 .. r0 + 3 of column colbase + (lane % 16) of a
-// row-major bf16 LDS tile, for every lane: one transposed 8-byte read per lane
-// (lane s of a 16-lane group reads 4 elements of row r0 + s / 4 at column
-// colbase + 4 (s % 4)).
-__device__ __forceinline__ s16x4 tr_rows4(const uint16_t* tile, int ld, int r0, int colbase, int lane) {
-    const int s = lane & 15;
-    const uint16_t* p = tile + (r0 + (s >> 2)) * ld + colbase + 4 * (s & 3);
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-}
-
-__device__ __forceinline__ s16x4 pack4_bf16(f32x4 v) {
-    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-    return __builtin_bit_cast(s16x4, __builtin_convertvector(v, bf16x4));
-}
-
-// partner lane l ^ 1 (state n ^ 1 of the same rows): DPP quad_perm [1, 0, 3, 2]
-__device__ __forceinline__ float swap_pair(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));
-}
 
 template <typename TI, int NP>
 __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments_kernel(MomArgs a) {
@@ -240,7 +218,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 #pragma unroll
         for (int c = 0; c < NT; ++c) m1p[c] = 0.f;
 
-        constexpr float kInv2Pi = 0.15915494309189535f;
         // rows of one step hold the R ranks; the K slots 4q + e of the write
         // MFMA beyond R are zero. Lane groups with no rank read the step's
         // first rows.
