@@ -764,6 +764,32 @@ constexpr int tr_row_stride(int ncols) {
     return ncols + 16 / esz;
 }
 
+// Row stride (elements) of the rotating walk's B tile, which is read both by
+// row runs (as for tr_row_stride) and along rows as 8-byte halves of 16-byte
+// fragments (the head's C B^T blocks), and written that way: the smallest
+// stride whose row runs fall in distinct banks and whose byte stride is 8
+// modulo 16 (the class that serves row reads without bank conflicts, as for
+// c_row_stride).
+template <typename TI>
+constexpr int rot_b_row_stride(int ncols) {
+    constexpr int esz = (int)sizeof(TI);
+    const int row_dw = ncols * esz / 4;
+    for (int pad = 2; pad < 64; pad += 4) {
+        const int sdw = row_dw + pad;
+        bool used[64] = {};
+        bool ok = true;
+        for (int r = 0; r < 4 && ok; ++r)
+            for (int c = 0; c < 4 && ok; ++c)
+                for (int w = 0; w < 2 * (esz == 2 ? 1 : 2) && ok; ++w) {
+                    const int bank = (r * sdw + (8 * c * esz) / 4 + w) & 63;
+                    if (used[bank]) ok = false;
+                    used[bank] = true;
+                }
+        if (ok) return ncols + pad * 4 / esz;
+    }
+    return ncols + 8 / esz;
+}
+
 // Row stride (elements) of the per-head x tile of the grouped walk, read as
 // the x^T operand by row runs starting at 16-column slices: bf16 lanes of one
 // 16-lane group read 4 consecutive rows, 8 dwords each; fp32 lane groups read
@@ -907,13 +933,16 @@ constexpr int cols_max_heads(int W) { return W / 2 + 1; }
 constexpr int kRotEntries = 512;
 // row (one time step) of a memory wave's rotation table: per pair group of two
 // state pairs, the four rows of its 4x4 turning matrix (8 bytes each)
-constexpr int rot_row_stride(int NP) { return (NP / 4) * 4; }
+// (plus 4 entries, so that the rows of the four time steps a 16-lane group
+// reads start 8 banks apart)
+constexpr int rot_row_stride(int NP) { return (NP / 4) * 4 + 4; }
 
 template <typename TI, int NP, int W, bool ROT>
 constexpr int cols_lds_bytes(int mode) {
     constexpr int esz = (int)sizeof(TI), epu = 16 / esz, F = kRows, CW = 16 * W;
     constexpr int MH = ROT ? 1 : cols_max_heads(W);
-    constexpr int ldx = x_row_stride<TI>(CW), ldb = tr_row_stride<TI>(NP), ldc = c_row_stride<TI>(NP);
+    constexpr int ldx = x_row_stride<TI>(CW), ldc = c_row_stride<TI>(NP);
+    constexpr int ldb = ROT ? rot_b_row_stride<TI>(NP) : tr_row_stride<TI>(NP);
     constexpr int mbytes = (int)sizeof(typename MBlock<TI>::type);
     const int out = mode == 0;
     return 2 * (F * ldx + epu) * esz + 2 * (F * ldb + epu) * esz +
@@ -945,7 +974,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     constexpr int CW = 16 * W;                     // columns per workgroup
     constexpr int MH = ROT ? 1 : cols_max_heads(W);  // a rotating block is one head
     constexpr int LDX = x_row_stride<TI>(CW);
-    constexpr int LDB = tr_row_stride<TI>(NP);
+    constexpr int LDB = ROT ? rot_b_row_stride<TI>(NP) : tr_row_stride<TI>(NP);
     constexpr int LDC = c_row_stride<TI>(NP);      // rows 8 bytes off 16-byte alignment
     constexpr int LDY = y_row_stride(CW);
     constexpr int NTILE = NP / 16;
@@ -1301,7 +1330,9 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                     const uint4 r = make_uint4(pack_bf16x2(d0[0], d0[1]), pack_bf16x2(d0[2], d0[3]),
                                                pack_bf16x2(d1[0], d1[1]), pack_bf16x2(d1[2], d1[3]));
                     if (gmat == 0) {
-                        *reinterpret_cast<uint4*>(&sB[buf][grow * LDB + 32 * s + 8 * q]) = r;
+                        uint2* d = reinterpret_cast<uint2*>(&sB[buf][grow * LDB + 32 * s + 8 * q]);
+                        d[0] = make_uint2(r.x, r.y);
+                        d[1] = make_uint2(r.z, r.w);
                     } else {
                         uint2* d = reinterpret_cast<uint2*>(&sC[buf][grow * LDC + 32 * s + 8 * q]);
                         d[0] = make_uint2(r.x, r.y);
@@ -1505,8 +1536,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                     const frag c1 = ld8_a8<TI>(tC + (16 + l16) * LDC + 32 * s + 8 * q);
                     yacc[0] = O::mma(hA, c0, yacc[0]);
                     yacc[1] = O::mma(hA, c1, yacc[1]);
-                    const frag b0 = O::ld8(tB + l16 * LDB + 32 * s + 8 * q);
-                    const frag b1 = O::ld8(tB + (16 + l16) * LDB + 32 * s + 8 * q);
+                    const frag b0 = ld8_a8<TI>(tB + l16 * LDB + 32 * s + 8 * q);
+                    const frag b1 = ld8_a8<TI>(tB + (16 + l16) * LDB + 32 * s + 8 * q);
                     cb00 = O::mma(b0, c0, cb00);
                     cb01 = O::mma(b0, c1, cb01);
                     cb11 = O::mma(b1, c1, cb11);
