@@ -72,7 +72,7 @@ struct BwdArgs {
     float* final_state;     // forward walk: h_{T-1} [b,H,P,N]
     float* dDp;             // [b*H][npg][S] partial sums of dy . x
     int64_t T, H, G, N, R, P;
-    int PG, S, SF, nsub, Qt;
+    int PG, S, SF, nsub, Qt, log2R;
 };
 
 // Staging of one 32-row tile by the memory waves: x, dy (as TI), B, C rows,
@@ -111,7 +111,9 @@ __device__ __forceinline__ float to_f32(TI v) {
 }
 
 // One memory thread's staging of tile k into registers (load) and LDS (store).
-template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C>
+// RAW: no rotation staged, and da kept as is (the chunked walks scan it)
+// instead of as the decay exp(da).
+template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C, bool RAW = false>
 struct Stager {
     using St = Stage<TI, NP, WANT_X, WANT_B, WANT_C>;
     uint4 rx[WANT_X ? St::XR : 1];
@@ -168,7 +170,7 @@ struct Stager {
         for (int m = 0; m < St::THR; ++m) {
             const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (a.theta && st < a.Qt && t0 + st < T)
+            if (!RAW && a.theta && st < a.Qt && t0 + st < T)
                 v = *reinterpret_cast<const float4*>(a.theta + ((b * T + t0 + st) * H + h) * (N / 2) + c);
             rth[m] = v;
         }
@@ -216,7 +218,7 @@ struct Stager {
             }
         }
 #pragma unroll
-        for (int m = 0; m < St::THR; ++m) {
+        for (int m = 0; m < (RAW ? 0 : St::THR); ++m) {
             const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
             if (st < a.Qt) {
                 const float v4[4] = {rth[m].x, rth[m].y, rth[m].z, rth[m].w};
@@ -228,7 +230,7 @@ struct Stager {
                 }
             }
         }
-        if (mt < a.Qt) s.sA[buf * kTileRows + mt] = __expf(rda);
+        if (mt < a.Qt) s.sA[buf * kTileRows + mt] = RAW ? rda : __expf(rda);
     }
 };
 
@@ -692,6 +694,509 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
     }
 }
 
+// ------------------------------------------------------------------------
+// Chunked walks (bf16 inputs, no rotation, headdim <= 64): one workgroup per
+// (batch, head, segment) holds the whole head. Per 32-row tile, with cum_m the
+// inclusive sum of da over the tile's steps up to row m's step:
+//   forward:  dC  = e^{cum} o (dy h_in) + (G o L) B,   G = dy x^T (rows m, j)
+//             h  <- e^{cum_last} h + (w o x)^T B,     w_j = e^{cum_last - cum_j}
+//   backward: dx  = w o (B H^T) + (CB^T o L')^T dy     (CB^T)[j][m] = C_j . B_m
+//             dB  = w o (x H)   + (G^T o L'^T) C
+//             H  <- e^{cum_last} H + (e^{cum} o dy)^T C
+// with H the state gradient entering the tile from its right, L the causal
+// decay e^{cum_m - cum_j} (step(j) <= step(m)) and L' its transpose. The
+// 32 x 32 products are three 16 x 16 blocks each, built by one wave per block
+// and shared through LDS.
+// ------------------------------------------------------------------------
+
+constexpr int kLdm = 24;             // row stride of a staged 16 x 16 block (bf16)
+
+// inclusive sum over the tile rows of da at each step's first rank: lane m < 32
+// receives cum_m (rows past the tile's steps add zeros)
+__device__ __forceinline__ float tile_cum(const float* sDa, int Qt, int log2R, int lane) {
+    const int st = lane >> log2R;
+    float v = (lane < kTileRows && (lane & ((1 << log2R) - 1)) == 0 && st < Qt) ? sDa[st] : 0.f;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        const float u = __shfl_up(v, o);
+        if ((lane & 31) >= o) v += u;
+    }
+    return v;
+}
+
+// D[m][j] = sum_k ta[mrow0 + m][k] tb[jrow0 + j][k] over k < K: rows of two
+// row-major bf16 tiles dotted along their columns (K a multiple of 16)
+__device__ __forceinline__ f32x4 rows_dot(const uint16_t* ta, int lda, int mrow0, const uint16_t* tb, int ldb,
+                                          int jrow0, int K, int lane) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int l16 = lane & 15, q = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 16)
+        acc = mma16(row4(ta + (mrow0 + l16) * lda + k0 + 4 * q), row4(tb + (jrow0 + l16) * ldb + k0 + 4 * q), acc);
+    return acc;
+}
+
+// One 16 x 16 block (rows m in block mb, columns j in block jb) of a 32 x 32
+// tile matrix, decay-masked: upper (step(j) >= step(m), factor e^{cum_j - cum_m})
+// or lower (step(j) <= step(m), e^{cum_m - cum_j}); stored as bf16 [m][j].
+__device__ __forceinline__ void put_masked(uint16_t* dst, f32x4 acc, int mb, int jb, bool upper, float cum,
+                                           int log2R, int lane) {
+    const int l16 = lane & 15, q = lane >> 4;
+    const int j = 16 * jb + l16;
+    const float cj = __shfl(cum, j);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 16 * mb + 4 * q + v;
+        const float cm = __shfl(cum, m);
+        const int sm = m >> log2R, sj = j >> log2R;
+        float val = 0.f;
+        if (upper ? (sj >= sm) : (sj <= sm)) val = acc[v] * __expf(upper ? cj - cm : cm - cj);
+        dst[(4 * q + v) * kLdm + l16] = __builtin_bit_cast(uint16_t, (__bf16)val);
+    }
+}
+
+// the A operand of rows m = 16 mb + (lane % 16), columns 4 (lane / 16) .. + 3
+// of a staged block
+__device__ __forceinline__ s16x4 blk_rows(const uint16_t* blk, int lane) {
+    return row4(blk + (lane & 15) * kLdm + 4 * (lane >> 4));
+}
+
+// A compute wave's share of per-head rows [32][NP] in its own LDS slot, in
+// accumulator order: fragment (i, c, lane) holds rows 16 i + 4 q + v of
+// column 16 c + l16.
+template <int NT>
+__device__ __forceinline__ void put_frags(float4* slot, const f32x4 (&z)[2][NT], int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int c = 0; c < NT; ++c)
+            slot[(i * NT + c) * 64 + lane] = make_float4(z[i][c][0], z[i][c][1], z[i][c][2], z[i][c][3]);
+}
+
+// The nw slots added in wave order and stored as the rows f0 + r (< TR) of dst.
+template <int NT>
+__device__ __forceinline__ void sum_frags(const float4* slots, int nw, float* dst, int64_t f0, int64_t TR, int N,
+                                          int tid, int nthr) {
+    constexpr int NF = 2 * NT * 64;
+    for (int f = tid; f < NF; f += nthr) {
+        float4 acc = slots[f];
+        for (int w = 1; w < nw; ++w) {
+            const float4 v = slots[w * NF + f];
+            acc.x += v.x;
+            acc.y += v.y;
+            acc.z += v.z;
+            acc.w += v.w;
+        }
+        const int ln = f & 63, ic = f >> 6, i = ic / NT, c = ic % NT;
+        const int n = 16 * c + (ln & 15), r0 = 16 * i + 4 * (ln >> 4);
+        if (n >= N) continue;
+        const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            if (f0 + r0 + v < TR) dst[(f0 + r0 + v) * N + n] = av[v];
+    }
+}
+
+__device__ __forceinline__ s16x4 scale4(s16x4 v, float a, float b, float c, float d) {
+    f32x4 f = {__uint_as_float((uint32_t)(uint16_t)v[0] << 16) * a, __uint_as_float((uint32_t)(uint16_t)v[1] << 16) * b,
+               __uint_as_float((uint32_t)(uint16_t)v[2] << 16) * c, __uint_as_float((uint32_t)(uint16_t)v[3] << 16) * d};
+    return pack4_bf16(f);
+}
+
+// Forward direction: the head's dC partial rows and the final state.
+template <int NP>
+__global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArgs a) {
+    using TI = uint16_t;
+    using St = Stage<TI, NP, true, true, false>;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = St::ROWS, PAD = St::PAD;
+    __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
+    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) uint16_t sM[3][16 * kLdm];
+    __shared__ __attribute__((aligned(16))) float4 sZ[kRowGroup / 16][2 * NT * 64];
+    const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], nullptr, nullptr, &sA[0][0]};
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, l16 = lane & 15;
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
+    const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
+    const bool memw = wv >= nw;
+    const int mt = tid - 64 * nw;
+    const int seg = blockIdx.x % S;
+    const int64_t bh = blockIdx.x / S;
+    const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    float* dst = a.part + bh * TR * N;
+
+    for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
+        sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+        sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+    }
+    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    __syncthreads();
+
+    if (memw) {
+        Stager<TI, NP, true, true, false, true> st;
+        if (k1 > k0) {
+            st.load(a, k0, mt, b, h, g, 0);
+            st.store(sm, a, 0, mt);
+            if (k0 + 1 < k1) st.load(a, k0 + 1, mt, b, h, g, 0);
+        }
+        __syncthreads();
+        for (int k = k0; k < k1; ++k) {
+            const int buf = (k - k0) & 1;
+            if (k + 1 < k1) {
+                st.store(sm, a, buf ^ 1, mt);
+                if (k + 2 < k1) st.load(a, k + 2, mt, b, h, g, 0);
+            }
+            __syncthreads();                               // blocks built
+            __syncthreads();                               // shares in their slots
+            sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+        }
+        return;
+    }
+
+    const int p0 = 16 * wv;
+    f32x4 hs[NT];                                  // D[p][n]: rows p0 + 4q + v, column 16c + l16
+    {
+        const float* src = (S == 1) ? a.init : a.seg_in;
+        const int64_t off = (S == 1) ? bh * P * N : (bh * S + seg) * (int64_t)a.SF * P * N;
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                hs[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int k = k0; k < k1; ++k) {
+        const int buf = (k - k0) & 1;
+        const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
+        const uint16_t* tDy = reinterpret_cast<const uint16_t*>(sDy[buf]);
+        const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
+        const float cum = tile_cum(sA[buf], Qt, log2R, lane);
+        const float last = __shfl(cum, kTileRows - 1);
+        // G o L blocks (0,0), (1,0), (1,1): rows m of dy against rows j of x
+        for (int u = wv; u < 3; u += nw) {
+            const int mb = u == 0 ? 0 : 1, jb = u == 2 ? 1 : 0;
+            const f32x4 gacc = rows_dot(tDy, LDX, 16 * mb, tX, LDX, 16 * jb, (int)P, lane);
+            put_masked(sM[u], gacc, mb, jb, false, cum, log2R, lane);
+        }
+        __syncthreads();
+        // dC = e^{cum_m} (dy h_in) over this wave's p  +  (G o L) B on the wave's column tiles
+        f32x4 z[2][NT];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const s16x4 dya = row4(tDy + (16 * i + l16) * LDX + p0 + 4 * q);
+            float ein[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) ein[v] = __expf(__shfl(cum, 16 * i + 4 * q + v));
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                z[i][c] = mma16(dya, pack4_bf16(hs[c]), zero);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) z[i][c][v] *= ein[v];
+            }
+        }
+        const s16x4 m00 = blk_rows(sM[0], lane), m10 = blk_rows(sM[1], lane), m11 = blk_rows(sM[2], lane);
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            if (c % nw != wv) continue;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const s16x4 bb = tr_rows4(tB, LDB, 16 * kb + 4 * q, 16 * c, lane);
+                if (kb == 0) {
+                    z[0][c] = mma16(m00, bb, z[0][c]);
+                    z[1][c] = mma16(m10, bb, z[1][c]);
+                } else {
+                    z[1][c] = mma16(m11, bb, z[1][c]);
+                }
+            }
+        }
+        // h <- e^{last} h + (w o x)^T B
+        const float carry = __expf(last);
+        s16x4 xw[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const s16x4 xt = tr_rows4(tX, LDX, 16 * kb + 4 * q, p0, lane);
+            float w4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w4[e] = __expf(last - __shfl(cum, 16 * kb + 4 * q + e));
+            xw[kb] = scale4(xt, w4[0], w4[1], w4[2], w4[3]);
+        }
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hs[c][v] *= carry;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                hs[c] = mma16(xw[kb], tr_rows4(tB, LDB, 16 * kb + 4 * q, 16 * c, lane), hs[c]);
+        }
+        put_frags<NT>(sZ[wv], z, lane);
+        __syncthreads();
+        sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+    }
+    if (seg == S - 1 && a.final_state) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n < N) a.final_state[bh * P * N + (int64_t)(p0 + 4 * q + v) * N + n] = hs[c][v];
+        }
+    }
+}
+
+// Backward direction (tiles in reverse). MODE 1: only the state gradient, from
+// zero, to the segment's left end (the carry's local term); MODE 0: dx, the
+// head's dB partial, the dy . x partial and dinit.
+template <int NP, int MODE>
+__global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdArgs a) {
+    using TI = uint16_t;
+    constexpr bool OUT = MODE == 0;
+    using St = Stage<TI, NP, OUT, OUT, true>;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = St::ROWS, PAD = St::PAD;
+    __shared__ __attribute__((aligned(16))) TI sX[2][OUT ? ROWS * LDX : 8];
+    __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
+    __shared__ __attribute__((aligned(16))) TI sB[2][OUT ? ROWS * LDB : 8];
+    __shared__ __attribute__((aligned(16))) TI sC[2][ROWS * LDB];
+    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) uint16_t sM[OUT ? 6 : 1][16 * kLdm];
+    __shared__ __attribute__((aligned(16))) float4 sZ[OUT ? kRowGroup / 16 : 1][OUT ? 2 * NT * 64 : 1];
+    __shared__ float sDd[kRowGroup / 16];
+    const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], &sC[0][0], nullptr, &sA[0][0]};
+
+    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int q = lane >> 4, l16 = lane & 15;
+    const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
+    const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
+    const bool memw = wv >= nw;
+    const int mt = tid - 64 * nw;
+    const int seg = blockIdx.x % S;
+    const int64_t bh = blockIdx.x / S;
+    const int64_t b = bh / H, h = bh % H, g = h / (H / G);
+    const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    float* dst = OUT ? a.part + bh * TR * N : nullptr;
+
+    for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
+        if (OUT) sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+        sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
+    }
+    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) {
+        if (OUT) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+        sC[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    }
+    __syncthreads();
+
+    if (memw) {
+        Stager<TI, NP, OUT, OUT, true, true> st;
+        if (k1 > k0) {
+            st.load(a, k1 - 1, mt, b, h, g, 0);
+            st.store(sm, a, 0, mt);
+            if (k1 - 2 >= k0) st.load(a, k1 - 2, mt, b, h, g, 0);
+        }
+        __syncthreads();
+        for (int k = k1 - 1; k >= k0; --k) {
+            const int buf = (k1 - 1 - k) & 1;
+            if (k > k0) {
+                st.store(sm, a, buf ^ 1, mt);
+                if (k - 2 >= k0) st.load(a, k - 2, mt, b, h, g, 0);
+            }
+            __syncthreads();                                   // blocks built / tile walked
+            if constexpr (OUT) {
+                __syncthreads();                               // shares in their slots
+                sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+            }
+        }
+        __syncthreads();                                       // the dy . x shares
+        return;
+    }
+
+    const int p0 = 16 * wv;
+    f32x4 hp[NT], hn[NT];                          // D[p][n] and D[n][p]
+    {
+        const float* src = nullptr;
+        int64_t off = 0;
+        if (OUT) {
+            if (seg == S - 1) {
+                src = a.dfinal;
+                off = bh * P * N;
+            } else {
+                src = a.seg_in;
+                off = (bh * S + seg) * P * N;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                hp[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
+                const int nn = 16 * c + 4 * q + v;
+                hn[c][v] = (OUT && src && nn < N) ? src[off + (int64_t)(p0 + l16) * N + nn] : 0.f;
+            }
+        }
+    }
+    const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
+    float dd = 0.f;
+    __syncthreads();
+    for (int k = k1 - 1; k >= k0; --k) {
+        const int buf = (k1 - 1 - k) & 1;
+        const uint16_t* tDy = reinterpret_cast<const uint16_t*>(sDy[buf]);
+        const uint16_t* tC = reinterpret_cast<const uint16_t*>(sC[buf]);
+        const float cum = tile_cum(sA[buf], Qt, log2R, lane);
+        const float last = __shfl(cum, kTileRows - 1);
+        if constexpr (OUT) {
+            const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
+            const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
+            // the tile's fp32 dy (for D dy and the dy . x sum), loaded now, used last
+            const int64_t f0 = (int64_t)k * kTileRows;
+            float dyr[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * q + v;
+                    dyr[i][v] = (f0 + r < TR) ? a.dy[((b * TR + f0 + r) * H + h) * P + p0 + l16] : 0.f;
+                }
+            // upper blocks (0,0), (0,1), (1,1): CB' = B_m . C_j (jobs 0-2) and
+            // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
+            for (int u = wv; u < 6; u += nw) {
+                const int ub = u % 3, mb = ub == 2 ? 1 : 0, jb = ub == 0 ? 0 : 1;
+                const f32x4 acc = u < 3 ? rows_dot(tB, LDB, 16 * mb, tC, LDB, 16 * jb, (int)NP, lane)
+                                        : rows_dot(tX, LDX, 16 * mb, tDy, LDX, 16 * jb, (int)P, lane);
+                put_masked(sM[u], acc, mb, jb, true, cum, log2R, lane);
+            }
+            __syncthreads();
+            float wr[2][4];                        // e^{last - cum_m}, rows 16 i + 4 q + v
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) wr[i][v] = __expf(last - __shfl(cum, 16 * i + 4 * q + v));
+            // dx = w o (B H^T) + (CB' o L') dy;  dB share = w o (x H) (+ (G' o L') C on the wave's tiles)
+            f32x4 zx[2], zb[2][NT];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                zx[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+                const s16x4 xs = row4(tX + (16 * i + l16) * LDX + p0 + 4 * q);
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    const s16x4 bs = row4(tB + (16 * i + l16) * LDB + 16 * c + 4 * q);
+                    zx[i] = mma16(bs, pack4_bf16(hn[c]), zx[i]);
+                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                    zb[i][c] = mma16(xs, pack4_bf16(hp[c]), zero);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) zb[i][c][v] *= wr[i][v];
+                }
+#pragma unroll
+                for (int v = 0; v < 4; ++v) zx[i][v] *= wr[i][v];
+            }
+            {
+                const s16x4 c00 = blk_rows(sM[0], lane), c01 = blk_rows(sM[1], lane), c11 = blk_rows(sM[2], lane);
+                const s16x4 d0 = tr_rows4(tDy, LDX, 4 * q, p0, lane), d1 = tr_rows4(tDy, LDX, 16 + 4 * q, p0, lane);
+                zx[0] = mma16(c00, d0, zx[0]);
+                zx[0] = mma16(c01, d1, zx[0]);
+                zx[1] = mma16(c11, d1, zx[1]);
+                const s16x4 g00 = blk_rows(sM[3], lane), g01 = blk_rows(sM[4], lane), g11 = blk_rows(sM[5], lane);
+#pragma unroll
+                for (int c = 0; c < NT; ++c) {
+                    if (c % nw != wv) continue;
+                    const s16x4 cc0 = tr_rows4(tC, LDB, 4 * q, 16 * c, lane);
+                    const s16x4 cc1 = tr_rows4(tC, LDB, 16 + 4 * q, 16 * c, lane);
+                    zb[0][c] = mma16(g00, cc0, zb[0][c]);
+                    zb[0][c] = mma16(g01, cc1, zb[0][c]);
+                    zb[1][c] = mma16(g11, cc1, zb[1][c]);
+                }
+            }
+            // dx rows
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * q + v;
+                    if (f0 + r < TR) {
+                        const int64_t o = ((b * TR + f0 + r) * H + h) * P + p0 + l16;
+                        a.dx[o] = fmaf(Dh, dyr[i][v], zx[i][v]);
+                        dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
+                    }
+                }
+            // H <- e^{last} H + (e^{cum} o dy)^T C, both layouts
+            const float carry = __expf(last);
+            s16x4 ed[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
+                float e4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
+                ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
+            }
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    hp[c][v] *= carry;
+                    hn[c][v] *= carry;
+                }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const s16x4 cc = tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane);
+                    hp[c] = mma16(ed[kb], cc, hp[c]);
+                    hn[c] = mma16(cc, ed[kb], hn[c]);
+                }
+            }
+            put_frags<NT>(sZ[wv], zb, lane);
+        } else {
+            const float carry = __expf(last);
+            s16x4 ed[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
+                float e4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
+                ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
+            }
+#pragma unroll
+            for (int c = 0; c < NT; ++c) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) hp[c][v] *= carry;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    hp[c] = mma16(ed[kb], tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane), hp[c]);
+            }
+        }
+        __syncthreads();                           // shares in their slots (MODE 1: tile walked)
+        if constexpr (OUT) sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+    }
+    float* out = nullptr;
+    if (!OUT && seg > 0) out = a.seg_out + (bh * S + seg) * P * N;
+    if (OUT && seg == 0 && a.dinit) out = a.dinit + bh * P * N;
+    if (out) {
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+            const int n = 16 * c + l16;
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (n < N) out[(int64_t)(p0 + 4 * q + v) * N + n] = hp[c][v];
+        }
+    }
+    if constexpr (OUT) {
+        for (int o = 32; o >= 1; o >>= 1) dd += __shfl_xor(dd, o);
+        if (lane == 0) sDd[wv] = dd;
+    }
+    __syncthreads();
+    if (OUT && tid == 0) {
+        float acc = 0.f;
+        for (int w = 0; w < nw; ++w) acc += sDd[w];
+        a.dDp[bh * S + seg] = acc;
+    }
+}
+
 // Per (batch, head, segment): Lambda = sum of da and Phi[k] = sum of theta over
 // the segment's steps (thread k < N/2: Phi[k]; thread N/2: Lambda).
 __global__ __launch_bounds__(128) void ssd_bwd_segsums(const float* __restrict__ da, const float* __restrict__ theta,
@@ -808,47 +1313,85 @@ __global__ __launch_bounds__(128) void ssd_bwd_reduce(const float* __restrict__ 
     }
 }
 
-// dda and dtheta: reverse cumulative sums over the steps of the per-step
-// terms, with the final state's terms at the last step; dD over the partials.
-// One workgroup per (batch, head): thread k < N/2 for dtheta[.., k], thread
-// N/2 for dda; the final-state inner product reduced by the whole group.
-__global__ __launch_bounds__(128) void ssd_bwd_cumsum(const float* __restrict__ hv, const float* __restrict__ th,
-                                                     const float* __restrict__ dfinal, const float* __restrict__ fin,
-                                                     const float* __restrict__ dDp, float* __restrict__ dda,
-                                                     float* __restrict__ dtheta, float* __restrict__ dD,
-                                                     int64_t B_, int64_t T, int64_t H, int64_t P, int64_t N, int nparts) {
+// dda and dtheta are reverse cumulative sums over the steps of the per-step
+// terms (column k < N/2: the turn of pair k; column N/2: the decay), plus the
+// final state's terms at the last step. Three kernels: the final state's terms
+// and dD (per (batch, head)), the sums of chunks of kScanChunk steps, and the
+// scan of each chunk from the sums of the chunks after it.
+constexpr int kScanChunk = 256;
+
+__global__ __launch_bounds__(128) void ssd_bwd_final_terms(const float* __restrict__ dfinal,
+                                                          const float* __restrict__ fin,
+                                                          const float* __restrict__ dDp, float* __restrict__ ft,
+                                                          float* __restrict__ dD, int64_t B_, int64_t H, int64_t P,
+                                                          int64_t N, int nparts) {
     const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
-    const int k = threadIdx.x;
+    const int k = threadIdx.x, nc = (int)(N / 2 + 1);
     __shared__ float sfin[2];
-    // <dfinal, final>
     float v = 0.f;
     if (dfinal)
         for (int64_t i = k; i < P * N; i += blockDim.x) v += dfinal[bh * P * N + i] * fin[bh * P * N + i];
     for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
     if ((k & 63) == 0) sfin[k >> 6] = v;
     __syncthreads();
-    if (k < N / 2 && dtheta) {
+    if (k < N / 2) {
         float acc = 0.f;
         if (dfinal)
             for (int64_t p = 0; p < P; ++p) {
                 const int64_t o = bh * P * N + p * N + 2 * k;
                 acc += dfinal[o + 1] * fin[o] - dfinal[o] * fin[o + 1];
             }
-        for (int64_t t = T - 1; t >= 0; --t) {
-            acc += th[((b * T + t) * H + h) * (N / 2) + k];
-            dtheta[((b * T + t) * H + h) * (N / 2) + k] = acc;
-        }
+        ft[bh * nc + k] = acc;
     } else if (k == N / 2) {
-        float acc = sfin[0] + sfin[1];
-        for (int64_t t = T - 1; t >= 0; --t) {
-            acc += hv[(b * T + t) * H + h];
-            dda[(b * T + t) * H + h] = acc;
-        }
+        ft[bh * nc + k] = sfin[0] + sfin[1];
     } else if (k == N / 2 + 1 && dD && b == 0) {
         float acc = 0.f;
         for (int64_t bb = 0; bb < B_; ++bb)
             for (int i = 0; i < nparts; ++i) acc += dDp[(bb * H + h) * nparts + i];
         dD[h] = acc;
+    }
+}
+
+// the value of column k at step t (k < N/2: th, k == N/2: hv)
+__device__ __forceinline__ float step_term(const float* hv, const float* th, int64_t b, int64_t t, int64_t T,
+                                           int64_t H, int64_t h, int64_t N, int k) {
+    return k < N / 2 ? th[((b * T + t) * H + h) * (N / 2) + k] : hv[(b * T + t) * H + h];
+}
+
+// thread -> (batch-head, chunk, column k0 + i): columns fastest, then chunks
+__global__ __launch_bounds__(128) void ssd_bwd_chunk_sums(const float* __restrict__ hv, const float* __restrict__ th,
+                                                         float* __restrict__ csum, int64_t T, int64_t H, int64_t N,
+                                                         int nchunk, int k0, int64_t items) {
+    const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= items) return;
+    const int nc = (int)(N / 2 + 1), ncols = nc - k0;
+    const int k = k0 + (int)(it % ncols), ch = (int)((it / ncols) % nchunk);
+    const int64_t bh = it / ((int64_t)ncols * nchunk), b = bh / H, h = bh % H;
+    const int64_t t0 = (int64_t)ch * kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t t = t0; t < t1; ++t) acc += step_term(hv, th, b, t, T, H, h, N, k);
+    csum[(bh * nchunk + ch) * nc + k] = acc;
+}
+
+__global__ __launch_bounds__(128) void ssd_bwd_chunk_scan(const float* __restrict__ hv, const float* __restrict__ th,
+                                                         const float* __restrict__ csum, const float* __restrict__ ft,
+                                                         float* __restrict__ dda, float* __restrict__ dtheta,
+                                                         int64_t T, int64_t H, int64_t N, int nchunk, int k0,
+                                                         int64_t items) {
+    const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= items) return;
+    const int nc = (int)(N / 2 + 1), ncols = nc - k0;
+    const int k = k0 + (int)(it % ncols), ch = (int)((it / ncols) % nchunk);
+    const int64_t bh = it / ((int64_t)ncols * nchunk), b = bh / H, h = bh % H;
+    float acc = ft[bh * nc + k];
+    for (int c = nchunk - 1; c > ch; --c) acc += csum[(bh * nchunk + c) * nc + k];
+    const int64_t t0 = (int64_t)ch * kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
+    float* out = k < N / 2 ? dtheta : dda;
+    for (int64_t t = t1 - 1; t >= t0; --t) {
+        acc += step_term(hv, th, b, t, T, H, h, N, k);
+        if (k < N / 2) out[((b * T + t) * H + h) * (N / 2) + k] = acc;
+        else out[(b * T + t) * H + h] = acc;
     }
 }
 
@@ -858,6 +1401,25 @@ void* bwd_forward_np(int NP) {
         case 32: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 32>);
         case 64: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 64>);
         case 128: return reinterpret_cast<void*>(&ssd_bwd_forward_kernel<TI, 128>);
+    }
+    return nullptr;
+}
+
+void* bwdc_forward_np(int NP) {
+    switch (NP) {
+        case 32: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<32>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<64>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<128>);
+    }
+    return nullptr;
+}
+
+template <int MODE>
+void* bwdc_backward_np(int NP) {
+    switch (NP) {
+        case 32: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<32, MODE>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<64, MODE>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<128, MODE>);
     }
     return nullptr;
 }
@@ -921,15 +1483,21 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     if (st != SSD_OK) return st;
     const int NP = (int)pl.NP;
     const bool bf = d->in_dtype == SSD_BF16;
-    void* kf = bf ? bwd_forward_np<uint16_t>(NP) : bwd_forward_np<float>(NP);
-    void* kb0 = bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
-    void* kb1 = bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
+    // bf16 without rotation and a whole head per workgroup: the chunked walks;
+    // otherwise the step-by-step walks
+    const bool chunked = bf && !rot && P <= kRowGroup;
+    void* kf = chunked ? bwdc_forward_np(NP) : bf ? bwd_forward_np<uint16_t>(NP) : bwd_forward_np<float>(NP);
+    void* kb0 = chunked ? bwdc_backward_np<0>(NP) : bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
+    void* kb1 = chunked ? bwdc_backward_np<1>(NP) : bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
     void* kr = bf ? reinterpret_cast<void*>(&ssd_bwd_reduce<uint16_t>) : reinterpret_cast<void*>(&ssd_bwd_reduce<float>);
     if (!kf || !kb0 || !kb1) return SSD_ERR_UNSUPPORTED;
     const int PG = (int)(P < kRowGroup ? P : kRowGroup), npg = (int)(P / PG);
+    if (chunked && npg != 1) return SSD_ERR_UNSUPPORTED;
     const int S = pl.S;
     const int64_t nwg = b * H * npg * S;
     if (nwg > 0x7fffffff || b * T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if ((b * H * ((T + kScanChunk - 1) / kScanChunk) * (N / 2 + 1) + 127) / 128 > 0x7fffffff)
+        return SSD_ERR_UNSUPPORTED;
 
     // workspace: forward state passes | partial dC | partial dB | final state |
     // per-step terms (hv, th) | dD partials | backward segment states, locals, sums
@@ -945,6 +1513,9 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     const size_t o_segin = take(S > 1 ? (size_t)(b * H * S * P * N) * 4 : 4);
     const size_t o_local = take(S > 1 ? (size_t)(b * H * S * P * N) * 4 : 4);
     const size_t o_sums = take(S > 1 ? (size_t)(b * H * S * (N / 2 + 1)) * 4 : 4);
+    const int64_t nchunks = (T + kScanChunk - 1) / kScanChunk;
+    const size_t o_ft = take((size_t)(b * H * (N / 2 + 1)) * 4);
+    const size_t o_csum = take((size_t)(b * H * nchunks * (N / 2 + 1)) * 4);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     int entry = -1;
     char* ws = static_cast<char*>(scratch_acquire(hs, off, &entry, kSlotBackward));
@@ -956,7 +1527,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     ba.x = x; ba.da = da; ba.B = B; ba.C = C; ba.theta = theta; ba.dy = dy; ba.D = D;
     ba.init = init_state; ba.dfinal = dfinal; ba.dx = dx; ba.dinit = dinit;
     ba.T = T; ba.H = H; ba.G = G; ba.N = N; ba.R = R; ba.P = P;
-    ba.PG = PG; ba.S = S; ba.SF = pl.SF; ba.nsub = pl.nsub; ba.Qt = pl.Qt;
+    ba.PG = PG; ba.S = S; ba.SF = pl.SF; ba.nsub = pl.nsub; ba.Qt = pl.Qt; ba.log2R = pl.log2R;
     const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + kMemWaves)));
 
     // 1. forward walk: states from the forward's state passes, dC partials, final state
@@ -1011,9 +1582,20 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
                          (void*)&th, (void*)&Tv, (void*)&Hv, (void*)&Gv, (void*)&Nv, (void*)&Rv, (void*)&npgv,
                          (void*)&rotv};
         if (hipLaunchKernel(kr, dim3((unsigned)(b * T)), dim3(128), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        // final-state terms and dD; chunk sums; chunk scans (columns from k0:
+        // all pairs with rotation, only the decay column without)
+        const int nc = (int)(N / 2 + 1), nchunk = (int)((T + kScanChunk - 1) / kScanChunk);
+        const int k0 = rot ? 0 : (int)(N / 2);
+        float* ft = reinterpret_cast<float*>(ws + o_ft);
+        float* csum = reinterpret_cast<float*>(ws + o_csum);
         if (rs == SSD_OK) {
-            hipLaunchKernelGGL(ssd_bwd_cumsum, dim3((unsigned)(b * H)), dim3(128), 0, hs, hv, th, dfinal, fin,
-                               reinterpret_cast<const float*>(ws + o_dd), dda, dtheta, dD, b, T, H, P, N, npg * S);
+            hipLaunchKernelGGL(ssd_bwd_final_terms, dim3((unsigned)(b * H)), dim3(128), 0, hs, dfinal, fin,
+                               reinterpret_cast<const float*>(ws + o_dd), ft, dD, b, H, P, N, npg * S);
+            const int64_t items = b * H * nchunk * (int64_t)(nc - k0);
+            const dim3 sgrid((unsigned)((items + 127) / 128));
+            hipLaunchKernelGGL(ssd_bwd_chunk_sums, sgrid, dim3(128), 0, hs, hv, th, csum, T, H, N, nchunk, k0, items);
+            hipLaunchKernelGGL(ssd_bwd_chunk_scan, sgrid, dim3(128), 0, hs, hv, th, csum, ft, dda, dtheta, T, H, N,
+                               nchunk, k0, items);
             if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
         }
     }

@@ -86,6 +86,14 @@ CASES = [
     (257, 32, 64, 1, 4, 2, "bf16", False, True, "randn", True),
     (64, 64, 128, 16, 2, 1, "bf16", True, True, "randn", False),
     (130, 128, 128, 2, 2, 1, "bf16", True, False, "none", True),
+    # bf16 without rotation, headdim <= 64: the chunked walks
+    (300, 64, 128, 1, 2, 1, "bf16", False, True, "randn", True),
+    (77, 16, 16, 2, 3, 1, "bf16", False, False, "none", True),
+    (129, 32, 32, 4, 4, 2, "bf16", False, True, "randn", False),
+    (64, 64, 64, 16, 2, 1, "bf16", False, True, "none", True),
+    (1, 64, 128, 1, 2, 1, "bf16", False, True, "randn", True),
+    (500, 64, 128, 8, 2, 2, "bf16", False, False, "randn", True),
+    (45, 32, 128, 2, 2, 1, "bf16", False, True, "randn", True),
 ]
 
 
@@ -101,16 +109,16 @@ def test_backward_cases(T, P, N, R, H, G, dtype, rot, init, skip, dfin):
             inp)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_long_sequence_segments(dtype):
+@pytest.mark.parametrize("dtype,rot", [("f32", True), ("bf16", True), ("bf16", False)])
+def test_backward_long_sequence_segments(dtype, rot):
     # few (batch, head) pairs and a long sequence: the plan splits it into
     # segments, so both walks start from carried states (forward: the state
     # passes; backward: the reverse state pass and its carry)
     shape = si.small_shape(batch=1, seqlen=3000, nheads=2, headdim=64, dstate=128, mimo_rank=4,
-                           dtype=dtype, rotation=True, init_state=True, skip="randn", dt_shift=5.0)
+                           dtype=dtype, rotation=rot, init_state=True, skip="randn", dt_shift=5.0)
     inp = si.make_inputs(shape, seed=91)
     dy, df = si.make_cotangents(shape, seed=91)
-    compare(run(inp, dy, df), ref(inp, dy, df), TOL[dtype], f"segments {dtype}", inp)
+    compare(run(inp, dy, df), ref(inp, dy, df), TOL[dtype], f"segments {dtype} rot={rot}", inp)
 
 
 def test_backward_in_place_and_deterministic():
