@@ -15,16 +15,16 @@ void* select_cols_bf16(int mode, int w, int NP, bool ysub) {
 void* select_cols_rot_bf16(int mode, int w, int NP, bool ysub) {
     if (w == 4) {
         switch (NP) {
-            case 64: return mode ? cols_ptr<uint16_t, 64, 4, 1, true>()
+            case 64: return mode ? (ysub ? cols_ptr<uint16_t, 64, 4, 1, true, true>() : cols_ptr<uint16_t, 64, 4, 1, true>())
                                  : ysub ? cols_ptr<uint16_t, 64, 4, 0, true, true>() : cols_ptr<uint16_t, 64, 4, 0, true>();
-            case 128: return mode ? cols_ptr<uint16_t, 128, 4, 1, true>()
+            case 128: return mode ? (ysub ? cols_ptr<uint16_t, 128, 4, 1, true, true>() : cols_ptr<uint16_t, 128, 4, 1, true>())
                                   : ysub ? cols_ptr<uint16_t, 128, 4, 0, true, true>() : cols_ptr<uint16_t, 128, 4, 0, true>();
         }
     } else if (w == 8) {
         switch (NP) {
-            case 64: return mode ? cols_ptr<uint16_t, 64, 8, 1, true>()
+            case 64: return mode ? (ysub ? cols_ptr<uint16_t, 64, 8, 1, true, true>() : cols_ptr<uint16_t, 64, 8, 1, true>())
                                  : ysub ? cols_ptr<uint16_t, 64, 8, 0, true, true>() : cols_ptr<uint16_t, 64, 8, 0, true>();
-            case 128: return mode ? cols_ptr<uint16_t, 128, 8, 1, true>()
+            case 128: return mode ? (ysub ? cols_ptr<uint16_t, 128, 8, 1, true, true>() : cols_ptr<uint16_t, 128, 8, 1, true>())
                                   : ysub ? cols_ptr<uint16_t, 128, 8, 0, true, true>() : cols_ptr<uint16_t, 128, 8, 0, true>();
         }
     }

@@ -84,10 +84,23 @@ ssd_status forward_plan(const ssd_dims* d, const void* x, const float* da, const
                         const void* C, const float* D, const float* init_state, int64_t chunk_len,
                         int64_t R, const float* theta, float* y, float* final_state,
                         const ssd_launch_opts* opts, int ysub, FwdPlan* out);
+// The trapezoid's own inputs, when the rotating column walk stages its
+// sub-steps straight from the source arrays (forward_launch with trap set:
+// the plan is for 2T sub-steps; x, B, C, theta have T steps, da is the
+// per-sub-step da, with scale, the per-sub-step write scale).
+struct TrapSrc {
+    const float* scale;      // [b][2T][H]
+    const void* prev_x;      // may be null (with prev_B)
+    const void* prev_B;
+};
 ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, const void* B,
                           const void* C, const float* D, const float* init_state, const float* theta,
                           float* y, float* final_state, void* ws, void* const* walk_events,
-                          hipStream_t hs);
+                          hipStream_t hs, const TrapSrc* trap = nullptr);
+// forward_plan without the argument checks (shape, options and pointers are
+// the caller's to check): the launch plan and workspace of problem d.
+ssd_status forward_plan_shape(const ssd_dims* d, int64_t R, bool rot, const ssd_launch_opts* opts, int ysub,
+                              FwdPlan* out);
 
 // The trapezoid's sub-step inputs (trap_scan.hip): every step t of the
 // two-write recurrence becomes sub-steps 2t (decay, the previous write scaled

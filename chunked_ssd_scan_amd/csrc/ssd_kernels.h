@@ -701,6 +701,14 @@ struct TileArgs {
     int SF;                // output pass: state-pass segments per segment
     int NB;                // column blocks per B/C group
     int ysub;              // 1: y keeps only the odd time steps, as step (t - 1) / 2
+    // trapezoid sub-steps (the rotating walk with YS): T counts sub-steps;
+    // x, B, C, theta have T / 2 steps, and sub-step s takes x and B of step
+    // (s - 1) >> 1 (prev_x, prev_B before step 0), C of step s >> 1 and theta
+    // on odd sub-steps; da and the write scale (beta on even, gamma on odd
+    // sub-steps) come per sub-step in da and scale
+    const float* scale;    // [b,T,H]
+    const void* prev_x;    // [b,R,H,P] or null
+    const void* prev_B;    // [b,R,G,N] or null
 };
 
 // Operand whose reduction index runs down the rows of a row-major LDS tile:
@@ -1000,6 +1008,8 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
     __shared__ float sCarry[4][MH];
     // da of the block's heads, staged by the memory waves: [tile ring][step][head]
     __shared__ __attribute__((aligned(16))) float sDa[4][kRows][DAH];
+    // trapezoid: per sub-step write scale (beta or gamma), same ring
+    __shared__ float sSc[ROT ? 4 : 1][ROT ? kRows : 1];
     // rotation: each memory wave's table for the time steps of its 16-row
     // block: per step and pair group (2 state pairs), the four rows of the bf16
     // matrix that turns them by R(-Phi), Phi the angle from the segment start;
@@ -1076,26 +1086,63 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
         lam += last;
     };
 
+    // trapezoid source geometry: a tile of Qt sub-steps covers Qt / 2 source
+    // steps (16 source rows); x and B resources start one step before the
+    // segment (its first even sub-step reads the previous step), except in the
+    // first segment, whose step -1 comes from prev_x / prev_B
+    constexpr bool trap = ROT && YS;            // the rotating walk with YS runs trapezoid sub-steps
+    const int64_t Ts = trap ? T / 2 : T;                          // source steps
+    const int64_t sb = trap ? (int64_t)k0 * (Qt >> 1) : 0;       // segment's first source step
+    const int64_t se = trap ? (((int64_t)k1 * (Qt >> 1) < Ts) ? (int64_t)k1 * (Qt >> 1) : Ts) : 0;
+    const int adj = (trap && k0 > 0) ? 1 : 0;
+    const bool first_seg = trap && k0 == 0;
+
     if (memw) {
         // ============ memory waves: x, B, C, C B^T and da staged into LDS ============
-        const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * TR + row0) * xrow_el + col0,
-                                    (uint32_t)(((vrows - 1) * xrow_el + CW) * ESZ));
-        const uint32_t xstep = (uint32_t)(F * xrow_el * ESZ);
-        uint32_t xgoff[XPT];
+        const int64_t xr0 = trap ? (sb - adj) * R : row0, xvr = trap ? (se - sb + adj) * R : vrows;
+        const auto rs_x = make_rsrc(static_cast<const TI*>(a.x) + (b * Ts * R + xr0) * xrow_el + col0,
+                                    (uint32_t)(((xvr - 1) * xrow_el + CW) * ESZ));
+        const uint32_t xstep = (uint32_t)((trap ? (F >> 1) : F) * xrow_el * ESZ);
+        uint32_t xgoff[XPT], xpoff[XPT];
         int xloff[XPT];
 #pragma unroll
         for (int m = 0; m < XPT; ++m) {
             const int u = mt + m * NTM;
             const int r = u / XUR, col = (u % XUR) * EPU;
-            xgoff[m] = (u < XU) ? (uint32_t)((r * xrow_el + col) * ESZ) : kOOB;
+            int srow = r;
+            if (trap) {
+                const int sl = r >> log2R, rr = r & ((1 << log2R) - 1);
+                srow = (((sl - 1) >> 1) + adj) * (int)R + rr;   // may be -R..-1: out of range
+                xpoff[m] = (u < XU && sl == 0) ? (uint32_t)((rr * xrow_el + col) * ESZ) : kOOB;
+            } else {
+                xpoff[m] = kOOB;
+            }
+            xgoff[m] = (u < XU) ? (uint32_t)((int64_t)(srow * xrow_el + col) * ESZ) : kOOB;
             xloff[m] = (u < XU) ? r * LDX + col : F * LDX;
         }
         uint4 rx[2][XPT];            // x of tile t in slot t & 1
         auto load_x = [&](int slot, int k) {
             const uint32_t o = (uint32_t)k * xstep;
 #pragma unroll
-            for (int m = 0; m < XPT; ++m)   // non-temporal: x is read once
-                rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, 2));
+            for (int m = 0; m < XPT; ++m)   // non-temporal: x is read once (plain walk)
+                rx[slot][m] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, xgoff[m] + o, 0, trap ? 0 : 2));
+        };
+        // trapezoid, first segment: sub-step 0 writes prev_x, whose units the
+        // first load_x left zero (out of range); called once, after it
+        auto patch_x0 = [&](int slot) {
+            if constexpr (trap) {
+                if (!first_seg || !a.prev_x) return;
+                const auto rs_px = make_rsrc(static_cast<const TI*>(a.prev_x) + b * R * xrow_el + col0,
+                                             (uint32_t)(((R - 1) * xrow_el + CW) * ESZ));
+#pragma unroll
+                for (int m = 0; m < XPT; ++m) {
+                    const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_px, xpoff[m], 0, 0));
+                    rx[slot][m].x |= v.x;
+                    rx[slot][m].y |= v.y;
+                    rx[slot][m].z |= v.z;
+                    rx[slot][m].w |= v.w;
+                }
+            }
         };
         auto store_x = [&](int slot, int buf) {
 #pragma unroll
@@ -1103,6 +1150,7 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
         };
         // da of tile t in slot t & 1: element (step, head) of the block's heads,
         // lane-contiguous along the heads of a step (one short run per step)
+        // da (and, for the trapezoid, the write scale) per step of the walk
         const int64_t step0 = (int64_t)k0 * Qt;
         const int64_t vsteps = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - step0;
         const auto rs_da = make_rsrc(a.da + (b * T + step0) * H + hfirst, (uint32_t)(((vsteps - 1) * H + nhb) * 4));
@@ -1113,19 +1161,29 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             const int u = mt + m * NTM, st = u / DAH, hd = u % DAH;
             daoff[m] = (st < Qt && hd < nhb) ? (uint32_t)((st * H + hd) * 4) : kOOB;
         }
-        float rda[2][DPM];
+        float rda[2][DPM], rsc[2][trap ? DPM : 1];
         auto load_da = [&](int slot, int k) {
             const uint32_t o = (uint32_t)k * dastep;
 #pragma unroll
             for (int m = 0; m < DPM; ++m)
                 rda[slot][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_da, daoff[m] + o, 0, 0));
+            if constexpr (trap) {
+                const auto rs_sc = make_rsrc(a.scale + (b * T + step0) * H + hfirst, (uint32_t)(((vsteps - 1) * H + nhb) * 4));
+#pragma unroll
+                for (int m = 0; m < DPM; ++m)
+                    rsc[slot][m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs_sc, daoff[m] + o, 0, 0));
+            }
         };
         auto store_da = [&](int slot, int k) {
 #pragma unroll
-            for (int m = 0; m < DPM; ++m)
+            for (int m = 0; m < DPM; ++m) {
                 // (the shared walk's units fill the ring slot exactly; an
                 // unneeded guard there costs registers)
                 if (!ROT || mt + m * NTM < F * DAH) (&sDa[k & 3][0][0])[mt + m * NTM] = rda[slot][m];
+                if constexpr (trap) {
+                    if (mt + m * NTM < F) sSc[k & 3][mt + m * NTM] = rsc[slot][m];
+                }
+            }
         };
         // B and C of tile t: one register slot, refilled a tile ahead
         const uint32_t bspan = (uint32_t)(((vrows - 1) * brow_el + N) * ESZ);
@@ -1254,16 +1312,48 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             const int gmat = mw >> 1, grb = mw & 1;      // matrix (0 = B, 1 = C) and row block
             const bool gon = OUT || gmat == 0;
             const int grow = 16 * grb + l16;             // this lane's row of the tile
-            const uint32_t goff = gon ? (uint32_t)((grow * brow_el + 8 * q) * ESZ) : kOOB;
-            const auto rs_g = gmat ? rs_c : rs_b;
+            // trapezoid: the source row of this lane's sub-step row (B: step
+            // (s - 1) >> 1 from a resource one step early unless first segment;
+            // C: step s >> 1), tiles 16 source rows apart
+            int gsrc = grow;
+            uint32_t gpoff = kOOB;
+            if (trap) {
+                const int sl = grow >> log2R, rr = grow & ((1 << log2R) - 1);
+                gsrc = (gmat ? (sl >> 1) : ((sl - 1) >> 1) + adj) * (int)R + rr;
+                if (gmat == 0 && sl == 0) gpoff = (uint32_t)((rr * brow_el + 8 * q) * ESZ);
+            }
+            const uint32_t goff = gon ? (uint32_t)((int64_t)(gsrc * brow_el + 8 * q) * ESZ) : kOOB;
+            const int64_t gr0 = gmat ? sb * R : (sb - adj) * R, gvr = gmat ? (se - sb) * R : (se - sb + adj) * R;
+            const auto rs_g = trap ? make_rsrc(static_cast<const TI*>(gmat ? a.C : a.B) + (b * Ts * R + gr0) * brow_el + grp * N,
+                                               (uint32_t)(((gvr - 1) * brow_el + N) * ESZ))
+                                   : (gmat ? rs_c : rs_b);
+            const uint32_t gstep = trap ? (uint32_t)((F >> 1) * brow_el * ESZ) : bstep;
             // B / C fragments and angles of tile t in register slot t & 1,
             // loaded a full tile before they are used
             uint4 rf[2][KS];
             auto load_frags = [&](int slot, int k) {
-                const uint32_t o = (uint32_t)k * bstep;
+                const uint32_t o = (uint32_t)k * gstep;
 #pragma unroll
                 for (int s = 0; s < KS; ++s)
                     rf[slot][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs_g, goff + s * 64 + o, 0, 0));
+            };
+            // trapezoid, first segment: sub-step 0 writes prev_B (out of range
+            // in the first load_frags); called once, after it
+            auto patch_frags0 = [&](int slot) {
+                if constexpr (trap) {
+                    if (!first_seg || gmat != 0 || !a.prev_B) return;
+                    const auto rs_pg = make_rsrc(static_cast<const TI*>(a.prev_B) + b * R * brow_el + grp * N,
+                                                 (uint32_t)(((R - 1) * brow_el + N) * ESZ));
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                      rs_pg, gpoff == kOOB ? kOOB : gpoff + s * 64, 0, 0));
+                        rf[slot][s].x |= v.x;
+                        rf[slot][s].y |= v.y;
+                        rf[slot][s].z |= v.z;
+                        rf[slot][s].w |= v.w;
+                    }
+                }
             };
             // angles: every memory wave keeps, per pair (lane), the running
             // angle from the segment start (wrapped to [-pi, pi]) and tables
@@ -1271,17 +1361,24 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             const int spb = 16 >> log2R;                 // time steps per 16-row block
             const int st0 = grb * spb;
             const int64_t NH2 = N / 2;
-            const auto rs_th = make_rsrc(a.theta + ((b * T + step0) * H + hfirst) * NH2,
-                                         (uint32_t)((((vsteps - 1) * H) * NH2 + NH2) * 4));
-            const uint32_t throw_b = (uint32_t)(H * NH2 * 4), thstep = (uint32_t)(Qt * H * NH2 * 4);
+            const int64_t th0 = trap ? sb : step0, thv = trap ? se - sb : vsteps;
+            const auto rs_th = make_rsrc(a.theta + ((b * Ts + th0) * H + hfirst) * NH2,
+                                         (uint32_t)((((thv - 1) * H) * NH2 + NH2) * 4));
+            const uint32_t throw_b = (uint32_t)(H * NH2 * 4);
+            const uint32_t thstep = (uint32_t)((trap ? (Qt >> 1) : Qt) * H * NH2 * 4);
             const uint32_t thoff = (gon && lane < NH2) ? (uint32_t)(lane * 4) : kOOB;
             float rth[2][QTM], carry = 0.f;
+            // theta of sub-step st: step st (plain) or, for the trapezoid, step
+            // st >> 1 on odd sub-steps and no turn on even ones
             auto load_th = [&](int slot, int k) {
                 const uint32_t o = (uint32_t)k * thstep;
 #pragma unroll
-                for (int st = 0; st < QTM; ++st)
+                for (int st = 0; st < QTM; ++st) {
+                    const bool on = st < Qt && (!trap || (st & 1));
+                    const uint32_t so = trap ? (uint32_t)(st >> 1) * throw_b : (uint32_t)st * throw_b;
                     rth[slot][st] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                                  rs_th, st < Qt ? thoff + st * throw_b + o : kOOB, 0, 0));
+                                                                  rs_th, on ? thoff + so + o : kOOB, 0, 0));
+                }
             };
             uint2* tab = sRot[mw];
             // table of the tile whose angles are in rth, then B~ / C~ of that
@@ -1344,10 +1441,12 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
             // fragments are loaded during tile t-3, as soon as their register
             // slot drains, so that more than a tile of work covers the latency.
             load_frags(0, 0);
+            patch_frags0(0);
             load_th(0, 0);
             load_frags(1, 1);
             load_th(1, 1);
             load_x(0, 0);
+            patch_x0(0);
             load_x(1, 1);
             load_da(0, 0);
             load_da(1, 1);
@@ -1576,6 +1675,17 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                     v1[v] = cb01[v] * __builtin_amdgcn_exp2f(fminf(ci1 - cjv0[v], 0.f));
                     v2[v] = fmaf(dsel[v], Dr, k11 ? cb11[v] * __builtin_amdgcn_exp2f(fminf(ci1 - cjv1[v], 0.f)) : 0.f);
                 }
+                if (trap) {
+                    // the source rows' write scales (source rows 4q + v and
+                    // 16 + 4q + v, one time step each since R >= 4)
+                    const float s0 = sSc[vb][(4 * q) >> log2R], s1 = sSc[vb][(16 + 4 * q) >> log2R];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        v0[v] *= s0;
+                        v1[v] *= s0;
+                        v2[v] *= s1;
+                    }
+                }
                 m00 = pack_m<TI>(v0[0], v0[1], v0[2], v0[3]);
                 m01 = pack_m<TI>(v1[0], v1[1], v1[2], v1[3]);
                 m11 = pack_m<TI>(v2[0], v2[1], v2[2], v2[3]);
@@ -1594,6 +1704,16 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
         const float4 w1 = *reinterpret_cast<const float4*>(&sW[vb][hl][16 + 4 * q]);
         xv[0] *= w0.x; xv[1] *= w0.y; xv[2] *= w0.z; xv[3] *= w0.w;
         xv[4] *= w1.x; xv[5] *= w1.y; xv[6] *= w1.z; xv[7] *= w1.w;
+        if constexpr (ROT) {
+            if (trap) {
+                const float s0 = sSc[vb][(4 * q) >> log2R], s1 = sSc[vb][(16 + 4 * q) >> log2R];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    xv[e] *= s0;
+                    xv[4 + e] *= s1;
+                }
+            }
+        }
         const frag xw = O::pack(xv);
         const float carry = sCarry[vb][hl];
 #pragma unroll

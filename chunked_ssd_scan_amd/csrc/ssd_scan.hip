@@ -520,9 +520,14 @@ ssd_status forward_plan(const ssd_dims* d, const void* x, const float* da, const
         if (!same_state && overlap(sf, ins[i])) return SSD_ERR_ALIAS;
     }
 
+    return forward_plan_shape(d, R, theta != nullptr, opts, ysub, out);
+}
+
+ssd_status forward_plan_shape(const ssd_dims* d, int64_t R, bool rot, const ssd_launch_opts* opts, int ysub,
+                              FwdPlan* out) {
     FwdPlan fp;
-    fp.rot = theta != nullptr;
-    st = make_plan(d, R, fp.rot, opts ? opts->segments : 0, opts ? opts->block_slices : 0, &fp.pl);
+    fp.rot = rot;
+    ssd_status st = make_plan(d, R, fp.rot, opts ? opts->segments : 0, opts ? opts->block_slices : 0, &fp.pl);
     if (st != SSD_OK) return st;
     // column-block walk (C B^T tile pack shared by the heads of a group unless
     // rotated), or the general walk for shapes it does not cover
@@ -541,7 +546,10 @@ ssd_status forward_plan(const ssd_dims* d, const void* x, const float* da, const
 ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, const void* B,
                           const void* C, const float* D, const float* init_state, const float* theta,
                           float* y, float* final_state, void* ws, void* const* walk_events,
-                          hipStream_t hs) {
+                          hipStream_t hs, const TrapSrc* trap) {
+    // the rotating column walk's odd-step output mode is the trapezoid's
+    // sub-step walk, and the trapezoid's sources need that walk
+    if ((trap != nullptr) != (fp.cols && fp.rot && fp.ysub != 0)) return SSD_ERR_UNSUPPORTED;
     const Plan& pl = fp.pl;
     const WsLayout wl = workspace_layout(pl, !fp.shared);
     char* wsc = static_cast<char*>(ws);
@@ -585,6 +593,10 @@ ssd_status forward_launch(const FwdPlan& fp, const void* x, const float* da, con
             args.theta = theta;
             args.NB = (int)((pl.H / pl.G) * (pl.P / 16) / pl.W);
             args.ysub = fp.ysub;
+            if (trap) {
+                args.scale = trap->scale;
+                args.prev_x = trap->prev_x; args.prev_B = trap->prev_B;
+            }
             rs = run_passes(pl, fp.rot, args, init_state, hs, walk_events);
         }
     }

@@ -98,6 +98,22 @@ __global__ __launch_bounds__(256) void trap_expand_rows(TrapExpand a) {
     }
 }
 
+// Per sub-step da and write scale of the trapezoid, for the rotating column
+// walk, which stages x, B, C and theta from the source arrays itself: element
+// (b, t, h) gives sub-steps 2t (da_t, beta_t) and 2t + 1 (0, gamma_t).
+__global__ __launch_bounds__(256) void trap_da_scale(const float* __restrict__ da, const float* __restrict__ beta,
+                                                    const float* __restrict__ gamma, float* __restrict__ dah,
+                                                    float* __restrict__ sch, int64_t T, int64_t H, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const int64_t h = i % H, bt = i / H, t = bt % T, b = bt / T;
+    const int64_t e = (b * 2 * T + 2 * t) * H + h, o = e + H;
+    dah[e] = da[i];
+    dah[o] = 0.f;
+    sch[e] = beta[i];
+    sch[o] = gamma[i];
+}
+
 }  // namespace
 
 namespace ssd_detail {
@@ -180,14 +196,51 @@ ssd_status ssd_trapezoid_forward(const ssd_dims* d, const void* x, const float* 
         overlap(sf, span_of(init_state, b * H * P * N * 4)))
         return SSD_ERR_ALIAS;
 
-    // sub-step inputs in the expansion slot
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    {
+        // the rotating column walk stages the sub-steps from the source arrays
+        // itself (write scales in fp32, nothing expanded through HBM)
+        FwdPlan fp;
+        ssd_status ps = forward_plan_shape(&d2, R, theta != nullptr, opts, 1, &fp);
+        if (ps != SSD_OK) return ps;
+        if (fp.cols && fp.rot) {
+            // per sub-step da (da_t, 0) and write scale (beta_t, gamma_t)
+            const size_t half = align256((size_t)(b * 2 * T * H) * 4);
+            int sentry = -1;
+            char* sws = static_cast<char*>(scratch_acquire(hs, 2 * half, &sentry, kSlotExpand));
+            if (!sws) return SSD_ERR_HIP;
+            void* fws = nullptr;
+            int fentry = -1;
+            ssd_status rs = SSD_OK;
+            if (fp.ws_bytes) {
+                fws = scratch_acquire(hs, fp.ws_bytes, &fentry);
+                if (!fws) rs = SSD_ERR_HIP;
+            }
+            float* dah = reinterpret_cast<float*>(sws);
+            float* sch = reinterpret_cast<float*>(sws + half);
+            if (rs == SSD_OK) {
+                const int64_t n = b * T * H;
+                hipLaunchKernelGGL(trap_da_scale, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, da, beta, gamma,
+                                   dah, sch, T, H, n);
+                if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+            }
+            const TrapSrc ts{sch, prev_x, prev_B};
+            if (rs == SSD_OK)
+                rs = forward_launch(fp, x, dah, B, C, nullptr, init_state, theta, y, final_state, fws,
+                                    opts ? opts->walk_events : nullptr, hs, &ts);
+            if (fws && !scratch_release(fentry) && rs == SSD_OK) rs = SSD_ERR_HIP;
+            if (!scratch_release(sentry) && rs == SSD_OK) rs = SSD_ERR_HIP;
+            return rs;
+        }
+    }
+
+    // other shapes: the sub-step inputs in the expansion slot
     TrapExpand a;
     memset(&a, 0, sizeof(a));
     a.x = x; a.da = da; a.B = B; a.C = C; a.beta = beta; a.gamma = gamma;
     a.prev_x = prev_x; a.prev_B = prev_B; a.theta = theta;
     a.b = b; a.T = T; a.R = R; a.H = H; a.P = P; a.G = G; a.N = N;
     a.esz = (int)esz;
-    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     int entry = -1;
     void* ws = scratch_acquire(hs, trap_expand_bytes(a), &entry, kSlotExpand);
     if (!ws) return SSD_ERR_HIP;

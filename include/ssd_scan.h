@@ -223,8 +223,11 @@ ssd_status ssd_selective_scan_ex(const float *u, const float *delta, const float
  * Runs as the single-write scan over 2T sub-steps (decay then turn), which
  * writes y for the odd sub-steps only, so the envelope is ssd_forward's at
  * seqlen 2T; opts apply to that scan (walk events bracket its output walk).
- * With bf16 inputs the sub-step inputs beta_t x_{t-1} and gamma_t x_t are
- * stored as bf16 before that scan: one extra rounding (at most 2^-9
+ * Where the scan takes its rotating column walk (bf16, rotation, headdim 64
+ * or 128, dstate 64 or 128, R >= 4) that walk reads the sub-steps straight
+ * from x, B, C and theta and applies beta and gamma in fp32. Other shapes
+ * first expand the sub-step inputs into scratch; with bf16 inputs that stores
+ * beta_t x_{t-1} and gamma_t x_t as bf16, one extra rounding (at most 2^-9
  * relative) of the scaled x.
  * Scratch: the sub-step inputs (about 2x x, B, C, da and theta in bytes) in
  * a second per-(device, stream) buffer of the library, besides
