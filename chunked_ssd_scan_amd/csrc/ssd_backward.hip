@@ -66,13 +66,14 @@ struct BwdArgs {
     const float* seg_in;    // entering (adjoint) states [b*H][S*SF][P][N] (forward walk) or
                             // [b*H][S][P][N] (backward walk), null with one segment
     float* seg_out;         // backward state pass: local adjoints [b*H][S][P][N]
-    float* part;            // per-head partials [b*H][npg][T*R][N] (dC or dB)
+    float* part;            // per-head partials [b][T*R][H][npg][N] (dC or dB): heads interleaved per row
     float* dx;              // [b,T,R,H,P]
     float* dinit;           // [b,H,P,N] or null
     float* final_state;     // forward walk: h_{T-1} [b,H,P,N]
     float* dDp;             // [b*H][npg][S] partial sums of dy . x
     int64_t T, H, G, N, R, P;
     int PG, S, SF, nsub, Qt, log2R;
+    const float* phi;       // [b,T,H,N/2] cumulative angles (chunked walks with rotation), or null
 };
 
 // Staging of one 32-row tile by the memory waves: x, dy (as TI), B, C rows,
@@ -112,16 +113,40 @@ __device__ __forceinline__ float to_f32(TI v) {
 
 // One memory thread's staging of tile k into registers (load) and LDS (store).
 // RAW: no rotation staged, and da kept as is (the chunked walks scan it)
-// instead of as the decay exp(da).
-template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C, bool RAW = false>
+// instead of as the decay exp(da). TURN (bf16): B and C rows stored turned
+// into the folded frame, B~ = R(-Phi_t) B, with Phi from a.phi.
+template <typename TI, int NP, bool WANT_X, bool WANT_B, bool WANT_C, bool RAW = false, bool TURN = false>
 struct Stager {
     using St = Stage<TI, NP, WANT_X, WANT_B, WANT_C>;
     uint4 rx[WANT_X ? St::XR : 1];
     float4 rdy[St::DYR];
     uint4 rb[WANT_B ? St::BRG : 1];
     uint4 rc[WANT_C ? St::BRG : 1];
+    float4 rpb[(TURN && WANT_B) ? St::BRG : 1], rpc[(TURN && WANT_C) ? St::BRG : 1];
     float4 rth[St::THR];
     float rda;
+
+    // Phi of the 4 pairs of a staged 16-byte unit (row r of tile k, columns c..c+7)
+    __device__ float4 load_phi(const BwdArgs& a, int64_t f, int c, int64_t b, int64_t h) const {
+        const int64_t t = f / a.R;
+        return *reinterpret_cast<const float4*>(a.phi + ((b * a.T + t) * a.H + h) * (a.N / 2) + c / 2);
+    }
+    // the 4 pairs of v turned by R(-Phi): (e0, e1) -> (c e0 + s e1, c e1 - s e0)
+    __device__ static uint4 turn(uint4 v, float4 ph) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const float pv[4] = {ph.x, ph.y, ph.z, ph.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e0 = __uint_as_float(w[i] << 16), e1 = __uint_as_float(w[i] & 0xffff0000u);
+            const float rev = pv[i] * kInv2Pi;
+            const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+            const float n0 = fmaf(cs, e0, sn * e1), n1 = fmaf(cs, e1, -sn * e0);
+            o[i] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)n0) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)n1) << 16);
+        }
+        return make_uint4(o[0], o[1], o[2], o[3]);
+    }
 
     __device__ void load(const BwdArgs& a, int k, int mt, int64_t b, int64_t h, int64_t g, int pbase) {
         const int64_t T = a.T, H = a.H, G = a.G, N = a.N, P = a.P, TR = a.T * a.R;
@@ -153,6 +178,9 @@ struct Stager {
                 rb[m] = (u < kTileRows * nbu && f0 + r < TR)
                             ? *reinterpret_cast<const uint4*>(Bg + ((b * TR + f0 + r) * G + g) * N + c)
                             : make_uint4(0, 0, 0, 0);
+                if constexpr (TURN)
+                    rpb[m] = (u < kTileRows * nbu && f0 + r < TR) ? load_phi(a, f0 + r, c, b, h)
+                                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         if constexpr (WANT_C) {
@@ -163,6 +191,9 @@ struct Stager {
                 rc[m] = (u < kTileRows * nbu && f0 + r < TR)
                             ? *reinterpret_cast<const uint4*>(Cg + ((b * TR + f0 + r) * G + g) * N + c)
                             : make_uint4(0, 0, 0, 0);
+                if constexpr (TURN)
+                    rpc[m] = (u < kTileRows * nbu && f0 + r < TR) ? load_phi(a, f0 + r, c, b, h)
+                                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         const int64_t t0 = (int64_t)k * a.Qt;
@@ -207,14 +238,16 @@ struct Stager {
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
                 const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
-                if (u < kTileRows * nbu) *reinterpret_cast<uint4*>(&s.sB[buf * BS + r * St::LDB + c]) = rb[m];
+                if (u < kTileRows * nbu)
+                    *reinterpret_cast<uint4*>(&s.sB[buf * BS + r * St::LDB + c]) = TURN ? turn(rb[m], rpb[m]) : rb[m];
             }
         }
         if constexpr (WANT_C) {
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
                 const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
-                if (u < kTileRows * nbu) *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = rc[m];
+                if (u < kTileRows * nbu)
+                    *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = TURN ? turn(rc[m], rpc[m]) : rc[m];
             }
         }
 #pragma unroll
@@ -263,15 +296,16 @@ __device__ __forceinline__ void put_share(float* sZ, const f32x4 (&z)[2][NT], bo
             }
 }
 
-// The reduced rows of a tile (those before TR) to the head's partial.
+// The reduced rows of a tile (those before TR) to the head's partial, whose
+// rows are rs elements apart (the partials interleave the heads per row).
 template <int NP>
-__device__ __forceinline__ void copy_rows(const float* sZ, float* dst, int64_t f0, int64_t TR, int N, int tid,
-                                          int nthr) {
+__device__ __forceinline__ void copy_rows(const float* sZ, float* dst, int64_t f0, int64_t TR, int N, int64_t rs,
+                                          int tid, int nthr) {
     const int nu = N / 4;
     for (int i = tid; i < kTileRows * nu; i += nthr) {
         const int r = i / nu, c = (i % nu) * 4;
         if (f0 + r < TR)
-            *reinterpret_cast<float4*>(dst + (f0 + r) * N + c) = *reinterpret_cast<const float4*>(&sZ[r * NP + c]);
+            *reinterpret_cast<float4*>(dst + (f0 + r) * rs + c) = *reinterpret_cast<const float4*>(&sZ[r * NP + c]);
     }
 }
 
@@ -311,7 +345,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_forward_kernel(BwdArgs
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     const int pbase = pg * PG;
-    float* dst = a.part + (bh * npg + pg) * TR * N;
+    float* dst = a.part + ((b * TR * H + h) * npg + pg) * N;   // [b][TR][H][npg][N]
 
     if constexpr (PAD > 0)
         for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
@@ -333,7 +367,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_forward_kernel(BwdArgs
                 st.store(sm, a, buf ^ 1, mt);
             }
             for (int w = 0; w < nw; ++w) __syncthreads();
-            copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+            copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, H * npg * N, tid, nthr);
             __syncthreads();
         }
         return;
@@ -427,7 +461,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_forward_kernel(BwdArgs
             if (wv == w) put_share<NT>(sZ, z, w == 0, lane);
             __syncthreads();
         }
-        copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+        copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, H * npg * N, tid, nthr);
         __syncthreads();
     }
     if (seg == S - 1 && a.final_state) {
@@ -478,7 +512,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     const int pbase = pg * PG;
-    float* dst = OUT ? a.part + (bh * npg + pg) * TR * N : nullptr;
+    float* dst = OUT ? a.part + ((b * TR * H + h) * npg + pg) * N : nullptr;
 
     if constexpr (PAD > 0)
         for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
@@ -506,7 +540,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
             }
             if constexpr (OUT) {
                 for (int w = 0; w < nw; ++w) __syncthreads();
-                copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+                copy_rows<NP>(sZ, dst, (int64_t)k * kTileRows, TR, (int)N, H * npg * N, tid, nthr);
             }
             __syncthreads();
         }
@@ -664,7 +698,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
                 if (wv == w) put_share<NT>(sZ, zb, w == 0, lane);
                 __syncthreads();
             }
-            copy_rows<NP>(sZ, dst, f0, TR, (int)N, tid, nthr);
+            copy_rows<NP>(sZ, dst, f0, TR, (int)N, H * npg * N, tid, nthr);
         }
         __syncthreads();
     }
@@ -775,7 +809,7 @@ __device__ __forceinline__ void put_frags(float4* slot, const f32x4 (&z)[2][NT],
 // The nw slots added in wave order and stored as the rows f0 + r (< TR) of dst.
 template <int NT>
 __device__ __forceinline__ void sum_frags(const float4* slots, int nw, float* dst, int64_t f0, int64_t TR, int N,
-                                          int tid, int nthr) {
+                                          int64_t rs, int tid, int nthr) {
     constexpr int NF = 2 * NT * 64;
     for (int f = tid; f < NF; f += nthr) {
         float4 acc = slots[f];
@@ -792,7 +826,7 @@ __device__ __forceinline__ void sum_frags(const float4* slots, int nw, float* ds
         const float av[4] = {acc.x, acc.y, acc.z, acc.w};
 #pragma unroll
         for (int v = 0; v < 4; ++v)
-            if (f0 + r0 + v < TR) dst[(f0 + r0 + v) * N + n] = av[v];
+            if (f0 + r0 + v < TR) dst[(f0 + r0 + v) * rs + n] = av[v];
     }
 }
 
@@ -802,8 +836,46 @@ __device__ __forceinline__ s16x4 scale4(s16x4 v, float a, float b, float c, floa
     return pack4_bf16(f);
 }
 
-// Forward direction: the head's dC partial rows and the final state.
-template <int NP>
+// Frame changes of state tiles: every state pair (2k, 2k+1) turned by
+// R(sgn Phi[k]) (phirow: the angles of one step, one head). Layout D[p][n]
+// (pairs in neighbouring lanes) and D[n][p] (pairs in one lane).
+template <int NT>
+__device__ __forceinline__ void turn_pn(f32x4 (&hs)[NT], const float* phirow, int N, float sgn, int lane) {
+    const int l16 = lane & 15;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+        const int n = 16 * c + l16;
+        const float rev = (n < N ? phirow[n >> 1] : 0.f) * sgn * kInv2Pi;
+        const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+        const float part = (n & 1) ? sn : -sn;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const float pv = swap_pair(hs[c][v]);
+            hs[c][v] = fmaf(cs, hs[c][v], part * pv);
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void turn_np(f32x4 (&hn)[NT], const float* phirow, int N, float sgn, int lane) {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < NT; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; v += 2) {
+            const int nn = 16 * c + 4 * q + v;
+            const float rev = (nn < N ? phirow[nn >> 1] : 0.f) * sgn * kInv2Pi;
+            const float cs = __builtin_amdgcn_cosf(rev), sn = __builtin_amdgcn_sinf(rev);
+            const float e0 = hn[c][v], e1 = hn[c][v + 1];
+            hn[c][v] = fmaf(cs, e0, -sn * e1);
+            hn[c][v + 1] = fmaf(sn, e0, cs * e1);
+        }
+}
+
+// Forward direction: the head's dC partial rows and the final state. ROT: in
+// the folded frame g = R(-Phi) h (B~, C~ turned while staged; the partial
+// rows are dC~, turned back in the reduction).
+template <int NP, bool ROT>
 __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArgs a) {
     using TI = uint16_t;
     using St = Stage<TI, NP, true, true, false>;
@@ -827,7 +899,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
     const int64_t bh = blockIdx.x / S;
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
-    float* dst = a.part + bh * TR * N;
+    float* dst = a.part + (b * TR * H + h) * N;            // [b][TR][H][N]
 
     for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
         sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
@@ -837,7 +909,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
     __syncthreads();
 
     if (memw) {
-        Stager<TI, NP, true, true, false, true> st;
+        Stager<TI, NP, true, true, false, true, ROT> st;
         if (k1 > k0) {
             st.load(a, k0, mt, b, h, g, 0);
             st.store(sm, a, 0, mt);
@@ -852,7 +924,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
             }
             __syncthreads();                               // blocks built
             __syncthreads();                               // shares in their slots
-            sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+            sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
         }
         return;
     }
@@ -869,6 +941,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
             for (int v = 0; v < 4; ++v)
                 hs[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
         }
+        // the physical state entering a later segment, into the folded frame
+        if (ROT && S > 1 && seg > 0)
+            turn_pn<NT>(hs, a.phi + ((b * T + (int64_t)k0 * Qt - 1) * H + h) * (N / 2), (int)N, -1.f, lane);
     }
     __syncthreads();
     for (int k = k0; k < k1; ++k) {
@@ -937,9 +1012,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
         }
         put_frags<NT>(sZ[wv], z, lane);
         __syncthreads();
-        sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+        sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
     }
     if (seg == S - 1 && a.final_state) {
+        if (ROT) turn_pn<NT>(hs, a.phi + ((b * T + T - 1) * H + h) * (N / 2), (int)N, 1.f, lane);
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
             const int n = 16 * c + l16;
@@ -952,8 +1028,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
 
 // Backward direction (tiles in reverse). MODE 1: only the state gradient, from
 // zero, to the segment's left end (the carry's local term); MODE 0: dx, the
-// head's dB partial, the dy . x partial and dinit.
-template <int NP, int MODE>
+// head's dB partial, the dy . x partial and dinit. ROT: the gradient of the
+// folded state G = R(-Phi) H, converted at the segment ends.
+template <int NP, int MODE, bool ROT>
 __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdArgs a) {
     using TI = uint16_t;
     constexpr bool OUT = MODE == 0;
@@ -980,7 +1057,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
     const int64_t bh = blockIdx.x / S;
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
-    float* dst = OUT ? a.part + bh * TR * N : nullptr;
+    float* dst = OUT ? a.part + (b * TR * H + h) * N : nullptr;
 
     for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
         if (OUT) sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
@@ -993,7 +1070,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
     __syncthreads();
 
     if (memw) {
-        Stager<TI, NP, OUT, OUT, true, true> st;
+        Stager<TI, NP, OUT, OUT, true, true, ROT> st;
         if (k1 > k0) {
             st.load(a, k1 - 1, mt, b, h, g, 0);
             st.store(sm, a, 0, mt);
@@ -1009,7 +1086,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
             __syncthreads();                                   // blocks built / tile walked
             if constexpr (OUT) {
                 __syncthreads();                               // shares in their slots
-                sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+                sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
             }
         }
         __syncthreads();                                       // the dy . x shares
@@ -1039,6 +1116,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                 const int nn = 16 * c + 4 * q + v;
                 hn[c][v] = (OUT && src && nn < N) ? src[off + (int64_t)(p0 + l16) * N + nn] : 0.f;
             }
+        }
+        // the physical gradient at the segment's last step, into the folded frame
+        if (ROT && OUT && src) {
+            const int64_t tl = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - 1;
+            const float* pr = a.phi + ((b * T + tl) * H + h) * (N / 2);
+            turn_pn<NT>(hp, pr, (int)N, -1.f, lane);
+            turn_np<NT>(hn, pr, (int)N, -1.f, lane);
         }
     }
     const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
@@ -1171,11 +1255,14 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
             }
         }
         __syncthreads();                           // shares in their slots (MODE 1: tile walked)
-        if constexpr (OUT) sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, tid, nthr);
+        if constexpr (OUT) sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
     }
     float* out = nullptr;
     if (!OUT && seg > 0) out = a.seg_out + (bh * S + seg) * P * N;
     if (OUT && seg == 0 && a.dinit) out = a.dinit + bh * P * N;
+    // back to the physical frame at step k0 Qt - 1 (none before step 0)
+    if (ROT && out && seg > 0)
+        turn_pn<NT>(hp, a.phi + ((b * T + (int64_t)k0 * Qt - 1) * H + h) * (N / 2), (int)N, 1.f, lane);
     if (out) {
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
@@ -1200,8 +1287,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
 // Per (batch, head, segment): Lambda = sum of da and Phi[k] = sum of theta over
 // the segment's steps (thread k < N/2: Phi[k]; thread N/2: Lambda).
 __global__ __launch_bounds__(128) void ssd_bwd_segsums(const float* __restrict__ da, const float* __restrict__ theta,
-                                                      float* __restrict__ sums, int64_t T, int64_t H, int64_t N,
-                                                      int S, int nsub, int Qt) {
+                                                      const float* __restrict__ phi, float* __restrict__ sums,
+                                                      int64_t T, int64_t H, int64_t N, int S, int nsub, int Qt) {
     const int64_t bh = blockIdx.x / S;
     const int seg = blockIdx.x % S;
     const int64_t b = bh / H, h = bh % H;
@@ -1210,12 +1297,24 @@ __global__ __launch_bounds__(128) void ssd_bwd_segsums(const float* __restrict__
     const int k = threadIdx.x;
     float acc = 0.f;
     if (k < N / 2) {
-        if (theta)
+        if (phi) {
+            // from the cumulative angles: Phi[t1 - 1] - Phi[t0 - 1] (mod 2 pi)
+            acc = phi[((b * T + t1 - 1) * H + h) * (N / 2) + k] -
+                  (t0 > 0 ? phi[((b * T + t0 - 1) * H + h) * (N / 2) + k] : 0.f);
+        } else if (theta) {
+#pragma unroll 8
             for (int64_t t = t0; t < t1; ++t) acc += theta[((b * T + t) * H + h) * (N / 2) + k];
-    } else if (k == N / 2) {
-        for (int64_t t = t0; t < t1; ++t) acc += da[(b * T + t) * H + h];
+        }
+        sums[(bh * S + seg) * (N / 2 + 1) + k] = acc;
     }
-    if (k <= N / 2) sums[(bh * S + seg) * (N / 2 + 1) + k] = acc;
+    // Lambda: the whole workgroup, strided, then reduced in a fixed order
+    __shared__ float sl[2];
+    float lam = 0.f;
+    for (int64_t t = t0 + k; t < t1; t += blockDim.x) lam += da[(b * T + t) * H + h];
+    for (int o = 32; o >= 1; o >>= 1) lam += __shfl_xor(lam, o);
+    if ((k & 63) == 0) sl[k >> 6] = lam;
+    __syncthreads();
+    if (k == 0) sums[(bh * S + seg) * (N / 2 + 1) + N / 2] = sl[0] + sl[1];
 }
 
 // Reverse carry, one thread per (p, state pair): c_{S-1} = dfinal (or 0);
@@ -1248,69 +1347,188 @@ __global__ __launch_bounds__(256) void ssd_bwd_carry(const float* __restrict__ d
 
 // dB and dC of every group (the heads' and row groups' partials added in
 // order) and, per head and step, the inner products and pair cross products
-// of the decay and turn gradients. One workgroup per (batch, step); thread n.
-template <typename TI>
-__global__ __launch_bounds__(128) void ssd_bwd_reduce(const float* __restrict__ pC, const float* __restrict__ pB,
+// of the decay and turn gradients. One workgroup of 4 waves per (batch,
+// step). The ranks go in blocks of RM: wave w takes the heads w, w + 4, ...
+// of a group, HU of them at a time, and keeps its sums of dB and dC for each
+// rank of the block in registers; lanes take n = lane and lane + 64. The four waves' sums meet in
+// LDS and are added in wave order. A head's decay and turn terms add up over
+// the ranks of a block in registers and over blocks in its own output slot.
+// With phi the partials are of the folded frame and are turned back by
+// R(Phi_t) first. Loads take clamped, in-bounds indexes and are masked after,
+// so that all of a head's loads are in flight together.
+template <typename TI, int RM, int HU>
+__global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ pC, const float* __restrict__ pB,
                                                      const void* __restrict__ Bv, const void* __restrict__ Cv,
                                                      float* __restrict__ dB, float* __restrict__ dC,
                                                      float* __restrict__ hv, float* __restrict__ th,
                                                      int64_t T, int64_t H, int64_t G, int64_t N, int64_t R, int npg,
-                                                     int rot) {
+                                                     int rot, const float* __restrict__ phi) {
+    __shared__ float sred[2][4][RM][128];
     const int64_t bt = blockIdx.x, b = bt / T, t = bt % T;
-    const int n = threadIdx.x, lane = n & 63, wvi = n >> 6;
-    const int64_t TR = T * R, HG = H / G;
-    const TI* Bg = static_cast<const TI*>(Bv);
-    const TI* Cg = static_cast<const TI*>(Cv);
-    auto ld = [](const TI* p, int64_t i) -> float {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int64_t HG = H / G;
+    // this step's rows: R ranks x H heads x npg row groups x N partials, and
+    // R ranks x G groups x N entries of B, C, dB and dC; offsets in them fit 32 bits
+    const int64_t row0 = bt * R;
+    const float* pBt = pB + row0 * H * npg * N;
+    const float* pCt = pC + row0 * H * npg * N;
+    const TI* Bt = static_cast<const TI*>(Bv) + row0 * G * N;
+    const TI* Ct = static_cast<const TI*>(Cv) + row0 * G * N;
+    float* dBt = dB + row0 * G * N;
+    float* dCt = dC + row0 * G * N;
+    const float* phit = phi ? phi + bt * H * (N / 2) : nullptr;
+    float* tht = th + bt * H * (N / 2);
+    // without phi the angle loads read entry 0 of the partials, unused: no branch
+    const float* phs = phit ? phit : pBt;
+    const uint32_t phm = phit ? 0xffffffffu : 0u;
+    const uint32_t Hu = (uint32_t)H, Gu = (uint32_t)G, Nu = (uint32_t)N, npu = (uint32_t)npg;
+    auto ld = [](const TI* p, uint32_t i) -> float {
         if constexpr (sizeof(TI) == 2) return __uint_as_float((uint32_t)p[i] << 16);
         else return p[i];
     };
-    __shared__ float sred[2][2];
-    for (int64_t g = 0; g < G; ++g) {
-        for (int64_t r = 0; r < R; ++r) {
-            const int64_t row = (b * TR + t * R + r);
-            const float bn = n < N ? ld(Bg, (row * G + g) * N + n) : 0.f;
-            const float cn = n < N ? ld(Cg, (row * G + g) * N + n) : 0.f;
-            float sb = 0.f, sc = 0.f;
-            for (int64_t hh = 0; hh < HG; ++hh) {
-                const int64_t h = g * HG + hh, bh = b * H + h;
-                float db = 0.f, dc = 0.f;
-                for (int pg = 0; pg < npg; ++pg) {
-                    const int64_t base = ((bh * npg + pg) * TR + t * R + r) * N + n;
-                    if (n < N) {
-                        db += pB[base];
-                        dc += pC[base];
+    bool nok[2];
+    uint32_t nc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const uint32_t n = lane + 64 * e;
+        nok[e] = n < Nu;
+        nc[e] = nok[e] ? n : 0;
+    }
+    for (uint32_t g = 0; g < Gu; ++g) {
+        for (int64_t r0 = 0; r0 < R; r0 += RM) {
+            float sb[RM][2], sc[RM][2], bn[RM][2], cn[RM][2];
+            bool ok[RM][2];
+            uint32_t rc[RM];
+#pragma unroll
+            for (int k = 0; k < RM; ++k) {
+                const bool rin = r0 + k < R;
+                rc[k] = rin ? (uint32_t)(r0 + k) : 0;
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    ok[k][e] = rin && nok[e];
+                    const uint32_t i = (rc[k] * Gu + g) * Nu + nc[e];
+                    sb[k][e] = 0.f;
+                    sc[k][e] = 0.f;
+                    const float bv = ld(Bt, i), cv = ld(Ct, i);
+                    bn[k][e] = ok[k][e] ? bv : 0.f;
+                    cn[k][e] = ok[k][e] ? cv : 0.f;
+                }
+            }
+            const uint32_t hend = (g + 1) * (uint32_t)HG;
+            for (uint32_t h0 = g * (uint32_t)HG + w; h0 < hend; h0 += 4 * HU) {
+                // heads h0 + 4 j of this pass; one past the group's end is
+                // clamped to h0 and its terms are dropped
+                uint32_t hj[HU];
+                bool hok[HU];
+#pragma unroll
+                for (int j = 0; j < HU; ++j) {
+                    hok[j] = h0 + 4 * j < hend;
+                    hj[j] = hok[j] ? h0 + 4 * j : h0;
+                }
+                float db[HU][RM][2], dc[HU][RM][2], ph[HU][2];
+#pragma unroll
+                for (int j = 0; j < HU; ++j)
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        ph[j][e] = phs[(hj[j] * (Nu / 2) + (nc[e] >> 1)) & phm];
+#pragma unroll
+                        for (int k = 0; k < RM; ++k) {
+                            const uint32_t i = (rc[k] * Hu + hj[j]) * npu * Nu + nc[e];
+                            db[j][k][e] = pBt[i];
+                            dc[j][k][e] = pCt[i];
+                        }
+                    }
+                for (uint32_t pg = 1; pg < npu; ++pg)
+#pragma unroll
+                    for (int j = 0; j < HU; ++j)
+#pragma unroll
+                        for (int k = 0; k < RM; ++k)
+#pragma unroll
+                            for (int e = 0; e < 2; ++e) {
+                                const uint32_t i = ((rc[k] * Hu + hj[j]) * npu + pg) * Nu + nc[e];
+                                db[j][k][e] += pBt[i];
+                                dc[j][k][e] += pCt[i];
+                            }
+#pragma unroll
+                for (int j = 0; j < HU; ++j) {
+                    float cs[2] = {1.f, 1.f}, sn[2] = {0.f, 0.f};
+                    if (phit) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const float rev = ph[j][e] * kInv2Pi;
+                            cs[e] = __builtin_amdgcn_cosf(rev);
+                            sn[e] = __builtin_amdgcn_sinf(rev);
+                        }
+                    }
+                    float hvacc = 0.f, thacc[2] = {0.f, 0.f};
+#pragma unroll
+                    for (int k = 0; k < RM; ++k) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            float bd = db[j][k][e], cd = dc[j][k][e];
+                            if (!(ok[k][e] && hok[j])) bd = cd = 0.f;
+                            if (phit) {
+                                // partials of the folded frame: dB = R(Phi_t) dB~, dC = R(Phi_t) dC~
+                                const float part = (lane & 1) ? sn[e] : -sn[e];
+                                const float bp = __shfl_xor(bd, 1), cp = __shfl_xor(cd, 1);
+                                bd = fmaf(cs[e], bd, part * bp);
+                                cd = fmaf(cs[e], cd, part * cp);
+                            }
+                            sb[k][e] += bd;
+                            sc[k][e] += cd;
+                            hvacc = fmaf(cn[k][e], cd, fmaf(-bn[k][e], bd, hvacc));
+                            if (rot) {
+                                // lanes n (even) and n + 1: (dC_n C_n+1 - dC_n+1 C_n) + (dB_n B_n+1 - dB_n+1 B_n)
+                                const float cdn = __shfl_xor(cd, 1), cnn = __shfl_xor(cn[k][e], 1);
+                                const float bdn = __shfl_xor(bd, 1), bnn = __shfl_xor(bn[k][e], 1);
+                                thacc[e] += (cd * cnn - cdn * cn[k][e]) + (bd * bnn - bdn * bn[k][e]);
+                            }
+                        }
+                    }
+                    if (!hok[j]) continue;
+                    for (int o = 32; o >= 1; o >>= 1) hvacc += __shfl_xor(hvacc, o);
+                    const int64_t ht = bt * H + hj[j];
+                    if (lane == 0) hv[ht] = r0 == 0 ? hvacc : hv[ht] + hvacc;
+                    if (rot) {
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            if ((lane & 1) == 0 && nok[e]) {
+                                float* q = tht + hj[j] * (Nu / 2) + ((lane + 64 * e) >> 1);
+                                *q = r0 == 0 ? thacc[e] : *q + thacc[e];
+                            }
+                        }
                     }
                 }
-                sb += db;
-                sc += dc;
-                // per head: C . dC - B . dB over n (and ranks), and the pair cross products
-                float v = cn * dc - bn * db;
-                for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-                if (lane == 0) sred[wvi][0] = v;
-                if (rot) {
-                    // lanes n (even) and n + 1: (dC_n C_n+1 - dC_n+1 C_n) + (dB_n B_n+1 - dB_n+1 B_n)
-                    const float dcn = __shfl_xor(dc, 1), cnn = __shfl_xor(cn, 1);
-                    const float dbn = __shfl_xor(db, 1), bnn = __shfl_xor(bn, 1);
-                    if ((n & 1) == 0 && n < N) {
-                        const float cr = (dc * cnn - dcn * cn) + (db * bnn - dbn * bn);
-                        float* tp = th + (((b * T + t) * H + h) * (N / 2) + n / 2);
-                        *tp = (r == 0 ? 0.f : *tp) + cr;
-                    }
-                }
-                __syncthreads();
-                if (n == 0) {
-                    float* hp = hv + (b * T + t) * H + h;
-                    *hp = (r == 0 ? 0.f : *hp) + sred[0][0] + sred[1][0];
-                }
-                __syncthreads();
             }
-            if (n < N) {
-                dB[(row * G + g) * N + n] = sb;
-                dC[(row * G + g) * N + n] = sc;
+#pragma unroll
+            for (int k = 0; k < RM; ++k)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    sred[0][w][k][lane + 64 * e] = sb[k][e];
+                    sred[1][w][k][lane + 64 * e] = sc[k][e];
+                }
+            __syncthreads();
+            for (int i = tid; i < RM * 128; i += 256) {
+                const int k = i >> 7, n = i & 127;
+                if (n >= N || r0 + k >= R) continue;
+                const float vb = sred[0][0][k][n] + sred[0][1][k][n] + sred[0][2][k][n] + sred[0][3][k][n];
+                const float vc = sred[1][0][k][n] + sred[1][1][k][n] + sred[1][2][k][n] + sred[1][3][k][n];
+                const uint32_t o = ((uint32_t)(r0 + k) * Gu + g) * Nu + n;
+                dBt[o] = vb;
+                dCt[o] = vc;
             }
+            __syncthreads();
         }
     }
+}
+
+// the blocks of the reduction: one rank and four heads per pass, two ranks
+// and two heads, or four ranks and one head
+template <typename TI>
+void* bwd_reduce_for(int64_t R) {
+    if (R <= 1) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 1, 4>);
+    if (R == 2) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 2, 2>);
+    return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 4, 1>);
 }
 
 // dda and dtheta are reverse cumulative sums over the steps of the per-step
@@ -1319,6 +1537,45 @@ __global__ __launch_bounds__(128) void ssd_bwd_reduce(const float* __restrict__ 
 // and dD (per (batch, head)), the sums of chunks of kScanChunk steps, and the
 // scan of each chunk from the sums of the chunks after it.
 constexpr int kScanChunk = 256;
+
+// Phi[b,t,h,k] = sum over s <= t of theta[b,s,h,k], kept in [-pi, pi] (the
+// running sum is wrapped each step so that it keeps its absolute precision;
+// 2 pi split into a head exact in few bits and a tail, as in Cody and
+// Waite's argument reduction). Two kernels over chunks of kScanChunk steps:
+// the chunks' sums, then each chunk's scan from the earlier chunks' sums.
+// Thread -> (batch-head, chunk, pair), pairs fastest.
+__device__ __forceinline__ float wrap_2pi(float v) {
+    const float m = rintf(v * kInv2Pi);
+    return fmaf(-m, 1.9353071795864769e-3f, fmaf(-m, 6.28125f, v));
+}
+
+__global__ __launch_bounds__(256) void ssd_bwd_phi_sums(const float* __restrict__ theta, float* __restrict__ psum,
+                                                       int64_t T, int64_t H, int64_t NH, int nchunk, int64_t items) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= items) return;
+    const int64_t k = i % NH, ch = (i / NH) % nchunk, bh = i / (NH * nchunk), h = bh % H, b = bh / H;
+    const int64_t t0 = ch * (int64_t)kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int64_t t = t0; t < t1; ++t) acc += theta[((b * T + t) * H + h) * NH + k];
+    psum[i] = wrap_2pi(acc);
+}
+
+__global__ __launch_bounds__(256) void ssd_bwd_phi(const float* __restrict__ theta, const float* __restrict__ psum,
+                                                  float* __restrict__ phi, int64_t T, int64_t H, int64_t NH,
+                                                  int nchunk, int64_t items) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= items) return;
+    const int64_t k = i % NH, ch = (i / NH) % nchunk, bh = i / (NH * nchunk), h = bh % H, b = bh / H;
+    float run = 0.f;
+    for (int c = 0; c < ch; ++c) run = wrap_2pi(run + psum[(bh * nchunk + c) * NH + k]);
+    const int64_t t0 = ch * (int64_t)kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
+    for (int64_t t = t0; t < t1; ++t) {
+        const int64_t o = ((b * T + t) * H + h) * NH + k;
+        run = wrap_2pi(run + theta[o]);
+        phi[o] = run;
+    }
+}
 
 __global__ __launch_bounds__(128) void ssd_bwd_final_terms(const float* __restrict__ dfinal,
                                                           const float* __restrict__ fin,
@@ -1405,21 +1662,22 @@ void* bwd_forward_np(int NP) {
     return nullptr;
 }
 
+template <bool ROT>
 void* bwdc_forward_np(int NP) {
     switch (NP) {
-        case 32: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<32>);
-        case 64: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<64>);
-        case 128: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<128>);
+        case 32: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<32, ROT>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<64, ROT>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwdc_forward_kernel<128, ROT>);
     }
     return nullptr;
 }
 
-template <int MODE>
+template <int MODE, bool ROT>
 void* bwdc_backward_np(int NP) {
     switch (NP) {
-        case 32: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<32, MODE>);
-        case 64: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<64, MODE>);
-        case 128: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<128, MODE>);
+        case 32: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<32, MODE, ROT>);
+        case 64: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<64, MODE, ROT>);
+        case 128: return reinterpret_cast<void*>(&ssd_bwdc_backward_kernel<128, MODE, ROT>);
     }
     return nullptr;
 }
@@ -1485,17 +1743,21 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     const bool bf = d->in_dtype == SSD_BF16;
     // bf16 without rotation and a whole head per workgroup: the chunked walks;
     // otherwise the step-by-step walks
-    const bool chunked = bf && !rot && P <= kRowGroup;
-    void* kf = chunked ? bwdc_forward_np(NP) : bf ? bwd_forward_np<uint16_t>(NP) : bwd_forward_np<float>(NP);
-    void* kb0 = chunked ? bwdc_backward_np<0>(NP) : bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
-    void* kb1 = chunked ? bwdc_backward_np<1>(NP) : bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
-    void* kr = bf ? reinterpret_cast<void*>(&ssd_bwd_reduce<uint16_t>) : reinterpret_cast<void*>(&ssd_bwd_reduce<float>);
+    const bool chunked = bf && P <= kRowGroup;
+    void* kf = chunked ? (rot ? bwdc_forward_np<true>(NP) : bwdc_forward_np<false>(NP))
+                       : bf ? bwd_forward_np<uint16_t>(NP) : bwd_forward_np<float>(NP);
+    void* kb0 = chunked ? (rot ? bwdc_backward_np<0, true>(NP) : bwdc_backward_np<0, false>(NP))
+                        : bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
+    void* kb1 = chunked ? (rot ? bwdc_backward_np<1, true>(NP) : bwdc_backward_np<1, false>(NP))
+                        : bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
+    void* kr = bf ? bwd_reduce_for<uint16_t>(R) : bwd_reduce_for<float>(R);
     if (!kf || !kb0 || !kb1) return SSD_ERR_UNSUPPORTED;
     const int PG = (int)(P < kRowGroup ? P : kRowGroup), npg = (int)(P / PG);
     if (chunked && npg != 1) return SSD_ERR_UNSUPPORTED;
     const int S = pl.S;
     const int64_t nwg = b * H * npg * S;
     if (nwg > 0x7fffffff || b * T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
+    if (R * H * npg * N > 0x7fffffff) return SSD_ERR_UNSUPPORTED;   // one step's partials, 32-bit offsets
     if ((b * H * ((T + kScanChunk - 1) / kScanChunk) * (N / 2 + 1) + 127) / 128 > 0x7fffffff)
         return SSD_ERR_UNSUPPORTED;
 
@@ -1515,6 +1777,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     const size_t o_sums = take(S > 1 ? (size_t)(b * H * S * (N / 2 + 1)) * 4 : 4);
     const int64_t nchunks = (T + kScanChunk - 1) / kScanChunk;
     const size_t o_ft = take((size_t)(b * H * (N / 2 + 1)) * 4);
+    const bool cphi = chunked && rot;                  // the folded frame's angles
+    const size_t o_phi = take(cphi ? (size_t)(b * T * H * (N / 2)) * 4 : 4);
     const size_t o_csum = take((size_t)(b * H * nchunks * (N / 2 + 1)) * 4);
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
     int entry = -1;
@@ -1528,11 +1792,26 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     ba.init = init_state; ba.dfinal = dfinal; ba.dx = dx; ba.dinit = dinit;
     ba.T = T; ba.H = H; ba.G = G; ba.N = N; ba.R = R; ba.P = P;
     ba.PG = PG; ba.S = S; ba.SF = pl.SF; ba.nsub = pl.nsub; ba.Qt = pl.Qt; ba.log2R = pl.log2R;
+    float* phi = cphi ? reinterpret_cast<float*>(ws + o_phi) : nullptr;
+    ba.phi = phi;
     const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + kMemWaves)));
 
+    // 0. the cumulative angles (chunked walks with rotation)
+    ssd_status rs = SSD_OK;
+    if (cphi) {
+        // chunk sums of theta in the dda scan's chunk-sum buffer (free until then)
+        const int nch = (int)((T + kScanChunk - 1) / kScanChunk);
+        const int64_t n = b * H * nch * (N / 2);
+        float* psum = reinterpret_cast<float*>(ws + o_csum);
+        hipLaunchKernelGGL(ssd_bwd_phi_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, theta, psum, T, H,
+                           N / 2, nch, n);
+        hipLaunchKernelGGL(ssd_bwd_phi, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, theta, psum, phi, T, H,
+                           N / 2, nch, n);
+        if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
+    }
     // 1. forward walk: states from the forward's state passes, dC partials, final state
     float* fws_state = nullptr;
-    ssd_status rs = states_launch(pl, rot, x, da, B, init_state, theta, ws + o_states, hs, &fws_state);
+    if (rs == SSD_OK) rs = states_launch(pl, rot, x, da, B, init_state, theta, ws + o_states, hs, &fws_state);
     if (rs == SSD_OK) {
         BwdArgs fa = ba;
         fa.seg_in = fws_state;
@@ -1544,7 +1823,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     // 2. backward state pass and reverse carry (more than one segment)
     float* seg_in = reinterpret_cast<float*>(ws + o_segin);
     if (rs == SSD_OK && S > 1) {
-        hipLaunchKernelGGL(ssd_bwd_segsums, dim3((unsigned)(b * H * S)), dim3(128), 0, hs, da, theta,
+        hipLaunchKernelGGL(ssd_bwd_segsums, dim3((unsigned)(b * H * S)), dim3(128), 0, hs, da, theta, phi,
                            reinterpret_cast<float*>(ws + o_sums), T, H, N, S, pl.nsub, pl.Qt);
         if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
         if (rs == SSD_OK) {
@@ -1578,10 +1857,11 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         float* th = reinterpret_cast<float*>(ws + o_th);
         int64_t Tv = T, Hv = H, Gv = G, Nv = N, Rv = R;
         int npgv = npg, rotv = rot ? 1 : 0;
+        const float* phiv = phi;
         void* kargs[] = {(void*)&pC, (void*)&pB, (void*)&B, (void*)&C, (void*)&dB, (void*)&dC, (void*)&hv,
                          (void*)&th, (void*)&Tv, (void*)&Hv, (void*)&Gv, (void*)&Nv, (void*)&Rv, (void*)&npgv,
-                         (void*)&rotv};
-        if (hipLaunchKernel(kr, dim3((unsigned)(b * T)), dim3(128), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+                         (void*)&rotv, (void*)&phiv};
+        if (hipLaunchKernel(kr, dim3((unsigned)(b * T)), dim3(256), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
         // final-state terms and dD; chunk sums; chunk scans (columns from k0:
         // all pairs with rotation, only the decay column without)
         const int nc = (int)(N / 2 + 1), nchunk = (int)((T + kScanChunk - 1) / kScanChunk);

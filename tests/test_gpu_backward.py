@@ -94,6 +94,14 @@ CASES = [
     (1, 64, 128, 1, 2, 1, "bf16", False, True, "randn", True),
     (500, 64, 128, 8, 2, 2, "bf16", False, False, "randn", True),
     (45, 32, 128, 2, 2, 1, "bf16", False, True, "randn", True),
+    # bf16 with rotation, headdim <= 64: the chunked walks in the folded frame
+    (210, 32, 64, 8, 4, 2, "bf16", True, True, "randn", True),
+    (1, 16, 32, 4, 2, 1, "bf16", True, True, "none", True),
+    # the partials' reduction in several rank passes with odd head counts,
+    # and nine heads a group at rank 1 (heads four at a time)
+    (90, 32, 64, 8, 5, 1, "bf16", True, True, "randn", True),
+    (70, 16, 32, 16, 3, 1, "f32", True, True, "none", True),
+    (110, 64, 128, 1, 18, 2, "bf16", True, False, "randn", True),
 ]
 
 
