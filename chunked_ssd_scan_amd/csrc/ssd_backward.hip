@@ -122,15 +122,12 @@ struct Stager {
     float4 rdy[St::DYR];
     uint4 rb[WANT_B ? St::BRG : 1];
     uint4 rc[WANT_C ? St::BRG : 1];
-    float4 rpb[(TURN && WANT_B) ? St::BRG : 1], rpc[(TURN && WANT_C) ? St::BRG : 1];
+    // the angles of a unit's pairs: B and C units of one row share them
+    static constexpr bool OWN_PC = TURN && WANT_C && !WANT_B;
+    float4 rpb[(TURN && WANT_B) ? St::BRG : 1], rpc[OWN_PC ? St::BRG : 1];
     float4 rth[St::THR];
     float rda;
 
-    // Phi of the 4 pairs of a staged 16-byte unit (row r of tile k, columns c..c+7)
-    __device__ float4 load_phi(const BwdArgs& a, int64_t f, int c, int64_t b, int64_t h) const {
-        const int64_t t = f / a.R;
-        return *reinterpret_cast<const float4*>(a.phi + ((b * a.T + t) * a.H + h) * (a.N / 2) + c / 2);
-    }
     // the 4 pairs of v turned by R(-Phi): (e0, e1) -> (c e0 + s e1, c e1 - s e0)
     __device__ static uint4 turn(uint4 v, float4 ph) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -148,68 +145,84 @@ struct Stager {
         return make_uint4(o[0], o[1], o[2], o[3]);
     }
 
+    // a load at a byte offset from a tile's base (the base is uniform, the
+    // offset a 32-bit lane value)
+    template <typename V, typename E>
+    __device__ static V at(const E* base, uint32_t byteoff) {
+        return *reinterpret_cast<const V*>(reinterpret_cast<const char*>(base) + byteoff);
+    }
+
     __device__ void load(const BwdArgs& a, int k, int mt, int64_t b, int64_t h, int64_t g, int pbase) {
         const int64_t T = a.T, H = a.H, G = a.G, N = a.N, P = a.P, TR = a.T * a.R;
-        const int64_t f0 = (int64_t)k * kTileRows;
+        const int64_t f0 = (int64_t)k * kTileRows, rem = TR - f0;   // rows r < rem are in range
         const int PG = a.PG;
         const int xur = PG / St::EPU, dur = PG / 4, nbu = (int)(N / St::EPU), thu = (int)(N / 8);
+        // rows of x and dy are H P elements apart, rows of B and C G N
+        const uint32_t xrs = (uint32_t)(H * P), brs = (uint32_t)(G * N);
         if constexpr (WANT_X) {
-            const TI* xg = static_cast<const TI*>(a.x);
+            const TI* xt = static_cast<const TI*>(a.x) + ((b * TR + f0) * H + h) * P + pbase;
 #pragma unroll
             for (int m = 0; m < St::XR; ++m) {
                 const int u = mt + m * St::NTM, r = u / xur, c = (u % xur) * St::EPU;
-                rx[m] = (u < kTileRows * xur && f0 + r < TR)
-                            ? *reinterpret_cast<const uint4*>(xg + ((b * TR + f0 + r) * H + h) * P + pbase + c)
-                            : make_uint4(0, 0, 0, 0);
+                rx[m] = (u < kTileRows * xur && r < rem) ? at<uint4>(xt, ((uint32_t)r * xrs + c) * sizeof(TI))
+                                                         : make_uint4(0, 0, 0, 0);
             }
         }
+        {
+            const float* dyt = a.dy + ((b * TR + f0) * H + h) * P + pbase;
 #pragma unroll
-        for (int m = 0; m < St::DYR; ++m) {
-            const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
-            rdy[m] = (u < kTileRows * dur && f0 + r < TR)
-                         ? *reinterpret_cast<const float4*>(a.dy + ((b * TR + f0 + r) * H + h) * P + pbase + c)
-                         : make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int m = 0; m < St::DYR; ++m) {
+                const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
+                rdy[m] = (u < kTileRows * dur && r < rem) ? at<float4>(dyt, ((uint32_t)r * xrs + c) * 4u)
+                                                          : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
+        // with TURN, the angles of the tile's steps: row r is step f0 / R + r / R
+        const float* pht = nullptr;
+        if constexpr (TURN) pht = a.phi + ((b * T + (f0 >> a.log2R)) * H + h) * (N / 2);
+        const uint32_t prs = (uint32_t)(H * (N / 2));
         if constexpr (WANT_B) {
-            const TI* Bg = static_cast<const TI*>(a.B);
+            const TI* Bt = static_cast<const TI*>(a.B) + ((b * TR + f0) * G + g) * N;
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
                 const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
-                rb[m] = (u < kTileRows * nbu && f0 + r < TR)
-                            ? *reinterpret_cast<const uint4*>(Bg + ((b * TR + f0 + r) * G + g) * N + c)
-                            : make_uint4(0, 0, 0, 0);
+                const bool ok = u < kTileRows * nbu && r < rem;
+                rb[m] = ok ? at<uint4>(Bt, ((uint32_t)r * brs + c) * sizeof(TI)) : make_uint4(0, 0, 0, 0);
                 if constexpr (TURN)
-                    rpb[m] = (u < kTileRows * nbu && f0 + r < TR) ? load_phi(a, f0 + r, c, b, h)
-                                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                    rpb[m] = ok ? at<float4>(pht, (((uint32_t)r >> a.log2R) * prs + c / 2) * 4u)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         if constexpr (WANT_C) {
-            const TI* Cg = static_cast<const TI*>(a.C);
+            const TI* Ct = static_cast<const TI*>(a.C) + ((b * TR + f0) * G + g) * N;
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
                 const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
-                rc[m] = (u < kTileRows * nbu && f0 + r < TR)
-                            ? *reinterpret_cast<const uint4*>(Cg + ((b * TR + f0 + r) * G + g) * N + c)
-                            : make_uint4(0, 0, 0, 0);
-                if constexpr (TURN)
-                    rpc[m] = (u < kTileRows * nbu && f0 + r < TR) ? load_phi(a, f0 + r, c, b, h)
-                                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+                const bool ok = u < kTileRows * nbu && r < rem;
+                rc[m] = ok ? at<uint4>(Ct, ((uint32_t)r * brs + c) * sizeof(TI)) : make_uint4(0, 0, 0, 0);
+                if constexpr (OWN_PC)
+                    rpc[m] = ok ? at<float4>(pht, (((uint32_t)r >> a.log2R) * prs + c / 2) * 4u)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
             }
         }
         const int64_t t0 = (int64_t)k * a.Qt;
+        if constexpr (!RAW) {
+            const float* tht = a.theta ? a.theta + ((b * T + t0) * H + h) * (N / 2) : nullptr;
 #pragma unroll
-        for (int m = 0; m < St::THR; ++m) {
-            const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (!RAW && a.theta && st < a.Qt && t0 + st < T)
-                v = *reinterpret_cast<const float4*>(a.theta + ((b * T + t0 + st) * H + h) * (N / 2) + c);
-            rth[m] = v;
+            for (int m = 0; m < St::THR; ++m) {
+                const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
+                rth[m] = (tht && st < a.Qt && t0 + st < T) ? at<float4>(tht, ((uint32_t)st * prs + c) * 4u)
+                                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
         }
-        rda = (mt < a.Qt && t0 + mt < T) ? a.da[(b * T + t0 + mt) * H + h] : 0.f;
+        const float* dat = a.da + (b * T + t0) * H + h;
+        rda = (mt < a.Qt && t0 + mt < T) ? at<float>(dat, (uint32_t)mt * (uint32_t)H * 4u) : 0.f;
     }
 
     __device__ void store(const StageMem<TI>& s, const BwdArgs& a, int buf, int mt) {
-        constexpr int XS = St::ROWS * St::LDX, BS = St::ROWS * St::LDB;
+        // the chunked walks read no row past a tile: their buffers hold 32 rows
+        constexpr int RW = RAW ? kTileRows : St::ROWS;
+        constexpr int XS = RW * St::LDX, BS = RW * St::LDB;
         const int PG = a.PG, N = (int)a.N;
         const int xur = PG / St::EPU, dur = PG / 4, nbu = N / St::EPU, thu = N / 8;
         if constexpr (WANT_X) {
@@ -247,7 +260,7 @@ struct Stager {
             for (int m = 0; m < St::BRG; ++m) {
                 const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
                 if (u < kTileRows * nbu)
-                    *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = TURN ? turn(rc[m], rpc[m]) : rc[m];
+                    *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = TURN ? turn(rc[m], OWN_PC ? rpc[m] : rpb[m]) : rc[m];
             }
         }
 #pragma unroll
@@ -872,23 +885,52 @@ __device__ __forceinline__ void turn_np(f32x4 (&hn)[NT], const float* phirow, in
         }
 }
 
+// The state entering a tile, as bf16 [n][p] (row stride kLdh): every compute
+// wave puts its rows p0 .. p0 + 15 (accumulator layout D[p][n]) so that each
+// wave can contract over all p for its own column tiles.
+constexpr int kLdh = kRowGroup + 8;
+
+template <int NT>
+__device__ __forceinline__ void put_state(uint16_t* sH, const f32x4 (&hs)[NT], int p0, int lane) {
+    const int q = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int c = 0; c < NT; ++c) *reinterpret_cast<s16x4*>(sH + (16 * c + l16) * kLdh + p0 + 4 * q) = pack4_bf16(hs[c]);
+}
+
+// Rows f0 + 16 i + 4 q + v (< TR), column 16 c + l16 (< N) of a partial: two
+// accumulator blocks of a wave's column tile c
+__device__ __forceinline__ void store_rows(float* dst, const f32x4& z0, const f32x4& z1, int64_t f0, int64_t TR,
+                                           int N, int64_t rs, int c, int lane) {
+    const int q = lane >> 4, n = 16 * c + (lane & 15);
+    if (n >= N) return;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t r0 = f0 + 4 * q + v, r1 = r0 + 16;
+        if (r0 < TR) dst[r0 * rs + n] = z0[v];
+        if (r1 < TR) dst[r1 * rs + n] = z1[v];
+    }
+}
+
 // Forward direction: the head's dC partial rows and the final state. ROT: in
 // the folded frame g = R(-Phi) h (B~, C~ turned while staged; the partial
-// rows are dC~, turned back in the reduction).
+// rows are dC~, turned back in the reduction). Each compute wave keeps rows
+// p0 .. p0 + 15 of the state and, for the partial, takes the column tiles
+// c = wv, wv + nw, ... with the contraction over every p read from the staged
+// entering state.
 template <int NP, bool ROT>
-__global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kMaxWaves, 3) void ssd_bwdc_forward_kernel(BwdArgs a) {
     using TI = uint16_t;
     using St = Stage<TI, NP, true, true, false>;
-    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = St::ROWS, PAD = St::PAD;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = kTileRows;
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
     __shared__ float sA[2][kTileRows];
     __shared__ __attribute__((aligned(16))) uint16_t sM[3][16 * kLdm];
-    __shared__ __attribute__((aligned(16))) float4 sZ[kRowGroup / 16][2 * NT * 64];
+    __shared__ __attribute__((aligned(16))) uint16_t sH[NP * kLdh];
     const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], nullptr, nullptr, &sA[0][0]};
 
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
@@ -900,12 +942,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     float* dst = a.part + (b * TR * H + h) * N;            // [b][TR][H][N]
+    const int64_t rs = H * N;
 
-    for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
-        sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
-        sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
-    }
-    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    // columns n >= N of B stay zero
+    for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
     __syncthreads();
 
     if (memw) {
@@ -922,9 +962,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
                 st.store(sm, a, buf ^ 1, mt);
                 if (k + 2 < k1) st.load(a, k + 2, mt, b, h, g, 0);
             }
-            __syncthreads();                               // blocks built
-            __syncthreads();                               // shares in their slots
-            sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
+            __syncthreads();                               // blocks built, entering state put
+            __syncthreads();                               // tile walked
         }
         return;
     }
@@ -953,6 +992,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
         const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
         const float cum = tile_cum(sA[buf], Qt, log2R, lane);
         const float last = __shfl(cum, kTileRows - 1);
+        put_state<NT>(sH, hs, p0, lane);
         // G o L blocks (0,0), (1,0), (1,1): rows m of dy against rows j of x
         for (int u = wv; u < 3; u += nw) {
             const int mb = u == 0 ? 0 : 1, jb = u == 2 ? 1 : 0;
@@ -960,36 +1000,37 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
             put_masked(sM[u], gacc, mb, jb, false, cum, log2R, lane);
         }
         __syncthreads();
-        // dC = e^{cum_m} (dy h_in) over this wave's p  +  (G o L) B on the wave's column tiles
-        f32x4 z[2][NT];
+        // dC = e^{cum_m} (dy h_in) + (G o L) B on the wave's column tiles
+        float ein[2][4];
+        s16x4 dya[2][kRowGroup / 16];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const s16x4 dya = row4(tDy + (16 * i + l16) * LDX + p0 + 4 * q);
-            float ein[4];
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ein[v] = __expf(__shfl(cum, 16 * i + 4 * q + v));
+            for (int v = 0; v < 4; ++v) ein[i][v] = __expf(__shfl(cum, 16 * i + 4 * q + v));
 #pragma unroll
-            for (int c = 0; c < NT; ++c) {
-                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                z[i][c] = mma16(dya, pack4_bf16(hs[c]), zero);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) z[i][c][v] *= ein[v];
-            }
+            for (int kb = 0; kb < kRowGroup / 16; ++kb)
+                if (kb < nw) dya[i][kb] = row4(tDy + (16 * i + l16) * LDX + 16 * kb + 4 * q);
         }
         const s16x4 m00 = blk_rows(sM[0], lane), m10 = blk_rows(sM[1], lane), m11 = blk_rows(sM[2], lane);
+        for (int c = wv; c < NT; c += nw) {
+            f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < NT; ++c) {
-            if (c % nw != wv) continue;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const s16x4 bb = tr_rows4(tB, LDB, 16 * kb + 4 * q, 16 * c, lane);
-                if (kb == 0) {
-                    z[0][c] = mma16(m00, bb, z[0][c]);
-                    z[1][c] = mma16(m10, bb, z[1][c]);
-                } else {
-                    z[1][c] = mma16(m11, bb, z[1][c]);
-                }
+            for (int kb = 0; kb < kRowGroup / 16; ++kb) {
+                if (kb >= nw) break;
+                const s16x4 hb = row4(sH + (16 * c + l16) * kLdh + 16 * kb + 4 * q);
+                z0 = mma16(dya[0][kb], hb, z0);
+                z1 = mma16(dya[1][kb], hb, z1);
             }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                z0[v] *= ein[0][v];
+                z1[v] *= ein[1][v];
+            }
+            const s16x4 bb0 = tr_rows4(tB, LDB, 4 * q, 16 * c, lane), bb1 = tr_rows4(tB, LDB, 16 + 4 * q, 16 * c, lane);
+            z0 = mma16(m00, bb0, z0);
+            z1 = mma16(m10, bb0, z1);
+            z1 = mma16(m11, bb1, z1);
+            store_rows(dst, z0, z1, (int64_t)k * kTileRows, TR, (int)N, rs, c, lane);
         }
         // h <- e^{last} h + (w o x)^T B
         const float carry = __expf(last);
@@ -1010,9 +1051,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
             for (int kb = 0; kb < 2; ++kb)
                 hs[c] = mma16(xw[kb], tr_rows4(tB, LDB, 16 * kb + 4 * q, 16 * c, lane), hs[c]);
         }
-        put_frags<NT>(sZ[wv], z, lane);
-        __syncthreads();
-        sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
+        __syncthreads();                           // tile walked: its buffers and sH free
     }
     if (seg == S - 1 && a.final_state) {
         if (ROT) turn_pn<NT>(hs, a.phi + ((b * T + T - 1) * H + h) * (N / 2), (int)N, 1.f, lane);
@@ -1029,24 +1068,27 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_forward_kernel(BwdArg
 // Backward direction (tiles in reverse). MODE 1: only the state gradient, from
 // zero, to the segment's left end (the carry's local term); MODE 0: dx, the
 // head's dB partial, the dy . x partial and dinit. ROT: the gradient of the
-// folded state G = R(-Phi) H, converted at the segment ends.
+// folded state G = R(-Phi) H, converted at the segment ends. Each compute wave
+// keeps rows p0 .. p0 + 15 of the state gradient; MODE 0 stages the entering
+// one as bf16 [n][p], read transposed for dx and, for the dB partial on the
+// wave's column tiles c = wv, wv + nw, ..., contracted over every p.
 template <int NP, int MODE, bool ROT>
 __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdArgs a) {
     using TI = uint16_t;
     constexpr bool OUT = MODE == 0;
     using St = Stage<TI, NP, OUT, OUT, true>;
-    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = St::ROWS, PAD = St::PAD;
+    constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = kTileRows;
     __shared__ __attribute__((aligned(16))) TI sX[2][OUT ? ROWS * LDX : 8];
     __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][OUT ? ROWS * LDB : 8];
     __shared__ __attribute__((aligned(16))) TI sC[2][ROWS * LDB];
     __shared__ float sA[2][kTileRows];
     __shared__ __attribute__((aligned(16))) uint16_t sM[OUT ? 6 : 1][16 * kLdm];
-    __shared__ __attribute__((aligned(16))) float4 sZ[OUT ? kRowGroup / 16 : 1][OUT ? 2 * NT * 64 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sH[OUT ? NP * kLdh : 8];
     __shared__ float sDd[kRowGroup / 16];
     const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], &sC[0][0], nullptr, &sA[0][0]};
 
-    const int tid = threadIdx.x, nthr = blockDim.x;
+    const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
@@ -1058,12 +1100,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     float* dst = OUT ? a.part + (b * TR * H + h) * N : nullptr;
+    const int64_t rs = H * N;
 
-    for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
-        if (OUT) sX[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
-        sDy[i / (PAD * LDX)][kTileRows * LDX + i % (PAD * LDX)] = TI(0);
-    }
-    for (int i = tid; i < 2 * ROWS * LDB; i += nthr) {
+    // columns n >= N of B and C stay zero
+    for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) {
         if (OUT) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
         sC[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
     }
@@ -1083,18 +1123,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                 st.store(sm, a, buf ^ 1, mt);
                 if (k - 2 >= k0) st.load(a, k - 2, mt, b, h, g, 0);
             }
-            __syncthreads();                                   // blocks built / tile walked
-            if constexpr (OUT) {
-                __syncthreads();                               // shares in their slots
-                sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
-            }
+            if constexpr (OUT) __syncthreads();                // blocks built, entering state put
+            __syncthreads();                                   // tile walked
         }
         __syncthreads();                                       // the dy . x shares
         return;
     }
 
     const int p0 = 16 * wv;
-    f32x4 hp[NT], hn[NT];                          // D[p][n] and D[n][p]
+    f32x4 hp[NT];                                  // D[p][n]: rows p0 + 4q + v, column 16c + l16
     {
         const float* src = nullptr;
         int64_t off = 0;
@@ -1111,18 +1148,12 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
         for (int c = 0; c < NT; ++c) {
             const int n = 16 * c + l16;
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                hp[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
-                const int nn = 16 * c + 4 * q + v;
-                hn[c][v] = (OUT && src && nn < N) ? src[off + (int64_t)(p0 + l16) * N + nn] : 0.f;
-            }
+            for (int v = 0; v < 4; ++v) hp[c][v] = (src && n < N) ? src[off + (int64_t)(p0 + 4 * q + v) * N + n] : 0.f;
         }
         // the physical gradient at the segment's last step, into the folded frame
         if (ROT && OUT && src) {
             const int64_t tl = (((int64_t)k1 * Qt < T) ? (int64_t)k1 * Qt : T) - 1;
-            const float* pr = a.phi + ((b * T + tl) * H + h) * (N / 2);
-            turn_pn<NT>(hp, pr, (int)N, -1.f, lane);
-            turn_np<NT>(hn, pr, (int)N, -1.f, lane);
+            turn_pn<NT>(hp, a.phi + ((b * T + tl) * H + h) * (N / 2), (int)N, -1.f, lane);
         }
     }
     const float Dh = (OUT && a.D) ? a.D[h] : 0.f;
@@ -1137,16 +1168,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
         if constexpr (OUT) {
             const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
             const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
-            // the tile's fp32 dy (for D dy and the dy . x sum), loaded now, used last
             const int64_t f0 = (int64_t)k * kTileRows;
-            float dyr[2][4];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * q + v;
-                    dyr[i][v] = (f0 + r < TR) ? a.dy[((b * TR + f0 + r) * H + h) * P + p0 + l16] : 0.f;
-                }
+            put_state<NT>(sH, hp, p0, lane);
             // upper blocks (0,0), (0,1), (1,1): CB' = B_m . C_j (jobs 0-2) and
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
             for (int u = wv; u < 6; u += nw) {
@@ -1161,20 +1184,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) wr[i][v] = __expf(last - __shfl(cum, 16 * i + 4 * q + v));
-            // dx = w o (B H^T) + (CB' o L') dy;  dB share = w o (x H) (+ (G' o L') C on the wave's tiles)
-            f32x4 zx[2], zb[2][NT];
+            // dx = w o (B H^T) + (CB' o L') dy over this wave's p
+            f32x4 zx[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 zx[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-                const s16x4 xs = row4(tX + (16 * i + l16) * LDX + p0 + 4 * q);
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
                     const s16x4 bs = row4(tB + (16 * i + l16) * LDB + 16 * c + 4 * q);
-                    zx[i] = mma16(bs, pack4_bf16(hn[c]), zx[i]);
-                    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                    zb[i][c] = mma16(xs, pack4_bf16(hp[c]), zero);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) zb[i][c][v] *= wr[i][v];
+                    zx[i] = mma16(bs, tr_rows4(sH, kLdh, 16 * c + 4 * q, p0, lane), zx[i]);
                 }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) zx[i][v] *= wr[i][v];
@@ -1185,18 +1203,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                 zx[0] = mma16(c00, d0, zx[0]);
                 zx[0] = mma16(c01, d1, zx[0]);
                 zx[1] = mma16(c11, d1, zx[1]);
-                const s16x4 g00 = blk_rows(sM[3], lane), g01 = blk_rows(sM[4], lane), g11 = blk_rows(sM[5], lane);
+            }
+            // dB partial = w o (x H) + (G' o L') C on the wave's column tiles
+            {
+                s16x4 xs[2][kRowGroup / 16];
 #pragma unroll
-                for (int c = 0; c < NT; ++c) {
-                    if (c % nw != wv) continue;
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int kb = 0; kb < kRowGroup / 16; ++kb)
+                        if (kb < nw) xs[i][kb] = row4(tX + (16 * i + l16) * LDX + 16 * kb + 4 * q);
+                const s16x4 g00 = blk_rows(sM[3], lane), g01 = blk_rows(sM[4], lane), g11 = blk_rows(sM[5], lane);
+                for (int c = wv; c < NT; c += nw) {
+                    f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < kRowGroup / 16; ++kb) {
+                        if (kb >= nw) break;
+                        const s16x4 hb = row4(sH + (16 * c + l16) * kLdh + 16 * kb + 4 * q);
+                        z0 = mma16(xs[0][kb], hb, z0);
+                        z1 = mma16(xs[1][kb], hb, z1);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        z0[v] *= wr[0][v];
+                        z1[v] *= wr[1][v];
+                    }
                     const s16x4 cc0 = tr_rows4(tC, LDB, 4 * q, 16 * c, lane);
                     const s16x4 cc1 = tr_rows4(tC, LDB, 16 + 4 * q, 16 * c, lane);
-                    zb[0][c] = mma16(g00, cc0, zb[0][c]);
-                    zb[0][c] = mma16(g01, cc1, zb[0][c]);
-                    zb[1][c] = mma16(g11, cc1, zb[1][c]);
+                    z0 = mma16(g00, cc0, z0);
+                    z0 = mma16(g01, cc1, z0);
+                    z1 = mma16(g11, cc1, z1);
+                    store_rows(dst, z0, z1, f0, TR, (int)N, rs, c, lane);
                 }
             }
-            // dx rows
+            // dx rows, with D dy and the dy . x sum from the tile's fp32 dy
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1204,58 +1243,32 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                     const int r = 16 * i + 4 * q + v;
                     if (f0 + r < TR) {
                         const int64_t o = ((b * TR + f0 + r) * H + h) * P + p0 + l16;
-                        a.dx[o] = fmaf(Dh, dyr[i][v], zx[i][v]);
-                        dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
+                        const float dyv = a.dy[o];
+                        a.dx[o] = fmaf(Dh, dyv, zx[i][v]);
+                        dd = fmaf(dyv, to_f32(sX[buf][r * LDX + p0 + l16]), dd);
                     }
                 }
-            // H <- e^{last} H + (e^{cum} o dy)^T C, both layouts
-            const float carry = __expf(last);
-            s16x4 ed[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
-                float e4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
-                ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
-            }
-#pragma unroll
-            for (int c = 0; c < NT; ++c) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    hp[c][v] *= carry;
-                    hn[c][v] *= carry;
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const s16x4 cc = tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane);
-                    hp[c] = mma16(ed[kb], cc, hp[c]);
-                    hn[c] = mma16(cc, ed[kb], hn[c]);
-                }
-            }
-            put_frags<NT>(sZ[wv], zb, lane);
-        } else {
-            const float carry = __expf(last);
-            s16x4 ed[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
-                float e4[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
-                ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
-            }
-#pragma unroll
-            for (int c = 0; c < NT; ++c) {
-#pragma unroll
-                for (int v = 0; v < 4; ++v) hp[c][v] *= carry;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-                    hp[c] = mma16(ed[kb], tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane), hp[c]);
-            }
         }
-        __syncthreads();                           // shares in their slots (MODE 1: tile walked)
-        if constexpr (OUT) sum_frags<NT>(&sZ[0][0], nw, dst, (int64_t)k * kTileRows, TR, (int)N, H * N, tid, nthr);
+        // H <- e^{last} H + (e^{cum} o dy)^T C
+        const float carry = __expf(last);
+        s16x4 ed[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
+            float e4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
+            ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
+        }
+#pragma unroll
+        for (int c = 0; c < NT; ++c) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) hp[c][v] *= carry;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                hp[c] = mma16(ed[kb], tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane), hp[c]);
+        }
+        __syncthreads();                           // tile walked: its buffers and sH free
     }
     float* out = nullptr;
     if (!OUT && seg > 0) out = a.seg_out + (bh * S + seg) * P * N;
@@ -1758,6 +1771,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     const int64_t nwg = b * H * npg * S;
     if (nwg > 0x7fffffff || b * T > 0x7fffffff) return SSD_ERR_UNSUPPORTED;
     if (R * H * npg * N > 0x7fffffff) return SSD_ERR_UNSUPPORTED;   // one step's partials, 32-bit offsets
+    // a tile's rows of x, dy, B, C and its steps' angles: 32-bit byte offsets
+    if ((int64_t)kTileRows * H * (P > N ? P : N) * 4 > 0xffffffffLL) return SSD_ERR_UNSUPPORTED;
     if ((b * H * ((T + kScanChunk - 1) / kScanChunk) * (N / 2 + 1) + 127) / 128 > 0x7fffffff)
         return SSD_ERR_UNSUPPORTED;
 
