@@ -1168,7 +1168,16 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
         if constexpr (OUT) {
             const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
             const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
+            // the tile's fp32 dy (for D dy and the dy . x sum), loaded now, used last
             const int64_t f0 = (int64_t)k * kTileRows;
+            float dyr[2][4];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * q + v;
+                    dyr[i][v] = (f0 + r < TR) ? a.dy[((b * TR + f0 + r) * H + h) * P + p0 + l16] : 0.f;
+                }
             put_state<NT>(sH, hp, p0, lane);
             // upper blocks (0,0), (0,1), (1,1): CB' = B_m . C_j (jobs 0-2) and
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
@@ -1235,7 +1244,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                     store_rows(dst, z0, z1, f0, TR, (int)N, rs, c, lane);
                 }
             }
-            // dx rows, with D dy and the dy . x sum from the tile's fp32 dy
+            // dx rows
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1243,9 +1252,8 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                     const int r = 16 * i + 4 * q + v;
                     if (f0 + r < TR) {
                         const int64_t o = ((b * TR + f0 + r) * H + h) * P + p0 + l16;
-                        const float dyv = a.dy[o];
-                        a.dx[o] = fmaf(Dh, dyv, zx[i][v]);
-                        dd = fmaf(dyv, to_f32(sX[buf][r * LDX + p0 + l16]), dd);
+                        a.dx[o] = fmaf(Dh, dyr[i][v], zx[i][v]);
+                        dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
                     }
                 }
         }
