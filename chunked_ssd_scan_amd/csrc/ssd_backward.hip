@@ -276,7 +276,31 @@ struct Stager {
                 }
             }
         }
-        if (mt < a.Qt) s.sA[buf * kTileRows + mt] = RAW ? rda : __expf(rda);
+        if constexpr (RAW) {
+            // the first memory wave: the tile's decay sums for the compute
+            // waves, per fused row m: cum_m (the sum of da over the tile's
+            // steps up to m's), e^{cum_m} and e^{last - cum_m}, last = cum_31;
+            // lanes 32 .. 63 repeat lanes 0 .. 31
+            if (mt < 64) {
+                const int m = mt & 31, rmask = (1 << a.log2R) - 1;
+                float v = __shfl(rda, m >> a.log2R);
+                if (m & rmask) v = 0.f;
+#pragma unroll
+                for (int o = 1; o < kTileRows; o <<= 1) {
+                    const float u = __shfl_up(v, o);
+                    if (m >= o) v += u;
+                }
+                const float last = __shfl(v, kTileRows - 1);
+                if (mt < kTileRows) {
+                    float* d = s.sA + buf * 3 * kTileRows;
+                    d[m] = v;
+                    d[kTileRows + m] = __expf(v);
+                    d[2 * kTileRows + m] = __expf(last - v);
+                }
+            }
+        } else {
+            if (mt < a.Qt) s.sA[buf * kTileRows + mt] = __expf(rda);
+        }
     }
 };
 
@@ -758,18 +782,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
 
 constexpr int kLdm = 24;             // row stride of a staged 16 x 16 block (bf16)
 
-// inclusive sum over the tile rows of da at each step's first rank: lane m < 32
-// receives cum_m (rows past the tile's steps add zeros)
-__device__ __forceinline__ float tile_cum(const float* sDa, int Qt, int log2R, int lane) {
-    const int st = lane >> log2R;
-    float v = (lane < kTileRows && (lane & ((1 << log2R) - 1)) == 0 && st < Qt) ? sDa[st] : 0.f;
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-        const float u = __shfl_up(v, o);
-        if ((lane & 31) >= o) v += u;
-    }
-    return v;
-}
+// A tile's decay sums, staged per fused row m by the memory waves: cum_m at
+// [m], e^{cum_m} at [32 + m] and e^{last - cum_m} at [64 + m].
+constexpr int kCumE = kTileRows, kCumW = 2 * kTileRows;
 
 // D[m][j] = sum_k ta[mrow0 + m][k] tb[jrow0 + j][k] over k < K: rows of two
 // row-major bf16 tiles dotted along their columns (K a multiple of 16)
@@ -785,15 +800,17 @@ __device__ __forceinline__ f32x4 rows_dot(const uint16_t* ta, int lda, int mrow0
 // One 16 x 16 block (rows m in block mb, columns j in block jb) of a 32 x 32
 // tile matrix, decay-masked: upper (step(j) >= step(m), factor e^{cum_j - cum_m})
 // or lower (step(j) <= step(m), e^{cum_m - cum_j}); stored as bf16 [m][j].
-__device__ __forceinline__ void put_masked(uint16_t* dst, f32x4 acc, int mb, int jb, bool upper, float cum,
+__device__ __forceinline__ void put_masked(uint16_t* dst, f32x4 acc, int mb, int jb, bool upper, const float* cum,
                                            int log2R, int lane) {
     const int l16 = lane & 15, q = lane >> 4;
     const int j = 16 * jb + l16;
-    const float cj = __shfl(cum, j);
+    const float cj = cum[j];
+    const float4 c4 = *reinterpret_cast<const float4*>(cum + 16 * mb + 4 * q);
+    const float cmv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int m = 16 * mb + 4 * q + v;
-        const float cm = __shfl(cum, m);
+        const float cm = cmv[v];
         const int sm = m >> log2R, sj = j >> log2R;
         float val = 0.f;
         if (upper ? (sj >= sm) : (sj <= sm)) val = acc[v] * __expf(upper ? cj - cm : cm - cj);
@@ -925,7 +942,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void ssd_bwdc_forward_kernel(Bwd
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
-    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) float sA[2][3 * kTileRows];
     __shared__ __attribute__((aligned(16))) uint16_t sM[3][16 * kLdm];
     __shared__ __attribute__((aligned(16))) uint16_t sH[NP * kLdh];
     const StageMem<TI> sm{&sX[0][0], &sDy[0][0], &sB[0][0], nullptr, nullptr, &sA[0][0]};
@@ -990,8 +1007,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void ssd_bwdc_forward_kernel(Bwd
         const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
         const uint16_t* tDy = reinterpret_cast<const uint16_t*>(sDy[buf]);
         const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
-        const float cum = tile_cum(sA[buf], Qt, log2R, lane);
-        const float last = __shfl(cum, kTileRows - 1);
+        const float* cum = sA[buf];
         put_state<NT>(sH, hs, p0, lane);
         // G o L blocks (0,0), (1,0), (1,1): rows m of dy against rows j of x
         for (int u = wv; u < 3; u += nw) {
@@ -1006,7 +1022,7 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void ssd_bwdc_forward_kernel(Bwd
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) ein[i][v] = __expf(__shfl(cum, 16 * i + 4 * q + v));
+            for (int v = 0; v < 4; ++v) ein[i][v] = cum[kCumE + 16 * i + 4 * q + v];
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 16; ++kb)
                 if (kb < nw) dya[i][kb] = row4(tDy + (16 * i + l16) * LDX + 16 * kb + 4 * q);
@@ -1033,15 +1049,13 @@ __global__ __launch_bounds__(64 * kMaxWaves, 3) void ssd_bwdc_forward_kernel(Bwd
             store_rows(dst, z0, z1, (int64_t)k * kTileRows, TR, (int)N, rs, c, lane);
         }
         // h <- e^{last} h + (w o x)^T B
-        const float carry = __expf(last);
+        const float carry = cum[kCumE + kTileRows - 1];
         s16x4 xw[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const s16x4 xt = tr_rows4(tX, LDX, 16 * kb + 4 * q, p0, lane);
-            float w4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) w4[e] = __expf(last - __shfl(cum, 16 * kb + 4 * q + e));
-            xw[kb] = scale4(xt, w4[0], w4[1], w4[2], w4[3]);
+            const float4 w4 = *reinterpret_cast<const float4*>(cum + kCumW + 16 * kb + 4 * q);
+            xw[kb] = scale4(xt, w4.x, w4.y, w4.z, w4.w);
         }
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
@@ -1082,7 +1096,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
     __shared__ __attribute__((aligned(16))) TI sDy[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][OUT ? ROWS * LDB : 8];
     __shared__ __attribute__((aligned(16))) TI sC[2][ROWS * LDB];
-    __shared__ float sA[2][kTileRows];
+    __shared__ __attribute__((aligned(16))) float sA[2][3 * kTileRows];
     __shared__ __attribute__((aligned(16))) uint16_t sM[OUT ? 6 : 1][16 * kLdm];
     __shared__ __attribute__((aligned(16))) uint16_t sH[OUT ? NP * kLdh : 8];
     __shared__ float sDd[kRowGroup / 16];
@@ -1163,8 +1177,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
         const int buf = (k1 - 1 - k) & 1;
         const uint16_t* tDy = reinterpret_cast<const uint16_t*>(sDy[buf]);
         const uint16_t* tC = reinterpret_cast<const uint16_t*>(sC[buf]);
-        const float cum = tile_cum(sA[buf], Qt, log2R, lane);
-        const float last = __shfl(cum, kTileRows - 1);
+        const float* cum = sA[buf];
         if constexpr (OUT) {
             const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
             const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
@@ -1192,7 +1205,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) wr[i][v] = __expf(last - __shfl(cum, 16 * i + 4 * q + v));
+                for (int v = 0; v < 4; ++v) wr[i][v] = cum[kCumW + 16 * i + 4 * q + v];
             // dx = w o (B H^T) + (CB' o L') dy over this wave's p
             f32x4 zx[2];
 #pragma unroll
@@ -1258,15 +1271,13 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwdc_backward_kernel(BwdAr
                 }
         }
         // H <- e^{last} H + (e^{cum} o dy)^T C
-        const float carry = __expf(last);
+        const float carry = cum[kCumE + kTileRows - 1];
         s16x4 ed[2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
-            float e4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) e4[e] = __expf(__shfl(cum, 16 * kb + 4 * q + e));
-            ed[kb] = scale4(dt, e4[0], e4[1], e4[2], e4[3]);
+            const float4 e4 = *reinterpret_cast<const float4*>(cum + kCumE + 16 * kb + 4 * q);
+            ed[kb] = scale4(dt, e4.x, e4.y, e4.z, e4.w);
         }
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
