@@ -307,14 +307,16 @@ def trapezoid_bench(args) -> dict:
     call_ms, walk_ms = tc["call_ms_median"], tc["walk_ms_median"]
     if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite output")
-    # the dominant kernel is the rotating walk over 2T sub-steps: its own
-    # compulsory bytes are those of that single-write problem (no D), less
-    # the y of the even sub-steps, which it does not write
-    sub = dataclasses.replace(shape, seqlen=2 * T, skip="none")
-    walk_bytes = algorithmic_bytes(sub) - b * T * R * H * P * 4
+    # the dominant kernel is the rotating walk over 2T sub-steps, which on this
+    # shape stages its sub-steps from the original arrays: its compulsory bytes
+    # are x, B, C and theta read once, the sub-steps' decay and scale (2T per
+    # head, written by a small kernel before it) instead of da, the previous
+    # token's x and B, init, and the odd sub-steps' y and the final state
     esz = 2 if shape.dtype == "bf16" else 4
-    trap_bytes = (algorithmic_bytes(dataclasses.replace(shape, skip="none"))
-                  + 2 * b * T * H * 4 + b * R * (H * P + shape.ngroups * N) * esz)
+    one = algorithmic_bytes(dataclasses.replace(shape, skip="none"))
+    prev = b * R * (H * P + shape.ngroups * N) * esz
+    walk_bytes = one - b * T * H * 4 + 2 * b * 2 * T * H * 4 + prev
+    trap_bytes = one + 2 * b * T * H * 4 + prev
     achieved = walk_bytes / (walk_ms * 1e-3) / 1e9
     out = {
         "metric": "trapezoid fwd tokens/s + % of HBM roofline (b4,T4096,H32,P64,N128,R4)",
