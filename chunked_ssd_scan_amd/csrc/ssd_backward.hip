@@ -918,17 +918,23 @@ __device__ __forceinline__ void put_state(uint16_t* sH, const f32x4 (&hs)[NT], i
     for (int c = 0; c < NT; ++c) *reinterpret_cast<s16x4*>(sH + (16 * c + l16) * kLdh + p0 + 4 * q) = pack4_bf16(hs[c]);
 }
 
-// Rows f0 + 16 i + 4 q + v (< TR), column 16 c + l16 (< N) of a partial: two
-// accumulator blocks of a wave's column tile c
-__device__ __forceinline__ void store_rows(float* dst, const f32x4& z0, const f32x4& z1, int64_t f0, int64_t TR,
-                                           int N, int64_t rs, int c, int lane) {
-    const int q = lane >> 4, n = 16 * c + (lane & 15);
-    if (n >= N) return;
+// Rows [f0, f0 + 32) of a row-major fp32 array (row stride rs floats, `base`
+// at row 0) as a buffer resource that ends at row TR: stores to later rows are
+// dropped and loads from them read zero, with no branch. The byte range fits
+// 32 bits (the host checks 32 H max(P, N) 4 bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rows(const float* base, int64_t f0, int64_t TR, int64_t rs) {
+    const int64_t rem = TR - f0, rows = rem < kTileRows ? rem : kTileRows;
+    return make_rsrc(base + f0 * rs, (uint32_t)(rows * rs * 4));
+}
+
+// Rows 16 i + 4 q + v of a tile, columns 16 c + l16 from the lane's byte
+// offset voff (row 4 q, column l16) and the uniform row and column steps
+__device__ __forceinline__ void store_tile_rows(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
+                                                uint32_t voff, uint32_t rowb, uint32_t colb) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-        const int64_t r0 = f0 + 4 * q + v, r1 = r0 + 16;
-        if (r0 < TR) dst[r0 * rs + n] = z0[v];
-        if (r1 < TR) dst[r1 * rs + n] = z1[v];
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z0[v]), rsrc, voff, colb + v * rowb, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z1[v]), rsrc, voff, colb + (16 + v) * rowb, 0);
     }
 }
 
@@ -965,6 +971,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     float* dst = a.part + (b * TR * H + h) * N;            // [b][TR][H][N]
     const int64_t rs = H * N;
+    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 4), rowb = (uint32_t)(rs * 4);
 
     // columns n >= N of B stay zero
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
@@ -1033,7 +1040,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
                 if (kb < nw) dya[i][kb] = row4(tDy + (16 * i + l16) * LDX + 16 * kb + 4 * q);
         }
         const s16x4 m00 = blk_rows(sM[0], lane), m10 = blk_rows(sM[1], lane), m11 = blk_rows(sM[2], lane);
-        for (int c = wv; c < NT; c += nw) {
+        const auto prs = tile_rows(dst, (int64_t)k * kTileRows, TR, rs);
+        // N is a multiple of 16: a column tile is all in range or all out
+        for (int c = wv; c < NT && 16 * c < N; c += nw) {
             f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 16; ++kb) {
@@ -1051,7 +1060,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
             z0 = mma16(m00, bb0, z0);
             z1 = mma16(m10, bb0, z1);
             z1 = mma16(m11, bb1, z1);
-            store_rows(dst, z0, z1, (int64_t)k * kTileRows, TR, (int)N, rs, c, lane);
+            store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
         }
         // h <- e^{last} h + (w o x)^T B
         const float carry = cum[kCumE + kTileRows - 1];
@@ -1121,6 +1130,12 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     float* dst = OUT ? a.part + (b * TR * H + h) * N : nullptr;
     const int64_t rs = H * N;
+    // lane byte offsets of a tile's rows 4 q (+ uniform steps): partial rows
+    // (stride H N) at column l16, dy and dx rows (stride H P) at column p0 + l16
+    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 4), rowb = (uint32_t)(rs * 4);
+    const uint32_t xrow = (uint32_t)((4 * q * H * P + 16 * wv + l16) * 4), xrowb = (uint32_t)(H * P * 4);
+    const float* dyh = a.dy + (b * TR * H + h) * P;
+    float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
 
     // columns n >= N of B and C stay zero
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) {
@@ -1187,16 +1202,16 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
         if constexpr (OUT) {
             const uint16_t* tX = reinterpret_cast<const uint16_t*>(sX[buf]);
             const uint16_t* tB = reinterpret_cast<const uint16_t*>(sB[buf]);
-            // the tile's fp32 dy (for D dy and the dy . x sum), loaded now, used last
+            // the tile's fp32 dy (for D dy and the dy . x sum), loaded now, used
+            // last; rows past TR read zero
             const int64_t f0 = (int64_t)k * kTileRows;
+            const auto xrs = tile_rows(dyh, f0, TR, H * P), drs = tile_rows(dxh, f0, TR, H * P);
             float dyr[2][4];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * q + v;
-                    dyr[i][v] = (f0 + r < TR) ? a.dy[((b * TR + f0 + r) * H + h) * P + p0 + l16] : 0.f;
-                }
+                for (int v = 0; v < 4; ++v)
+                    dyr[i][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xrs, xrow, (16 * i + v) * xrowb, 0));
             put_state<NT>(sH, hp, p0, lane);
             // upper blocks (0,0), (0,1), (1,1): CB' = B_m . C_j (jobs 0-2) and
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
@@ -1241,7 +1256,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
                     for (int kb = 0; kb < kRowGroup / 16; ++kb)
                         if (kb < nw) xs[i][kb] = row4(tX + (16 * i + l16) * LDX + 16 * kb + 4 * q);
                 const s16x4 g00 = blk_rows(sM[3], lane), g01 = blk_rows(sM[4], lane), g11 = blk_rows(sM[5], lane);
-                for (int c = wv; c < NT; c += nw) {
+                const auto prs = tile_rows(dst, f0, TR, rs);
+                // N is a multiple of 16: a column tile is all in range or all out
+                for (int c = wv; c < NT && 16 * c < N; c += nw) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < kRowGroup / 16; ++kb) {
@@ -1260,20 +1277,18 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
                     z0 = mma16(g00, cc0, z0);
                     z0 = mma16(g01, cc1, z0);
                     z1 = mma16(g11, cc1, z1);
-                    store_rows(dst, z0, z1, f0, TR, (int)N, rs, c, lane);
+                    store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
                 }
             }
-            // dx rows
+            // dx rows (rows past TR dropped; their dy and x are zero)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
                     const int r = 16 * i + 4 * q + v;
-                    if (f0 + r < TR) {
-                        const int64_t o = ((b * TR + f0 + r) * H + h) * P + p0 + l16;
-                        a.dx[o] = fmaf(Dh, dyr[i][v], zx[i][v]);
-                        dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
-                    }
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(Dh, dyr[i][v], zx[i][v])), drs, xrow,
+                                                          (16 * i + v) * xrowb, 0);
+                    dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
                 }
         }
         // H <- e^{last} H + (e^{cum} o dy)^T C
