@@ -161,13 +161,16 @@ struct Stager {
         const int64_t f0 = (int64_t)k * kTileRows, rem = TR - f0;   // rows r < rem are in range
         const int PG = a.PG;
         const int xur = PG / St::EPU, dur = PG / 4, nbu = (int)(N / St::EPU), thu = (int)(N / 8);
+        // the unit counts per row are powers of two (P and N are): shifts, not divisions
+        const int xurs = __builtin_ctz(xur), durs = __builtin_ctz(dur), nbus = __builtin_ctz(nbu),
+                  thus = __builtin_ctz(thu);
         // rows of x and dy are H P elements apart, rows of B and C G N
         const uint32_t xrs = (uint32_t)(H * P), brs = (uint32_t)(G * N);
         if constexpr (WANT_X) {
             const TI* xt = static_cast<const TI*>(a.x) + ((b * TR + f0) * H + h) * P + pbase;
 #pragma unroll
             for (int m = 0; m < St::XR; ++m) {
-                const int u = mt + m * St::NTM, r = u / xur, c = (u % xur) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> xurs, c = (u & (xur - 1)) * St::EPU;
                 rx[m] = (u < kTileRows * xur && r < rem) ? at<uint4>(xt, ((uint32_t)r * xrs + c) * sizeof(TI))
                                                          : make_uint4(0, 0, 0, 0);
             }
@@ -176,7 +179,7 @@ struct Stager {
             const float* dyt = a.dy + ((b * TR + f0) * H + h) * P + pbase;
 #pragma unroll
             for (int m = 0; m < St::DYR; ++m) {
-                const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
+                const int u = mt + m * St::NTM, r = u >> durs, c = (u & (dur - 1)) * 4;
                 rdy[m] = (u < kTileRows * dur && r < rem) ? at<float4>(dyt, ((uint32_t)r * xrs + c) * 4u)
                                                           : make_float4(0.f, 0.f, 0.f, 0.f);
             }
@@ -189,7 +192,7 @@ struct Stager {
             const TI* Bt = static_cast<const TI*>(a.B) + ((b * TR + f0) * G + g) * N;
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
-                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> nbus, c = (u & (nbu - 1)) * St::EPU;
                 const bool ok = u < kTileRows * nbu && r < rem;
                 rb[m] = ok ? at<uint4>(Bt, ((uint32_t)r * brs + c) * sizeof(TI)) : make_uint4(0, 0, 0, 0);
                 if constexpr (TURN)
@@ -201,7 +204,7 @@ struct Stager {
             const TI* Ct = static_cast<const TI*>(a.C) + ((b * TR + f0) * G + g) * N;
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
-                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> nbus, c = (u & (nbu - 1)) * St::EPU;
                 const bool ok = u < kTileRows * nbu && r < rem;
                 rc[m] = ok ? at<uint4>(Ct, ((uint32_t)r * brs + c) * sizeof(TI)) : make_uint4(0, 0, 0, 0);
                 if constexpr (OWN_PC)
@@ -214,7 +217,7 @@ struct Stager {
             const float* tht = a.theta ? a.theta + ((b * T + t0) * H + h) * (N / 2) : nullptr;
 #pragma unroll
             for (int m = 0; m < St::THR; ++m) {
-                const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
+                const int u = mt + m * St::NTM, st = u >> thus, c = (u & (thu - 1)) * 4;
                 rth[m] = (tht && st < a.Qt && t0 + st < T) ? at<float4>(tht, ((uint32_t)st * prs + c) * 4u)
                                                            : make_float4(0.f, 0.f, 0.f, 0.f);
             }
@@ -229,16 +232,18 @@ struct Stager {
         constexpr int XS = RW * St::LDX, BS = RW * St::LDB;
         const int PG = a.PG, N = (int)a.N;
         const int xur = PG / St::EPU, dur = PG / 4, nbu = N / St::EPU, thu = N / 8;
+        const int xurs = __builtin_ctz(xur), durs = __builtin_ctz(dur), nbus = __builtin_ctz(nbu),
+                  thus = __builtin_ctz(thu);
         if constexpr (WANT_X) {
 #pragma unroll
             for (int m = 0; m < St::XR; ++m) {
-                const int u = mt + m * St::NTM, r = u / xur, c = (u % xur) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> xurs, c = (u & (xur - 1)) * St::EPU;
                 if (u < kTileRows * xur) *reinterpret_cast<uint4*>(&s.sX[buf * XS + r * St::LDX + c]) = rx[m];
             }
         }
 #pragma unroll
         for (int m = 0; m < St::DYR; ++m) {
-            const int u = mt + m * St::NTM, r = u / dur, c = (u % dur) * 4;
+            const int u = mt + m * St::NTM, r = u >> durs, c = (u & (dur - 1)) * 4;
             if (u < kTileRows * dur) {
                 TI* d = &s.sDy[buf * XS + r * St::LDX + c];
                 if constexpr (sizeof(TI) == 2) {
@@ -254,7 +259,7 @@ struct Stager {
         if constexpr (WANT_B) {
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
-                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> nbus, c = (u & (nbu - 1)) * St::EPU;
                 if (u < kTileRows * nbu)
                     *reinterpret_cast<uint4*>(&s.sB[buf * BS + r * St::LDB + c]) = TURN ? turn(rb[m], rpb[m]) : rb[m];
             }
@@ -262,14 +267,14 @@ struct Stager {
         if constexpr (WANT_C) {
 #pragma unroll
             for (int m = 0; m < St::BRG; ++m) {
-                const int u = mt + m * St::NTM, r = u / nbu, c = (u % nbu) * St::EPU;
+                const int u = mt + m * St::NTM, r = u >> nbus, c = (u & (nbu - 1)) * St::EPU;
                 if (u < kTileRows * nbu)
                     *reinterpret_cast<uint4*>(&s.sC[buf * BS + r * St::LDB + c]) = TURN ? turn(rc[m], OWN_PC ? rpc[m] : rpb[m]) : rc[m];
             }
         }
 #pragma unroll
         for (int m = 0; m < (RAW ? 0 : St::THR); ++m) {
-            const int u = mt + m * St::NTM, st = u / thu, c = (u % thu) * 4;
+            const int u = mt + m * St::NTM, st = u >> thus, c = (u & (thu - 1)) * 4;
             if (st < a.Qt) {
                 const float v4[4] = {rth[m].x, rth[m].y, rth[m].z, rth[m].w};
 #pragma unroll
