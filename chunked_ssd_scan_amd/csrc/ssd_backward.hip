@@ -39,6 +39,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssd_common.h"
 #include "ssd_step.h"
 
@@ -1750,6 +1752,40 @@ void* bwd_backward_np(int NP) {
     return nullptr;
 }
 
+// A second stream per device for the forward-direction chain (the forward's
+// state passes and the forward-direction walk), which reads nothing the
+// backward chain writes: the two chains run side by side and each fills the
+// other's last round of workgroups. Created on first use with default
+// priority; a call holds the lock from the fork to the join, so calls on one
+// device take their turns on it.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+SideStream g_side[kMaxDevices];
+
+ssd_status side_stream(SideStream** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+    SideStream& ss = g_side[dev];
+    if (!ss.fork && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) {
+        ss.fork = nullptr;
+        return SSD_ERR_HIP;
+    }
+    if (!ss.join && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+        ss.join = nullptr;
+        return SSD_ERR_HIP;
+    }
+    if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) {
+        ss.s = nullptr;
+        return SSD_ERR_HIP;
+    }
+    *out = &ss;
+    return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float* da, const void* B,
@@ -1872,16 +1908,28 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
                            N / 2, nch, n);
         if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
     }
+    // fork: the forward-direction chain on the side stream, after everything
+    // the caller's stream holds so far (inputs, the angles)
+    std::unique_lock<std::mutex> side_lock(g_side_mu);
+    SideStream* side = nullptr;
+    hipStream_t fs = hs;
+    if (rs == SSD_OK) rs = side_stream(&side);
+    if (rs == SSD_OK) {
+        if (hipEventRecord(side->fork, hs) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+            rs = SSD_ERR_HIP;
+        else
+            fs = side->s;
+    }
     // 1. forward walk: states from the forward's state passes, dC partials, final state
     float* fws_state = nullptr;
-    if (rs == SSD_OK) rs = states_launch(pl, rot, x, da, B, init_state, theta, ws + o_states, hs, &fws_state);
+    if (rs == SSD_OK) rs = states_launch(pl, rot, x, da, B, init_state, theta, ws + o_states, fs, &fws_state);
     if (rs == SSD_OK) {
         BwdArgs fa = ba;
         fa.seg_in = fws_state;
         fa.part = reinterpret_cast<float*>(ws + o_pC);
         fa.final_state = fin;
         void* kargs[] = {&fa};
-        if (hipLaunchKernel(kf, grid, block_f, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        if (hipLaunchKernel(kf, grid, block_f, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
     }
     // 2. backward state pass and reverse carry (more than one segment)
     float* seg_in = reinterpret_cast<float*>(ws + o_segin);
@@ -1912,6 +1960,11 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         void* kargs[] = {&oa};
         if (hipLaunchKernel(kb0, grid, block_b, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
     }
+    // join: the caller's stream waits for the forward-direction chain (the
+    // reduction reads its dC partials, the final terms its final state)
+    if (fs != hs && (hipEventRecord(side->join, fs) != hipSuccess || hipStreamWaitEvent(hs, side->join, 0) != hipSuccess))
+        rs = SSD_ERR_HIP;
+    side_lock.unlock();
     // 4. group sums and per-step terms; 5. reverse cumulative sums
     if (rs == SSD_OK) {
         const float* pC = reinterpret_cast<const float*>(ws + o_pC);

@@ -312,6 +312,13 @@ ssd_status ssd_state_moments(const ssd_dims *d, const void *x, const float *da, 
  * forward's segment states, per-head partial sums of dB and dC
  * (2 b H T R N fp32) and the backward's segment states, in a separate
  * per-(device, stream) buffer of the library.
+ * Streams: the recomputation of the forward direction (the forward's state
+ * passes and the walk that gives the dC partials and the final state) runs on
+ * a second stream that the library creates once per device (default
+ * priority), forked from `stream` after the work already queued there and
+ * joined back into it before the first kernel that reads its results; to the
+ * caller the call is ordered on `stream` alone. Calls on one device take
+ * turns enqueueing on that second stream (a lock held from fork to join).
  */
 ssd_status ssd_backward(const ssd_dims *d, const void *x, const float *da, const void *B,
                         const void *C, const float *D, const float *init_state, int64_t R,

@@ -147,6 +147,37 @@ def test_backward_in_place_and_deterministic():
         assert np.array_equal(res[k].cpu().numpy(), v), k
 
 
+@pytest.mark.parametrize("segments_shape", [False, True])
+def test_backward_on_a_caller_stream(segments_shape):
+    # the call runs its forward-direction chain on a stream of its own and
+    # joins it back into the caller's stream: on a non-default caller stream
+    # the outputs match the default stream's bit for bit, and a copy queued on
+    # that stream right after the call (before any host synchronisation) sees
+    # them complete. The long shape has segments (state passes on both chains)
+    ssd = _ssd()
+    dev = _dev()
+    if segments_shape:
+        shape = si.small_shape(batch=1, seqlen=3000, nheads=2, headdim=64, dstate=128, mimo_rank=4,
+                               dtype="bf16", rotation=True, init_state=True, skip="randn", dt_shift=5.0)
+    else:
+        shape = si.small_shape(seqlen=300, headdim=64, dstate=128, mimo_rank=1, nheads=4,
+                               dtype="bf16", skip="randn")
+    inp = si.make_inputs(shape, seed=93)
+    dy, df = si.make_cotangents(shape, seed=93)
+    first = run(inp, dy, df)
+    g = inp.to(dev)
+    dyg, dfg = dy.to(dev), df.to(dev)
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        res = ssd.backward(g.x, g.da, g.B, g.C, dyg, D=g.D, init_state=g.init_state, theta=g.theta,
+                           dfinal=dfg, stream=side.cuda_stream)
+        copies = {k: v.clone() for k, v in res.items()}
+    side.synchronize()
+    for k, v in first.items():
+        assert np.array_equal(copies[k].cpu().numpy(), v), k
+
+
 @pytest.mark.parametrize("cfg", [1, 3])
 def test_backward_full_layer_every_element(cfg):
     # full layer shapes, every output element compared: the Mamba-2 130M
