@@ -835,6 +835,61 @@ __device__ __forceinline__ s16x4 blk_rows(const uint16_t* blk, int lane) {
     return row4(blk + (lane & 15) * kLdm + 4 * (lane >> 4));
 }
 
+__device__ __forceinline__ s16x4 scale4(s16x4 v, float a, float b, float c, float d) {
+    f32x4 f = {__uint_as_float((uint32_t)(uint16_t)v[0] << 16) * a, __uint_as_float((uint32_t)(uint16_t)v[1] << 16) * b,
+               __uint_as_float((uint32_t)(uint16_t)v[2] << 16) * c, __uint_as_float((uint32_t)(uint16_t)v[3] << 16) * d};
+    return pack4_bf16(f);
+}
+
+// Products of contraction length 32 (v_mfma_f32_16x16x32_bf16, twice the work
+// of the 16 x 16 x 16 form in the same cycles). Operand layout: lane l holds
+// row (A) or column (B) l % 16 and k = 8 (l / 16) .. + 7; the result as mma16.
+typedef __attribute__((ext_vector_type(8))) short s16x8;
+
+__device__ __forceinline__ f32x4 mma32(s16x8 a, s16x8 b, f32x4 c) {
+    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+}
+
+// eight consecutive elements of one row (16 bytes, 16-byte aligned)
+__device__ __forceinline__ s16x8 row8(const uint16_t* p) { return *reinterpret_cast<const s16x8*>(p); }
+
+__device__ __forceinline__ s16x8 cat8(s16x4 lo, s16x4 hi) {
+    return (s16x8){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// rows r0 .. r0 + 7 of column colbase + (lane % 16) of a row-major tile
+__device__ __forceinline__ s16x8 tr_rows8(const uint16_t* tile, int ld, int r0, int colbase, int lane) {
+    return cat8(tr_rows4(tile, ld, r0, colbase, lane), tr_rows4(tile, ld, r0 + 4, colbase, lane));
+}
+
+__device__ __forceinline__ s16x8 scale8(s16x8 v, float4 a, float4 b) {
+    const s16x4 lo = scale4((s16x4){v[0], v[1], v[2], v[3]}, a.x, a.y, a.z, a.w);
+    const s16x4 hi = scale4((s16x4){v[4], v[5], v[6], v[7]}, b.x, b.y, b.z, b.w);
+    return cat8(lo, hi);
+}
+
+// A operand of the 16 x 32 block row [left | right] of two staged 16 x 16
+// blocks; a null half is zero (a block the causal mask removes)
+__device__ __forceinline__ s16x8 blk_pair(const uint16_t* left, const uint16_t* right, int lane) {
+    const int l16 = lane & 15, q = lane >> 4;
+    const uint16_t* blk = q < 2 ? left : right;
+    s16x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (blk) v = row8(blk + l16 * kLdm + 8 * (q & 1));
+    return v;
+}
+
+// rows_dot with contraction length 32 (K a multiple of 32)
+__device__ __forceinline__ f32x4 rows_dot32(const uint16_t* ta, int lda, int mrow0, const uint16_t* tb, int ldb,
+                                            int jrow0, int K, int lane) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int l16 = lane & 15, q = lane >> 4;
+    for (int k0 = 0; k0 < K; k0 += 32)
+        acc = mma32(row8(ta + (mrow0 + l16) * lda + k0 + 8 * q), row8(tb + (jrow0 + l16) * ldb + k0 + 8 * q), acc);
+    return acc;
+}
+
 // A compute wave's share of per-head rows [32][NP] in its own LDS slot, in
 // accumulator order: fragment (i, c, lane) holds rows 16 i + 4 q + v of
 // column 16 c + l16.
@@ -871,11 +926,6 @@ __device__ __forceinline__ void sum_frags(const float4* slots, int nw, float* ds
     }
 }
 
-__device__ __forceinline__ s16x4 scale4(s16x4 v, float a, float b, float c, float d) {
-    f32x4 f = {__uint_as_float((uint32_t)(uint16_t)v[0] << 16) * a, __uint_as_float((uint32_t)(uint16_t)v[1] << 16) * b,
-               __uint_as_float((uint32_t)(uint16_t)v[2] << 16) * c, __uint_as_float((uint32_t)(uint16_t)v[3] << 16) * d};
-    return pack4_bf16(f);
-}
 
 // Frame changes of state tiles: every state pair (2k, 2k+1) turned by
 // R(sgn Phi[k]) (phirow: the angles of one step, one head). Layout D[p][n]
@@ -970,6 +1020,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
     const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
+    const int KP = (int)((P + 31) & ~31);              // contractions over p, in steps of 32
     const bool memw = wv >= nw;
     const int mt = tid - 64 * nw;
     const int seg = blockIdx.x % S;
@@ -980,8 +1031,14 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
     const int64_t rs = H * N;
     const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 4), rowb = (uint32_t)(rs * 4);
 
-    // columns n >= N of B stay zero
+    // columns n >= N of B, p >= P of x and dy, and of the staged state stay
+    // zero (the contractions over p run in steps of 32)
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    for (int i = tid; i < 2 * ROWS * LDX; i += blockDim.x) {
+        sX[i / (ROWS * LDX)][i % (ROWS * LDX)] = TI(0);
+        sDy[i / (ROWS * LDX)][i % (ROWS * LDX)] = TI(0);
+    }
+    for (int i = tid; i < NP * kLdh; i += blockDim.x) sH[i] = 0;
     __syncthreads();
 
     if (memw) {
@@ -1031,60 +1088,54 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
         // G o L blocks (0,0), (1,0), (1,1): rows m of dy against rows j of x
         for (int u = wv; u < 3; u += nw) {
             const int mb = u == 0 ? 0 : 1, jb = u == 2 ? 1 : 0;
-            const f32x4 gacc = rows_dot(tDy, LDX, 16 * mb, tX, LDX, 16 * jb, (int)P, lane);
+            const f32x4 gacc = rows_dot32(tDy, LDX, 16 * mb, tX, LDX, 16 * jb, KP, lane);
             put_masked(sM[u], gacc, mb, jb, false, cum, log2R, lane);
         }
         __syncthreads();
         // dC = e^{cum_m} (dy h_in) + (G o L) B on the wave's column tiles
         float ein[2][4];
-        s16x4 dya[2][kRowGroup / 16];
+        s16x8 dya[2][kRowGroup / 32];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) ein[i][v] = cum[kCumE + 16 * i + 4 * q + v];
 #pragma unroll
-            for (int kb = 0; kb < kRowGroup / 16; ++kb)
-                if (kb < nw) dya[i][kb] = row4(tDy + (16 * i + l16) * LDX + 16 * kb + 4 * q);
+            for (int kb = 0; kb < kRowGroup / 32; ++kb)
+                if (32 * kb < KP) dya[i][kb] = row8(tDy + (16 * i + l16) * LDX + 32 * kb + 8 * q);
         }
-        const s16x4 m00 = blk_rows(sM[0], lane), m10 = blk_rows(sM[1], lane), m11 = blk_rows(sM[2], lane);
+        // block rows [G o L (0,0) | 0] and [(1,0) | (1,1)]
+        const s16x8 m0 = blk_pair(sM[0], nullptr, lane), m1 = blk_pair(sM[1], sM[2], lane);
         const auto prs = tile_rows(dst, (int64_t)k * kTileRows, TR, rs);
         // N is a multiple of 16: a column tile is all in range or all out
         for (int c = wv; c < NT && 16 * c < N; c += nw) {
             f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kb = 0; kb < kRowGroup / 16; ++kb) {
-                if (kb >= nw) break;
-                const s16x4 hb = row4(sH + (16 * c + l16) * kLdh + 16 * kb + 4 * q);
-                z0 = mma16(dya[0][kb], hb, z0);
-                z1 = mma16(dya[1][kb], hb, z1);
+            for (int kb = 0; kb < kRowGroup / 32; ++kb) {
+                if (32 * kb >= KP) break;
+                const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
+                z0 = mma32(dya[0][kb], hb, z0);
+                z1 = mma32(dya[1][kb], hb, z1);
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 z0[v] *= ein[0][v];
                 z1[v] *= ein[1][v];
             }
-            const s16x4 bb0 = tr_rows4(tB, LDB, 4 * q, 16 * c, lane), bb1 = tr_rows4(tB, LDB, 16 + 4 * q, 16 * c, lane);
-            z0 = mma16(m00, bb0, z0);
-            z1 = mma16(m10, bb0, z1);
-            z1 = mma16(m11, bb1, z1);
+            const s16x8 bb = tr_rows8(tB, LDB, 8 * q, 16 * c, lane);
+            z0 = mma32(m0, bb, z0);
+            z1 = mma32(m1, bb, z1);
             store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
         }
-        // h <- e^{last} h + (w o x)^T B
+        // h <- e^{last} h + (w o x)^T B, contracted over the tile's 32 rows
         const float carry = cum[kCumE + kTileRows - 1];
-        s16x4 xw[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const s16x4 xt = tr_rows4(tX, LDX, 16 * kb + 4 * q, p0, lane);
-            const float4 w4 = *reinterpret_cast<const float4*>(cum + kCumW + 16 * kb + 4 * q);
-            xw[kb] = scale4(xt, w4.x, w4.y, w4.z, w4.w);
-        }
+        const s16x8 xw = scale8(tr_rows8(tX, LDX, 8 * q, p0, lane),
+                                *reinterpret_cast<const float4*>(cum + kCumW + 8 * q),
+                                *reinterpret_cast<const float4*>(cum + kCumW + 8 * q + 4));
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) hs[c][v] *= carry;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                hs[c] = mma16(xw[kb], tr_rows4(tB, LDB, 16 * kb + 4 * q, 16 * c, lane), hs[c]);
+            hs[c] = mma32(xw, tr_rows8(tB, LDB, 8 * q, 16 * c, lane), hs[c]);
         }
         __syncthreads();                           // tile walked: its buffers and sH free
     }
@@ -1129,6 +1180,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
     const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
+    const int KP = (int)((P + 31) & ~31);              // contractions over p, in steps of 32
     const bool memw = wv >= nw;
     const int mt = tid - 64 * nw;
     const int seg = blockIdx.x % S;
@@ -1144,11 +1196,18 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
     const float* dyh = a.dy + (b * TR * H + h) * P;
     float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
 
-    // columns n >= N of B and C stay zero
+    // columns n >= N of B and C, p >= P of x and dy, and of the staged state
+    // stay zero (the contractions over p run in steps of 32)
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) {
         if (OUT) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
         sC[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
     }
+    for (int i = tid; i < 2 * ROWS * LDX; i += blockDim.x) {
+        if (OUT) sX[i / (ROWS * LDX)][i % (ROWS * LDX)] = TI(0);
+        sDy[i / (ROWS * LDX)][i % (ROWS * LDX)] = TI(0);
+    }
+    if (OUT)
+        for (int i = tid; i < NP * kLdh; i += blockDim.x) sH[i] = 0;
     __syncthreads();
 
     if (memw) {
@@ -1224,8 +1283,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
             for (int u = wv; u < 6; u += nw) {
                 const int ub = u % 3, mb = ub == 2 ? 1 : 0, jb = ub == 0 ? 0 : 1;
-                const f32x4 acc = u < 3 ? rows_dot(tB, LDB, 16 * mb, tC, LDB, 16 * jb, (int)NP, lane)
-                                        : rows_dot(tX, LDX, 16 * mb, tDy, LDX, 16 * jb, (int)P, lane);
+                const f32x4 acc = u < 3 ? rows_dot32(tB, LDB, 16 * mb, tC, LDB, 16 * jb, NP, lane)
+                                        : rows_dot32(tX, LDX, 16 * mb, tDy, LDX, 16 * jb, KP, lane);
                 put_masked(sM[u], acc, mb, jb, true, cum, log2R, lane);
             }
             __syncthreads();
@@ -1240,50 +1299,48 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
             for (int i = 0; i < 2; ++i) {
                 zx[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int c = 0; c < NT; ++c) {
-                    const s16x4 bs = row4(tB + (16 * i + l16) * LDB + 16 * c + 4 * q);
-                    zx[i] = mma16(bs, tr_rows4(sH, kLdh, 16 * c + 4 * q, p0, lane), zx[i]);
+                for (int c2 = 0; c2 < NT / 2; ++c2) {
+                    const s16x8 bs = row8(tB + (16 * i + l16) * LDB + 32 * c2 + 8 * q);
+                    zx[i] = mma32(bs, tr_rows8(sH, kLdh, 32 * c2 + 8 * q, p0, lane), zx[i]);
                 }
 #pragma unroll
                 for (int v = 0; v < 4; ++v) zx[i][v] *= wr[i][v];
             }
             {
-                const s16x4 c00 = blk_rows(sM[0], lane), c01 = blk_rows(sM[1], lane), c11 = blk_rows(sM[2], lane);
-                const s16x4 d0 = tr_rows4(tDy, LDX, 4 * q, p0, lane), d1 = tr_rows4(tDy, LDX, 16 + 4 * q, p0, lane);
-                zx[0] = mma16(c00, d0, zx[0]);
-                zx[0] = mma16(c01, d1, zx[0]);
-                zx[1] = mma16(c11, d1, zx[1]);
+                // block rows [CB' (0,0) | (0,1)] and [0 | (1,1)] against dy's 32 rows
+                const s16x8 d8 = tr_rows8(tDy, LDX, 8 * q, p0, lane);
+                zx[0] = mma32(blk_pair(sM[0], sM[1], lane), d8, zx[0]);
+                zx[1] = mma32(blk_pair(nullptr, sM[2], lane), d8, zx[1]);
             }
             // dB partial = w o (x H) + (G' o L') C on the wave's column tiles
             {
-                s16x4 xs[2][kRowGroup / 16];
+                s16x8 xs[2][kRowGroup / 32];
 #pragma unroll
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
-                    for (int kb = 0; kb < kRowGroup / 16; ++kb)
-                        if (kb < nw) xs[i][kb] = row4(tX + (16 * i + l16) * LDX + 16 * kb + 4 * q);
-                const s16x4 g00 = blk_rows(sM[3], lane), g01 = blk_rows(sM[4], lane), g11 = blk_rows(sM[5], lane);
+                    for (int kb = 0; kb < kRowGroup / 32; ++kb)
+                        if (32 * kb < KP) xs[i][kb] = row8(tX + (16 * i + l16) * LDX + 32 * kb + 8 * q);
+                // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
+                const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
                 const auto prs = tile_rows(dst, f0, TR, rs);
                 // N is a multiple of 16: a column tile is all in range or all out
                 for (int c = wv; c < NT && 16 * c < N; c += nw) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kb = 0; kb < kRowGroup / 16; ++kb) {
-                        if (kb >= nw) break;
-                        const s16x4 hb = row4(sH + (16 * c + l16) * kLdh + 16 * kb + 4 * q);
-                        z0 = mma16(xs[0][kb], hb, z0);
-                        z1 = mma16(xs[1][kb], hb, z1);
+                    for (int kb = 0; kb < kRowGroup / 32; ++kb) {
+                        if (32 * kb >= KP) break;
+                        const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
+                        z0 = mma32(xs[0][kb], hb, z0);
+                        z1 = mma32(xs[1][kb], hb, z1);
                     }
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         z0[v] *= wr[0][v];
                         z1[v] *= wr[1][v];
                     }
-                    const s16x4 cc0 = tr_rows4(tC, LDB, 4 * q, 16 * c, lane);
-                    const s16x4 cc1 = tr_rows4(tC, LDB, 16 + 4 * q, 16 * c, lane);
-                    z0 = mma16(g00, cc0, z0);
-                    z0 = mma16(g01, cc1, z0);
-                    z1 = mma16(g11, cc1, z1);
+                    const s16x8 cc = tr_rows8(tC, LDB, 8 * q, 16 * c, lane);
+                    z0 = mma32(g0, cc, z0);
+                    z1 = mma32(g1, cc, z1);
                     store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
                 }
             }
@@ -1298,22 +1355,16 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
                     dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
                 }
         }
-        // H <- e^{last} H + (e^{cum} o dy)^T C
+        // H <- e^{last} H + (e^{cum} o dy)^T C, contracted over the tile's 32 rows
         const float carry = cum[kCumE + kTileRows - 1];
-        s16x4 ed[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const s16x4 dt = tr_rows4(tDy, LDX, 16 * kb + 4 * q, p0, lane);
-            const float4 e4 = *reinterpret_cast<const float4*>(cum + kCumE + 16 * kb + 4 * q);
-            ed[kb] = scale4(dt, e4.x, e4.y, e4.z, e4.w);
-        }
+        const s16x8 ed = scale8(tr_rows8(tDy, LDX, 8 * q, p0, lane),
+                                *reinterpret_cast<const float4*>(cum + kCumE + 8 * q),
+                                *reinterpret_cast<const float4*>(cum + kCumE + 8 * q + 4));
 #pragma unroll
         for (int c = 0; c < NT; ++c) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) hp[c][v] *= carry;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                hp[c] = mma16(ed[kb], tr_rows4(tC, LDB, 16 * kb + 4 * q, 16 * c, lane), hp[c]);
+            hp[c] = mma32(ed, tr_rows8(tC, LDB, 8 * q, 16 * c, lane), hp[c]);
         }
         __syncthreads();                           // tile walked: its buffers and sH free
     }
