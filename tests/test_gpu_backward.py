@@ -9,6 +9,8 @@ size of those products, max over (b, t) of sum |C dC| + |B dB|.
 """
 from __future__ import annotations
 
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -200,3 +202,24 @@ def test_backward_full_layer_every_element(cfg):
     print(f"{shape.name}: worst (batch, head) slice of dx/dinit {worst:.2e}", flush=True)
     assert worst <= TOL[shape.dtype]
     assert max(errs.values()) <= TOL[shape.dtype]
+
+
+def test_backward_bench_layer_sampled_batches():
+    # the backward bench's layer at full size (Mamba-2 2.7B: b8 T8192 H80 P64
+    # N128, D, dfinal), one call as bench.py times it; the oracle runs on two
+    # whole batches (batches are independent; every head of a batch, so dB and
+    # dC are complete), and dx, dda, dB, dC and dinit of those batches are
+    # compared element by element. dD sums over the batches and is left out
+    shape = si.CONFIGS[2]
+    inp = si.make_inputs(shape, seed=0)
+    dy, df = si.make_cotangents(shape, seed=0)
+    got = run(inp, dy, df)
+    for bi in (0, shape.batch - 1):
+        sl = lambda t: None if t is None else t[bi:bi + 1]
+        want = oracle.ssd_backward(sl(inp.x), sl(inp.da), sl(inp.B), sl(inp.C), sl(dy), inp.D,
+                                   sl(inp.init_state), sl(inp.theta), sl(df))
+        want = {k: v for k, v in want.items() if k in ("dx", "dda", "dB", "dC", "dinit")}
+        g = {k: got[k][bi:bi + 1] for k in want}
+        compare(g, want, TOL[shape.dtype], f"{shape.name} batch {bi}",
+                types.SimpleNamespace(B=inp.B[bi:bi + 1], C=inp.C[bi:bi + 1]))
+
