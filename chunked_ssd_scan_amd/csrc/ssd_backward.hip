@@ -1679,8 +1679,11 @@ __global__ __launch_bounds__(256) void ssd_bwd_phi(const float* __restrict__ the
     if (i >= items) return;
     const int64_t k = i % NH, ch = (i / NH) % nchunk, bh = i / (NH * nchunk), h = bh % H, b = bh / H;
     float run = 0.f;
+#pragma unroll 8
     for (int c = 0; c < ch; ++c) run = wrap_2pi(run + psum[(bh * nchunk + c) * NH + k]);
     const int64_t t0 = ch * (int64_t)kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
+    // the loads do not depend on the running angle: unrolled, several are in flight
+#pragma unroll 8
     for (int64_t t = t0; t < t1; ++t) {
         const int64_t o = ((b * T + t) * H + h) * NH + k;
         run = wrap_2pi(run + theta[o]);
