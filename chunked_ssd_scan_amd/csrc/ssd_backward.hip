@@ -1730,14 +1730,30 @@ __device__ __forceinline__ float step_term(const float* hv, const float* th, int
 }
 
 // thread -> (batch-head, chunk, column k0 + i): columns fastest, then chunks
+// Thread item of the chunked reverse scans: the column k (a pair's angle term,
+// or the decay term at k = N/2) fastest, then the head, the chunk and the batch,
+// so that a wave's per-step loads and stores of one step are contiguous over
+// heads (or columns)
+__device__ __forceinline__ int scan_item(int64_t it, int ncols, int k0, int64_t H, int nchunk, int64_t* h,
+                                         int* ch, int64_t* b) {
+    const int k = k0 + (int)(it % ncols);
+    const int64_t r = it / ncols;
+    *h = r % H;
+    *ch = (int)((r / H) % nchunk);
+    *b = r / (H * nchunk);
+    return k;
+}
+
 __global__ __launch_bounds__(128) void ssd_bwd_chunk_sums(const float* __restrict__ hv, const float* __restrict__ th,
                                                          float* __restrict__ csum, int64_t T, int64_t H, int64_t N,
                                                          int nchunk, int k0, int64_t items) {
     const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (it >= items) return;
     const int nc = (int)(N / 2 + 1), ncols = nc - k0;
-    const int k = k0 + (int)(it % ncols), ch = (int)((it / ncols) % nchunk);
-    const int64_t bh = it / ((int64_t)ncols * nchunk), b = bh / H, h = bh % H;
+    int ch;
+    int64_t b, h;
+    const int k = scan_item(it, ncols, k0, H, nchunk, &h, &ch, &b);
+    const int64_t bh = b * H + h;
     const int64_t t0 = (int64_t)ch * kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
     float acc = 0.f;
 #pragma unroll 8
@@ -1753,12 +1769,17 @@ __global__ __launch_bounds__(128) void ssd_bwd_chunk_scan(const float* __restric
     const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (it >= items) return;
     const int nc = (int)(N / 2 + 1), ncols = nc - k0;
-    const int k = k0 + (int)(it % ncols), ch = (int)((it / ncols) % nchunk);
-    const int64_t bh = it / ((int64_t)ncols * nchunk), b = bh / H, h = bh % H;
+    int ch;
+    int64_t b, h;
+    const int k = scan_item(it, ncols, k0, H, nchunk, &h, &ch, &b);
+    const int64_t bh = b * H + h;
     float acc = ft[bh * nc + k];
+    // loads do not depend on the running sum: unrolled, several are in flight
+#pragma unroll 8
     for (int c = nchunk - 1; c > ch; --c) acc += csum[(bh * nchunk + c) * nc + k];
     const int64_t t0 = (int64_t)ch * kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
     float* out = k < N / 2 ? dtheta : dda;
+#pragma unroll 8
     for (int64_t t = t1 - 1; t >= t0; --t) {
         acc += step_term(hv, th, b, t, T, H, h, N, k);
         if (k < N / 2) out[((b * T + t) * H + h) * (N / 2) + k] = acc;
