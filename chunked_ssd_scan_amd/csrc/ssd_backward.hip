@@ -559,6 +559,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
     const int64_t bh = item / npg;
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    // the state pass: the first segment's local gradient is never used (the
+    // carry starts from dfinal), so its workgroups leave at once, together
+    if (!OUT && seg == 0) return;
     const int pbase = pg * PG;
     float* dst = OUT ? a.part + ((b * TR * H + h) * npg + pg) * N : nullptr;
 
@@ -1187,6 +1190,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false)))
     const int64_t bh = blockIdx.x / S;
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
+    // the state pass: the first segment's local gradient is never used (the
+    // carry starts from dfinal), so its workgroups leave at once, together
+    if (!OUT && seg == 0) return;
     float* dst = OUT ? a.part + (b * TR * H + h) * N : nullptr;
     const int64_t rs = H * N;
     // lane byte offsets of a tile's rows 4 q (+ uniform steps): partial rows
