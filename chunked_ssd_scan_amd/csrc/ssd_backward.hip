@@ -56,7 +56,7 @@ constexpr int kMemWaves = 2;
 constexpr int kMaxWaves = kRowGroup / 16 + kMemWaves;
 // memory waves of the chunked walks: with rotation they also turn B and C
 // (measured on the Mamba-3 MIMO layer: four take the call from 3.48 to 2.89 ms)
-constexpr int bwdc_mem_waves(bool rot, bool fwd) { return rot ? 4 : 2; }
+constexpr int bwdc_mem_waves(bool rot) { return rot ? 4 : 2; }
 
 struct BwdArgs {
     const void* x;
@@ -1005,9 +1005,9 @@ __device__ __forceinline__ void store_tile_rows(__amdgpu_buffer_rsrc_t rsrc, con
 // c = wv, wv + nw, ... with the contraction over every p read from the staged
 // entering state.
 template <int NP, bool ROT>
-__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) void ssd_bwdc_forward_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void ssd_bwdc_forward_kernel(BwdArgs a) {
     using TI = uint16_t;
-    constexpr int MW = bwdc_mem_waves(ROT, true);
+    constexpr int MW = bwdc_mem_waves(ROT);
     using St = Stage<TI, NP, true, true, false, MW>;
     constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = kTileRows;
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
@@ -1162,10 +1162,10 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, true))) 
 // one as bf16 [n][p], read transposed for dx and, for the dB partial on the
 // wave's column tiles c = wv, wv + nw, ..., contracted over every p.
 template <int NP, int MODE, bool ROT>
-__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT, false))) void ssd_bwdc_backward_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void ssd_bwdc_backward_kernel(BwdArgs a) {
     using TI = uint16_t;
     constexpr bool OUT = MODE == 0;
-    constexpr int MW = bwdc_mem_waves(ROT, false);
+    constexpr int MW = bwdc_mem_waves(ROT);
     using St = Stage<TI, NP, OUT, OUT, true, MW>;
     constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = kTileRows;
     __shared__ __attribute__((aligned(16))) TI sX[2][OUT ? ROWS * LDX : 8];
@@ -1971,10 +1971,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     ba.PG = PG; ba.S = S; ba.SF = pl.SF; ba.nsub = pl.nsub; ba.Qt = pl.Qt; ba.log2R = pl.log2R;
     float* phi = cphi ? reinterpret_cast<float*>(ws + o_phi) : nullptr;
     ba.phi = phi;
-    const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + kMemWaves)));
-    // the chunked walks size their memory waves by direction
-    const dim3 block_f((unsigned)(64 * (PG / 16 + (chunked ? bwdc_mem_waves(rot, true) : kMemWaves))));
-    const dim3 block_b((unsigned)(64 * (PG / 16 + (chunked ? bwdc_mem_waves(rot, false) : kMemWaves))));
+    // the chunked walks with rotation run four memory waves, the others two
+    const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + (chunked ? bwdc_mem_waves(rot) : kMemWaves))));
 
     // 0. the cumulative angles (chunked walks with rotation)
     ssd_status rs = SSD_OK;
@@ -2010,7 +2008,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         fa.part = reinterpret_cast<float*>(ws + o_pC);
         fa.final_state = fin;
         void* kargs[] = {&fa};
-        if (hipLaunchKernel(kf, grid, block_f, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
+        if (hipLaunchKernel(kf, grid, block, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
     }
     // 2. backward state pass and reverse carry (more than one segment)
     float* seg_in = reinterpret_cast<float*>(ws + o_segin);
@@ -2022,7 +2020,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
             BwdArgs la = ba;
             la.seg_out = reinterpret_cast<float*>(ws + o_local);
             void* kargs[] = {&la};
-            if (hipLaunchKernel(kb1, grid, block_b, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+            if (hipLaunchKernel(kb1, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
         }
         if (rs == SSD_OK) {
             dim3 cg((unsigned)((P * (N / 2) + 255) / 256), (unsigned)(b * H));
@@ -2039,7 +2037,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         oa.part = reinterpret_cast<float*>(ws + o_pB);
         oa.dDp = reinterpret_cast<float*>(ws + o_dd);
         void* kargs[] = {&oa};
-        if (hipLaunchKernel(kb0, grid, block_b, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
+        if (hipLaunchKernel(kb0, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
     }
     // join: the caller's stream waits for the forward-direction chain (the
     // reduction reads its dC partials, the final terms its final state)
