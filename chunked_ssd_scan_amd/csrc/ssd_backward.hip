@@ -1735,7 +1735,6 @@ __device__ __forceinline__ float step_term(const float* hv, const float* th, int
     return k < N / 2 ? th[((b * T + t) * H + h) * (N / 2) + k] : hv[(b * T + t) * H + h];
 }
 
-// thread -> (batch-head, chunk, column k0 + i): columns fastest, then chunks
 // Thread item of the chunked reverse scans: the column k (a pair's angle term,
 // or the decay term at k = N/2) fastest, then the head, the chunk and the batch,
 // so that a wave's per-step loads and stores of one step are contiguous over
