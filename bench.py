@@ -18,6 +18,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -155,7 +156,6 @@ def time_calls(step, calls: int, flush_bytes: int) -> dict:
     of events on the launch stream, and the library records a second pair just
     before and after the output walk. Returns the median and min of each.
     """
-    import statistics
     import torch
     hip = _hip()
     flush = torch.empty(max(flush_bytes // 4, 1), dtype=torch.float32, device="cuda:0")
@@ -181,6 +181,15 @@ def time_calls(step, calls: int, flush_bytes: int) -> dict:
     return {"call_ms_median": statistics.median(call), "call_ms_min": min(call),
             "walk_ms_median": statistics.median(walk), "walk_ms_min": min(walk),
             "calls": calls, "flush_bytes": flush_bytes}
+
+
+def flushed_block(tc: dict, walk_bytes: int, call_bytes: int) -> dict:
+    """The flushed per-call timings of a workload and their HBM fractions."""
+    frac = lambda nb, ms: nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS
+    return {"kernel_ms_median": tc["walk_ms_median"], "kernel_ms_min": tc["walk_ms_min"],
+            "forward_ms_median": tc["call_ms_median"], "forward_ms_min": tc["call_ms_min"],
+            "frac_median": frac(walk_bytes, tc["walk_ms_median"]),
+            "forward_frac_median": frac(call_bytes, tc["call_ms_median"])}
 
 
 def cpu_model() -> str:
@@ -231,9 +240,11 @@ def selective_bench(args) -> dict:
                            chunks=args.segments, walk_events=walk_events)
 
     nwarm = prewarm(step, args.prewarm)
-    wall = timed_region(step, args)
+    wall, walks = timed_region_walks(step, args)
     tc = time_calls(step, args.calls, FLUSH_BYTES)
-    call_ms, out_ms = tc["call_ms_median"], tc["walk_ms_median"]
+    # the timed region's averages (the output pass, the whole call); the
+    # flushed per-call medians and minima beside them
+    call_ms, out_ms = wall * 1e3 / args.steps, statistics.fmean(walks)
     if not torch.isfinite(y).all():
         raise RuntimeError("non-finite output")
     b, T, D, N = shape.batch, shape.seqlen, shape.d_model, shape.d_state
@@ -262,7 +273,10 @@ def selective_bench(args) -> dict:
                      "traffic": profiled_traffic("selective_scan", "selective_scan"),
                      "algorithmic_slots": slots, "kernel_ms": out_ms, "forward_ms": call_ms,
                      "forward_frac": slots / (call_ms * 1e-3) / 1e12 / peak,
-                     "hbm_frac_forward": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "hbm_frac_forward": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "flushed": {"kernel_ms_median": tc["walk_ms_median"], "kernel_ms_min": tc["walk_ms_min"],
+                                 "forward_ms_median": tc["call_ms_median"],
+                                 "forward_ms_min": tc["call_ms_min"]}},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -302,9 +316,11 @@ def trapezoid_bench(args) -> dict:
                       stream=stream.cuda_stream, walk_events=walk_events)
 
     nwarm = prewarm(step, args.prewarm)
-    wall = timed_region(step, args)
+    wall, walks = timed_region_walks(step, args)
     tc = time_calls(step, args.calls, FLUSH_BYTES)
-    call_ms, walk_ms = tc["call_ms_median"], tc["walk_ms_median"]
+    # the timed region's averages (the roofline figure); the flushed per-call
+    # medians and minima beside them
+    walk_ms, call_ms = statistics.fmean(walks), wall * 1e3 / args.steps
     if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
         raise RuntimeError("non-finite output")
     # the dominant kernel is the rotating walk over 2T sub-steps, which on this
@@ -340,7 +356,8 @@ def trapezoid_bench(args) -> dict:
                      "traffic": profiled_traffic("trapezoid", "trapezoid"),
                      "algorithmic_bytes": walk_bytes, "kernel_ms": walk_ms, "forward_ms": call_ms,
                      "forward_bytes": trap_bytes,
-                     "forward_frac": trap_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "forward_frac": trap_bytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "flushed": flushed_block(tc, walk_bytes, trap_bytes)},
     }
     if not args.no_cpu_baseline:
         import oracle
@@ -366,15 +383,36 @@ FLUSH_BYTES = 1 << 30           # overwritten before each per-call timing: beyon
 def timed_region(step, args) -> float:
     """The contract's timed loop: W warm-up steps, then exactly K steps
     bracketed by device synchronisation. Returns the wall time of the K steps."""
+    return timed_region_walks(step, args, False)[0]
+
+
+def timed_region_walks(step, args, walks: bool = True):
+    """The contract's timed loop, with the output walk of every timed step
+    bracketed by a pair of HIP events that the library records on the launch
+    stream (created beforehand, without the system-scope fence). Returns the
+    wall time of the K steps and the K walk durations in ms (None without)."""
     import torch
+    hip = _hip() if walks else None
+    ev = [(_timing_event(hip), _timing_event(hip)) for _ in range(args.steps)] if walks else None
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        if ev:
+            step(walk_events=ev[i])
+        else:
+            step()
     torch.cuda.synchronize()
-    return time.perf_counter() - t0
+    wall = time.perf_counter() - t0
+    if not ev:
+        return wall, None
+    vp = __import__("ctypes").c_void_p
+    ms = [_elapsed_ms(hip, w0, w1) for w0, w1 in ev]
+    for pair in ev:
+        for h in pair:
+            hip.hipEventDestroy(vp(h))
+    return wall, ms
 
 
 def ssd_step_fn(ssd, g, shape, y, fin, stream, segments=0, block_slices=0):
@@ -402,8 +440,9 @@ def ssd_workload(cfg: int, args, with_timed_region: bool):
     stream = torch.cuda.current_stream(dev).cuda_stream
     step = ssd_step_fn(ssd, g, shape, y, fin, stream, args.segments, args.block_slices)
     nwarm = prewarm(step, args.prewarm)
-    wall = timed_region(step, args) if with_timed_region else None
+    wall, walks = timed_region_walks(step, args) if with_timed_region else (None, None)
     tc = time_calls(step, args.calls, FLUSH_BYTES)
+    tc["walks_timed"] = walks
     if not (torch.isfinite(y).all() and torch.isfinite(fin).all()):
         raise RuntimeError(f"workload {cfg}: non-finite output")
     nbytes = algorithmic_bytes(shape)
@@ -463,7 +502,6 @@ def moments_bench(args) -> dict:
     wall = timed_region(step, args)
     # per-call event timing after the same flush as the other lines (the
     # moments entry point has no walk events: the call is the unit)
-    import statistics
     flush = torch.empty(FLUSH_BYTES // 4, device=dev)
     ts = []
     for i in range(args.calls):
@@ -475,7 +513,9 @@ def moments_bench(args) -> dict:
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     del flush
-    call_ms = statistics.median(ts)
+    # the timed region's average call is the roofline figure; the flushed
+    # per-call median and minimum beside it
+    call_ms = wall * 1e3 / args.steps
     if not (torch.isfinite(m2).all() and torch.isfinite(m1).all()):
         raise RuntimeError("non-finite output")
     flops = moments_flops(shape, True, vl)
@@ -500,7 +540,8 @@ def moments_bench(args) -> dict:
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": None, "algorithmic_flops": flops, "kernel_ms": call_ms,
-                     "kernel_ms_min": min(ts), "forward_ms": call_ms},
+                     "forward_ms": call_ms,
+                     "flushed": {"kernel_ms_median": statistics.median(ts), "kernel_ms_min": min(ts)}},
         "timing": {"prewarm_s": args.prewarm, "prewarm_calls": nwarm},
     }
     if not args.no_cpu_baseline:
@@ -554,7 +595,6 @@ def backward_flops(shape) -> int:
 
 def backward_bench(args) -> dict:
     """Gradients of the scan (dx, dda, dB, dC, dinit, dtheta, dD) on one layer shape."""
-    import statistics
     import torch
     import chunked_ssd_scan_amd as ssd
     import ssd_inputs as si
@@ -593,7 +633,9 @@ def backward_bench(args) -> dict:
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
     del flush
-    call_ms = statistics.median(ts)
+    # the timed region's average call is the roofline figure; the flushed
+    # per-call median and minimum beside it
+    call_ms = wall * 1e3 / args.steps
     for k, v in out_t.items():
         if not torch.isfinite(v).all():
             raise RuntimeError(f"non-finite {k}")
@@ -620,7 +662,8 @@ def backward_bench(args) -> dict:
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None,
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_frac": flops / (call_ms * 1e-3) / 1e12 / mfma_peak,
-                     "kernel_ms": call_ms, "kernel_ms_min": min(ts), "unit_timed": "whole call"},
+                     "kernel_ms": call_ms, "unit_timed": "whole call",
+                     "flushed": {"kernel_ms_median": statistics.median(ts), "kernel_ms_min": min(ts)}},
         "timing": {"prewarm_s": args.prewarm, "prewarm_calls": nwarm},
     }
     if not args.no_cpu_baseline:
@@ -727,8 +770,12 @@ def main() -> int:
     ms_per_step = wall * 1e3 / args.steps
     nbytes = algorithmic_bytes(shape)
     flops = algorithmic_flops(shape)
-    walk_ms = tc["walk_ms_median"]
-    call_ms = tc["call_ms_median"]
+    # the roofline figure: the output walk's average duration over the timed
+    # region (HIP events around every timed walk); the whole call's is the
+    # timed region's time per step. The flushed per-call medians and minima
+    # are reported beside them.
+    walk_ms = statistics.fmean(tc["walks_timed"])
+    call_ms = ms_per_step
     achieved = nbytes / (walk_ms * 1e-3) / 1e9
     mfma_peak = MFMA_BF16_PEAK_TFLOPS if shape.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     out = {
@@ -754,19 +801,23 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": main_summary["traffic"],
                      "algorithmic_bytes": nbytes, "kernel_ms": walk_ms,
-                     "kernel_ms_min": tc["walk_ms_min"],
-                     "forward_ms": call_ms, "forward_ms_min": tc["call_ms_min"],
-                     "forward_frac": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                     "kernel_ms_timed_min": min(tc["walks_timed"]),
+                     "kernel_ms_timed_max": max(tc["walks_timed"]),
+                     "forward_ms": call_ms,
+                     "forward_frac": nbytes / (call_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "flushed": flushed_block(tc, nbytes, nbytes)},
         "mfma": {"algorithmic_tflop": flops / 1e12,
                  "tile_rows": KERNEL_TILE_ROWS,
                  "achieved_tflops": flops / (walk_ms * 1e-3) / 1e12,
                  "peak_tflops": mfma_peak,
                  "frac": flops / (walk_ms * 1e-3) / 1e12 / mfma_peak},
         "timing": {"prewarm_s": args.prewarm, "prewarm_calls": main_summary["prewarm_calls"],
-                   "per_call": f"{args.calls} calls, each after a {FLUSH_BYTES >> 20} MiB fill "
-                               "that evicts L2 and MALL; medians reported, min beside them",
                    "timed_region": "the K steps back to back, wall clock between two device "
-                                   "synchronisations"},
+                                   "synchronisations; the roofline's kernel_ms is the mean of "
+                                   "HIP events around each timed step's output walk",
+                   "flushed": f"{args.calls} calls, each after a {FLUSH_BYTES >> 20} MiB fill "
+                              "that evicts L2 and MALL; medians and minima",
+                   "workloads": "other workloads: flushed per-call medians"},
         "workloads": others,
     }
     if not args.no_cpu_baseline:
