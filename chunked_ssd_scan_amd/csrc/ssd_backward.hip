@@ -71,7 +71,8 @@ struct BwdArgs {
     const float* seg_in;    // entering (adjoint) states [b*H][S*SF][P][N] (forward walk) or
                             // [b*H][S][P][N] (backward walk), null with one segment
     float* seg_out;         // backward state pass: local adjoints [b*H][S][P][N]
-    float* part;            // per-head partials [b][T*R][H][npg][N] (dC or dB): heads interleaved per row
+    void* part;             // per-head partials [b][T*R][H][npg][N] (dC or dB): heads interleaved per row;
+                            // fp32 from the step walks, bf16 from the chunked walks
     float* dx;              // [b,T,R,H,P]
     float* dinit;           // [b,H,P,N] or null
     float* final_state;     // forward walk: h_{T-1} [b,H,P,N]
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_forward_kernel(BwdArgs
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     const int pbase = pg * PG;
-    float* dst = a.part + ((b * TR * H + h) * npg + pg) * N;   // [b][TR][H][npg][N]
+    float* dst = static_cast<float*>(a.part) + ((b * TR * H + h) * npg + pg) * N;   // [b][TR][H][npg][N]
 
     if constexpr (PAD > 0)
         for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void ssd_bwd_backward_kernel(BwdArg
     // carry starts from dfinal), so its workgroups leave at once, together
     if (!OUT && seg == 0) return;
     const int pbase = pg * PG;
-    float* dst = OUT ? a.part + ((b * TR * H + h) * npg + pg) * N : nullptr;
+    float* dst = OUT ? static_cast<float*>(a.part) + ((b * TR * H + h) * npg + pg) * N : nullptr;
 
     if constexpr (PAD > 0)
         for (int i = tid; i < 2 * PAD * LDX; i += nthr) {
@@ -987,6 +988,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rows(const float* base, i
     return make_rsrc(base + f0 * rs, (uint32_t)(rows * rs * 4));
 }
 
+// The same rows of a row-major bf16 array.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rows16(const uint16_t* base, int64_t f0, int64_t TR,
+                                                              int64_t rs) {
+    const int64_t rem = TR - f0, rows = rem < kTileRows ? rem : kTileRows;
+    return make_rsrc(base + f0 * rs, (uint32_t)(rows * rs * 2));
+}
+
 // Rows 16 i + 4 q + v of a tile, columns 16 c + l16 from the lane's byte
 // offset voff (row 4 q, column l16) and the uniform row and column steps
 __device__ __forceinline__ void store_tile_rows(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
@@ -995,6 +1003,17 @@ __device__ __forceinline__ void store_tile_rows(__amdgpu_buffer_rsrc_t rsrc, con
     for (int v = 0; v < 4; ++v) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z0[v]), rsrc, voff, colb + v * rowb, 0);
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z1[v]), rsrc, voff, colb + (16 + v) * rowb, 0);
+    }
+}
+
+// The same rows and columns rounded to bf16 (to nearest even), 2 bytes each
+__device__ __forceinline__ void store_tile_rows16(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
+                                                  uint32_t voff, uint32_t rowb, uint32_t colb) {
+    const s16x4 h0 = pack4_bf16(z0), h1 = pack4_bf16(z1);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h0[v], rsrc, voff, colb + v * rowb, 0);
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h1[v], rsrc, voff, colb + (16 + v) * rowb, 0);
     }
 }
 
@@ -1030,9 +1049,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     const int64_t bh = blockIdx.x / S;
     const int64_t b = bh / H, h = bh % H, g = h / (H / G);
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
-    float* dst = a.part + (b * TR * H + h) * N;            // [b][TR][H][N]
+    uint16_t* dst = static_cast<uint16_t*>(a.part) + (b * TR * H + h) * N;   // [b][TR][H][N], bf16
     const int64_t rs = H * N;
-    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 4), rowb = (uint32_t)(rs * 4);
+    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 2), rowb = (uint32_t)(rs * 2);
 
     // columns n >= N of B, p >= P of x and dy, and of the staged state stay
     // zero (the contractions over p run in steps of 32)
@@ -1108,7 +1127,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
         }
         // block rows [G o L (0,0) | 0] and [(1,0) | (1,1)]
         const s16x8 m0 = blk_pair(sM[0], nullptr, lane), m1 = blk_pair(sM[1], sM[2], lane);
-        const auto prs = tile_rows(dst, (int64_t)k * kTileRows, TR, rs);
+        const auto prs = tile_rows16(dst, (int64_t)k * kTileRows, TR, rs);
         // N is a multiple of 16: a column tile is all in range or all out
         for (int c = wv; c < NT && 16 * c < N; c += nw) {
             f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
@@ -1127,7 +1146,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             const s16x8 bb = tr_rows8(tB, LDB, 8 * q, 16 * c, lane);
             z0 = mma32(m0, bb, z0);
             z1 = mma32(m1, bb, z1);
-            store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
+            store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
         }
         // h <- e^{last} h + (w o x)^T B, contracted over the tile's 32 rows
         const float carry = cum[kCumE + kTileRows - 1];
@@ -1193,11 +1212,11 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     // the state pass: the first segment's local gradient is never used (the
     // carry starts from dfinal), so its workgroups leave at once, together
     if (!OUT && seg == 0) return;
-    float* dst = OUT ? a.part + (b * TR * H + h) * N : nullptr;
+    uint16_t* dst = OUT ? static_cast<uint16_t*>(a.part) + (b * TR * H + h) * N : nullptr;   // bf16
     const int64_t rs = H * N;
     // lane byte offsets of a tile's rows 4 q (+ uniform steps): partial rows
-    // (stride H N) at column l16, dy and dx rows (stride H P) at column p0 + l16
-    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 4), rowb = (uint32_t)(rs * 4);
+    // (stride H N, bf16) at column l16, dy and dx rows (stride H P) at column p0 + l16
+    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 2), rowb = (uint32_t)(rs * 2);
     const uint32_t xrow = (uint32_t)((4 * q * H * P + 16 * wv + l16) * 4), xrowb = (uint32_t)(H * P * 4);
     const float* dyh = a.dy + (b * TR * H + h) * P;
     float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
@@ -1328,7 +1347,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                         if (32 * kb < KP) xs[i][kb] = row8(tX + (16 * i + l16) * LDX + 32 * kb + 8 * q);
                 // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
                 const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
-                const auto prs = tile_rows(dst, f0, TR, rs);
+                const auto prs = tile_rows16(dst, f0, TR, rs);
                 // N is a multiple of 16: a column tile is all in range or all out
                 for (int c = wv; c < NT && 16 * c < N; c += nw) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
@@ -1347,7 +1366,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                     const s16x8 cc = tr_rows8(tC, LDB, 8 * q, 16 * c, lane);
                     z0 = mma32(g0, cc, z0);
                     z1 = mma32(g1, cc, z1);
-                    store_tile_rows(prs, z0, z1, prow, rowb, 64u * c);
+                    store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
                 }
             }
             // dx rows (rows past TR dropped; their dy and x are zero)
@@ -1462,79 +1481,90 @@ __global__ __launch_bounds__(256) void ssd_bwd_carry(const float* __restrict__ d
     }
 }
 
+// The sum over the 64 lanes, in every lane: DPP row shifts leave each 16-lane
+// row's total in its lane 15, the row broadcasts add rows 0 and 2 into rows 1
+// and 3 and then lane 31 into rows 2 and 3, so that lane 63 holds the total.
+__device__ __forceinline__ float wave_sum64(float v) {
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Two consecutive entries (a state pair) of a row: bf16 or fp32 storage.
+__device__ __forceinline__ float2 ld_pair(const uint16_t* p, uint32_t pair) {
+    const uint32_t w = reinterpret_cast<const uint32_t*>(p)[pair];
+    return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+}
+__device__ __forceinline__ float2 ld_pair(const float* p, uint32_t pair) {
+    return reinterpret_cast<const float2*>(p)[pair];
+}
+
 // dB and dC of every group (the heads' and row groups' partials added in
 // order) and, per head and step, the inner products and pair cross products
 // of the decay and turn gradients. One workgroup of 4 waves per (batch,
-// step). The ranks go in blocks of RM: wave w takes the heads w, w + 4, ...
-// of a group, HU of them at a time, and keeps its sums of dB and dC for each
-// rank of the block in registers; lanes take n = lane and lane + 64. The four waves' sums meet in
-// LDS and are added in wave order. A head's decay and turn terms add up over
-// the ranks of a block in registers and over blocks in its own output slot.
-// With phi the partials are of the folded frame and are turned back by
-// R(Phi_t) first. Loads take clamped, in-bounds indexes and are masked after,
-// so that all of a head's loads are in flight together.
-template <typename TI, int RM, int HU>
-__global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ pC, const float* __restrict__ pB,
+// step); lane k takes the state pair (2k, 2k + 1). The ranks go in blocks of
+// RM: wave w takes the heads w, w + 4, ... of a group, HU of them at a time,
+// and keeps its sums of dB and dC for each rank of the block in registers.
+// The four waves' sums meet in LDS and are added in wave order. A head's
+// decay and turn terms add up over the ranks of a block in registers and over
+// blocks in its own output slot. With phi the partials are of the folded
+// frame and are turned back by R(Phi_t) first. Loads take clamped, in-bounds
+// indexes and are masked after, so that all of a pass's loads are in flight
+// together. PT is the partials' storage type (bf16 from the chunked walks).
+template <typename TI, typename PT, int RM, int HU>
+__global__ __launch_bounds__(256) void ssd_bwd_reduce(const PT* __restrict__ pC, const PT* __restrict__ pB,
                                                      const void* __restrict__ Bv, const void* __restrict__ Cv,
                                                      float* __restrict__ dB, float* __restrict__ dC,
                                                      float* __restrict__ hv, float* __restrict__ th,
                                                      int64_t T, int64_t H, int64_t G, int64_t N, int64_t R, int npg,
                                                      int rot, const float* __restrict__ phi) {
-    __shared__ float sred[2][4][RM][128];
-    const int64_t bt = blockIdx.x, b = bt / T, t = bt % T;
+    __shared__ __attribute__((aligned(16))) float sred[2][4][RM][128];
+    const int64_t bt = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int64_t HG = H / G;
     // this step's rows: R ranks x H heads x npg row groups x N partials, and
     // R ranks x G groups x N entries of B, C, dB and dC; offsets in them fit 32 bits
     const int64_t row0 = bt * R;
-    const float* pBt = pB + row0 * H * npg * N;
-    const float* pCt = pC + row0 * H * npg * N;
+    const PT* pBt = pB + row0 * H * npg * N;
+    const PT* pCt = pC + row0 * H * npg * N;
     const TI* Bt = static_cast<const TI*>(Bv) + row0 * G * N;
     const TI* Ct = static_cast<const TI*>(Cv) + row0 * G * N;
     float* dBt = dB + row0 * G * N;
     float* dCt = dC + row0 * G * N;
     const float* phit = phi ? phi + bt * H * (N / 2) : nullptr;
     float* tht = th + bt * H * (N / 2);
-    // without phi the angle loads read entry 0 of the partials, unused: no branch
-    const float* phs = phit ? phit : pBt;
+    // without phi the angle loads read the first word of the partials, unused: no branch
+    const float* phs = phit ? phit : reinterpret_cast<const float*>(pBt);
     const uint32_t phm = phit ? 0xffffffffu : 0u;
-    const uint32_t Hu = (uint32_t)H, Gu = (uint32_t)G, Nu = (uint32_t)N, npu = (uint32_t)npg;
-    auto ld = [](const TI* p, uint32_t i) -> float {
-        if constexpr (sizeof(TI) == 2) return __uint_as_float((uint32_t)p[i] << 16);
-        else return p[i];
-    };
-    bool nok[2];
-    uint32_t nc[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-        const uint32_t n = lane + 64 * e;
-        nok[e] = n < Nu;
-        nc[e] = nok[e] ? n : 0;
-    }
+    const uint32_t Hu = (uint32_t)H, Gu = (uint32_t)G, NP2 = (uint32_t)(N / 2), npu = (uint32_t)npg;
+    const bool kok = (uint32_t)lane < NP2;
+    const uint32_t kc = kok ? (uint32_t)lane : 0;
+    const float2 zero2 = make_float2(0.f, 0.f);
     for (uint32_t g = 0; g < Gu; ++g) {
         for (int64_t r0 = 0; r0 < R; r0 += RM) {
-            float sb[RM][2], sc[RM][2], bn[RM][2], cn[RM][2];
-            bool ok[RM][2];
+            float2 sb[RM], sc[RM], bn[RM], cn[RM];
+            bool ok[RM];
             uint32_t rc[RM];
 #pragma unroll
             for (int k = 0; k < RM; ++k) {
                 const bool rin = r0 + k < R;
                 rc[k] = rin ? (uint32_t)(r0 + k) : 0;
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    ok[k][e] = rin && nok[e];
-                    const uint32_t i = (rc[k] * Gu + g) * Nu + nc[e];
-                    sb[k][e] = 0.f;
-                    sc[k][e] = 0.f;
-                    const float bv = ld(Bt, i), cv = ld(Ct, i);
-                    bn[k][e] = ok[k][e] ? bv : 0.f;
-                    cn[k][e] = ok[k][e] ? cv : 0.f;
-                }
+                ok[k] = rin && kok;
+                sb[k] = zero2;
+                sc[k] = zero2;
+                const uint32_t i = (rc[k] * Gu + g) * NP2 + kc;
+                const float2 bv = ld_pair(Bt, i), cv = ld_pair(Ct, i);
+                bn[k] = ok[k] ? bv : zero2;
+                cn[k] = ok[k] ? cv : zero2;
             }
             const uint32_t hend = (g + 1) * (uint32_t)HG;
             for (uint32_t h0 = g * (uint32_t)HG + w; h0 < hend; h0 += 4 * HU) {
-                // heads h0 + 4 j of this pass; one past the group's end is
-                // clamped to h0 and its terms are dropped
+                // heads h0 + 4 j of this pass; past the group's end they are
+                // clamped to h0 and their terms are dropped
                 uint32_t hj[HU];
                 bool hok[HU];
 #pragma unroll
@@ -1542,95 +1572,78 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ 
                     hok[j] = h0 + 4 * j < hend;
                     hj[j] = hok[j] ? h0 + 4 * j : h0;
                 }
-                float db[HU][RM][2], dc[HU][RM][2], ph[HU][2];
+                float2 db[HU][RM], dc[HU][RM];
+                float ph[HU];
 #pragma unroll
-                for (int j = 0; j < HU; ++j)
+                for (int j = 0; j < HU; ++j) {
+                    ph[j] = phs[(hj[j] * NP2 + kc) & phm];
 #pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        ph[j][e] = phs[(hj[j] * (Nu / 2) + (nc[e] >> 1)) & phm];
-#pragma unroll
-                        for (int k = 0; k < RM; ++k) {
-                            const uint32_t i = (rc[k] * Hu + hj[j]) * npu * Nu + nc[e];
-                            db[j][k][e] = pBt[i];
-                            dc[j][k][e] = pCt[i];
-                        }
+                    for (int k = 0; k < RM; ++k) {
+                        const uint32_t i = (rc[k] * Hu + hj[j]) * npu * NP2 + kc;
+                        db[j][k] = ld_pair(pBt, i);
+                        dc[j][k] = ld_pair(pCt, i);
                     }
+                }
                 for (uint32_t pg = 1; pg < npu; ++pg)
 #pragma unroll
                     for (int j = 0; j < HU; ++j)
 #pragma unroll
-                        for (int k = 0; k < RM; ++k)
-#pragma unroll
-                            for (int e = 0; e < 2; ++e) {
-                                const uint32_t i = ((rc[k] * Hu + hj[j]) * npu + pg) * Nu + nc[e];
-                                db[j][k][e] += pBt[i];
-                                dc[j][k][e] += pCt[i];
-                            }
+                        for (int k = 0; k < RM; ++k) {
+                            const uint32_t i = ((rc[k] * Hu + hj[j]) * npu + pg) * NP2 + kc;
+                            const float2 b2 = ld_pair(pBt, i), c2 = ld_pair(pCt, i);
+                            db[j][k].x += b2.x;
+                            db[j][k].y += b2.y;
+                            dc[j][k].x += c2.x;
+                            dc[j][k].y += c2.y;
+                        }
 #pragma unroll
                 for (int j = 0; j < HU; ++j) {
-                    float cs[2] = {1.f, 1.f}, sn[2] = {0.f, 0.f};
+                    float cs = 1.f, sn = 0.f;
                     if (phit) {
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            const float rev = ph[j][e] * kInv2Pi;
-                            cs[e] = __builtin_amdgcn_cosf(rev);
-                            sn[e] = __builtin_amdgcn_sinf(rev);
-                        }
+                        const float rev = ph[j] * kInv2Pi;
+                        cs = __builtin_amdgcn_cosf(rev);
+                        sn = __builtin_amdgcn_sinf(rev);
                     }
-                    float hvacc = 0.f, thacc[2] = {0.f, 0.f};
+                    float hvacc = 0.f, thacc = 0.f;
 #pragma unroll
                     for (int k = 0; k < RM; ++k) {
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            float bd = db[j][k][e], cd = dc[j][k][e];
-                            if (!(ok[k][e] && hok[j])) bd = cd = 0.f;
-                            if (phit) {
-                                // partials of the folded frame: dB = R(Phi_t) dB~, dC = R(Phi_t) dC~
-                                const float part = (lane & 1) ? sn[e] : -sn[e];
-                                const float bp = __shfl_xor(bd, 1), cp = __shfl_xor(cd, 1);
-                                bd = fmaf(cs[e], bd, part * bp);
-                                cd = fmaf(cs[e], cd, part * cp);
-                            }
-                            sb[k][e] += bd;
-                            sc[k][e] += cd;
-                            hvacc = fmaf(cn[k][e], cd, fmaf(-bn[k][e], bd, hvacc));
-                            if (rot) {
-                                // lanes n (even) and n + 1: (dC_n C_n+1 - dC_n+1 C_n) + (dB_n B_n+1 - dB_n+1 B_n)
-                                const float cdn = __shfl_xor(cd, 1), cnn = __shfl_xor(cn[k][e], 1);
-                                const float bdn = __shfl_xor(bd, 1), bnn = __shfl_xor(bn[k][e], 1);
-                                thacc[e] += (cd * cnn - cdn * cn[k][e]) + (bd * bnn - bdn * bn[k][e]);
-                            }
+                        float2 bd = db[j][k], cd = dc[j][k];
+                        if (!(ok[k] && hok[j])) bd = cd = zero2;
+                        if (phit) {
+                            // partials of the folded frame: dB = R(Phi_t) dB~, dC = R(Phi_t) dC~
+                            bd = make_float2(fmaf(cs, bd.x, -sn * bd.y), fmaf(cs, bd.y, sn * bd.x));
+                            cd = make_float2(fmaf(cs, cd.x, -sn * cd.y), fmaf(cs, cd.y, sn * cd.x));
                         }
+                        sb[k].x += bd.x;
+                        sb[k].y += bd.y;
+                        sc[k].x += cd.x;
+                        sc[k].y += cd.y;
+                        hvacc = fmaf(cn[k].x, cd.x, fmaf(cn[k].y, cd.y, fmaf(-bn[k].x, bd.x, fmaf(-bn[k].y, bd.y, hvacc))));
+                        // (dC_2k C_2k+1 - dC_2k+1 C_2k) + (dB_2k B_2k+1 - dB_2k+1 B_2k)
+                        if (rot) thacc += (cd.x * cn[k].y - cd.y * cn[k].x) + (bd.x * bn[k].y - bd.y * bn[k].x);
                     }
                     if (!hok[j]) continue;
-                    for (int o = 32; o >= 1; o >>= 1) hvacc += __shfl_xor(hvacc, o);
+                    hvacc = wave_sum64(hvacc);
                     const int64_t ht = bt * H + hj[j];
                     if (lane == 0) hv[ht] = r0 == 0 ? hvacc : hv[ht] + hvacc;
-                    if (rot) {
-#pragma unroll
-                        for (int e = 0; e < 2; ++e) {
-                            if ((lane & 1) == 0 && nok[e]) {
-                                float* q = tht + hj[j] * (Nu / 2) + ((lane + 64 * e) >> 1);
-                                *q = r0 == 0 ? thacc[e] : *q + thacc[e];
-                            }
-                        }
+                    if (rot && kok) {
+                        float* q = tht + hj[j] * NP2 + lane;
+                        *q = r0 == 0 ? thacc : *q + thacc;
                     }
                 }
             }
 #pragma unroll
-            for (int k = 0; k < RM; ++k)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    sred[0][w][k][lane + 64 * e] = sb[k][e];
-                    sred[1][w][k][lane + 64 * e] = sc[k][e];
-                }
+            for (int k = 0; k < RM; ++k) {
+                *reinterpret_cast<float2*>(&sred[0][w][k][2 * lane]) = sb[k];
+                *reinterpret_cast<float2*>(&sred[1][w][k][2 * lane]) = sc[k];
+            }
             __syncthreads();
             for (int i = tid; i < RM * 128; i += 256) {
                 const int k = i >> 7, n = i & 127;
                 if (n >= N || r0 + k >= R) continue;
                 const float vb = sred[0][0][k][n] + sred[0][1][k][n] + sred[0][2][k][n] + sred[0][3][k][n];
                 const float vc = sred[1][0][k][n] + sred[1][1][k][n] + sred[1][2][k][n] + sred[1][3][k][n];
-                const uint32_t o = ((uint32_t)(r0 + k) * Gu + g) * Nu + n;
+                const uint32_t o = ((uint32_t)(r0 + k) * Gu + g) * (uint32_t)N + n;
                 dBt[o] = vb;
                 dCt[o] = vc;
             }
@@ -1639,13 +1652,13 @@ __global__ __launch_bounds__(256) void ssd_bwd_reduce(const float* __restrict__ 
     }
 }
 
-// the blocks of the reduction: one rank and four heads per pass, two ranks
-// and two heads, or four ranks and one head
-template <typename TI>
+// the blocks of the reduction (16 pair loads in flight per wave and pass):
+// one rank and eight heads, two ranks and four heads, or four ranks and two
+template <typename TI, typename PT>
 void* bwd_reduce_for(int64_t R) {
-    if (R <= 1) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 1, 4>);
-    if (R == 2) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 2, 2>);
-    return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, 4, 1>);
+    if (R <= 1) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, PT, 1, 4>);
+    if (R == 2) return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, PT, 2, 2>);
+    return reinterpret_cast<void*>(&ssd_bwd_reduce<TI, PT, 4, 1>);
 }
 
 // dda and dtheta are reverse cumulative sums over the steps of the per-step
@@ -1924,7 +1937,9 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
                         : bf ? bwd_backward_np<uint16_t, 0>(NP) : bwd_backward_np<float, 0>(NP);
     void* kb1 = chunked ? (rot ? bwdc_backward_np<1, true>(NP) : bwdc_backward_np<1, false>(NP))
                         : bf ? bwd_backward_np<uint16_t, 1>(NP) : bwd_backward_np<float, 1>(NP);
-    void* kr = bf ? bwd_reduce_for<uint16_t>(R) : bwd_reduce_for<float>(R);
+    // partials: bf16 from the chunked walks, fp32 from the step walks
+    void* kr = chunked ? bwd_reduce_for<uint16_t, uint16_t>(R)
+                       : bf ? bwd_reduce_for<uint16_t, float>(R) : bwd_reduce_for<float, float>(R);
     if (!kf || !kb0 || !kb1) return SSD_ERR_UNSUPPORTED;
     const int PG = (int)(P < kRowGroup ? P : kRowGroup), npg = (int)(P / PG);
     if (chunked && npg != 1) return SSD_ERR_UNSUPPORTED;
@@ -1943,7 +1958,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off += align256(bytes); return o; };
     const size_t o_states = take(st_bytes);
-    const size_t o_pC = take(n_part * 4), o_pB = take(n_part * 4);
+    const size_t psz = chunked ? 2 : 4;                // bytes per partial entry
+    const size_t o_pC = take(n_part * psz), o_pB = take(n_part * psz);
     const size_t o_fin = take((size_t)(b * H * P * N) * 4);
     const size_t o_hv = take((size_t)(b * T * H) * 4);
     const size_t o_th = take(rot ? (size_t)(b * T * H * (N / 2)) * 4 : 4);
@@ -2004,7 +2020,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     if (rs == SSD_OK) {
         BwdArgs fa = ba;
         fa.seg_in = fws_state;
-        fa.part = reinterpret_cast<float*>(ws + o_pC);
+        fa.part = ws + o_pC;
         fa.final_state = fin;
         void* kargs[] = {&fa};
         if (hipLaunchKernel(kf, grid, block, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
@@ -2033,7 +2049,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     if (rs == SSD_OK) {
         BwdArgs oa = ba;
         oa.seg_in = S > 1 ? seg_in : nullptr;
-        oa.part = reinterpret_cast<float*>(ws + o_pB);
+        oa.part = ws + o_pB;
         oa.dDp = reinterpret_cast<float*>(ws + o_dd);
         void* kargs[] = {&oa};
         if (hipLaunchKernel(kb0, grid, block, kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
@@ -2045,8 +2061,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     side_lock.unlock();
     // 4. group sums and per-step terms; 5. reverse cumulative sums
     if (rs == SSD_OK) {
-        const float* pC = reinterpret_cast<const float*>(ws + o_pC);
-        const float* pB = reinterpret_cast<const float*>(ws + o_pB);
+        const void* pC = ws + o_pC;
+        const void* pB = ws + o_pB;
         float* hv = reinterpret_cast<float*>(ws + o_hv);
         float* th = reinterpret_cast<float*>(ws + o_th);
         int64_t Tv = T, Hv = H, Gv = G, Nv = N, Rv = R;
