@@ -79,6 +79,7 @@ KERNEL_SOURCES = {
     "ssd": SSD_SOURCES,
     "selective_scan": ("sel_scan.hip", "ssd_common.h"),
     "trapezoid": SSD_SOURCES + ("trap_scan.hip",),
+    "backward": SSD_SOURCES + ("ssd_backward.hip", "ssd_step.h"),
 }
 
 
@@ -659,7 +660,8 @@ def backward_bench(args) -> dict:
                    "headdim": P, "dstate": N, "mimo_rank": R, "rotation": shape.rotation,
                    "init_state": shape.init_state, "skip": shape.skip, "dfinal": True},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic(f"backward_cfg{args.config}", "backward"),
                      "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
                      "mfma_frac": flops / (call_ms * 1e-3) / 1e12 / mfma_peak,
                      "kernel_ms": call_ms, "unit_timed": "whole call",
