@@ -1663,16 +1663,19 @@ void* bwd_reduce_for(int64_t R) {
 
 // dda and dtheta are reverse cumulative sums over the steps of the per-step
 // terms (column k < N/2: the turn of pair k; column N/2: the decay), plus the
-// final state's terms at the last step. Three kernels: the final state's terms
-// and dD (per (batch, head)), the sums of chunks of kScanChunk steps, and the
-// scan of each chunk from the sums of the chunks after it.
-constexpr int kScanChunk = 256;
+// final state's terms at the last step. Four kernels: the final state's terms
+// and dD (per (batch, head)), the sums of chunks of kScanChunk steps, each
+// chunk's carry (the final terms plus the sums of the chunks after it, one
+// thread per (batch, head, column) walking the chunks), and the scan of each
+// chunk from its carry.
+constexpr int kScanChunk = 64;
 
 // Phi[b,t,h,k] = sum over s <= t of theta[b,s,h,k], kept in [-pi, pi] (the
 // running sum is wrapped each step so that it keeps its absolute precision;
 // 2 pi split into a head exact in few bits and a tail, as in Cody and
-// Waite's argument reduction). Two kernels over chunks of kScanChunk steps:
-// the chunks' sums, then each chunk's scan from the earlier chunks' sums.
+// Waite's argument reduction). Three kernels over chunks of kScanChunk steps:
+// the chunks' sums, the angle entering each chunk (one thread per (batch,
+// head, pair) walking the chunks), then each chunk's scan from it.
 // Thread -> (batch-head, chunk, pair), pairs fastest.
 __device__ __forceinline__ float wrap_2pi(float v) {
     const float m = rintf(v * kInv2Pi);
@@ -1691,15 +1694,30 @@ __global__ __launch_bounds__(256) void ssd_bwd_phi_sums(const float* __restrict_
     psum[i] = wrap_2pi(acc);
 }
 
-__global__ __launch_bounds__(256) void ssd_bwd_phi(const float* __restrict__ theta, const float* __restrict__ psum,
+// the chunks' sums replaced in place by the angle entering each chunk
+__global__ __launch_bounds__(256) void ssd_bwd_phi_carry(float* __restrict__ psum, int64_t NH, int nchunk,
+                                                        int64_t items) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= items) return;
+    const int64_t k = i % NH, bh = i / NH;
+    float run = 0.f;
+    // the loads do not depend on the running angle: unrolled, several are in flight
+#pragma unroll 8
+    for (int c = 0; c < nchunk; ++c) {
+        float* q = psum + (bh * nchunk + c) * NH + k;
+        const float v = *q;
+        *q = run;
+        run = wrap_2pi(run + v);
+    }
+}
+
+__global__ __launch_bounds__(256) void ssd_bwd_phi(const float* __restrict__ theta, const float* __restrict__ pin,
                                                   float* __restrict__ phi, int64_t T, int64_t H, int64_t NH,
                                                   int nchunk, int64_t items) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= items) return;
     const int64_t k = i % NH, ch = (i / NH) % nchunk, bh = i / (NH * nchunk), h = bh % H, b = bh / H;
-    float run = 0.f;
-#pragma unroll 8
-    for (int c = 0; c < ch; ++c) run = wrap_2pi(run + psum[(bh * nchunk + c) * NH + k]);
+    float run = pin[i];
     const int64_t t0 = ch * (int64_t)kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
     // the loads do not depend on the running angle: unrolled, several are in flight
 #pragma unroll 8
@@ -1715,26 +1733,31 @@ __global__ __launch_bounds__(128) void ssd_bwd_final_terms(const float* __restri
                                                           const float* __restrict__ dDp, float* __restrict__ ft,
                                                           float* __restrict__ dD, int64_t B_, int64_t H, int64_t P,
                                                           int64_t N, int nparts) {
+    // lane k takes the state pair (2k, 2k + 1) of rows p = half, half + 2, ...:
+    // dfinal . fin over the pair, and the pair's cross product
     const int64_t bh = blockIdx.x, b = bh / H, h = bh % H;
-    const int k = threadIdx.x, nc = (int)(N / 2 + 1);
-    __shared__ float sfin[2];
-    float v = 0.f;
-    if (dfinal)
-        for (int64_t i = k; i < P * N; i += blockDim.x) v += dfinal[bh * P * N + i] * fin[bh * P * N + i];
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    if ((k & 63) == 0) sfin[k >> 6] = v;
+    const int tid = threadIdx.x, k = tid & 63, half = tid >> 6, nc = (int)(N / 2 + 1);
+    __shared__ float sdot[2], scr[2][64];
+    float dot = 0.f, cr = 0.f;
+    if (dfinal && k < N / 2) {
+        const float2* df = reinterpret_cast<const float2*>(dfinal + bh * P * N) + k;
+        const float2* fi = reinterpret_cast<const float2*>(fin + bh * P * N) + k;
+#pragma unroll 4
+        for (int64_t p = half; p < P; p += 2) {
+            const float2 a = df[p * (N / 2)], c = fi[p * (N / 2)];
+            dot = fmaf(a.x, c.x, fmaf(a.y, c.y, dot));
+            cr += a.y * c.x - a.x * c.y;
+        }
+    }
+    dot = wave_sum64(dot);
+    if (k == 0) sdot[half] = dot;
+    scr[half][k] = cr;
     __syncthreads();
-    if (k < N / 2) {
-        float acc = 0.f;
-        if (dfinal)
-            for (int64_t p = 0; p < P; ++p) {
-                const int64_t o = bh * P * N + p * N + 2 * k;
-                acc += dfinal[o + 1] * fin[o] - dfinal[o] * fin[o + 1];
-            }
-        ft[bh * nc + k] = acc;
-    } else if (k == N / 2) {
-        ft[bh * nc + k] = sfin[0] + sfin[1];
-    } else if (k == N / 2 + 1 && dD && b == 0) {
+    if (tid < N / 2) {
+        ft[bh * nc + tid] = scr[0][tid] + scr[1][tid];
+    } else if (tid == N / 2) {
+        ft[bh * nc + tid] = sdot[0] + sdot[1];
+    } else if (tid == N / 2 + 1 && dD && b == 0) {
         float acc = 0.f;
         for (int64_t bb = 0; bb < B_; ++bb)
             for (int i = 0; i < nparts; ++i) acc += dDp[(bb * H + h) * nparts + i];
@@ -1779,11 +1802,30 @@ __global__ __launch_bounds__(128) void ssd_bwd_chunk_sums(const float* __restric
     csum[(bh * nchunk + ch) * nc + k] = acc;
 }
 
+// the chunks' sums replaced in place by each chunk's carry: the final terms
+// plus the sums of the chunks after it
+__global__ __launch_bounds__(128) void ssd_bwd_chunk_carry(const float* __restrict__ ft, float* __restrict__ csum,
+                                                          int nchunk, int nc, int k0, int64_t items) {
+    const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (it >= items) return;
+    const int ncols = nc - k0;
+    const int k = k0 + (int)(it % ncols);
+    const int64_t bh = it / ncols;
+    float acc = ft[bh * nc + k];
+    // loads do not depend on the running sum: unrolled, several are in flight
+#pragma unroll 8
+    for (int c = nchunk - 1; c >= 0; --c) {
+        float* q = csum + (bh * nchunk + c) * nc + k;
+        const float v = *q;
+        *q = acc;
+        acc += v;
+    }
+}
+
 __global__ __launch_bounds__(128) void ssd_bwd_chunk_scan(const float* __restrict__ hv, const float* __restrict__ th,
-                                                         const float* __restrict__ csum, const float* __restrict__ ft,
-                                                         float* __restrict__ dda, float* __restrict__ dtheta,
-                                                         int64_t T, int64_t H, int64_t N, int nchunk, int k0,
-                                                         int64_t items) {
+                                                         const float* __restrict__ carry, float* __restrict__ dda,
+                                                         float* __restrict__ dtheta, int64_t T, int64_t H, int64_t N,
+                                                         int nchunk, int k0, int64_t items) {
     const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (it >= items) return;
     const int nc = (int)(N / 2 + 1), ncols = nc - k0;
@@ -1791,10 +1833,7 @@ __global__ __launch_bounds__(128) void ssd_bwd_chunk_scan(const float* __restric
     int64_t b, h;
     const int k = scan_item(it, ncols, k0, H, nchunk, &h, &ch, &b);
     const int64_t bh = b * H + h;
-    float acc = ft[bh * nc + k];
-    // loads do not depend on the running sum: unrolled, several are in flight
-#pragma unroll 8
-    for (int c = nchunk - 1; c > ch; --c) acc += csum[(bh * nchunk + c) * nc + k];
+    float acc = carry[(bh * nchunk + ch) * nc + k];
     const int64_t t0 = (int64_t)ch * kScanChunk, t1 = t0 + kScanChunk < T ? t0 + kScanChunk : T;
     float* out = k < N / 2 ? dtheta : dda;
 #pragma unroll 8
@@ -1996,8 +2035,11 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         const int nch = (int)((T + kScanChunk - 1) / kScanChunk);
         const int64_t n = b * H * nch * (N / 2);
         float* psum = reinterpret_cast<float*>(ws + o_csum);
+        const int64_t nk = b * H * (N / 2);
         hipLaunchKernelGGL(ssd_bwd_phi_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, theta, psum, T, H,
                            N / 2, nch, n);
+        hipLaunchKernelGGL(ssd_bwd_phi_carry, dim3((unsigned)((nk + 255) / 256)), dim3(256), 0, hs, psum, N / 2, nch,
+                           nk);
         hipLaunchKernelGGL(ssd_bwd_phi, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, hs, theta, psum, phi, T, H,
                            N / 2, nch, n);
         if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
@@ -2072,8 +2114,8 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
                          (void*)&th, (void*)&Tv, (void*)&Hv, (void*)&Gv, (void*)&Nv, (void*)&Rv, (void*)&npgv,
                          (void*)&rotv, (void*)&phiv};
         if (hipLaunchKernel(kr, dim3((unsigned)(b * T)), dim3(256), kargs, 0, hs) != hipSuccess) rs = SSD_ERR_HIP;
-        // final-state terms and dD; chunk sums; chunk scans (columns from k0:
-        // all pairs with rotation, only the decay column without)
+        // final-state terms and dD; chunk sums; chunk carries; chunk scans
+        // (columns from k0: all pairs with rotation, only the decay column without)
         const int nc = (int)(N / 2 + 1), nchunk = (int)((T + kScanChunk - 1) / kScanChunk);
         const int k0 = rot ? 0 : (int)(N / 2);
         float* ft = reinterpret_cast<float*>(ws + o_ft);
@@ -2083,8 +2125,11 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
                                reinterpret_cast<const float*>(ws + o_dd), ft, dD, b, H, P, N, npg * S);
             const int64_t items = b * H * nchunk * (int64_t)(nc - k0);
             const dim3 sgrid((unsigned)((items + 127) / 128));
+            const int64_t citems = b * H * (int64_t)(nc - k0);
             hipLaunchKernelGGL(ssd_bwd_chunk_sums, sgrid, dim3(128), 0, hs, hv, th, csum, T, H, N, nchunk, k0, items);
-            hipLaunchKernelGGL(ssd_bwd_chunk_scan, sgrid, dim3(128), 0, hs, hv, th, csum, ft, dda, dtheta, T, H, N,
+            hipLaunchKernelGGL(ssd_bwd_chunk_carry, dim3((unsigned)((citems + 127) / 128)), dim3(128), 0, hs, ft, csum,
+                               nchunk, nc, k0, citems);
+            hipLaunchKernelGGL(ssd_bwd_chunk_scan, sgrid, dim3(128), 0, hs, hv, th, csum, dda, dtheta, T, H, N,
                                nchunk, k0, items);
             if (hipGetLastError() != hipSuccess) rs = SSD_ERR_HIP;
         }
