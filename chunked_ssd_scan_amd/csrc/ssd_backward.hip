@@ -1669,6 +1669,7 @@ void* bwd_reduce_for(int64_t R) {
 // thread per (batch, head, column) walking the chunks), and the scan of each
 // chunk from its carry.
 constexpr int kScanChunk = 64;
+constexpr int kCarryBlock = 16;   // chunks whose sums a carry thread loads at once
 
 // Phi[b,t,h,k] = sum over s <= t of theta[b,s,h,k], kept in [-pi, pi] (the
 // running sum is wrapped each step so that it keeps its absolute precision;
@@ -1700,14 +1701,19 @@ __global__ __launch_bounds__(256) void ssd_bwd_phi_carry(float* __restrict__ psu
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= items) return;
     const int64_t k = i % NH, bh = i / NH;
+    float* col = psum + bh * nchunk * NH + k;
     float run = 0.f;
-    // the loads do not depend on the running angle: unrolled, several are in flight
-#pragma unroll 8
-    for (int c = 0; c < nchunk; ++c) {
-        float* q = psum + (bh * nchunk + c) * NH + k;
-        const float v = *q;
-        *q = run;
-        run = wrap_2pi(run + v);
+    // blocks of kCarryBlock chunks: every load of a block is issued before its
+    // stores (same array), so that they are in flight together
+    for (int c0 = 0; c0 < nchunk; c0 += kCarryBlock) {
+        float v[kCarryBlock];
+#pragma unroll
+        for (int j = 0; j < kCarryBlock; ++j) v[j] = c0 + j < nchunk ? col[(int64_t)(c0 + j) * NH] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kCarryBlock; ++j) {
+            if (c0 + j < nchunk) col[(int64_t)(c0 + j) * NH] = run;
+            run = wrap_2pi(run + v[j]);
+        }
     }
 }
 
@@ -1811,14 +1817,19 @@ __global__ __launch_bounds__(128) void ssd_bwd_chunk_carry(const float* __restri
     const int ncols = nc - k0;
     const int k = k0 + (int)(it % ncols);
     const int64_t bh = it / ncols;
+    float* col = csum + bh * nchunk * nc + k;
     float acc = ft[bh * nc + k];
-    // loads do not depend on the running sum: unrolled, several are in flight
-#pragma unroll 8
-    for (int c = nchunk - 1; c >= 0; --c) {
-        float* q = csum + (bh * nchunk + c) * nc + k;
-        const float v = *q;
-        *q = acc;
-        acc += v;
+    // blocks of kCarryBlock chunks from the last: every load of a block is
+    // issued before its stores (same array), so that they are in flight together
+    for (int c0 = nchunk - 1; c0 >= 0; c0 -= kCarryBlock) {
+        float v[kCarryBlock];
+#pragma unroll
+        for (int j = 0; j < kCarryBlock; ++j) v[j] = c0 - j >= 0 ? col[(int64_t)(c0 - j) * nc] : 0.f;
+#pragma unroll
+        for (int j = 0; j < kCarryBlock; ++j) {
+            if (c0 - j >= 0) col[(int64_t)(c0 - j) * nc] = acc;
+            acc += v[j];
+        }
     }
 }
 
