@@ -1128,8 +1128,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
         // block rows [G o L (0,0) | 0] and [(1,0) | (1,1)]
         const s16x8 m0 = blk_pair(sM[0], nullptr, lane), m1 = blk_pair(sM[1], sM[2], lane);
         const auto prs = tile_rows16(dst, (int64_t)k * kTileRows, TR, rs);
-        // N is a multiple of 16: a column tile is all in range or all out
-        for (int c = wv; c < NT && 16 * c < N; c += nw) {
+        // the wave's dC column tiles c = wv, wv + nw, ...
+        auto dc_tile = [&](int c) {
             f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 32; ++kb) {
@@ -1147,6 +1147,15 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             z0 = mma32(m0, bb, z0);
             z1 = mma32(m1, bb, z1);
             store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
+        };
+        if (NT % (kRowGroup / 16) == 0 && nw == kRowGroup / 16 && N == NP) {
+            // four compute waves and every column tile in range: unrolled, so
+            // that one tile's LDS reads overlap the other's products
+#pragma unroll
+            for (int j = 0; j < NT / (kRowGroup / 16); ++j) dc_tile(wv + (kRowGroup / 16) * j);
+        } else {
+            // N is a multiple of 16: a column tile is all in range or all out
+            for (int c = wv; c < NT && 16 * c < N; c += nw) dc_tile(c);
         }
         // h <- e^{last} h + (w o x)^T B, contracted over the tile's 32 rows
         const float carry = cum[kCumE + kTileRows - 1];
@@ -1348,8 +1357,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
                 const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
                 const auto prs = tile_rows16(dst, f0, TR, rs);
-                // N is a multiple of 16: a column tile is all in range or all out
-                for (int c = wv; c < NT && 16 * c < N; c += nw) {
+                // the wave's dB column tiles c = wv, wv + nw, ...
+                auto db_tile = [&](int c) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < kRowGroup / 32; ++kb) {
@@ -1367,6 +1376,15 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                     z0 = mma32(g0, cc, z0);
                     z1 = mma32(g1, cc, z1);
                     store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
+                };
+                if (NT % (kRowGroup / 16) == 0 && nw == kRowGroup / 16 && N == NP) {
+                    // four compute waves and every column tile in range: unrolled, so
+                    // that one tile's LDS reads overlap the other's products
+#pragma unroll
+                    for (int j = 0; j < NT / (kRowGroup / 16); ++j) db_tile(wv + (kRowGroup / 16) * j);
+                } else {
+                    // N is a multiple of 16: a column tile is all in range or all out
+                    for (int c = wv; c < NT && 16 * c < N; c += nw) db_tile(c);
                 }
             }
             // dx rows (rows past TR dropped; their dy and x are zero)
