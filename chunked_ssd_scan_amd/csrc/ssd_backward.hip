@@ -885,10 +885,12 @@ __device__ __forceinline__ s16x8 blk_pair(const uint16_t* left, const uint16_t* 
 }
 
 // rows_dot with contraction length 32 (K a multiple of 32)
+template <int K>
 __device__ __forceinline__ f32x4 rows_dot32(const uint16_t* ta, int lda, int mrow0, const uint16_t* tb, int ldb,
-                                            int jrow0, int K, int lane) {
+                                            int jrow0, int lane) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int l16 = lane & 15, q = lane >> 4;
+#pragma unroll
     for (int k0 = 0; k0 < K; k0 += 32)
         acc = mma32(row8(ta + (mrow0 + l16) * lda + k0 + 8 * q), row8(tb + (jrow0 + l16) * ldb + k0 + 8 * q), acc);
     return acc;
@@ -1042,7 +1044,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
     const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
-    const int KP = (int)((P + 31) & ~31);              // contractions over p, in steps of 32
     const bool memw = wv >= nw;
     const int mt = tid - 64 * nw;
     const int seg = blockIdx.x % S;
@@ -1054,7 +1055,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 2), rowb = (uint32_t)(rs * 2);
 
     // columns n >= N of B, p >= P of x and dy, and of the staged state stay
-    // zero (the contractions over p run in steps of 32)
+    // zero (the contractions over p always run over the 64 rows of a group)
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
     for (int i = tid; i < 2 * ROWS * LDX; i += blockDim.x) {
         sX[i / (ROWS * LDX)][i % (ROWS * LDX)] = TI(0);
@@ -1110,7 +1111,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
         // G o L blocks (0,0), (1,0), (1,1): rows m of dy against rows j of x
         for (int u = wv; u < 3; u += nw) {
             const int mb = u == 0 ? 0 : 1, jb = u == 2 ? 1 : 0;
-            const f32x4 gacc = rows_dot32(tDy, LDX, 16 * mb, tX, LDX, 16 * jb, KP, lane);
+            const f32x4 gacc = rows_dot32<kRowGroup>(tDy, LDX, 16 * mb, tX, LDX, 16 * jb, lane);
             put_masked(sM[u], gacc, mb, jb, false, cum, log2R, lane);
         }
         __syncthreads();
@@ -1123,7 +1124,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             for (int v = 0; v < 4; ++v) ein[i][v] = cum[kCumE + 16 * i + 4 * q + v];
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 32; ++kb)
-                if (32 * kb < KP) dya[i][kb] = row8(tDy + (16 * i + l16) * LDX + 32 * kb + 8 * q);
+                dya[i][kb] = row8(tDy + (16 * i + l16) * LDX + 32 * kb + 8 * q);
         }
         // block rows [G o L (0,0) | 0] and [(1,0) | (1,1)]
         const s16x8 m0 = blk_pair(sM[0], nullptr, lane), m1 = blk_pair(sM[1], sM[2], lane);
@@ -1133,7 +1134,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 32; ++kb) {
-                if (32 * kb >= KP) break;
                 const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
                 z0 = mma32(dya[0][kb], hb, z0);
                 z1 = mma32(dya[1][kb], hb, z1);
@@ -1211,7 +1211,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     const int q = lane >> 4, l16 = lane & 15;
     const int64_t T = a.T, H = a.H, G = a.G, N = a.N, R = a.R, P = a.P, TR = T * R;
     const int nw = (int)(P >> 4), S = a.S, Qt = a.Qt, log2R = a.log2R;
-    const int KP = (int)((P + 31) & ~31);              // contractions over p, in steps of 32
     const bool memw = wv >= nw;
     const int mt = tid - 64 * nw;
     const int seg = blockIdx.x % S;
@@ -1231,7 +1230,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
 
     // columns n >= N of B and C, p >= P of x and dy, and of the staged state
-    // stay zero (the contractions over p run in steps of 32)
+    // stay zero (the contractions over p always run over the 64 rows of a group)
     for (int i = tid; i < 2 * ROWS * LDB; i += blockDim.x) {
         if (OUT) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
         sC[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
@@ -1317,8 +1316,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
             for (int u = wv; u < 6; u += nw) {
                 const int ub = u % 3, mb = ub == 2 ? 1 : 0, jb = ub == 0 ? 0 : 1;
-                const f32x4 acc = u < 3 ? rows_dot32(tB, LDB, 16 * mb, tC, LDB, 16 * jb, NP, lane)
-                                        : rows_dot32(tX, LDX, 16 * mb, tDy, LDX, 16 * jb, KP, lane);
+                const f32x4 acc = u < 3 ? rows_dot32<NP>(tB, LDB, 16 * mb, tC, LDB, 16 * jb, lane)
+                                        : rows_dot32<kRowGroup>(tX, LDX, 16 * mb, tDy, LDX, 16 * jb, lane);
                 put_masked(sM[u], acc, mb, jb, true, cum, log2R, lane);
             }
             __syncthreads();
@@ -1353,7 +1352,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 for (int i = 0; i < 2; ++i)
 #pragma unroll
                     for (int kb = 0; kb < kRowGroup / 32; ++kb)
-                        if (32 * kb < KP) xs[i][kb] = row8(tX + (16 * i + l16) * LDX + 32 * kb + 8 * q);
+                        xs[i][kb] = row8(tX + (16 * i + l16) * LDX + 32 * kb + 8 * q);
                 // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
                 const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
                 const auto prs = tile_rows16(dst, f0, TR, rs);
@@ -1362,7 +1361,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < kRowGroup / 32; ++kb) {
-                        if (32 * kb >= KP) break;
                         const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
                         z0 = mma32(xs[0][kb], hb, z0);
                         z1 = mma32(xs[1][kb], hb, z1);
