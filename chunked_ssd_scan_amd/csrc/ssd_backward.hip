@@ -1345,6 +1345,17 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 zx[0] = mma32(blk_pair(sM[0], sM[1], lane), d8, zx[0]);
                 zx[1] = mma32(blk_pair(nullptr, sM[2], lane), d8, zx[1]);
             }
+            // dx rows (rows past TR dropped; their dy and x are zero), stored before
+            // the dB partial rows so that using dy waits on no partial store
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int r = 16 * i + 4 * q + v;
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(Dh, dyr[i][v], zx[i][v])), drs, xrow,
+                                                          (16 * i + v) * xrowb, 0);
+                    dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
+                }
             // dB partial = w o (x H) + (G' o L') C on the wave's column tiles
             {
                 s16x8 xs[2][kRowGroup / 32];
@@ -1385,16 +1396,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                     for (int c = wv; c < NT && 16 * c < N; c += nw) db_tile(c);
                 }
             }
-            // dx rows (rows past TR dropped; their dy and x are zero)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * q + v;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(Dh, dyr[i][v], zx[i][v])), drs, xrow,
-                                                          (16 * i + v) * xrowb, 0);
-                    dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
-                }
         }
         // H <- e^{last} H + (e^{cum} o dy)^T C, contracted over the tile's 32 rows
         const float carry = cum[kCumE + kTileRows - 1];
