@@ -115,6 +115,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
     for (int i = tid; i < 2 * kPadRows * LDX; i += nthr)
         sX[i / (kPadRows * LDX)][kTileRows * LDX + i % (kPadRows * LDX)] = TI(0);
     for (int i = tid; i < 2 * ROWS * LDB; i += nthr) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
+    // the angles of pairs past N/2 are never staged: they stay zero, so that
+    // every lane reads its pair's angle without a guard
+    for (int i = tid; i < 2 * kTileRows * NH; i += nthr) (&sTh[0][0])[i] = 0.f;
     __syncthreads();
 
     // ---- staging (memory waves): tile k's x rows [32][PG], B rows [32][N],
@@ -222,6 +225,14 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
         // MFMA beyond R are zero. Lane groups with no rank read the step's
         // first rows.
         const int kr0 = (4 * q < Ri) ? 4 * q : 0;
+        // the K slots of the write: x slot 4q + e and B row e count when they
+        // hold one of the step's R ranks (bit masks, applied without a branch)
+        s16x4 xmask, bmask;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            xmask[e] = (4 * q + e < Ri) ? (short)-1 : (short)0;
+            bmask[e] = (e < Ri) ? (short)-1 : (short)0;
+        }
         const int xcol = 16 * wv;                  // this wave's columns in the staged x tile
 
         __syncthreads();                           // tile k0 staged
@@ -236,7 +247,7 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
                     const int n = 16 * c + l16;
-                    const float th = (n < N) ? sTh[buf][s * NH + (n >> 1)] : 0.f;
+                    const float th = sTh[buf][s * NH + (n >> 1)];
                     const float rev = th * kInv2Pi;
                     const float co = __builtin_amdgcn_cosf(rev), si = __builtin_amdgcn_sinf(rev);
                     cs_self[c] = al * co;
@@ -253,18 +264,12 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
                 // this step's rank-R write
                 const int row = s * Ri;
                 if constexpr (BF) {
-                    s16x4 xa = tr_rows4(reinterpret_cast<const uint16_t*>(sX[buf]), LDX, row + kr0, xcol, lane);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (4 * q + e >= Ri) xa[e] = 0;
+                    const s16x4 xa = tr_rows4(reinterpret_cast<const uint16_t*>(sX[buf]), LDX, row + kr0, xcol, lane) &
+                                     xmask;
 #pragma unroll
                     for (int c = 0; c < NT; ++c) {
-                        s16x4 bb = tr_rows4(reinterpret_cast<const uint16_t*>(sB[buf]), LDB, row + kr0, 16 * c, lane);
-                        if (Ri < 4) {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                if (e >= Ri) bb[e] = 0;
-                        }
+                        const s16x4 bb =
+                            tr_rows4(reinterpret_cast<const uint16_t*>(sB[buf]), LDB, row + kr0, 16 * c, lane) & bmask;
                         hs[c] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(xa, bb, hs[c], 0, 0, 0);
                     }
                 } else {
