@@ -83,7 +83,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
-    __shared__ __attribute__((aligned(16))) float sTh[2][kTileRows * NH];
+    // per step and state pair: cos and sin of the step's angle (the memory
+    // waves evaluate them while staging)
+    __shared__ __attribute__((aligned(16))) float2 sCS[2][kTileRows * NH];
     __shared__ float sDa[2][kTileRows];
     __shared__ __attribute__((aligned(16))) float sRed[NB2 * 256 + NP];
 
@@ -117,11 +119,12 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
     for (int i = tid; i < 2 * ROWS * LDB; i += nthr) sB[i / (ROWS * LDB)][i % (ROWS * LDB)] = TI(0);
     // the angles of pairs past N/2 are never staged: they stay zero, so that
     // every lane reads its pair's angle without a guard
-    for (int i = tid; i < 2 * kTileRows * NH; i += nthr) (&sTh[0][0])[i] = 0.f;
+    for (int i = tid; i < 2 * kTileRows * NH; i += nthr) (&sCS[0][0])[i] = make_float2(0.f, 0.f);
     __syncthreads();
 
     // ---- staging (memory waves): tile k's x rows [32][PG], B rows [32][N],
-    // theta [Qt][N/2], da [Qt]; rows past the sequence are zero (identity steps)
+    // theta [Qt][N/2] (as the cos and sin of each angle), da [Qt]; rows past the
+    // sequence are zero (identity steps)
     const TI* xg = static_cast<const TI*>(a.x);
     const TI* Bg = static_cast<const TI*>(a.B);
     const int xur = PG / EPU, nbu = (int)((N + EPU - 1) / EPU), thu = (int)((N / 2 + 3) / 4);
@@ -170,7 +173,18 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 #pragma unroll
         for (int m = 0; m < THR; ++m) {
             const int u = mt + m * NTM, st = u / thu, c = (u % thu) * 4;
-            if (st < Qt) *reinterpret_cast<uint4*>(&sTh[buf][st * NH + c]) = rth[m];
+            if (st < Qt) {
+                // the hardware sine and cosine take revolutions
+                const float th[4] = {__uint_as_float(rth[m].x), __uint_as_float(rth[m].y), __uint_as_float(rth[m].z),
+                                     __uint_as_float(rth[m].w)};
+                float4* d = reinterpret_cast<float4*>(&sCS[buf][st * NH + c]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const float r0 = th[2 * j] * kInv2Pi, r1 = th[2 * j + 1] * kInv2Pi;
+                    d[j] = make_float4(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_sinf(r0), __builtin_amdgcn_cosf(r1),
+                                       __builtin_amdgcn_sinf(r1));
+                }
+            }
         }
         if (mt < Qt) sDa[buf][mt] = rda;
     };
@@ -247,9 +261,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
                     const int n = 16 * c + l16;
-                    const float th = sTh[buf][s * NH + (n >> 1)];
-                    const float rev = th * kInv2Pi;
-                    const float co = __builtin_amdgcn_cosf(rev), si = __builtin_amdgcn_sinf(rev);
+                    const float2 csn = sCS[buf][s * NH + (n >> 1)];
+                    const float co = csn.x, si = csn.y;
                     cs_self[c] = al * co;
                     cs_part[c] = (n & 1) ? al * si : -al * si;
                 }
