@@ -83,10 +83,9 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
 
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
     __shared__ __attribute__((aligned(16))) TI sB[2][ROWS * LDB];
-    // per step and state pair: cos and sin of the step's angle (the memory
-    // waves evaluate them while staging)
+    // per step and state pair: e^{da} cos and e^{da} sin of the step's decay
+    // and angle (the memory waves evaluate them while staging)
     __shared__ __attribute__((aligned(16))) float2 sCS[2][kTileRows * NH];
-    __shared__ float sDa[2][kTileRows];
     __shared__ __attribute__((aligned(16))) float sRed[NB2 * 256 + NP];
 
     const int tid = threadIdx.x, nthr = blockDim.x;
@@ -123,13 +122,13 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
     __syncthreads();
 
     // ---- staging (memory waves): tile k's x rows [32][PG], B rows [32][N],
-    // theta [Qt][N/2] (as the cos and sin of each angle), da [Qt]; rows past the
-    // sequence are zero (identity steps)
+    // theta [Qt][N/2] and da [Qt] (as e^{da} times the cos and sin of each
+    // angle); rows past the sequence are zero (identity steps)
     const TI* xg = static_cast<const TI*>(a.x);
     const TI* Bg = static_cast<const TI*>(a.B);
     const int xur = PG / EPU, nbu = (int)((N + EPU - 1) / EPU), thu = (int)((N / 2 + 3) / 4);
     uint4 rx[XR], rb[BRG], rth[THR];
-    float rda = 0.f;
+    float rda[THR];
     auto load_tile = [&](int k) {
         const int64_t f0 = (int64_t)k * kTileRows;
 #pragma unroll
@@ -156,8 +155,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
                 if (c + 4 <= N / 2) v = *reinterpret_cast<const uint4*>(src);
             }
             rth[m] = v;
+            rda[m] = (st < Qt && t0 + st < T) ? a.da[(b * T + t0 + st) * H + h] : 0.f;
         }
-        rda = (mt < Qt && t0 + mt < T) ? a.da[(b * T + t0 + mt) * H + h] : 0.f;
     };
     auto store_tile = [&](int buf) {
 #pragma unroll
@@ -177,16 +176,16 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
                 // the hardware sine and cosine take revolutions
                 const float th[4] = {__uint_as_float(rth[m].x), __uint_as_float(rth[m].y), __uint_as_float(rth[m].z),
                                      __uint_as_float(rth[m].w)};
+                const float al = __expf(rda[m]);
                 float4* d = reinterpret_cast<float4*>(&sCS[buf][st * NH + c]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const float r0 = th[2 * j] * kInv2Pi, r1 = th[2 * j + 1] * kInv2Pi;
-                    d[j] = make_float4(__builtin_amdgcn_cosf(r0), __builtin_amdgcn_sinf(r0), __builtin_amdgcn_cosf(r1),
-                                       __builtin_amdgcn_sinf(r1));
+                    d[j] = make_float4(al * __builtin_amdgcn_cosf(r0), al * __builtin_amdgcn_sinf(r0),
+                                       al * __builtin_amdgcn_cosf(r1), al * __builtin_amdgcn_sinf(r1));
                 }
             }
         }
-        if (mt < Qt) sDa[buf][mt] = rda;
     };
 
     // Memory waves and compute waves run separate loops with the same
@@ -256,15 +255,13 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
                 const int64_t t = (int64_t)k * Qt + s;
                 if (t >= T) break;
                 // decay and turn of every state pair, against the partner lane
-                const float al = __expf(sDa[buf][s]);
                 float cs_self[NT], cs_part[NT];
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
                     const int n = 16 * c + l16;
                     const float2 csn = sCS[buf][s * NH + (n >> 1)];
-                    const float co = csn.x, si = csn.y;
-                    cs_self[c] = al * co;
-                    cs_part[c] = (n & 1) ? al * si : -al * si;
+                    cs_self[c] = csn.x;
+                    cs_part[c] = (n & 1) ? csn.y : -csn.y;
                 }
 #pragma unroll
                 for (int c = 0; c < NT; ++c) {
