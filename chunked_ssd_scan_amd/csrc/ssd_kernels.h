@@ -1414,10 +1414,29 @@ __global__ __launch_bounds__(64 * (W + cols_mem_waves(W, ROT))) void ssd_cols_ke
                 carry = wrap_angle(carry + run);
                 typedef __attribute__((ext_vector_type(4))) short s16x4;
                 const uint2* trow = tab + (l16 >> log2R) * RSTR + (lane & 3);
+                // the state pass, where the memory waves set the pace: every
+                // table row of the turn read before its first store, so that
+                // the reads are in flight together (the output walk keeps
+                // them interleaved, which measured faster there)
+                uint2 mr[OUT ? 1 : KS][2];
+                if constexpr (!OUT) {
+#pragma unroll
+                    for (int s = 0; s < KS; ++s) {
+                        mr[s][0] = trow[(8 * s + 2 * q) * 4];
+                        mr[s][1] = trow[(8 * s + 2 * q + 1) * 4];
+                    }
+                }
 #pragma unroll
                 for (int s = 0; s < KS; ++s) {
                     // pair groups 8 s + 2 q and 8 s + 2 q + 1 of this row's step
-                    const uint2 m0 = trow[(8 * s + 2 * q) * 4], m1 = trow[(8 * s + 2 * q + 1) * 4];
+                    uint2 m0, m1;
+                    if constexpr (!OUT) {
+                        m0 = mr[s][0];
+                        m1 = mr[s][1];
+                    } else {
+                        m0 = trow[(8 * s + 2 * q) * 4];
+                        m1 = trow[(8 * s + 2 * q + 1) * 4];
+                    }
                     const uint4 w = rf[slot][s];
                     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
                     const f32x4 d0 = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(
