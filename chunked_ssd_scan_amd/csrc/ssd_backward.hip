@@ -1683,8 +1683,7 @@ void* bwd_reduce_for(int64_t R) {
 // final state's terms at the last step. Four kernels: the final state's terms
 // and dD (per (batch, head)), the sums of chunks of kScanChunk steps, each
 // chunk's carry (the final terms plus the sums of the chunks after it, one
-// thread per (batch, head, column) walking the chunks), and the scan of each
-// chunk from its carry.
+// wave per (batch, head, column)), and the scan of each chunk from its carry.
 constexpr int kScanChunk = 64;
 constexpr int kCarryBlock = 16;   // chunks whose sums a carry thread loads at once
 
@@ -1826,27 +1825,37 @@ __global__ __launch_bounds__(128) void ssd_bwd_chunk_sums(const float* __restric
 }
 
 // the chunks' sums replaced in place by each chunk's carry: the final terms
-// plus the sums of the chunks after it
-__global__ __launch_bounds__(128) void ssd_bwd_chunk_carry(const float* __restrict__ ft, float* __restrict__ csum,
+// plus the sums of the chunks after it. One wave per (batch, head, column):
+// lane l takes the chunks [l per, l per + per), per = ceil(nchunk / 64); the
+// lanes' totals are summed from the last lane down by shuffles, then each lane
+// walks its chunks from its last one, storing the carries.
+__global__ __launch_bounds__(256) void ssd_bwd_chunk_carry(const float* __restrict__ ft, float* __restrict__ csum,
                                                           int nchunk, int nc, int k0, int64_t items) {
-    const int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (it >= items) return;
+    const int64_t it = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (it >= items) return;   // whole waves
+    const int lane = threadIdx.x & 63;
     const int ncols = nc - k0;
     const int k = k0 + (int)(it % ncols);
     const int64_t bh = it / ncols;
     float* col = csum + bh * nchunk * nc + k;
-    float acc = ft[bh * nc + k];
-    // blocks of kCarryBlock chunks from the last: every load of a block is
-    // issued before its stores (same array), so that they are in flight together
-    for (int c0 = nchunk - 1; c0 >= 0; c0 -= kCarryBlock) {
-        float v[kCarryBlock];
+    const int per = (nchunk + 63) >> 6;
+    const int c0 = lane * per, c1 = c0 + per < nchunk ? c0 + per : nchunk;
+    float tot = 0.f;
+    for (int c = c0; c < c1; ++c) tot += col[(int64_t)c * nc];
+    // inclusive sums over this lane and the lanes after it; the carry into a
+    // lane's chunks is the next lane's
+    float suf = tot;
 #pragma unroll
-        for (int j = 0; j < kCarryBlock; ++j) v[j] = c0 - j >= 0 ? col[(int64_t)(c0 - j) * nc] : 0.f;
-#pragma unroll
-        for (int j = 0; j < kCarryBlock; ++j) {
-            if (c0 - j >= 0) col[(int64_t)(c0 - j) * nc] = acc;
-            acc += v[j];
-        }
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_down(suf, d, 64);
+        suf += lane + d < 64 ? o : 0.f;
+    }
+    const float after = __shfl_down(suf, 1, 64);
+    float acc = ft[bh * nc + k] + (lane < 63 ? after : 0.f);
+    for (int c = c1 - 1; c >= c0; --c) {
+        const float v = col[(int64_t)c * nc];
+        col[(int64_t)c * nc] = acc;
+        acc += v;
     }
 }
 
@@ -2155,7 +2164,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
             const dim3 sgrid((unsigned)((items + 127) / 128));
             const int64_t citems = b * H * (int64_t)(nc - k0);
             hipLaunchKernelGGL(ssd_bwd_chunk_sums, sgrid, dim3(128), 0, hs, hv, th, csum, T, H, N, nchunk, k0, items);
-            hipLaunchKernelGGL(ssd_bwd_chunk_carry, dim3((unsigned)((citems + 127) / 128)), dim3(128), 0, hs, ft, csum,
+            hipLaunchKernelGGL(ssd_bwd_chunk_carry, dim3((unsigned)((citems + 3) / 4)), dim3(256), 0, hs, ft, csum,
                                nchunk, nc, k0, citems);
             hipLaunchKernelGGL(ssd_bwd_chunk_scan, sgrid, dim3(128), 0, hs, hv, th, csum, dda, dtheta, T, H, N,
                                nchunk, k0, items);
