@@ -997,26 +997,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rows16(const uint16_t* ba
     return make_rsrc(base + f0 * rs, (uint32_t)(rows * rs * 2));
 }
 
-// Rows 16 i + 4 q + v of a tile, columns 16 c + l16 from the lane's byte
-// offset voff (row 4 q, column l16) and the uniform row and column steps
-__device__ __forceinline__ void store_tile_rows(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
-                                                uint32_t voff, uint32_t rowb, uint32_t colb) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z0[v]), rsrc, voff, colb + v * rowb, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(z1[v]), rsrc, voff, colb + (16 + v) * rowb, 0);
-    }
-}
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
-// The same rows and columns rounded to bf16 (to nearest even), 2 bytes each
-__device__ __forceinline__ void store_tile_rows16(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
+// A tile computed transposed (the product's operands swapped, so that a lane
+// holds row l16 and the four columns 4 q .. 4 q + 3 of a 16-column tile):
+// rows i16 + l16 (i16 = 0, 16), rounded to bf16 (to nearest even), one 8-byte
+// store per row from the lane's byte offset voff (row l16, column 4 q)
+__device__ __forceinline__ void store_tile_cols16(__amdgpu_buffer_rsrc_t rsrc, const f32x4& z0, const f32x4& z1,
                                                   uint32_t voff, uint32_t rowb, uint32_t colb) {
-    const s16x4 h0 = pack4_bf16(z0), h1 = pack4_bf16(z1);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h0[v], rsrc, voff, colb + v * rowb, 0);
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)h1[v], rsrc, voff, colb + (16 + v) * rowb, 0);
-    }
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4_bf16(z0)), rsrc, voff, colb, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pack4_bf16(z1)), rsrc, voff, colb + 16 * rowb, 0);
 }
 
 // Forward direction: the head's dC partial rows and the final state. ROT: in
@@ -1052,7 +1042,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     const int k0 = (int)(((int64_t)seg * a.nsub) / S), k1 = (int)(((int64_t)(seg + 1) * a.nsub) / S);
     uint16_t* dst = static_cast<uint16_t*>(a.part) + (b * TR * H + h) * N;   // [b][TR][H][N], bf16
     const int64_t rs = H * N;
-    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 2), rowb = (uint32_t)(rs * 2);
+    // lane byte offset of the partial tiles (computed transposed): row l16, column 4 q
+    const uint32_t prow = (uint32_t)((l16 * rs + 4 * q) * 2), rowb = (uint32_t)(rs * 2);
 
     // columns n >= N of B, p >= P of x and dy, and of the staged state stay
     // zero (the contractions over p always run over the 64 rows of a group)
@@ -1115,13 +1106,13 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             put_masked(sM[u], gacc, mb, jb, false, cum, log2R, lane);
         }
         __syncthreads();
-        // dC = e^{cum_m} (dy h_in) + (G o L) B on the wave's column tiles
-        float ein[2][4];
+        // dC = e^{cum_m} (dy h_in) + (G o L) B on the wave's column tiles,
+        // computed transposed (lane: step row 16 i + l16, four columns)
+        float ein[2];
         s16x8 dya[2][kRowGroup / 32];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) ein[i][v] = cum[kCumE + 16 * i + 4 * q + v];
+            ein[i] = cum[kCumE + 16 * i + l16];
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 32; ++kb)
                 dya[i][kb] = row8(tDy + (16 * i + l16) * LDX + 32 * kb + 8 * q);
@@ -1135,18 +1126,18 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
 #pragma unroll
             for (int kb = 0; kb < kRowGroup / 32; ++kb) {
                 const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
-                z0 = mma32(dya[0][kb], hb, z0);
-                z1 = mma32(dya[1][kb], hb, z1);
+                z0 = mma32(hb, dya[0][kb], z0);
+                z1 = mma32(hb, dya[1][kb], z1);
             }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                z0[v] *= ein[0][v];
-                z1[v] *= ein[1][v];
+                z0[v] *= ein[0];
+                z1[v] *= ein[1];
             }
             const s16x8 bb = tr_rows8(tB, LDB, 8 * q, 16 * c, lane);
-            z0 = mma32(m0, bb, z0);
-            z1 = mma32(m1, bb, z1);
-            store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
+            z0 = mma32(bb, m0, z0);
+            z1 = mma32(bb, m1, z1);
+            store_tile_cols16(prs, z0, z1, prow, rowb, 32u * c);
         };
         if (NT % (kRowGroup / 16) == 0 && nw == kRowGroup / 16 && N == NP) {
             // four compute waves and every column tile in range: unrolled, so
@@ -1222,9 +1213,10 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     if (!OUT && seg == 0) return;
     uint16_t* dst = OUT ? static_cast<uint16_t*>(a.part) + (b * TR * H + h) * N : nullptr;   // bf16
     const int64_t rs = H * N;
-    // lane byte offsets of a tile's rows 4 q (+ uniform steps): partial rows
-    // (stride H N, bf16) at column l16, dy and dx rows (stride H P) at column p0 + l16
-    const uint32_t prow = (uint32_t)((4 * q * rs + l16) * 2), rowb = (uint32_t)(rs * 2);
+    // lane byte offsets (+ uniform steps): the partial tiles, computed
+    // transposed, at row l16, column 4 q (stride H N, bf16); dy and dx at
+    // row 4 q, column p0 + l16 (stride H P)
+    const uint32_t prow = (uint32_t)((l16 * rs + 4 * q) * 2), rowb = (uint32_t)(rs * 2);
     const uint32_t xrow = (uint32_t)((4 * q * H * P + 16 * wv + l16) * 4), xrowb = (uint32_t)(H * P * 4);
     const float* dyh = a.dy + (b * TR * H + h) * P;
     float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
@@ -1367,24 +1359,26 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
                 const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
                 const auto prs = tile_rows16(dst, f0, TR, rs);
+                // the partial tiles transposed: the lane's step row is 16 i + l16
+                const float wl[2] = {cum[kCumW + l16], cum[kCumW + 16 + l16]};
                 // the wave's dB column tiles c = wv, wv + nw, ...
                 auto db_tile = [&](int c) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int kb = 0; kb < kRowGroup / 32; ++kb) {
                         const s16x8 hb = row8(sH + (16 * c + l16) * kLdh + 32 * kb + 8 * q);
-                        z0 = mma32(xs[0][kb], hb, z0);
-                        z1 = mma32(xs[1][kb], hb, z1);
+                        z0 = mma32(hb, xs[0][kb], z0);
+                        z1 = mma32(hb, xs[1][kb], z1);
                     }
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
-                        z0[v] *= wr[0][v];
-                        z1[v] *= wr[1][v];
+                        z0[v] *= wl[0];
+                        z1[v] *= wl[1];
                     }
                     const s16x8 cc = tr_rows8(tC, LDB, 8 * q, 16 * c, lane);
-                    z0 = mma32(g0, cc, z0);
-                    z1 = mma32(g1, cc, z1);
-                    store_tile_rows16(prs, z0, z1, prow, rowb, 32u * c);
+                    z0 = mma32(cc, g0, z0);
+                    z1 = mma32(cc, g1, z1);
+                    store_tile_cols16(prs, z0, z1, prow, rowb, 32u * c);
                 };
                 if (NT % (kRowGroup / 16) == 0 && nw == kRowGroup / 16 && N == NP) {
                     // four compute waves and every column tile in range: unrolled, so
