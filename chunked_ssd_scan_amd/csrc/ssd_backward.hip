@@ -998,6 +998,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rows16(const uint16_t* ba
 }
 
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4v;
 
 // A tile computed transposed (the product's operands swapped, so that a lane
 // holds row l16 and the four columns 4 q .. 4 q + 3 of a 16-column tile):
@@ -1213,11 +1214,16 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
     if (!OUT && seg == 0) return;
     uint16_t* dst = OUT ? static_cast<uint16_t*>(a.part) + (b * TR * H + h) * N : nullptr;   // bf16
     const int64_t rs = H * N;
-    // lane byte offsets (+ uniform steps): the partial tiles, computed
-    // transposed, at row l16, column 4 q (stride H N, bf16); dy and dx at
-    // row 4 q, column p0 + l16 (stride H P)
+    // lane byte offsets (+ uniform steps): the partial tiles at row l16,
+    // column 4 q (stride H N, bf16); dy and dx at rows l16 and 16 + l16,
+    // columns p0 + 4 q .. p0 + 4 q + 3 (stride H P, fp32). The dx stores take
+    // the whole offset in the lane register and a zero scalar offset: for a
+    // 16-byte store in that form the compiler keeps the next instruction from
+    // overwriting the store's data registers, which it does not do for a
+    // register scalar offset
     const uint32_t prow = (uint32_t)((l16 * rs + 4 * q) * 2), rowb = (uint32_t)(rs * 2);
-    const uint32_t xrow = (uint32_t)((4 * q * H * P + 16 * wv + l16) * 4), xrowb = (uint32_t)(H * P * 4);
+    const uint32_t xrow0 = (uint32_t)((l16 * H * P + 16 * wv + 4 * q) * 4), xrowb = (uint32_t)(H * P * 4);
+    const uint32_t xrow1 = xrow0 + 16u * xrowb;
     const float* dyh = a.dy + (b * TR * H + h) * P;
     float* dxh = OUT ? a.dx + (b * TR * H + h) * P : nullptr;
 
@@ -1297,12 +1303,10 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
             // last; rows past TR read zero
             const int64_t f0 = (int64_t)k * kTileRows;
             const auto xrs = tile_rows(dyh, f0, TR, H * P), drs = tile_rows(dxh, f0, TR, H * P);
-            float dyr[2][4];
+            float4 dyr[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v)
-                    dyr[i][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(xrs, xrow, (16 * i + v) * xrowb, 0));
+                dyr[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(xrs, i ? xrow1 : xrow0, 0, 0));
             put_state<NT>(sH, hp, p0, lane);
             // upper blocks (0,0), (0,1), (1,1): CB' = B_m . C_j (jobs 0-2) and
             // G' = x_m . dy_j (jobs 3-5), masked by step(j) >= step(m)
@@ -1313,11 +1317,10 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 put_masked(sM[u], acc, mb, jb, true, cum, log2R, lane);
             }
             __syncthreads();
-            float wr[2][4];                        // e^{last - cum_m}, rows 16 i + 4 q + v
+            // the tiles below are computed transposed: the lane's step row is 16 i + l16
+            float wl[2];                           // e^{last - cum_m}
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) wr[i][v] = cum[kCumW + 16 * i + 4 * q + v];
+            for (int i = 0; i < 2; ++i) wl[i] = cum[kCumW + 16 * i + l16];
             // dx = w o (B H^T) + (CB' o L') dy over this wave's p
             f32x4 zx[2];
 #pragma unroll
@@ -1326,28 +1329,31 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
 #pragma unroll
                 for (int c2 = 0; c2 < NT / 2; ++c2) {
                     const s16x8 bs = row8(tB + (16 * i + l16) * LDB + 32 * c2 + 8 * q);
-                    zx[i] = mma32(bs, tr_rows8(sH, kLdh, 32 * c2 + 8 * q, p0, lane), zx[i]);
+                    zx[i] = mma32(tr_rows8(sH, kLdh, 32 * c2 + 8 * q, p0, lane), bs, zx[i]);
                 }
 #pragma unroll
-                for (int v = 0; v < 4; ++v) zx[i][v] *= wr[i][v];
+                for (int v = 0; v < 4; ++v) zx[i][v] *= wl[i];
             }
             {
                 // block rows [CB' (0,0) | (0,1)] and [0 | (1,1)] against dy's 32 rows
                 const s16x8 d8 = tr_rows8(tDy, LDX, 8 * q, p0, lane);
-                zx[0] = mma32(blk_pair(sM[0], sM[1], lane), d8, zx[0]);
-                zx[1] = mma32(blk_pair(nullptr, sM[2], lane), d8, zx[1]);
+                zx[0] = mma32(d8, blk_pair(sM[0], sM[1], lane), zx[0]);
+                zx[1] = mma32(d8, blk_pair(nullptr, sM[2], lane), zx[1]);
             }
             // dx rows (rows past TR dropped; their dy and x are zero), stored before
             // the dB partial rows so that using dy waits on no partial store
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i) {
+                const float dv[4] = {dyr[i].x, dyr[i].y, dyr[i].z, dyr[i].w};
+                const s16x4 xv = row4(reinterpret_cast<const uint16_t*>(sX[buf]) + (16 * i + l16) * LDX + p0 + 4 * q);
+                f32x4 o;
 #pragma unroll
                 for (int v = 0; v < 4; ++v) {
-                    const int r = 16 * i + 4 * q + v;
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(fmaf(Dh, dyr[i][v], zx[i][v])), drs, xrow,
-                                                          (16 * i + v) * xrowb, 0);
-                    dd = fmaf(dyr[i][v], to_f32(sX[buf][r * LDX + p0 + l16]), dd);
+                    o[v] = fmaf(Dh, dv[v], zx[i][v]);
+                    dd = fmaf(dv[v], __uint_as_float((uint32_t)(uint16_t)xv[v] << 16), dd);
                 }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4v, o), drs, i ? xrow1 : xrow0, 0, 0);
+            }
             // dB partial = w o (x H) + (G' o L') C on the wave's column tiles
             {
                 s16x8 xs[2][kRowGroup / 32];
@@ -1359,8 +1365,6 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void s
                 // block rows [G' (0,0) | (0,1)] and [0 | (1,1)]
                 const s16x8 g0 = blk_pair(sM[3], sM[4], lane), g1 = blk_pair(nullptr, sM[5], lane);
                 const auto prs = tile_rows16(dst, f0, TR, rs);
-                // the partial tiles transposed: the lane's step row is 16 i + l16
-                const float wl[2] = {cum[kCumW + l16], cum[kCumW + 16 + l16]};
                 // the wave's dB column tiles c = wv, wv + nw, ...
                 auto db_tile = [&](int c) {
                     f32x4 z0 = {0.f, 0.f, 0.f, 0.f}, z1 = {0.f, 0.f, 0.f, 0.f};
