@@ -1510,8 +1510,10 @@ __device__ __forceinline__ float wave_sum64(float v) {
 }
 
 // Two consecutive entries (a state pair) of a row: bf16 or fp32 storage.
+// bf16 rows (the chunked walks' partials, read once) load with the
+// non-temporal hint.
 __device__ __forceinline__ float2 ld_pair(const uint16_t* p, uint32_t pair) {
-    const uint32_t w = reinterpret_cast<const uint32_t*>(p)[pair];
+    const uint32_t w = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p) + pair);
     return make_float2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 __device__ __forceinline__ float2 ld_pair(const float* p, uint32_t pair) {
