@@ -54,9 +54,14 @@ constexpr int kPadRows = 4;          // zero rows after a tile (reads past its l
 constexpr int kRowGroup = 64;        // most state rows p per workgroup
 constexpr int kMemWaves = 2;
 constexpr int kMaxWaves = kRowGroup / 16 + kMemWaves;
-// memory waves of the chunked walks: with rotation they also turn B and C
-// (measured on the Mamba-3 MIMO layer: four take the call from 3.48 to 2.89 ms)
+// Memory waves of the chunked walks. With rotation four (they also turn B and
+// C while staging; measured on the Mamba-3 MIMO layer they took the call from
+// 3.48 to 2.89 ms). Without rotation four for the forward-direction walk
+// (2.7B layer 3.46 -> 3.33 ms a call) but two for the backward walk: at its
+// register count a workgroup of eight waves would leave one slot per CU
+// instead of two.
 constexpr int bwdc_mem_waves(bool rot) { return rot ? 4 : 2; }
+constexpr int bwdc_fwd_mem_waves(bool) { return 4; }
 
 struct BwdArgs {
     const void* x;
@@ -1017,9 +1022,9 @@ __device__ __forceinline__ void store_tile_cols16(__amdgpu_buffer_rsrc_t rsrc, c
 // c = wv, wv + nw, ... with the contraction over every p read from the staged
 // entering state.
 template <int NP, bool ROT>
-__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void ssd_bwdc_forward_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_fwd_mem_waves(ROT))) void ssd_bwdc_forward_kernel(BwdArgs a) {
     using TI = uint16_t;
-    constexpr int MW = bwdc_mem_waves(ROT);
+    constexpr int MW = bwdc_fwd_mem_waves(ROT);
     using St = Stage<TI, NP, true, true, false, MW>;
     constexpr int NT = NP / 16, LDX = St::LDX, LDB = St::LDB, ROWS = kTileRows;
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
@@ -2064,6 +2069,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
     ba.phi = phi;
     // the chunked walks with rotation run four memory waves, the others two
     const dim3 grid((unsigned)nwg), block((unsigned)(64 * (PG / 16 + (chunked ? bwdc_mem_waves(rot) : kMemWaves))));
+    const dim3 fblock((unsigned)(64 * (PG / 16 + (chunked ? bwdc_fwd_mem_waves(rot) : kMemWaves))));
 
     // 0. the cumulative angles (chunked walks with rotation)
     ssd_status rs = SSD_OK;
@@ -2102,7 +2108,7 @@ extern "C" ssd_status ssd_backward(const ssd_dims* d, const void* x, const float
         fa.part = ws + o_pC;
         fa.final_state = fin;
         void* kargs[] = {&fa};
-        if (hipLaunchKernel(kf, grid, block, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
+        if (hipLaunchKernel(kf, grid, fblock, kargs, 0, fs) != hipSuccess) rs = SSD_ERR_HIP;
     }
     // 2. backward state pass and reverse carry (more than one segment)
     float* seg_in = reinterpret_cast<float*>(ws + o_segin);
