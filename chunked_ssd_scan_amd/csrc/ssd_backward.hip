@@ -54,14 +54,17 @@ constexpr int kPadRows = 4;          // zero rows after a tile (reads past its l
 constexpr int kRowGroup = 64;        // most state rows p per workgroup
 constexpr int kMemWaves = 2;
 constexpr int kMaxWaves = kRowGroup / 16 + kMemWaves;
-// Memory waves of the chunked walks. With rotation four (they also turn B and
-// C while staging; measured on the Mamba-3 MIMO layer they took the call from
-// 3.48 to 2.89 ms). Without rotation four for the forward-direction walk
-// (2.7B layer 3.46 -> 3.33 ms a call) but two for the backward walk: at its
-// register count a workgroup of eight waves would leave one slot per CU
-// instead of two.
-constexpr int bwdc_mem_waves(bool rot) { return rot ? 4 : 2; }
+// Memory waves of the chunked walks: four. With rotation they also turn B and
+// C while staging (measured on the Mamba-3 MIMO layer four took the call from
+// 3.48 to 2.89 ms); without it four instead of two took the 2.7B layer's call
+// from 3.46 to 3.33 ms (forward-direction walk) and 3.21 ms (both walks). The
+// backward walk without rotation is then held to 128 VGPRs (four waves per
+// SIMD), so that two workgroups of eight waves still fit a CU; with rotation
+// that limit spills more and was slower (MIMO layer 1.77 -> 2.15 ms), so it
+// keeps three waves per SIMD.
+constexpr int bwdc_mem_waves(bool) { return 4; }
 constexpr int bwdc_fwd_mem_waves(bool) { return 4; }
+constexpr int bwdc_bwd_waves_per_simd(bool rot) { return rot ? 3 : 4; }
 
 struct BwdArgs {
     const void* x;
@@ -1187,7 +1190,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_fwd_mem_waves(ROT))) vo
 // one as bf16 [n][p], read transposed for dx and, for the dB partial on the
 // wave's column tiles c = wv, wv + nw, ..., contracted over every p.
 template <int NP, int MODE, bool ROT>
-__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT))) void ssd_bwdc_backward_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * (kRowGroup / 16 + bwdc_mem_waves(ROT)))
+__attribute__((amdgpu_waves_per_eu(bwdc_bwd_waves_per_simd(ROT)))) void ssd_bwdc_backward_kernel(BwdArgs a) {
     using TI = uint16_t;
     constexpr bool OUT = MODE == 0;
     constexpr int MW = bwdc_mem_waves(ROT);
