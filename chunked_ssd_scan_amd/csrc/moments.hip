@@ -44,7 +44,7 @@ using namespace ssd_step;
 constexpr int kTileRows = 32;        // fused rows staged per tile (32 / R steps)
 constexpr int kPadRows = 4;          // zero rows after a tile: reads past its last step
 constexpr int kRowGroup = 64;        // most state rows p per workgroup
-constexpr int kMemWaves = 2;         // waves that stage the tiles
+constexpr int kMemWaves = 4;         // waves that stage the tiles (four: 3.55 -> 3.47 ms against two)
 
 struct MomArgs {
     const void* x;
@@ -77,8 +77,8 @@ __global__ __launch_bounds__(64 * (kRowGroup / 16 + kMemWaves)) void ssd_moments
     constexpr int EPU = 16 / ESZ;                  // elements per 16-byte unit
     constexpr int NTM = 64 * kMemWaves;            // memory threads
     // staging units per memory thread: x rows of the group, B rows, theta
-    constexpr int XR = kTileRows * kRowGroup / EPU / NTM;
-    constexpr int BRG = kTileRows * NP / EPU / NTM;
+    constexpr int XR = (kTileRows * kRowGroup / EPU + NTM - 1) / NTM;
+    constexpr int BRG = (kTileRows * NP / EPU + NTM - 1) / NTM;
     constexpr int THR = (kTileRows * NH / 4 + NTM - 1) / NTM;
 
     __shared__ __attribute__((aligned(16))) TI sX[2][ROWS * LDX];
