@@ -28,9 +28,11 @@
 // forwards in time), dx and dB only the state gradients (a walk backwards),
 // each with its own segment states from a state pass and a carry.
 //
-// Both walks step one time step at a time with the state in registers as
-// 16 x 16 MFMA accumulators, a workgroup per (batch, head, group of at most
-// 64 state rows p, segment), two memory waves staging each 32-row tile.
+// The step walks (fp32 inputs, headdim 128) step one time step at a time with
+// the state in registers as 16 x 16 MFMA accumulators, a workgroup per (batch,
+// head, group of at most 64 state rows p, segment), two memory waves staging
+// each 32-row tile; the chunked walks (bf16, headdim <= 64) take a tile at a
+// time with four memory waves.
 // Contractions over p (dC, dB) need the layout D[p][n] (lanes across n); the
 // contraction over n (dx) needs D[n][p] (lanes across p), so the backward walk
 // keeps its state gradient in both layouts and updates both.
